@@ -1,0 +1,510 @@
+/*
+ * oracle.c -- plain, slow, sequential fp64 reference for the selective scan.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the bench's
+ * CPU-baseline leg may load this library.  It shares no code, header, table or
+ * helper with the HIP path (selective_state_space_chunked_amd/csrc); the only
+ * thing both sides consume is the seeded input arrays from synth/.
+ *
+ * Every routine is the defining recurrence written out as a loop over time,
+ * one independent sequence at a time, in double precision, with libm's exp /
+ * cos / sin (no fast-math).  Inputs arrive as doubles holding exactly the
+ * float32 / bfloat16 values the GPU consumes.
+ *
+ * The problem (the pages do not print it as one formula; the readings below
+ * are the plainest ones the pages support):
+ *   h_t = A_t h_{t-1} + b_t,  y_t = C_t . h_t,  t = 0..L-1,  h_{-1} = h0.
+ *   - diagonal real, selective (lpnh.cn "S3M" page, section 1.1: step size
+ *     delta = softplus(proj x) and a = exp(delta*A) with A < 0); the input
+ *     term uses the Euler form b_t = delta_t * x_t * B_t.
+ *   - diagonal real, dense: a_t and b_t given directly.
+ *   - diagonal complex with shared controls (SPARC page, abstract: two
+ *     input-dependent scalars, retention r_t and phase phi_t, steer every
+ *     complex mode, each with its own baseline rate lambda_m and frequency
+ *     theta_m): a_{t,m} = exp(r_t ln(lambda_m) + i phi_t theta_m),
+ *     b_t = u_t, y_t = Re sum_m c_m h_{t,m}.
+ *   - PD (Flash PD-SSM page, "Neuer Selektionsmechanismus"): at every step
+ *     the argmax over K scores picks one column-one-hot matrix P from a
+ *     dictionary; A_t = P diag(d_t), so h_t[i] = b_t[i] +
+ *     sum_{j : pi_t(j) = i} d_t[j] h_{t-1}[j].
+ * Gradients are those of the scalar loss  sum_t <gy_t, y_t> + <gh_last, h_{L-1}>
+ * (the PGF page's "exact analytical derivatives"), by the adjoint recurrence
+ * lambda_t = C_t gy_t + A_{t+1}^T lambda_{t+1}.  Complex gradients use the
+ * real-pair convention g = dL/dRe + i dL/dIm.
+ *
+ * Pins that tie this file to the mathematics rather than to itself live in
+ * tests/test_oracle_pins.py (brute-force sums, closed forms, dense-matrix
+ * routes, finite differences, a DFA simulation).
+ */
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+#include <stdint.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+typedef long long i64;
+
+static int nthreads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+static int thread_id(void) {
+#ifdef _OPENMP
+    return omp_get_thread_num();
+#else
+    return 0;
+#endif
+}
+
+int orc_threads(void) { return nthreads(); }
+
+/* ------------------------------------------------------------------------- */
+/* Diagonal real scan.                                                        */
+/* mode 0 = selective: a_t[n] = exp(delta[b,d,t] * A[d,n]),                    */
+/*                     b_t[n] = delta[b,d,t] * x[b,d,t] * Bm[b,t,n]            */
+/* mode 1 = dense:     a_t[n] = a[b,d,t,n], b_t[n] = b[b,d,t,n]               */
+/* Layouts: delta, x, y, gy (B,D,L); A (D,N); Bm, C (B,L,N); a, b (B,D,L,N);  */
+/* h0, hlast (B,D,N).                                                         */
+/* ------------------------------------------------------------------------- */
+static void real_terms(int mode, i64 D, i64 L, i64 N, i64 bi, i64 di, i64 t,
+                       const double* delta, const double* x, const double* A,
+                       const double* Bm, const double* a, const double* b,
+                       i64 n, double* at, double* bt) {
+    if (mode == 0) {
+        double dl = delta[(bi * D + di) * L + t];
+        *at = exp(dl * A[di * N + n]);
+        *bt = dl * x[(bi * D + di) * L + t] * Bm[(bi * L + t) * N + n];
+    } else {
+        i64 o = ((bi * D + di) * L + t) * N + n;
+        *at = a[o];
+        *bt = b[o];
+    }
+}
+
+void orc_real_fwd(int mode, i64 B, i64 D, i64 L, i64 N,
+                  const double* delta, const double* x, const double* A, const double* Bm,
+                  const double* a, const double* b, const double* C, const double* h0,
+                  double* y, double* hlast) {
+    #pragma omp parallel
+    {
+        double* h = (double*)malloc(sizeof(double) * N);
+        #pragma omp for schedule(static)
+        for (i64 s = 0; s < B * D; ++s) {
+            i64 bi = s / D, di = s % D;
+            for (i64 n = 0; n < N; ++n) h[n] = h0 ? h0[s * N + n] : 0.0;
+            for (i64 t = 0; t < L; ++t) {
+                double acc = 0.0;
+                for (i64 n = 0; n < N; ++n) {
+                    double at, bt;
+                    real_terms(mode, D, L, N, bi, di, t, delta, x, A, Bm, a, b, n, &at, &bt);
+                    h[n] = at * h[n] + bt;
+                    acc += C[(bi * L + t) * N + n] * h[n];
+                }
+                y[s * L + t] = acc;
+            }
+            if (hlast) for (i64 n = 0; n < N; ++n) hlast[s * N + n] = h[n];
+        }
+        free(h);
+    }
+}
+
+/* Backward of the real scan.  Any output pointer may be NULL (not wanted).
+ * Selective: gdelta, gx (B,D,L); gA (D,N); gBm (B,L,N).
+ * Dense:     ga, gb (B,D,L,N).
+ * Both:      gC (B,L,N); gh0 (B,D,N).
+ * Cross-sequence sums (gA over b and t, gBm and gC over d) are accumulated in
+ * per-thread partial arrays and added in thread order. */
+void orc_real_bwd(int mode, i64 B, i64 D, i64 L, i64 N,
+                  const double* delta, const double* x, const double* A, const double* Bm,
+                  const double* a, const double* b, const double* C, const double* h0,
+                  const double* gy, const double* ghlast,
+                  double* gdelta, double* gx, double* gA, double* gBm,
+                  double* ga, double* gb, double* gC, double* gh0) {
+    int T = nthreads();
+    double* pB = (double*)calloc((size_t)T * L * N, sizeof(double));
+    double* pC = (double*)calloc((size_t)T * L * N, sizeof(double));
+    double* pA = (double*)calloc((size_t)T * D * N, sizeof(double));
+    for (i64 bi = 0; bi < B; ++bi) {
+        #pragma omp parallel
+        {
+            int tid = thread_id();
+            double* hist = (double*)malloc(sizeof(double) * (L + 1) * N); /* h_{-1..L-1} */
+            double* lam = (double*)malloc(sizeof(double) * N);
+            double* myB = pB + (size_t)tid * L * N;
+            double* myC = pC + (size_t)tid * L * N;
+            double* myA = pA + (size_t)tid * D * N;
+            #pragma omp for schedule(static)
+            for (i64 di = 0; di < D; ++di) {
+                i64 s = bi * D + di;
+                /* forward, keeping the whole state history */
+                for (i64 n = 0; n < N; ++n) hist[n] = h0 ? h0[s * N + n] : 0.0;
+                for (i64 t = 0; t < L; ++t)
+                    for (i64 n = 0; n < N; ++n) {
+                        double at, bt;
+                        real_terms(mode, D, L, N, bi, di, t, delta, x, A, Bm, a, b, n, &at, &bt);
+                        hist[(t + 1) * N + n] = at * hist[t * N + n] + bt;
+                    }
+                /* reverse (adjoint) sweep */
+                for (i64 n = 0; n < N; ++n) lam[n] = ghlast ? ghlast[s * N + n] : 0.0;
+                for (i64 t = L - 1; t >= 0; --t) {
+                    double g = gy[s * L + t];
+                    double dsum = 0.0, xsum = 0.0;
+                    for (i64 n = 0; n < N; ++n) {
+                        double at, bt;
+                        real_terms(mode, D, L, N, bi, di, t, delta, x, A, Bm, a, b, n, &at, &bt);
+                        double ht = hist[(t + 1) * N + n], hp = hist[t * N + n];
+                        lam[n] += C[(bi * L + t) * N + n] * g;
+                        myC[t * N + n] += g * ht;
+                        double gat = lam[n] * hp; /* dL/da_t */
+                        if (mode == 0) {
+                            double dl = delta[s * L + t], xv = x[s * L + t];
+                            double bm = Bm[(bi * L + t) * N + n];
+                            dsum += gat * at * A[di * N + n] + lam[n] * xv * bm;
+                            xsum += lam[n] * bm;
+                            myB[t * N + n] += lam[n] * dl * xv;
+                            myA[di * N + n] += gat * at * dl;
+                        } else {
+                            i64 o = (s * L + t) * N + n;
+                            if (ga) ga[o] = gat;
+                            if (gb) gb[o] = lam[n];
+                        }
+                        lam[n] *= at;
+                    }
+                    if (mode == 0) {
+                        if (gdelta) gdelta[s * L + t] = dsum;
+                        if (gx) gx[s * L + t] = delta[s * L + t] * xsum;
+                    }
+                }
+                if (gh0) for (i64 n = 0; n < N; ++n) gh0[s * N + n] = lam[n];
+            }
+            free(hist);
+            free(lam);
+        }
+        /* fixed-order sum of the per-thread partials for this batch row */
+        for (i64 o = 0; o < L * N; ++o) {
+            double sb = 0.0, sc = 0.0;
+            for (int k = 0; k < T; ++k) {
+                sb += pB[(size_t)k * L * N + o];
+                sc += pC[(size_t)k * L * N + o];
+                pB[(size_t)k * L * N + o] = 0.0;
+                pC[(size_t)k * L * N + o] = 0.0;
+            }
+            if (gBm && mode == 0) gBm[bi * L * N + o] = sb;
+            if (gC) gC[bi * L * N + o] = sc;
+        }
+    }
+    if (gA && mode == 0)
+        for (i64 o = 0; o < D * N; ++o) {
+            double sa = 0.0;
+            for (int k = 0; k < T; ++k) sa += pA[(size_t)k * D * N + o];
+            gA[o] = sa;
+        }
+    free(pB);
+    free(pC);
+    free(pA);
+}
+
+/* Sensitivity of one output to every input of the selective real scan
+ * (PGF page, abstract: impulse-response sensitivity):
+ *   s[b,d,t] = d y[b,d,t_out] / d x[b,d,t]
+ *            = delta_t * sum_n Bm[b,t,n] * mu_t[n],  t <= t_out,  0 after,
+ * with mu_{t_out} = C[b,t_out,:] and mu_{t-1} = a_t * mu_t (reverse costate). */
+void orc_impulse_sens(i64 B, i64 D, i64 L, i64 N, i64 t_out,
+                      const double* delta, const double* A, const double* Bm,
+                      const double* C, double* s_out) {
+    #pragma omp parallel
+    {
+        double* mu = (double*)malloc(sizeof(double) * N);
+        #pragma omp for schedule(static)
+        for (i64 s = 0; s < B * D; ++s) {
+            i64 bi = s / D, di = s % D;
+            for (i64 t = t_out + 1; t < L; ++t) s_out[s * L + t] = 0.0;
+            for (i64 n = 0; n < N; ++n) mu[n] = C[(bi * L + t_out) * N + n];
+            for (i64 t = t_out; t >= 0; --t) {
+                double dl = delta[s * L + t], acc = 0.0;
+                for (i64 n = 0; n < N; ++n) acc += Bm[(bi * L + t) * N + n] * mu[n];
+                s_out[s * L + t] = dl * acc;
+                for (i64 n = 0; n < N; ++n) mu[n] *= exp(dl * A[di * N + n]);
+            }
+        }
+        free(mu);
+    }
+}
+
+/* ------------------------------------------------------------------------- */
+/* Complex diagonal scan with shared controls.  Complex arrays are            */
+/* interleaved (re, im).  r, phi, y, gy (B,H,L); lam, theta (H,M);            */
+/* u (B,H,L,M); c (H,M); h0, hlast (B,H,M).                                   */
+/* ------------------------------------------------------------------------- */
+static void cplx_a(double r, double phi, double lam, double theta, double* are, double* aim) {
+    double mag = exp(r * log(lam));
+    double ang = phi * theta;
+    *are = mag * cos(ang);
+    *aim = mag * sin(ang);
+}
+
+void orc_complex_fwd(i64 B, i64 H, i64 L, i64 M,
+                     const double* r, const double* phi, const double* lam, const double* theta,
+                     const double* u, const double* c, const double* h0,
+                     double* y, double* hlast) {
+    #pragma omp parallel
+    {
+        double* h = (double*)malloc(sizeof(double) * 2 * M);
+        #pragma omp for schedule(static)
+        for (i64 s = 0; s < B * H; ++s) {
+            i64 hi = s % H;
+            for (i64 m = 0; m < 2 * M; ++m) h[m] = h0 ? h0[s * 2 * M + m] : 0.0;
+            for (i64 t = 0; t < L; ++t) {
+                double acc = 0.0;
+                for (i64 m = 0; m < M; ++m) {
+                    double are, aim;
+                    cplx_a(r[s * L + t], phi[s * L + t], lam[hi * M + m], theta[hi * M + m], &are, &aim);
+                    const double* ut = u + ((s * L + t) * M + m) * 2;
+                    double hre = are * h[2 * m] - aim * h[2 * m + 1] + ut[0];
+                    double him = are * h[2 * m + 1] + aim * h[2 * m] + ut[1];
+                    h[2 * m] = hre;
+                    h[2 * m + 1] = him;
+                    acc += c[(hi * M + m) * 2] * hre - c[(hi * M + m) * 2 + 1] * him;
+                }
+                y[s * L + t] = acc;
+            }
+            if (hlast) for (i64 m = 0; m < 2 * M; ++m) hlast[s * 2 * M + m] = h[m];
+        }
+        free(h);
+    }
+}
+
+/* Backward of the complex scan.  Outputs (any may be NULL):
+ * gu (B,H,L,M) complex; gr, gphi (B,H,L); glam, gtheta (H,M); gc (H,M) complex;
+ * gh0 (B,H,M) complex. */
+void orc_complex_bwd(i64 B, i64 H, i64 L, i64 M,
+                     const double* r, const double* phi, const double* lam, const double* theta,
+                     const double* u, const double* c, const double* h0,
+                     const double* gy, const double* ghlast,
+                     double* gu, double* gr, double* gphi, double* glam, double* gtheta,
+                     double* gc, double* gh0) {
+    int T = nthreads();
+    double* pl = (double*)calloc((size_t)T * H * M, sizeof(double));
+    double* pt = (double*)calloc((size_t)T * H * M, sizeof(double));
+    double* pc = (double*)calloc((size_t)T * H * M * 2, sizeof(double));
+    #pragma omp parallel
+    {
+        int tid = thread_id();
+        double* hist = (double*)malloc(sizeof(double) * (L + 1) * 2 * M);
+        double* mu = (double*)malloc(sizeof(double) * 2 * M);
+        double* myl = pl + (size_t)tid * H * M;
+        double* myt = pt + (size_t)tid * H * M;
+        double* myc = pc + (size_t)tid * H * M * 2;
+        #pragma omp for schedule(static)
+        for (i64 s = 0; s < B * H; ++s) {
+            i64 hi = s % H;
+            for (i64 m = 0; m < 2 * M; ++m) hist[m] = h0 ? h0[s * 2 * M + m] : 0.0;
+            for (i64 t = 0; t < L; ++t)
+                for (i64 m = 0; m < M; ++m) {
+                    double are, aim;
+                    cplx_a(r[s * L + t], phi[s * L + t], lam[hi * M + m], theta[hi * M + m], &are, &aim);
+                    const double* hp = hist + t * 2 * M + 2 * m;
+                    const double* ut = u + ((s * L + t) * M + m) * 2;
+                    hist[(t + 1) * 2 * M + 2 * m] = are * hp[0] - aim * hp[1] + ut[0];
+                    hist[(t + 1) * 2 * M + 2 * m + 1] = are * hp[1] + aim * hp[0] + ut[1];
+                }
+            for (i64 m = 0; m < 2 * M; ++m) mu[m] = ghlast ? ghlast[s * 2 * M + m] : 0.0;
+            for (i64 t = L - 1; t >= 0; --t) {
+                double g = gy[s * L + t], sr = 0.0, sp = 0.0;
+                for (i64 m = 0; m < M; ++m) {
+                    double cre = c[(hi * M + m) * 2], cim = c[(hi * M + m) * 2 + 1];
+                    /* mu += gy * conj(c) */
+                    mu[2 * m] += g * cre;
+                    mu[2 * m + 1] += -g * cim;
+                    const double* ht = hist + (t + 1) * 2 * M + 2 * m;
+                    const double* hp = hist + t * 2 * M + 2 * m;
+                    /* gc += gy * conj(h_t) */
+                    myc[(hi * M + m) * 2] += g * ht[0];
+                    myc[(hi * M + m) * 2 + 1] += -g * ht[1];
+                    if (gu) {
+                        gu[((s * L + t) * M + m) * 2] = mu[2 * m];
+                        gu[((s * L + t) * M + m) * 2 + 1] = mu[2 * m + 1];
+                    }
+                    /* g_a = mu * conj(h_{t-1}) */
+                    double gare = mu[2 * m] * hp[0] + mu[2 * m + 1] * hp[1];
+                    double gaim = mu[2 * m + 1] * hp[0] - mu[2 * m] * hp[1];
+                    double are, aim;
+                    cplx_a(r[s * L + t], phi[s * L + t], lam[hi * M + m], theta[hi * M + m], &are, &aim);
+                    /* g_z = conj(a) * g_a */
+                    double gzre = are * gare + aim * gaim;
+                    double gzim = are * gaim - aim * gare;
+                    double lnl = log(lam[hi * M + m]);
+                    sr += gzre * lnl;
+                    sp += gzim * theta[hi * M + m];
+                    myl[hi * M + m] += gzre * r[s * L + t];
+                    myt[hi * M + m] += gzim * phi[s * L + t];
+                    /* mu <- conj(a) * mu */
+                    double mre = are * mu[2 * m] + aim * mu[2 * m + 1];
+                    double mim = are * mu[2 * m + 1] - aim * mu[2 * m];
+                    mu[2 * m] = mre;
+                    mu[2 * m + 1] = mim;
+                }
+                if (gr) gr[s * L + t] = sr;
+                if (gphi) gphi[s * L + t] = sp;
+            }
+            if (gh0) for (i64 m = 0; m < 2 * M; ++m) gh0[s * 2 * M + m] = mu[m];
+        }
+        free(hist);
+        free(mu);
+    }
+    for (i64 o = 0; o < H * M; ++o) {
+        double sl = 0.0, st = 0.0, scr = 0.0, sci = 0.0;
+        for (int k = 0; k < T; ++k) {
+            sl += pl[(size_t)k * H * M + o];
+            st += pt[(size_t)k * H * M + o];
+            scr += pc[((size_t)k * H * M + o) * 2];
+            sci += pc[((size_t)k * H * M + o) * 2 + 1];
+        }
+        /* d/d lambda = (d/d ln lambda) / lambda */
+        if (glam) glam[o] = sl / lam[o];
+        if (gtheta) gtheta[o] = st;
+        if (gc) { gc[o * 2] = scr; gc[o * 2 + 1] = sci; }
+    }
+    free(pl);
+    free(pt);
+    free(pc);
+}
+
+/* ------------------------------------------------------------------------- */
+/* PD scan.  logits (B,H,L,K); sel (B,H,L) int32; dict (H,K,N) int32 (row of  */
+/* the one in each column); d, b, C (B,H,L,N); y, gy (B,H,L); h0 (B,H,N).     */
+/* ------------------------------------------------------------------------- */
+static int argmax_first(const double* v, i64 K) {
+    int best = 0;
+    for (i64 k = 1; k < K; ++k)
+        if (v[k] > v[best]) best = (int)k;
+    return best;
+}
+
+void orc_pd_select(i64 B, i64 H, i64 L, i64 K, const double* logits, int32_t* sel) {
+    #pragma omp parallel for schedule(static)
+    for (i64 o = 0; o < B * H * L; ++o) sel[o] = argmax_first(logits + o * K, K);
+}
+
+void orc_pd_fwd(i64 B, i64 H, i64 L, i64 N, i64 K, const int32_t* sel, const int32_t* dict,
+                const double* d, const double* b, const double* C, const double* h0,
+                double* y, double* hlast) {
+    #pragma omp parallel
+    {
+        double* h = (double*)malloc(sizeof(double) * N);
+        double* hn = (double*)malloc(sizeof(double) * N);
+        #pragma omp for schedule(static)
+        for (i64 s = 0; s < B * H; ++s) {
+            i64 hi = s % H;
+            for (i64 i = 0; i < N; ++i) h[i] = h0 ? h0[s * N + i] : 0.0;
+            for (i64 t = 0; t < L; ++t) {
+                const int32_t* pi = dict + ((i64)hi * K + sel[s * L + t]) * N;
+                const double* dt = d + (s * L + t) * N;
+                const double* bt = b + (s * L + t) * N;
+                for (i64 i = 0; i < N; ++i) hn[i] = bt[i];
+                for (i64 j = 0; j < N; ++j) hn[pi[j]] += dt[j] * h[j]; /* ascending j */
+                double acc = 0.0;
+                for (i64 i = 0; i < N; ++i) {
+                    h[i] = hn[i];
+                    acc += C[(s * L + t) * N + i] * h[i];
+                }
+                y[s * L + t] = acc;
+            }
+            if (hlast) for (i64 i = 0; i < N; ++i) hlast[s * N + i] = h[i];
+        }
+        free(h);
+        free(hn);
+    }
+}
+
+/* Second, independent PD route: the transition as a dense N x N matrix
+ * A_t[i][j] = d_t[j] if pi_t(j) == i else 0, applied by a dense mat-vec. */
+void orc_pd_dense_fwd(i64 B, i64 H, i64 L, i64 N, i64 K, const int32_t* sel, const int32_t* dict,
+                      const double* d, const double* b, const double* C, const double* h0,
+                      double* y, double* hlast) {
+    #pragma omp parallel
+    {
+        double* h = (double*)malloc(sizeof(double) * N);
+        double* hn = (double*)malloc(sizeof(double) * N);
+        double* At = (double*)malloc(sizeof(double) * N * N);
+        #pragma omp for schedule(static)
+        for (i64 s = 0; s < B * H; ++s) {
+            i64 hi = s % H;
+            for (i64 i = 0; i < N; ++i) h[i] = h0 ? h0[s * N + i] : 0.0;
+            for (i64 t = 0; t < L; ++t) {
+                const int32_t* pi = dict + ((i64)hi * K + sel[s * L + t]) * N;
+                for (i64 i = 0; i < N; ++i)
+                    for (i64 j = 0; j < N; ++j)
+                        At[i * N + j] = (pi[j] == i) ? d[(s * L + t) * N + j] : 0.0;
+                double acc = 0.0;
+                for (i64 i = 0; i < N; ++i) {
+                    double v = b[(s * L + t) * N + i];
+                    for (i64 j = 0; j < N; ++j) v += At[i * N + j] * h[j];
+                    hn[i] = v;
+                }
+                for (i64 i = 0; i < N; ++i) {
+                    h[i] = hn[i];
+                    acc += C[(s * L + t) * N + i] * h[i];
+                }
+                y[s * L + t] = acc;
+            }
+            if (hlast) for (i64 i = 0; i < N; ++i) hlast[s * N + i] = h[i];
+        }
+        free(h);
+        free(hn);
+        free(At);
+    }
+}
+
+/* Backward of the PD scan with the selection held fixed (the argmax has zero
+ * derivative almost everywhere; surrogate selection gradients are not part of
+ * this routine).  Outputs (any may be NULL): gd, gb, gC (B,H,L,N); gh0 (B,H,N). */
+void orc_pd_bwd(i64 B, i64 H, i64 L, i64 N, i64 K, const int32_t* sel, const int32_t* dict,
+                const double* d, const double* b, const double* C, const double* h0,
+                const double* gy, const double* ghlast,
+                double* gd, double* gb, double* gC, double* gh0) {
+    #pragma omp parallel
+    {
+        double* hist = (double*)malloc(sizeof(double) * (L + 1) * N);
+        double* lam = (double*)malloc(sizeof(double) * N);
+        double* ln = (double*)malloc(sizeof(double) * N);
+        #pragma omp for schedule(static)
+        for (i64 s = 0; s < B * H; ++s) {
+            i64 hi = s % H;
+            for (i64 i = 0; i < N; ++i) hist[i] = h0 ? h0[s * N + i] : 0.0;
+            for (i64 t = 0; t < L; ++t) {
+                const int32_t* pi = dict + ((i64)hi * K + sel[s * L + t]) * N;
+                double* hn = hist + (t + 1) * N;
+                const double* hp = hist + t * N;
+                for (i64 i = 0; i < N; ++i) hn[i] = b[(s * L + t) * N + i];
+                for (i64 j = 0; j < N; ++j) hn[pi[j]] += d[(s * L + t) * N + j] * hp[j];
+            }
+            for (i64 i = 0; i < N; ++i) lam[i] = ghlast ? ghlast[s * N + i] : 0.0;
+            for (i64 t = L - 1; t >= 0; --t) {
+                const int32_t* pi = dict + ((i64)hi * K + sel[s * L + t]) * N;
+                double g = gy[s * L + t];
+                for (i64 i = 0; i < N; ++i) {
+                    lam[i] += C[(s * L + t) * N + i] * g;
+                    if (gb) gb[(s * L + t) * N + i] = lam[i];
+                    if (gC) gC[(s * L + t) * N + i] = g * hist[(t + 1) * N + i];
+                }
+                /* lambda_{t-1}[j] (before adding its own readout) = d_t[j] lambda_t[pi_t(j)] */
+                for (i64 j = 0; j < N; ++j) {
+                    double lp = lam[pi[j]];
+                    if (gd) gd[(s * L + t) * N + j] = lp * hist[t * N + j];
+                    ln[j] = d[(s * L + t) * N + j] * lp;
+                }
+                for (i64 j = 0; j < N; ++j) lam[j] = ln[j];
+            }
+            if (gh0) for (i64 i = 0; i < N; ++i) gh0[s * N + i] = lam[i];
+        }
+        free(hist);
+        free(lam);
+        free(ln);
+    }
+}
