@@ -1,0 +1,246 @@
+/*
+ * ssmscan.h -- C ABI of the MI355X (gfx950) selective state-space scan library.
+ *
+ * The library computes the input-dependent linear recurrence
+ *
+ *     h_t = A_t h_{t-1} + b_t,      y_t = C_t . h_t,      t = 0 .. L-1,  h_{-1} = h0,
+ *
+ * over many independent sequences, forward and backward, for three kinds of
+ * transition A_t:
+ *
+ *   - diagonal real.  SSM_REAL_SELECTIVE forms a_t = exp(delta_t * A) and the
+ *     Euler input term b_t = delta_t * x_t * B_t from a step size delta, as in
+ *     the selection-and-discretisation step of the lpnh.cn page "Selective
+ *     State Space Models (S3M)", section 1.1.  SSM_REAL_DENSE takes a_t and
+ *     b_t as given tensors.
+ *   - diagonal complex with shared controls (SPARC page, abstract): two
+ *     per-step scalars, retention r_t and phase phi_t, drive every complex mode
+ *     m through a_{t,m} = exp(r_t ln(lambda_m) + i phi_t theta_m), with
+ *     b_t = u_t and the real readout y_t = Re sum_m c_m h_{t,m}.
+ *   - PD (Flash PD-SSM page, section "Neuer Selektionsmechanismus"): per step,
+ *     argmax over K scores picks one column-one-hot matrix P from a per-head
+ *     dictionary; A_t = P diag(d_t), i.e. h_t[i] = b_t[i] + sum over the
+ *     columns j whose one sits in row i of d_t[j] h_{t-1}[j].
+ *
+ * The scan runs as a chunked (tiled) three-phase computation -- local scans
+ * inside chunks, a prefix over chunk summaries, a carry correction -- as the
+ * Flash PD-SSM page describes under "Hardwarebewusste Implementierung".  The
+ * forward leaves the state entering every chunk of chunk_len steps (the
+ * checkpoints); the backward recomputes states tile by tile from them, so the
+ * on-chip working set is one chunk and nothing of size O(L * state) is stored
+ * (PGF page, abstract: exact analytical derivatives by tiled operator-space
+ * evolution instead of a materialised graph).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  Memory.   Every pointer is a device pointer the caller owns, except where
+ *            noted.  Tensors are dense, row-major, in the shapes stated, with
+ *            no padding (the last dimension is contiguous).  The library never
+ *            allocates device memory; scratch memory is the caller's workspace
+ *            `ws` of at least ssm_workspace_bytes() bytes (256-byte aligned),
+ *            used only during the call's stream work.  No pointer is kept
+ *            after return.
+ *  Streams.  All work is enqueued on `stream` (a hipStream_t; NULL is the
+ *            legacy default stream).  There is no host synchronisation and no
+ *            host<->device copy.  Buffers must stay valid until the stream
+ *            work completes.  Calls on different streams must use different
+ *            workspaces and outputs.
+ *  Outputs.  Outputs are overwritten, never accumulated.  A NULL output (or
+ *            gradient) is not computed.  Outputs must not overlap inputs or
+ *            each other.
+ *  Types.    Accumulation is float32 everywhere.  For SSM_REAL_SELECTIVE the
+ *            streamed tensors (delta, x, Bm, C, y, gy and their gradients)
+ *            share `dtype` (SSM_F32 or SSM_BF16, bf16 rounded to nearest even
+ *            on output); A, h0, h_last, checkpoints and gA are float32.  All
+ *            other modes are float32 (complex64 = interleaved float32 re, im).
+ *  Errors.   0 (SSM_OK) on success, a negative SSM_ERR_* code otherwise.  The
+ *            arguments are validated completely before anything is enqueued;
+ *            on error nothing is written.  ssm_last_error_detail() returns a
+ *            thread-local description of the last error.  Device faults are
+ *            asynchronous and surface at the caller's next synchronisation.
+ *  Results.  Mathematically independent of chunk_len; bitwise deterministic
+ *            run to run (no floating-point atomics).
+ */
+#ifndef SSMSCAN_H
+#define SSMSCAN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSM_ABI_VERSION 1
+
+/* status codes */
+#define SSM_OK               0
+#define SSM_ERR_NULL        -1  /* a required pointer is NULL */
+#define SSM_ERR_SHAPE       -2  /* a size is < 1 or inconsistent, K or N out of range */
+#define SSM_ERR_DTYPE       -3  /* unknown or unsupported element type for the mode */
+#define SSM_ERR_LAYOUT      -4  /* misaligned pointer, or an output overlapping another buffer */
+#define SSM_ERR_WORKSPACE   -5  /* workspace NULL or smaller than ssm_workspace_bytes() */
+#define SSM_ERR_UNSUPPORTED -6  /* valid request this build does not implement (e.g. chunk_len) */
+#define SSM_ERR_DEVICE      -7  /* HIP reported an error while enqueuing */
+
+/* element types of streamed tensors */
+#define SSM_F32  0
+#define SSM_BF16 1
+
+/* transition kinds of ssm_scan_* */
+#define SSM_REAL_SELECTIVE 0
+#define SSM_REAL_DENSE     1
+#define SSM_COMPLEX_SHARED 2
+
+/* operation ids for ssm_workspace_bytes */
+#define SSM_OP_SCAN_FWD 0
+#define SSM_OP_SCAN_BWD 1
+#define SSM_OP_IMPULSE  2
+#define SSM_OP_PD_FWD   3
+#define SSM_OP_PD_BWD   4
+
+/*
+ * Arguments of the diagonal scans.  Sizes: batch = B; channels = D (real) or
+ * H heads (complex); length = L; state = N (real, 1..16) or M complex modes
+ * per head (complex, 1..64).  chunk_len = checkpoint interval T in steps:
+ * 0 picks the default (256 selective, 64 dense and complex); the selective
+ * mode accepts 64, 128 or 256, the dense and complex modes 64.
+ * n_chunks = ceil(L / T).
+ */
+typedef struct {
+    int32_t mode;      /* SSM_REAL_SELECTIVE, SSM_REAL_DENSE or SSM_COMPLEX_SHARED */
+    int32_t dtype;     /* SSM_F32 or SSM_BF16 (bf16: SSM_REAL_SELECTIVE only) */
+    int64_t batch, channels, length, state, chunk_len;
+    /* SSM_REAL_SELECTIVE */
+    const void*  delta;  /* (B,D,L) dtype, step sizes                      */
+    const void*  x;      /* (B,D,L) dtype, inputs                          */
+    const float* A;      /* (D,N)  f32, continuous-time diagonal (A < 0)   */
+    const void*  Bm;     /* (B,L,N) dtype, input projection B_t (shared over D) */
+    /* SSM_REAL_DENSE */
+    const float* a;      /* (B,D,L,N) f32, transition diagonal a_t         */
+    const float* b;      /* (B,D,L,N) f32, input term b_t                   */
+    /* both real modes */
+    const void*  C;      /* (B,L,N) dtype (f32 for dense), readout C_t (shared over D) */
+    /* SSM_COMPLEX_SHARED */
+    const float* r;      /* (B,H,L) retention control r_t                  */
+    const float* phi;    /* (B,H,L) phase control phi_t                    */
+    const float* lam;    /* (H,M) baseline rate, 0 < lambda <= 1           */
+    const float* theta;  /* (H,M) baseline frequency                       */
+    const float* u;      /* (B,H,L,M) complex64 input b_t = u_t            */
+    const float* c;      /* (H,M) complex64 readout                        */
+    /* all modes */
+    const float* h0;     /* nullable initial state (B,D,N) f32 / (B,H,M) complex64; NULL = 0 */
+} ssm_scan_args;
+
+typedef struct {
+    void*  y;        /* nullable (B,D,L) dtype; complex: (B,H,L) f32                       */
+    float* h_last;   /* nullable h_{L-1}: (B,D,N) f32 / (B,H,M) complex64                  */
+    float* ckpt;     /* nullable (B,D,n_chunks,N) f32 / (B,H,n_chunks,M) complex64:
+                        ckpt[.., c, :] = state entering chunk c (h_{cT-1}; c = 0 holds h0) */
+} ssm_scan_fwd_out;
+
+typedef struct {
+    const void*  gy;       /* (B,D,L) dtype / (B,H,L) f32: dLoss/dy                       */
+    const float* gh_last;  /* nullable dLoss/dh_{L-1}, same layout as h_last; NULL = 0    */
+    const float* ckpt;     /* nullable checkpoints from ssm_scan_fwd with the same args;
+                              NULL = recomputed into the workspace                         */
+} ssm_scan_bwd_in;
+
+/* Gradients of Loss = sum_t <gy_t, y_t> + <gh_last, h_{L-1}>; every pointer
+ * nullable.  Complex gradients use the real-pair convention
+ * g = dLoss/dRe + i dLoss/dIm (interleaved). */
+typedef struct {
+    void*  gdelta;  /* selective (B,D,L) dtype                  */
+    void*  gx;      /* selective (B,D,L) dtype                  */
+    float* gA;      /* selective (D,N) f32 (sum over b and t)   */
+    void*  gBm;     /* selective (B,L,N) dtype (sum over d)     */
+    float* ga;      /* dense (B,D,L,N) f32                      */
+    float* gb;      /* dense (B,D,L,N) f32                      */
+    void*  gC;      /* real (B,L,N) dtype (sum over d)          */
+    float* gu;      /* complex (B,H,L,M) complex64              */
+    float* gr;      /* complex (B,H,L) f32                      */
+    float* gphi;    /* complex (B,H,L) f32                      */
+    float* glam;    /* complex (H,M) f32 (sum over b and t)     */
+    float* gtheta;  /* complex (H,M) f32 (sum over b and t)     */
+    float* gc;      /* complex (H,M) complex64                  */
+    float* gh0;     /* (B,D,N) f32 / (B,H,M) complex64          */
+} ssm_scan_grads;
+
+/* Arguments of the PD scan.  N = state (1..16), K = dictionary size (1..64).
+ * chunk_len: 0 = default 64; only 64 is accepted. */
+typedef struct {
+    int64_t batch, heads, length, state, dict_size, chunk_len;
+    const float*   logits; /* (B,H,L,K) f32 selection scores; may be NULL if sel is given */
+    const int32_t* sel;    /* (B,H,L) selected entries; input alternative to logits (used
+                              when logits is NULL); values must lie in [0,K)               */
+    const int32_t* dict;   /* (H,K,N): dict[h,k,j] = row of the one in column j of entry k,
+                              values in [0,N)                                              */
+    const float* d;        /* (B,H,L,N) diagonal d_t                                        */
+    const float* b;        /* (B,H,L,N) input term b_t                                      */
+    const float* C;        /* (B,H,L,N) readout C_t                                         */
+    const float* h0;       /* nullable (B,H,N)                                              */
+} pd_scan_args;
+
+typedef struct {
+    float*   y;       /* nullable (B,H,L)                                               */
+    int32_t* sel;     /* nullable (B,H,L): argmax_k logits (lowest index among ties)    */
+    float*   h_last;  /* nullable (B,H,N)                                               */
+    float*   ckpt;    /* nullable (B,H,n_chunks,N): state entering each chunk           */
+} pd_scan_fwd_out;
+
+typedef struct {
+    const float* gy;       /* (B,H,L)                                                   */
+    const float* gh_last;  /* nullable (B,H,N)                                          */
+    const float* ckpt;     /* nullable checkpoints from pd_scan_fwd; NULL = recomputed  */
+} pd_scan_bwd_in;
+
+/* Gradients with the selection held fixed (argmax is piecewise constant). */
+typedef struct {
+    float* gd;   /* (B,H,L,N) */
+    float* gb;   /* (B,H,L,N) */
+    float* gC;   /* (B,H,L,N) */
+    float* gh0;  /* (B,H,N)   */
+} pd_scan_grads;
+
+/* Workspace size in bytes for operation `op` (SSM_OP_*) with `args`
+ * (ssm_scan_args* for the ssm_* ops, pd_scan_args* for the pd_* ops).
+ * Host-only; enqueues nothing.  Errors as for the operation itself. */
+int ssm_workspace_bytes(int op, const void* args, size_t* out_bytes);
+
+/* Forward scan: y, h_last and checkpoints (each nullable). */
+int ssm_scan_fwd(const ssm_scan_args* args, const ssm_scan_fwd_out* out,
+                 void* ws, size_t ws_bytes, void* stream);
+
+/* Exact backward of ssm_scan_fwd by tiled recompute from the checkpoints and a
+ * reverse adjoint scan lambda_t = C_t gy_t + A_{t+1}^T lambda_{t+1}. */
+int ssm_scan_bwd(const ssm_scan_args* args, const ssm_scan_bwd_in* in,
+                 const ssm_scan_grads* grads, void* ws, size_t ws_bytes, void* stream);
+
+/* Impulse-response sensitivity of a selective real scan (PGF page, abstract:
+ * sensitivity analysis on a 128,000-step impulse-response benchmark):
+ *   s[b,d,t] = d y[b,d,t_out] / d x[b,d,t]
+ *            = delta_t sum_n Bm[b,t,n] C[b,t_out,n] exp(A[d,n] sum_{s=t+1..t_out} delta_s)
+ * for t <= t_out and 0 for t > t_out, by reverse costate evolution in tiles
+ * (workspace O(n_chunks), no checkpoints).  t_out in [0,L); -1 means L-1.
+ * y (nullable, (B,D,L) dtype) additionally receives the forward output.
+ * s is (B,D,L) dtype.  SSM_REAL_SELECTIVE only. */
+int ssm_impulse_sensitivity(const ssm_scan_args* args, int64_t t_out, void* y, void* s,
+                            void* ws, size_t ws_bytes, void* stream);
+
+/* PD forward: selection (argmax of logits unless sel is given), scan, readout. */
+int pd_scan_fwd(const pd_scan_args* args, const pd_scan_fwd_out* out,
+                void* ws, size_t ws_bytes, void* stream);
+
+/* PD backward with the selection from args->sel (or recomputed from logits). */
+int pd_scan_bwd(const pd_scan_args* args, const pd_scan_bwd_in* in,
+                const pd_scan_grads* grads, void* ws, size_t ws_bytes, void* stream);
+
+const char* ssm_status_string(int status);   /* static string for a status code */
+const char* ssm_last_error_detail(void);     /* thread-local detail of the last error */
+int ssm_abi_version(void);                   /* SSM_ABI_VERSION of the built library */
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSMSCAN_H */

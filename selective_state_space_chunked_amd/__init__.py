@@ -1,0 +1,21 @@
+"""MI355X (gfx950) selective state-space scan: forward, backward, impulse
+sensitivity and PD-transition scans behind the C ABI of include/ssmscan.h.
+
+The Python functions marshal torch tensors into the C ABI of libssmscan.so;
+all computation runs in the library's HIP kernels.
+"""
+from .binding import (  # noqa: F401
+    SSM_BF16,
+    SSM_COMPLEX_SHARED,
+    SSM_F32,
+    SSM_REAL_DENSE,
+    SSM_REAL_SELECTIVE,
+    SSMError,
+    impulse_sensitivity,
+    lib,
+    n_chunks,
+    pd_scan_bwd,
+    pd_scan_fwd,
+    scan_bwd,
+    scan_fwd,
+)

@@ -1,0 +1,548 @@
+// Host side of the C ABI declared in include/ssmscan.h: argument validation
+// (host-only, nothing touches the device before it passes), planning (chunk
+// geometry, number of segments that run in parallel along the sequence),
+// workspace layout and kernel launches on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/ssmscan.h"
+#include "kernels.hpp"
+
+using namespace ssm;
+
+namespace {
+
+thread_local std::string g_detail;
+
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_detail = buf;
+    return code;
+}
+int ok() {
+    g_detail.clear();
+    return SSM_OK;
+}
+
+// Parallelism target: enough 256-lane workgroups to give every SIMD of the
+// 256 compute units several waves.
+constexpr int64_t kTargetWG = 1024;
+constexpr size_t kAlign = 256;
+
+struct Range {
+    const void* p;
+    size_t bytes;
+    const char* name;
+};
+
+bool overlaps(const Range& a, const Range& b) {
+    if (!a.p || !b.p || a.bytes == 0 || b.bytes == 0) return false;
+    auto a0 = (uintptr_t)a.p, b0 = (uintptr_t)b.p;
+    return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+// every output against every other buffer
+int check_overlaps(const std::vector<Range>& ins, const std::vector<Range>& outs) {
+    for (size_t i = 0; i < outs.size(); ++i) {
+        for (const auto& r : ins)
+            if (overlaps(outs[i], r)) return fail(SSM_ERR_LAYOUT, "output %s overlaps input %s", outs[i].name, r.name);
+        for (size_t j = i + 1; j < outs.size(); ++j)
+            if (overlaps(outs[i], outs[j]))
+                return fail(SSM_ERR_LAYOUT, "output %s overlaps output %s", outs[i].name, outs[j].name);
+    }
+    return SSM_OK;
+}
+int check_align(const void* p, size_t a, const char* name) {
+    if (p && ((uintptr_t)p % a) != 0) return fail(SSM_ERR_LAYOUT, "%s is not %zu-byte aligned", name, a);
+    return SSM_OK;
+}
+bool aligned16(const void* p) { return p == nullptr || ((uintptr_t)p % 16) == 0; }
+
+// bump allocator over the caller's workspace (or a size-only dry run)
+struct Carve {
+    char* base;
+    size_t off = 0;
+    explicit Carve(void* b) : base((char*)b) {}
+    template <typename T>
+    T* take(size_t count) {
+        off = (off + kAlign - 1) / kAlign * kAlign;
+        T* p = base ? (T*)(base + off) : nullptr;
+        off += count * sizeof(T);
+        return p;
+    }
+};
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int device_status(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(SSM_ERR_DEVICE, "%s: %s", what, hipGetErrorName(e));
+    return SSM_OK;
+}
+#define SSM_LAUNCH(expr, what)                            \
+    do {                                                  \
+        int rc_ = device_status((expr), what);            \
+        if (rc_ != SSM_OK) return rc_;                    \
+    } while (0)
+
+// segment count along the sequence so the grid reaches the parallelism target
+void plan_segments(int64_t wg_per_seg, int64_t nunits, int* G, int* per_seg) {
+    int64_t g = std::max<int64_t>(1, cdiv(kTargetWG, std::max<int64_t>(1, wg_per_seg)));
+    g = std::min<int64_t>(g, nunits);
+    int64_t ps = cdiv(nunits, g);
+    *per_seg = (int)ps;
+    *G = (int)cdiv(nunits, ps);
+}
+
+// ---------------------------------------------------------------------------
+// diagonal real / complex scans: shared validation
+// ---------------------------------------------------------------------------
+struct ScanPlan {
+    int mode, dtype;
+    int64_t B, D, L, N;
+    int T;         // checkpoint interval
+    int kpl;       // selective: steps per lane (T/16)
+    int nchunks;   // ceil(L/T)
+    size_t esz;    // bytes per streamed element
+};
+
+int validate_scan_args(const ssm_scan_args* a, ScanPlan* pl) {
+    if (!a) return fail(SSM_ERR_NULL, "args is NULL");
+    pl->mode = a->mode;
+    pl->dtype = a->dtype;
+    pl->B = a->batch; pl->D = a->channels; pl->L = a->length; pl->N = a->state;
+    if (a->mode != SSM_REAL_SELECTIVE && a->mode != SSM_REAL_DENSE && a->mode != SSM_COMPLEX_SHARED)
+        return fail(SSM_ERR_UNSUPPORTED, "unknown mode %d", a->mode);
+    if (a->dtype != SSM_F32 && a->dtype != SSM_BF16) return fail(SSM_ERR_DTYPE, "unknown dtype %d", a->dtype);
+    if (a->dtype == SSM_BF16 && a->mode != SSM_REAL_SELECTIVE)
+        return fail(SSM_ERR_DTYPE, "bf16 streams are supported by SSM_REAL_SELECTIVE only");
+    if (pl->B < 1 || pl->D < 1 || pl->L < 1 || pl->N < 1)
+        return fail(SSM_ERR_SHAPE, "sizes must be >= 1 (B=%lld D=%lld L=%lld N=%lld)", (long long)pl->B,
+                    (long long)pl->D, (long long)pl->L, (long long)pl->N);
+    const int64_t nmax = a->mode == SSM_COMPLEX_SHARED ? 64 : 16;
+    if (pl->N > nmax) return fail(SSM_ERR_SHAPE, "state size %lld exceeds %lld", (long long)pl->N, (long long)nmax);
+    if (pl->B > 65535) return fail(SSM_ERR_SHAPE, "batch %lld exceeds 65535", (long long)pl->B);
+    if (pl->L >= (1LL << 31) || pl->D >= (1LL << 24) || pl->B * pl->D * pl->L * pl->N >= (1LL << 46))
+        return fail(SSM_ERR_SHAPE, "problem too large");
+    pl->esz = a->dtype == SSM_BF16 ? 2 : 4;
+    int T = (int)a->chunk_len;
+    if (a->mode == SSM_REAL_SELECTIVE) {
+        if (T == 0) T = 256;
+        if (T != 64 && T != 128 && T != 256)
+            return fail(SSM_ERR_UNSUPPORTED, "chunk_len %d not supported (64, 128 or 256)", T);
+        pl->kpl = T / 16;
+    } else {
+        if (T == 0) T = 64;
+        if (T != 64) return fail(SSM_ERR_UNSUPPORTED, "chunk_len %d not supported (64)", T);
+        pl->kpl = 0;
+    }
+    if (a->chunk_len < 0) return fail(SSM_ERR_SHAPE, "negative chunk_len");
+    pl->T = T;
+    pl->nchunks = (int)cdiv(pl->L, T);
+    const size_t BDL = pl->B * pl->D * pl->L;
+    const size_t BLN = pl->B * pl->L * pl->N;
+    if (a->mode == SSM_REAL_SELECTIVE) {
+        if (!a->delta || !a->x || !a->A || !a->Bm || !a->C)
+            return fail(SSM_ERR_NULL, "SSM_REAL_SELECTIVE needs delta, x, A, Bm and C");
+        const size_t al = pl->esz;
+        int rc;
+        if ((rc = check_align(a->delta, al, "delta")) || (rc = check_align(a->x, al, "x")) ||
+            (rc = check_align(a->Bm, al, "Bm")) || (rc = check_align(a->C, al, "C")) ||
+            (rc = check_align(a->A, 4, "A")) || (rc = check_align(a->h0, 4, "h0")))
+            return rc;
+        (void)BDL; (void)BLN;
+    } else if (a->mode == SSM_REAL_DENSE) {
+        if (!a->a || !a->b || !a->C) return fail(SSM_ERR_NULL, "SSM_REAL_DENSE needs a, b and C");
+        int rc;
+        if ((rc = check_align(a->a, 4, "a")) || (rc = check_align(a->b, 4, "b")) ||
+            (rc = check_align(a->C, 4, "C")) || (rc = check_align(a->h0, 4, "h0")))
+            return rc;
+    } else {
+        if (!a->r || !a->phi || !a->lam || !a->theta || !a->u || !a->c)
+            return fail(SSM_ERR_NULL, "SSM_COMPLEX_SHARED needs r, phi, lam, theta, u and c");
+        int rc;
+        if ((rc = check_align(a->u, 8, "u")) || (rc = check_align(a->c, 8, "c")) ||
+            (rc = check_align(a->r, 4, "r")) || (rc = check_align(a->phi, 4, "phi")) ||
+            (rc = check_align(a->h0, 8, "h0")))
+            return rc;
+    }
+    return SSM_OK;
+}
+
+std::vector<Range> scan_inputs(const ssm_scan_args* a, const ScanPlan& p) {
+    const size_t BDL = p.B * p.D * p.L, BLN = p.B * p.L * p.N, BDLN = BDL * p.N;
+    const size_t st = p.N * (p.mode == SSM_COMPLEX_SHARED ? 8 : 4);
+    return {
+        {a->delta, BDL * p.esz, "delta"}, {a->x, BDL * p.esz, "x"},
+        {a->A, (size_t)p.D * p.N * 4, "A"}, {a->Bm, BLN * p.esz, "Bm"},
+        {a->a, BDLN * 4, "a"}, {a->b, BDLN * 4, "b"},
+        {a->C, BLN * (p.mode == SSM_REAL_SELECTIVE ? p.esz : 4), "C"},
+        {a->r, BDL * 4, "r"}, {a->phi, BDL * 4, "phi"},
+        {a->lam, (size_t)p.D * p.N * 4, "lam"}, {a->theta, (size_t)p.D * p.N * 4, "theta"},
+        {a->u, BDLN * 8, "u"}, {a->c, (size_t)p.D * p.N * 8, "c"},
+        {a->h0, (size_t)p.B * p.D * st, "h0"},
+    };
+}
+
+// ---------------------------------------------------------------------------
+// selective: forward plan + workspace
+// ---------------------------------------------------------------------------
+struct SelFwdLayout {
+    int G, tps;
+    float *segP = nullptr, *segS = nullptr, *carry = nullptr;
+};
+void sel_fwd_layout(const ScanPlan& p, Carve& cv, SelFwdLayout* lay) {
+    const int64_t wg = cdiv(p.D, 16) * p.B;
+    plan_segments(wg, p.nchunks, &lay->G, &lay->tps);
+    if (lay->G > 1) {
+        const size_t n = (size_t)p.B * p.D * lay->G * p.N;
+        lay->segP = cv.take<float>(n);
+        lay->segS = cv.take<float>(n);
+        lay->carry = cv.take<float>(n);
+    }
+}
+
+int sel_vec(const ScanPlan& p, std::initializer_list<const void*> ptrs) {
+    if (p.L % 8 != 0) return 0;
+    for (const void* q : ptrs)
+        if (!aligned16(q)) return 0;
+    return 1;
+}
+
+int run_sel_fwd(const ssm_scan_args* a, const ScanPlan& p, const SelFwdLayout& lay, void* y, float* h_last,
+                float* ckpt, float* tile_dsum, hipStream_t st) {
+    SelFwdParams q{};
+    q.delta = a->delta; q.x = a->x; q.A = a->A; q.Bm = a->Bm; q.C = a->C; q.h0 = a->h0;
+    q.carry_in = lay.carry;
+    q.y = y; q.h_last = h_last; q.ckpt = ckpt; q.tile_dsum = tile_dsum;
+    q.segP = lay.segP; q.segS = lay.segS;
+    q.B = (int)p.B; q.D = (int)p.D; q.L = (int)p.L; q.N = (int)p.N;
+    q.ntiles = p.nchunks; q.tiles_per_seg = lay.tps; q.G = lay.G;
+    q.vec = sel_vec(p, {a->delta, a->x, y});
+    if (lay.G > 1) {
+        SSM_LAUNCH(launch_sel_fwd(q, p.dtype, p.kpl, true, st), "selective forward summary");
+        SSM_LAUNCH(launch_seg_combine_fwd(lay.segP, lay.segS, a->h0, lay.carry, (int)(p.B * p.D), lay.G,
+                                          (int)p.N, st), "segment combine");
+    }
+    SSM_LAUNCH(launch_sel_fwd(q, p.dtype, p.kpl, false, st), "selective forward");
+    return SSM_OK;
+}
+
+// ---------------------------------------------------------------------------
+// selective: backward plan + workspace
+// ---------------------------------------------------------------------------
+struct SelBwdLayout {
+    SelFwdLayout fwd;          // only when checkpoints are recomputed
+    float* ckpt = nullptr;
+    int G, tps;
+    float *segQ = nullptr, *segR = nullptr, *nu = nullptr;
+    float *partB = nullptr, *partC = nullptr, *partA = nullptr;
+};
+void sel_bwd_layout(const ScanPlan& p, bool have_ckpt, bool wantB, bool wantC, bool wantA, Carve& cv,
+                    SelBwdLayout* lay) {
+    if (!have_ckpt) {
+        lay->ckpt = cv.take<float>((size_t)p.B * p.D * p.nchunks * p.N);
+        sel_fwd_layout(p, cv, &lay->fwd);
+    }
+    const int64_t wg = cdiv(p.D, 16) * p.B;
+    plan_segments(wg, p.nchunks, &lay->G, &lay->tps);
+    if (lay->G > 1) {
+        const size_t n = (size_t)p.B * p.D * lay->G * p.N;
+        lay->segQ = cv.take<float>(n);
+        lay->segR = cv.take<float>(n);
+        lay->nu = cv.take<float>(n);
+    }
+    const size_t np = (size_t)cdiv(p.D, 16) * p.B * p.N * p.L;
+    if (wantB) lay->partB = cv.take<float>(np);
+    if (wantC) lay->partC = cv.take<float>(np);
+    if (wantA) lay->partA = cv.take<float>((size_t)p.B * lay->G * p.D * p.N);
+}
+
+// ---------------------------------------------------------------------------
+// entry-point helpers per mode (dense, complex and PD live further below)
+// ---------------------------------------------------------------------------
+int scan_fwd_impl(const ssm_scan_args* a, const ssm_scan_fwd_out* out, void* ws, size_t ws_bytes,
+                  hipStream_t st, size_t* need_only);
+int scan_bwd_impl(const ssm_scan_args* a, const ssm_scan_bwd_in* in, const ssm_scan_grads* g, void* ws,
+                  size_t ws_bytes, hipStream_t st, size_t* need_only);
+int impulse_impl(const ssm_scan_args* a, int64_t t_out, void* y, void* s, void* ws, size_t ws_bytes,
+                 hipStream_t st, size_t* need_only);
+int pd_fwd_impl(const pd_scan_args* a, const pd_scan_fwd_out* out, void* ws, size_t ws_bytes, hipStream_t st,
+                size_t* need_only);
+int pd_bwd_impl(const pd_scan_args* a, const pd_scan_bwd_in* in, const pd_scan_grads* g, void* ws,
+                size_t ws_bytes, hipStream_t st, size_t* need_only);
+
+int check_ws(void* ws, size_t ws_bytes, size_t need) {
+    if (need == 0) return SSM_OK;
+    if (!ws) return fail(SSM_ERR_WORKSPACE, "workspace of %zu bytes required, got NULL", need);
+    if (ws_bytes < need) return fail(SSM_ERR_WORKSPACE, "workspace of %zu bytes required, got %zu", need, ws_bytes);
+    if (((uintptr_t)ws % kAlign) != 0) return fail(SSM_ERR_LAYOUT, "workspace is not %zu-byte aligned", kAlign);
+    return SSM_OK;
+}
+
+// ======================= dense + complex declarations ======================
+int dense_fwd(const ssm_scan_args* a, const ScanPlan& p, const ssm_scan_fwd_out* out, Carve& cv, bool dry,
+              hipStream_t st);
+int dense_bwd(const ssm_scan_args* a, const ScanPlan& p, const ssm_scan_bwd_in* in, const ssm_scan_grads* g,
+              Carve& cv, bool dry, hipStream_t st);
+int cplx_fwd(const ssm_scan_args* a, const ScanPlan& p, const ssm_scan_fwd_out* out, Carve& cv, bool dry,
+             hipStream_t st);
+int cplx_bwd(const ssm_scan_args* a, const ScanPlan& p, const ssm_scan_bwd_in* in, const ssm_scan_grads* g,
+             Carve& cv, bool dry, hipStream_t st);
+
+// ---------------------------------------------------------------------------
+// ssm_scan_fwd
+// ---------------------------------------------------------------------------
+int scan_fwd_impl(const ssm_scan_args* a, const ssm_scan_fwd_out* out, void* ws, size_t ws_bytes,
+                  hipStream_t st, size_t* need_only) {
+    ScanPlan p;
+    int rc = validate_scan_args(a, &p);
+    if (rc) return rc;
+    if (!need_only) {
+        if (!out) return fail(SSM_ERR_NULL, "out is NULL");
+        const size_t st_b = p.mode == SSM_COMPLEX_SHARED ? 8 : 4;
+        const size_t yb = p.B * p.D * p.L * (p.mode == SSM_REAL_SELECTIVE ? p.esz : 4);
+        const size_t hb = p.B * p.D * p.N * st_b;
+        std::vector<Range> outs = {{out->y, yb, "y"}, {out->h_last, hb, "h_last"},
+                                   {out->ckpt, hb * p.nchunks, "ckpt"}};
+        if ((rc = check_align(out->y, p.mode == SSM_REAL_SELECTIVE ? p.esz : 4, "y")) ||
+            (rc = check_align(out->h_last, st_b, "h_last")) || (rc = check_align(out->ckpt, st_b, "ckpt")))
+            return rc;
+        if ((rc = check_overlaps(scan_inputs(a, p), outs))) return rc;
+    }
+    Carve cv(need_only ? nullptr : ws);
+    if (p.mode == SSM_REAL_SELECTIVE) {
+        SelFwdLayout lay;
+        sel_fwd_layout(p, cv, &lay);
+        if (need_only) { *need_only = cv.off; return ok(); }
+        if ((rc = check_ws(ws, ws_bytes, cv.off))) return rc;
+        Carve real(ws);
+        sel_fwd_layout(p, real, &lay);
+        if ((rc = run_sel_fwd(a, p, lay, out->y, out->h_last, out->ckpt, nullptr, st))) return rc;
+        return ok();
+    }
+    if (p.mode == SSM_REAL_DENSE) {
+        if ((rc = dense_fwd(a, p, out, cv, true, st))) return rc;
+        if (need_only) { *need_only = cv.off; return ok(); }
+        if ((rc = check_ws(ws, ws_bytes, cv.off))) return rc;
+        Carve real(ws);
+        if ((rc = dense_fwd(a, p, out, real, false, st))) return rc;
+        return ok();
+    }
+    if ((rc = cplx_fwd(a, p, out, cv, true, st))) return rc;
+    if (need_only) { *need_only = cv.off; return ok(); }
+    if ((rc = check_ws(ws, ws_bytes, cv.off))) return rc;
+    Carve real(ws);
+    if ((rc = cplx_fwd(a, p, out, real, false, st))) return rc;
+    return ok();
+}
+
+// ---------------------------------------------------------------------------
+// ssm_scan_bwd
+// ---------------------------------------------------------------------------
+int scan_bwd_impl(const ssm_scan_args* a, const ssm_scan_bwd_in* in, const ssm_scan_grads* g, void* ws,
+                  size_t ws_bytes, hipStream_t st, size_t* need_only) {
+    ScanPlan p;
+    int rc = validate_scan_args(a, &p);
+    if (rc) return rc;
+    static const ssm_scan_grads kNoGrads{};
+    static const ssm_scan_bwd_in kNoIn{};
+    if (!need_only) {
+        if (!in) return fail(SSM_ERR_NULL, "in is NULL");
+        if (!g) return fail(SSM_ERR_NULL, "grads is NULL");
+        if (!in->gy) return fail(SSM_ERR_NULL, "gy is NULL");
+    }
+    if (!in) in = &kNoIn;
+    if (!g) g = &kNoGrads;
+    const bool have_ckpt = need_only ? false : in->ckpt != nullptr;
+    if (!need_only) {
+        const size_t st_b = p.mode == SSM_COMPLEX_SHARED ? 8 : 4;
+        const size_t es = p.mode == SSM_REAL_SELECTIVE ? p.esz : 4;
+        const size_t BDL = p.B * p.D * p.L, BLN = p.B * p.L * p.N;
+        const size_t hb = p.B * p.D * p.N * st_b;
+        std::vector<Range> ins = scan_inputs(a, p);
+        ins.push_back({in->gy, BDL * es, "gy"});
+        ins.push_back({in->gh_last, hb, "gh_last"});
+        ins.push_back({in->ckpt, hb * p.nchunks, "ckpt"});
+        std::vector<Range> outs = {
+            {g->gdelta, BDL * es, "gdelta"}, {g->gx, BDL * es, "gx"}, {g->gA, (size_t)p.D * p.N * 4, "gA"},
+            {g->gBm, BLN * es, "gBm"}, {g->ga, BDL * p.N * 4, "ga"}, {g->gb, BDL * p.N * 4, "gb"},
+            {g->gC, BLN * es, "gC"}, {g->gu, BDL * p.N * 8, "gu"}, {g->gr, BDL * 4, "gr"},
+            {g->gphi, BDL * 4, "gphi"}, {g->glam, (size_t)p.D * p.N * 4, "glam"},
+            {g->gtheta, (size_t)p.D * p.N * 4, "gtheta"}, {g->gc, (size_t)p.D * p.N * 8, "gc"},
+            {g->gh0, hb, "gh0"}};
+        for (const auto& o : outs)
+            if ((rc = check_align(o.p, 2, o.name))) return rc;
+        if ((rc = check_overlaps(ins, outs))) return rc;
+    }
+    Carve cv(need_only ? nullptr : ws);
+    if (p.mode == SSM_REAL_SELECTIVE) {
+        // workspace is sized for the worst case (checkpoints recomputed, every gradient wanted)
+        SelBwdLayout lay;
+        sel_bwd_layout(p, false, true, true, true, cv, &lay);
+        if (need_only) { *need_only = cv.off; return ok(); }
+        if ((rc = check_ws(ws, ws_bytes, cv.off))) return rc;
+        Carve real(ws);
+        sel_bwd_layout(p, have_ckpt, g->gBm != nullptr, g->gC != nullptr, g->gA != nullptr, real, &lay);
+        const float* ckpt = in->ckpt;
+        if (!have_ckpt) {
+            if ((rc = run_sel_fwd(a, p, lay.fwd, nullptr, nullptr, lay.ckpt, nullptr, st))) return rc;
+            ckpt = lay.ckpt;
+        }
+        SelBwdParams q{};
+        q.delta = a->delta; q.x = a->x; q.A = a->A; q.Bm = a->Bm; q.C = a->C;
+        q.gy = in->gy; q.gh_last = in->gh_last; q.ckpt = ckpt; q.nu_in = lay.nu;
+        q.gdelta = g->gdelta; q.gx = g->gx; q.gh0 = g->gh0;
+        q.partB = lay.partB; q.partC = lay.partC; q.partA = lay.partA;
+        q.segQ = lay.segQ; q.segR = lay.segR;
+        q.B = (int)p.B; q.D = (int)p.D; q.L = (int)p.L; q.N = (int)p.N;
+        q.ntiles = p.nchunks; q.tiles_per_seg = lay.tps; q.G = lay.G;
+        q.vec = sel_vec(p, {a->delta, a->x, in->gy, g->gdelta, g->gx});
+        if (lay.G > 1) {
+            SSM_LAUNCH(launch_sel_bwd(q, p.dtype, p.kpl, true, st), "selective backward summary");
+            SSM_LAUNCH(launch_seg_combine_rev(lay.segQ, lay.segR, in->gh_last, lay.nu, (int)(p.B * p.D), lay.G,
+                                              (int)p.N, st), "segment combine (reverse)");
+        }
+        SSM_LAUNCH(launch_sel_bwd(q, p.dtype, p.kpl, false, st), "selective backward");
+        const int nblk = (int)cdiv(p.D, 16);
+        if (g->gBm)
+            SSM_LAUNCH(launch_reduce_parts_btn(lay.partB, nblk, (int)p.B, (int)p.N, (int)p.L, g->gBm, p.dtype, st),
+                       "reduce gBm");
+        if (g->gC)
+            SSM_LAUNCH(launch_reduce_parts_btn(lay.partC, nblk, (int)p.B, (int)p.N, (int)p.L, g->gC, p.dtype, st),
+                       "reduce gC");
+        if (g->gA)
+            SSM_LAUNCH(launch_reduce_parts_dn(lay.partA, (int)p.B, lay.G, (int)p.D, (int)p.N, g->gA, st),
+                       "reduce gA");
+        return ok();
+    }
+    if (p.mode == SSM_REAL_DENSE) {
+        if ((rc = dense_bwd(a, p, in, g, cv, true, st))) return rc;
+        if (need_only) { *need_only = cv.off; return ok(); }
+        if ((rc = check_ws(ws, ws_bytes, cv.off))) return rc;
+        Carve real(ws);
+        if ((rc = dense_bwd(a, p, in, g, real, false, st))) return rc;
+        return ok();
+    }
+    if ((rc = cplx_bwd(a, p, in, g, cv, true, st))) return rc;
+    if (need_only) { *need_only = cv.off; return ok(); }
+    if ((rc = check_ws(ws, ws_bytes, cv.off))) return rc;
+    Carve real(ws);
+    if ((rc = cplx_bwd(a, p, in, g, real, false, st))) return rc;
+    return ok();
+}
+
+// ---------------------------------------------------------------------------
+// ssm_impulse_sensitivity
+// ---------------------------------------------------------------------------
+int impulse_impl(const ssm_scan_args* a, int64_t t_out, void* y, void* s, void* ws, size_t ws_bytes,
+                 hipStream_t st, size_t* need_only) {
+    ScanPlan p;
+    int rc = validate_scan_args(a, &p);
+    if (rc) return rc;
+    if (p.mode != SSM_REAL_SELECTIVE)
+        return fail(SSM_ERR_UNSUPPORTED, "ssm_impulse_sensitivity supports SSM_REAL_SELECTIVE only");
+    if (t_out == -1) t_out = p.L - 1;
+    if (t_out < 0 || t_out >= p.L) return fail(SSM_ERR_SHAPE, "t_out %lld outside [0, L)", (long long)t_out);
+    if (!need_only) {
+        if (!s) return fail(SSM_ERR_NULL, "s is NULL");
+        const size_t BDL = p.B * p.D * p.L;
+        if ((rc = check_align(s, p.esz, "s")) || (rc = check_align(y, p.esz, "y"))) return rc;
+        if ((rc = check_overlaps(scan_inputs(a, p), {{y, BDL * p.esz, "y"}, {s, BDL * p.esz, "s"}}))) return rc;
+    }
+    auto layout = [&](Carve& cv, SelFwdLayout* lay, float** tsum, double** send) {
+        sel_fwd_layout(p, cv, lay);
+        *tsum = cv.take<float>((size_t)p.B * p.D * p.nchunks);
+        *send = cv.take<double>((size_t)p.B * p.D * p.nchunks);
+    };
+    Carve cv(nullptr);
+    SelFwdLayout lay;
+    float* tsum;
+    double* send;
+    layout(cv, &lay, &tsum, &send);
+    if (need_only) { *need_only = cv.off; return ok(); }
+    if ((rc = check_ws(ws, ws_bytes, cv.off))) return rc;
+    Carve real(ws);
+    layout(real, &lay, &tsum, &send);
+    if (y) {
+        if ((rc = run_sel_fwd(a, p, lay, y, nullptr, nullptr, tsum, st))) return rc;
+    } else {
+        SSM_LAUNCH(launch_tile_dsum(a->delta, tsum, (int)p.B, (int)p.D, (int)p.L, p.nchunks, p.kpl, p.dtype, st),
+                   "tile sums");
+    }
+    SSM_LAUNCH(launch_sens_suffix(a->delta, tsum, send, (int)p.B, (int)p.D, (int)p.L, p.nchunks, p.T, (int)t_out,
+                                  p.dtype, st), "suffix sums");
+    SensParams q{};
+    q.delta = a->delta; q.A = a->A; q.Bm = a->Bm; q.C = a->C; q.send = send; q.s = s;
+    q.B = (int)p.B; q.D = (int)p.D; q.L = (int)p.L; q.N = (int)p.N; q.ntiles = p.nchunks; q.t_out = (int)t_out;
+    q.vec = sel_vec(p, {a->delta, s});
+    SSM_LAUNCH(launch_sens(q, p.dtype, p.kpl, st), "sensitivity");
+    return ok();
+}
+
+}  // namespace
+
+#include "api_modes.inc"
+
+// ===========================================================================
+// exported C ABI
+// ===========================================================================
+extern "C" {
+
+int ssm_workspace_bytes(int op, const void* args, size_t* out_bytes) {
+    if (!out_bytes) return fail(SSM_ERR_NULL, "out_bytes is NULL");
+    *out_bytes = 0;
+    switch (op) {
+        case SSM_OP_SCAN_FWD: return scan_fwd_impl((const ssm_scan_args*)args, nullptr, nullptr, 0, nullptr, out_bytes);
+        case SSM_OP_SCAN_BWD: return scan_bwd_impl((const ssm_scan_args*)args, nullptr, nullptr, nullptr, 0, nullptr, out_bytes);
+        case SSM_OP_IMPULSE: return impulse_impl((const ssm_scan_args*)args, -1, nullptr, nullptr, nullptr, 0, nullptr, out_bytes);
+        case SSM_OP_PD_FWD: return pd_fwd_impl((const pd_scan_args*)args, nullptr, nullptr, 0, nullptr, out_bytes);
+        case SSM_OP_PD_BWD: return pd_bwd_impl((const pd_scan_args*)args, nullptr, nullptr, nullptr, 0, nullptr, out_bytes);
+        default: return fail(SSM_ERR_UNSUPPORTED, "unknown op %d", op);
+    }
+}
+
+int ssm_scan_fwd(const ssm_scan_args* args, const ssm_scan_fwd_out* out, void* ws, size_t ws_bytes, void* stream) {
+    return scan_fwd_impl(args, out, ws, ws_bytes, (hipStream_t)stream, nullptr);
+}
+int ssm_scan_bwd(const ssm_scan_args* args, const ssm_scan_bwd_in* in, const ssm_scan_grads* grads, void* ws,
+                 size_t ws_bytes, void* stream) {
+    return scan_bwd_impl(args, in, grads, ws, ws_bytes, (hipStream_t)stream, nullptr);
+}
+int ssm_impulse_sensitivity(const ssm_scan_args* args, int64_t t_out, void* y, void* s, void* ws, size_t ws_bytes,
+                            void* stream) {
+    return impulse_impl(args, t_out, y, s, ws, ws_bytes, (hipStream_t)stream, nullptr);
+}
+int pd_scan_fwd(const pd_scan_args* args, const pd_scan_fwd_out* out, void* ws, size_t ws_bytes, void* stream) {
+    return pd_fwd_impl(args, out, ws, ws_bytes, (hipStream_t)stream, nullptr);
+}
+int pd_scan_bwd(const pd_scan_args* args, const pd_scan_bwd_in* in, const pd_scan_grads* grads, void* ws,
+                size_t ws_bytes, void* stream) {
+    return pd_bwd_impl(args, in, grads, ws, ws_bytes, (hipStream_t)stream, nullptr);
+}
+
+const char* ssm_status_string(int status) {
+    switch (status) {
+        case SSM_OK: return "SSM_OK";
+        case SSM_ERR_NULL: return "SSM_ERR_NULL";
+        case SSM_ERR_SHAPE: return "SSM_ERR_SHAPE";
+        case SSM_ERR_DTYPE: return "SSM_ERR_DTYPE";
+        case SSM_ERR_LAYOUT: return "SSM_ERR_LAYOUT";
+        case SSM_ERR_WORKSPACE: return "SSM_ERR_WORKSPACE";
+        case SSM_ERR_UNSUPPORTED: return "SSM_ERR_UNSUPPORTED";
+        case SSM_ERR_DEVICE: return "SSM_ERR_DEVICE";
+        default: return "SSM_ERR_UNKNOWN";
+    }
+}
+const char* ssm_last_error_detail(void) { return g_detail.c_str(); }
+int ssm_abi_version(void) { return SSM_ABI_VERSION; }
+
+}  // extern "C"

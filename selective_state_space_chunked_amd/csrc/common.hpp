@@ -1,0 +1,233 @@
+// Device helpers for the gfx950 scan kernels: element conversion, DPP lane
+// moves inside 16-lane rows, the affine-operator row scans and the
+// transpose-reductions used to sum per-lane partials across lanes.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssm {
+
+typedef uint16_t bf16_t;  // bfloat16 bit pattern
+
+// ---------------------------------------------------------------------------
+// element conversion
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(bf16_t v) { return __uint_as_float(((uint32_t)v) << 16); }
+
+template <typename T> __device__ __forceinline__ T from_f32(float f);
+template <> __device__ __forceinline__ float from_f32<float>(float f) { return f; }
+template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);  // keep NaN
+    u += 0x7fffu + ((u >> 16) & 1u);                                           // nearest even
+    return (bf16_t)(u >> 16);
+}
+
+// Load KPL consecutive elements starting at p (element index), as float.
+// `vec` selects 16-byte vector loads; the caller guarantees alignment then.
+template <int KPL>
+__device__ __forceinline__ void load_run(const float* __restrict__ p, float (&v)[KPL], bool vec) {
+    if (vec) {
+#pragma unroll
+        for (int q = 0; q < KPL / 4; ++q) {
+            float4 w = *reinterpret_cast<const float4*>(p + 4 * q);
+            v[4 * q] = w.x; v[4 * q + 1] = w.y; v[4 * q + 2] = w.z; v[4 * q + 3] = w.w;
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < KPL; ++j) v[j] = p[j];
+    }
+}
+template <int KPL>
+__device__ __forceinline__ void load_run(const bf16_t* __restrict__ p, float (&v)[KPL], bool vec) {
+    if (vec && (KPL % 8) == 0) {
+#pragma unroll
+        for (int q = 0; q < KPL / 8; ++q) {
+            uint4 w = *reinterpret_cast<const uint4*>(p + 8 * q);
+            uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                v[8 * q + 2 * e] = __uint_as_float(ws[e] << 16);
+                v[8 * q + 2 * e + 1] = __uint_as_float(ws[e] & 0xffff0000u);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < KPL; ++j) v[j] = to_f32(p[j]);
+    }
+}
+// Masked variant: elements with index >= n read as 0.
+template <typename T, int KPL>
+__device__ __forceinline__ void load_run_masked(const T* __restrict__ p, float (&v)[KPL], int n) {
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) v[j] = (j < n) ? to_f32(p[j]) : 0.0f;
+}
+
+template <int KPL>
+__device__ __forceinline__ void store_run(float* __restrict__ p, const float (&v)[KPL], bool vec, int n) {
+    if (vec && n >= KPL) {
+#pragma unroll
+        for (int q = 0; q < KPL / 4; ++q)
+            *reinterpret_cast<float4*>(p + 4 * q) = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+    } else {
+#pragma unroll
+        for (int j = 0; j < KPL; ++j)
+            if (j < n) p[j] = v[j];
+    }
+}
+template <int KPL>
+__device__ __forceinline__ void store_run(bf16_t* __restrict__ p, const float (&v)[KPL], bool vec, int n) {
+    if (vec && n >= KPL && (KPL % 8) == 0) {
+#pragma unroll
+        for (int q = 0; q < KPL / 8; ++q) {
+            uint32_t w[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                w[e] = (uint32_t)from_f32<bf16_t>(v[8 * q + 2 * e]) |
+                       ((uint32_t)from_f32<bf16_t>(v[8 * q + 2 * e + 1]) << 16);
+            *reinterpret_cast<uint4*>(p + 8 * q) = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < KPL; ++j)
+            if (j < n) p[j] = from_f32<bf16_t>(v[j]);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// DPP moves (gfx9 encodings).  Lanes whose source is outside their 16-lane
+// row, or masked off, receive `old`.
+// ---------------------------------------------------------------------------
+#define SSM_DPP_ROW_SHL(n) (0x100 + (n))
+#define SSM_DPP_ROW_SHR(n) (0x110 + (n))
+#define SSM_DPP_ROW_ROR(n) (0x120 + (n))
+#define SSM_DPP_ROW_MIRROR 0x140
+#define SSM_DPP_ROW_HALF_MIRROR 0x141
+#define SSM_DPP_ROW_BCAST(n) (0x150 + (n))  // row_newbcast: lane n of each row to the row
+#define SSM_DPP_QUAD(a, b, c, d) ((a) | ((b) << 2) | ((c) << 4) | ((d) << 6))
+
+template <int CTRL, int ROWMASK = 0xf, int BANKMASK = 0xf>
+__device__ __forceinline__ float dpp(float old, float src) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(src), CTRL,
+                                                      ROWMASK, BANKMASK, false));
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int old, int src) {
+    return __builtin_amdgcn_update_dpp(old, src, CTRL, 0xf, 0xf, false);
+}
+
+// Broadcast lane `n` (compile-time) of each 16-lane row to the whole row.
+template <int n>
+__device__ __forceinline__ float row_bcast(float v) { return dpp<SSM_DPP_ROW_BCAST(n)>(0.0f, v); }
+
+// Runtime lane index version (for loops that are not unrolled).
+__device__ __forceinline__ float row_bcast_rt(float v, int n) {
+    int lane = threadIdx.x & 63;
+    int src = (lane & ~15) | n;
+    return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(v)));
+}
+
+// Sum over the 16 lanes of each row; every lane receives the row total.
+__device__ __forceinline__ float row_sum(float v) {
+    v += dpp<SSM_DPP_QUAD(1, 0, 3, 2)>(0.0f, v);
+    v += dpp<SSM_DPP_QUAD(2, 3, 0, 1)>(0.0f, v);
+    v += dpp<SSM_DPP_ROW_HALF_MIRROR>(0.0f, v);
+    v += dpp<SSM_DPP_ROW_MIRROR>(0.0f, v);
+    return v;
+}
+
+// Inclusive scan, inside each 16-lane row from lane 0 upward, of the affine
+// maps f_i(h) = P_i h + S_i under composition (later lane applied last):
+// afterwards (P, S) of lane i describe f_i o ... o f_0.
+__device__ __forceinline__ void row_scan_affine_up(float& P, float& S) {
+#define SSM_SCAN_STEP(k)                                        \
+    {                                                           \
+        float Pp = dpp<SSM_DPP_ROW_SHR(k)>(1.0f, P);            \
+        float Sp = dpp<SSM_DPP_ROW_SHR(k)>(0.0f, S);            \
+        S = fmaf(P, Sp, S);                                     \
+        P = P * Pp;                                             \
+    }
+    SSM_SCAN_STEP(1) SSM_SCAN_STEP(2) SSM_SCAN_STEP(4) SSM_SCAN_STEP(8)
+#undef SSM_SCAN_STEP
+}
+// Inclusive scan from lane 15 downward (lane i composes lanes i..15, lane i
+// applied last): used by the reverse-time adjoint recurrence.
+__device__ __forceinline__ void row_scan_affine_down(float& P, float& S) {
+#define SSM_SCAN_STEP(k)                                        \
+    {                                                           \
+        float Pp = dpp<SSM_DPP_ROW_SHL(k)>(1.0f, P);            \
+        float Sp = dpp<SSM_DPP_ROW_SHL(k)>(0.0f, S);            \
+        S = fmaf(P, Sp, S);                                     \
+        P = P * Pp;                                             \
+    }
+    SSM_SCAN_STEP(1) SSM_SCAN_STEP(2) SSM_SCAN_STEP(4) SSM_SCAN_STEP(8)
+#undef SSM_SCAN_STEP
+}
+
+// Exclusive prefix sum within each 16-lane row (lane 0 gets 0).
+__device__ __forceinline__ float row_excl_sum_up(float v) {
+    float s = v;
+    s += dpp<SSM_DPP_ROW_SHR(1)>(0.0f, s);
+    s += dpp<SSM_DPP_ROW_SHR(2)>(0.0f, s);
+    s += dpp<SSM_DPP_ROW_SHR(4)>(0.0f, s);
+    s += dpp<SSM_DPP_ROW_SHR(8)>(0.0f, s);
+    return s - v;
+}
+// Exclusive suffix sum within each row (lane 15 gets 0).
+__device__ __forceinline__ float row_excl_sum_down(float v) {
+    float s = v;
+    s += dpp<SSM_DPP_ROW_SHL(1)>(0.0f, s);
+    s += dpp<SSM_DPP_ROW_SHL(2)>(0.0f, s);
+    s += dpp<SSM_DPP_ROW_SHL(4)>(0.0f, s);
+    s += dpp<SSM_DPP_ROW_SHL(8)>(0.0f, s);
+    return s - v;
+}
+
+// ---------------------------------------------------------------------------
+// Transpose-reductions: every lane holds V partial values v[0..V-1]; after the
+// call, lane i of each group holds the sum over the group's lanes of slot i.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// one halving level inside a 16-lane row, pairing lanes that differ in the bit
+// selected by the DPP pattern; `hi` = this lane keeps the upper slot.
+template <int CTRL>
+__device__ __forceinline__ float pair_level(float lo, float up, bool hi) {
+    float keep = hi ? up : lo;
+    float send = hi ? lo : up;
+    return keep + dpp<CTRL>(0.0f, send);
+}
+
+// 16 slots across the 16 lanes of each row: lane i returns sum_lanes v[i].
+__device__ __forceinline__ float row_transpose_sum16(const float (&v)[16]) {
+    const int l = lane_id() & 15;
+    float w[8], z[4], q[2];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) w[k] = pair_level<SSM_DPP_ROW_ROR(8)>(v[k], v[k + 8], (l & 8) != 0);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) z[k] = pair_level<SSM_DPP_ROW_HALF_MIRROR>(w[k], w[k + 4], (l & 4) != 0);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) q[k] = pair_level<SSM_DPP_QUAD(2, 3, 0, 1)>(z[k], z[k + 2], (l & 2) != 0);
+    return pair_level<SSM_DPP_QUAD(1, 0, 3, 2)>(q[0], q[1], (l & 1) != 0);
+}
+
+// 64 slots across the 64 lanes of a wave: lane i returns sum_lanes v[i].
+__device__ __forceinline__ float wave_transpose_sum64(float (&v)[64]) {
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+        auto s = __builtin_amdgcn_permlane32_swap(__float_as_int(v[k]), __float_as_int(v[k + 32]), false, false);
+        v[k] = __int_as_float(s[0]) + __int_as_float(s[1]);
+    }
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        auto s = __builtin_amdgcn_permlane16_swap(__float_as_int(v[k]), __float_as_int(v[k + 16]), false, false);
+        v[k] = __int_as_float(s[0]) + __int_as_float(s[1]);
+    }
+    float w[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) w[k] = v[k];
+    return row_transpose_sum16(w);
+}
+
+}  // namespace ssm

@@ -1,0 +1,110 @@
+// Internal interface between the host library (api.cpp) and the HIP kernels.
+// Not part of the C ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ssm {
+
+// ------------------------------- real, selective ---------------------------
+struct SelFwdParams {
+    const void* delta; const void* x; const float* A; const void* Bm; const void* C;
+    const float* h0;        // (B,D,N) or null
+    const float* carry_in;  // (B,D,G,N) state entering each segment (G > 1)
+    void* y;                // (B,D,L) or null
+    float* h_last;          // (B,D,N) or null
+    float* ckpt;            // (B,D,ntiles,N) or null
+    float* segP;            // summary pass: product of a over each segment (B,D,G,N)
+    float* segS;            // summary pass: local state at segment end (B,D,G,N)
+    float* tile_dsum;       // (B,D,ntiles) sum of delta over each tile, or null
+    int B, D, L, N, ntiles, tiles_per_seg, G, vec;
+};
+struct SelBwdParams {
+    const void* delta; const void* x; const float* A; const void* Bm; const void* C;
+    const void* gy; const float* gh_last; const float* ckpt;
+    const float* nu_in;     // (B,D,G,N) adjoint entering each segment from the right (G > 1)
+    void* gdelta; void* gx; float* gh0;
+    float* partB; float* partC;  // (nblk,B,N,L) partial sums over each block of 16 channels
+    float* partA;                // (B,G,D,N)
+    float* segQ; float* segR;    // summary pass outputs (B,D,G,N)
+    int B, D, L, N, ntiles, tiles_per_seg, G, vec;
+};
+struct SensParams {
+    const void* delta; const float* A; const void* Bm; const void* C;
+    const double* send;     // (B,D,ntiles) sum of delta over later steps up to t_out
+    void* s;
+    int B, D, L, N, ntiles, t_out, vec;
+};
+
+hipError_t launch_sel_fwd(const SelFwdParams& p, int dtype, int kpl, bool summary, hipStream_t st);
+hipError_t launch_sel_bwd(const SelBwdParams& p, int dtype, int kpl, bool summary, hipStream_t st);
+hipError_t launch_seg_combine_fwd(const float* P, const float* S, const float* h0, float* carry_in,
+                                  int BD, int G, int N, hipStream_t st);
+hipError_t launch_seg_combine_rev(const float* Q, const float* R, const float* nu_last, float* nu_in,
+                                  int BD, int G, int N, hipStream_t st);
+hipError_t launch_reduce_parts_btn(const float* part, int nblk, int B, int N, int L, void* out, int dtype,
+                                   hipStream_t st);
+hipError_t launch_reduce_parts_dn(const float* part, int B, int G, int D, int N, float* out, hipStream_t st);
+hipError_t launch_sens_suffix(const void* delta, const float* tile_dsum, double* send, int B, int D, int L,
+                              int ntiles, int tile_len, int t_out, int dtype, hipStream_t st);
+hipError_t launch_tile_dsum(const void* delta, float* tile_dsum, int B, int D, int L, int ntiles, int kpl,
+                            int dtype, hipStream_t st);
+hipError_t launch_sens(const SensParams& p, int dtype, int kpl, hipStream_t st);
+
+// ------------------------------- real, dense -------------------------------
+struct DenseParams {
+    const float* a; const float* b; const float* C; const float* h0;
+    const float* carry_in;   // (B,D,G,N)
+    const float* gy; const float* gh_last; const float* ckpt; const float* nu_in;
+    float* y; float* h_last; float* ckpt_out;
+    float* segP; float* segS;      // forward summaries
+    float* segQ; float* segR;      // backward summaries
+    float* ga; float* gb; float* gh0;
+    float* partC;                  // (nblk,B,N,L)
+    int B, D, L, N, nchunks, chunk, chunks_per_seg, G;
+};
+hipError_t launch_dense_fwd(const DenseParams& p, bool summary, hipStream_t st);
+hipError_t launch_dense_bwd(const DenseParams& p, bool summary, hipStream_t st);
+
+// ------------------------------- complex -----------------------------------
+struct CplxParams {
+    const float* r; const float* phi; const float* lam; const float* theta;
+    const float* u; const float* c; const float* h0;
+    const float* carry_in;   // (B,H,G,M) complex
+    const float* gy; const float* gh_last; const float* ckpt; const float* nu_in;
+    float* y; float* h_last; float* ckpt_out;
+    float* segP; float* segS; float* segQ; float* segR;   // complex (B,H,G,M)
+    float* gu; float* gr; float* gphi; float* gh0;
+    float* partL; float* partT; float* partC;             // (B,G,H,M) [partC complex]
+    int B, H, L, M, nchunks, chunk, chunks_per_seg, G;
+};
+hipError_t launch_cplx_fwd(const CplxParams& p, bool summary, hipStream_t st);
+hipError_t launch_cplx_bwd(const CplxParams& p, bool summary, hipStream_t st);
+hipError_t launch_cplx_combine_fwd(const CplxParams& p, hipStream_t st);
+hipError_t launch_cplx_combine_rev(const CplxParams& p, hipStream_t st);
+hipError_t launch_cplx_reduce(const CplxParams& p, float* glam, float* gtheta, float* gc, hipStream_t st);
+
+// ------------------------------- PD ----------------------------------------
+struct PDParams {
+    const float* logits; const int32_t* sel_in; const int32_t* dict;
+    const float* d; const float* b; const float* C; const float* h0;
+    const float* gy; const float* gh_last; const float* ckpt;
+    int32_t* sel_out;              // selection written by the summary pass
+    const int32_t* sel;            // selection read by the later passes
+    int8_t* pre;                   // (H,K,N,N) preimage lists, -1 padded
+    int32_t* pre_cnt;              // (H,K,N)
+    int32_t* segPi; float* segD; float* segS;   // (B,H,G,N) chunk summaries
+    float* carry_in;               // (B,H,G,N)
+    float* nu_in;                  // (B,H,G,N)
+    float* y; float* h_last; float* ckpt_out;
+    float* gd; float* gb; float* gC; float* gh0;
+    int B, H, L, N, K, chunk, G;   // G = number of chunks
+};
+hipError_t launch_pd_prep(const PDParams& p, hipStream_t st);
+hipError_t launch_pd_fwd(const PDParams& p, bool summary, hipStream_t st);
+hipError_t launch_pd_combine_fwd(const PDParams& p, hipStream_t st);
+hipError_t launch_pd_bwd(const PDParams& p, bool summary, hipStream_t st);
+hipError_t launch_pd_combine_rev(const PDParams& p, hipStream_t st);
+
+}  // namespace ssm

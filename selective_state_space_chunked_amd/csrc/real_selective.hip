@@ -1,0 +1,649 @@
+// Diagonal real selective scan on gfx950: a_t[n] = exp(delta_t A[d,n]),
+// b_t[n] = delta_t x_t B_t[n], y_t = sum_n C_t[n] h_t[n] (Mamba-style selection
+// and discretisation, lpnh.cn "S3M" page, section 1.1; Euler input term).
+//
+// Work mapping.  A workgroup of 256 lanes is 16 rows of 16 lanes.  Row r owns
+// channel d = 16*blockIdx.x + r of batch blockIdx.y; blockIdx.z is a segment
+// of consecutive tiles.  A tile is TILE = 16*KPL consecutive steps; lane l of a
+// row owns steps l*KPL .. l*KPL+KPL-1 of the tile.  The state index n is a loop
+// inside the lane, so sums over n (y, the delta and x gradients) stay in
+// registers.  Per-state quantities of a row (A[d,n], the carried state) live
+// in lane n of that row and are broadcast with DPP row_newbcast.
+//
+// Per tile and state n (the three phases of the Flash PD-SSM page's
+// "Hardwarebewusste Implementierung", re-mapped onto a 16-lane DPP row):
+//   A: every lane folds its KPL steps into one affine map (P, S) with
+//      P = prod a = exp2(A2n * sum delta) and S = local state from zero;
+//   B: a 4-level DPP scan composes the lane maps across the row; the tile's
+//      carry-in comes from the previous tile (sequential within a segment) or,
+//      for the first tile of a segment, from a separate segment-combine pass;
+//   C: each lane re-runs its KPL steps from its exact entering state and
+//      accumulates C_t[n] h_t[n] into y.
+// B_t and C_t are shared by all 16 rows and staged once per tile in LDS,
+// transposed to [n][t] with 4 floats of padding after every lane's run so the
+// 16-byte LDS reads of a row hit distinct banks.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace ssm {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float bcast_n(float v, int n) {
+    switch (n) {
+        case 0: return row_bcast<0>(v);   case 1: return row_bcast<1>(v);
+        case 2: return row_bcast<2>(v);   case 3: return row_bcast<3>(v);
+        case 4: return row_bcast<4>(v);   case 5: return row_bcast<5>(v);
+        case 6: return row_bcast<6>(v);   case 7: return row_bcast<7>(v);
+        case 8: return row_bcast<8>(v);   case 9: return row_bcast<9>(v);
+        case 10: return row_bcast<10>(v); case 11: return row_bcast<11>(v);
+        case 12: return row_bcast<12>(v); case 13: return row_bcast<13>(v);
+        case 14: return row_bcast<14>(v); default: return row_bcast<15>(v);
+    }
+}
+
+template <int KPL> struct TileGeom {
+    static constexpr int TILE = 16 * KPL;
+    static constexpr int SEG = KPL + 4;          // a lane's run plus padding, in floats
+    static constexpr int LDSW = 16 * SEG + 4;    // one state's row; +4 spreads the rows over banks
+    __device__ static int idx(int n, int tt) { return n * LDSW + (tt / KPL) * SEG + (tt % KPL); }
+};
+
+// Stage a (TILE x N) block of a (B,L,N) tensor into LDS as float [n][t'].
+// Steps beyond L read as zero.  Optionally scaled elementwise by scale[n].
+template <typename T, int KPL>
+__device__ __forceinline__ void stage_tile(float* __restrict__ dst, const T* __restrict__ src, int b, int t0,
+                                           int L, int N) {
+    using G = TileGeom<KPL>;
+    const int total = G::TILE * N;
+    for (int e = threadIdx.x; e < total; e += 256) {
+        const int tt = e / N, n = e - tt * N;
+        const int t = t0 + tt;
+        float v = 0.0f;
+        if (t < L) v = to_f32(src[((size_t)b * L + t) * N + n]);
+        dst[G::idx(n, tt)] = v;
+    }
+}
+
+template <int KPL>
+__device__ __forceinline__ void read_run(const float* __restrict__ s, float (&v)[KPL]) {
+#pragma unroll
+    for (int q = 0; q < KPL / 4; ++q) {
+        float4 w = *reinterpret_cast<const float4*>(s + 4 * q);
+        v[4 * q] = w.x; v[4 * q + 1] = w.y; v[4 * q + 2] = w.z; v[4 * q + 3] = w.w;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// forward (SUMMARY: segment summaries only, no outputs)
+// ---------------------------------------------------------------------------
+template <typename T, int KPL, bool SUMMARY>
+__global__ __launch_bounds__(256) void sel_fwd_kernel(SelFwdParams p) {
+    using G = TileGeom<KPL>;
+    constexpr int TILE = G::TILE;
+    __shared__ __align__(16) float sB[16 * G::LDSW];
+    __shared__ __align__(16) float sC[SUMMARY ? 4 : 16 * G::LDSW];
+
+    const int tid = threadIdx.x, lane = tid & 15, row = tid >> 4;
+    const int b = blockIdx.y, g = blockIdx.z;
+    const int d = blockIdx.x * 16 + row;
+    const bool act = d < p.D;
+    const int dc = act ? d : p.D - 1;
+    const int N = p.N, L = p.L;
+    const T* __restrict__ delta = (const T*)p.delta;
+    const T* __restrict__ xin = (const T*)p.x;
+    const size_t seq = (size_t)b * p.D + dc;
+    const size_t rowoff = seq * L;
+
+    float A2 = 0.0f, carry = 0.0f, Pseg = 1.0f;
+    if (lane < N) {
+        A2 = p.A[(size_t)dc * N + lane] * kLog2e;
+        if (!SUMMARY) {
+            if (p.G > 1) carry = p.carry_in[(seq * p.G + g) * N + lane];
+            else if (p.h0) carry = p.h0[seq * N + lane];
+        }
+    }
+    const int tile0 = g * p.tiles_per_seg;
+    const int tile1 = min(tile0 + p.tiles_per_seg, p.ntiles);
+    const bool vec = p.vec != 0;
+
+    for (int tile = tile0; tile < tile1; ++tile) {
+        const int t0 = tile * TILE;
+        __syncthreads();
+        stage_tile<T, KPL>(sB, (const T*)p.Bm, b, t0, L, N);
+        if (!SUMMARY) stage_tile<T, KPL>(sC, (const T*)p.C, b, t0, L, N);
+        __syncthreads();
+
+        const int tl = t0 + lane * KPL;
+        const int nval = L - tl;
+        float dl[KPL], dx[KPL];
+        if (nval >= KPL) {
+            float xv[KPL];
+            load_run<KPL>(delta + rowoff + tl, dl, vec);
+            load_run<KPL>(xin + rowoff + tl, xv, vec);
+#pragma unroll
+            for (int j = 0; j < KPL; ++j) dx[j] = dl[j] * xv[j];
+        } else {
+            float xv[KPL];
+            load_run_masked<T, KPL>(delta + rowoff + tl, dl, nval);
+            load_run_masked<T, KPL>(xin + rowoff + tl, xv, nval);
+#pragma unroll
+            for (int j = 0; j < KPL; ++j) dx[j] = dl[j] * xv[j];
+        }
+        float dsum = 0.0f;
+#pragma unroll
+        for (int j = 0; j < KPL; ++j) dsum += dl[j];
+        if (!SUMMARY && p.tile_dsum) {
+            float ts = row_sum(dsum);
+            if (act && lane == 0) p.tile_dsum[seq * p.ntiles + tile] = ts;
+        }
+        if (!SUMMARY && p.ckpt && act && lane < N) p.ckpt[(seq * p.ntiles + tile) * N + lane] = carry;
+
+        float yacc[KPL];
+#pragma unroll
+        for (int j = 0; j < KPL; ++j) yacc[j] = 0.0f;
+
+#pragma unroll
+        for (int n = 0; n < 16; ++n) {
+            if (n >= N) break;
+            const float A2n = bcast_n(A2, n);
+            const float cin = bcast_n(carry, n);
+            float bv[KPL], a[KPL], bx[KPL];
+            read_run<KPL>(sB + n * G::LDSW + lane * G::SEG, bv);
+            float S = 0.0f;
+#pragma unroll
+            for (int j = 0; j < KPL; ++j) {
+                a[j] = __builtin_amdgcn_exp2f(dl[j] * A2n);
+                bx[j] = dx[j] * bv[j];
+                S = fmaf(a[j], S, bx[j]);
+            }
+            float P = __builtin_amdgcn_exp2f(dsum * A2n);
+            row_scan_affine_up(P, S);
+            float newc;
+            if (SUMMARY) {
+                const float Pt = row_bcast<15>(P), St = row_bcast<15>(S);
+                newc = fmaf(Pt, cin, St);
+                if (lane == n) Pseg *= Pt;
+            } else {
+                const float hend = fmaf(P, cin, S);
+                float h = dpp<SSM_DPP_ROW_SHR(1)>(cin, hend);  // state entering this lane's run
+                newc = row_bcast<15>(hend);
+                float cv[KPL];
+                read_run<KPL>(sC + n * G::LDSW + lane * G::SEG, cv);
+#pragma unroll
+                for (int j = 0; j < KPL; ++j) {
+                    h = fmaf(a[j], h, bx[j]);
+                    yacc[j] = fmaf(cv[j], h, yacc[j]);
+                }
+            }
+            carry = (lane == n) ? newc : carry;
+        }
+        if (!SUMMARY && p.y && act && nval > 0)
+            store_run<KPL>((T*)p.y + rowoff + tl, yacc, vec, nval);
+    }
+    if (SUMMARY) {
+        if (act && lane < N) {
+            p.segP[(seq * p.G + g) * N + lane] = Pseg;
+            p.segS[(seq * p.G + g) * N + lane] = carry;
+        }
+    } else if (p.h_last && g == p.G - 1 && act && lane < N) {
+        p.h_last[seq * N + lane] = carry;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// backward.  Reverse over the tiles of a segment.  Per tile and state n: the
+// forward is recomputed from the checkpoint (phases A-C as above, states kept
+// in registers), then the adjoint nu_t = a_t (C_t gy_t + nu_{t+1}) runs right
+// to left with the same lane-fold / DPP-scan structure, seeded by the adjoint
+// entering from the next tile (gh_last at the sequence end).
+//   lambda_t = C_t gy_t + nu_{t+1},   dLoss/da_t = lambda_t h_{t-1},
+//   gdelta_t = sum_n (A lambda a h_{t-1} + lambda x B),  gx_t = delta_t sum_n lambda B,
+//   gB_t[n] = sum_d lambda delta x,  gC_t[n] = sum_d gy h_t,  gA = sum_{b,t} lambda a h_{t-1} delta.
+// Sums over d are first taken over the 16 rows in LDS and written as one
+// partial per 16-channel block; a second kernel adds the blocks in order.
+// SUMMARY: per segment, the composed adjoint map nu_start = Q nu_end + R.
+// ---------------------------------------------------------------------------
+template <typename T, int KPL, bool SUMMARY>
+__global__ __launch_bounds__(256) void sel_bwd_kernel(SelBwdParams p) {
+    using G = TileGeom<KPL>;
+    constexpr int TILE = G::TILE;
+    __shared__ __align__(16) float sB[SUMMARY ? 4 : 16 * G::LDSW];
+    __shared__ __align__(16) float sC[16 * G::LDSW];
+    __shared__ __align__(16) float red[SUMMARY ? 4 : 2 * 16 * TILE];
+
+    const int tid = threadIdx.x, lane = tid & 15, row = tid >> 4;
+    const int b = blockIdx.y, g = blockIdx.z;
+    const int d = blockIdx.x * 16 + row;
+    const bool act = d < p.D;
+    const int dc = act ? d : p.D - 1;
+    const int N = p.N, L = p.L;
+    const T* __restrict__ delta = (const T*)p.delta;
+    const T* __restrict__ xin = (const T*)p.x;
+    const T* __restrict__ gyin = (const T*)p.gy;
+    const size_t seq = (size_t)b * p.D + dc;
+    const size_t rowoff = seq * L;
+    const bool vec = p.vec != 0;
+    const bool wantB = p.partB != nullptr, wantC = p.partC != nullptr, wantA = p.partA != nullptr;
+
+    float A2 = 0.0f, Ao = 0.0f, nu = 0.0f, gAacc = 0.0f, Qseg = 1.0f;
+    if (lane < N) {
+        Ao = p.A[(size_t)dc * N + lane];
+        A2 = Ao * kLog2e;
+        if (!SUMMARY) {
+            if (p.G > 1) nu = p.nu_in[(seq * p.G + g) * N + lane];
+            else if (p.gh_last) nu = p.gh_last[seq * N + lane];
+        }
+    }
+    const int tile0 = g * p.tiles_per_seg;
+    const int tile1 = min(tile0 + p.tiles_per_seg, p.ntiles);
+
+    for (int tile = tile1 - 1; tile >= tile0; --tile) {
+        const int t0 = tile * TILE;
+        __syncthreads();
+        if (!SUMMARY) stage_tile<T, KPL>(sB, (const T*)p.Bm, b, t0, L, N);
+        stage_tile<T, KPL>(sC, (const T*)p.C, b, t0, L, N);
+        __syncthreads();
+
+        const int tl = t0 + lane * KPL;
+        const int nval = L - tl;
+        float dl[KPL], dx[KPL], gyv[KPL];
+        {
+            float xv[KPL];
+            if (nval >= KPL) {
+                load_run<KPL>(delta + rowoff + tl, dl, vec);
+                load_run<KPL>(gyin + rowoff + tl, gyv, vec);
+                if (!SUMMARY) load_run<KPL>(xin + rowoff + tl, xv, vec);
+            } else {
+                load_run_masked<T, KPL>(delta + rowoff + tl, dl, nval);
+                load_run_masked<T, KPL>(gyin + rowoff + tl, gyv, nval);
+                if (!SUMMARY) load_run_masked<T, KPL>(xin + rowoff + tl, xv, nval);
+            }
+#pragma unroll
+            for (int j = 0; j < KPL; ++j) dx[j] = SUMMARY ? 0.0f : dl[j] * xv[j];
+        }
+        float dsum = 0.0f;
+#pragma unroll
+        for (int j = 0; j < KPL; ++j) dsum += dl[j];
+        float hs = 0.0f;
+        if (!SUMMARY && lane < N) hs = p.ckpt[(seq * p.ntiles + tile) * N + lane];
+
+        float Gd[KPL], Sb[KPL];
+#pragma unroll
+        for (int j = 0; j < KPL; ++j) { Gd[j] = 0.0f; Sb[j] = 0.0f; }
+
+#pragma unroll
+        for (int n = 0; n < 16; ++n) {
+            if (n >= N) break;
+            const float A2n = bcast_n(A2, n);
+            const float nin = bcast_n(nu, n);
+            float a[KPL], cv[KPL];
+            read_run<KPL>(sC + n * G::LDSW + lane * G::SEG, cv);
+#pragma unroll
+            for (int j = 0; j < KPL; ++j) a[j] = __builtin_amdgcn_exp2f(dl[j] * A2n);
+            const float P = __builtin_amdgcn_exp2f(dsum * A2n);
+
+            // adjoint lane fold, right to left: nu_j = a_j (c_j + nu_{j+1})
+            float R = 0.0f;
+#pragma unroll
+            for (int j = KPL - 1; j >= 0; --j) R = a[j] * fmaf(cv[j], gyv[j], R);
+            float Q = P;
+            row_scan_affine_down(Q, R);
+            const float nfirst = fmaf(Q, nin, R);     // adjoint at this lane's first step
+            const float newnu = row_bcast<0>(nfirst);
+            if (SUMMARY) {
+                const float Qt = row_bcast<0>(Q);
+                if (lane == n) Qseg *= Qt;
+                nu = (lane == n) ? newnu : nu;
+                continue;
+            }
+            float nnext = dpp<SSM_DPP_ROW_SHL(1)>(nin, nfirst);  // adjoint entering from the right
+
+            // recompute the forward states of this lane's run
+            const float An = bcast_n(Ao, n);
+            const float cin = bcast_n(hs, n);
+            float bv[KPL], bx[KPL], h[KPL + 1];
+            read_run<KPL>(sB + n * G::LDSW + lane * G::SEG, bv);
+            float S = 0.0f;
+#pragma unroll
+            for (int j = 0; j < KPL; ++j) {
+                bx[j] = dx[j] * bv[j];
+                S = fmaf(a[j], S, bx[j]);
+            }
+            float Pf = P;
+            row_scan_affine_up(Pf, S);
+            const float hend = fmaf(Pf, cin, S);
+            h[0] = dpp<SSM_DPP_ROW_SHR(1)>(cin, hend);
+#pragma unroll
+            for (int j = 0; j < KPL; ++j) h[j + 1] = fmaf(a[j], h[j], bx[j]);
+
+            float gAl = 0.0f;
+            float* rB = red + row * TILE + lane * KPL;
+            float* rC = red + 16 * TILE + row * TILE + lane * KPL;
+#pragma unroll
+            for (int j = KPL - 1; j >= 0; --j) {
+                const float lam = fmaf(cv[j], gyv[j], nnext);
+                const float ah = a[j] * h[j];
+                const float t1 = lam * ah;
+                Gd[j] = fmaf(An, t1, Gd[j]);
+                Sb[j] = fmaf(lam, bv[j], Sb[j]);
+                gAl = fmaf(t1, dl[j], gAl);
+                if (wantB) rB[j] = act ? lam * dx[j] : 0.0f;
+                if (wantC) rC[j] = act ? gyv[j] * h[j + 1] : 0.0f;
+                nnext = a[j] * lam;
+            }
+            nu = (lane == n) ? newnu : nu;
+            if (wantA) {
+                const float ga = row_sum(gAl);
+                if (lane == n) gAacc += ga;
+            }
+            if (wantB || wantC) {
+                __syncthreads();
+                const int nblk = gridDim.x;
+                for (int o = tid; o < 2 * TILE; o += 256) {
+                    const int which = o / TILE, tt = o - which * TILE;
+                    const int t = t0 + tt;
+                    const float* src = red + which * 16 * TILE + tt;
+                    float s = 0.0f;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) s += src[r * TILE];
+                    float* part = which ? p.partC : p.partB;
+                    if (part && t < L)
+                        part[(((size_t)blockIdx.x * p.B + b) * N + n) * L + t] = s;
+                }
+                (void)nblk;
+                __syncthreads();
+            }
+        }
+        if (!SUMMARY && act && nval > 0) {
+            if (p.gx) {
+                float v[KPL];
+#pragma unroll
+                for (int j = 0; j < KPL; ++j) v[j] = dl[j] * Sb[j];
+                store_run<KPL>((T*)p.gx + rowoff + tl, v, vec, nval);
+            }
+            if (p.gdelta) {
+                float xv[KPL], v[KPL];
+                if (nval >= KPL) load_run<KPL>(xin + rowoff + tl, xv, vec);
+                else load_run_masked<T, KPL>(xin + rowoff + tl, xv, nval);
+#pragma unroll
+                for (int j = 0; j < KPL; ++j) v[j] = fmaf(xv[j], Sb[j], Gd[j]);
+                store_run<KPL>((T*)p.gdelta + rowoff + tl, v, vec, nval);
+            }
+        }
+    }
+    if (SUMMARY) {
+        if (act && lane < N) {
+            p.segQ[(seq * p.G + g) * N + lane] = Qseg;
+            p.segR[(seq * p.G + g) * N + lane] = nu;
+        }
+        return;
+    }
+    if (act && lane < N) {
+        if (p.gh0 && g == 0) p.gh0[seq * N + lane] = nu;
+        if (wantA) p.partA[(((size_t)b * p.G + g) * p.D + dc) * N + lane] = gAacc;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// segment combines (phase B across segments), one lane per (sequence, state)
+// ---------------------------------------------------------------------------
+__global__ void seg_combine_fwd_kernel(const float* __restrict__ P, const float* __restrict__ S,
+                                       const float* __restrict__ h0, float* __restrict__ carry_in, int BD,
+                                       int G, int N) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= BD * N) return;
+    const int s = i / N, n = i - s * N;
+    float h = h0 ? h0[(size_t)s * N + n] : 0.0f;
+    for (int g = 0; g < G; ++g) {
+        const size_t o = ((size_t)s * G + g) * N + n;
+        carry_in[o] = h;
+        h = fmaf(P[o], h, S[o]);
+    }
+}
+__global__ void seg_combine_rev_kernel(const float* __restrict__ Q, const float* __restrict__ R,
+                                       const float* __restrict__ nu_last, float* __restrict__ nu_in, int BD,
+                                       int G, int N) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= BD * N) return;
+    const int s = i / N, n = i - s * N;
+    float v = nu_last ? nu_last[(size_t)s * N + n] : 0.0f;
+    for (int g = G - 1; g >= 0; --g) {
+        const size_t o = ((size_t)s * G + g) * N + n;
+        nu_in[o] = v;
+        v = fmaf(Q[o], v, R[o]);
+    }
+}
+
+// partial (nblk,B,N,L) -> out (B,L,N), adding the blocks in index order
+template <typename T>
+__global__ void reduce_parts_btn_kernel(const float* __restrict__ part, int nblk, int B, int N, int L,
+                                        T* __restrict__ out) {
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const size_t total = (size_t)B * N * L;
+    if (i >= total) return;
+    const int t = (int)(i % L);
+    const size_t bn = i / L;
+    const int n = (int)(bn % N), b = (int)(bn / N);
+    float s = 0.0f;
+    for (int k = 0; k < nblk; ++k) s += part[(size_t)k * total + i];
+    out[((size_t)b * L + t) * N + n] = from_f32<T>(s);
+}
+// partial (B,G,D,N) -> out (D,N)
+__global__ void reduce_parts_dn_kernel(const float* __restrict__ part, int B, int G, int D, int N,
+                                       float* __restrict__ out) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= D * N) return;
+    float s = 0.0f;
+    for (int k = 0; k < B * G; ++k) s += part[(size_t)k * D * N + i];
+    out[i] = s;
+}
+
+// ---------------------------------------------------------------------------
+// impulse sensitivity: s_t = delta_t sum_n B_t[n] C_out[n] exp2(A2[n] S_t),
+// S_t = sum_{s=t+1..t_out} delta_s (the reverse costate mu_t = C_out prod a in
+// closed form).  The suffix sums over tiles come from a per-sequence pass in
+// double precision; inside a tile they are DPP row suffix sums plus in-lane
+// suffix sums.  Every tile is independent, so the grid spans all tiles.
+// ---------------------------------------------------------------------------
+template <typename T, int KPL>
+__global__ void tile_dsum_kernel(const T* __restrict__ delta, float* __restrict__ out, int B, int D, int L,
+                                 int ntiles) {
+    const int lane = threadIdx.x & 15, row = threadIdx.x >> 4;
+    const int d = blockIdx.x * 16 + row, b = blockIdx.y, tile = blockIdx.z;
+    const bool act = d < D;
+    const int dc = act ? d : D - 1;
+    const int tl = tile * 16 * KPL + lane * KPL;
+    float v[KPL];
+    load_run_masked<T, KPL>(delta + ((size_t)b * D + dc) * L + tl, v, L - tl);
+    float s = 0.0f;
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) s += v[j];
+    s = row_sum(s);
+    if (act && lane == 0) out[((size_t)b * D + dc) * ntiles + tile] = s;
+}
+
+template <typename T>
+__global__ void sens_suffix_kernel(const T* __restrict__ delta, const float* __restrict__ tile_dsum,
+                                   double* __restrict__ send, int BD, int L, int ntiles, int tile_len,
+                                   int t_out) {
+    const int s = blockIdx.x * blockDim.x + threadIdx.x;
+    if (s >= BD) return;
+    const int tout_tile = t_out / tile_len;
+    double acc = 0.0;
+    for (int tile = ntiles - 1; tile >= 0; --tile) {
+        send[(size_t)s * ntiles + tile] = acc;  // steps of later tiles up to t_out
+        if (tile < tout_tile) {
+            acc += (double)tile_dsum[(size_t)s * ntiles + tile];
+        } else if (tile == tout_tile) {
+            double part = 0.0;
+            for (int t = tile * tile_len; t <= t_out; ++t) part += (double)to_f32(delta[(size_t)s * L + t]);
+            acc += part;
+        }
+    }
+}
+
+template <typename T, int KPL>
+__global__ __launch_bounds__(256) void sens_kernel(SensParams p) {
+    using Gm = TileGeom<KPL>;
+    constexpr int TILE = Gm::TILE;
+    __shared__ __align__(16) float sBC[16 * Gm::LDSW];
+    __shared__ float sCout[16];
+    const int tid = threadIdx.x, lane = tid & 15, row = tid >> 4;
+    const int b = blockIdx.y, tile = blockIdx.z;
+    const int d = blockIdx.x * 16 + row;
+    const bool act = d < p.D;
+    const int dc = act ? d : p.D - 1;
+    const int N = p.N, L = p.L;
+    const size_t seq = (size_t)b * p.D + dc;
+    const int t0 = tile * TILE;
+    if (t0 > p.t_out) {  // whole tile after t_out: zero sensitivity
+        const int tl = t0 + lane * KPL;
+        if (act && tl < L) {
+            float z[KPL];
+#pragma unroll
+            for (int j = 0; j < KPL; ++j) z[j] = 0.0f;
+            store_run<KPL>((T*)p.s + seq * L + tl, z, p.vec != 0, L - tl);
+        }
+        return;
+    }
+    if (tid < N) sCout[tid] = to_f32(((const T*)p.C)[((size_t)b * L + p.t_out) * N + tid]);
+    __syncthreads();
+    {
+        const T* Bm = (const T*)p.Bm;
+        for (int e = tid; e < TILE * N; e += 256) {
+            const int tt = e / N, n = e - tt * N;
+            const int t = t0 + tt;
+            float v = 0.0f;
+            if (t < L) v = to_f32(Bm[((size_t)b * L + t) * N + n]) * sCout[n];
+            sBC[Gm::idx(n, tt)] = v;
+        }
+    }
+    __syncthreads();
+    const int tl = t0 + lane * KPL;
+    float dl[KPL];
+    load_run_masked<T, KPL>((const T*)p.delta + seq * L + tl, dl, min(L, p.t_out + 1) - tl);
+    // S_j = sum of delta over steps after j up to t_out
+    float lsum = 0.0f;
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) lsum += dl[j];
+    const float base = (float)p.send[seq * p.ntiles + tile] + row_excl_sum_down(lsum);
+    float S[KPL];
+    {
+        float run = 0.0f;
+#pragma unroll
+        for (int j = KPL - 1; j >= 0; --j) {
+            S[j] = base + run;
+            run += dl[j];
+        }
+    }
+    float A2 = 0.0f;
+    if (lane < N) A2 = p.A[(size_t)dc * N + lane] * kLog2e;
+    float acc[KPL];
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) acc[j] = 0.0f;
+#pragma unroll
+    for (int n = 0; n < 16; ++n) {
+        if (n >= N) break;
+        const float A2n = bcast_n(A2, n);
+        float bc[KPL];
+        read_run<KPL>(sBC + n * Gm::LDSW + lane * Gm::SEG, bc);
+#pragma unroll
+        for (int j = 0; j < KPL; ++j) acc[j] = fmaf(bc[j], __builtin_amdgcn_exp2f(A2n * S[j]), acc[j]);
+    }
+    if (act && tl < L) {
+        float v[KPL];
+#pragma unroll
+        for (int j = 0; j < KPL; ++j) v[j] = (tl + j <= p.t_out) ? dl[j] * acc[j] : 0.0f;
+        store_run<KPL>((T*)p.s + seq * L + tl, v, p.vec != 0, L - tl);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+#define SSM_DISPATCH_KPL(kpl, ...)                         \
+    switch (kpl) {                                         \
+        case 4: { constexpr int K_ = 4; __VA_ARGS__; } break;   \
+        case 8: { constexpr int K_ = 8; __VA_ARGS__; } break;   \
+        case 16: { constexpr int K_ = 16; __VA_ARGS__; } break; \
+        default: return hipErrorInvalidValue;              \
+    }
+
+hipError_t launch_sel_fwd(const SelFwdParams& p, int dtype, int kpl, bool summary, hipStream_t st) {
+    dim3 grid((p.D + 15) / 16, p.B, p.G), block(256);
+    if (dtype == 0) {
+        if (summary) { SSM_DISPATCH_KPL(kpl, sel_fwd_kernel<float, K_, true><<<grid, block, 0, st>>>(p)) }
+        else { SSM_DISPATCH_KPL(kpl, sel_fwd_kernel<float, K_, false><<<grid, block, 0, st>>>(p)) }
+    } else {
+        if (summary) { SSM_DISPATCH_KPL(kpl, sel_fwd_kernel<bf16_t, K_, true><<<grid, block, 0, st>>>(p)) }
+        else { SSM_DISPATCH_KPL(kpl, sel_fwd_kernel<bf16_t, K_, false><<<grid, block, 0, st>>>(p)) }
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_sel_bwd(const SelBwdParams& p, int dtype, int kpl, bool summary, hipStream_t st) {
+    dim3 grid((p.D + 15) / 16, p.B, p.G), block(256);
+    if (dtype == 0) {
+        if (summary) { SSM_DISPATCH_KPL(kpl, sel_bwd_kernel<float, K_, true><<<grid, block, 0, st>>>(p)) }
+        else { SSM_DISPATCH_KPL(kpl, sel_bwd_kernel<float, K_, false><<<grid, block, 0, st>>>(p)) }
+    } else {
+        if (summary) { SSM_DISPATCH_KPL(kpl, sel_bwd_kernel<bf16_t, K_, true><<<grid, block, 0, st>>>(p)) }
+        else { SSM_DISPATCH_KPL(kpl, sel_bwd_kernel<bf16_t, K_, false><<<grid, block, 0, st>>>(p)) }
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_seg_combine_fwd(const float* P, const float* S, const float* h0, float* carry_in, int BD,
+                                  int G, int N, hipStream_t st) {
+    const int total = BD * N;
+    seg_combine_fwd_kernel<<<(total + 255) / 256, 256, 0, st>>>(P, S, h0, carry_in, BD, G, N);
+    return hipGetLastError();
+}
+hipError_t launch_seg_combine_rev(const float* Q, const float* R, const float* nu_last, float* nu_in, int BD,
+                                  int G, int N, hipStream_t st) {
+    const int total = BD * N;
+    seg_combine_rev_kernel<<<(total + 255) / 256, 256, 0, st>>>(Q, R, nu_last, nu_in, BD, G, N);
+    return hipGetLastError();
+}
+hipError_t launch_reduce_parts_btn(const float* part, int nblk, int B, int N, int L, void* out, int dtype,
+                                   hipStream_t st) {
+    const size_t total = (size_t)B * N * L;
+    const unsigned blocks = (unsigned)((total + 255) / 256);
+    if (dtype == 0) reduce_parts_btn_kernel<float><<<blocks, 256, 0, st>>>(part, nblk, B, N, L, (float*)out);
+    else reduce_parts_btn_kernel<bf16_t><<<blocks, 256, 0, st>>>(part, nblk, B, N, L, (bf16_t*)out);
+    return hipGetLastError();
+}
+hipError_t launch_reduce_parts_dn(const float* part, int B, int G, int D, int N, float* out, hipStream_t st) {
+    reduce_parts_dn_kernel<<<(D * N + 255) / 256, 256, 0, st>>>(part, B, G, D, N, out);
+    return hipGetLastError();
+}
+hipError_t launch_tile_dsum(const void* delta, float* tile_dsum, int B, int D, int L, int ntiles, int kpl,
+                            int dtype, hipStream_t st) {
+    dim3 grid((D + 15) / 16, B, ntiles);
+    if (dtype == 0) {
+        SSM_DISPATCH_KPL(kpl, tile_dsum_kernel<float, K_><<<grid, 256, 0, st>>>((const float*)delta, tile_dsum, B, D, L, ntiles))
+    } else {
+        SSM_DISPATCH_KPL(kpl, tile_dsum_kernel<bf16_t, K_><<<grid, 256, 0, st>>>((const bf16_t*)delta, tile_dsum, B, D, L, ntiles))
+    }
+    return hipGetLastError();
+}
+hipError_t launch_sens_suffix(const void* delta, const float* tile_dsum, double* send, int B, int D, int L,
+                              int ntiles, int tile_len, int t_out, int dtype, hipStream_t st) {
+    const int BD = B * D;
+    if (dtype == 0)
+        sens_suffix_kernel<float><<<(BD + 127) / 128, 128, 0, st>>>((const float*)delta, tile_dsum, send, BD, L,
+                                                                    ntiles, tile_len, t_out);
+    else
+        sens_suffix_kernel<bf16_t><<<(BD + 127) / 128, 128, 0, st>>>((const bf16_t*)delta, tile_dsum, send, BD,
+                                                                     L, ntiles, tile_len, t_out);
+    return hipGetLastError();
+}
+hipError_t launch_sens(const SensParams& p, int dtype, int kpl, hipStream_t st) {
+    dim3 grid((p.D + 15) / 16, p.B, p.ntiles);
+    if (dtype == 0) { SSM_DISPATCH_KPL(kpl, sens_kernel<float, K_><<<grid, 256, 0, st>>>(p)) }
+    else { SSM_DISPATCH_KPL(kpl, sens_kernel<bf16_t, K_><<<grid, 256, 0, st>>>(p)) }
+    return hipGetLastError();
+}
+
+}  // namespace ssm
