@@ -235,6 +235,16 @@ int pd_scan_fwd(const pd_scan_args* args, const pd_scan_fwd_out* out,
 int pd_scan_bwd(const pd_scan_args* args, const pd_scan_bwd_in* in,
                 const pd_scan_grads* grads, void* ws, size_t ws_bytes, void* stream);
 
+/* Diagnostics: per-kernel timing with HIP events.  After ssm_profile_begin(n)
+ * every kernel the entry points enqueue from this thread is bracketed by two
+ * HIP events recorded on the same stream (at most n kernels; later ones are
+ * not recorded).  ssm_profile_end waits for the last event, writes up to
+ * `capacity` per-kernel durations in milliseconds and static kernel names,
+ * sets *n_launches to the number recorded, and stops recording.  The events
+ * are created by the library and kept for reuse until the process ends. */
+int ssm_profile_begin(int max_launches);
+int ssm_profile_end(int* n_launches, float* ms, const char** names, int capacity);
+
 const char* ssm_status_string(int status);   /* static string for a status code */
 const char* ssm_last_error_detail(void);     /* thread-local detail of the last error */
 int ssm_abi_version(void);                   /* SSM_ABI_VERSION of the built library */

@@ -87,15 +87,37 @@ int device_status(hipError_t e, const char* what) {
     if (e != hipSuccess) return fail(SSM_ERR_DEVICE, "%s: %s", what, hipGetErrorName(e));
     return SSM_OK;
 }
+// Optional per-kernel timing (ssm_profile_begin / ssm_profile_end).
+struct Profile {
+    bool on = false;
+    int cap = 0, n = 0;
+    std::vector<hipEvent_t> ev;  // 2 per launch
+    std::vector<const char*> names;
+};
+thread_local Profile g_prof;
+
+void prof_pre(hipStream_t st) {
+    if (g_prof.on && g_prof.n < g_prof.cap) hipEventRecord(g_prof.ev[2 * g_prof.n], st);
+}
+void prof_post(hipStream_t st, const char* what) {
+    if (g_prof.on && g_prof.n < g_prof.cap) {
+        hipEventRecord(g_prof.ev[2 * g_prof.n + 1], st);
+        g_prof.names[g_prof.n] = what;
+        ++g_prof.n;
+    }
+}
+
 #define SSM_LAUNCH(expr, what)                            \
     do {                                                  \
+        prof_pre(st);                                     \
         int rc_ = device_status((expr), what);            \
         if (rc_ != SSM_OK) return rc_;                    \
+        prof_post(st, what);                              \
     } while (0)
 
 // segment count along the sequence so the grid reaches the parallelism target
-void plan_segments(int64_t wg_per_seg, int64_t nunits, int* G, int* per_seg) {
-    int64_t g = std::max<int64_t>(1, cdiv(kTargetWG, std::max<int64_t>(1, wg_per_seg)));
+void plan_segments(int64_t wg_per_seg, int64_t nunits, int* G, int* per_seg, int64_t target = kTargetWG) {
+    int64_t g = std::max<int64_t>(1, cdiv(target, std::max<int64_t>(1, wg_per_seg)));
     g = std::min<int64_t>(g, nunits);
     int64_t ps = cdiv(nunits, g);
     *per_seg = (int)ps;
@@ -252,15 +274,16 @@ void sel_bwd_layout(const ScanPlan& p, bool have_ckpt, bool wantB, bool wantC, b
         lay->ckpt = cv.take<float>((size_t)p.B * p.D * p.nchunks * p.N);
         sel_fwd_layout(p, cv, &lay->fwd);
     }
-    const int64_t wg = cdiv(p.D, 16) * p.B;
-    plan_segments(wg, p.nchunks, &lay->G, &lay->tps);
+    // 512-lane workgroups, one per compute unit at a time: two rounds of 256 CUs
+    const int64_t wg = cdiv(p.D, sel_bwd_rows()) * p.B;
+    plan_segments(wg, p.nchunks, &lay->G, &lay->tps, kTargetWG / 2);
     if (lay->G > 1) {
         const size_t n = (size_t)p.B * p.D * lay->G * p.N;
         lay->segQ = cv.take<float>(n);
         lay->segR = cv.take<float>(n);
         lay->nu = cv.take<float>(n);
     }
-    const size_t np = (size_t)cdiv(p.D, 16) * p.B * p.N * p.L;
+    const size_t np = (size_t)cdiv(p.D, sel_bwd_rows()) * p.B * p.N * p.L;
     if (wantB) lay->partB = cv.take<float>(np);
     if (wantC) lay->partC = cv.take<float>(np);
     if (wantA) lay->partA = cv.take<float>((size_t)p.B * lay->G * p.D * p.N);
@@ -412,7 +435,7 @@ int scan_bwd_impl(const ssm_scan_args* a, const ssm_scan_bwd_in* in, const ssm_s
                                               (int)p.N, st), "segment combine (reverse)");
         }
         SSM_LAUNCH(launch_sel_bwd(q, p.dtype, p.kpl, false, st), "selective backward");
-        const int nblk = (int)cdiv(p.D, 16);
+        const int nblk = (int)cdiv(p.D, sel_bwd_rows());
         if (g->gBm)
             SSM_LAUNCH(launch_reduce_parts_btn(lay.partB, nblk, (int)p.B, (int)p.N, (int)p.L, g->gBm, p.dtype, st),
                        "reduce gBm");
@@ -527,6 +550,39 @@ int pd_scan_fwd(const pd_scan_args* args, const pd_scan_fwd_out* out, void* ws, 
 int pd_scan_bwd(const pd_scan_args* args, const pd_scan_bwd_in* in, const pd_scan_grads* grads, void* ws,
                 size_t ws_bytes, void* stream) {
     return pd_bwd_impl(args, in, grads, ws, ws_bytes, (hipStream_t)stream, nullptr);
+}
+
+int ssm_profile_begin(int max_launches) {
+    if (max_launches < 0) return fail(SSM_ERR_SHAPE, "max_launches < 0");
+    Profile& p = g_prof;
+    while ((int)p.ev.size() < 2 * max_launches) {
+        hipEvent_t e;
+        hipError_t err = hipEventCreate(&e);
+        if (err != hipSuccess) return fail(SSM_ERR_DEVICE, "hipEventCreate: %s", hipGetErrorName(err));
+        p.ev.push_back(e);
+    }
+    p.names.assign(max_launches, nullptr);
+    p.cap = max_launches;
+    p.n = 0;
+    p.on = max_launches > 0;
+    return ok();
+}
+int ssm_profile_end(int* n_launches, float* ms, const char** names, int capacity) {
+    Profile& p = g_prof;
+    p.on = false;
+    if (n_launches) *n_launches = p.n;
+    if (p.n > 0) {
+        hipError_t err = hipEventSynchronize(p.ev[2 * p.n - 1]);
+        if (err != hipSuccess) return fail(SSM_ERR_DEVICE, "hipEventSynchronize: %s", hipGetErrorName(err));
+    }
+    for (int i = 0; i < p.n && i < capacity; ++i) {
+        float t = 0.0f;
+        hipError_t err = hipEventElapsedTime(&t, p.ev[2 * i], p.ev[2 * i + 1]);
+        if (err != hipSuccess) return fail(SSM_ERR_DEVICE, "hipEventElapsedTime: %s", hipGetErrorName(err));
+        if (ms) ms[i] = t;
+        if (names) names[i] = p.names[i];
+    }
+    return ok();
 }
 
 const char* ssm_status_string(int status) {

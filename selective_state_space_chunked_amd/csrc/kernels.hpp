@@ -25,7 +25,7 @@ struct SelBwdParams {
     const void* gy; const float* gh_last; const float* ckpt;
     const float* nu_in;     // (B,D,G,N) adjoint entering each segment from the right (G > 1)
     void* gdelta; void* gx; float* gh0;
-    float* partB; float* partC;  // (nblk,B,N,L) partial sums over each block of 16 channels
+    float* partB; float* partC;  // (nblk,B,N,L) partial sums over each block of channels
     float* partA;                // (B,G,D,N)
     float* segQ; float* segR;    // summary pass outputs (B,D,G,N)
     int B, D, L, N, ntiles, tiles_per_seg, G, vec;
@@ -39,6 +39,7 @@ struct SensParams {
 
 hipError_t launch_sel_fwd(const SelFwdParams& p, int dtype, int kpl, bool summary, hipStream_t st);
 hipError_t launch_sel_bwd(const SelBwdParams& p, int dtype, int kpl, bool summary, hipStream_t st);
+int sel_bwd_rows();  // channels per backward workgroup (one gB/gC partial per block)
 hipError_t launch_seg_combine_fwd(const float* P, const float* S, const float* h0, float* carry_in,
                                   int BD, int G, int N, hipStream_t st);
 hipError_t launch_seg_combine_rev(const float* Q, const float* R, const float* nu_last, float* nu_in,

@@ -28,18 +28,33 @@
 namespace ssm {
 
 constexpr float kLog2e = 1.4426950408889634f;
+// backward workgroup: 32 rows of 16 lanes (channels 32*blockIdx.x ...)
+constexpr int kBwdRows = 32;
+constexpr int kBwdThreads = 16 * kBwdRows;
 
-__device__ __forceinline__ float bcast_n(float v, int n) {
-    switch (n) {
-        case 0: return row_bcast<0>(v);   case 1: return row_bcast<1>(v);
-        case 2: return row_bcast<2>(v);   case 3: return row_bcast<3>(v);
-        case 4: return row_bcast<4>(v);   case 5: return row_bcast<5>(v);
-        case 6: return row_bcast<6>(v);   case 7: return row_bcast<7>(v);
-        case 8: return row_bcast<8>(v);   case 9: return row_bcast<9>(v);
-        case 10: return row_bcast<10>(v); case 11: return row_bcast<11>(v);
-        case 12: return row_bcast<12>(v); case 13: return row_bcast<13>(v);
-        case 14: return row_bcast<14>(v); default: return row_bcast<15>(v);
+// State index of the loop over n: compile-time (fully unrolled loop, DPP
+// row_newbcast) or runtime (generic state counts, ds_bpermute broadcast).
+template <int NC> struct CState {
+    static constexpr int n = NC;
+    __device__ __forceinline__ float bc(float v) const { return row_bcast<NC>(v); }
+};
+struct RState {
+    int n;
+    __device__ __forceinline__ float bc(float v) const { return row_bcast_rt(v, n); }
+};
+template <int I, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (I < E) {
+        f(CState<I>{});
+        static_for<I + 1, E>(f);
     }
+}
+// Run body(state) for n = 0..N-1: NT = 16 unrolls with compile-time lanes.
+template <int NT, typename F>
+__device__ __forceinline__ void for_states(int N, F&& body) {
+    const int n_end = NT ? NT : N;
+#pragma unroll 1
+    for (int n = 0; n < n_end; ++n) body(RState{n});
 }
 
 template <int KPL> struct TileGeom {
@@ -50,18 +65,33 @@ template <int KPL> struct TileGeom {
 };
 
 // Stage a (TILE x N) block of a (B,L,N) tensor into LDS as float [n][t'].
-// Steps beyond L read as zero.  Optionally scaled elementwise by scale[n].
-template <typename T, int KPL>
+// Steps beyond L read as zero.  NT = 16: one thread per step row, 16-byte loads.
+template <typename T, int KPL, int NT, int THREADS = 256>
 __device__ __forceinline__ void stage_tile(float* __restrict__ dst, const T* __restrict__ src, int b, int t0,
                                            int L, int N) {
     using G = TileGeom<KPL>;
-    const int total = G::TILE * N;
-    for (int e = threadIdx.x; e < total; e += 256) {
-        const int tt = e / N, n = e - tt * N;
-        const int t = t0 + tt;
-        float v = 0.0f;
-        if (t < L) v = to_f32(src[((size_t)b * L + t) * N + n]);
-        dst[G::idx(n, tt)] = v;
+    if constexpr (NT == 16) {
+        for (int tt = threadIdx.x; tt < G::TILE; tt += THREADS) {
+            const int t = t0 + tt;
+            float v[16];
+            if (t < L) load_run<16>(src + ((size_t)b * L + t) * 16, v, true);
+            else {
+#pragma unroll
+                for (int n = 0; n < 16; ++n) v[n] = 0.0f;
+            }
+            const int base = (tt / KPL) * G::SEG + (tt % KPL);
+#pragma unroll
+            for (int n = 0; n < 16; ++n) dst[n * G::LDSW + base] = v[n];
+        }
+    } else {
+        const int total = G::TILE * N;
+        for (int e = threadIdx.x; e < total; e += THREADS) {
+            const int tt = e / N, n = e - tt * N;
+            const int t = t0 + tt;
+            float v = 0.0f;
+            if (t < L) v = to_f32(src[((size_t)b * L + t) * N + n]);
+            dst[G::idx(n, tt)] = v;
+        }
     }
 }
 
@@ -77,8 +107,8 @@ __device__ __forceinline__ void read_run(const float* __restrict__ s, float (&v)
 // ---------------------------------------------------------------------------
 // forward (SUMMARY: segment summaries only, no outputs)
 // ---------------------------------------------------------------------------
-template <typename T, int KPL, bool SUMMARY>
-__global__ __launch_bounds__(256) void sel_fwd_kernel(SelFwdParams p) {
+template <typename T, int KPL, int NT, bool SUMMARY>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void sel_fwd_kernel(SelFwdParams p) {
     using G = TileGeom<KPL>;
     constexpr int TILE = G::TILE;
     __shared__ __align__(16) float sB[16 * G::LDSW];
@@ -89,7 +119,7 @@ __global__ __launch_bounds__(256) void sel_fwd_kernel(SelFwdParams p) {
     const int d = blockIdx.x * 16 + row;
     const bool act = d < p.D;
     const int dc = act ? d : p.D - 1;
-    const int N = p.N, L = p.L;
+    const int N = NT ? NT : p.N, L = p.L;
     const T* __restrict__ delta = (const T*)p.delta;
     const T* __restrict__ xin = (const T*)p.x;
     const size_t seq = (size_t)b * p.D + dc;
@@ -110,23 +140,22 @@ __global__ __launch_bounds__(256) void sel_fwd_kernel(SelFwdParams p) {
     for (int tile = tile0; tile < tile1; ++tile) {
         const int t0 = tile * TILE;
         __syncthreads();
-        stage_tile<T, KPL>(sB, (const T*)p.Bm, b, t0, L, N);
-        if (!SUMMARY) stage_tile<T, KPL>(sC, (const T*)p.C, b, t0, L, N);
+        stage_tile<T, KPL, NT>(sB, (const T*)p.Bm, b, t0, L, N);
+        if (!SUMMARY) stage_tile<T, KPL, NT>(sC, (const T*)p.C, b, t0, L, N);
         __syncthreads();
 
         const int tl = t0 + lane * KPL;
         const int nval = L - tl;
         float dl[KPL], dx[KPL];
-        if (nval >= KPL) {
+        {
             float xv[KPL];
-            load_run<KPL>(delta + rowoff + tl, dl, vec);
-            load_run<KPL>(xin + rowoff + tl, xv, vec);
-#pragma unroll
-            for (int j = 0; j < KPL; ++j) dx[j] = dl[j] * xv[j];
-        } else {
-            float xv[KPL];
-            load_run_masked<T, KPL>(delta + rowoff + tl, dl, nval);
-            load_run_masked<T, KPL>(xin + rowoff + tl, xv, nval);
+            if (nval >= KPL) {
+                load_run<KPL>(delta + rowoff + tl, dl, vec);
+                load_run<KPL>(xin + rowoff + tl, xv, vec);
+            } else {
+                load_run_masked<T, KPL>(delta + rowoff + tl, dl, nval);
+                load_run_masked<T, KPL>(xin + rowoff + tl, xv, nval);
+            }
 #pragma unroll
             for (int j = 0; j < KPL; ++j) dx[j] = dl[j] * xv[j];
         }
@@ -143,11 +172,10 @@ __global__ __launch_bounds__(256) void sel_fwd_kernel(SelFwdParams p) {
 #pragma unroll
         for (int j = 0; j < KPL; ++j) yacc[j] = 0.0f;
 
-#pragma unroll
-        for (int n = 0; n < 16; ++n) {
-            if (n >= N) break;
-            const float A2n = bcast_n(A2, n);
-            const float cin = bcast_n(carry, n);
+        for_states<NT>(N, [&](auto st) {
+            const int n = st.n;
+            const float A2n = st.bc(A2);
+            const float cin = st.bc(carry);
             float bv[KPL], a[KPL], bx[KPL];
             read_run<KPL>(sB + n * G::LDSW + lane * G::SEG, bv);
             float S = 0.0f;
@@ -160,7 +188,7 @@ __global__ __launch_bounds__(256) void sel_fwd_kernel(SelFwdParams p) {
             float P = __builtin_amdgcn_exp2f(dsum * A2n);
             row_scan_affine_up(P, S);
             float newc;
-            if (SUMMARY) {
+            if constexpr (SUMMARY) {
                 const float Pt = row_bcast<15>(P), St = row_bcast<15>(S);
                 newc = fmaf(Pt, cin, St);
                 if (lane == n) Pseg *= Pt;
@@ -177,7 +205,7 @@ __global__ __launch_bounds__(256) void sel_fwd_kernel(SelFwdParams p) {
                 }
             }
             carry = (lane == n) ? newc : carry;
-        }
+        });
         if (!SUMMARY && p.y && act && nval > 0)
             store_run<KPL>((T*)p.y + rowoff + tl, yacc, vec, nval);
     }
@@ -204,27 +232,30 @@ __global__ __launch_bounds__(256) void sel_fwd_kernel(SelFwdParams p) {
 // partial per 16-channel block; a second kernel adds the blocks in order.
 // SUMMARY: per segment, the composed adjoint map nu_start = Q nu_end + R.
 // ---------------------------------------------------------------------------
-template <typename T, int KPL, bool SUMMARY>
-__global__ __launch_bounds__(256) void sel_bwd_kernel(SelBwdParams p) {
+template <typename T, int KPL, int NT, bool SUMMARY, bool WA>
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))) void sel_bwd_kernel(SelBwdParams p) {
     using G = TileGeom<KPL>;
     constexpr int TILE = G::TILE;
+    constexpr int ROWS = kBwdRows;
     __shared__ __align__(16) float sB[SUMMARY ? 4 : 16 * G::LDSW];
     __shared__ __align__(16) float sC[16 * G::LDSW];
-    __shared__ __align__(16) float red[SUMMARY ? 4 : 2 * 16 * TILE];
+    // per-row partials of gB and gC for one state, laid out like the B/C tiles
+    // ([row][lane run + 4 pad]) so the 16-byte writes of a row hit distinct banks
+    __shared__ __align__(16) float red[SUMMARY ? 4 : 2 * ROWS * G::LDSW];
 
     const int tid = threadIdx.x, lane = tid & 15, row = tid >> 4;
     const int b = blockIdx.y, g = blockIdx.z;
-    const int d = blockIdx.x * 16 + row;
+    const int d = blockIdx.x * ROWS + row;
     const bool act = d < p.D;
     const int dc = act ? d : p.D - 1;
-    const int N = p.N, L = p.L;
+    const int N = NT ? NT : p.N, L = p.L;
     const T* __restrict__ delta = (const T*)p.delta;
     const T* __restrict__ xin = (const T*)p.x;
     const T* __restrict__ gyin = (const T*)p.gy;
     const size_t seq = (size_t)b * p.D + dc;
     const size_t rowoff = seq * L;
     const bool vec = p.vec != 0;
-    const bool wantB = p.partB != nullptr, wantC = p.partC != nullptr, wantA = p.partA != nullptr;
+    const bool wantB = p.partB != nullptr, wantC = p.partC != nullptr;
 
     float A2 = 0.0f, Ao = 0.0f, nu = 0.0f, gAacc = 0.0f, Qseg = 1.0f;
     if (lane < N) {
@@ -241,8 +272,8 @@ __global__ __launch_bounds__(256) void sel_bwd_kernel(SelBwdParams p) {
     for (int tile = tile1 - 1; tile >= tile0; --tile) {
         const int t0 = tile * TILE;
         __syncthreads();
-        if (!SUMMARY) stage_tile<T, KPL>(sB, (const T*)p.Bm, b, t0, L, N);
-        stage_tile<T, KPL>(sC, (const T*)p.C, b, t0, L, N);
+        if (!SUMMARY) stage_tile<T, KPL, NT, kBwdThreads>(sB, (const T*)p.Bm, b, t0, L, N);
+        stage_tile<T, KPL, NT, kBwdThreads>(sC, (const T*)p.C, b, t0, L, N);
         __syncthreads();
 
         const int tl = t0 + lane * KPL;
@@ -259,8 +290,13 @@ __global__ __launch_bounds__(256) void sel_bwd_kernel(SelBwdParams p) {
                 load_run_masked<T, KPL>(gyin + rowoff + tl, gyv, nval);
                 if (!SUMMARY) load_run_masked<T, KPL>(xin + rowoff + tl, xv, nval);
             }
+            // rows past D contribute nothing to the sums over channels
+            const float live = act ? 1.0f : 0.0f;
 #pragma unroll
-            for (int j = 0; j < KPL; ++j) dx[j] = SUMMARY ? 0.0f : dl[j] * xv[j];
+            for (int j = 0; j < KPL; ++j) {
+                dx[j] = SUMMARY ? 0.0f : dl[j] * xv[j] * live;
+                if (!SUMMARY) gyv[j] *= live;
+            }
         }
         float dsum = 0.0f;
 #pragma unroll
@@ -272,11 +308,10 @@ __global__ __launch_bounds__(256) void sel_bwd_kernel(SelBwdParams p) {
 #pragma unroll
         for (int j = 0; j < KPL; ++j) { Gd[j] = 0.0f; Sb[j] = 0.0f; }
 
-#pragma unroll
-        for (int n = 0; n < 16; ++n) {
-            if (n >= N) break;
-            const float A2n = bcast_n(A2, n);
-            const float nin = bcast_n(nu, n);
+        for_states<NT>(N, [&](auto st) {
+            const int n = st.n;
+            const float A2n = st.bc(A2);
+            const float nin = st.bc(nu);
             float a[KPL], cv[KPL];
             read_run<KPL>(sC + n * G::LDSW + lane * G::SEG, cv);
 #pragma unroll
@@ -291,70 +326,80 @@ __global__ __launch_bounds__(256) void sel_bwd_kernel(SelBwdParams p) {
             row_scan_affine_down(Q, R);
             const float nfirst = fmaf(Q, nin, R);     // adjoint at this lane's first step
             const float newnu = row_bcast<0>(nfirst);
-            if (SUMMARY) {
+            if constexpr (SUMMARY) {
                 const float Qt = row_bcast<0>(Q);
                 if (lane == n) Qseg *= Qt;
                 nu = (lane == n) ? newnu : nu;
-                continue;
-            }
-            float nnext = dpp<SSM_DPP_ROW_SHL(1)>(nin, nfirst);  // adjoint entering from the right
+            } else {
+                float nnext = dpp<SSM_DPP_ROW_SHL(1)>(nin, nfirst);  // adjoint entering from the right
 
-            // recompute the forward states of this lane's run
-            const float An = bcast_n(Ao, n);
-            const float cin = bcast_n(hs, n);
-            float bv[KPL], bx[KPL], h[KPL + 1];
-            read_run<KPL>(sB + n * G::LDSW + lane * G::SEG, bv);
-            float S = 0.0f;
+                // recompute the forward states of this lane's run
+                const float An = st.bc(Ao);
+                const float cin = st.bc(hs);
+                float bv[KPL], bx[KPL], h[KPL + 1];
+                read_run<KPL>(sB + n * G::LDSW + lane * G::SEG, bv);
+                float S = 0.0f;
 #pragma unroll
-            for (int j = 0; j < KPL; ++j) {
-                bx[j] = dx[j] * bv[j];
-                S = fmaf(a[j], S, bx[j]);
-            }
-            float Pf = P;
-            row_scan_affine_up(Pf, S);
-            const float hend = fmaf(Pf, cin, S);
-            h[0] = dpp<SSM_DPP_ROW_SHR(1)>(cin, hend);
-#pragma unroll
-            for (int j = 0; j < KPL; ++j) h[j + 1] = fmaf(a[j], h[j], bx[j]);
-
-            float gAl = 0.0f;
-            float* rB = red + row * TILE + lane * KPL;
-            float* rC = red + 16 * TILE + row * TILE + lane * KPL;
-#pragma unroll
-            for (int j = KPL - 1; j >= 0; --j) {
-                const float lam = fmaf(cv[j], gyv[j], nnext);
-                const float ah = a[j] * h[j];
-                const float t1 = lam * ah;
-                Gd[j] = fmaf(An, t1, Gd[j]);
-                Sb[j] = fmaf(lam, bv[j], Sb[j]);
-                gAl = fmaf(t1, dl[j], gAl);
-                if (wantB) rB[j] = act ? lam * dx[j] : 0.0f;
-                if (wantC) rC[j] = act ? gyv[j] * h[j + 1] : 0.0f;
-                nnext = a[j] * lam;
-            }
-            nu = (lane == n) ? newnu : nu;
-            if (wantA) {
-                const float ga = row_sum(gAl);
-                if (lane == n) gAacc += ga;
-            }
-            if (wantB || wantC) {
-                __syncthreads();
-                const int nblk = gridDim.x;
-                for (int o = tid; o < 2 * TILE; o += 256) {
-                    const int which = o / TILE, tt = o - which * TILE;
-                    const int t = t0 + tt;
-                    const float* src = red + which * 16 * TILE + tt;
-                    float s = 0.0f;
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) s += src[r * TILE];
-                    float* part = which ? p.partC : p.partB;
-                    if (part && t < L)
-                        part[(((size_t)blockIdx.x * p.B + b) * N + n) * L + t] = s;
+                for (int j = 0; j < KPL; ++j) {
+                    bx[j] = dx[j] * bv[j];
+                    S = fmaf(a[j], S, bx[j]);
                 }
-                (void)nblk;
-                __syncthreads();
+                float Pf = P;
+                row_scan_affine_up(Pf, S);
+                const float hend = fmaf(Pf, cin, S);
+                h[0] = dpp<SSM_DPP_ROW_SHR(1)>(cin, hend);
+#pragma unroll
+                for (int j = 0; j < KPL; ++j) h[j + 1] = fmaf(a[j], h[j], bx[j]);
+
+                float gAl = 0.0f;
+                float pB[KPL], pC[KPL];
+#pragma unroll
+                for (int j = KPL - 1; j >= 0; --j) {
+                    const float lam = fmaf(cv[j], gyv[j], nnext);
+                    const float ah = a[j] * h[j];
+                    const float t1 = lam * ah;
+                    Gd[j] = fmaf(An, t1, Gd[j]);
+                    Sb[j] = fmaf(lam, bv[j], Sb[j]);
+                    if constexpr (WA) gAl = fmaf(t1, dl[j], gAl);
+                    pB[j] = lam * dx[j];
+                    pC[j] = gyv[j] * h[j + 1];
+                    nnext = a[j] * lam;
+                }
+                {
+                    float* rB = red + row * G::LDSW + lane * G::SEG;
+                    float* rC = rB + ROWS * G::LDSW;
+#pragma unroll
+                    for (int q = 0; q < KPL / 4; ++q) {
+                        *reinterpret_cast<float4*>(rB + 4 * q) =
+                            make_float4(pB[4 * q], pB[4 * q + 1], pB[4 * q + 2], pB[4 * q + 3]);
+                        *reinterpret_cast<float4*>(rC + 4 * q) =
+                            make_float4(pC[4 * q], pC[4 * q + 1], pC[4 * q + 2], pC[4 * q + 3]);
+                    }
+                }
+                nu = (lane == n) ? newnu : nu;
+                if constexpr (WA) {
+                    const float ga = row_sum(gAl);
+                    if (lane == n) gAacc += ga;
+                }
+                if (wantB || wantC) {
+                    __syncthreads();
+                    // one output per thread; thread i of a tensor takes step 16*(i%16) + i/16 so
+                    // the 64 lanes of a wave read 16 lane runs x 4 steps = 64 distinct banks
+                    for (int o = tid; o < 2 * TILE; o += kBwdThreads) {
+                        const int which = o / TILE, i = o - which * TILE;
+                        const int tt = (i % 16) * KPL + (i / 16);
+                        const float* src = red + which * ROWS * G::LDSW + (tt / KPL) * G::SEG + (tt % KPL);
+                        float sum = 0.0f;
+#pragma unroll
+                        for (int r = 0; r < ROWS; ++r) sum += src[r * G::LDSW];
+                        float* part = which ? p.partC : p.partB;
+                        const int t = t0 + tt;
+                        if (part && t < L) part[(((size_t)blockIdx.x * p.B + b) * N + n) * L + t] = sum;
+                    }
+                    __syncthreads();
+                }
             }
-        }
+        });
         if (!SUMMARY && act && nval > 0) {
             if (p.gx) {
                 float v[KPL];
@@ -381,7 +426,7 @@ __global__ __launch_bounds__(256) void sel_bwd_kernel(SelBwdParams p) {
     }
     if (act && lane < N) {
         if (p.gh0 && g == 0) p.gh0[seq * N + lane] = nu;
-        if (wantA) p.partA[(((size_t)b * p.G + g) * p.D + dc) * N + lane] = gAacc;
+        if (WA) p.partA[(((size_t)b * p.G + g) * p.D + dc) * N + lane] = gAacc;
     }
 }
 
@@ -483,7 +528,7 @@ __global__ void sens_suffix_kernel(const T* __restrict__ delta, const float* __r
     }
 }
 
-template <typename T, int KPL>
+template <typename T, int KPL, int NT>
 __global__ __launch_bounds__(256) void sens_kernel(SensParams p) {
     using Gm = TileGeom<KPL>;
     constexpr int TILE = Gm::TILE;
@@ -494,7 +539,7 @@ __global__ __launch_bounds__(256) void sens_kernel(SensParams p) {
     const int d = blockIdx.x * 16 + row;
     const bool act = d < p.D;
     const int dc = act ? d : p.D - 1;
-    const int N = p.N, L = p.L;
+    const int N = NT ? NT : p.N, L = p.L;
     const size_t seq = (size_t)b * p.D + dc;
     const int t0 = tile * TILE;
     if (t0 > p.t_out) {  // whole tile after t_out: zero sensitivity
@@ -542,15 +587,13 @@ __global__ __launch_bounds__(256) void sens_kernel(SensParams p) {
     float acc[KPL];
 #pragma unroll
     for (int j = 0; j < KPL; ++j) acc[j] = 0.0f;
-#pragma unroll
-    for (int n = 0; n < 16; ++n) {
-        if (n >= N) break;
-        const float A2n = bcast_n(A2, n);
+    for_states<NT>(N, [&](auto st) {
+        const float A2n = st.bc(A2);
         float bc[KPL];
-        read_run<KPL>(sBC + n * Gm::LDSW + lane * Gm::SEG, bc);
+        read_run<KPL>(sBC + st.n * Gm::LDSW + lane * Gm::SEG, bc);
 #pragma unroll
         for (int j = 0; j < KPL; ++j) acc[j] = fmaf(bc[j], __builtin_amdgcn_exp2f(A2n * S[j]), acc[j]);
-    }
+    });
     if (act && tl < L) {
         float v[KPL];
 #pragma unroll
@@ -570,28 +613,32 @@ __global__ __launch_bounds__(256) void sens_kernel(SensParams p) {
         default: return hipErrorInvalidValue;              \
     }
 
-hipError_t launch_sel_fwd(const SelFwdParams& p, int dtype, int kpl, bool summary, hipStream_t st) {
+template <typename T, int NT>
+hipError_t sel_fwd_t(const SelFwdParams& p, int kpl, bool summary, hipStream_t st) {
     dim3 grid((p.D + 15) / 16, p.B, p.G), block(256);
-    if (dtype == 0) {
-        if (summary) { SSM_DISPATCH_KPL(kpl, sel_fwd_kernel<float, K_, true><<<grid, block, 0, st>>>(p)) }
-        else { SSM_DISPATCH_KPL(kpl, sel_fwd_kernel<float, K_, false><<<grid, block, 0, st>>>(p)) }
-    } else {
-        if (summary) { SSM_DISPATCH_KPL(kpl, sel_fwd_kernel<bf16_t, K_, true><<<grid, block, 0, st>>>(p)) }
-        else { SSM_DISPATCH_KPL(kpl, sel_fwd_kernel<bf16_t, K_, false><<<grid, block, 0, st>>>(p)) }
-    }
+    if (summary) { SSM_DISPATCH_KPL(kpl, sel_fwd_kernel<T, K_, NT, true><<<grid, block, 0, st>>>(p)) }
+    else { SSM_DISPATCH_KPL(kpl, sel_fwd_kernel<T, K_, NT, false><<<grid, block, 0, st>>>(p)) }
     return hipGetLastError();
 }
+hipError_t launch_sel_fwd(const SelFwdParams& p, int dtype, int kpl, bool summary, hipStream_t st) {
+    const bool n16 = p.N == 16;
+    if (dtype == 0) return n16 ? sel_fwd_t<float, 16>(p, kpl, summary, st) : sel_fwd_t<float, 0>(p, kpl, summary, st);
+    return n16 ? sel_fwd_t<bf16_t, 16>(p, kpl, summary, st) : sel_fwd_t<bf16_t, 0>(p, kpl, summary, st);
+}
 
-hipError_t launch_sel_bwd(const SelBwdParams& p, int dtype, int kpl, bool summary, hipStream_t st) {
-    dim3 grid((p.D + 15) / 16, p.B, p.G), block(256);
-    if (dtype == 0) {
-        if (summary) { SSM_DISPATCH_KPL(kpl, sel_bwd_kernel<float, K_, true><<<grid, block, 0, st>>>(p)) }
-        else { SSM_DISPATCH_KPL(kpl, sel_bwd_kernel<float, K_, false><<<grid, block, 0, st>>>(p)) }
-    } else {
-        if (summary) { SSM_DISPATCH_KPL(kpl, sel_bwd_kernel<bf16_t, K_, true><<<grid, block, 0, st>>>(p)) }
-        else { SSM_DISPATCH_KPL(kpl, sel_bwd_kernel<bf16_t, K_, false><<<grid, block, 0, st>>>(p)) }
-    }
+template <typename T, int NT>
+hipError_t sel_bwd_t(const SelBwdParams& p, int kpl, bool summary, hipStream_t st) {
+    dim3 grid((p.D + kBwdRows - 1) / kBwdRows, p.B, p.G), block(kBwdThreads);
+    if (summary) { SSM_DISPATCH_KPL(kpl, sel_bwd_kernel<T, K_, NT, true, false><<<grid, block, 0, st>>>(p)) }
+    else if (p.partA) { SSM_DISPATCH_KPL(kpl, sel_bwd_kernel<T, K_, NT, false, true><<<grid, block, 0, st>>>(p)) }
+    else { SSM_DISPATCH_KPL(kpl, sel_bwd_kernel<T, K_, NT, false, false><<<grid, block, 0, st>>>(p)) }
     return hipGetLastError();
+}
+int sel_bwd_rows() { return kBwdRows; }
+hipError_t launch_sel_bwd(const SelBwdParams& p, int dtype, int kpl, bool summary, hipStream_t st) {
+    const bool n16 = p.N == 16;
+    if (dtype == 0) return n16 ? sel_bwd_t<float, 16>(p, kpl, summary, st) : sel_bwd_t<float, 0>(p, kpl, summary, st);
+    return n16 ? sel_bwd_t<bf16_t, 16>(p, kpl, summary, st) : sel_bwd_t<bf16_t, 0>(p, kpl, summary, st);
 }
 
 hipError_t launch_seg_combine_fwd(const float* P, const float* S, const float* h0, float* carry_in, int BD,
@@ -641,8 +688,14 @@ hipError_t launch_sens_suffix(const void* delta, const float* tile_dsum, double*
 }
 hipError_t launch_sens(const SensParams& p, int dtype, int kpl, hipStream_t st) {
     dim3 grid((p.D + 15) / 16, p.B, p.ntiles);
-    if (dtype == 0) { SSM_DISPATCH_KPL(kpl, sens_kernel<float, K_><<<grid, 256, 0, st>>>(p)) }
-    else { SSM_DISPATCH_KPL(kpl, sens_kernel<bf16_t, K_><<<grid, 256, 0, st>>>(p)) }
+    const bool n16 = p.N == 16;
+    if (dtype == 0) {
+        if (n16) { SSM_DISPATCH_KPL(kpl, sens_kernel<float, K_, 16><<<grid, 256, 0, st>>>(p)) }
+        else { SSM_DISPATCH_KPL(kpl, sens_kernel<float, K_, 0><<<grid, 256, 0, st>>>(p)) }
+    } else {
+        if (n16) { SSM_DISPATCH_KPL(kpl, sens_kernel<bf16_t, K_, 16><<<grid, 256, 0, st>>>(p)) }
+        else { SSM_DISPATCH_KPL(kpl, sens_kernel<bf16_t, K_, 0><<<grid, 256, 0, st>>>(p)) }
+    }
     return hipGetLastError();
 }
 
