@@ -103,8 +103,8 @@ extern "C" {
  * Arguments of the diagonal scans.  Sizes: batch = B; channels = D (real) or
  * H heads (complex); length = L; state = N (real, 1..16) or M complex modes
  * per head (complex, 1..64).  chunk_len = checkpoint interval T in steps:
- * 0 picks the default (256 selective, 64 dense and complex); the selective
- * mode accepts 64, 128 or 256, the dense and complex modes 64.
+ * 0 picks the default (256 selective, 32 dense and complex); the selective
+ * mode accepts 64, 128 or 256, the dense and complex modes 32.
  * n_chunks = ceil(L / T).
  */
 typedef struct {

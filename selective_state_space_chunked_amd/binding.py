@@ -186,7 +186,7 @@ def _scan_args(mode, *, delta=None, x=None, A=None, Bm=None, a=None, b=None, C=N
 def _chunk(mode, chunk_len):
     if chunk_len:
         return chunk_len
-    return 256 if mode == SSM_REAL_SELECTIVE else 64
+    return 256 if mode == SSM_REAL_SELECTIVE else 32
 
 
 def scan_fwd(mode, *, want_y=True, want_h_last=False, want_ckpt=False, chunk_len=0, out=None, **tensors):

@@ -162,8 +162,8 @@ int validate_scan_args(const ssm_scan_args* a, ScanPlan* pl) {
             return fail(SSM_ERR_UNSUPPORTED, "chunk_len %d not supported (64, 128 or 256)", T);
         pl->kpl = T / 16;
     } else {
-        if (T == 0) T = 64;
-        if (T != 64) return fail(SSM_ERR_UNSUPPORTED, "chunk_len %d not supported (64)", T);
+        if (T == 0) T = 32;
+        if (T != 32) return fail(SSM_ERR_UNSUPPORTED, "chunk_len %d not supported (32)", T);
         pl->kpl = 0;
     }
     if (a->chunk_len < 0) return fail(SSM_ERR_SHAPE, "negative chunk_len");

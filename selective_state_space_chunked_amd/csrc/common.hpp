@@ -121,6 +121,21 @@ __device__ __forceinline__ int dpp_i(int old, int src) {
 template <int n>
 __device__ __forceinline__ float row_bcast(float v) { return dpp<SSM_DPP_ROW_BCAST(n)>(0.0f, v); }
 
+// Lane n of each row to the whole row, for an n that is a constant once the
+// caller's loop is fully unrolled (the switch then folds to one DPP move).
+__device__ __forceinline__ float bcast16(float v, int n) {
+    switch (n) {
+        case 0: return row_bcast<0>(v);   case 1: return row_bcast<1>(v);
+        case 2: return row_bcast<2>(v);   case 3: return row_bcast<3>(v);
+        case 4: return row_bcast<4>(v);   case 5: return row_bcast<5>(v);
+        case 6: return row_bcast<6>(v);   case 7: return row_bcast<7>(v);
+        case 8: return row_bcast<8>(v);   case 9: return row_bcast<9>(v);
+        case 10: return row_bcast<10>(v); case 11: return row_bcast<11>(v);
+        case 12: return row_bcast<12>(v); case 13: return row_bcast<13>(v);
+        case 14: return row_bcast<14>(v); default: return row_bcast<15>(v);
+    }
+}
+
 // Runtime lane index version (for loops that are not unrolled).
 __device__ __forceinline__ float row_bcast_rt(float v, int n) {
     int lane = threadIdx.x & 63;
@@ -228,6 +243,84 @@ __device__ __forceinline__ float wave_transpose_sum64(float (&v)[64]) {
 #pragma unroll
     for (int k = 0; k < 16; ++k) w[k] = v[k];
     return row_transpose_sum16(w);
+}
+
+// 32 slots across the 64 lanes of a wave: lanes 2i and 2i+1 return the sum
+// over all lanes of slot i.
+__device__ __forceinline__ float wave_transpose_sum32(float (&v)[32]) {
+    const int l = lane_id() & 15;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        auto s = __builtin_amdgcn_permlane32_swap(__float_as_int(v[k]), __float_as_int(v[k + 16]), false, false);
+        v[k] = __int_as_float(s[0]) + __int_as_float(s[1]);
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        auto s = __builtin_amdgcn_permlane16_swap(__float_as_int(v[k]), __float_as_int(v[k + 8]), false, false);
+        v[k] = __int_as_float(s[0]) + __int_as_float(s[1]);
+    }
+    float w[4], z[2];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) w[k] = pair_level<SSM_DPP_ROW_ROR(8)>(v[k], v[k + 4], (l & 8) != 0);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) z[k] = pair_level<SSM_DPP_ROW_HALF_MIRROR>(w[k], w[k + 2], (l & 4) != 0);
+    float q = pair_level<SSM_DPP_QUAD(2, 3, 0, 1)>(z[0], z[1], (l & 2) != 0);
+    return q + dpp<SSM_DPP_QUAD(1, 0, 3, 2)>(0.0f, q);
+}
+
+// ---------------------------------------------------------------------------
+// fp64 lane moves and transpose-reduction (both 32-bit words move together)
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ double dpp_d(double v) {
+    const long long b = __double_as_longlong(v);
+    const int lo = __builtin_amdgcn_update_dpp(0, (int)(b & 0xffffffffll), CTRL, 0xf, 0xf, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, (int)(b >> 32), CTRL, 0xf, 0xf, false);
+    return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+template <bool WIDE>
+__device__ __forceinline__ void permswap_d(double& x, double& y) {
+    const long long bx = __double_as_longlong(x), by = __double_as_longlong(y);
+    int xl = (int)(bx & 0xffffffffll), xh = (int)(bx >> 32), yl = (int)(by & 0xffffffffll), yh = (int)(by >> 32);
+    if (WIDE) {
+        auto l = __builtin_amdgcn_permlane32_swap(xl, yl, false, false);
+        auto h = __builtin_amdgcn_permlane32_swap(xh, yh, false, false);
+        xl = l[0]; yl = l[1]; xh = h[0]; yh = h[1];
+    } else {
+        auto l = __builtin_amdgcn_permlane16_swap(xl, yl, false, false);
+        auto h = __builtin_amdgcn_permlane16_swap(xh, yh, false, false);
+        xl = l[0]; yl = l[1]; xh = h[0]; yh = h[1];
+    }
+    x = __longlong_as_double(((long long)xh << 32) | (unsigned int)xl);
+    y = __longlong_as_double(((long long)yh << 32) | (unsigned int)yl);
+}
+template <int CTRL>
+__device__ __forceinline__ double pair_level_d(double lo, double up, bool hi) {
+    const double keep = hi ? up : lo;
+    const double send = hi ? lo : up;
+    return keep + dpp_d<CTRL>(send);
+}
+// 16 slots across the 64 lanes of a wave, in fp64: lanes 4i..4i+3 return the
+// sum over all lanes of slot i.
+__device__ __forceinline__ double wave_transpose_sum16_f64(double (&v)[16]) {
+    const int l = lane_id() & 15;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        permswap_d<true>(v[k], v[k + 8]);
+        v[k] = v[k] + v[k + 8];
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        permswap_d<false>(v[k], v[k + 4]);
+        v[k] = v[k] + v[k + 4];
+    }
+    double z[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) z[k] = pair_level_d<SSM_DPP_ROW_ROR(8)>(v[k], v[k + 2], (l & 8) != 0);
+    double q = pair_level_d<SSM_DPP_ROW_HALF_MIRROR>(z[0], z[1], (l & 4) != 0);
+    q = q + dpp_d<SSM_DPP_QUAD(1, 0, 3, 2)>(q);
+    q = q + dpp_d<SSM_DPP_QUAD(2, 3, 0, 1)>(q);
+    return q;
 }
 
 }  // namespace ssm

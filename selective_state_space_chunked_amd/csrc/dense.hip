@@ -1,0 +1,191 @@
+// Diagonal real scan with the transition diagonal a_t and input term b_t given
+// as (B,D,L,N) tensors (the generic h_t = a_t h_{t-1} + b_t, y_t = C_t . h_t).
+//
+// Work mapping.  This mode streams 8 bytes per element and does one fma, so it
+// is bound by HBM, not by arithmetic: a 16-lane row holds the N states of one
+// (batch, channel) and walks time sequentially, so every step of a row moves
+// one contiguous 64-byte line of a and of b.  y_t = sum_n C_t[n] h_t[n] is kept
+// per step for 16 steps and summed across the row with one transpose-reduction.
+// Segments of 32-step chunks along L run in parallel (summary / combine /
+// re-run, as for the other modes).  The backward recomputes each 32-step chunk
+// from its checkpoint into registers and runs the adjoint nu_t = a_t lambda_t
+// backwards; sums over channels (gC) are taken over the 16 rows in LDS.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace ssm {
+
+constexpr int kDChunk = 32;
+
+template <bool SUMMARY>
+__global__ __launch_bounds__(256) void dense_fwd_kernel(DenseParams p) {
+    const int tid = threadIdx.x, lane = tid & 15, row = tid >> 4;
+    const int b = blockIdx.y, g = blockIdx.z;
+    const int d = blockIdx.x * 16 + row;
+    const bool act = d < p.D;
+    const int dc = act ? d : p.D - 1;
+    const int N = p.N, L = p.L;
+    const bool nl = lane < N;
+    const int n = nl ? lane : N - 1;
+    const size_t seq = (size_t)b * p.D + dc;
+    float h = 0.0f, P = 1.0f;
+    if (!SUMMARY && nl) {
+        if (p.G > 1) h = p.carry_in[(seq * p.G + g) * N + n];
+        else if (p.h0) h = p.h0[seq * N + n];
+    }
+    const int c0 = g * p.chunks_per_seg;
+    const int c1 = min(c0 + p.chunks_per_seg, p.nchunks);
+    const float* arow = p.a + seq * L * N;
+    const float* brow = p.b + seq * L * N;
+    const float* crow = p.C + (size_t)b * L * N;
+    for (int ch = c0; ch < c1; ++ch) {
+        const int t0 = ch * kDChunk;
+        if (!SUMMARY && p.ckpt_out && act && nl) p.ckpt_out[(seq * p.nchunks + ch) * N + n] = h;
+#pragma unroll
+        for (int blk = 0; blk < kDChunk / 16; ++blk) {
+            float yp[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int t = t0 + 16 * blk + j;
+                yp[j] = 0.0f;
+                if (t < L) {
+                    const size_t o = (size_t)t * N + n;
+                    const float av = nl ? arow[o] : 1.0f;
+                    const float bv = nl ? brow[o] : 0.0f;
+                    h = fmaf(av, h, bv);
+                    if (SUMMARY) P *= av;
+                    else yp[j] = nl ? crow[o] * h : 0.0f;
+                }
+            }
+            if (!SUMMARY && p.y) {
+                const float ys = row_transpose_sum16(yp);
+                const int t = t0 + 16 * blk + lane;
+                if (act && t < L) p.y[seq * L + t] = ys;
+            }
+        }
+    }
+    if (!act || !nl) return;
+    if (SUMMARY) {
+        p.segP[(seq * p.G + g) * N + n] = P;
+        p.segS[(seq * p.G + g) * N + n] = h;
+    } else if (p.h_last && g == p.G - 1) {
+        p.h_last[seq * N + n] = h;
+    }
+}
+
+// gC partials of one chunk: [row][step][state] with rows padded by 16 floats
+constexpr int kDRedRow = kDChunk * 16 + 16;
+
+template <bool SUMMARY>
+__global__ __launch_bounds__(256) void dense_bwd_kernel(DenseParams p) {
+    __shared__ float red[SUMMARY ? 4 : 16 * kDRedRow];
+    const int tid = threadIdx.x, lane = tid & 15, row = tid >> 4;
+    const int b = blockIdx.y, g = blockIdx.z;
+    const int d = blockIdx.x * 16 + row;
+    const bool act = d < p.D;
+    const int dc = act ? d : p.D - 1;
+    const int N = p.N, L = p.L;
+    const bool nl = lane < N;
+    const int n = nl ? lane : N - 1;
+    const size_t seq = (size_t)b * p.D + dc;
+    float nu = 0.0f, Q = 1.0f;
+    if (!SUMMARY && nl) {
+        if (p.G > 1) nu = p.nu_in[(seq * p.G + g) * N + n];
+        else if (p.gh_last) nu = p.gh_last[seq * N + n];
+    }
+    const int c0 = g * p.chunks_per_seg;
+    const int c1 = min(c0 + p.chunks_per_seg, p.nchunks);
+    const float* arow = p.a + seq * L * N;
+    const float* brow = p.b + seq * L * N;
+    const float* crow = p.C + (size_t)b * L * N;
+    const float live = act ? 1.0f : 0.0f;
+    for (int ch = c1 - 1; ch >= c0; --ch) {
+        const int t0 = ch * kDChunk;
+        // gy of the chunk: lane l holds steps l and l + 16
+        float gyl[kDChunk / 16];
+#pragma unroll
+        for (int q = 0; q < kDChunk / 16; ++q) {
+            const int t = t0 + 16 * q + lane;
+            gyl[q] = t < L ? p.gy[seq * L + t] * live : 0.0f;
+        }
+        if (SUMMARY) {
+#pragma unroll
+            for (int jj = kDChunk - 1; jj >= 0; --jj) {
+                const int t = t0 + jj;
+                const float gyt = bcast16(gyl[jj / 16], jj % 16);
+                if (t < L && nl) {
+                    const size_t o = (size_t)t * N + n;
+                    const float av = arow[o];
+                    nu = av * fmaf(crow[o], gyt, nu);
+                    Q *= av;
+                }
+            }
+            continue;
+        }
+        float hs[kDChunk + 1], as[kDChunk];
+        hs[0] = nl ? p.ckpt[(seq * p.nchunks + ch) * N + n] : 0.0f;
+#pragma unroll
+        for (int j = 0; j < kDChunk; ++j) {
+            const int t = t0 + j;
+            as[j] = 1.0f;
+            hs[j + 1] = hs[j];
+            if (t < L && nl) {
+                const size_t o = (size_t)t * N + n;
+                as[j] = arow[o];
+                hs[j + 1] = fmaf(as[j], hs[j], brow[o]);
+            }
+        }
+        float* rrow = red + row * kDRedRow;
+#pragma unroll
+        for (int j = kDChunk - 1; j >= 0; --j) {
+            const int t = t0 + j;
+            const float gyt = bcast16(gyl[j / 16], j % 16);
+            float pc = 0.0f;
+            if (t < L && nl) {
+                const size_t o = (size_t)t * N + n;
+                const float lam = fmaf(crow[o], gyt, nu);
+                if (act) {
+                    if (p.ga) p.ga[seq * L * N + o] = lam * hs[j];
+                    if (p.gb) p.gb[seq * L * N + o] = lam;
+                }
+                pc = gyt * hs[j + 1];
+                nu = as[j] * lam;
+            }
+            if (p.partC) rrow[j * 16 + lane] = pc;
+        }
+        if (p.partC) {
+            __syncthreads();
+            for (int o = tid; o < kDChunk * 16; o += 256) {
+                const int tt = o / 16, nn = o % 16;
+                float s = 0.0f;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) s += red[r * kDRedRow + tt * 16 + nn];
+                const int t = t0 + tt;
+                if (t < L && nn < N) p.partC[(((size_t)blockIdx.x * p.B + b) * N + nn) * L + t] = s;
+            }
+            __syncthreads();
+        }
+    }
+    if (!act || !nl) return;
+    if (SUMMARY) {
+        p.segQ[(seq * p.G + g) * N + n] = Q;
+        p.segR[(seq * p.G + g) * N + n] = nu;
+    } else if (p.gh0 && g == 0) {
+        p.gh0[seq * N + n] = nu;
+    }
+}
+
+hipError_t launch_dense_fwd(const DenseParams& p, bool summary, hipStream_t st) {
+    dim3 grid((p.D + 15) / 16, p.B, p.G);
+    if (summary) dense_fwd_kernel<true><<<grid, 256, 0, st>>>(p);
+    else dense_fwd_kernel<false><<<grid, 256, 0, st>>>(p);
+    return hipGetLastError();
+}
+hipError_t launch_dense_bwd(const DenseParams& p, bool summary, hipStream_t st) {
+    dim3 grid((p.D + 15) / 16, p.B, p.G);
+    if (summary) dense_bwd_kernel<true><<<grid, 256, 0, st>>>(p);
+    else dense_bwd_kernel<false><<<grid, 256, 0, st>>>(p);
+    return hipGetLastError();
+}
+
+}  // namespace ssm

@@ -72,12 +72,13 @@ hipError_t launch_dense_bwd(const DenseParams& p, bool summary, hipStream_t st);
 struct CplxParams {
     const float* r; const float* phi; const float* lam; const float* theta;
     const float* u; const float* c; const float* h0;
-    const float* carry_in;   // (B,H,G,M) complex
-    const float* gy; const float* gh_last; const float* ckpt; const float* nu_in;
+    double* carry_in;        // (B,H,G,M) complex double, written by the combine pass
+    const float* gy; const float* gh_last; const float* ckpt;
+    double* nu_in;           // (B,H,G,M) complex double, written by the reverse combine pass
     float* y; float* h_last; float* ckpt_out;
-    float* segP; float* segS; float* segQ; float* segR;   // complex (B,H,G,M)
+    double* segP; double* segS; double* segQ; double* segR;   // complex double (B,H,G,M)
     float* gu; float* gr; float* gphi; float* gh0;
-    float* partL; float* partT; float* partC;             // (B,G,H,M) [partC complex]
+    double* partL; double* partT; double* partC;              // (B,G,H,M) [partC complex]
     int B, H, L, M, nchunks, chunk, chunks_per_seg, G;
 };
 hipError_t launch_cplx_fwd(const CplxParams& p, bool summary, hipStream_t st);
@@ -95,7 +96,8 @@ struct PDParams {
     const int32_t* sel;            // selection read by the later passes
     int8_t* pre;                   // (H,K,N,N) preimage lists, -1 padded
     int32_t* pre_cnt;              // (H,K,N)
-    int32_t* segPi; float* segD; float* segS;   // (B,H,G,N) chunk summaries
+    int32_t* segPi; float* segD; float* segS;   // (B,H,G,N) chunk summaries: forward local
+                                                // state, or in the backward the adjoint R
     float* carry_in;               // (B,H,G,N)
     float* nu_in;                  // (B,H,G,N)
     float* y; float* h_last; float* ckpt_out;

@@ -1,0 +1,185 @@
+"""GPU parity of the dense real, complex shared-control and PD scans against
+the fp64 oracle, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests._compare import F32, assert_close
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def T(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def _ssm():
+    import selective_state_space_chunked_amd as ssm
+    return ssm
+
+
+# ---------------------------------------------------------------------------
+# dense real
+# ---------------------------------------------------------------------------
+def run_dense(B, D, L, N, seed, h0=False, ghl=False):
+    ssm = _ssm()
+    g = np.random.default_rng(seed)
+    a = g.uniform(0.5, 1.0, (B, D, L, N)).astype(np.float32)
+    b = (g.standard_normal((B, D, L, N)) / 4).astype(np.float32)
+    C = (g.standard_normal((B, L, N)) / 4).astype(np.float32)
+    gy = g.standard_normal((B, D, L)).astype(np.float32)
+    hh = g.standard_normal((B, D, N)).astype(np.float32) if h0 else None
+    gl = g.standard_normal((B, D, N)).astype(np.float32) if ghl else None
+    t = dict(a=T(a), b=T(b), C=T(C), h0=None if hh is None else T(hh))
+    f = ssm.scan_fwd(ssm.SSM_REAL_DENSE, want_h_last=True, want_ckpt=True, **t)
+    gr = ssm.scan_bwd(ssm.SSM_REAL_DENSE, gy=T(gy), ckpt=f["ckpt"], gh_last=None if gl is None else T(gl), **t)
+    gr2 = ssm.scan_bwd(ssm.SSM_REAL_DENSE, gy=T(gy), gh_last=None if gl is None else T(gl), **t)
+    torch.cuda.synchronize()
+    y, hl = oracle.real_fwd(a=a, b=b, C=C, h0=hh, B=B, D=D, L=L, N=N)
+    og = oracle.real_bwd(a=a, b=b, C=C, h0=hh, gy=gy, ghlast=gl, B=B, D=D, L=L, N=N)
+    assert_close("y", f["y"], y, **F32)
+    assert_close("h_last", f["h_last"], hl, **F32)
+    for k in ("ga", "gb", "gC", "gh0"):
+        assert_close(k, gr[k], og[k], **F32)
+        assert torch.equal(gr[k], gr2[k]), k
+
+
+@pytest.mark.parametrize("L", [1, 31, 32, 33, 500])
+def test_dense_lengths(L):
+    run_dense(2, 20, L, 16, seed=L, h0=True, ghl=True)
+
+
+def test_dense_small_state():
+    run_dense(1, 5, 200, 3, seed=3)
+
+
+def test_dense_many_segments():
+    run_dense(1, 16, 3000, 16, seed=4, h0=True)
+
+
+# ---------------------------------------------------------------------------
+# complex
+# ---------------------------------------------------------------------------
+def run_complex(cfg, h0=None, ghl=None):
+    ssm = _ssm()
+    B, H, L, M = cfg["B"], cfg["H"], cfg["L"], cfg["M"]
+    t = {k: T(cfg[k]) for k in ("r", "phi", "lam", "theta", "u", "c")}
+    if h0 is not None:
+        t["h0"] = T(h0.astype(np.complex64))
+    gyt = T(cfg["gy"])
+    glt = None if ghl is None else T(ghl.astype(np.complex64))
+    f = ssm.scan_fwd(ssm.SSM_COMPLEX_SHARED, want_h_last=True, want_ckpt=True, **t)
+    g = ssm.scan_bwd(ssm.SSM_COMPLEX_SHARED, gy=gyt, ckpt=f["ckpt"], gh_last=glt, **t)
+    g2 = ssm.scan_bwd(ssm.SSM_COMPLEX_SHARED, gy=gyt, gh_last=glt, **t)
+    torch.cuda.synchronize()
+    kw = {k: cfg[k] for k in ("r", "phi", "lam", "theta", "u", "c")}
+    h0c = None if h0 is None else h0.astype(np.complex64)
+    y, hl = oracle.complex_fwd(**kw, h0=h0c, B=B, H=H, L=L, M=M)
+    og = oracle.complex_bwd(**kw, h0=h0c, gy=cfg["gy"], ghlast=None if ghl is None else ghl.astype(np.complex64),
+                            B=B, H=H, L=L, M=M)
+    errs = {"y": assert_close("y", f["y"], y, **F32), "h_last": assert_close("h_last", f["h_last"], hl, **F32)}
+    for k in ("gu", "gr", "gphi", "glam", "gtheta", "gc", "gh0"):
+        errs[k] = assert_close(k, g[k], og[k], **F32)
+        assert torch.equal(g[k], g2[k]), k
+    return errs
+
+
+def test_complex_small():
+    cfg = synth.make_complex(B=2, H=3, M=64, L=300, seed=1)
+    g = np.random.default_rng(5)
+    run_complex(cfg, h0=g.standard_normal((2, 3, 64)) + 1j * g.standard_normal((2, 3, 64)),
+                ghl=g.standard_normal((2, 3, 64)) + 1j * g.standard_normal((2, 3, 64)))
+
+
+@pytest.mark.parametrize("M,L", [(5, 100), (64, 1), (64, 33), (32, 64)])
+def test_complex_shapes(M, L):
+    run_complex(synth.make_complex(B=1, H=2, M=M, L=L, seed=M + L))
+
+
+def test_complex_full_config():
+    """B=16 H=8 M=64 L=2048 complex64, seed 0: every output compared element-wise."""
+    run_complex(synth.make_complex(B=16, H=8, M=64, L=2048, seed=0))
+
+
+# ---------------------------------------------------------------------------
+# PD
+# ---------------------------------------------------------------------------
+def run_pd(cfg, h0=None, ghl=None, use_sel=False):
+    ssm = _ssm()
+    B, H, L, N, K = cfg["B"], cfg["H"], cfg["L"], cfg["N"], cfg["K"]
+    osel = oracle.pd_select(cfg["logits"])
+    t = dict(dict=T(cfg["dict"]), d=T(cfg["d"]), b=T(cfg["b"]), C=T(cfg["C"]))
+    if use_sel:
+        t["sel"] = T(osel)
+    else:
+        t["logits"] = T(cfg["logits"])
+    if h0 is not None:
+        t["h0"] = T(h0.astype(np.float32))
+    gyt = T(cfg["gy"])
+    glt = None if ghl is None else T(ghl.astype(np.float32))
+    f = ssm.pd_scan_fwd(want_h_last=True, want_ckpt=True, **t)
+    g = ssm.pd_scan_bwd(gy=gyt, ckpt=f["ckpt"], gh_last=glt, **t)
+    g2 = ssm.pd_scan_bwd(gy=gyt, gh_last=glt, **t)
+    torch.cuda.synchronize()
+    assert np.array_equal(f["sel"].cpu().numpy(), osel), "selection indices differ"
+    kw = dict(sel=osel, dict=cfg["dict"], d=cfg["d"], b=cfg["b"], C=cfg["C"],
+              h0=None if h0 is None else h0.astype(np.float32), B=B, H=H, L=L, N=N, K=K)
+    y, hl = oracle.pd_fwd(**kw)
+    og = oracle.pd_bwd(**kw, gy=cfg["gy"], ghlast=None if ghl is None else ghl.astype(np.float32))
+    assert_close("y", f["y"], y, **F32)
+    assert_close("h_last", f["h_last"], hl, **F32)
+    for k in ("gd", "gb", "gC", "gh0"):
+        assert_close(k, g[k], og[k], **F32)
+        assert torch.equal(g[k], g2[k]), k
+
+
+def test_pd_small():
+    cfg = synth.make_pd(B=2, H=3, N=16, L=500, K=8, seed=1)
+    g = np.random.default_rng(2)
+    run_pd(cfg, h0=g.standard_normal((2, 3, 16)), ghl=g.standard_normal((2, 3, 16)))
+
+
+@pytest.mark.parametrize("N,K,L", [(16, 8, 1), (16, 8, 64), (16, 8, 65), (5, 3, 300), (16, 64, 200), (1, 1, 130)])
+def test_pd_shapes(N, K, L):
+    run_pd(synth.make_pd(B=1, H=2, N=N, L=L, K=K, seed=N * 100 + K + L))
+
+
+def test_pd_given_selection():
+    run_pd(synth.make_pd(B=1, H=2, N=16, L=777, K=8, seed=9), use_sel=True)
+
+
+def test_pd_ties_lowest_index():
+    cfg = synth.make_pd(B=1, H=2, N=16, L=300, K=8, seed=10)
+    cfg["logits"] = np.round(cfg["logits"]).astype(np.float32)  # many exact ties
+    run_pd(cfg)
+
+
+def test_pd_dfa_exact():
+    """Dictionary read as a 16-state automaton: d = 1, b = 0, h0 = e_q0 gives y_t = 2^{q_t} exactly."""
+    ssm = _ssm()
+    cfg = synth.make_pd(B=2, H=4, N=16, L=3000, K=8, seed=11)
+    B, H, L, N = 2, 4, 3000, 16
+    q0 = np.array([[3, 0, 15, 7], [1, 2, 9, 11]])
+    h0 = np.zeros((B, H, N), np.float32)
+    for bi in range(B):
+        for hi in range(H):
+            h0[bi, hi, q0[bi, hi]] = 1
+    C = np.broadcast_to((2.0 ** np.arange(N)).astype(np.float32), (B, H, L, N)).copy()
+    f = ssm.pd_scan_fwd(logits=T(cfg["logits"]), dict=T(cfg["dict"]), d=T(np.ones((B, H, L, N), np.float32)),
+                        b=T(np.zeros((B, H, L, N), np.float32)), C=T(C), h0=T(h0))
+    sel = f["sel"].cpu().numpy()
+    y = f["y"].cpu().numpy()
+    for bi in range(B):
+        for hi in range(H):
+            q = q0[bi, hi]
+            for t in range(L):
+                q = cfg["dict"][hi, sel[bi, hi, t], q]
+                assert y[bi, hi, t] == 2.0 ** q
+
+
+def test_pd_full_config():
+    """B=8 H=32 N=16 L=17000 K=8, seed 0: selection bit-exact, values element-wise."""
+    run_pd(synth.make_pd(B=8, H=32, N=16, L=17000, K=8, seed=0))
