@@ -5,20 +5,23 @@ A step is one forward + backward pass (every hot-path kernel) over one batch
 of seeded synthetic inputs.  The headline workload is the Mamba-layer-shaped
 selective scan B=8 D=2048 N=16 L=4096 with bf16 streams, fp32 state and
 accumulation, chunk length 256; value = B*D*N*L / (time of forward+backward).
+The other workloads (impulse sensitivity at L=128000, complex shared-control
+scan, PD scan, dense-a/b scan at the Mamba-layer shape, the small fp32 case)
+are reported under "others" with the same fields.
 
 Inputs are resident in HBM before timing.  The timed region is K steps
 bracketed by torch.cuda.synchronize(); per-kernel durations come from HIP
 events the library records around each of its launches on the same stream
 (ssm_profile_begin / ssm_profile_end), in a separate pass after the timed one.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-others]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+                       [--no-others | --workloads a,b,...] [--calib-copy]
 """
 from __future__ import annotations
 
 import argparse
 import ctypes
 import json
-import math
 import os
 import sys
 import time
@@ -28,10 +31,20 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-HBM_PEAK = 8.0e12          # MI355X HBM3E, bytes/s
+HBM_PEAK = 8.0e12  # MI355X HBM3E, bytes/s
+# fp32 vector peak without packed fp32: 256 CUs x 4 SIMDs x 16 lanes x 2 flops x 2.4 GHz
+VALU_F32_PEAK = 256 * 4 * 16 * 2 * 2.4e9
 METRIC = "scan elements/s (B·D·N·L) fwd+bwd at 1 GPU; % of HBM peak BW"
-# Vector ALU peak with packed fp32 disabled: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
-VALU_PEAK_OPS = 256 * 4 * 16 * 2.4e9
+HEADLINE = "real-mamba"
+
+# Algorithmic flops per scan element (the recurrence's arithmetic, exp counted
+# as one operation, fused multiply-add as two):
+#   forward:  delta*A, exp, (delta x)*B, a*h + b, y += C*h                      = 7
+#   backward: recompute (delta*A, exp, (delta x)*B, a*h + b)                   = 5
+#             lambda = C*gy + nu, nu = a*lambda                                 = 3
+#             gdelta += A*lambda*(a*h_prev), gx term += lambda*B                = 5
+#             gB += lambda*(delta x), gC += gy*h (products + channel sums)      = 4   -> 17
+FLOPS_PER_ELEMENT = {"selective forward": 7, "selective backward": 17}
 
 
 def parse():
@@ -40,15 +53,19 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--no-others", action="store_true", help="skip the secondary workloads")
-    ap.add_argument("--cpu-batches", type=int, default=8, help="batch rows of the headline workload in the CPU sample")
+    ap.add_argument("--no-others", action="store_true", help="only the headline workload")
+    ap.add_argument("--workloads", default="", help="comma list of secondary workloads to run")
+    ap.add_argument("--cpu-batches", type=int, default=8, help="batch rows of the headline in the CPU sample")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run one 1 GiB device copy (calibrates HBM byte counters)")
     return ap.parse_args()
 
 
 # ---------------------------------------------------------------------------
-# per-kernel timing through the library's event hook
+# timing helpers
 # ---------------------------------------------------------------------------
-def profile_kernels(fn, reps=5, cap=4096):
+def profile_kernels(fn, reps=5, cap=8192):
+    """Average duration (ms) and launches per call of every kernel fn enqueues."""
     import torch
     from selective_state_space_chunked_amd import lib
     L = lib()
@@ -65,9 +82,8 @@ def profile_kernels(fn, reps=5, cap=4096):
     assert L.ssm_profile_end(ctypes.byref(n), ms, names, cap) == 0
     agg = {}
     for i in range(n.value):
-        k = names[i].decode()
-        agg.setdefault(k, []).append(ms[i])
-    return {k: (sum(v) / len(v), len(v) // reps) for k, v in agg.items()}
+        agg.setdefault(names[i].decode(), []).append(ms[i])
+    return {k: (sum(v) / len(v), len(v) / reps) for k, v in agg.items()}
 
 
 def time_steps(step, steps, warmup):
@@ -90,46 +106,44 @@ def to_dev(arr, bf16=False):
 
 
 # ---------------------------------------------------------------------------
-# workloads
+# workloads: each returns elements, ms per step, kernel times, algorithmic bytes
 # ---------------------------------------------------------------------------
-def real_workload(name, shape, dtype, steps, warmup):
-    """Selective real scan, forward + backward (gradients w.r.t. delta, x, B, C)."""
+def w_real(name, B, D, N, L, dtype, steps, warmup, keep_inputs=False):
+    """Selective real scan forward + backward (gradients w.r.t. delta, x, B, C)."""
     import synth
     import selective_state_space_chunked_amd as ssm
-    B, D, N, L = shape["B"], shape["D"], shape["N"], shape["L"]
     cfg = synth.make_real(B=B, D=D, N=N, L=L, dtype=dtype, seed=0)
     bf = dtype == "bf16"
     t = {k: to_dev(cfg[k], bf) for k in ("delta", "x", "Bm", "C")}
     t["A"] = to_dev(cfg["A"])
     gy = to_dev(cfg["gy"], bf)
-    es = 2 if bf else 4
-    fwd_out = ssm.scan_fwd(ssm.SSM_REAL_SELECTIVE, want_ckpt=True, **t)
-    grads = ssm.scan_bwd(ssm.SSM_REAL_SELECTIVE, gy=gy, ckpt=fwd_out["ckpt"], want=("gdelta", "gx", "gBm", "gC"), **t)
+    want = ("gdelta", "gx", "gBm", "gC")
+    fo = ssm.scan_fwd(ssm.SSM_REAL_SELECTIVE, want_ckpt=True, **t)
+    go = ssm.scan_bwd(ssm.SSM_REAL_SELECTIVE, gy=gy, ckpt=fo["ckpt"], want=want, **t)
 
     def step():
-        ssm.scan_fwd(ssm.SSM_REAL_SELECTIVE, want_ckpt=True, out=fwd_out, **t)
-        ssm.scan_bwd(ssm.SSM_REAL_SELECTIVE, gy=gy, ckpt=fwd_out["ckpt"], want=("gdelta", "gx", "gBm", "gC"),
-                     out=grads, **t)
+        ssm.scan_fwd(ssm.SSM_REAL_SELECTIVE, want_ckpt=True, out=fo, **t)
+        ssm.scan_bwd(ssm.SSM_REAL_SELECTIVE, gy=gy, ckpt=fo["ckpt"], want=want, out=go, **t)
 
     ms = time_steps(step, steps, warmup)
-    kern = profile_kernels(step)
+    es = 2 if bf else 4
     nc = -(-L // 256)
-    BDL, BLN = B * D * L, B * L * N
-    ck = B * D * nc * N * 4
-    fwd_bytes = 2 * BDL * es + 2 * BLN * es + D * N * 4 + BDL * es + ck
-    bwd_kernel_bytes = 3 * BDL * es + 2 * BLN * es + D * N * 4 + ck + 2 * BDL * es
-    bwd_bytes = bwd_kernel_bytes + 2 * BLN * es
-    return dict(name=name, elements=B * D * N * L, ms=ms, kernels=kern,
-                bytes=dict(total=fwd_bytes + bwd_bytes, fwd=fwd_bytes, bwd=bwd_bytes,
-                           per_kernel={"selective forward": fwd_bytes, "selective backward": bwd_kernel_bytes}),
-                config=dict(B=B, D=D, N=N, L=L, streams=dtype, chunk_len=256), inputs=cfg)
+    BDL, BLN, ck = B * D * L, B * L * N, B * D * nc * N * 4
+    fwd = 3 * BDL * es + 2 * BLN * es + D * N * 4 + ck            # read delta, x, B, C, A; write y, ckpt
+    bwd_k = 5 * BDL * es + 2 * BLN * es + D * N * 4 + ck          # read delta, x, gy, B, C, A, ckpt; write gdelta, gx
+    bwd = bwd_k + 2 * BLN * es                                    # + write gB, gC
+    return dict(name=name, elements=B * D * N * L, ms=ms, kernels=profile_kernels(step),
+                bytes_total=fwd + bwd, bytes_kernel={"selective forward": fwd, "selective backward": bwd_k},
+                config=dict(B=B, D=D, N=N, L=L, streams=dtype, chunk_len=256),
+                inputs=cfg if keep_inputs else None)
 
 
-def impulse_workload(steps, warmup):
-    """Impulse response + full sensitivity, B=1 D=1024 N=16 L=128000 fp32."""
+def w_impulse(steps, warmup):
+    """Impulse response y and sensitivity dy[L-1]/dx[t], B=1 D=1024 N=16 L=128000 fp32."""
     import synth
     import selective_state_space_chunked_amd as ssm
-    cfg = synth.make_impulse(B=1, D=1024, N=16, L=128000, seed=0)
+    B, D, N, L = 1, 1024, 16, 128000
+    cfg = synth.make_impulse(B=B, D=D, N=N, L=L, seed=0)
     t = {k: to_dev(cfg[k]) for k in ("delta", "x", "Bm", "C", "A")}
     out = ssm.impulse_sensitivity(**t)
 
@@ -137,18 +151,94 @@ def impulse_workload(steps, warmup):
         ssm.impulse_sensitivity(out=out, **t)
 
     ms = time_steps(step, max(3, steps // 4), max(1, warmup // 2))
-    BDL, BLN = 1024 * 128000, 128000 * 16
-    byts = 2 * BDL * 4 + 2 * BLN * 4 + BDL * 4 + (BDL * 4 + BLN * 4 + BDL * 4)
-    return dict(name="impulse", elements=BDL * 16, ms=ms, kernels=profile_kernels(step, reps=2),
-                bytes=dict(total=byts), config=dict(B=1, D=1024, N=16, L=128000, streams="f32"))
+    BDL, BLN = B * D * L, B * L * N
+    byts = (2 * BDL + 2 * BLN + BDL) * 4 + (BDL + BLN + BDL) * 4  # forward: x, delta, B, C -> y; sens: delta, B -> s
+    return dict(name="impulse", elements=BDL * N, ms=ms, kernels=profile_kernels(step, reps=2),
+                bytes_total=byts, config=dict(B=B, D=D, N=N, L=L, streams="f32", t_out=L - 1))
+
+
+def w_complex(steps, warmup):
+    """Complex shared-control scan, B=16 H=8 M=64 L=2048, forward + backward."""
+    import synth
+    import selective_state_space_chunked_amd as ssm
+    B, H, M, L = 16, 8, 64, 2048
+    cfg = synth.make_complex(B=B, H=H, M=M, L=L, seed=0)
+    t = {k: to_dev(cfg[k]) for k in ("r", "phi", "lam", "theta", "u", "c")}
+    gy = to_dev(cfg["gy"])
+    fo = ssm.scan_fwd(ssm.SSM_COMPLEX_SHARED, want_ckpt=True, **t)
+    go = ssm.scan_bwd(ssm.SSM_COMPLEX_SHARED, gy=gy, ckpt=fo["ckpt"], **t)
+
+    def step():
+        ssm.scan_fwd(ssm.SSM_COMPLEX_SHARED, want_ckpt=True, out=fo, **t)
+        ssm.scan_bwd(ssm.SSM_COMPLEX_SHARED, gy=gy, ckpt=fo["ckpt"], out=go, **t)
+
+    ms = time_steps(step, steps, warmup)
+    BHL, E = B * H * L, B * H * L * M
+    ck = B * H * (-(-L // 32)) * M * 8
+    fwd = E * 8 + 2 * BHL * 4 + BHL * 4 + ck                       # read u, r, phi; write y, ckpt
+    bwd = E * 8 + 3 * BHL * 4 + ck + E * 8 + 2 * BHL * 4            # read u, r, phi, gy, ckpt; write gu, gr, gphi
+    return dict(name="complex", elements=E, ms=ms, kernels=profile_kernels(step), bytes_total=fwd + bwd,
+                config=dict(B=B, H=H, M=M, L=L, streams="complex64", chunk_len=32))
+
+
+def w_pd(steps, warmup):
+    """PD scan, B=8 H=32 N=16 L=17000 K=8, forward (with selection) + backward."""
+    import synth
+    import selective_state_space_chunked_amd as ssm
+    B, H, N, L, K = 8, 32, 16, 17000, 8
+    cfg = synth.make_pd(B=B, H=H, N=N, L=L, K=K, seed=0)
+    t = {k: to_dev(cfg[k]) for k in ("logits", "dict", "d", "b", "C")}
+    gy = to_dev(cfg["gy"])
+    fo = ssm.pd_scan_fwd(want_ckpt=True, **t)
+    tb = dict(t)
+    tb.pop("logits")
+    go = ssm.pd_scan_bwd(gy=gy, ckpt=fo["ckpt"], sel=fo["sel"], **tb)
+
+    def step():
+        ssm.pd_scan_fwd(want_ckpt=True, out=fo, **t)
+        ssm.pd_scan_bwd(gy=gy, ckpt=fo["ckpt"], sel=fo["sel"], out=go, **tb)
+
+    ms = time_steps(step, steps, warmup)
+    BHL, E = B * H * L, B * H * L * N
+    ck = B * H * (-(-L // 64)) * N * 4
+    fwd = BHL * K * 4 + 3 * E * 4 + BHL * 4 * 2 + ck               # read logits, d, b, C; write y, sel, ckpt
+    bwd = BHL * 4 + 3 * E * 4 + BHL * 4 + ck + 3 * E * 4            # read sel, d, b, C, gy, ckpt; write gd, gb, gC
+    return dict(name="pd", elements=E, ms=ms, kernels=profile_kernels(step), bytes_total=fwd + bwd,
+                config=dict(B=B, H=H, N=N, L=L, K=K, chunk_len=64))
+
+
+def w_dense(steps, warmup):
+    """Dense a_t, b_t scan at the Mamba-layer shape B=8 D=2048 N=16 L=4096, fp32."""
+    import torch
+    import selective_state_space_chunked_amd as ssm
+    B, D, N, L = 8, 2048, 16, 4096
+    gen = torch.Generator(device="cuda").manual_seed(0)
+    a = torch.rand((B, D, L, N), device="cuda", generator=gen) * 0.5 + 0.5
+    b = torch.randn((B, D, L, N), device="cuda", generator=gen) * 0.25
+    C = torch.randn((B, L, N), device="cuda", generator=gen) * 0.25
+    gy = torch.randn((B, D, L), device="cuda", generator=gen)
+    t = dict(a=a, b=b, C=C)
+    fo = ssm.scan_fwd(ssm.SSM_REAL_DENSE, want_ckpt=True, **t)
+    go = ssm.scan_bwd(ssm.SSM_REAL_DENSE, gy=gy, ckpt=fo["ckpt"], **t)
+
+    def step():
+        ssm.scan_fwd(ssm.SSM_REAL_DENSE, want_ckpt=True, out=fo, **t)
+        ssm.scan_bwd(ssm.SSM_REAL_DENSE, gy=gy, ckpt=fo["ckpt"], out=go, **t)
+
+    ms = time_steps(step, max(3, steps // 4), max(1, warmup // 2))
+    E, BDL, BLN = B * D * L * N, B * D * L, B * L * N
+    ck = B * D * (L // 32) * N * 4
+    fwd = 2 * E * 4 + BLN * 4 + BDL * 4 + ck                       # read a, b, C; write y, ckpt
+    bwd = 2 * E * 4 + BLN * 4 + BDL * 4 + ck + 2 * E * 4 + BLN * 4  # read a, b, C, gy, ckpt; write ga, gb, gC
+    return dict(name="dense", elements=E, ms=ms, kernels=profile_kernels(step, reps=2), bytes_total=fwd + bwd,
+                config=dict(B=B, D=D, N=N, L=L, streams="f32", chunk_len=32, data="torch-generated on device"))
 
 
 def summarize(w):
     ms = w["ms"]
-    r = dict(el_per_s=w["elements"] / (ms * 1e-3), ms_per_step=ms,
-             hbm_frac=w["bytes"]["total"] / (ms * 1e-3) / HBM_PEAK, config=w["config"],
-             kernels_ms={k: round(v[0], 4) for k, v in w["kernels"].items()})
-    return r
+    return dict(el_per_s=w["elements"] / (ms * 1e-3), ms_per_step=ms,
+                hbm_frac=w["bytes_total"] / (ms * 1e-3) / HBM_PEAK, algorithmic_bytes=w["bytes_total"],
+                config=w["config"], kernels_ms={k: round(v[0], 4) for k, v in w["kernels"].items()})
 
 
 def cpu_baseline(inputs, batches):
@@ -168,6 +258,18 @@ def cpu_baseline(inputs, batches):
                       f"forward + backward in fp64, {dt:.1f} s wall"}
 
 
+def calib_copy():
+    """One device copy of exactly 1 GiB (reads 1 GiB, writes 1 GiB)."""
+    import torch
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -178,20 +280,34 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
-    head = real_workload("real-mamba", dict(B=8, D=2048, N=16, L=4096), "bf16", args.steps, args.warmup)
+    if args.calib_copy:
+        calib_copy()
+    head = w_real(HEADLINE, 8, 2048, 16, 4096, "bf16", args.steps, args.warmup, keep_inputs=not args.no_cpu)
     s = summarize(head)
     kern = head["kernels"]
-    # dominant kernel by time
-    dom = max(kern, key=lambda k: kern[k][0] * kern[k][1])
+    dom = max((k for k in kern if k in head["bytes_kernel"]), key=lambda k: kern[k][0] * kern[k][1])
     dur = kern[dom][0] * 1e-3
-    byts = head["bytes"]["per_kernel"].get(dom)
-    roof = {"kernel": dom, "bound": "hbm", "achieved": byts / dur / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-            "frac": byts / dur / HBM_PEAK, "traffic": None, "duration_ms": kern[dom][0]}
+    flops = FLOPS_PER_ELEMENT[dom] * head["elements"]
+    roof = {"kernel": dom, "bound": "alu", "achieved": flops / dur / 1e12, "peak": VALU_F32_PEAK / 1e12,
+            "unit": "TFLOP/s", "frac": flops / dur / VALU_F32_PEAK, "traffic": None,
+            "duration_ms": kern[dom][0], "hbm_frac": head["bytes_kernel"][dom] / dur / HBM_PEAK,
+            "flops_per_element": FLOPS_PER_ELEMENT[dom]}
     others = {}
     if not args.no_others:
-        others["impulse"] = summarize(impulse_workload(args.steps, args.warmup))
-        small = real_workload("real-small", dict(B=1, D=16, N=16, L=1024), "f32", args.steps, args.warmup)
-        others["real-small"] = summarize(small)
+        todo = [w.strip() for w in args.workloads.split(",") if w.strip()] or \
+            ["impulse", "complex", "pd", "dense", "real-small"]
+        for w in todo:
+            if w == "impulse":
+                others[w] = summarize(w_impulse(args.steps, args.warmup))
+            elif w == "complex":
+                others[w] = summarize(w_complex(args.steps, args.warmup))
+            elif w == "pd":
+                others[w] = summarize(w_pd(args.steps, args.warmup))
+            elif w == "dense":
+                others[w] = summarize(w_dense(args.steps, args.warmup))
+            elif w == "real-small":
+                others[w] = summarize(w_real(w, 1, 16, 16, 1024, "f32", args.steps, args.warmup))
+            torch.cuda.empty_cache()
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(head["inputs"], args.cpu_batches)
@@ -201,7 +317,7 @@ def main():
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": "real-mamba: selective scan fwd+bwd, B=8 D=2048 N=16 L=4096, bf16 streams, "
                                "fp32 state, chunk 256", **head["config"]},
-        "hbm_frac": s["hbm_frac"], "algorithmic_bytes_per_step": head["bytes"]["total"],
+        "hbm_frac": s["hbm_frac"], "algorithmic_bytes_per_step": head["bytes_total"],
         "kernels_ms": s["kernels_ms"], "roofline": roof, "cpu_baseline": cpu, "others": others,
     }
     print(json.dumps(line))

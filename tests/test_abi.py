@@ -1,0 +1,159 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function the
+header declares, and rejects invalid arguments on the host before anything is
+enqueued (no compute call reaches the device here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from selective_state_space_chunked_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssmscan.h")
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(\w+)\s*\(", src, flags=re.M)))
+
+
+def test_exports_every_declared_function():
+    names = header_functions()
+    assert {"ssm_scan_fwd", "ssm_scan_bwd", "ssm_impulse_sensitivity", "pd_scan_fwd", "pd_scan_bwd",
+            "ssm_workspace_bytes"} <= set(names)
+    lib = B.lib()
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_header_constants_match_binding():
+    src = open(HEADER).read()
+    consts = dict((k, int(v)) for k, v in re.findall(r"#define\s+(SSM_\w+)\s+(-?\d+)", src))
+    assert consts["SSM_F32"] == B.SSM_F32 and consts["SSM_BF16"] == B.SSM_BF16
+    assert consts["SSM_REAL_SELECTIVE"] == B.SSM_REAL_SELECTIVE
+    assert consts["SSM_REAL_DENSE"] == B.SSM_REAL_DENSE
+    assert consts["SSM_COMPLEX_SHARED"] == B.SSM_COMPLEX_SHARED
+    assert consts["SSM_OP_PD_BWD"] == B.SSM_OP_PD_BWD
+    assert B.lib().ssm_abi_version() == consts["SSM_ABI_VERSION"]
+
+
+def test_struct_layouts():
+    # 2 x int32 + 5 x int64 + 14 pointers
+    assert ctypes.sizeof(B.ScanArgs) == 8 + 5 * 8 + 14 * 8
+    assert ctypes.sizeof(B.ScanGrads) == 14 * 8
+    assert ctypes.sizeof(B.PDArgs) == 6 * 8 + 7 * 8
+
+
+FAKE = 1 << 20  # never dereferenced: validation fails or only sizes are computed
+
+
+def sel_args(**over):
+    a = B.ScanArgs(mode=B.SSM_REAL_SELECTIVE, dtype=B.SSM_F32, batch=2, channels=32, length=1000, state=16,
+                   chunk_len=0, delta=FAKE, x=FAKE * 2, A=FAKE * 3, Bm=FAKE * 4, C=FAKE * 5)
+    for k, v in over.items():
+        setattr(a, k, v)
+    return a
+
+
+def ws_bytes(op, args):
+    n = ctypes.c_size_t(123)
+    rc = B.lib().ssm_workspace_bytes(op, ctypes.byref(args), ctypes.byref(n))
+    return rc, n.value
+
+
+def status(name):
+    src = open(HEADER).read()
+    return int(re.search(r"#define\s+%s\s+(-?\d+)" % name, src).group(1))
+
+
+def test_workspace_query_valid():
+    for op in (B.SSM_OP_SCAN_FWD, B.SSM_OP_SCAN_BWD, B.SSM_OP_IMPULSE):
+        rc, n = ws_bytes(op, sel_args())
+        assert rc == 0, B.lib().ssm_last_error_detail()
+        assert n > 0 and n % 1 == 0
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(delta=None), "SSM_ERR_NULL"),
+    (dict(C=None), "SSM_ERR_NULL"),
+    (dict(batch=0), "SSM_ERR_SHAPE"),
+    (dict(length=0), "SSM_ERR_SHAPE"),
+    (dict(state=17), "SSM_ERR_SHAPE"),
+    (dict(dtype=7), "SSM_ERR_DTYPE"),
+    (dict(mode=9), "SSM_ERR_UNSUPPORTED"),
+    (dict(chunk_len=100), "SSM_ERR_UNSUPPORTED"),
+    (dict(x=FAKE * 2 + 2), "SSM_ERR_LAYOUT"),
+])
+def test_validation_errors(over, code):
+    rc, _ = ws_bytes(B.SSM_OP_SCAN_FWD, sel_args(**over))
+    assert rc == status(code), (rc, B.lib().ssm_last_error_detail())
+    assert B.lib().ssm_last_error_detail()
+    assert B.lib().ssm_status_string(rc).decode() == code
+
+
+def test_bf16_only_for_selective():
+    a = sel_args(mode=B.SSM_REAL_DENSE, dtype=B.SSM_BF16, a=FAKE * 6, b=FAKE * 7)
+    rc, _ = ws_bytes(B.SSM_OP_SCAN_FWD, a)
+    assert rc == status("SSM_ERR_DTYPE")
+
+
+def test_errors_before_enqueue():
+    """Entry points reject bad calls without touching the device."""
+    L = B.lib()
+    a = sel_args()
+    out = B.ScanFwdOut(y=FAKE * 2 + 64, h_last=None, ckpt=None)  # y overlaps x
+    rc = L.ssm_scan_fwd(ctypes.byref(a), ctypes.byref(out), None, 0, None)
+    assert rc == status("SSM_ERR_LAYOUT"), L.ssm_last_error_detail()
+    out = B.ScanFwdOut(y=FAKE * 64, h_last=None, ckpt=None)
+    rc = L.ssm_scan_fwd(ctypes.byref(a), ctypes.byref(out), None, 0, None)  # no workspace
+    assert rc == status("SSM_ERR_WORKSPACE"), L.ssm_last_error_detail()
+    rc = L.ssm_scan_fwd(ctypes.byref(a), ctypes.byref(out), FAKE * 128, 16, None)  # too small
+    assert rc == status("SSM_ERR_WORKSPACE")
+    rc = L.ssm_scan_fwd(ctypes.byref(a), None, None, 0, None)
+    assert rc == status("SSM_ERR_NULL")
+    gi = B.ScanBwdIn(gy=None)
+    gr = B.ScanGrads()
+    rc = L.ssm_scan_bwd(ctypes.byref(a), ctypes.byref(gi), ctypes.byref(gr), None, 0, None)
+    assert rc == status("SSM_ERR_NULL")
+    rc = L.ssm_impulse_sensitivity(ctypes.byref(a), 1000, None, FAKE * 64, None, 0, None)
+    assert rc == status("SSM_ERR_SHAPE")  # t_out outside [0, L)
+
+
+def test_workspace_independent_of_length_for_sensitivity():
+    """The sensitivity path needs O(n_chunks) scratch: per chunk a few numbers, no per-step state."""
+    _, n1 = ws_bytes(B.SSM_OP_IMPULSE, sel_args(length=16384, batch=1, channels=64))
+    _, n2 = ws_bytes(B.SSM_OP_IMPULSE, sel_args(length=131072, batch=1, channels=64))
+    chunks1, chunks2 = 16384 // 256, 131072 // 256
+    per_chunk = (n2 - n1) / (chunks2 - chunks1)
+    # at most ~ (3 segment arrays x N floats + one float + one double) per chunk and channel
+    assert per_chunk <= 64 * (3 * 16 * 4 + 4 + 8) + 64
+
+
+def pd_args(**over):
+    a = B.PDArgs(batch=2, heads=4, length=500, state=16, dict_size=8, chunk_len=0, logits=FAKE, sel=None,
+                 dict=FAKE * 2, d=FAKE * 3, b=FAKE * 4, C=FAKE * 5)
+    for k, v in over.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(logits=None), "SSM_ERR_NULL"),
+    (dict(dict=None), "SSM_ERR_NULL"),
+    (dict(state=17), "SSM_ERR_SHAPE"),
+    (dict(dict_size=65), "SSM_ERR_SHAPE"),
+    (dict(length=0), "SSM_ERR_SHAPE"),
+    (dict(chunk_len=32), "SSM_ERR_UNSUPPORTED"),
+])
+def test_pd_validation(over, code):
+    n = ctypes.c_size_t()
+    rc = B.lib().ssm_workspace_bytes(B.SSM_OP_PD_FWD, ctypes.byref(pd_args(**over)), ctypes.byref(n))
+    assert rc == status(code), B.lib().ssm_last_error_detail()
+
+
+def test_pd_workspace_query():
+    n = ctypes.c_size_t()
+    assert B.lib().ssm_workspace_bytes(B.SSM_OP_PD_BWD, ctypes.byref(pd_args()), ctypes.byref(n)) == 0
+    assert n.value > 0
