@@ -341,7 +341,7 @@ int scan_fwd_impl(const ssm_scan_args* a, const ssm_scan_fwd_out* out, void* ws,
             return rc;
         if ((rc = check_overlaps(scan_inputs(a, p), outs))) return rc;
     }
-    Carve cv(need_only ? nullptr : ws);
+    Carve cv(nullptr);
     if (p.mode == SSM_REAL_SELECTIVE) {
         SelFwdLayout lay;
         sel_fwd_layout(p, cv, &lay);
@@ -406,14 +406,15 @@ int scan_bwd_impl(const ssm_scan_args* a, const ssm_scan_bwd_in* in, const ssm_s
             if ((rc = check_align(o.p, 2, o.name))) return rc;
         if ((rc = check_overlaps(ins, outs))) return rc;
     }
-    Carve cv(need_only ? nullptr : ws);
+    Carve cv(nullptr);
     if (p.mode == SSM_REAL_SELECTIVE) {
         // workspace is sized for the worst case (checkpoints recomputed, every gradient wanted)
-        SelBwdLayout lay;
-        sel_bwd_layout(p, false, true, true, true, cv, &lay);
+        SelBwdLayout sizing;
+        sel_bwd_layout(p, false, true, true, true, cv, &sizing);
         if (need_only) { *need_only = cv.off; return ok(); }
         if ((rc = check_ws(ws, ws_bytes, cv.off))) return rc;
         Carve real(ws);
+        SelBwdLayout lay;  // only the buffers this call needs are non-null
         sel_bwd_layout(p, have_ckpt, g->gBm != nullptr, g->gC != nullptr, g->gA != nullptr, real, &lay);
         const float* ckpt = in->ckpt;
         if (!have_ckpt) {

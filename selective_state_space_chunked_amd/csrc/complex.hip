@@ -294,19 +294,38 @@ __global__ void cplx_combine_rev_kernel(CplxParams p) {
         v = cfma({p.segQ[2 * o], p.segQ[2 * o + 1]}, v, {p.segR[2 * o], p.segR[2 * o + 1]});
     }
 }
-// (B,G,H,M) partials -> (H,M), summed over (b, g) in index order
-__global__ void cplx_reduce_kernel(CplxParams p, float* glam, float* gtheta, float* gc) {
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+// (B,G,H,M) partials -> (H,M): one wave per (head, mode); lane l adds the
+// partials l, l+64, ... in order, then a fixed butterfly over the 64 lanes.
+__device__ __forceinline__ double wave_sum_f64(double v) {
+    v += dpp_d<SSM_DPP_QUAD(1, 0, 3, 2)>(v);
+    v += dpp_d<SSM_DPP_QUAD(2, 3, 0, 1)>(v);
+    v += dpp_d<SSM_DPP_ROW_HALF_MIRROR>(v);
+    v += dpp_d<SSM_DPP_ROW_MIRROR>(v);
+    double w = v;
+    permswap_d<false>(v, w);  // rows 0<->1, 2<->3
+    v += w;
+    w = v;
+    permswap_d<true>(v, w);   // halves
+    return v + w;
+}
+__global__ __launch_bounds__(256) void cplx_reduce_kernel(CplxParams p, float* glam, float* gtheta, float* gc) {
+    const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int HM = p.H * p.M;
-    if (i >= HM) return;
+    if (i >= HM) return;  // whole waves leave together
+    const int lane = threadIdx.x & 63;
     double sl = 0.0, st = 0.0, cr = 0.0, ci = 0.0;
-    for (int k = 0; k < p.B * p.G; ++k) {
+    for (int k = lane; k < p.B * p.G; k += 64) {
         const size_t o = (size_t)k * HM + i;
         sl += p.partL[o];
         st += p.partT[o];
         cr += p.partC[2 * o];
         ci += p.partC[2 * o + 1];
     }
+    sl = wave_sum_f64(sl);
+    st = wave_sum_f64(st);
+    cr = wave_sum_f64(cr);
+    ci = wave_sum_f64(ci);
+    if (lane != 0) return;
     if (glam) glam[i] = (float)(sl / (double)p.lam[i]);  // d/d lambda = (d/d ln lambda) / lambda
     if (gtheta) gtheta[i] = (float)st;
     if (gc) {
@@ -341,7 +360,7 @@ hipError_t launch_cplx_combine_rev(const CplxParams& p, hipStream_t st) {
 }
 hipError_t launch_cplx_reduce(const CplxParams& p, float* glam, float* gtheta, float* gc, hipStream_t st) {
     const int n = p.H * p.M;
-    cplx_reduce_kernel<<<(n + 255) / 256, 256, 0, st>>>(p, glam, gtheta, gc);
+    cplx_reduce_kernel<<<(n + 3) / 4, 256, 0, st>>>(p, glam, gtheta, gc);
     return hipGetLastError();
 }
 

@@ -60,7 +60,8 @@ __device__ __forceinline__ void pd_load_tables(const PDParams& p, int hh, int32_
                                                int32_t* scnt) {
     const int K = p.K, N = p.N;
     for (int e = threadIdx.x; e < K * N; e += 256) {
-        sdict[e] = p.dict[(size_t)hh * K * N + e];
+        // entries outside [0, N) are a precondition violation; clamping keeps every access in bounds
+        sdict[e] = min(max(p.dict[(size_t)hh * K * N + e], 0), N - 1);
         scnt[e] = p.pre_cnt[(size_t)hh * K * N + e];
     }
     for (int e = threadIdx.x; e < K * N * N; e += 256) spre[e] = p.pre[(size_t)hh * K * N * N + e];
@@ -141,6 +142,7 @@ __global__ __launch_bounds__(256) void pd_fwd_kernel(PDParams p) {
             if (tv) {
                 if (SUMMARY) k = p.logits ? pd_argmax(p.logits + (srow + t) * K, K) : p.sel_in[srow + t];
                 else k = p.sel[srow + t];
+                k = min(max(k, 0), K - 1);  // given selections outside [0, K) are clamped
             }
             if (r.lane == j) selbuf = k;
             const size_t o = (srow + (tv ? t : 0)) * N + i;
@@ -213,7 +215,7 @@ __global__ __launch_bounds__(256) void pd_bwd_kernel(PDParams p) {
         for (int q = 0; q < kPChunk; ++q) {
             const int t = t0 + q;
             const bool tv = t < L;
-            const int k = tv ? p.sel[srow + t] : 0;
+            const int k = tv ? min(max(p.sel[srow + t], 0), p.K - 1) : 0;
             const size_t o = (srow + (tv ? t : 0)) * N + j;
             const float dv = (tv && nl) ? p.d[o] : 0.0f;
             const float bv = (tv && nl) ? p.b[o] : 0.0f;
@@ -225,7 +227,7 @@ __global__ __launch_bounds__(256) void pd_bwd_kernel(PDParams p) {
     for (int q = kPChunk - 1; q >= 0; --q) {
         const int t = t0 + q;
         const bool tv = t < L;
-        const int k = tv ? p.sel[srow + t] : 0;
+        const int k = tv ? min(max(p.sel[srow + t], 0), p.K - 1) : 0;
         const int pj = sdict[k * N + j];
         const size_t o = (srow + (tv ? t : 0)) * N + j;
         const float gyt = tv ? p.gy[srow + t] : 0.0f;
@@ -261,34 +263,77 @@ __global__ __launch_bounds__(256) void pd_bwd_kernel(PDParams p) {
     }
 }
 
-// chunk chains, one thread per (batch, head); N <= 16 states in registers
-__global__ void pd_combine_fwd_kernel(PDParams p) {
-    const int s = blockIdx.x * blockDim.x + threadIdx.x;
-    if (s >= p.B * p.H) return;
+// Chunk chains.  One 16-lane row per (batch, head), lane = state; the chain
+// over chunks is sequential, each link a PD-affine map applied to 16 values.
+// Forward link: h'[i] = S[i] + sum over columns j (ascending) with pi(j) = i of
+// D[j] h[j]; the columns are visited with DPP broadcasts.  Reverse link:
+// v'[j] = D[j] v[pi(j)] + R[j], one gather.  The next chunk's summary is
+// loaded one link ahead.
+__device__ __forceinline__ float pd_link_fwd(float h, float S, float D, int pi, int i, int N) {
+    const float v = D * h;
+    float acc = S;
+    const float pf = __int_as_float(pi);
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj) {
+        const int pj = __float_as_int(bcast16(pf, jj));
+        const float vj = bcast16(v, jj);
+        if (jj < N && pj == i) acc += vj;
+    }
+    return acc;
+}
+
+__global__ __launch_bounds__(256) void pd_combine_fwd_kernel(PDParams p) {
+    const int s = blockIdx.x * 16 + (threadIdx.x >> 4);
+    const int i = threadIdx.x & 15;
+    if (s >= p.B * p.H) return;  // whole rows leave together
     const int N = p.N;
-    float h[16], hn[16];
-    for (int i = 0; i < 16; ++i) h[i] = (i < N && p.h0) ? p.h0[(size_t)s * N + i] : 0.0f;
+    const bool nl = i < N;
+    const int ic = nl ? i : N - 1;
+    float h = (nl && p.h0) ? p.h0[(size_t)s * N + ic] : 0.0f;
+    size_t base = (size_t)s * p.G * N;
+    float S = p.segS[base + ic], D = p.segD[base + ic];
+    int pi = p.segPi[base + ic];
     for (int g = 0; g < p.G; ++g) {
-        const size_t base = ((size_t)s * p.G + g) * N;
-        for (int i = 0; i < N; ++i) {
-            p.carry_in[base + i] = h[i];
-            hn[i] = p.segS[base + i];
+        float S2 = 0.0f, D2 = 0.0f;
+        int pi2 = 0;
+        if (g + 1 < p.G) {
+            const size_t nb = base + N;
+            S2 = p.segS[nb + ic];
+            D2 = p.segD[nb + ic];
+            pi2 = p.segPi[nb + ic];
         }
-        for (int jj = 0; jj < N; ++jj) hn[p.segPi[base + jj]] += p.segD[base + jj] * h[jj];
-        for (int i = 0; i < N; ++i) h[i] = hn[i];
+        if (nl) p.carry_in[base + ic] = h;
+        h = pd_link_fwd(h, S, D, pi, i, N);
+        if (!nl) h = 0.0f;
+        S = S2; D = D2; pi = pi2;
+        base += N;
     }
 }
-__global__ void pd_combine_rev_kernel(PDParams p) {
-    const int s = blockIdx.x * blockDim.x + threadIdx.x;
+__global__ __launch_bounds__(256) void pd_combine_rev_kernel(PDParams p) {
+    const int s = blockIdx.x * 16 + (threadIdx.x >> 4);
+    const int j = threadIdx.x & 15;
     if (s >= p.B * p.H) return;
     const int N = p.N;
-    float v[16], vn[16];
-    for (int i = 0; i < 16; ++i) v[i] = (i < N && p.gh_last) ? p.gh_last[(size_t)s * N + i] : 0.0f;
+    const bool nl = j < N;
+    const int jc = nl ? j : N - 1;
+    float v = (nl && p.gh_last) ? p.gh_last[(size_t)s * N + jc] : 0.0f;
+    size_t base = ((size_t)s * p.G + p.G - 1) * N;
+    float R = p.segS[base + jc], D = p.segD[base + jc];
+    int pi = p.segPi[base + jc];
     for (int g = p.G - 1; g >= 0; --g) {
-        const size_t base = ((size_t)s * p.G + g) * N;
-        for (int i = 0; i < N; ++i) p.nu_in[base + i] = v[i];
-        for (int jj = 0; jj < N; ++jj) vn[jj] = fmaf(p.segD[base + jj], v[p.segPi[base + jj]], p.segS[base + jj]);
-        for (int i = 0; i < N; ++i) v[i] = vn[i];
+        float R2 = 0.0f, D2 = 0.0f;
+        int pi2 = 0;
+        if (g > 0) {
+            const size_t nb = base - N;
+            R2 = p.segS[nb + jc];
+            D2 = p.segD[nb + jc];
+            pi2 = p.segPi[nb + jc];
+        }
+        if (nl) p.nu_in[base + jc] = v;
+        const float vn = fmaf(D, row_pull(v, pi), R);
+        v = nl ? vn : 0.0f;
+        R = R2; D = D2; pi = pi2;
+        base -= N;
     }
 }
 
@@ -305,7 +350,7 @@ hipError_t launch_pd_fwd(const PDParams& p, bool summary, hipStream_t st) {
 }
 hipError_t launch_pd_combine_fwd(const PDParams& p, hipStream_t st) {
     const int n = p.B * p.H;
-    pd_combine_fwd_kernel<<<(n + 63) / 64, 64, 0, st>>>(p);
+    pd_combine_fwd_kernel<<<(n + 15) / 16, 256, 0, st>>>(p);
     return hipGetLastError();
 }
 hipError_t launch_pd_bwd(const PDParams& p, bool summary, hipStream_t st) {
@@ -316,7 +361,7 @@ hipError_t launch_pd_bwd(const PDParams& p, bool summary, hipStream_t st) {
 }
 hipError_t launch_pd_combine_rev(const PDParams& p, hipStream_t st) {
     const int n = p.B * p.H;
-    pd_combine_rev_kernel<<<(n + 63) / 64, 64, 0, st>>>(p);
+    pd_combine_rev_kernel<<<(n + 15) / 16, 256, 0, st>>>(p);
     return hipGetLastError();
 }
 
