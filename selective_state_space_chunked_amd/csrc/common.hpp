@@ -155,30 +155,46 @@ __device__ __forceinline__ float row_sum(float v) {
 // Inclusive scan, inside each 16-lane row from lane 0 upward, of the affine
 // maps f_i(h) = P_i h + S_i under composition (later lane applied last):
 // afterwards (P, S) of lane i describe f_i o ... o f_0.
+//
+// Each of the four levels is two DPP-fused VALU instructions:
+//   S_i += S_{i-k} * P_i   (v_fmac_f32 with a row_shr:k source)
+//   P_i  = P_{i-k} * P_i   (v_mul_f32 with a row_shr:k source)
+// Lanes whose source falls outside the row are not written (bound_ctrl off),
+// which leaves lanes i < k unchanged as the scan requires.  A DPP read of a
+// VGPR needs two wait states after the VALU write of that VGPR; the s_nop 1
+// before every level provides them (the asm block is opaque to the
+// compiler's hazard recogniser).
+#define SSM_ASM_SCAN_LEVEL(DIR, K)                                               \
+    "s_nop 1\n\t"                                                                \
+    "v_fmac_f32_dpp %1, %1, %0 " DIR ":" #K " row_mask:0xf bank_mask:0xf\n\t"    \
+    "v_mul_f32_dpp %0, %0, %0 " DIR ":" #K " row_mask:0xf bank_mask:0xf\n\t"
 __device__ __forceinline__ void row_scan_affine_up(float& P, float& S) {
-#define SSM_SCAN_STEP(k)                                        \
-    {                                                           \
-        float Pp = dpp<SSM_DPP_ROW_SHR(k)>(1.0f, P);            \
-        float Sp = dpp<SSM_DPP_ROW_SHR(k)>(0.0f, S);            \
-        S = fmaf(P, Sp, S);                                     \
-        P = P * Pp;                                             \
-    }
-    SSM_SCAN_STEP(1) SSM_SCAN_STEP(2) SSM_SCAN_STEP(4) SSM_SCAN_STEP(8)
-#undef SSM_SCAN_STEP
+    asm volatile(SSM_ASM_SCAN_LEVEL("row_shr", 1) SSM_ASM_SCAN_LEVEL("row_shr", 2)
+                 SSM_ASM_SCAN_LEVEL("row_shr", 4) SSM_ASM_SCAN_LEVEL("row_shr", 8)
+                 : "+v"(P), "+v"(S));
 }
 // Inclusive scan from lane 15 downward (lane i composes lanes i..15, lane i
 // applied last): used by the reverse-time adjoint recurrence.
 __device__ __forceinline__ void row_scan_affine_down(float& P, float& S) {
-#define SSM_SCAN_STEP(k)                                        \
-    {                                                           \
-        float Pp = dpp<SSM_DPP_ROW_SHL(k)>(1.0f, P);            \
-        float Sp = dpp<SSM_DPP_ROW_SHL(k)>(0.0f, S);            \
-        S = fmaf(P, Sp, S);                                     \
-        P = P * Pp;                                             \
-    }
-    SSM_SCAN_STEP(1) SSM_SCAN_STEP(2) SSM_SCAN_STEP(4) SSM_SCAN_STEP(8)
-#undef SSM_SCAN_STEP
+    asm volatile(SSM_ASM_SCAN_LEVEL("row_shl", 1) SSM_ASM_SCAN_LEVEL("row_shl", 2)
+                 SSM_ASM_SCAN_LEVEL("row_shl", 4) SSM_ASM_SCAN_LEVEL("row_shl", 8)
+                 : "+v"(P), "+v"(S));
 }
+#undef SSM_ASM_SCAN_LEVEL
+// Both scans at once, interleaved: (P, S) upward, (Q, R) downward.  Every DPP
+// read is at least three instructions after the write of its source, so only
+// the entry needs wait states.
+#define SSM_ASM_SCAN2_LEVEL(K)                                                   \
+    "v_fmac_f32_dpp %1, %1, %0 row_shr:" #K " row_mask:0xf bank_mask:0xf\n\t"    \
+    "v_fmac_f32_dpp %3, %3, %2 row_shl:" #K " row_mask:0xf bank_mask:0xf\n\t"    \
+    "v_mul_f32_dpp %0, %0, %0 row_shr:" #K " row_mask:0xf bank_mask:0xf\n\t"     \
+    "v_mul_f32_dpp %2, %2, %2 row_shl:" #K " row_mask:0xf bank_mask:0xf\n\t"
+__device__ __forceinline__ void row_scan_affine_updown(float& P, float& S, float& Q, float& R) {
+    asm volatile("s_nop 1\n\t" SSM_ASM_SCAN2_LEVEL(1) SSM_ASM_SCAN2_LEVEL(2)
+                 SSM_ASM_SCAN2_LEVEL(4) SSM_ASM_SCAN2_LEVEL(8)
+                 : "+v"(P), "+v"(S), "+v"(Q), "+v"(R));
+}
+#undef SSM_ASM_SCAN2_LEVEL
 
 // Exclusive prefix sum within each 16-lane row (lane 0 gets 0).
 __device__ __forceinline__ float row_excl_sum_up(float v) {

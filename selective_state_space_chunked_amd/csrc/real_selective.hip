@@ -323,17 +323,15 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
 #pragma unroll
             for (int j = KPL - 1; j >= 0; --j) R = a[j] * fmaf(cv[j], gyv[j], R);
             float Q = P;
-            row_scan_affine_down(Q, R);
-            const float nfirst = fmaf(Q, nin, R);     // adjoint at this lane's first step
-            const float newnu = row_bcast<0>(nfirst);
             if constexpr (SUMMARY) {
+                row_scan_affine_down(Q, R);
+                const float nfirst = fmaf(Q, nin, R);     // adjoint at this lane's first step
+                const float newnu = row_bcast<0>(nfirst);
                 const float Qt = row_bcast<0>(Q);
                 if (lane == n) Qseg *= Qt;
                 nu = (lane == n) ? newnu : nu;
             } else {
-                float nnext = dpp<SSM_DPP_ROW_SHL(1)>(nin, nfirst);  // adjoint entering from the right
-
-                // recompute the forward states of this lane's run
+                // forward lane fold of the recomputed states, scanned together with the adjoint
                 const float An = st.bc(Ao);
                 const float cin = st.bc(hs);
                 float bv[KPL], bx[KPL], h[KPL + 1];
@@ -345,9 +343,12 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
                     S = fmaf(a[j], S, bx[j]);
                 }
                 float Pf = P;
-                row_scan_affine_up(Pf, S);
+                row_scan_affine_updown(Pf, S, Q, R);
+                const float nfirst = fmaf(Q, nin, R);     // adjoint at this lane's first step
+                const float newnu = row_bcast<0>(nfirst);
+                float nnext = dpp<SSM_DPP_ROW_SHL(1)>(nin, nfirst);  // adjoint entering from the right
                 const float hend = fmaf(Pf, cin, S);
-                h[0] = dpp<SSM_DPP_ROW_SHR(1)>(cin, hend);
+                h[0] = dpp<SSM_DPP_ROW_SHR(1)>(cin, hend);         // state entering this lane's run
 #pragma unroll
                 for (int j = 0; j < KPL; ++j) h[j + 1] = fmaf(a[j], h[j], bx[j]);
 
@@ -356,14 +357,13 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
 #pragma unroll
                 for (int j = KPL - 1; j >= 0; --j) {
                     const float lam = fmaf(cv[j], gyv[j], nnext);
-                    const float ah = a[j] * h[j];
-                    const float t1 = lam * ah;
+                    nnext = a[j] * lam;                       // nu_j
+                    const float t1 = nnext * h[j];            // lambda_j a_j h_{j-1}
                     Gd[j] = fmaf(An, t1, Gd[j]);
                     Sb[j] = fmaf(lam, bv[j], Sb[j]);
                     if constexpr (WA) gAl = fmaf(t1, dl[j], gAl);
                     pB[j] = lam * dx[j];
                     pC[j] = gyv[j] * h[j + 1];
-                    nnext = a[j] * lam;
                 }
                 {
                     float* rB = red + row * G::LDSW + lane * G::SEG;
