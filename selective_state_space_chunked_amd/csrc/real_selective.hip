@@ -31,6 +31,9 @@ constexpr float kLog2e = 1.4426950408889634f;
 // backward workgroup: 32 rows of 16 lanes (channels 32*blockIdx.x ...)
 constexpr int kBwdRows = 32;
 constexpr int kBwdThreads = 16 * kBwdRows;
+// Rows of a wave whose gB/gC products are summed in registers (permlane
+// swaps) before the sum over the workgroup's rows in LDS: 1, 2 or 4.
+constexpr int kPresum = 4;
 
 // State index of the loop over n: compile-time (fully unrolled loop, DPP
 // row_newbcast) or runtime (generic state counts, ds_bpermute broadcast).
@@ -228,8 +231,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void s
 //   lambda_t = C_t gy_t + nu_{t+1},   dLoss/da_t = lambda_t h_{t-1},
 //   gdelta_t = sum_n (A lambda a h_{t-1} + lambda x B),  gx_t = delta_t sum_n lambda B,
 //   gB_t[n] = sum_d lambda delta x,  gC_t[n] = sum_d gy h_t,  gA = sum_{b,t} lambda a h_{t-1} delta.
-// Sums over d are first taken over the 16 rows in LDS and written as one
-// partial per 16-channel block; a second kernel adds the blocks in order.
+// Sums over d (gB, gC) are taken over the 4 rows of each wave with permlane
+// swaps, then over the 8 waves in LDS, and written as one partial per
+// 32-channel block; a second kernel adds the blocks in order.
 // SUMMARY: per segment, the composed adjoint map nu_start = Q nu_end + R.
 // ---------------------------------------------------------------------------
 template <typename T, int KPL, int NT, bool SUMMARY, bool WA>
@@ -239,9 +243,11 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
     constexpr int ROWS = kBwdRows;
     __shared__ __align__(16) float sB[SUMMARY ? 4 : 16 * G::LDSW];
     __shared__ __align__(16) float sC[16 * G::LDSW];
-    // per-row partials of gB and gC for one state, laid out like the B/C tiles
-    // ([row][lane run + 4 pad]) so the 16-byte writes of a row hit distinct banks
-    __shared__ __align__(16) float red[SUMMARY ? 4 : 2 * ROWS * G::LDSW];
+    // Partials of gB and gC for one state after the in-wave pre-sum, laid out
+    // like the B/C tiles ([pre-summed row][lane run + 4 pad]); two buffers
+    // (state parity) so one barrier per state suffices.
+    constexpr int RB = ROWS / kPresum;
+    __shared__ __align__(16) float red[SUMMARY ? 4 : 2 * 2 * RB * G::LDSW];
 
     const int tid = threadIdx.x, lane = tid & 15, row = tid >> 4;
     const int b = blockIdx.y, g = blockIdx.z;
@@ -365,15 +371,50 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
                     pB[j] = lam * dx[j];
                     pC[j] = gyv[j] * h[j + 1];
                 }
-                {
-                    float* rB = red + row * G::LDSW + lane * G::SEG;
-                    float* rC = rB + ROWS * G::LDSW;
+                // sum the wave's rows in registers: level 1 adds rows r and r+2 (lanes l, l+32),
+                // level 2 rows r and r+1; afterwards a lane holds KPL/kPresum consecutive steps
+                // of its lane run, summed over the kPresum rows
+                constexpr int CNT = KPL / kPresum;
+                if constexpr (kPresum >= 2) {
 #pragma unroll
-                    for (int q = 0; q < KPL / 4; ++q) {
-                        *reinterpret_cast<float4*>(rB + 4 * q) =
-                            make_float4(pB[4 * q], pB[4 * q + 1], pB[4 * q + 2], pB[4 * q + 3]);
-                        *reinterpret_cast<float4*>(rC + 4 * q) =
-                            make_float4(pC[4 * q], pC[4 * q + 1], pC[4 * q + 2], pC[4 * q + 3]);
+                    for (int j = 0; j < KPL / 2; ++j) {
+                        auto sb = __builtin_amdgcn_permlane32_swap(__float_as_int(pB[j]), __float_as_int(pB[j + KPL / 2]),
+                                                                   false, false);
+                        pB[j] = __int_as_float(sb[0]) + __int_as_float(sb[1]);
+                        auto sc = __builtin_amdgcn_permlane32_swap(__float_as_int(pC[j]), __float_as_int(pC[j + KPL / 2]),
+                                                                   false, false);
+                        pC[j] = __int_as_float(sc[0]) + __int_as_float(sc[1]);
+                    }
+                }
+                if constexpr (kPresum >= 4) {
+#pragma unroll
+                    for (int j = 0; j < KPL / 4; ++j) {
+                        auto sb = __builtin_amdgcn_permlane16_swap(__float_as_int(pB[j]), __float_as_int(pB[j + KPL / 4]),
+                                                                   false, false);
+                        pB[j] = __int_as_float(sb[0]) + __int_as_float(sb[1]);
+                        auto sc = __builtin_amdgcn_permlane16_swap(__float_as_int(pC[j]), __float_as_int(pC[j + KPL / 4]),
+                                                                   false, false);
+                        pC[j] = __int_as_float(sc[0]) + __int_as_float(sc[1]);
+                    }
+                }
+                float* buf = red + (n & 1) * (2 * RB * G::LDSW);
+                {
+                    constexpr int GRP = 4 / kPresum;             // pre-summed rows per wave
+                    const int q = row & 3, w = row >> 2;
+                    const int rb = w * GRP + (q % GRP);
+                    float* rB = buf + rb * G::LDSW + lane * G::SEG + (q / GRP) * CNT;
+                    float* rC = rB + RB * G::LDSW;
+                    if constexpr (CNT % 4 == 0) {
+#pragma unroll
+                        for (int k = 0; k < CNT / 4; ++k) {
+                            *reinterpret_cast<float4*>(rB + 4 * k) =
+                                make_float4(pB[4 * k], pB[4 * k + 1], pB[4 * k + 2], pB[4 * k + 3]);
+                            *reinterpret_cast<float4*>(rC + 4 * k) =
+                                make_float4(pC[4 * k], pC[4 * k + 1], pC[4 * k + 2], pC[4 * k + 3]);
+                        }
+                    } else {
+#pragma unroll
+                        for (int k = 0; k < CNT; ++k) { rB[k] = pB[k]; rC[k] = pC[k]; }
                     }
                 }
                 nu = (lane == n) ? newnu : nu;
@@ -382,21 +423,22 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
                     if (lane == n) gAacc += ga;
                 }
                 if (wantB || wantC) {
+                    // the other buffer was last read before the previous state's barrier, so
+                    // this single barrier orders both the writes above and the reads below
                     __syncthreads();
                     // one output per thread; thread i of a tensor takes step 16*(i%16) + i/16 so
                     // the 64 lanes of a wave read 16 lane runs x 4 steps = 64 distinct banks
                     for (int o = tid; o < 2 * TILE; o += kBwdThreads) {
                         const int which = o / TILE, i = o - which * TILE;
                         const int tt = (i % 16) * KPL + (i / 16);
-                        const float* src = red + which * ROWS * G::LDSW + (tt / KPL) * G::SEG + (tt % KPL);
+                        const float* src = buf + which * RB * G::LDSW + (tt / KPL) * G::SEG + (tt % KPL);
                         float sum = 0.0f;
 #pragma unroll
-                        for (int r = 0; r < ROWS; ++r) sum += src[r * G::LDSW];
+                        for (int r = 0; r < RB; ++r) sum += src[r * G::LDSW];
                         float* part = which ? p.partC : p.partB;
                         const int t = t0 + tt;
                         if (part && t < L) part[(((size_t)blockIdx.x * p.B + b) * N + n) * L + t] = sum;
                     }
-                    __syncthreads();
                 }
             }
         });
