@@ -437,12 +437,10 @@ int scan_bwd_impl(const ssm_scan_args* a, const ssm_scan_bwd_in* in, const ssm_s
         }
         SSM_LAUNCH(launch_sel_bwd(q, p.dtype, p.kpl, false, st), "selective backward");
         const int nblk = (int)cdiv(p.D, sel_bwd_rows());
-        if (g->gBm)
-            SSM_LAUNCH(launch_reduce_parts_btn(lay.partB, nblk, (int)p.B, (int)p.N, (int)p.L, g->gBm, p.dtype, st),
-                       "reduce gBm");
-        if (g->gC)
-            SSM_LAUNCH(launch_reduce_parts_btn(lay.partC, nblk, (int)p.B, (int)p.N, (int)p.L, g->gC, p.dtype, st),
-                       "reduce gC");
+        if (g->gBm || g->gC)
+            SSM_LAUNCH(launch_reduce_parts_btn(g->gBm ? lay.partB : nullptr, g->gC ? lay.partC : nullptr, nblk,
+                                               (int)p.B, (int)p.N, (int)p.L, g->gBm, g->gC, p.dtype, st),
+                       "reduce gB gC");
         if (g->gA)
             SSM_LAUNCH(launch_reduce_parts_dn(lay.partA, (int)p.B, lay.G, (int)p.D, (int)p.N, g->gA, st),
                        "reduce gA");

@@ -44,8 +44,9 @@ hipError_t launch_seg_combine_fwd(const float* P, const float* S, const float* h
                                   int BD, int G, int N, hipStream_t st);
 hipError_t launch_seg_combine_rev(const float* Q, const float* R, const float* nu_last, float* nu_in,
                                   int BD, int G, int N, hipStream_t st);
-hipError_t launch_reduce_parts_btn(const float* part, int nblk, int B, int N, int L, void* out, int dtype,
-                                   hipStream_t st);
+// (nblk, B, N, L) channel-block partials of gB and/or gC (null skips) -> (B, L, N)
+hipError_t launch_reduce_parts_btn(const float* partB, const float* partC, int nblk, int B, int N, int L,
+                                   void* outB, void* outC, int dtype, hipStream_t st);
 hipError_t launch_reduce_parts_dn(const float* part, int B, int G, int D, int N, float* out, hipStream_t st);
 hipError_t launch_sens_suffix(const void* delta, const float* tile_dsum, double* send, int B, int D, int L,
                               int ntiles, int tile_len, int t_out, int dtype, hipStream_t st);

@@ -426,11 +426,12 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
                     // the other buffer was last read before the previous state's barrier, so
                     // this single barrier orders both the writes above and the reads below
                     __syncthreads();
-                    // one output per thread; thread i of a tensor takes step 16*(i%16) + i/16 so
-                    // the 64 lanes of a wave read 16 lane runs x 4 steps = 64 distinct banks
+                    // one output per thread; each half-wave takes 8 lane runs x 4 steps, whose
+                    // words (run * (KPL + 4) + step) fall in 32 distinct banks
                     for (int o = tid; o < 2 * TILE; o += kBwdThreads) {
                         const int which = o / TILE, i = o - which * TILE;
-                        const int tt = (i % 16) * KPL + (i / 16);
+                        const int k = i & 63;
+                        const int tt = ((k & 7) + 8 * (k >> 5)) * KPL + 4 * (i >> 6) + ((k >> 3) & 3);
                         const float* src = buf + which * RB * G::LDSW + (tt / KPL) * G::SEG + (tt % KPL);
                         float sum = 0.0f;
 #pragma unroll
@@ -503,18 +504,54 @@ __global__ void seg_combine_rev_kernel(const float* __restrict__ Q, const float*
 }
 
 // partial (nblk,B,N,L) -> out (B,L,N), adding the blocks in index order
+// Channel-block partials (nblk, B, N, L) of gB and gC -> outputs (B, L, N).
+// A workgroup takes 64 steps of one batch row and one tensor (blockIdx.z);
+// thread (n, q) adds the nblk partials of steps 4q..4q+3 in block order, then
+// the 64 x N tile is transposed through LDS so the (t, n) output rows are
+// written contiguously.
 template <typename T>
-__global__ void reduce_parts_btn_kernel(const float* __restrict__ part, int nblk, int B, int N, int L,
-                                        T* __restrict__ out) {
-    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const size_t total = (size_t)B * N * L;
-    if (i >= total) return;
-    const int t = (int)(i % L);
-    const size_t bn = i / L;
-    const int n = (int)(bn % N), b = (int)(bn / N);
-    float s = 0.0f;
-    for (int k = 0; k < nblk; ++k) s += part[(size_t)k * total + i];
-    out[((size_t)b * L + t) * N + n] = from_f32<T>(s);
+__global__ __launch_bounds__(256) void reduce_parts_btn_kernel(const float* __restrict__ partB,
+                                                               const float* __restrict__ partC, int nblk, int B,
+                                                               int N, int L, T* __restrict__ outB,
+                                                               T* __restrict__ outC) {
+    __shared__ float tile[64][17];
+    const float* __restrict__ part = blockIdx.z ? partC : partB;
+    T* __restrict__ out = blockIdx.z ? outC : outB;
+    if (!part || !out) return;
+    const int b = blockIdx.y, t0 = blockIdx.x * 64;
+    const int n = threadIdx.x >> 4, q = threadIdx.x & 15;
+    const int tl = 4 * q, t = t0 + tl;
+    const size_t stride = (size_t)B * N * L;
+    float s[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (n < N) {
+        const float* src = part + ((size_t)b * N + n) * L + t;
+        if ((L & 3) == 0 && t < L) {
+            // eight loads in flight per thread; the additions stay in block order
+            int k = 0;
+            for (; k + 8 <= nblk; k += 8) {
+                float4 v[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const float4*>(src + (size_t)(k + u) * stride);
+#pragma unroll
+                for (int u = 0; u < 8; ++u) { s[0] += v[u].x; s[1] += v[u].y; s[2] += v[u].z; s[3] += v[u].w; }
+            }
+            for (; k < nblk; ++k) {
+                const float4 v = *reinterpret_cast<const float4*>(src + (size_t)k * stride);
+                s[0] += v.x; s[1] += v.y; s[2] += v.z; s[3] += v.w;
+            }
+        } else {
+            for (int k = 0; k < nblk; ++k)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (t + i < L) s[i] += src[(size_t)k * stride + i];
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) tile[tl + i][n] = s[i];
+    __syncthreads();
+    const int steps = min(64, L - t0);
+    T* dst = out + ((size_t)b * L + t0) * N;
+    for (int i = threadIdx.x; i < steps * N; i += 256) dst[i] = from_f32<T>(tile[i / N][i % N]);
 }
 // partial (B,G,D,N) -> out (D,N)
 __global__ void reduce_parts_dn_kernel(const float* __restrict__ part, int B, int G, int D, int N,
@@ -695,12 +732,14 @@ hipError_t launch_seg_combine_rev(const float* Q, const float* R, const float* n
     seg_combine_rev_kernel<<<(total + 255) / 256, 256, 0, st>>>(Q, R, nu_last, nu_in, BD, G, N);
     return hipGetLastError();
 }
-hipError_t launch_reduce_parts_btn(const float* part, int nblk, int B, int N, int L, void* out, int dtype,
-                                   hipStream_t st) {
-    const size_t total = (size_t)B * N * L;
-    const unsigned blocks = (unsigned)((total + 255) / 256);
-    if (dtype == 0) reduce_parts_btn_kernel<float><<<blocks, 256, 0, st>>>(part, nblk, B, N, L, (float*)out);
-    else reduce_parts_btn_kernel<bf16_t><<<blocks, 256, 0, st>>>(part, nblk, B, N, L, (bf16_t*)out);
+hipError_t launch_reduce_parts_btn(const float* partB, const float* partC, int nblk, int B, int N, int L,
+                                   void* outB, void* outC, int dtype, hipStream_t st) {
+    dim3 grid((unsigned)((L + 63) / 64), (unsigned)B, 2);
+    if (dtype == 0)
+        reduce_parts_btn_kernel<float><<<grid, 256, 0, st>>>(partB, partC, nblk, B, N, L, (float*)outB, (float*)outC);
+    else
+        reduce_parts_btn_kernel<bf16_t><<<grid, 256, 0, st>>>(partB, partC, nblk, B, N, L, (bf16_t*)outB,
+                                                              (bf16_t*)outC);
     return hipGetLastError();
 }
 hipError_t launch_reduce_parts_dn(const float* part, int B, int G, int D, int N, float* out, hipStream_t st) {
