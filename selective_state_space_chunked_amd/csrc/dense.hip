@@ -17,6 +17,24 @@ namespace ssm {
 
 constexpr int kDChunk = 32;
 
+// Steps tb .. tb+K-1 of state n of a (L,N) row-major stream.  When the whole
+// block lies inside the sequence the loads are unconditional, so all K are in
+// flight together; otherwise steps past L read `fill`.
+template <int K>
+__device__ __forceinline__ void load_steps(const float* __restrict__ row, int tb, int L, int N, int n, float fill,
+                                           float (&v)[K]) {
+    if (tb + K <= L) {
+#pragma unroll
+        for (int j = 0; j < K; ++j) v[j] = row[(size_t)(tb + j) * N + n];
+    } else {
+#pragma unroll
+        for (int j = 0; j < K; ++j) v[j] = (tb + j < L) ? row[(size_t)(tb + j) * N + n] : fill;
+    }
+}
+
+// Forward.  Time is walked in 16-step blocks; the a and b values of the next
+// block are loaded while the current block is computed (two register sets),
+// and C of the current block is requested before them.
 template <bool SUMMARY>
 __global__ __launch_bounds__(256) void dense_fwd_kernel(DenseParams p) {
     const int tid = threadIdx.x, lane = tid & 15, row = tid >> 4;
@@ -26,7 +44,7 @@ __global__ __launch_bounds__(256) void dense_fwd_kernel(DenseParams p) {
     const int dc = act ? d : p.D - 1;
     const int N = p.N, L = p.L;
     const bool nl = lane < N;
-    const int n = nl ? lane : N - 1;
+    const int n = nl ? lane : N - 1;     // lanes past N load a valid state and discard it
     const size_t seq = (size_t)b * p.D + dc;
     float h = 0.0f, P = 1.0f;
     if (!SUMMARY && nl) {
@@ -38,31 +56,49 @@ __global__ __launch_bounds__(256) void dense_fwd_kernel(DenseParams p) {
     const float* arow = p.a + seq * L * N;
     const float* brow = p.b + seq * L * N;
     const float* crow = p.C + (size_t)b * L * N;
-    for (int ch = c0; ch < c1; ++ch) {
-        const int t0 = ch * kDChunk;
-        if (!SUMMARY && p.ckpt_out && act && nl) p.ckpt_out[(seq * p.nchunks + ch) * N + n] = h;
+    constexpr int BPC = kDChunk / 16;   // 16-step blocks per chunk
+    const int k0 = c0 * BPC;
+    const int k1 = min(c1 * BPC, (L + 15) / 16);
+
+    auto block = [&](int k, const float (&av)[16], const float (&bv)[16]) {
+        const int tb = 16 * k;
+        if (!SUMMARY && (k % BPC) == 0 && p.ckpt_out && act && nl)
+            p.ckpt_out[(seq * p.nchunks + k / BPC) * N + n] = h;
+        float cv[16];
+        if (!SUMMARY) load_steps<16>(crow, tb, L, N, n, 0.0f, cv);
+        float yp[16];
 #pragma unroll
-        for (int blk = 0; blk < kDChunk / 16; ++blk) {
-            float yp[16];
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const int t = t0 + 16 * blk + j;
-                yp[j] = 0.0f;
-                if (t < L) {
-                    const size_t o = (size_t)t * N + n;
-                    const float av = nl ? arow[o] : 1.0f;
-                    const float bv = nl ? brow[o] : 0.0f;
-                    h = fmaf(av, h, bv);
-                    if (SUMMARY) P *= av;
-                    else yp[j] = nl ? crow[o] * h : 0.0f;
-                }
-            }
-            if (!SUMMARY && p.y) {
-                const float ys = row_transpose_sum16(yp);
-                const int t = t0 + 16 * blk + lane;
-                if (act && t < L) p.y[seq * L + t] = ys;
-            }
+        for (int j = 0; j < 16; ++j) {
+            const bool on = nl && tb + j < L;
+            const float a = on ? av[j] : 1.0f;
+            h = fmaf(a, h, on ? bv[j] : 0.0f);
+            if (SUMMARY) P *= a;
+            else yp[j] = on ? cv[j] * h : 0.0f;
         }
+        if (!SUMMARY && p.y) {
+            const float ys = row_transpose_sum16(yp);
+            const int t = tb + lane;
+            if (act && t < L) p.y[seq * L + t] = ys;
+        }
+    };
+
+    float a0[16], b0[16], a1[16], b1[16];
+    if (k0 < k1) {
+        load_steps<16>(arow, 16 * k0, L, N, n, 1.0f, a0);
+        load_steps<16>(brow, 16 * k0, L, N, n, 0.0f, b0);
+    }
+    for (int k = k0; k < k1; k += 2) {
+        if (k + 1 < k1) {
+            load_steps<16>(arow, 16 * (k + 1), L, N, n, 1.0f, a1);
+            load_steps<16>(brow, 16 * (k + 1), L, N, n, 0.0f, b1);
+        }
+        block(k, a0, b0);
+        if (k + 1 >= k1) break;
+        if (k + 2 < k1) {
+            load_steps<16>(arow, 16 * (k + 2), L, N, n, 1.0f, a0);
+            load_steps<16>(brow, 16 * (k + 2), L, N, n, 0.0f, b0);
+        }
+        block(k + 1, a1, b1);
     }
     if (!act || !nl) return;
     if (SUMMARY) {
@@ -76,8 +112,11 @@ __global__ __launch_bounds__(256) void dense_fwd_kernel(DenseParams p) {
 // gC partials of one chunk: [row][step][state] with rows padded by 16 floats
 constexpr int kDRedRow = kDChunk * 16 + 16;
 
+// Backward, reverse over chunks.  Per chunk every load (checkpoint, gy, a, b,
+// C) is issued before any use; the chunk's states are recomputed into
+// registers, then the adjoint runs right to left.
 template <bool SUMMARY>
-__global__ __launch_bounds__(256) void dense_bwd_kernel(DenseParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void dense_bwd_kernel(DenseParams p) {
     __shared__ float red[SUMMARY ? 4 : 16 * kDRedRow];
     const int tid = threadIdx.x, lane = tid & 15, row = tid >> 4;
     const int b = blockIdx.y, g = blockIdx.z;
@@ -108,50 +147,42 @@ __global__ __launch_bounds__(256) void dense_bwd_kernel(DenseParams p) {
             const int t = t0 + 16 * q + lane;
             gyl[q] = t < L ? p.gy[seq * L + t] * live : 0.0f;
         }
+        float as[kDChunk], cs[kDChunk];
+        load_steps<kDChunk>(arow, t0, L, N, n, 1.0f, as);
+        load_steps<kDChunk>(crow, t0, L, N, n, 0.0f, cs);
         if (SUMMARY) {
 #pragma unroll
             for (int jj = kDChunk - 1; jj >= 0; --jj) {
-                const int t = t0 + jj;
                 const float gyt = bcast16(gyl[jj / 16], jj % 16);
-                if (t < L && nl) {
-                    const size_t o = (size_t)t * N + n;
-                    const float av = arow[o];
-                    nu = av * fmaf(crow[o], gyt, nu);
-                    Q *= av;
-                }
+                const float av = nl ? as[jj] : 1.0f;
+                nu = av * fmaf(nl ? cs[jj] : 0.0f, gyt, nu);
+                Q *= av;
             }
             continue;
         }
-        float hs[kDChunk + 1], as[kDChunk];
-        hs[0] = nl ? p.ckpt[(seq * p.nchunks + ch) * N + n] : 0.0f;
+        float hs[kDChunk + 1];
+        {
+            float bs[kDChunk];
+            load_steps<kDChunk>(brow, t0, L, N, n, 0.0f, bs);
+            hs[0] = p.ckpt[(seq * p.nchunks + ch) * N + n];
 #pragma unroll
-        for (int j = 0; j < kDChunk; ++j) {
-            const int t = t0 + j;
-            as[j] = 1.0f;
-            hs[j + 1] = hs[j];
-            if (t < L && nl) {
-                const size_t o = (size_t)t * N + n;
-                as[j] = arow[o];
-                hs[j + 1] = fmaf(as[j], hs[j], brow[o]);
-            }
+            for (int j = 0; j < kDChunk; ++j) hs[j + 1] = fmaf(as[j], hs[j], bs[j]);
         }
         float* rrow = red + row * kDRedRow;
+        const bool wr = act && nl;
 #pragma unroll
         for (int j = kDChunk - 1; j >= 0; --j) {
             const int t = t0 + j;
             const float gyt = bcast16(gyl[j / 16], j % 16);
-            float pc = 0.0f;
-            if (t < L && nl) {
+            const bool on = nl && t < L;
+            const float lam = fmaf(cs[j], gyt, nu);
+            if (wr && t < L) {
                 const size_t o = (size_t)t * N + n;
-                const float lam = fmaf(crow[o], gyt, nu);
-                if (act) {
-                    if (p.ga) p.ga[seq * L * N + o] = lam * hs[j];
-                    if (p.gb) p.gb[seq * L * N + o] = lam;
-                }
-                pc = gyt * hs[j + 1];
-                nu = as[j] * lam;
+                if (p.ga) p.ga[seq * L * N + o] = lam * hs[j];
+                if (p.gb) p.gb[seq * L * N + o] = lam;
             }
-            if (p.partC) rrow[j * 16 + lane] = pc;
+            if (p.partC) rrow[j * 16 + lane] = on ? gyt * hs[j + 1] : 0.0f;
+            nu = on ? as[j] * lam : nu;
         }
         if (p.partC) {
             __syncthreads();
