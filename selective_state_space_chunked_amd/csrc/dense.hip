@@ -23,26 +23,27 @@ constexpr int kDChunk = 32;
 template <int K>
 __device__ __forceinline__ void load_steps(const float* __restrict__ row, int tb, int L, int N, int n, float fill,
                                            float (&v)[K]) {
+    const float* __restrict__ q = row + (size_t)tb * N + n;   // step j at q[j * N]: immediate offsets when N is fixed
     if (tb + K <= L) {
 #pragma unroll
-        for (int j = 0; j < K; ++j) v[j] = row[(size_t)(tb + j) * N + n];
+        for (int j = 0; j < K; ++j) v[j] = q[j * N];
     } else {
 #pragma unroll
-        for (int j = 0; j < K; ++j) v[j] = (tb + j < L) ? row[(size_t)(tb + j) * N + n] : fill;
+        for (int j = 0; j < K; ++j) v[j] = (tb + j < L) ? q[j * N] : fill;
     }
 }
 
 // Forward.  Time is walked in 16-step blocks; the a and b values of the next
 // block are loaded while the current block is computed (two register sets),
 // and C of the current block is requested before them.
-template <bool SUMMARY>
+template <bool SUMMARY, int NT>
 __global__ __launch_bounds__(256) void dense_fwd_kernel(DenseParams p) {
     const int tid = threadIdx.x, lane = tid & 15, row = tid >> 4;
     const int b = blockIdx.y, g = blockIdx.z;
     const int d = blockIdx.x * 16 + row;
     const bool act = d < p.D;
     const int dc = act ? d : p.D - 1;
-    const int N = p.N, L = p.L;
+    const int N = NT ? NT : p.N, L = p.L;  // NT = 16: compile-time state count
     const bool nl = lane < N;
     const int n = nl ? lane : N - 1;     // lanes past N load a valid state and discard it
     const size_t seq = (size_t)b * p.D + dc;
@@ -115,7 +116,7 @@ constexpr int kDRedRow = kDChunk * 16 + 16;
 // Backward, reverse over chunks.  Per chunk every load (checkpoint, gy, a, b,
 // C) is issued before any use; the chunk's states are recomputed into
 // registers, then the adjoint runs right to left.
-template <bool SUMMARY>
+template <bool SUMMARY, int NT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void dense_bwd_kernel(DenseParams p) {
     __shared__ float red[SUMMARY ? 4 : 16 * kDRedRow];
     const int tid = threadIdx.x, lane = tid & 15, row = tid >> 4;
@@ -123,7 +124,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void d
     const int d = blockIdx.x * 16 + row;
     const bool act = d < p.D;
     const int dc = act ? d : p.D - 1;
-    const int N = p.N, L = p.L;
+    const int N = NT ? NT : p.N, L = p.L;  // NT = 16: compile-time state count
     const bool nl = lane < N;
     const int n = nl ? lane : N - 1;
     const size_t seq = (size_t)b * p.D + dc;
@@ -208,14 +209,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void d
 
 hipError_t launch_dense_fwd(const DenseParams& p, bool summary, hipStream_t st) {
     dim3 grid((p.D + 15) / 16, p.B, p.G);
-    if (summary) dense_fwd_kernel<true><<<grid, 256, 0, st>>>(p);
-    else dense_fwd_kernel<false><<<grid, 256, 0, st>>>(p);
+    if (p.N == 16) {
+        if (summary) dense_fwd_kernel<true, 16><<<grid, 256, 0, st>>>(p);
+        else dense_fwd_kernel<false, 16><<<grid, 256, 0, st>>>(p);
+    } else {
+        if (summary) dense_fwd_kernel<true, 0><<<grid, 256, 0, st>>>(p);
+        else dense_fwd_kernel<false, 0><<<grid, 256, 0, st>>>(p);
+    }
     return hipGetLastError();
 }
 hipError_t launch_dense_bwd(const DenseParams& p, bool summary, hipStream_t st) {
     dim3 grid((p.D + 15) / 16, p.B, p.G);
-    if (summary) dense_bwd_kernel<true><<<grid, 256, 0, st>>>(p);
-    else dense_bwd_kernel<false><<<grid, 256, 0, st>>>(p);
+    // the backward keeps the generic state count: at N = 16 the specialised
+    // variant measured slower (its register allocation spills more)
+    if (summary) dense_bwd_kernel<true, 0><<<grid, 256, 0, st>>>(p);
+    else dense_bwd_kernel<false, 0><<<grid, 256, 0, st>>>(p);
     return hipGetLastError();
 }
 

@@ -36,7 +36,7 @@ __device__ __forceinline__ int row_pull_i(int v, int src) {
 }
 
 // preimage lists: pre[(h*K+k)*N*N + i*N + r] = r-th column j (ascending) with
-// dict[h,k,j] == i, or -1; cnt[(h*K+k)*N + i] = number of such columns.
+// dict[h,k,j] == i, padded with 0; cnt[(h*K+k)*N + i] = number of such columns.
 __global__ void pd_prep_kernel(const int32_t* __restrict__ dict, int8_t* __restrict__ pre,
                                int32_t* __restrict__ cnt, int H, int K, int N) {
     const int idx = blockIdx.x * blockDim.x + threadIdx.x;
@@ -46,7 +46,7 @@ __global__ void pd_prep_kernel(const int32_t* __restrict__ dict, int8_t* __restr
     int c = 0;
     for (int j = 0; j < N; ++j)
         if (col[j] == i) pre[(size_t)hk * N * N + i * N + c++] = (int8_t)j;
-    for (int r = c; r < N; ++r) pre[(size_t)hk * N * N + i * N + r] = -1;
+    for (int r = c; r < N; ++r) pre[(size_t)hk * N * N + i * N + r] = 0;
     cnt[idx] = c;
 }
 
@@ -55,31 +55,52 @@ struct PDRow {
     bool act;  // row maps to an existing chunk
 };
 
-// Load the head's dictionary and preimage lists into LDS (whole workgroup).
-__device__ __forceinline__ void pd_load_tables(const PDParams& p, int hh, int32_t* sdict, int8_t* spre,
-                                               int32_t* scnt) {
+// A head's tables in LDS: the dictionary, the preimage counts, the preimage
+// lists at a fixed 16-byte stride per (entry, target row) so a lane reads its
+// whole list with one 16-byte load, and the largest count (the number of
+// gather rounds every step needs).
+struct PDShared {
+    int32_t dict[kPMaxK * 16];
+    int32_t cnt[kPMaxK * 16];
+    __attribute__((aligned(16))) uint8_t pre[kPMaxK * 16 * 16];
+    int maxc;
+};
+
+__device__ __forceinline__ void pd_load_tables(const PDParams& p, int hh, PDShared& t) {
     const int K = p.K, N = p.N;
+    if (threadIdx.x == 0) t.maxc = 0;
+    __syncthreads();
+    int m = 0;
     for (int e = threadIdx.x; e < K * N; e += 256) {
         // entries outside [0, N) are a precondition violation; clamping keeps every access in bounds
-        sdict[e] = min(max(p.dict[(size_t)hh * K * N + e], 0), N - 1);
-        scnt[e] = p.pre_cnt[(size_t)hh * K * N + e];
+        t.dict[e] = min(max(p.dict[(size_t)hh * K * N + e], 0), N - 1);
+        const int c = p.pre_cnt[(size_t)hh * K * N + e];
+        t.cnt[e] = c;
+        m = max(m, c);
     }
-    for (int e = threadIdx.x; e < K * N * N; e += 256) spre[e] = p.pre[(size_t)hh * K * N * N + e];
+    for (int e = threadIdx.x; e < K * N * 16; e += 256) {
+        const int ki = e >> 4, r = e & 15;
+        t.pre[e] = r < N ? (uint8_t)p.pre[(size_t)hh * K * N * N + ki * N + r] : 0;
+    }
+    if (m) atomicMax(&t.maxc, m);
     __syncthreads();
 }
 
-// h'[i] = b[i] + sum over the preimage of i (ascending j) of v[j]; rows that
-// take no step (past L) keep their state.
-__device__ __forceinline__ float pd_scatter(float v, float bv, int k, int i, int N, const int8_t* spre,
-                                            const int32_t* scnt) {
-    const int c = scnt[k * N + i];
-    const int8_t* lst = spre + (k * N + i) * N;
-    float acc = bv;
-    for (int r = 0; r < N; ++r) {
-        if (!__any(r < c)) break;
-        const int src = r < c ? (int)lst[r] : 0;
-        const float pv = row_pull(v, src);
-        if (r < c) acc += pv;
+// Lane i of the row: acc + sum over the preimage of i under dictionary entry
+// k, in ascending column order, of v[j] (v lives in lane j of the row).  The
+// number of rounds is the head's largest preimage, uniform for the workgroup.
+__device__ __forceinline__ float pd_gather_sum(float v, float acc, int k, int i, int N, const PDShared& t) {
+    const int c = t.cnt[k * N + i];
+    const uint4 w = *reinterpret_cast<const uint4*>(t.pre + (k * N + i) * 16);
+    const int M = t.maxc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        if (r < M) {   // uniform: a scalar branch, so unused rounds cost nothing
+            const uint32_t word = r < 4 ? w.x : r < 8 ? w.y : r < 12 ? w.z : w.w;
+            const int src = (word >> (8 * (r & 3))) & 0xff;
+            const float pv = row_pull(v, src);
+            acc += r < c ? pv : 0.0f;
+        }
     }
     return acc;
 }
@@ -105,18 +126,32 @@ __device__ __forceinline__ PDRow pd_row(const PDParams& p) {
     return r;
 }
 
+// 16 steps tb.. of state i of a (L, N) stream; steps past L read 0.
+template <int NT>
+__device__ __forceinline__ void pd_load16(const float* __restrict__ base, int tb, int L, int N, int i,
+                                          float (&v)[16]) {
+    const float* __restrict__ q = base + (size_t)tb * (NT ? NT : N) + i;
+    if (tb + 16 <= L) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) v[j] = q[j * (NT ? NT : N)];
+    } else {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) v[j] = tb + j < L ? q[j * (NT ? NT : N)] : 0.0f;
+    }
+}
+
 // ---------------------------------------------------------------------------
 // forward.  SUMMARY: chunk composition (pi, D), local state from zero, sel.
+// Each 16-step block first loads everything it needs (lane l takes the
+// selection of step l; d, b and C for all 16 steps), then runs the steps.
 // ---------------------------------------------------------------------------
-template <bool SUMMARY>
+template <bool SUMMARY, int NT>
 __global__ __launch_bounds__(256) void pd_fwd_kernel(PDParams p) {
-    __shared__ int32_t sdict[kPMaxK * 16];
-    __shared__ int32_t scnt[kPMaxK * 16];
-    __shared__ int8_t spre[kPMaxK * 16 * 16];
+    __shared__ PDShared tb_;
     const PDRow r = pd_row(p);
-    pd_load_tables(p, r.hh, sdict, spre, scnt);
+    pd_load_tables(p, r.hh, tb_);
     if (!r.act) return;
-    const int N = p.N, K = p.K, L = p.L;
+    const int N = NT ? NT : p.N, K = p.K, L = p.L;
     const bool nl = r.lane < N;
     const int i = nl ? r.lane : N - 1;
     const size_t srow = (size_t)r.s * L;
@@ -129,44 +164,45 @@ __global__ __launch_bounds__(256) void pd_fwd_kernel(PDParams p) {
         if (p.ckpt_out && nl) p.ckpt_out[((size_t)r.s * p.G + r.ch) * N + i] = h;
         if (!nl) h = 0.0f;
     }
+    const float* dbase = p.d + srow * N;
+    const float* bbase = p.b + srow * N;
+    const float* cbase = p.C + srow * N;
     const int t0 = r.ch * kPChunk;
     for (int blk = 0; blk < kPChunk / 16; ++blk) {
+        const int tb = t0 + 16 * blk;
+        const int tl = tb + r.lane;          // the step whose selection this lane loads
+        int kl = 0;
+        if (tl < L) {
+            if (SUMMARY) kl = p.logits ? pd_argmax(p.logits + (srow + tl) * K, K) : p.sel_in[srow + tl];
+            else kl = p.sel[srow + tl];
+            kl = min(max(kl, 0), K - 1);   // given selections outside [0, K) are clamped
+        }
+        if (SUMMARY && p.sel_out && tl < L) p.sel_out[srow + tl] = kl;
+        float dv[16], bv[16], cv[16];
+        pd_load16<NT>(dbase, tb, L, N, i, dv);
+        pd_load16<NT>(bbase, tb, L, N, i, bv);
+        if (!SUMMARY) pd_load16<NT>(cbase, tb, L, N, i, cv);
         float yp[16];
-        int selbuf = 0;
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-            const int t = t0 + 16 * blk + j;
-            yp[j] = 0.0f;
-            const bool tv = t < L;
-            int k = 0;
-            if (tv) {
-                if (SUMMARY) k = p.logits ? pd_argmax(p.logits + (srow + t) * K, K) : p.sel_in[srow + t];
-                else k = p.sel[srow + t];
-                k = min(max(k, 0), K - 1);  // given selections outside [0, K) are clamped
-            }
-            if (r.lane == j) selbuf = k;
-            const size_t o = (srow + (tv ? t : 0)) * N + i;
-            const float dv = (tv && nl) ? p.d[o] : 0.0f;
-            const float bv = (tv && nl) ? p.b[o] : 0.0f;
-            const float hn = pd_scatter(dv * h, bv, k, i, N, spre, scnt);
+            const bool tv = tb + j < L;
+            const int k = __float_as_int(bcast16(__int_as_float(kl), j));
+            const float hn = pd_gather_sum(dv[j] * h, bv[j], k, i, N, tb_);
             if (SUMMARY) {
                 // composition with the step, later step applied last
-                const int pn = sdict[k * N + pacc];
-                const float dsrc = row_pull(dv, pacc);
+                const int pn = tb_.dict[k * N + pacc];
+                const float dsrc = row_pull(dv[j], pacc);
                 if (tv) {
                     Dacc = dsrc * Dacc;
                     pacc = pn;
                 }
             }
             if (tv) h = nl ? hn : 0.0f;
-            if (!SUMMARY) yp[j] = (tv && nl) ? p.C[o] * h : 0.0f;
+            if (!SUMMARY) yp[j] = (tv && nl) ? cv[j] * h : 0.0f;
         }
-        const int t = t0 + 16 * blk + r.lane;
-        if (SUMMARY) {
-            if (p.sel_out && t < L) p.sel_out[srow + t] = selbuf;
-        } else if (p.y) {
+        if (!SUMMARY && p.y) {
             const float ys = row_transpose_sum16(yp);
-            if (t < L) p.y[srow + t] = ys;
+            if (tl < L) p.y[srow + tl] = ys;
         }
     }
     if (!nl) return;
@@ -184,19 +220,18 @@ __global__ __launch_bounds__(256) void pd_fwd_kernel(PDParams p) {
 // backward (selection held fixed).  With nu_t = M_t^T lambda_t (nu_L = gh_last):
 //   lambda_t = C_t gy_t + nu_{t+1},   nu_t[j] = d_t[j] lambda_t[pi_t(j)],
 //   gd_t[j] = lambda_t[pi_t(j)] h_{t-1}[j],  gb_t = lambda_t,  gC_t = gy_t h_t.
-// The chunk's states are recomputed from its checkpoint into registers.
+// The chunk's states are recomputed from its checkpoint into registers, 16
+// steps per batch of loads; the reverse sweep loads its blocks in the same way.
 // SUMMARY: chunk transition (pi_c, D_c) composed right to left, and the
 // adjoint entering the chunk start from zero (R), so nu_start = D_c*nu[pi_c] + R.
 // ---------------------------------------------------------------------------
-template <bool SUMMARY>
+template <bool SUMMARY, int NT>
 __global__ __launch_bounds__(256) void pd_bwd_kernel(PDParams p) {
-    __shared__ int32_t sdict[kPMaxK * 16];
-    __shared__ int32_t scnt[kPMaxK * 16];
-    __shared__ int8_t spre[kPMaxK * 16 * 16];
+    __shared__ PDShared tb_;
     const PDRow r = pd_row(p);
-    pd_load_tables(p, r.hh, sdict, spre, scnt);
+    pd_load_tables(p, r.hh, tb_);
     if (!r.act) return;
-    const int N = p.N, L = p.L;
+    const int N = NT ? NT : p.N, K = p.K, L = p.L;
     const bool nl = r.lane < N;
     const int j = nl ? r.lane : N - 1;  // this lane's state index
     const size_t srow = (size_t)r.s * L;
@@ -208,48 +243,63 @@ __global__ __launch_bounds__(256) void pd_bwd_kernel(PDParams p) {
         if (p.G > 1) nu = p.nu_in[((size_t)r.s * p.G + r.ch) * N + j];
         else if (p.gh_last) nu = p.gh_last[(size_t)r.s * N + j];
     }
+    const float* dbase = p.d + srow * N;
+    const float* bbase = p.b + srow * N;
+    const float* cbase = p.C + srow * N;
+    auto sel_of = [&](int tl) { return tl < L ? min(max(p.sel[srow + tl], 0), K - 1) : 0; };
     float hs[kPChunk + 1];
     if (!SUMMARY) {
         hs[0] = nl ? p.ckpt[((size_t)r.s * p.G + r.ch) * N + j] : 0.0f;
 #pragma unroll
-        for (int q = 0; q < kPChunk; ++q) {
-            const int t = t0 + q;
-            const bool tv = t < L;
-            const int k = tv ? min(max(p.sel[srow + t], 0), p.K - 1) : 0;
-            const size_t o = (srow + (tv ? t : 0)) * N + j;
-            const float dv = (tv && nl) ? p.d[o] : 0.0f;
-            const float bv = (tv && nl) ? p.b[o] : 0.0f;
-            const float hn = pd_scatter(dv * hs[q], bv, k, j, N, spre, scnt);
-            hs[q + 1] = (tv && nl) ? hn : hs[q];
+        for (int blk = 0; blk < kPChunk / 16; ++blk) {
+            const int tb = t0 + 16 * blk;
+            const int kl = sel_of(tb + r.lane);
+            float dv[16], bv[16];
+            pd_load16<NT>(dbase, tb, L, N, j, dv);
+            pd_load16<NT>(bbase, tb, L, N, j, bv);
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const int k = __float_as_int(bcast16(__int_as_float(kl), q));
+                const float hn = pd_gather_sum(dv[q] * hs[16 * blk + q], bv[q], k, j, N, tb_);
+                hs[16 * blk + q + 1] = (tb + q < L && nl) ? hn : hs[16 * blk + q];
+            }
         }
     }
 #pragma unroll
-    for (int q = kPChunk - 1; q >= 0; --q) {
-        const int t = t0 + q;
-        const bool tv = t < L;
-        const int k = tv ? min(max(p.sel[srow + t], 0), p.K - 1) : 0;
-        const int pj = sdict[k * N + j];
-        const size_t o = (srow + (tv ? t : 0)) * N + j;
-        const float gyt = tv ? p.gy[srow + t] : 0.0f;
-        const float cv = (tv && nl) ? p.C[o] : 0.0f;
-        const float dv = (tv && nl) ? p.d[o] : 0.0f;
-        const float lam = fmaf(cv, gyt, nu);
-        const float lp = row_pull(lam, pj);  // lambda_t[pi_t(j)]
-        if (SUMMARY) {
-            const int pn = row_pull_i(pacc, pj);
-            const float dn = row_pull(Dacc, pj);
-            if (tv) {
-                pacc = pn;
-                Dacc = dn * dv;
-                nu = dv * lp;
+    for (int blk = kPChunk / 16 - 1; blk >= 0; --blk) {
+        const int tb = t0 + 16 * blk;
+        const int tl = tb + r.lane;
+        const int kl = sel_of(tl);
+        const float gyl = tl < L ? p.gy[srow + tl] : 0.0f;
+        float dv[16], cv[16];
+        pd_load16<NT>(dbase, tb, L, N, j, dv);
+        pd_load16<NT>(cbase, tb, L, N, j, cv);
+        const size_t obase = (srow + tb) * N + j;   // step q at obase + q * N
+#pragma unroll
+        for (int q = 15; q >= 0; --q) {
+            const bool tv = tb + q < L;
+            const int k = __float_as_int(bcast16(__int_as_float(kl), q));
+            const float gyt = bcast16(gyl, q);
+            const int pj = tb_.dict[k * N + j];
+            const float lam = fmaf(cv[q], gyt, nu);
+            const float lp = row_pull(lam, pj);  // lambda_t[pi_t(j)]
+            if (SUMMARY) {
+                const int pn = row_pull_i(pacc, pj);
+                const float dn = row_pull(Dacc, pj);
+                if (tv) {
+                    pacc = pn;
+                    Dacc = dn * dv[q];
+                    nu = dv[q] * lp;
+                }
+            } else if (tv) {
+                if (nl) {
+                    const size_t o = obase + (size_t)q * N;
+                    if (p.gb) p.gb[o] = lam;
+                    if (p.gC) p.gC[o] = gyt * hs[16 * blk + q + 1];
+                    if (p.gd) p.gd[o] = lp * hs[16 * blk + q];
+                }
+                nu = dv[q] * lp;
             }
-        } else if (tv) {
-            if (nl) {
-                if (p.gb) p.gb[o] = lam;
-                if (p.gC) p.gC[o] = gyt * hs[q + 1];
-                if (p.gd) p.gd[o] = lp * hs[q];
-            }
-            nu = dv * lp;
         }
     }
     if (!nl) return;
@@ -344,8 +394,13 @@ hipError_t launch_pd_prep(const PDParams& p, hipStream_t st) {
 }
 hipError_t launch_pd_fwd(const PDParams& p, bool summary, hipStream_t st) {
     dim3 grid((p.G + 15) / 16, p.B * p.H);
-    if (summary) pd_fwd_kernel<true><<<grid, 256, 0, st>>>(p);
-    else pd_fwd_kernel<false><<<grid, 256, 0, st>>>(p);
+    if (p.N == 16) {
+        if (summary) pd_fwd_kernel<true, 16><<<grid, 256, 0, st>>>(p);
+        else pd_fwd_kernel<false, 16><<<grid, 256, 0, st>>>(p);
+    } else {
+        if (summary) pd_fwd_kernel<true, 0><<<grid, 256, 0, st>>>(p);
+        else pd_fwd_kernel<false, 0><<<grid, 256, 0, st>>>(p);
+    }
     return hipGetLastError();
 }
 hipError_t launch_pd_combine_fwd(const PDParams& p, hipStream_t st) {
@@ -355,8 +410,13 @@ hipError_t launch_pd_combine_fwd(const PDParams& p, hipStream_t st) {
 }
 hipError_t launch_pd_bwd(const PDParams& p, bool summary, hipStream_t st) {
     dim3 grid((p.G + 15) / 16, p.B * p.H);
-    if (summary) pd_bwd_kernel<true><<<grid, 256, 0, st>>>(p);
-    else pd_bwd_kernel<false><<<grid, 256, 0, st>>>(p);
+    if (p.N == 16) {
+        if (summary) pd_bwd_kernel<true, 16><<<grid, 256, 0, st>>>(p);
+        else pd_bwd_kernel<false, 16><<<grid, 256, 0, st>>>(p);
+    } else {
+        if (summary) pd_bwd_kernel<true, 0><<<grid, 256, 0, st>>>(p);
+        else pd_bwd_kernel<false, 0><<<grid, 256, 0, st>>>(p);
+    }
     return hipGetLastError();
 }
 hipError_t launch_pd_combine_rev(const PDParams& p, hipStream_t st) {
