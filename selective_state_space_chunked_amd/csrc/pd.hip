@@ -313,12 +313,17 @@ __global__ __launch_bounds__(256) void pd_bwd_kernel(PDParams p) {
     }
 }
 
-// Chunk chains.  One 16-lane row per (batch, head), lane = state; the chain
-// over chunks is sequential, each link a PD-affine map applied to 16 values.
-// Forward link: h'[i] = S[i] + sum over columns j (ascending) with pi(j) = i of
-// D[j] h[j]; the columns are visited with DPP broadcasts.  Reverse link:
-// v'[j] = D[j] v[pi(j)] + R[j], one gather.  The next chunk's summary is
-// loaded one link ahead.
+// Chunk chains, one workgroup (16 rows of 16 lanes, lane = state) per
+// (batch, head), in three phases so the serial depth is about 3 * G / 16
+// links instead of G:
+//   1. row r composes the chunk maps of its range [r P, (r+1) P) into one map;
+//   2. row 0 chains the 16 range maps from the sequence's initial value,
+//      leaving each range's entering value in LDS;
+//   3. row r re-runs its range from that value and writes every chunk's
+//      entering value.
+// Forward maps are h -> P_pi diag(D) h + S (a scatter: the columns j with
+// pi(j) = i are visited in ascending order with DPP broadcasts); reverse maps
+// are v -> D * v[pi] + R (one gather).
 __device__ __forceinline__ float pd_link_fwd(float h, float S, float D, int pi, int i, int N) {
     const float v = D * h;
     float acc = S;
@@ -333,57 +338,93 @@ __device__ __forceinline__ float pd_link_fwd(float h, float S, float D, int pi, 
 }
 
 __global__ __launch_bounds__(256) void pd_combine_fwd_kernel(PDParams p) {
-    const int s = blockIdx.x * 16 + (threadIdx.x >> 4);
-    const int i = threadIdx.x & 15;
-    if (s >= p.B * p.H) return;  // whole rows leave together
-    const int N = p.N;
+    __shared__ float sS[16][16], sD[16][16], sH[16][16];
+    __shared__ int sPi[16][16];
+    const int s = blockIdx.x, row = threadIdx.x >> 4, i = threadIdx.x & 15;
+    const int N = p.N, G = p.G;
     const bool nl = i < N;
     const int ic = nl ? i : N - 1;
-    float h = (nl && p.h0) ? p.h0[(size_t)s * N + ic] : 0.0f;
-    size_t base = (size_t)s * p.G * N;
-    float S = p.segS[base + ic], D = p.segD[base + ic];
-    int pi = p.segPi[base + ic];
-    for (int g = 0; g < p.G; ++g) {
-        float S2 = 0.0f, D2 = 0.0f;
-        int pi2 = 0;
-        if (g + 1 < p.G) {
-            const size_t nb = base + N;
-            S2 = p.segS[nb + ic];
-            D2 = p.segD[nb + ic];
-            pi2 = p.segPi[nb + ic];
+    const int P = (G + 15) / 16;
+    const int g0 = min(row * P, G), g1 = min(g0 + P, G);
+    const size_t base = (size_t)s * G * N;
+    // phase 1: compose the chunk maps of the range, later chunk applied last:
+    // pi <- pi_g[pi], D <- D_g[pi] * D, S <- P_{pi_g} D_g S + S_g
+    float S = 0.0f, D = 1.0f;
+    int pi = i;
+    for (int g = g0; g < g1; ++g) {
+        const size_t o = base + (size_t)g * N + ic;
+        const float Sg = nl ? p.segS[o] : 0.0f, Dg = nl ? p.segD[o] : 0.0f;
+        const int pig = nl ? p.segPi[o] : i;
+        S = pd_link_fwd(S, Sg, Dg, pig, i, N);
+        if (!nl) S = 0.0f;
+        D = row_pull(Dg, pi) * D;
+        pi = row_pull_i(pig, pi);
+    }
+    sS[row][i] = S; sD[row][i] = D; sPi[row][i] = pi;
+    __syncthreads();
+    // phase 2: chain the range maps
+    if (row == 0) {
+        float h = (nl && p.h0) ? p.h0[(size_t)s * N + ic] : 0.0f;
+        for (int rr = 0; rr < 16; ++rr) {
+            sH[rr][i] = h;
+            h = pd_link_fwd(h, sS[rr][i], sD[rr][i], sPi[rr][i], i, N);
+            if (!nl) h = 0.0f;
         }
-        if (nl) p.carry_in[base + ic] = h;
-        h = pd_link_fwd(h, S, D, pi, i, N);
+    }
+    __syncthreads();
+    // phase 3: re-run the range from its entering value
+    float h = sH[row][i];
+    for (int g = g0; g < g1; ++g) {
+        const size_t o = base + (size_t)g * N + ic;
+        const float Sg = nl ? p.segS[o] : 0.0f, Dg = nl ? p.segD[o] : 0.0f;
+        const int pig = nl ? p.segPi[o] : i;
+        if (nl) p.carry_in[o] = h;
+        h = pd_link_fwd(h, Sg, Dg, pig, i, N);
         if (!nl) h = 0.0f;
-        S = S2; D = D2; pi = pi2;
-        base += N;
     }
 }
+
 __global__ __launch_bounds__(256) void pd_combine_rev_kernel(PDParams p) {
-    const int s = blockIdx.x * 16 + (threadIdx.x >> 4);
-    const int j = threadIdx.x & 15;
-    if (s >= p.B * p.H) return;
-    const int N = p.N;
+    __shared__ float sR[16][16], sD[16][16], sV[16][16];
+    __shared__ int sPi[16][16];
+    const int s = blockIdx.x, row = threadIdx.x >> 4, j = threadIdx.x & 15;
+    const int N = p.N, G = p.G;
     const bool nl = j < N;
     const int jc = nl ? j : N - 1;
-    float v = (nl && p.gh_last) ? p.gh_last[(size_t)s * N + jc] : 0.0f;
-    size_t base = ((size_t)s * p.G + p.G - 1) * N;
-    float R = p.segS[base + jc], D = p.segD[base + jc];
-    int pi = p.segPi[base + jc];
-    for (int g = p.G - 1; g >= 0; --g) {
-        float R2 = 0.0f, D2 = 0.0f;
-        int pi2 = 0;
-        if (g > 0) {
-            const size_t nb = base - N;
-            R2 = p.segS[nb + jc];
-            D2 = p.segD[nb + jc];
-            pi2 = p.segPi[nb + jc];
+    const int P = (G + 15) / 16;
+    const int g0 = min(row * P, G), g1 = min(g0 + P, G);
+    const size_t base = (size_t)s * G * N;
+    // phase 1: F = f_{g0} o ... o f_{g1-1}; composing f_g after the range so far:
+    // D <- D_g * D[pi_g], R <- D_g * R[pi_g] + R_g, pi <- pi[pi_g]
+    float R = 0.0f, D = 1.0f;
+    int pi = j;
+    for (int g = g1 - 1; g >= g0; --g) {
+        const size_t o = base + (size_t)g * N + jc;
+        const float Rg = nl ? p.segS[o] : 0.0f, Dg = nl ? p.segD[o] : 0.0f;
+        const int pig = nl ? p.segPi[o] : j;
+        R = fmaf(Dg, row_pull(R, pig), Rg);
+        D = Dg * row_pull(D, pig);
+        pi = row_pull_i(pi, pig);
+    }
+    sR[row][j] = R; sD[row][j] = D; sPi[row][j] = pi;
+    __syncthreads();
+    if (row == 0) {
+        float v = (nl && p.gh_last) ? p.gh_last[(size_t)s * N + jc] : 0.0f;
+        for (int rr = 15; rr >= 0; --rr) {
+            sV[rr][j] = v;
+            const float vn = fmaf(sD[rr][j], row_pull(v, sPi[rr][j]), sR[rr][j]);
+            v = nl ? vn : 0.0f;
         }
-        if (nl) p.nu_in[base + jc] = v;
-        const float vn = fmaf(D, row_pull(v, pi), R);
+    }
+    __syncthreads();
+    float v = sV[row][j];
+    for (int g = g1 - 1; g >= g0; --g) {
+        const size_t o = base + (size_t)g * N + jc;
+        const float Rg = nl ? p.segS[o] : 0.0f, Dg = nl ? p.segD[o] : 0.0f;
+        const int pig = nl ? p.segPi[o] : j;
+        if (nl) p.nu_in[o] = v;
+        const float vn = fmaf(Dg, row_pull(v, pig), Rg);
         v = nl ? vn : 0.0f;
-        R = R2; D = D2; pi = pi2;
-        base -= N;
     }
 }
 
@@ -404,8 +445,7 @@ hipError_t launch_pd_fwd(const PDParams& p, bool summary, hipStream_t st) {
     return hipGetLastError();
 }
 hipError_t launch_pd_combine_fwd(const PDParams& p, hipStream_t st) {
-    const int n = p.B * p.H;
-    pd_combine_fwd_kernel<<<(n + 15) / 16, 256, 0, st>>>(p);
+    pd_combine_fwd_kernel<<<p.B * p.H, 256, 0, st>>>(p);
     return hipGetLastError();
 }
 hipError_t launch_pd_bwd(const PDParams& p, bool summary, hipStream_t st) {
@@ -420,8 +460,7 @@ hipError_t launch_pd_bwd(const PDParams& p, bool summary, hipStream_t st) {
     return hipGetLastError();
 }
 hipError_t launch_pd_combine_rev(const PDParams& p, hipStream_t st) {
-    const int n = p.B * p.H;
-    pd_combine_rev_kernel<<<(n + 15) / 16, 256, 0, st>>>(p);
+    pd_combine_rev_kernel<<<p.B * p.H, 256, 0, st>>>(p);
     return hipGetLastError();
 }
 
