@@ -17,6 +17,8 @@
 // Three phases: the summary pass composes each chunk's transition (pi_c, D_c)
 // and local state (and writes sel); the combine pass chains the chunks per
 // (batch, head); the main pass re-runs each chunk from its entering state.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -78,31 +80,50 @@ __device__ __forceinline__ void pd_load_tables(const PDParams& p, int hh, PDShar
         t.cnt[e] = c;
         m = max(m, c);
     }
+    // list entries are stored as byte offsets (4 * source lane) for ds_bpermute
     for (int e = threadIdx.x; e < K * N * 16; e += 256) {
         const int ki = e >> 4, r = e & 15;
-        t.pre[e] = r < N ? (uint8_t)p.pre[(size_t)hh * K * N * N + ki * N + r] : 0;
+        t.pre[e] = r < N ? (uint8_t)(4 * p.pre[(size_t)hh * K * N * N + ki * N + r]) : 0;
     }
     if (m) atomicMax(&t.maxc, m);
     __syncthreads();
 }
 
 // Lane i of the row: acc + sum over the preimage of i under dictionary entry
-// k, in ascending column order, of v[j] (v lives in lane j of the row).  The
-// number of rounds is the head's largest preimage, uniform for the workgroup.
+// k, in ascending column order, of v[j] (v lives in lane j of the row).  RM
+// rounds, at least the head's largest preimage.
+template <int RM>
 __device__ __forceinline__ float pd_gather_sum(float v, float acc, int k, int i, int N, const PDShared& t) {
     const int c = t.cnt[k * N + i];
     const uint4 w = *reinterpret_cast<const uint4*>(t.pre + (k * N + i) * 16);
-    const int M = t.maxc;
+    const int rowbase = (threadIdx.x & 48) << 2;   // byte offset of this row's lane 0
+    // pulls in batches of up to four in flight (bounded register use)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        if (r < M) {   // uniform: a scalar branch, so unused rounds cost nothing
+    for (int r0 = 0; r0 < RM; r0 += 4) {
+        constexpr int B4 = RM < 4 ? RM : 4;
+        float pv[B4];
+#pragma unroll
+        for (int q = 0; q < B4; ++q) {
+            const int r = r0 + q;
             const uint32_t word = r < 4 ? w.x : r < 8 ? w.y : r < 12 ? w.z : w.w;
-            const int src = (word >> (8 * (r & 3))) & 0xff;
-            const float pv = row_pull(v, src);
-            acc += r < c ? pv : 0.0f;
+            const int addr = rowbase + (int)((word >> (8 * (r & 3))) & 0xff);
+            pv[q] = __int_as_float(__builtin_amdgcn_ds_bpermute(addr, __float_as_int(v)));
         }
+#pragma unroll
+        for (int q = 0; q < B4; ++q) acc += r0 + q < c ? pv[q] : 0.0f;
     }
     return acc;
+}
+
+// Run body(integral_constant<int, RM>) with the smallest supported round
+// count RM >= the head's largest preimage (uniform for the workgroup).
+template <typename F>
+__device__ __forceinline__ void pd_with_rounds(int maxc, F&& body) {
+    if (maxc <= 2) body(std::integral_constant<int, 2>{});
+    else if (maxc <= 4) body(std::integral_constant<int, 4>{});
+    else if (maxc <= 6) body(std::integral_constant<int, 6>{});
+    else if (maxc <= 8) body(std::integral_constant<int, 8>{});
+    else body(std::integral_constant<int, 16>{});
 }
 
 __device__ __forceinline__ int pd_argmax(const float* __restrict__ lg, int K) {
@@ -151,69 +172,73 @@ __global__ __launch_bounds__(256) void pd_fwd_kernel(PDParams p) {
     const PDRow r = pd_row(p);
     pd_load_tables(p, r.hh, tb_);
     if (!r.act) return;
-    const int N = NT ? NT : p.N, K = p.K, L = p.L;
-    const bool nl = r.lane < N;
-    const int i = nl ? r.lane : N - 1;
-    const size_t srow = (size_t)r.s * L;
-    float h = 0.0f;
-    int pacc = i;
-    float Dacc = 1.0f;
-    if (!SUMMARY) {
-        if (p.G > 1) h = p.carry_in[((size_t)r.s * p.G + r.ch) * N + i];
-        else if (p.h0) h = p.h0[(size_t)r.s * N + i];
-        if (p.ckpt_out && nl) p.ckpt_out[((size_t)r.s * p.G + r.ch) * N + i] = h;
-        if (!nl) h = 0.0f;
-    }
-    const float* dbase = p.d + srow * N;
-    const float* bbase = p.b + srow * N;
-    const float* cbase = p.C + srow * N;
-    const int t0 = r.ch * kPChunk;
-    for (int blk = 0; blk < kPChunk / 16; ++blk) {
-        const int tb = t0 + 16 * blk;
-        const int tl = tb + r.lane;          // the step whose selection this lane loads
-        int kl = 0;
-        if (tl < L) {
-            if (SUMMARY) kl = p.logits ? pd_argmax(p.logits + (srow + tl) * K, K) : p.sel_in[srow + tl];
-            else kl = p.sel[srow + tl];
-            kl = min(max(kl, 0), K - 1);   // given selections outside [0, K) are clamped
+    pd_with_rounds(tb_.maxc, [&](auto rounds) {
+        constexpr int RM = decltype(rounds)::value;
+        const int N = NT ? NT : p.N, K = p.K, L = p.L;
+        const bool nl = r.lane < N;
+        const int i = nl ? r.lane : N - 1;
+        const size_t srow = (size_t)r.s * L;
+        float h = 0.0f;
+        int pacc = i;
+        float Dacc = 1.0f;
+        if (!SUMMARY) {
+            if (p.G > 1) h = p.carry_in[((size_t)r.s * p.G + r.ch) * N + i];
+            else if (p.h0) h = p.h0[(size_t)r.s * N + i];
+            if (p.ckpt_out && nl) p.ckpt_out[((size_t)r.s * p.G + r.ch) * N + i] = h;
+            if (!nl) h = 0.0f;
         }
-        if (SUMMARY && p.sel_out && tl < L) p.sel_out[srow + tl] = kl;
-        float dv[16], bv[16], cv[16];
-        pd_load16<NT>(dbase, tb, L, N, i, dv);
-        pd_load16<NT>(bbase, tb, L, N, i, bv);
-        if (!SUMMARY) pd_load16<NT>(cbase, tb, L, N, i, cv);
-        float yp[16];
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const bool tv = tb + j < L;
-            const int k = __float_as_int(bcast16(__int_as_float(kl), j));
-            const float hn = pd_gather_sum(dv[j] * h, bv[j], k, i, N, tb_);
-            if (SUMMARY) {
-                // composition with the step, later step applied last
-                const int pn = tb_.dict[k * N + pacc];
-                const float dsrc = row_pull(dv[j], pacc);
-                if (tv) {
-                    Dacc = dsrc * Dacc;
-                    pacc = pn;
-                }
+        const float* dbase = p.d + srow * N;
+        const float* bbase = p.b + srow * N;
+        const float* cbase = p.C + srow * N;
+        const int t0 = r.ch * kPChunk;
+        for (int blk = 0; blk < kPChunk / 16; ++blk) {
+            const int tb = t0 + 16 * blk;
+            const int tl = tb + r.lane;          // the step whose selection this lane loads
+            int kl = 0;
+            if (tl < L) {
+                if (SUMMARY) kl = p.logits ? pd_argmax(p.logits + (srow + tl) * K, K) : p.sel_in[srow + tl];
+                else kl = p.sel[srow + tl];
+                kl = min(max(kl, 0), K - 1);   // given selections outside [0, K) are clamped
             }
-            if (tv) h = nl ? hn : 0.0f;
-            if (!SUMMARY) yp[j] = (tv && nl) ? cv[j] * h : 0.0f;
+            if (SUMMARY && p.sel_out && tl < L) p.sel_out[srow + tl] = kl;
+            float dv[16], bv[16], cv[16];
+            pd_load16<NT>(dbase, tb, L, N, i, dv);
+            pd_load16<NT>(bbase, tb, L, N, i, bv);
+            if (!SUMMARY) pd_load16<NT>(cbase, tb, L, N, i, cv);
+            float yp[16];
+    #pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const bool tv = tb + j < L;
+                const int k = __float_as_int(bcast16(__int_as_float(kl), j));
+                const float hn = pd_gather_sum<RM>(dv[j] * h, bv[j], k, i, N, tb_);
+                if (SUMMARY) {
+                    // composition with the step, later step applied last
+                    const int pn = tb_.dict[k * N + pacc];
+                    const float dsrc = row_pull(dv[j], pacc);
+                    if (tv) {
+                        Dacc = dsrc * Dacc;
+                        pacc = pn;
+                    }
+                }
+                if (tv) h = nl ? hn : 0.0f;
+                if (!SUMMARY) yp[j] = (tv && nl) ? cv[j] * h : 0.0f;
+            }
+            if (!SUMMARY && p.y) {
+                const float ys = row_transpose_sum16(yp);
+                if (tl < L) p.y[srow + tl] = ys;
+            }
         }
-        if (!SUMMARY && p.y) {
-            const float ys = row_transpose_sum16(yp);
-            if (tl < L) p.y[srow + tl] = ys;
+        if (!nl) return;
+        const size_t so = ((size_t)r.s * p.G + r.ch) * N + i;
+        if (SUMMARY) {
+            p.segPi[so] = pacc;
+            p.segD[so] = Dacc;
+            p.segS[so] = h;
+        } else if (p.h_last && r.ch == p.G - 1) {
+            p.h_last[(size_t)r.s * N + i] = h;
         }
-    }
-    if (!nl) return;
-    const size_t so = ((size_t)r.s * p.G + r.ch) * N + i;
-    if (SUMMARY) {
-        p.segPi[so] = pacc;
-        p.segD[so] = Dacc;
-        p.segS[so] = h;
-    } else if (p.h_last && r.ch == p.G - 1) {
-        p.h_last[(size_t)r.s * N + i] = h;
-    }
+
+    });
 }
 
 // ---------------------------------------------------------------------------
@@ -226,91 +251,95 @@ __global__ __launch_bounds__(256) void pd_fwd_kernel(PDParams p) {
 // adjoint entering the chunk start from zero (R), so nu_start = D_c*nu[pi_c] + R.
 // ---------------------------------------------------------------------------
 template <bool SUMMARY, int NT>
-__global__ __launch_bounds__(256) void pd_bwd_kernel(PDParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void pd_bwd_kernel(PDParams p) {
     __shared__ PDShared tb_;
     const PDRow r = pd_row(p);
     pd_load_tables(p, r.hh, tb_);
     if (!r.act) return;
-    const int N = NT ? NT : p.N, K = p.K, L = p.L;
-    const bool nl = r.lane < N;
-    const int j = nl ? r.lane : N - 1;  // this lane's state index
-    const size_t srow = (size_t)r.s * L;
-    const int t0 = r.ch * kPChunk;
-    float nu = 0.0f;
-    int pacc = j;
-    float Dacc = 1.0f;
-    if (!SUMMARY && nl) {
-        if (p.G > 1) nu = p.nu_in[((size_t)r.s * p.G + r.ch) * N + j];
-        else if (p.gh_last) nu = p.gh_last[(size_t)r.s * N + j];
-    }
-    const float* dbase = p.d + srow * N;
-    const float* bbase = p.b + srow * N;
-    const float* cbase = p.C + srow * N;
-    auto sel_of = [&](int tl) { return tl < L ? min(max(p.sel[srow + tl], 0), K - 1) : 0; };
-    float hs[kPChunk + 1];
-    if (!SUMMARY) {
-        hs[0] = nl ? p.ckpt[((size_t)r.s * p.G + r.ch) * N + j] : 0.0f;
-#pragma unroll
-        for (int blk = 0; blk < kPChunk / 16; ++blk) {
-            const int tb = t0 + 16 * blk;
-            const int kl = sel_of(tb + r.lane);
-            float dv[16], bv[16];
-            pd_load16<NT>(dbase, tb, L, N, j, dv);
-            pd_load16<NT>(bbase, tb, L, N, j, bv);
-#pragma unroll
-            for (int q = 0; q < 16; ++q) {
-                const int k = __float_as_int(bcast16(__int_as_float(kl), q));
-                const float hn = pd_gather_sum(dv[q] * hs[16 * blk + q], bv[q], k, j, N, tb_);
-                hs[16 * blk + q + 1] = (tb + q < L && nl) ? hn : hs[16 * blk + q];
+    pd_with_rounds(tb_.maxc, [&](auto rounds) {
+        constexpr int RM = decltype(rounds)::value;
+        const int N = NT ? NT : p.N, K = p.K, L = p.L;
+        const bool nl = r.lane < N;
+        const int j = nl ? r.lane : N - 1;  // this lane's state index
+        const size_t srow = (size_t)r.s * L;
+        const int t0 = r.ch * kPChunk;
+        float nu = 0.0f;
+        int pacc = j;
+        float Dacc = 1.0f;
+        if (!SUMMARY && nl) {
+            if (p.G > 1) nu = p.nu_in[((size_t)r.s * p.G + r.ch) * N + j];
+            else if (p.gh_last) nu = p.gh_last[(size_t)r.s * N + j];
+        }
+        const float* dbase = p.d + srow * N;
+        const float* bbase = p.b + srow * N;
+        const float* cbase = p.C + srow * N;
+        auto sel_of = [&](int tl) { return tl < L ? min(max(p.sel[srow + tl], 0), K - 1) : 0; };
+        float hs[kPChunk + 1];
+        if (!SUMMARY) {
+            hs[0] = nl ? p.ckpt[((size_t)r.s * p.G + r.ch) * N + j] : 0.0f;
+    #pragma unroll
+            for (int blk = 0; blk < kPChunk / 16; ++blk) {
+                const int tb = t0 + 16 * blk;
+                const int kl = sel_of(tb + r.lane);
+                float dv[16], bv[16];
+                pd_load16<NT>(dbase, tb, L, N, j, dv);
+                pd_load16<NT>(bbase, tb, L, N, j, bv);
+    #pragma unroll
+                for (int q = 0; q < 16; ++q) {
+                    const int k = __float_as_int(bcast16(__int_as_float(kl), q));
+                    const float hn = pd_gather_sum<RM>(dv[q] * hs[16 * blk + q], bv[q], k, j, N, tb_);
+                    hs[16 * blk + q + 1] = (tb + q < L && nl) ? hn : hs[16 * blk + q];
+                }
             }
         }
-    }
-#pragma unroll
-    for (int blk = kPChunk / 16 - 1; blk >= 0; --blk) {
-        const int tb = t0 + 16 * blk;
-        const int tl = tb + r.lane;
-        const int kl = sel_of(tl);
-        const float gyl = tl < L ? p.gy[srow + tl] : 0.0f;
-        float dv[16], cv[16];
-        pd_load16<NT>(dbase, tb, L, N, j, dv);
-        pd_load16<NT>(cbase, tb, L, N, j, cv);
-        const size_t obase = (srow + tb) * N + j;   // step q at obase + q * N
-#pragma unroll
-        for (int q = 15; q >= 0; --q) {
-            const bool tv = tb + q < L;
-            const int k = __float_as_int(bcast16(__int_as_float(kl), q));
-            const float gyt = bcast16(gyl, q);
-            const int pj = tb_.dict[k * N + j];
-            const float lam = fmaf(cv[q], gyt, nu);
-            const float lp = row_pull(lam, pj);  // lambda_t[pi_t(j)]
-            if (SUMMARY) {
-                const int pn = row_pull_i(pacc, pj);
-                const float dn = row_pull(Dacc, pj);
-                if (tv) {
-                    pacc = pn;
-                    Dacc = dn * dv[q];
+    #pragma unroll
+        for (int blk = kPChunk / 16 - 1; blk >= 0; --blk) {
+            const int tb = t0 + 16 * blk;
+            const int tl = tb + r.lane;
+            const int kl = sel_of(tl);
+            const float gyl = tl < L ? p.gy[srow + tl] : 0.0f;
+            float dv[16], cv[16];
+            pd_load16<NT>(dbase, tb, L, N, j, dv);
+            pd_load16<NT>(cbase, tb, L, N, j, cv);
+            const size_t obase = (srow + tb) * N + j;   // step q at obase + q * N
+    #pragma unroll
+            for (int q = 15; q >= 0; --q) {
+                const bool tv = tb + q < L;
+                const int k = __float_as_int(bcast16(__int_as_float(kl), q));
+                const float gyt = bcast16(gyl, q);
+                const int pj = tb_.dict[k * N + j];
+                const float lam = fmaf(cv[q], gyt, nu);
+                const float lp = row_pull(lam, pj);  // lambda_t[pi_t(j)]
+                if (SUMMARY) {
+                    const int pn = row_pull_i(pacc, pj);
+                    const float dn = row_pull(Dacc, pj);
+                    if (tv) {
+                        pacc = pn;
+                        Dacc = dn * dv[q];
+                        nu = dv[q] * lp;
+                    }
+                } else if (tv) {
+                    if (nl) {
+                        const size_t o = obase + (size_t)q * N;
+                        if (p.gb) p.gb[o] = lam;
+                        if (p.gC) p.gC[o] = gyt * hs[16 * blk + q + 1];
+                        if (p.gd) p.gd[o] = lp * hs[16 * blk + q];
+                    }
                     nu = dv[q] * lp;
                 }
-            } else if (tv) {
-                if (nl) {
-                    const size_t o = obase + (size_t)q * N;
-                    if (p.gb) p.gb[o] = lam;
-                    if (p.gC) p.gC[o] = gyt * hs[16 * blk + q + 1];
-                    if (p.gd) p.gd[o] = lp * hs[16 * blk + q];
-                }
-                nu = dv[q] * lp;
             }
         }
-    }
-    if (!nl) return;
-    const size_t so = ((size_t)r.s * p.G + r.ch) * N + j;
-    if (SUMMARY) {
-        p.segPi[so] = pacc;
-        p.segD[so] = Dacc;
-        p.segS[so] = nu;
-    } else if (p.gh0 && r.ch == 0) {
-        p.gh0[(size_t)r.s * N + j] = nu;
-    }
+        if (!nl) return;
+        const size_t so = ((size_t)r.s * p.G + r.ch) * N + j;
+        if (SUMMARY) {
+            p.segPi[so] = pacc;
+            p.segD[so] = Dacc;
+            p.segS[so] = nu;
+        } else if (p.gh0 && r.ch == 0) {
+            p.gh0[(size_t)r.s * N + j] = nu;
+        }
+
+    });
 }
 
 // Chunk chains, one workgroup (16 rows of 16 lanes, lane = state) per
@@ -450,12 +479,13 @@ hipError_t launch_pd_combine_fwd(const PDParams& p, hipStream_t st) {
 }
 hipError_t launch_pd_bwd(const PDParams& p, bool summary, hipStream_t st) {
     dim3 grid((p.G + 15) / 16, p.B * p.H);
-    if (p.N == 16) {
-        if (summary) pd_bwd_kernel<true, 16><<<grid, 256, 0, st>>>(p);
-        else pd_bwd_kernel<false, 16><<<grid, 256, 0, st>>>(p);
+    // the main backward keeps the generic state count: specialised to 16 its
+    // register allocation exceeds the three-waves-per-SIMD budget and spills
+    if (summary) {
+        if (p.N == 16) pd_bwd_kernel<true, 16><<<grid, 256, 0, st>>>(p);
+        else pd_bwd_kernel<true, 0><<<grid, 256, 0, st>>>(p);
     } else {
-        if (summary) pd_bwd_kernel<true, 0><<<grid, 256, 0, st>>>(p);
-        else pd_bwd_kernel<false, 0><<<grid, 256, 0, st>>>(p);
+        pd_bwd_kernel<false, 0><<<grid, 256, 0, st>>>(p);
     }
     return hipGetLastError();
 }
