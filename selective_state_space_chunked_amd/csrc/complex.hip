@@ -14,6 +14,8 @@
 // Segments along L run in parallel: a summary pass composes each segment's
 // affine map (product of a, local state), a combine pass chains the segments,
 // the main pass re-runs each segment from its exact entering state.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -37,16 +39,131 @@ __device__ __forceinline__ cd cfma(cd a, cd b, cd c) {  // a*b + c
     return {fma(a.re, b.re, fma(-a.im, b.im, c.re)), fma(a.re, b.im, fma(a.im, b.re, c.im))};
 }
 
+// Double-precision exp and sincos for the transition factors, written out
+// from their series (the library routines also carry large-argument paths
+// that cost more than the whole recurrence step).  Constants: ln 2 and pi/2
+// split into a head with trailing zero bits (so k * head is exact) and a
+// tail, each part the correctly rounded value of the exact remainder.
+constexpr double kLog2eD = 0x1.71547652b82fep+0;   // 1 / ln 2
+constexpr double kLn2Hi = 0x1.62e42ff000000p-1;    // ln 2, first 29 bits
+constexpr double kLn2Lo = -0x1.718432a1b0e26p-35;  // ln 2 - kLn2Hi
+constexpr double k2OverPi = 0x1.45f306dc9c883p-1;  // 2 / pi
+constexpr double kPio2A = 0x1.921fb54400000p+0;    // pi/2, first 33 bits
+constexpr double kPio2B = 0x1.0b4611a600000p-34;   // next 33 bits
+constexpr double kPio2C = 0x1.3198a2e037073p-69;   // remainder
+
+// exp(x) = 2^k exp(f), x = k ln 2 + f, |f| <= ln2 / 2; exp(f) by its Taylor
+// series through f^13 (truncation below 4e-18 relative).
+__device__ __forceinline__ double exp_d(double x) {
+    const double k = fmin(fmax(rint(x * kLog2eD), -1100.0), 1100.0);
+    double f = fma(-k, kLn2Hi, x);
+    f = fma(-k, kLn2Lo, f);
+    double e = 1.0 / 6227020800.0;        // 1/13!
+    e = fma(e, f, 1.0 / 479001600.0);     // 1/12!
+    e = fma(e, f, 1.0 / 39916800.0);      // 1/11!
+    e = fma(e, f, 1.0 / 3628800.0);       // 1/10!
+    e = fma(e, f, 1.0 / 362880.0);        // 1/9!
+    e = fma(e, f, 1.0 / 40320.0);         // 1/8!
+    e = fma(e, f, 1.0 / 5040.0);          // 1/7!
+    e = fma(e, f, 1.0 / 720.0);           // 1/6!
+    e = fma(e, f, 1.0 / 120.0);           // 1/5!
+    e = fma(e, f, 1.0 / 24.0);            // 1/4!
+    e = fma(e, f, 1.0 / 6.0);             // 1/3!
+    e = fma(e, f, 0.5);
+    e = fma(e, f, 1.0);
+    e = fma(e, f, 1.0);
+    return ldexp(e, (int)k);
+}
+
+// sin w and cos w for |w| <= kFastTrig: w = q pi/2 + r with |r| <= pi/4
+// (three-part reduction, exact products for |q| < 2^20), Taylor series of
+// sin r through r^17 and of cos r through r^16 (truncation below 1e-19), then
+// the quadrant q mod 4.  Larger arguments use the library routine (chosen per
+// chunk, see trans_a).
+constexpr double kFastTrig = 1.0e6;
+__device__ __forceinline__ void sincos_d(double w, double* sp, double* cp) {
+    const double q = rint(w * k2OverPi);
+    double r = fma(-q, kPio2A, w);
+    r = fma(-q, kPio2B, r);
+    r = fma(-q, kPio2C, r);
+    const double r2 = r * r;
+    double ps = 1.0 / 355687428096000.0;          // 1/17!
+    ps = fma(ps, r2, -1.0 / 1307674368000.0);     // -1/15!
+    ps = fma(ps, r2, 1.0 / 6227020800.0);         // 1/13!
+    ps = fma(ps, r2, -1.0 / 39916800.0);          // -1/11!
+    ps = fma(ps, r2, 1.0 / 362880.0);             // 1/9!
+    ps = fma(ps, r2, -1.0 / 5040.0);              // -1/7!
+    ps = fma(ps, r2, 1.0 / 120.0);                // 1/5!
+    ps = fma(ps, r2, -1.0 / 6.0);                 // -1/3!
+    const double sr = fma(r * r2, ps, r);
+    double pc = 1.0 / 20922789888000.0;           // 1/16!
+    pc = fma(pc, r2, -1.0 / 87178291200.0);       // -1/14!
+    pc = fma(pc, r2, 1.0 / 479001600.0);          // 1/12!
+    pc = fma(pc, r2, -1.0 / 3628800.0);           // -1/10!
+    pc = fma(pc, r2, 1.0 / 40320.0);              // 1/8!
+    pc = fma(pc, r2, -1.0 / 720.0);               // -1/6!
+    pc = fma(pc, r2, 1.0 / 24.0);                 // 1/4!
+    pc = fma(pc, r2, -0.5);                       // -1/2!
+    const double cr = fma(r2, pc, 1.0);
+    const int n = (int)q & 3;
+    const double s1 = (n & 1) ? cr : sr, c1 = (n & 1) ? sr : cr;
+    *sp = (n & 2) ? -s1 : s1;
+    *cp = ((n + 1) & 2) ? -c1 : c1;
+}
+
 // a = exp(r ln(lambda)) (cos w + i sin w), w = phi * theta (exact in double:
-// the product of two floats fits in the 53-bit mantissa).
+// the product of two floats fits in the 53-bit mantissa).  FAST: every
+// |w| of the chunk is at most kFastTrig.
+template <bool FAST>
 __device__ __forceinline__ cd trans_a(float r, double lnlam, float phi, float th) {
-    const double mag = exp((double)r * lnlam);
+    const double mag = exp_d((double)r * lnlam);
     double s, c;
-    sincos((double)phi * (double)th, &s, &c);
+    if (FAST) sincos_d((double)phi * (double)th, &s, &c);
+    else sincos((double)phi * (double)th, &s, &c);
     return {mag * c, mag * s};
 }
 
+// Wave maximum of |x| (all 64 lanes).
+__device__ __forceinline__ float wave_absmax(float x) {
+    float m = fabsf(x);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+    return m;
+}
+// Run body(FAST, FULL) for one chunk: FAST when no phase argument of the
+// chunk can exceed kFastTrig, FULL when all kCChunk steps lie inside L.
+template <typename F>
+__device__ __forceinline__ void cplx_chunk(float pv, float thmax, bool full, F&& body) {
+    const bool fast = !__any((double)fabsf(pv) * (double)thmax > kFastTrig);
+    if (fast) {
+        if (full) body(std::true_type{}, std::true_type{});
+        else body(std::true_type{}, std::false_type{});
+    } else {
+        body(std::false_type{}, std::false_type{});
+    }
+}
+
 __device__ __forceinline__ float lanev(float v, int j) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), j)); }
+
+// u of steps t0 .. t0+K-1 for mode mc (complex64); zero past L and on idle
+// lanes.  A block inside the sequence loads unconditionally, so all K loads
+// are in flight before the first step runs.
+template <int K>
+__device__ __forceinline__ void load_u(const float* __restrict__ urow, int t0, int L, int M, int mc, bool act,
+                                       float2 (&v)[K]) {
+    const float2* __restrict__ q = reinterpret_cast<const float2*>(urow) + (size_t)t0 * M + mc;
+    if (t0 + K <= L) {
+#pragma unroll
+        for (int j = 0; j < K; ++j) v[j] = q[(size_t)j * M];
+    } else {
+#pragma unroll
+        for (int j = 0; j < K; ++j) v[j] = t0 + j < L ? q[(size_t)j * M] : make_float2(0.0f, 0.0f);
+    }
+    if (!act) {
+#pragma unroll
+        for (int j = 0; j < K; ++j) v[j] = make_float2(0.0f, 0.0f);
+    }
+}
 
 struct CUnit {
     int s, g, b, hh, m, mc;
@@ -70,7 +187,7 @@ __device__ __forceinline__ bool cunit(const CplxParams& p, CUnit& u) {
 // forward.  SUMMARY: per segment the map h_end = P h_start + S (h_start = 0).
 // ---------------------------------------------------------------------------
 template <bool SUMMARY>
-__global__ __launch_bounds__(256) void cplx_fwd_kernel(CplxParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void cplx_fwd_kernel(CplxParams p) {
     CUnit u;
     if (!cunit(p, u)) return;
     const int L = p.L, M = p.M;
@@ -78,6 +195,7 @@ __global__ __launch_bounds__(256) void cplx_fwd_kernel(CplxParams p) {
     const double lnl = log((double)p.lam[pm]);
     const float th = p.theta[pm];
     const double c_re = p.c[2 * pm], c_im = p.c[2 * pm + 1];
+    const float thmax = wave_absmax(th);
     const size_t us = ((size_t)u.s * p.G + u.g) * M + u.mc;  // (B*H, G, M)
     cd h = {0.0, 0.0}, P = {1.0, 0.0};
     if (!SUMMARY) {
@@ -100,19 +218,25 @@ __global__ __launch_bounds__(256) void cplx_fwd_kernel(CplxParams p) {
         const float rv = tv ? p.r[(size_t)u.s * L + tl] : 0.0f;
         const float pv = tv ? p.phi[(size_t)u.s * L + tl] : 0.0f;
         float yp[kCChunk];
+        cplx_chunk(pv, thmax, t0 + kCChunk <= L, [&](auto fastc, auto fullc) {
+            constexpr bool FAST = decltype(fastc)::value, FULL = decltype(fullc)::value;
 #pragma unroll
-        for (int j = 0; j < kCChunk; ++j) {
-            const int t = t0 + j;
-            yp[j] = 0.0f;
-            if (t < L) {  // uniform
-                const cd a = trans_a(lanev(rv, j), lnl, lanev(pv, j), th);
-                cd ut = {0.0, 0.0};
-                if (u.act) ut = {urow[((size_t)t * M + u.m) * 2], urow[((size_t)t * M + u.m) * 2 + 1]};
-                h = cfma(a, h, ut);
-                if (SUMMARY) P = cmul(a, P);
-                else yp[j] = (float)fma(c_re, h.re, -c_im * h.im);
+            for (int hb = 0; hb < kCChunk / 16; ++hb) {
+                float2 uv[16];
+                load_u<16>(urow, t0 + 16 * hb, L, M, u.mc, u.act, uv);
+#pragma unroll
+                for (int jj = 0; jj < 16; ++jj) {
+                    const int j = 16 * hb + jj;
+                    yp[j] = 0.0f;
+                    if (FULL || t0 + j < L) {  // uniform
+                        const cd a = trans_a<FAST>(lanev(rv, j), lnl, lanev(pv, j), th);
+                        h = cfma(a, h, cd{uv[jj].x, uv[jj].y});
+                        if (SUMMARY) P = cmul(a, P);
+                        else yp[j] = (float)fma(c_re, h.re, -c_im * h.im);
+                    }
+                }
             }
-        }
+        });
         if (!SUMMARY && p.y) {
             const float ys = wave_transpose_sum32(yp);
             const int t = t0 + (u.m >> 1);
@@ -142,7 +266,7 @@ __global__ __launch_bounds__(256) void cplx_fwd_kernel(CplxParams p) {
 // SUMMARY: per segment the adjoint map nu_start = Q nu_end + R.
 // ---------------------------------------------------------------------------
 template <bool SUMMARY>
-__global__ __launch_bounds__(256) void cplx_bwd_kernel(CplxParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void cplx_bwd_kernel(CplxParams p) {
     CUnit u;
     if (!cunit(p, u)) return;
     const int L = p.L, M = p.M;
@@ -150,6 +274,7 @@ __global__ __launch_bounds__(256) void cplx_bwd_kernel(CplxParams p) {
     const double lnl = log((double)p.lam[pm]);
     const float th = p.theta[pm];
     const double cjr = p.c[2 * pm], cji = -(double)p.c[2 * pm + 1];  // conj(c)
+    const float thmax = wave_absmax(th);
     const size_t us = ((size_t)u.s * p.G + u.g) * M + u.mc;
     cd nu = {0.0, 0.0}, Q = {1.0, 0.0};
     if (!SUMMARY) {
@@ -168,18 +293,20 @@ __global__ __launch_bounds__(256) void cplx_bwd_kernel(CplxParams p) {
         const float rv = tv ? p.r[(size_t)u.s * L + tl] : 0.0f;
         const float pv = tv ? p.phi[(size_t)u.s * L + tl] : 0.0f;
         const float gv = tv ? p.gy[(size_t)u.s * L + tl] : 0.0f;
+        cplx_chunk(pv, thmax, t0 + kCChunk <= L, [&](auto fastc, auto fullc) {
+        constexpr bool FAST = decltype(fastc)::value, FULL = decltype(fullc)::value;
         if (SUMMARY) {
 #pragma unroll
             for (int j = kCChunk - 1; j >= 0; --j) {
-                if (t0 + j < L) {
-                    const cd a = trans_a(lanev(rv, j), lnl, lanev(pv, j), th);
+                if (FULL || t0 + j < L) {
+                    const cd a = trans_a<FAST>(lanev(rv, j), lnl, lanev(pv, j), th);
                     const double g = lanev(gv, j);
                     const cd mu = {fma(g, cjr, nu.re), fma(g, cji, nu.im)};
                     nu = cmul_conj_a(a, mu);
                     Q = cmul_conj_a(a, Q);
                 }
             }
-            continue;
+            return;
         }
         // recompute the chunk's states from its checkpoint
         float hre[kCChunk + 1], him[kCChunk + 1];
@@ -191,15 +318,19 @@ __global__ __launch_bounds__(256) void cplx_bwd_kernel(CplxParams p) {
             him[0] = (float)hcur.im;
         }
 #pragma unroll
-        for (int j = 0; j < kCChunk; ++j) {
-            if (t0 + j < L) {
-                const cd a = trans_a(lanev(rv, j), lnl, lanev(pv, j), th);
-                cd ut = {0.0, 0.0};
-                if (u.act) ut = {urow[((size_t)(t0 + j) * M + u.m) * 2], urow[((size_t)(t0 + j) * M + u.m) * 2 + 1]};
-                hcur = cfma(a, hcur, ut);
+        for (int hb = 0; hb < kCChunk / 16; ++hb) {
+            float2 uv[16];
+            load_u<16>(urow, t0 + 16 * hb, L, M, u.mc, u.act, uv);
+#pragma unroll
+            for (int jj = 0; jj < 16; ++jj) {
+                const int j = 16 * hb + jj;
+                if (FULL || t0 + j < L) {
+                    const cd a = trans_a<FAST>(lanev(rv, j), lnl, lanev(pv, j), th);
+                    hcur = cfma(a, hcur, cd{uv[jj].x, uv[jj].y});
+                }
+                hre[j + 1] = (float)hcur.re;
+                him[j + 1] = (float)hcur.im;
             }
-            hre[j + 1] = (float)hcur.re;
-            him[j + 1] = (float)hcur.im;
         }
         // reverse in two halves of 16 steps; the per-step sums over modes of
         // terms that cancel strongly are formed in fp64
@@ -212,10 +343,10 @@ __global__ __launch_bounds__(256) void cplx_bwd_kernel(CplxParams p) {
                 grp[jj] = 0.0;
                 gpp[jj] = 0.0;
                 const int t = t0 + j;
-                if (t < L) {
+                if (FULL || t < L) {
                     const float rj = lanev(rv, j), pj = lanev(pv, j);
                     const double g = lanev(gv, j);
-                    const cd a = trans_a(rj, lnl, pj, th);
+                    const cd a = trans_a<FAST>(rj, lnl, pj, th);
                     const cd mu = {fma(g, cjr, nu.re), fma(g, cji, nu.im)};
                     if (p.gu && u.act) {
                         float* dst = p.gu + (((size_t)u.s * L + t) * M + u.m) * 2;
@@ -243,6 +374,7 @@ __global__ __launch_bounds__(256) void cplx_bwd_kernel(CplxParams p) {
                 if (p.gphi) p.gphi[(size_t)u.s * L + t] = (float)sp;
             }
         }
+        });
     }
     if (!u.act) return;
     if (SUMMARY) {
