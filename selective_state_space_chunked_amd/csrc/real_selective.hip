@@ -587,23 +587,49 @@ __global__ void tile_dsum_kernel(const T* __restrict__ delta, float* __restrict_
     if (act && lane == 0) out[((size_t)b * D + dc) * ntiles + tile] = s;
 }
 
+// send[s, k] = sum of delta over the steps of tiles after k, up to t_out, in
+// double.  One workgroup per sequence: tile contributions (whole tile sums
+// before t_out's tile, the partial sum of t_out's tile, zero after it) are
+// taken in blocks of 256 from the end, suffix-scanned in LDS, and each
+// block's total is carried to the next.
 template <typename T>
-__global__ void sens_suffix_kernel(const T* __restrict__ delta, const float* __restrict__ tile_dsum,
-                                   double* __restrict__ send, int BD, int L, int ntiles, int tile_len,
-                                   int t_out) {
-    const int s = blockIdx.x * blockDim.x + threadIdx.x;
-    if (s >= BD) return;
+__global__ __launch_bounds__(256) void sens_suffix_kernel(const T* __restrict__ delta,
+                                                          const float* __restrict__ tile_dsum,
+                                                          double* __restrict__ send, int BD, int L, int ntiles,
+                                                          int tile_len, int t_out) {
+    __shared__ double sc[257];
+    const int s = blockIdx.x, tid = threadIdx.x;
     const int tout_tile = t_out / tile_len;
-    double acc = 0.0;
-    for (int tile = ntiles - 1; tile >= 0; --tile) {
-        send[(size_t)s * ntiles + tile] = acc;  // steps of later tiles up to t_out
-        if (tile < tout_tile) {
-            acc += (double)tile_dsum[(size_t)s * ntiles + tile];
-        } else if (tile == tout_tile) {
-            double part = 0.0;
-            for (int t = tile * tile_len; t <= t_out; ++t) part += (double)to_f32(delta[(size_t)s * L + t]);
-            acc += part;
+    // partial sum of t_out's own tile (fixed-order tree reduction)
+    double part = 0.0;
+    for (int t = tout_tile * tile_len + tid; t <= t_out; t += 256) part += (double)to_f32(delta[(size_t)s * L + t]);
+    sc[tid] = part;
+    __syncthreads();
+    for (int w = 128; w >= 1; w >>= 1) {
+        if (tid < w) sc[tid] += sc[tid + w];
+        __syncthreads();
+    }
+    const double tpart = sc[0];
+    __syncthreads();
+    double carry = 0.0;
+    for (int base = ((ntiles - 1) / 256) * 256; base >= 0; base -= 256) {
+        const int k = base + tid;
+        double c = 0.0;
+        if (k < tout_tile) c = (double)tile_dsum[(size_t)s * ntiles + k];
+        else if (k == tout_tile) c = tpart;
+        sc[tid] = c;
+        if (tid == 0) sc[256] = 0.0;
+        __syncthreads();
+        for (int off = 1; off < 256; off <<= 1) {   // inclusive suffix scan
+            const double v = tid + off < 256 ? sc[tid + off] : 0.0;
+            __syncthreads();
+            sc[tid] += v;
+            __syncthreads();
         }
+        if (k < ntiles) send[(size_t)s * ntiles + k] = carry + sc[tid + 1];   // tiles after k
+        const double tot = sc[0];
+        __syncthreads();
+        carry += tot;
     }
 }
 
@@ -760,10 +786,10 @@ hipError_t launch_sens_suffix(const void* delta, const float* tile_dsum, double*
                               int ntiles, int tile_len, int t_out, int dtype, hipStream_t st) {
     const int BD = B * D;
     if (dtype == 0)
-        sens_suffix_kernel<float><<<(BD + 127) / 128, 128, 0, st>>>((const float*)delta, tile_dsum, send, BD, L,
+        sens_suffix_kernel<float><<<BD, 256, 0, st>>>((const float*)delta, tile_dsum, send, BD, L,
                                                                     ntiles, tile_len, t_out);
     else
-        sens_suffix_kernel<bf16_t><<<(BD + 127) / 128, 128, 0, st>>>((const bf16_t*)delta, tile_dsum, send, BD,
+        sens_suffix_kernel<bf16_t><<<BD, 256, 0, st>>>((const bf16_t*)delta, tile_dsum, send, BD,
                                                                      L, ntiles, tile_len, t_out);
     return hipGetLastError();
 }
