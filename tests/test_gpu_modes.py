@@ -99,6 +99,15 @@ def test_complex_shapes(M, L):
     run_complex(synth.make_complex(B=1, H=2, M=M, L=L, seed=M + L))
 
 
+def test_complex_large_phase_arguments():
+    """Chunks whose phase arguments phi_t * theta_m exceed 1e6 take the library sincos; the others the series path."""
+    cfg = synth.make_complex(B=1, H=2, M=64, L=200, seed=21)
+    cfg["phi"] = cfg["phi"].copy()
+    cfg["phi"][:, :, 40:52] *= np.float32(3.0e7)   # a full chunk and part of the next
+    cfg["phi"][:, :, 195:] *= np.float32(3.0e7)    # the partial last chunk
+    run_complex(cfg)
+
+
 def test_complex_full_config():
     """B=16 H=8 M=64 L=2048 complex64, seed 0: every output compared element-wise."""
     run_complex(synth.make_complex(B=16, H=8, M=64, L=2048, seed=0))
@@ -145,6 +154,16 @@ def test_pd_small():
 @pytest.mark.parametrize("N,K,L", [(16, 8, 1), (16, 8, 64), (16, 8, 65), (5, 3, 300), (16, 64, 200), (1, 1, 130)])
 def test_pd_shapes(N, K, L):
     run_pd(synth.make_pd(B=1, H=2, N=N, L=L, K=K, seed=N * 100 + K + L))
+
+
+@pytest.mark.parametrize("m", [16, 4, 3, 2, 1])
+def test_pd_preimage_sizes(m):
+    """Dictionary entries pi_k(j) = (j + k) mod m: largest preimage ceil(16 / m), so every gather round count
+    (2, 4, 6, 8, 16) is exercised; rows >= m only receive b, which keeps the recurrence contractive."""
+    cfg = synth.make_pd(B=1, H=2, N=16, L=400, K=8, seed=30 + m)
+    j = np.arange(16)
+    cfg["dict"] = np.stack([np.stack([(j + k) % m for k in range(8)]) for _ in range(2)]).astype(np.int32)
+    run_pd(cfg)
 
 
 def test_pd_given_selection():
