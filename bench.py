@@ -21,6 +21,7 @@ from __future__ import annotations
 
 import argparse
 import ctypes
+import hashlib
 import json
 import os
 import sys
@@ -45,6 +46,25 @@ HEADLINE = "real-mamba"
 #             gdelta += A*lambda*(a*h_prev), gx term += lambda*B                = 5
 #             gB += lambda*(delta x), gC += gy*h (products + channel sums)      = 4   -> 17
 FLOPS_PER_ELEMENT = {"selective forward": 7, "selective backward": 17}
+
+# HBM bytes per launch of the dominant kernel, measured with rocprofv3 --pmc
+# FETCH_SIZE and --pmc WRITE_SIZE and scaled by what the same counters read for
+# a 1 GiB device copy (reads x2.0, writes x1.0).  Kept with the SHA-256 of the
+# kernel sources they were measured on and reported only while those are
+# unchanged (profiles/selective_mamba_layer_fwd_bwd.md holds the run).
+MEASURED_TRAFFIC = {
+    "selective backward": {"read_bytes": 511.7e6, "written_bytes": 543.8e6,
+                           "sources_sha256": "6d2abe05ed4e671996cd9b6d1c721fd4a7df125bb1859eb5b28455c8ebed8714"},
+}
+TRAFFIC_SOURCES = ("real_selective.hip", "common.hpp", "kernels.hpp")
+
+
+def kernel_sources_sha256():
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, "selective_state_space_chunked_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
 
 
 def parse():
@@ -288,8 +308,13 @@ def main():
     dom = max((k for k in kern if k in head["bytes_kernel"]), key=lambda k: kern[k][0] * kern[k][1])
     dur = kern[dom][0] * 1e-3
     flops = FLOPS_PER_ELEMENT[dom] * head["elements"]
+    meas = MEASURED_TRAFFIC.get(dom)
+    traffic = None
+    if meas and meas["sources_sha256"] == kernel_sources_sha256():
+        traffic = meas["read_bytes"] + meas["written_bytes"]
     roof = {"kernel": dom, "bound": "alu", "achieved": flops / dur / 1e12, "peak": VALU_F32_PEAK / 1e12,
-            "unit": "TFLOP/s", "frac": flops / dur / VALU_F32_PEAK, "traffic": None,
+            "unit": "TFLOP/s", "frac": flops / dur / VALU_F32_PEAK, "traffic": traffic,
+            "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
             "duration_ms": kern[dom][0], "hbm_frac": head["bytes_kernel"][dom] / dur / HBM_PEAK,
             "flops_per_element": FLOPS_PER_ELEMENT[dom]}
     others = {}
