@@ -33,8 +33,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK = 8.0e12  # MI355X HBM3E, bytes/s
-# fp32 vector peak without packed fp32: 256 CUs x 4 SIMDs x 16 lanes x 2 flops x 2.4 GHz
-VALU_F32_PEAK = 256 * 4 * 16 * 2 * 2.4e9
+# fp32 vector peak: 256 CUs x 4 SIMDs x 32 lanes per cycle x 2 flops (FMA) x 2.4 GHz = 157.3 TFLOP/s.
+# Non-packed v_fma_f32 / v_mul_f32 issue a wave64 in two cycles on gfx950 (measured), so this peak
+# holds with packed fp32 disabled; v_exp_f32 issues at a quarter of that rate.
+VALU_F32_PEAK = 256 * 4 * 32 * 2 * 2.4e9
 METRIC = "scan elements/s (B·D·N·L) fwd+bwd at 1 GPU; % of HBM peak BW"
 HEADLINE = "real-mamba"
 

@@ -23,8 +23,8 @@ namespace ssm {
 
 constexpr int kCChunk = 32;  // checkpoint interval (steps) of the complex mode
 
-// The recurrence runs in fp64 (the vector fp64 rate of CDNA4 equals its
-// unpacked fp32 rate): for the slow modes (|a| close to 1, horizons of ~10^3
+// The recurrence runs in fp64 (the vector fp64 rate of CDNA4 is half its
+// fp32 rate): for the slow modes (|a| close to 1, horizons of ~10^3
 // steps) the rounding of fp32 transition factors and states accumulates to
 // ~1e-6 relative, which the fp32 outputs must not inherit.  Streams,
 // checkpoints and outputs stay complex64.

@@ -633,77 +633,116 @@ __global__ __launch_bounds__(256) void sens_suffix_kernel(const T* __restrict__ 
     }
 }
 
+// Tiles per sensitivity workgroup: the next tile's B values and step sizes
+// are loaded while the current tile is computed.
+constexpr int kSensTiles = 4;
+
 template <typename T, int KPL, int NT>
 __global__ __launch_bounds__(256) void sens_kernel(SensParams p) {
     using Gm = TileGeom<KPL>;
     constexpr int TILE = Gm::TILE;
+    constexpr int SPT = NT ? TILE * NT / 256 : 1;   // staged values per thread (N = 16)
     __shared__ __align__(16) float sBC[16 * Gm::LDSW];
     __shared__ float sCout[16];
     const int tid = threadIdx.x, lane = tid & 15, row = tid >> 4;
-    const int b = blockIdx.y, tile = blockIdx.z;
+    const int b = blockIdx.y;
     const int d = blockIdx.x * 16 + row;
     const bool act = d < p.D;
     const int dc = act ? d : p.D - 1;
     const int N = NT ? NT : p.N, L = p.L;
     const size_t seq = (size_t)b * p.D + dc;
-    const int t0 = tile * TILE;
-    if (t0 > p.t_out) {  // whole tile after t_out: zero sensitivity
-        const int tl = t0 + lane * KPL;
-        if (act && tl < L) {
-            float z[KPL];
-#pragma unroll
-            for (int j = 0; j < KPL; ++j) z[j] = 0.0f;
-            store_run<KPL>((T*)p.s + seq * L + tl, z, p.vec != 0, L - tl);
-        }
-        return;
-    }
+    const int tile0 = blockIdx.z * kSensTiles;
+    const int tile1 = min(tile0 + kSensTiles, p.ntiles);
+    const T* Bm = (const T*)p.Bm;
+    const bool vec = p.vec != 0;
     if (tid < N) sCout[tid] = to_f32(((const T*)p.C)[((size_t)b * L + p.t_out) * N + tid]);
-    __syncthreads();
-    {
-        const T* Bm = (const T*)p.Bm;
-        for (int e = tid; e < TILE * N; e += 256) {
-            const int tt = e / N, n = e - tt * N;
-            const int t = t0 + tt;
-            float v = 0.0f;
-            if (t < L) v = to_f32(Bm[((size_t)b * L + t) * N + n]) * sCout[n];
-            sBC[Gm::idx(n, tt)] = v;
-        }
-    }
-    __syncthreads();
-    const int tl = t0 + lane * KPL;
-    float dl[KPL];
-    load_run_masked<T, KPL>((const T*)p.delta + seq * L + tl, dl, min(L, p.t_out + 1) - tl);
-    // S_j = sum of delta over steps after j up to t_out
-    float lsum = 0.0f;
-#pragma unroll
-    for (int j = 0; j < KPL; ++j) lsum += dl[j];
-    const float base = (float)p.send[seq * p.ntiles + tile] + row_excl_sum_down(lsum);
-    float S[KPL];
-    {
-        float run = 0.0f;
-#pragma unroll
-        for (int j = KPL - 1; j >= 0; --j) {
-            S[j] = base + run;
-            run += dl[j];
-        }
-    }
     float A2 = 0.0f;
     if (lane < N) A2 = p.A[(size_t)dc * N + lane] * kLog2e;
-    float acc[KPL];
+    // B of one tile: thread tid holds entries e = tid + 256 i, e = tt * N + n
+    auto fetchB = [&](int tile, float (&v)[SPT]) {
+        const int t0 = tile * TILE;
+        if constexpr (NT != 0) {
 #pragma unroll
-    for (int j = 0; j < KPL; ++j) acc[j] = 0.0f;
-    for_states<NT>(N, [&](auto st) {
-        const float A2n = st.bc(A2);
-        float bc[KPL];
-        read_run<KPL>(sBC + st.n * Gm::LDSW + lane * Gm::SEG, bc);
+            for (int q = 0; q < SPT; ++q) {
+                const int e = tid + 256 * q, tt = e / NT;
+                v[q] = t0 + tt < L ? to_f32(Bm[((size_t)b * L + t0) * NT + e]) : 0.0f;
+            }
+        }
+    };
+    auto putB = [&](int tile, const float (&v)[SPT]) {
+        if constexpr (NT != 0) {
 #pragma unroll
-        for (int j = 0; j < KPL; ++j) acc[j] = fmaf(bc[j], __builtin_amdgcn_exp2f(A2n * S[j]), acc[j]);
-    });
-    if (act && tl < L) {
-        float v[KPL];
+            for (int q = 0; q < SPT; ++q) {
+                const int e = tid + 256 * q, tt = e / NT, n = e - tt * NT;
+                sBC[Gm::idx(n, tt)] = v[q] * sCout[n];
+            }
+        } else {
+            const int t0 = tile * TILE;
+            for (int e = tid; e < TILE * N; e += 256) {
+                const int tt = e / N, n = e - tt * N;
+                const int t = t0 + tt;
+                sBC[Gm::idx(n, tt)] = t < L ? to_f32(Bm[((size_t)b * L + t) * N + n]) * sCout[n] : 0.0f;
+            }
+        }
+    };
+    float nb[SPT];
+    fetchB(tile0, nb);
+    __syncthreads();          // sCout
+    putB(tile0, nb);
+    __syncthreads();
+    for (int tile = tile0; tile < tile1; ++tile) {
+        const int t0 = tile * TILE;
+        const int tl = t0 + lane * KPL;
+        if (t0 > p.t_out) {   // tile after t_out: zero sensitivity (uniform: later tiles are too)
+            if (act && tl < L) {
+                float z[KPL];
 #pragma unroll
-        for (int j = 0; j < KPL; ++j) v[j] = (tl + j <= p.t_out) ? dl[j] * acc[j] : 0.0f;
-        store_run<KPL>((T*)p.s + seq * L + tl, v, p.vec != 0, L - tl);
+                for (int j = 0; j < KPL; ++j) z[j] = 0.0f;
+                store_run<KPL>((T*)p.s + seq * L + tl, z, vec, L - tl);
+            }
+            continue;
+        }
+        const bool more = tile + 1 < tile1 && (tile + 1) * TILE <= p.t_out;
+        if (more) fetchB(tile + 1, nb);   // in flight while this tile runs
+        float dl[KPL];
+        load_run_masked<T, KPL>((const T*)p.delta + seq * L + tl, dl, min(L, p.t_out + 1) - tl);
+        // S_j = sum of delta over steps after j up to t_out
+        float lsum = 0.0f;
+#pragma unroll
+        for (int j = 0; j < KPL; ++j) lsum += dl[j];
+        const float base = (float)p.send[seq * p.ntiles + tile] + row_excl_sum_down(lsum);
+        float S[KPL];
+        {
+            float run = 0.0f;
+#pragma unroll
+            for (int j = KPL - 1; j >= 0; --j) {
+                S[j] = base + run;
+                run += dl[j];
+            }
+        }
+        float acc[KPL];
+#pragma unroll
+        for (int j = 0; j < KPL; ++j) acc[j] = 0.0f;
+        for_states<NT>(N, [&](auto st) {
+            const float A2n = st.bc(A2);
+            float bc[KPL], e[KPL];
+            read_run<KPL>(sBC + st.n * Gm::LDSW + lane * Gm::SEG, bc);
+#pragma unroll
+            for (int j = 0; j < KPL; ++j) e[j] = __builtin_amdgcn_exp2f(A2n * S[j]);
+#pragma unroll
+            for (int j = 0; j < KPL; ++j) acc[j] = fmaf(bc[j], e[j], acc[j]);
+        });
+        if (act && tl < L) {
+            float v[KPL];
+#pragma unroll
+            for (int j = 0; j < KPL; ++j) v[j] = (tl + j <= p.t_out) ? dl[j] * acc[j] : 0.0f;
+            store_run<KPL>((T*)p.s + seq * L + tl, v, vec, L - tl);
+        }
+        if (more) {
+            __syncthreads();   // every lane is done with this tile's values
+            putB(tile + 1, nb);
+            __syncthreads();
+        }
     }
 }
 
@@ -794,7 +833,7 @@ hipError_t launch_sens_suffix(const void* delta, const float* tile_dsum, double*
     return hipGetLastError();
 }
 hipError_t launch_sens(const SensParams& p, int dtype, int kpl, hipStream_t st) {
-    dim3 grid((p.D + 15) / 16, p.B, p.ntiles);
+    dim3 grid((p.D + 15) / 16, p.B, (p.ntiles + kSensTiles - 1) / kSensTiles);
     const bool n16 = p.N == 16;
     if (dtype == 0) {
         if (n16) { SSM_DISPATCH_KPL(kpl, sens_kernel<float, K_, 16><<<grid, 256, 0, st>>>(p)) }
