@@ -28,6 +28,7 @@
 namespace ssm {
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 // backward workgroup: 32 rows of 16 lanes (channels 32*blockIdx.x ...)
 constexpr int kBwdRows = 32;
 constexpr int kBwdThreads = 16 * kBwdRows;
@@ -98,6 +99,37 @@ __device__ __forceinline__ void stage_tile(float* __restrict__ dst, const T* __r
     }
 }
 
+// Stage states [nb, ne) of a (TILE x N) block into rows 0 .. ne-nb-1 of dst.
+// NT = 16 (halves of 8 states): one thread per step, 8 contiguous values.
+template <typename T, int KPL, int NT, int NH, int THREADS = 256>
+__device__ __forceinline__ void stage_states(float* __restrict__ dst, const T* __restrict__ src, int b, int t0,
+                                             int L, int N, int nb, int ne) {
+    using G = TileGeom<KPL>;
+    if constexpr (NT == 16) {
+        for (int tt = threadIdx.x; tt < G::TILE; tt += THREADS) {
+            const int t = t0 + tt;
+            float v[NH];
+            if (t < L) load_run<NH>(src + ((size_t)b * L + t) * 16 + nb, v, true);
+            else {
+#pragma unroll
+                for (int n = 0; n < NH; ++n) v[n] = 0.0f;
+            }
+            const int base = (tt / KPL) * G::SEG + (tt % KPL);
+#pragma unroll
+            for (int n = 0; n < NH; ++n) dst[n * G::LDSW + base] = v[n];
+        }
+    } else {
+        const int cnt = ne - nb, total = G::TILE * cnt;
+        for (int e = threadIdx.x; e < total; e += THREADS) {
+            const int tt = e / cnt, n = e - tt * cnt;
+            const int t = t0 + tt;
+            float v = 0.0f;
+            if (t < L) v = to_f32(src[((size_t)b * L + t) * N + nb + n]);
+            dst[G::idx(n, tt)] = v;
+        }
+    }
+}
+
 template <int KPL>
 __device__ __forceinline__ void read_run(const float* __restrict__ s, float (&v)[KPL]) {
 #pragma unroll
@@ -110,12 +142,17 @@ __device__ __forceinline__ void read_run(const float* __restrict__ s, float (&v)
 // ---------------------------------------------------------------------------
 // forward (SUMMARY: segment summaries only, no outputs)
 // ---------------------------------------------------------------------------
+// B and C tiles are staged eight states at a time (LDS 2 x 20.7 KB for KPL 16),
+// so four workgroups fit on a CU next to the 128-VGPR budget of four waves per SIMD.
+constexpr int kFwdStates = 8;
+
 template <typename T, int KPL, int NT, bool SUMMARY>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void sel_fwd_kernel(SelFwdParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void sel_fwd_kernel(SelFwdParams p) {
     using G = TileGeom<KPL>;
     constexpr int TILE = G::TILE;
-    __shared__ __align__(16) float sB[16 * G::LDSW];
-    __shared__ __align__(16) float sC[SUMMARY ? 4 : 16 * G::LDSW];
+    constexpr int NH = kFwdStates;
+    __shared__ __align__(16) float sB[NH * G::LDSW];
+    __shared__ __align__(16) float sC[SUMMARY ? 4 : NH * G::LDSW];
 
     const int tid = threadIdx.x, lane = tid & 15, row = tid >> 4;
     const int b = blockIdx.y, g = blockIdx.z;
@@ -142,11 +179,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void s
 
     for (int tile = tile0; tile < tile1; ++tile) {
         const int t0 = tile * TILE;
-        __syncthreads();
-        stage_tile<T, KPL, NT>(sB, (const T*)p.Bm, b, t0, L, N);
-        if (!SUMMARY) stage_tile<T, KPL, NT>(sC, (const T*)p.C, b, t0, L, N);
-        __syncthreads();
-
         const int tl = t0 + lane * KPL;
         const int nval = L - tl;
         float dl[KPL], dx[KPL];
@@ -175,40 +207,55 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void s
 #pragma unroll
         for (int j = 0; j < KPL; ++j) yacc[j] = 0.0f;
 
-        for_states<NT>(N, [&](auto st) {
-            const int n = st.n;
-            const float A2n = st.bc(A2);
-            const float cin = st.bc(carry);
-            float bv[KPL], a[KPL], bx[KPL];
-            read_run<KPL>(sB + n * G::LDSW + lane * G::SEG, bv);
-            float S = 0.0f;
-#pragma unroll
-            for (int j = 0; j < KPL; ++j) {
-                a[j] = __builtin_amdgcn_exp2f(dl[j] * A2n);
-                bx[j] = dx[j] * bv[j];
-                S = fmaf(a[j], S, bx[j]);
-            }
-            float P = __builtin_amdgcn_exp2f(dsum * A2n);
-            row_scan_affine_up(P, S);
-            float newc;
-            if constexpr (SUMMARY) {
-                const float Pt = row_bcast<15>(P), St = row_bcast<15>(S);
-                newc = fmaf(Pt, cin, St);
-                if (lane == n) Pseg *= Pt;
-            } else {
-                const float hend = fmaf(P, cin, S);
-                float h = dpp<SSM_DPP_ROW_SHR(1)>(cin, hend);  // state entering this lane's run
-                newc = row_bcast<15>(hend);
-                float cv[KPL];
-                read_run<KPL>(sC + n * G::LDSW + lane * G::SEG, cv);
+        for (int nb = 0; nb < N; nb += NH) {
+            const int ne = min(nb + NH, N);
+            __syncthreads();
+            stage_states<T, KPL, NT, NH>(sB, (const T*)p.Bm, b, t0, L, N, nb, ne);
+            if (!SUMMARY) stage_states<T, KPL, NT, NH>(sC, (const T*)p.C, b, t0, L, N, nb, ne);
+            __syncthreads();
+            // the broadcasts for state n+1 are issued while state n runs (lane n+1's
+            // carry does not change during step n)
+            float A2n_nx = row_bcast_rt(A2, nb), cin_nx = row_bcast_rt(carry, nb);
+#pragma unroll 1
+            for (int n = nb; n < ne; ++n) {
+                const int nr = n - nb;   // row of state n in the staged half
+                const float A2n = A2n_nx, cin = cin_nx;
+                {
+                    const int nn = min(n + 1, ne - 1);
+                    A2n_nx = row_bcast_rt(A2, nn);
+                    cin_nx = row_bcast_rt(carry, nn);
+                }
+                float bv[KPL], a[KPL], bx[KPL];
+                read_run<KPL>(sB + nr * G::LDSW + lane * G::SEG, bv);
+                float S = 0.0f;
 #pragma unroll
                 for (int j = 0; j < KPL; ++j) {
-                    h = fmaf(a[j], h, bx[j]);
-                    yacc[j] = fmaf(cv[j], h, yacc[j]);
+                    a[j] = __builtin_amdgcn_exp2f(dl[j] * A2n);
+                    bx[j] = dx[j] * bv[j];
+                    S = fmaf(a[j], S, bx[j]);
                 }
+                float P = __builtin_amdgcn_exp2f(dsum * A2n);
+                row_scan_affine_up(P, S);
+                float newc;
+                if constexpr (SUMMARY) {
+                    const float Pt = row_bcast<15>(P), St = row_bcast<15>(S);
+                    newc = fmaf(Pt, cin, St);
+                    if (lane == n) Pseg *= Pt;
+                } else {
+                    const float hend = fmaf(P, cin, S);
+                    float h = dpp<SSM_DPP_ROW_SHR(1)>(cin, hend);  // state entering this lane's run
+                    newc = row_bcast<15>(hend);
+                    float cv[KPL];
+                    read_run<KPL>(sC + nr * G::LDSW + lane * G::SEG, cv);
+#pragma unroll
+                    for (int j = 0; j < KPL; ++j) {
+                        h = fmaf(a[j], h, bx[j]);
+                        yacc[j] = fmaf(cv[j], h, yacc[j]);
+                    }
+                }
+                carry = (lane == n) ? newc : carry;
             }
-            carry = (lane == n) ? newc : carry;
-        });
+        }
         if (!SUMMARY && p.y && act && nval > 0)
             store_run<KPL>((T*)p.y + rowoff + tl, yacc, vec, nval);
     }
@@ -263,10 +310,9 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
     const bool vec = p.vec != 0;
     const bool wantB = p.partB != nullptr, wantC = p.partC != nullptr;
 
-    float A2 = 0.0f, Ao = 0.0f, nu = 0.0f, gAacc = 0.0f, Qseg = 1.0f;
+    float A2 = 0.0f, nu = 0.0f, gAacc = 0.0f, Qseg = 1.0f;
     if (lane < N) {
-        Ao = p.A[(size_t)dc * N + lane];
-        A2 = Ao * kLog2e;
+        A2 = p.A[(size_t)dc * N + lane] * kLog2e;
         if (!SUMMARY) {
             if (p.G > 1) nu = p.nu_in[(seq * p.G + g) * N + lane];
             else if (p.gh_last) nu = p.gh_last[seq * N + lane];
@@ -314,10 +360,19 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
 #pragma unroll
         for (int j = 0; j < KPL; ++j) { Gd[j] = 0.0f; Sb[j] = 0.0f; }
 
-        for_states<NT>(N, [&](auto st) {
-            const int n = st.n;
-            const float A2n = st.bc(A2);
-            const float nin = st.bc(nu);
+        // broadcasts of state n+1 are issued while state n runs (lane n+1's adjoint
+        // does not change during step n)
+        float A2n_nx = row_bcast_rt(A2, 0), nin_nx = row_bcast_rt(nu, 0), cin_nx = row_bcast_rt(hs, 0);
+        const int n_end = NT ? NT : N;
+#pragma unroll 1
+        for (int n = 0; n < n_end; ++n) {
+            const float A2n = A2n_nx, nin = nin_nx, cin = cin_nx;
+            {
+                const int nn = min(n + 1, n_end - 1);
+                A2n_nx = row_bcast_rt(A2, nn);
+                nin_nx = row_bcast_rt(nu, nn);
+                if (!SUMMARY) cin_nx = row_bcast_rt(hs, nn);
+            }
             float a[KPL], cv[KPL];
             read_run<KPL>(sC + n * G::LDSW + lane * G::SEG, cv);
 #pragma unroll
@@ -338,8 +393,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
                 nu = (lane == n) ? newnu : nu;
             } else {
                 // forward lane fold of the recomputed states, scanned together with the adjoint
-                const float An = st.bc(Ao);
-                const float cin = st.bc(hs);
+                const float An = A2n * kLn2;   // A[d, n]
                 float bv[KPL], bx[KPL], h[KPL + 1];
                 read_run<KPL>(sB + n * G::LDSW + lane * G::SEG, bv);
                 float S = 0.0f;
@@ -442,7 +496,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
                     }
                 }
             }
-        });
+        }
         if (!SUMMARY && act && nval > 0) {
             if (p.gx) {
                 float v[KPL];
