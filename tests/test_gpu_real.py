@@ -118,3 +118,25 @@ def test_impulse_sensitivity(t_out):
     y, _ = oracle.real_fwd(x=cfg["x"], **kw)
     assert_close("s", out["s"], s, **F32)
     assert_close("y", out["y"], y, **F32)
+
+
+@pytest.mark.parametrize("dt,N,chunk_len,L,t_out", [
+    ("bf16", 16, 256, 5500, 2999),   # 22 tiles: the last workgroup of tiles is partial
+    ("f32", 5, 128, 3000, -1),       # generic state count, 128-step tiles
+    ("f32", 16, 64, 2100, 1500),     # 64-step tiles
+    ("bf16", 7, 256, 700, 0),
+])
+def test_impulse_sensitivity_variants(dt, N, chunk_len, L, t_out):
+    """Sensitivity and y for bf16 streams, generic state counts and every tile length, against the oracle."""
+    ssm = _ssm()
+    cfg = synth.make_real(B=2, D=20, N=N, L=L, dtype=dt, seed=40 + N + L)
+    t = {k: _dev(cfg[k], dt) for k in ("delta", "x", "Bm", "C")}
+    t["A"] = _dev(cfg["A"], "f32")
+    out = ssm.impulse_sensitivity(t_out=t_out, chunk_len=chunk_len, **t)
+    torch.cuda.synchronize()
+    kw = dict(delta=cfg["delta"], A=cfg["A"], Bm=cfg["Bm"], C=cfg["C"], B=2, D=20, L=L, N=N)
+    s = oracle.impulse_sens(**kw, t_out=None if t_out == -1 else t_out)
+    y, _ = oracle.real_fwd(x=cfg["x"], **kw)
+    tol = BF16 if dt == "bf16" else F32
+    assert_close("s", out["s"], s, **tol)
+    assert_close("y", out["y"], y, **tol)
