@@ -59,6 +59,7 @@ def _load():
         lib.orc_impulse_sens.argtypes = [_L, _L, _L, _L, _L] + [_D] * 5
         lib.orc_complex_fwd.argtypes = [_L, _L, _L, _L] + [_D] * 9
         lib.orc_complex_bwd.argtypes = [_L, _L, _L, _L] + [_D] * 16
+        lib.orc_complex_rtrl.argtypes = [_L, _L, _L, _L] + [_D] * 12
         lib.orc_pd_select.argtypes = [_L, _L, _L, _L, _D, _I]
         lib.orc_pd_fwd.argtypes = [_L, _L, _L, _L, _L, _I, _I] + [_D] * 6
         lib.orc_pd_dense_fwd.argtypes = [_L, _L, _L, _L, _L, _I, _I] + [_D] * 6
@@ -167,6 +168,15 @@ def complex_bwd(*, r, phi, lam, theta, u, c, h0=None, gy, ghlast=None, B, H, L, 
                             _p(glam), _p(gtheta), _p(gc), _p(gh0))
     return dict(gu=_c(gu).reshape(B, H, L, M), gr=gr, gphi=gphi, glam=glam, gtheta=gtheta,
                 gc=_c(gc).reshape(H, M), gh0=_c(gh0).reshape(B, H, M))
+
+
+def complex_rtrl(*, r, phi, lam, theta, u, c, h0=None, gy, ghlast=None, B, H, L, M):
+    """Forward-mode gradients of sum_t gy_t y_t (+ <ghlast, h_L>) w.r.t. lambda and theta, and y."""
+    args = [_w(v) for v in (r, phi, lam, theta, u, c, h0, gy, ghlast)]
+    y = _z((B, H, L))
+    glam, gtheta = _z((H, M)), _z((H, M))
+    _load().orc_complex_rtrl(B, H, L, M, *[_p(v) for v in args], _p(y), _p(glam), _p(gtheta))
+    return dict(y=y, glam=glam, gtheta=gtheta)
 
 
 # ---------------------------------------------------------------------------

@@ -375,6 +375,89 @@ void orc_complex_bwd(i64 B, i64 H, i64 L, i64 M,
     free(pc);
 }
 
+/* Forward-mode (real-time recurrent) gradient of the complex scan with respect
+ * to the per-mode parameters lambda and theta (SPARC page, abstract: the
+ * structured recurrence admits exact real-time recurrent learning).  The
+ * sensitivities of the state are carried alongside it:
+ *   a_t = exp(r_t ln lambda + i phi_t theta),  da/dlambda = a r_t / lambda,
+ *   da/dtheta = i phi_t a,
+ *   sl_t = a_t sl_{t-1} + (r_t / lambda) a_t h_{t-1},
+ *   st_t = a_t st_{t-1} + i phi_t a_t h_{t-1},     sl_{-1} = st_{-1} = 0,
+ * and the gradient of  sum_t gy_t y_t + <ghlast, h_{L-1}>  (real-pair inner
+ * product) accumulates online:
+ *   glam += gy_t Re(c sl_t),  gtheta += gy_t Re(c st_t),
+ * plus  Re(conj(ghlast) sl_{L-1})  and the same for st at the end.
+ * y (B,H,L) and ghlast (B,H,M complex) may be NULL; glam, gtheta are (H,M). */
+void orc_complex_rtrl(i64 B, i64 H, i64 L, i64 M,
+                      const double* r, const double* phi, const double* lam, const double* theta,
+                      const double* u, const double* c, const double* h0,
+                      const double* gy, const double* ghlast,
+                      double* y, double* glam, double* gtheta) {
+    int T = nthreads();
+    double* pl = (double*)calloc((size_t)T * H * M, sizeof(double));
+    double* pt = (double*)calloc((size_t)T * H * M, sizeof(double));
+    #pragma omp parallel
+    {
+        int tid = thread_id();
+        double* st = (double*)malloc(sizeof(double) * 6 * M);   /* per mode: h, sl, st (re, im) */
+        double* myl = pl + (size_t)tid * H * M;
+        double* myt = pt + (size_t)tid * H * M;
+        #pragma omp for schedule(static)
+        for (i64 s = 0; s < B * H; ++s) {
+            i64 hi = s % H;
+            for (i64 m = 0; m < M; ++m) {
+                st[6 * m] = h0 ? h0[(s * M + m) * 2] : 0.0;
+                st[6 * m + 1] = h0 ? h0[(s * M + m) * 2 + 1] : 0.0;
+                for (int k = 2; k < 6; ++k) st[6 * m + k] = 0.0;
+            }
+            for (i64 t = 0; t < L; ++t) {
+                double acc = 0.0, g = gy[s * L + t], rt = r[s * L + t], pht = phi[s * L + t];
+                for (i64 m = 0; m < M; ++m) {
+                    double lm = lam[hi * M + m], are, aim;
+                    cplx_a(rt, pht, lm, theta[hi * M + m], &are, &aim);
+                    double* q = st + 6 * m;
+                    /* a h_{t-1} */
+                    double ahre = are * q[0] - aim * q[1], ahim = are * q[1] + aim * q[0];
+                    /* a sl, a st */
+                    double aslre = are * q[2] - aim * q[3], aslim = are * q[3] + aim * q[2];
+                    double astre = are * q[4] - aim * q[5], astim = are * q[5] + aim * q[4];
+                    const double* ut = u + ((s * L + t) * M + m) * 2;
+                    q[0] = ahre + ut[0];
+                    q[1] = ahim + ut[1];
+                    q[2] = aslre + (rt / lm) * ahre;
+                    q[3] = aslim + (rt / lm) * ahim;
+                    q[4] = astre - pht * ahim;
+                    q[5] = astim + pht * ahre;
+                    double cre = c[(hi * M + m) * 2], cim = c[(hi * M + m) * 2 + 1];
+                    acc += cre * q[0] - cim * q[1];
+                    myl[hi * M + m] += g * (cre * q[2] - cim * q[3]);
+                    myt[hi * M + m] += g * (cre * q[4] - cim * q[5]);
+                }
+                if (y) y[s * L + t] = acc;
+            }
+            if (ghlast)
+                for (i64 m = 0; m < M; ++m) {
+                    const double* gl = ghlast + (s * M + m) * 2;
+                    const double* q = st + 6 * m;
+                    myl[hi * M + m] += gl[0] * q[2] + gl[1] * q[3];
+                    myt[hi * M + m] += gl[0] * q[4] + gl[1] * q[5];
+                }
+        }
+        free(st);
+    }
+    for (i64 o = 0; o < H * M; ++o) {
+        double sl = 0.0, stt = 0.0;
+        for (int k = 0; k < T; ++k) {
+            sl += pl[(size_t)k * H * M + o];
+            stt += pt[(size_t)k * H * M + o];
+        }
+        glam[o] = sl;
+        gtheta[o] = stt;
+    }
+    free(pl);
+    free(pt);
+}
+
 /* ------------------------------------------------------------------------- */
 /* PD scan.  logits (B,H,L,K); sel (B,H,L) int32; dict (H,K,N) int32 (row of  */
 /* the one in each column); d, b, C (B,H,L,N); y, gy (B,H,L); h0 (B,H,N).     */

@@ -386,6 +386,28 @@ def test_complex_adjoint_identity():
     assert abs(lhs - rhs) <= 1e-11 * max(1.0, abs(lhs))
 
 
+@pytest.mark.parametrize("name", ["lam", "theta"])
+def test_complex_rtrl_fd(name):
+    """Forward-mode (RTRL) parameter gradients against central differences of the forward scan."""
+    p = small_complex(B=2, H=2, M=3, L=10, seed=14)
+    g = oracle.complex_rtrl(**{k: p[k] for k in ("r", "phi", "lam", "theta", "u", "c", "h0", "gy", "ghlast")},
+                            B=2, H=2, L=10, M=3)
+    p["u_re"], p["u_im"] = p["u"].real.copy(), p["u"].imag.copy()
+    fd_check(_loss_complex, p, name, g["g" + name], rtol=5e-6)
+
+
+def test_complex_rtrl_equals_bptt():
+    """Forward-mode gradients equal the reverse-mode (adjoint) ones of the same loss; y equals the forward scan."""
+    p = small_complex(B=3, H=2, M=5, L=120, seed=15)
+    kw = {k: p[k] for k in ("r", "phi", "lam", "theta", "u", "c", "h0")}
+    rt = oracle.complex_rtrl(**kw, gy=p["gy"], ghlast=p["ghlast"], B=3, H=2, L=120, M=5)
+    bw = oracle.complex_bwd(**kw, gy=p["gy"], ghlast=p["ghlast"], B=3, H=2, L=120, M=5)
+    y, _ = oracle.complex_fwd(**kw, B=3, H=2, L=120, M=5)
+    close(rt["glam"], bw["glam"], rtol=1e-11, atol=1e-12)
+    close(rt["gtheta"], bw["gtheta"], rtol=1e-11, atol=1e-12)
+    close(rt["y"], y, rtol=1e-14, atol=1e-14)
+
+
 # ---------------------------------------------------------------------------
 # PD scan
 # ---------------------------------------------------------------------------
