@@ -203,6 +203,26 @@ def w_complex(steps, warmup):
                 config=dict(B=B, H=H, M=M, L=L, streams="complex64", chunk_len=32))
 
 
+def w_complex_rtrl(steps, warmup):
+    """Forward-mode glam, gtheta of the complex scan (with y), B=16 H=8 M=64 L=2048."""
+    import synth
+    import selective_state_space_chunked_amd as ssm
+    B, H, M, L = 16, 8, 64, 2048
+    cfg = synth.make_complex(B=B, H=H, M=M, L=L, seed=0)
+    t = {k: to_dev(cfg[k]) for k in ("r", "phi", "lam", "theta", "u", "c")}
+    gy = to_dev(cfg["gy"])
+    o = ssm.complex_rtrl(gy=gy, **t)
+
+    def step():
+        ssm.complex_rtrl(gy=gy, out=o, **t)
+
+    ms = time_steps(step, steps, warmup)
+    BHL, E = B * H * L, B * H * L * M
+    nbytes = E * 8 + 3 * BHL * 4 + BHL * 4                         # read u, r, phi, gy; write y
+    return dict(name="complex-rtrl", elements=E, ms=ms, kernels=profile_kernels(step), bytes_total=nbytes,
+                config=dict(B=B, H=H, M=M, L=L, streams="complex64", state="fp64 (h, dh/dlambda, dh/dtheta)"))
+
+
 def w_pd(steps, warmup):
     """PD scan, B=8 H=32 N=16 L=17000 K=8, forward (with selection) + backward."""
     import synth
@@ -322,12 +342,14 @@ def main():
     others = {}
     if not args.no_others:
         todo = [w.strip() for w in args.workloads.split(",") if w.strip()] or \
-            ["impulse", "complex", "pd", "dense", "real-small"]
+            ["impulse", "complex", "complex-rtrl", "pd", "dense", "real-small"]
         for w in todo:
             if w == "impulse":
                 others[w] = summarize(w_impulse(args.steps, args.warmup))
             elif w == "complex":
                 others[w] = summarize(w_complex(args.steps, args.warmup))
+            elif w == "complex-rtrl":
+                others[w] = summarize(w_complex_rtrl(args.steps, args.warmup))
             elif w == "pd":
                 others[w] = summarize(w_pd(args.steps, args.warmup))
             elif w == "dense":

@@ -98,6 +98,7 @@ extern "C" {
 #define SSM_OP_IMPULSE  2
 #define SSM_OP_PD_FWD   3
 #define SSM_OP_PD_BWD   4
+#define SSM_OP_COMPLEX_RTRL 5
 
 /*
  * Arguments of the diagonal scans.  Sizes: batch = B; channels = D (real) or
@@ -226,6 +227,27 @@ int ssm_scan_bwd(const ssm_scan_args* args, const ssm_scan_bwd_in* in,
  * s is (B,D,L) dtype.  SSM_REAL_SELECTIVE only. */
 int ssm_impulse_sensitivity(const ssm_scan_args* args, int64_t t_out, void* y, void* s,
                             void* ws, size_t ws_bytes, void* stream);
+
+/* Forward-mode (real-time recurrent) gradients of the complex mode w.r.t. its
+ * per-mode parameters (SPARC page, abstract: exact structured real-time
+ * recurrent learning for online credit assignment).  Carries the state
+ * sensitivities S^lambda_t = dh_t/dlambda and S^theta_t = dh_t/dtheta forward
+ * with the state:
+ *   S^lambda_t = a_t S^lambda_{t-1} + (r_t / lambda) a_t h_{t-1},
+ *   S^theta_t  = a_t S^theta_{t-1}  + i phi_t a_t h_{t-1}   (S_{-1} = 0),
+ * and accumulates, for Loss = sum_t gy_t y_t + <gh_last, h_{L-1}>,
+ *   glam[h,m]   = sum_{b,t} gy_t Re(c_m S^lambda_t) + <gh_last, S^lambda_{L-1}>,
+ *   gtheta[h,m] = the same with S^theta.
+ * The results equal ssm_scan_bwd's glam and gtheta up to rounding; no
+ * checkpoints or reverse pass.  args: mode SSM_COMPLEX_SHARED, f32 (the
+ * ssm_scan_fwd argument rules).  gy: (B,H,L) f32, required.  gh_last:
+ * nullable (B,H,M) complex64, real-pair convention.  y: nullable (B,H,L) f32,
+ * receives the forward output.  glam, gtheta: nullable (H,M) f32, overwritten.
+ * Segments of the sequence run in parallel (workspace from
+ * ssm_workspace_bytes(SSM_OP_COMPLEX_RTRL, ...)).  Errors as for ssm_scan_fwd;
+ * SSM_ERR_UNSUPPORTED for another mode. */
+int ssm_complex_rtrl(const ssm_scan_args* args, const float* gy, const float* gh_last, float* y,
+                     float* glam, float* gtheta, void* ws, size_t ws_bytes, void* stream);
 
 /* PD forward: selection (argmax of logits unless sel is given), scan, readout. */
 int pd_scan_fwd(const pd_scan_args* args, const pd_scan_fwd_out* out,

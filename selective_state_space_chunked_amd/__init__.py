@@ -1,5 +1,6 @@
 """MI355X (gfx950) selective state-space scan: forward, backward, impulse
-sensitivity and PD-transition scans behind the C ABI of include/ssmscan.h.
+sensitivity, forward-mode complex gradients and PD-transition scans behind
+the C ABI of include/ssmscan.h.
 
 The Python functions marshal torch tensors into the C ABI of libssmscan.so;
 all computation runs in the library's HIP kernels.
@@ -11,6 +12,7 @@ from .binding import (  # noqa: F401
     SSM_REAL_DENSE,
     SSM_REAL_SELECTIVE,
     SSMError,
+    complex_rtrl,
     impulse_sensitivity,
     lib,
     n_chunks,

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libssmscan.so")
 
 SSM_F32, SSM_BF16 = 0, 1
 SSM_REAL_SELECTIVE, SSM_REAL_DENSE, SSM_COMPLEX_SHARED = 0, 1, 2
-SSM_OP_SCAN_FWD, SSM_OP_SCAN_BWD, SSM_OP_IMPULSE, SSM_OP_PD_FWD, SSM_OP_PD_BWD = range(5)
+SSM_OP_SCAN_FWD, SSM_OP_SCAN_BWD, SSM_OP_IMPULSE, SSM_OP_PD_FWD, SSM_OP_PD_BWD, SSM_OP_COMPLEX_RTRL = range(6)
 
 _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -79,6 +79,7 @@ def lib():
         L.ssm_scan_bwd.argtypes = [ctypes.POINTER(ScanArgs), ctypes.POINTER(ScanBwdIn), ctypes.POINTER(ScanGrads),
                                    _vp, ctypes.c_size_t, _vp]
         L.ssm_impulse_sensitivity.argtypes = [ctypes.POINTER(ScanArgs), _i64, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+        L.ssm_complex_rtrl.argtypes = [ctypes.POINTER(ScanArgs), _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
         L.pd_scan_fwd.argtypes = [ctypes.POINTER(PDArgs), ctypes.POINTER(PDFwdOut), _vp, ctypes.c_size_t, _vp]
         L.pd_scan_bwd.argtypes = [ctypes.POINTER(PDArgs), ctypes.POINTER(PDBwdIn), ctypes.POINTER(PDGrads),
                                   _vp, ctypes.c_size_t, _vp]
@@ -262,6 +263,27 @@ def impulse_sensitivity(*, t_out=-1, want_y=True, chunk_len=0, out=None, **tenso
     ws, nws = _workspace(SSM_OP_IMPULSE, ctypes.byref(args), dev)
     _check(lib().ssm_impulse_sensitivity(ctypes.byref(args), int(t_out), _ptr(out.get("y")), _ptr(out["s"]),
                                          _ptr(ws), nws, _stream(dev)))
+    return out
+
+
+def complex_rtrl(*, gy, gh_last=None, want_y=True, chunk_len=0, out=None, **tensors):
+    """Forward-mode (real-time recurrent) glam and gtheta of the complex mode (and y).
+
+    Loss = sum_t gy_t y_t + <gh_last, h_{L-1}>; returns dict with glam, gtheta
+    ((H, M) float32) and y ((B, H, L) float32) when ``want_y``.
+    """
+    args, (Bsz, H, L, M), dev = _scan_args(SSM_COMPLEX_SHARED, chunk_len=chunk_len, **tensors)
+    _need(gy, "gy", torch.float32, (Bsz, H, L), dev)
+    _need(gh_last, "gh_last", torch.complex64, (Bsz, H, M), dev)
+    out = dict(out or {})
+    for k in ("glam", "gtheta"):
+        if k not in out:
+            out[k] = torch.empty((H, M), dtype=torch.float32, device=dev)
+    if want_y and "y" not in out:
+        out["y"] = torch.empty((Bsz, H, L), dtype=torch.float32, device=dev)
+    ws, nws = _workspace(SSM_OP_COMPLEX_RTRL, ctypes.byref(args), dev)
+    _check(lib().ssm_complex_rtrl(ctypes.byref(args), _ptr(gy), _ptr(gh_last), _ptr(out.get("y")),
+                                  _ptr(out["glam"]), _ptr(out["gtheta"]), _ptr(ws), nws, _stream(dev)))
     return out
 
 

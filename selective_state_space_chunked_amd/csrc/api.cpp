@@ -528,6 +528,8 @@ int ssm_workspace_bytes(int op, const void* args, size_t* out_bytes) {
         case SSM_OP_IMPULSE: return impulse_impl((const ssm_scan_args*)args, -1, nullptr, nullptr, nullptr, 0, nullptr, out_bytes);
         case SSM_OP_PD_FWD: return pd_fwd_impl((const pd_scan_args*)args, nullptr, nullptr, 0, nullptr, out_bytes);
         case SSM_OP_PD_BWD: return pd_bwd_impl((const pd_scan_args*)args, nullptr, nullptr, nullptr, 0, nullptr, out_bytes);
+        case SSM_OP_COMPLEX_RTRL:
+            return rtrl_impl((const ssm_scan_args*)args, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0, nullptr, out_bytes);
         default: return fail(SSM_ERR_UNSUPPORTED, "unknown op %d", op);
     }
 }
@@ -542,6 +544,10 @@ int ssm_scan_bwd(const ssm_scan_args* args, const ssm_scan_bwd_in* in, const ssm
 int ssm_impulse_sensitivity(const ssm_scan_args* args, int64_t t_out, void* y, void* s, void* ws, size_t ws_bytes,
                             void* stream) {
     return impulse_impl(args, t_out, y, s, ws, ws_bytes, (hipStream_t)stream, nullptr);
+}
+int ssm_complex_rtrl(const ssm_scan_args* args, const float* gy, const float* gh_last, float* y, float* glam,
+                     float* gtheta, void* ws, size_t ws_bytes, void* stream) {
+    return rtrl_impl(args, gy, gh_last, y, glam, gtheta, ws, ws_bytes, (hipStream_t)stream, nullptr);
 }
 int pd_scan_fwd(const pd_scan_args* args, const pd_scan_fwd_out* out, void* ws, size_t ws_bytes, void* stream) {
     return pd_fwd_impl(args, out, ws, ws_bytes, (hipStream_t)stream, nullptr);

@@ -466,6 +466,180 @@ __global__ __launch_bounds__(256) void cplx_reduce_kernel(CplxParams p, float* g
     }
 }
 
+// ---------------------------------------------------------------------------
+// Forward-mode (real-time recurrent) gradients w.r.t. lambda and theta (SPARC
+// page, abstract: exact recurrent learning for the structured recurrence).
+// With a_t = exp(r_t ln lambda + i phi_t theta): da/dlambda = a r_t / lambda and
+// da/dtheta = i phi_t a, so the state sensitivities obey the same diagonal
+// recurrence as h:
+//   sl_t = a_t sl_{t-1} + (r_t / lambda) a_t h_{t-1},  st_t = a_t st_{t-1} + i phi_t a_t h_{t-1},
+// and glam += gy_t Re(c sl_t), gtheta += gy_t Re(c st_t) accumulate online.
+// Per step (h, sl, st) -> a_t (I + N_t)(h, sl, st) + (u_t, 0, 0) with N_t
+// nonzero only in its first column and N_t N_s = 0, so a segment's map is
+// P (I + sum N) with P = prod a and sum N = (r-sum / lambda, i phi-sum):
+// segments compose from (P, sum r, sum phi, local state).  Layout as the
+// forward: one wave per (batch, head, segment), lane = mode, fp64 state.
+// ---------------------------------------------------------------------------
+template <bool SUMMARY>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void cplx_rtrl_kernel(RtrlParams p) {
+    const int wave = threadIdx.x >> 6;
+    const int unit = blockIdx.x * 4 + wave;
+    if (unit >= p.B * p.H * p.G) return;
+    const int s = unit / p.G, g = unit - s * p.G;
+    const int b = s / p.H, hh = s - b * p.H;
+    const int m = threadIdx.x & 63;
+    const bool act = m < p.M;
+    const int mc = act ? m : p.M - 1;
+    const int L = p.L, M = p.M;
+    const size_t pm = (size_t)hh * M + mc;
+    const double lamd = p.lam[pm];
+    const double lnl = log(lamd), ilam = 1.0 / lamd;
+    const float th = p.theta[pm];
+    const double c_re = p.c[2 * pm], c_im = p.c[2 * pm + 1];
+    const float thmax = wave_absmax(th);
+    const size_t us = ((size_t)s * p.G + g) * M + mc;   // (B*H, G, M)
+    cd h = {0.0, 0.0}, sl = {0.0, 0.0}, stt = {0.0, 0.0}, P = {1.0, 0.0};
+    double rsum = 0.0, psum = 0.0, gl = 0.0, gt = 0.0;
+    if (!SUMMARY) {
+        if (p.G > 1) {
+            const double* q = p.carry + 6 * us;
+            h = {q[0], q[1]}; sl = {q[2], q[3]}; stt = {q[4], q[5]};
+        } else if (p.h0) {
+            h = {p.h0[2 * ((size_t)s * M + mc)], p.h0[2 * ((size_t)s * M + mc) + 1]};
+        }
+        if (!act) h = sl = stt = cd{0.0, 0.0};
+    }
+    const int c0 = g * p.chunks_per_seg;
+    const int c1 = min(c0 + p.chunks_per_seg, p.nchunks);
+    const float* urow = p.u + (size_t)s * L * M * 2;
+    for (int ch = c0; ch < c1; ++ch) {
+        const int t0 = ch * kCChunk;
+        const int tl = t0 + (m & 31);
+        const bool tv = tl < L;
+        const float rv = tv ? p.r[(size_t)s * L + tl] : 0.0f;
+        const float pv = tv ? p.phi[(size_t)s * L + tl] : 0.0f;
+        const float gv = (!SUMMARY && tv) ? p.gy[(size_t)s * L + tl] : 0.0f;
+        float yp[kCChunk];
+        cplx_chunk(pv, thmax, t0 + kCChunk <= L, [&](auto fastc, auto fullc) {
+            constexpr bool FAST = decltype(fastc)::value, FULL = decltype(fullc)::value;
+#pragma unroll
+            for (int hb = 0; hb < kCChunk / 16; ++hb) {
+                float2 uv[16];
+                load_u<16>(urow, t0 + 16 * hb, L, M, mc, act, uv);
+#pragma unroll
+                for (int jj = 0; jj < 16; ++jj) {
+                    const int j = 16 * hb + jj;
+                    yp[j] = 0.0f;
+                    if (FULL || t0 + j < L) {  // uniform
+                        const float rj = lanev(rv, j), pj = lanev(pv, j);
+                        const cd a = trans_a<FAST>(rj, lnl, pj, th);
+                        const cd ah = cmul(a, h);
+                        const double rl = (double)rj * ilam, ph = (double)pj;
+                        sl = cfma(a, sl, cd{rl * ah.re, rl * ah.im});
+                        stt = cfma(a, stt, cd{-ph * ah.im, ph * ah.re});
+                        h = {ah.re + uv[jj].x, ah.im + uv[jj].y};
+                        if (SUMMARY) {
+                            P = cmul(a, P);
+                            rsum += (double)rj;
+                            psum += ph;
+                        } else {
+                            const double gj = lanev(gv, j);
+                            gl = fma(gj, fma(c_re, sl.re, -c_im * sl.im), gl);
+                            gt = fma(gj, fma(c_re, stt.re, -c_im * stt.im), gt);
+                            yp[j] = (float)fma(c_re, h.re, -c_im * h.im);
+                        }
+                    }
+                }
+            }
+        });
+        if (!SUMMARY && p.y) {
+            const float ys = wave_transpose_sum32(yp);
+            const int t = t0 + (m >> 1);
+            if ((m & 1) == 0 && t < L) p.y[(size_t)s * L + t] = ys;
+        }
+    }
+    if (SUMMARY) {
+        if (act) {
+            double* q = p.segS + 6 * us;
+            q[0] = h.re; q[1] = h.im; q[2] = sl.re; q[3] = sl.im; q[4] = stt.re; q[5] = stt.im;
+            p.segP[2 * us] = P.re;
+            p.segP[2 * us + 1] = P.im;
+        }
+        if (m == 0) {
+            p.segRP[2 * ((size_t)s * p.G + g)] = rsum;
+            p.segRP[2 * ((size_t)s * p.G + g) + 1] = psum;
+        }
+        return;
+    }
+    if (!act) return;
+    if (p.gh_last && g == p.G - 1) {   // <gh_last, h_{L-1}> in the real-pair convention
+        const double gre = p.gh_last[2 * ((size_t)s * M + m)], gim = p.gh_last[2 * ((size_t)s * M + m) + 1];
+        gl = fma(gre, sl.re, fma(gim, sl.im, gl));
+        gt = fma(gre, stt.re, fma(gim, stt.im, gt));
+    }
+    const size_t po = (((size_t)b * p.G + g) * p.H + hh) * M + m;
+    p.partL[po] = gl;
+    p.partT[po] = gt;
+}
+
+// Entering (h, sl, st) of every segment, one lane per (batch, head, mode).
+__global__ void cplx_rtrl_combine_kernel(RtrlParams p) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= p.B * p.H * p.M) return;
+    const int s = i / p.M, m = i - s * p.M;
+    const double ilam = 1.0 / (double)p.lam[(size_t)(s % p.H) * p.M + m];
+    cd h = {0.0, 0.0}, sl = {0.0, 0.0}, stt = {0.0, 0.0};
+    if (p.h0) h = {p.h0[2 * (size_t)i], p.h0[2 * (size_t)i + 1]};
+    for (int g = 0; g < p.G; ++g) {
+        const size_t o = ((size_t)s * p.G + g) * p.M + m;
+        double* q = p.carry + 6 * o;
+        q[0] = h.re; q[1] = h.im; q[2] = sl.re; q[3] = sl.im; q[4] = stt.re; q[5] = stt.im;
+        const cd P = {p.segP[2 * o], p.segP[2 * o + 1]};
+        const double* S = p.segS + 6 * o;
+        const double R = p.segRP[2 * ((size_t)s * p.G + g)] * ilam, Ph = p.segRP[2 * ((size_t)s * p.G + g) + 1];
+        const cd sl_in = {fma(R, h.re, sl.re), fma(R, h.im, sl.im)};
+        const cd st_in = {fma(-Ph, h.im, stt.re), fma(Ph, h.re, stt.im)};
+        sl = cfma(P, sl_in, {S[2], S[3]});
+        stt = cfma(P, st_in, {S[4], S[5]});
+        h = cfma(P, h, {S[0], S[1]});
+    }
+}
+
+// (B, G, H, M) partials -> glam, gtheta (H, M), one wave per (head, mode).
+__global__ __launch_bounds__(256) void cplx_rtrl_reduce_kernel(RtrlParams p) {
+    const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int HM = p.H * p.M;
+    if (i >= HM) return;
+    const int lane = threadIdx.x & 63;
+    double sl = 0.0, st = 0.0;
+    for (int k = lane; k < p.B * p.G; k += 64) {
+        sl += p.partL[(size_t)k * HM + i];
+        st += p.partT[(size_t)k * HM + i];
+    }
+    sl = wave_sum_f64(sl);
+    st = wave_sum_f64(st);
+    if (lane != 0) return;
+    if (p.glam) p.glam[i] = (float)sl;
+    if (p.gtheta) p.gtheta[i] = (float)st;
+}
+
+hipError_t launch_cplx_rtrl(const RtrlParams& p, bool summary, hipStream_t st) {
+    const int units = p.B * p.H * p.G;
+    if (summary) cplx_rtrl_kernel<true><<<(units + 3) / 4, 256, 0, st>>>(p);
+    else cplx_rtrl_kernel<false><<<(units + 3) / 4, 256, 0, st>>>(p);
+    return hipGetLastError();
+}
+hipError_t launch_cplx_rtrl_combine(const RtrlParams& p, hipStream_t st) {
+    const int n = p.B * p.H * p.M;
+    cplx_rtrl_combine_kernel<<<(n + 255) / 256, 256, 0, st>>>(p);
+    return hipGetLastError();
+}
+hipError_t launch_cplx_rtrl_reduce(const RtrlParams& p, hipStream_t st) {
+    const int HM = p.H * p.M;
+    cplx_rtrl_reduce_kernel<<<(HM + 3) / 4, 256, 0, st>>>(p);
+    return hipGetLastError();
+}
+
 hipError_t launch_cplx_fwd(const CplxParams& p, bool summary, hipStream_t st) {
     const int units = p.B * p.H * p.G;
     dim3 grid((units + 3) / 4), block(256);

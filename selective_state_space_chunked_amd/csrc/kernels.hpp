@@ -88,6 +88,22 @@ hipError_t launch_cplx_combine_fwd(const CplxParams& p, hipStream_t st);
 hipError_t launch_cplx_combine_rev(const CplxParams& p, hipStream_t st);
 hipError_t launch_cplx_reduce(const CplxParams& p, float* glam, float* gtheta, float* gc, hipStream_t st);
 
+struct RtrlParams {
+    const float* r; const float* phi; const float* lam; const float* theta;
+    const float* u; const float* c; const float* h0;
+    const float* gy; const float* gh_last;
+    float* y; float* glam; float* gtheta;
+    double* segP;    // (B,H,G,M) complex: product of a over the segment
+    double* segS;    // (B,H,G,M) x (h, sl, st) complex: local state from zero
+    double* segRP;   // (B,H,G) x (sum r, sum phi)
+    double* carry;   // (B,H,G,M) x (h, sl, st) complex entering each segment
+    double* partL; double* partT;   // (B,G,H,M)
+    int B, H, L, M, nchunks, chunks_per_seg, G;
+};
+hipError_t launch_cplx_rtrl(const RtrlParams& p, bool summary, hipStream_t st);
+hipError_t launch_cplx_rtrl_combine(const RtrlParams& p, hipStream_t st);
+hipError_t launch_cplx_rtrl_reduce(const RtrlParams& p, hipStream_t st);
+
 // ------------------------------- PD ----------------------------------------
 struct PDParams {
     const float* logits; const int32_t* sel_in; const int32_t* dict;

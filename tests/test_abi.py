@@ -22,7 +22,7 @@ def header_functions():
 def test_exports_every_declared_function():
     names = header_functions()
     assert {"ssm_scan_fwd", "ssm_scan_bwd", "ssm_impulse_sensitivity", "pd_scan_fwd", "pd_scan_bwd",
-            "ssm_workspace_bytes"} <= set(names)
+            "ssm_complex_rtrl", "ssm_workspace_bytes"} <= set(names)
     lib = B.lib()
     missing = [n for n in names if not hasattr(lib, n)]
     assert not missing, missing
@@ -36,6 +36,7 @@ def test_header_constants_match_binding():
     assert consts["SSM_REAL_DENSE"] == B.SSM_REAL_DENSE
     assert consts["SSM_COMPLEX_SHARED"] == B.SSM_COMPLEX_SHARED
     assert consts["SSM_OP_PD_BWD"] == B.SSM_OP_PD_BWD
+    assert consts["SSM_OP_COMPLEX_RTRL"] == B.SSM_OP_COMPLEX_RTRL
     assert B.lib().ssm_abi_version() == consts["SSM_ABI_VERSION"]
 
 
@@ -157,3 +158,33 @@ def test_pd_workspace_query():
     n = ctypes.c_size_t()
     assert B.lib().ssm_workspace_bytes(B.SSM_OP_PD_BWD, ctypes.byref(pd_args()), ctypes.byref(n)) == 0
     assert n.value > 0
+
+
+def cplx_args(**over):
+    a = B.ScanArgs(mode=B.SSM_COMPLEX_SHARED, dtype=B.SSM_F32, batch=2, channels=4, length=1000, state=64,
+                   chunk_len=0, r=FAKE, phi=FAKE * 2, lam=FAKE * 3, theta=FAKE * 4, u=FAKE * 8, c=FAKE * 16)
+    for k, v in over.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_complex_rtrl_host_checks():
+    """Workspace query and argument checks of the forward-mode gradient entry point."""
+    L = B.lib()
+    rc, n = ws_bytes(B.SSM_OP_COMPLEX_RTRL, cplx_args())
+    assert rc == 0 and n > 0, L.ssm_last_error_detail()
+    # one segment workspace grows with B*H*M only, not with L
+    _, n2 = ws_bytes(B.SSM_OP_COMPLEX_RTRL, cplx_args(length=100000))
+    assert n2 < 64 * n
+    rc, _ = ws_bytes(B.SSM_OP_COMPLEX_RTRL, sel_args())
+    assert rc == status("SSM_ERR_UNSUPPORTED")
+    a = cplx_args()
+    gy, gl, gt = FAKE * 32, FAKE * 64, FAKE * 65
+    rc = L.ssm_complex_rtrl(ctypes.byref(a), None, None, None, gl, gt, None, 0, None)
+    assert rc == status("SSM_ERR_NULL")
+    rc = L.ssm_complex_rtrl(ctypes.byref(a), gy, None, None, FAKE * 2 + 4, gt, None, 0, None)  # glam inside phi
+    assert rc == status("SSM_ERR_LAYOUT"), L.ssm_last_error_detail()
+    rc = L.ssm_complex_rtrl(ctypes.byref(a), gy, FAKE * 40 + 4, None, gl, gt, None, 0, None)  # gh_last misaligned
+    assert rc == status("SSM_ERR_LAYOUT")
+    rc = L.ssm_complex_rtrl(ctypes.byref(a), gy, None, None, gl, gt, None, 0, None)
+    assert rc == status("SSM_ERR_WORKSPACE")

@@ -114,6 +114,66 @@ def test_complex_full_config():
 
 
 # ---------------------------------------------------------------------------
+# complex: forward-mode (RTRL) gradients of lambda and theta
+# ---------------------------------------------------------------------------
+def run_complex_rtrl(cfg, h0=None, ghl=None):
+    """GPU forward-mode glam, gtheta against the oracle's forward-mode recursion,
+    and against the GPU reverse-mode (BPTT) gradients of the same loss."""
+    ssm = _ssm()
+    B, H, L, M = cfg["B"], cfg["H"], cfg["L"], cfg["M"]
+    t = {k: T(cfg[k]) for k in ("r", "phi", "lam", "theta", "u", "c")}
+    if h0 is not None:
+        t["h0"] = T(h0.astype(np.complex64))
+    gyt = T(cfg["gy"])
+    glt = None if ghl is None else T(ghl.astype(np.complex64))
+    g = ssm.complex_rtrl(gy=gyt, gh_last=glt, **t)
+    g2 = ssm.complex_rtrl(gy=gyt, gh_last=glt, want_y=False, **t)
+    bp = ssm.scan_bwd(ssm.SSM_COMPLEX_SHARED, gy=gyt, gh_last=glt, want=("glam", "gtheta"), **t)
+    torch.cuda.synchronize()
+    kw = {k: cfg[k] for k in ("r", "phi", "lam", "theta", "u", "c")}
+    h0c = None if h0 is None else h0.astype(np.complex64)
+    o = oracle.complex_rtrl(**kw, h0=h0c, gy=cfg["gy"], ghlast=None if ghl is None else ghl.astype(np.complex64),
+                            B=B, H=H, L=L, M=M)
+    assert_close("y", g["y"], o["y"], **F32)
+    for k in ("glam", "gtheta"):
+        assert_close(k, g[k], o[k], **F32)
+        assert_close(k + " vs bptt", g[k], bp[k].cpu().numpy().astype(np.float64), rtol=2e-4, atol=2e-5)
+        assert torch.equal(g[k], g2[k]), k
+
+
+def test_complex_rtrl_small():
+    cfg = synth.make_complex(B=2, H=3, M=64, L=300, seed=11)
+    g = np.random.default_rng(12)
+    run_complex_rtrl(cfg, h0=g.standard_normal((2, 3, 64)) + 1j * g.standard_normal((2, 3, 64)),
+                     ghl=g.standard_normal((2, 3, 64)) + 1j * g.standard_normal((2, 3, 64)))
+
+
+@pytest.mark.parametrize("M,L", [(5, 100), (64, 1), (64, 33), (17, 700)])
+def test_complex_rtrl_shapes(M, L):
+    run_complex_rtrl(synth.make_complex(B=1, H=2, M=M, L=L, seed=3 * M + L))
+
+
+def test_complex_rtrl_many_segments():
+    """B*H small, L long: many segments chained by the combine pass."""
+    cfg = synth.make_complex(B=1, H=1, M=64, L=6000, seed=13)
+    g = np.random.default_rng(14)
+    run_complex_rtrl(cfg, h0=g.standard_normal((1, 1, 64)) + 1j * g.standard_normal((1, 1, 64)),
+                     ghl=g.standard_normal((1, 1, 64)) + 1j * g.standard_normal((1, 1, 64)))
+
+
+def test_complex_rtrl_large_phase_arguments():
+    cfg = synth.make_complex(B=1, H=2, M=64, L=200, seed=22)
+    cfg["phi"] = cfg["phi"].copy()
+    cfg["phi"][:, :, 40:52] *= np.float32(3.0e7)
+    run_complex_rtrl(cfg)
+
+
+def test_complex_rtrl_full_config():
+    """B=16 H=8 M=64 L=2048, seed 0."""
+    run_complex_rtrl(synth.make_complex(B=16, H=8, M=64, L=2048, seed=0))
+
+
+# ---------------------------------------------------------------------------
 # PD
 # ---------------------------------------------------------------------------
 def run_pd(cfg, h0=None, ghl=None, use_sel=False):
