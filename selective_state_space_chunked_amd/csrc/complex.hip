@@ -399,6 +399,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
     }
 }
 
+// complex value i of an interleaved (re, im) fp64 array, as one 16-byte access
+__device__ __forceinline__ cd ld_cd(const double* base, size_t i) {
+    const double2 v = reinterpret_cast<const double2*>(base)[i];
+    return {v.x, v.y};
+}
+__device__ __forceinline__ void st_cd(double* base, size_t i, cd v) {
+    reinterpret_cast<double2*>(base)[i] = make_double2(v.re, v.im);
+}
+
 // segment combines, one thread per (sequence, mode)
 __global__ void cplx_combine_fwd_kernel(CplxParams p) {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -406,11 +415,16 @@ __global__ void cplx_combine_fwd_kernel(CplxParams p) {
     const int s = i / p.M, m = i - s * p.M;
     cd h = {0.0, 0.0};
     if (p.h0) h = {p.h0[2 * (size_t)i], p.h0[2 * (size_t)i + 1]};
-    for (int g = 0; g < p.G; ++g) {
-        const size_t o = ((size_t)s * p.G + g) * p.M + m;
-        p.carry_in[2 * o] = h.re;
-        p.carry_in[2 * o + 1] = h.im;
-        h = cfma({p.segP[2 * o], p.segP[2 * o + 1]}, h, {p.segS[2 * o], p.segS[2 * o + 1]});
+    // the next segment's summary is loaded before this one's carry is stored
+    // (the stores could alias the summaries as far as the compiler knows)
+    size_t o = (size_t)s * p.G * p.M + m;
+    cd P = ld_cd(p.segP, o), S = ld_cd(p.segS, o);
+    for (int g = 0; g < p.G; ++g, o += p.M) {
+        cd Pn = P, Sn = S;
+        if (g + 1 < p.G) { Pn = ld_cd(p.segP, o + p.M); Sn = ld_cd(p.segS, o + p.M); }
+        st_cd(p.carry_in, o, h);
+        h = cfma(P, h, S);
+        P = Pn; S = Sn;
     }
 }
 __global__ void cplx_combine_rev_kernel(CplxParams p) {
@@ -419,11 +433,14 @@ __global__ void cplx_combine_rev_kernel(CplxParams p) {
     const int s = i / p.M, m = i - s * p.M;
     cd v = {0.0, 0.0};
     if (p.gh_last) v = {p.gh_last[2 * (size_t)i], p.gh_last[2 * (size_t)i + 1]};
-    for (int g = p.G - 1; g >= 0; --g) {
-        const size_t o = ((size_t)s * p.G + g) * p.M + m;
-        p.nu_in[2 * o] = v.re;
-        p.nu_in[2 * o + 1] = v.im;
-        v = cfma({p.segQ[2 * o], p.segQ[2 * o + 1]}, v, {p.segR[2 * o], p.segR[2 * o + 1]});
+    size_t o = ((size_t)s * p.G + p.G - 1) * p.M + m;
+    cd Q = ld_cd(p.segQ, o), R = ld_cd(p.segR, o);
+    for (int g = p.G - 1; g >= 0; --g, o -= p.M) {
+        cd Qn = Q, Rn = R;
+        if (g > 0) { Qn = ld_cd(p.segQ, o - p.M); Rn = ld_cd(p.segR, o - p.M); }
+        st_cd(p.nu_in, o, v);
+        v = cfma(Q, v, R);
+        Q = Qn; R = Rn;
     }
 }
 // (B,G,H,M) partials -> (H,M): one wave per (head, mode); lane l adds the
@@ -480,6 +497,8 @@ __global__ __launch_bounds__(256) void cplx_reduce_kernel(CplxParams p, float* g
 // segments compose from (P, sum r, sum phi, local state).  Layout as the
 // forward: one wave per (batch, head, segment), lane = mode, fp64 state.
 // ---------------------------------------------------------------------------
+// Triples (h, sl, st) are stored as three planes of complex values, so a wave's
+// 64 modes move as contiguous 1 KB rows.
 template <bool SUMMARY>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void cplx_rtrl_kernel(RtrlParams p) {
     const int wave = threadIdx.x >> 6;
@@ -502,8 +521,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
     double rsum = 0.0, psum = 0.0, gl = 0.0, gt = 0.0;
     if (!SUMMARY) {
         if (p.G > 1) {
-            const double* q = p.carry + 6 * us;
-            h = {q[0], q[1]}; sl = {q[2], q[3]}; stt = {q[4], q[5]};
+            const size_t n3 = (size_t)p.B * p.H * p.G * M;
+            h = ld_cd(p.carry, us);
+            sl = ld_cd(p.carry, n3 + us);
+            stt = ld_cd(p.carry, 2 * n3 + us);
         } else if (p.h0) {
             h = {p.h0[2 * ((size_t)s * M + mc)], p.h0[2 * ((size_t)s * M + mc) + 1]};
         }
@@ -560,10 +581,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
     }
     if (SUMMARY) {
         if (act) {
-            double* q = p.segS + 6 * us;
-            q[0] = h.re; q[1] = h.im; q[2] = sl.re; q[3] = sl.im; q[4] = stt.re; q[5] = stt.im;
-            p.segP[2 * us] = P.re;
-            p.segP[2 * us + 1] = P.im;
+            const size_t n3 = (size_t)p.B * p.H * p.G * M;
+            st_cd(p.segS, us, h);
+            st_cd(p.segS, n3 + us, sl);
+            st_cd(p.segS, 2 * n3 + us, stt);
+            st_cd(p.segP, us, P);
         }
         if (m == 0) {
             p.segRP[2 * ((size_t)s * p.G + g)] = rsum;
@@ -588,20 +610,37 @@ __global__ void cplx_rtrl_combine_kernel(RtrlParams p) {
     if (i >= p.B * p.H * p.M) return;
     const int s = i / p.M, m = i - s * p.M;
     const double ilam = 1.0 / (double)p.lam[(size_t)(s % p.H) * p.M + m];
+    const size_t n3 = (size_t)p.B * p.H * p.G * p.M;
     cd h = {0.0, 0.0}, sl = {0.0, 0.0}, stt = {0.0, 0.0};
     if (p.h0) h = {p.h0[2 * (size_t)i], p.h0[2 * (size_t)i + 1]};
-    for (int g = 0; g < p.G; ++g) {
+    // segment g's summary is loaded while segment g-1 is applied (the loads do
+    // not depend on the chain)
+    auto load = [&](int g, cd& P, cd& S0, cd& S1, cd& S2, double& R, double& Ph) {
         const size_t o = ((size_t)s * p.G + g) * p.M + m;
-        double* q = p.carry + 6 * o;
-        q[0] = h.re; q[1] = h.im; q[2] = sl.re; q[3] = sl.im; q[4] = stt.re; q[5] = stt.im;
-        const cd P = {p.segP[2 * o], p.segP[2 * o + 1]};
-        const double* S = p.segS + 6 * o;
-        const double R = p.segRP[2 * ((size_t)s * p.G + g)] * ilam, Ph = p.segRP[2 * ((size_t)s * p.G + g) + 1];
+        P = ld_cd(p.segP, o);
+        S0 = ld_cd(p.segS, o);
+        S1 = ld_cd(p.segS, n3 + o);
+        S2 = ld_cd(p.segS, 2 * n3 + o);
+        R = p.segRP[2 * ((size_t)s * p.G + g)] * ilam;
+        Ph = p.segRP[2 * ((size_t)s * p.G + g) + 1];
+    };
+    cd P, S0, S1, S2;
+    double R, Ph;
+    load(0, P, S0, S1, S2, R, Ph);
+    for (int g = 0; g < p.G; ++g) {
+        cd Pn = P, S0n = S0, S1n = S1, S2n = S2;
+        double Rn = R, Phn = Ph;
+        if (g + 1 < p.G) load(g + 1, Pn, S0n, S1n, S2n, Rn, Phn);
+        const size_t o = ((size_t)s * p.G + g) * p.M + m;
+        st_cd(p.carry, o, h);
+        st_cd(p.carry, n3 + o, sl);
+        st_cd(p.carry, 2 * n3 + o, stt);
         const cd sl_in = {fma(R, h.re, sl.re), fma(R, h.im, sl.im)};
         const cd st_in = {fma(-Ph, h.im, stt.re), fma(Ph, h.re, stt.im)};
-        sl = cfma(P, sl_in, {S[2], S[3]});
-        stt = cfma(P, st_in, {S[4], S[5]});
-        h = cfma(P, h, {S[0], S[1]});
+        sl = cfma(P, sl_in, S1);
+        stt = cfma(P, st_in, S2);
+        h = cfma(P, h, S0);
+        P = Pn; S0 = S0n; S1 = S1n; S2 = S2n; R = Rn; Ph = Phn;
     }
 }
 

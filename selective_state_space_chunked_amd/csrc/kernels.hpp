@@ -94,9 +94,9 @@ struct RtrlParams {
     const float* gy; const float* gh_last;
     float* y; float* glam; float* gtheta;
     double* segP;    // (B,H,G,M) complex: product of a over the segment
-    double* segS;    // (B,H,G,M) x (h, sl, st) complex: local state from zero
+    double* segS;    // 3 planes (h, sl, st) of (B,H,G,M) complex: local triple from zero
     double* segRP;   // (B,H,G) x (sum r, sum phi)
-    double* carry;   // (B,H,G,M) x (h, sl, st) complex entering each segment
+    double* carry;   // 3 planes (h, sl, st) of (B,H,G,M) complex entering each segment
     double* partL; double* partT;   // (B,G,H,M)
     int B, H, L, M, nchunks, chunks_per_seg, G;
 };
