@@ -409,38 +409,53 @@ __device__ __forceinline__ void st_cd(double* base, size_t i, cd v) {
 }
 
 // segment combines, one thread per (sequence, mode)
-__global__ void cplx_combine_fwd_kernel(CplxParams p) {
+constexpr int kCombBatch = 8;
+__global__ __launch_bounds__(256) void cplx_combine_fwd_kernel(CplxParams p) {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= p.B * p.H * p.M) return;
     const int s = i / p.M, m = i - s * p.M;
     cd h = {0.0, 0.0};
     if (p.h0) h = {p.h0[2 * (size_t)i], p.h0[2 * (size_t)i + 1]};
-    // the next segment's summary is loaded before this one's carry is stored
-    // (the stores could alias the summaries as far as the compiler knows)
-    size_t o = (size_t)s * p.G * p.M + m;
-    cd P = ld_cd(p.segP, o), S = ld_cd(p.segS, o);
-    for (int g = 0; g < p.G; ++g, o += p.M) {
-        cd Pn = P, Sn = S;
-        if (g + 1 < p.G) { Pn = ld_cd(p.segP, o + p.M); Sn = ld_cd(p.segS, o + p.M); }
-        st_cd(p.carry_in, o, h);
-        h = cfma(P, h, S);
-        P = Pn; S = Sn;
+    // summaries are loaded kCombBatch segments at a time, all in flight before
+    // the chain consumes them
+    const size_t o0 = (size_t)s * p.G * p.M + m;
+    for (int g0 = 0; g0 < p.G; g0 += kCombBatch) {
+        cd P[kCombBatch], S[kCombBatch];
+#pragma unroll
+        for (int j = 0; j < kCombBatch; ++j)
+            if (g0 + j < p.G) {
+                P[j] = ld_cd(p.segP, o0 + (size_t)(g0 + j) * p.M);
+                S[j] = ld_cd(p.segS, o0 + (size_t)(g0 + j) * p.M);
+            }
+#pragma unroll
+        for (int j = 0; j < kCombBatch; ++j)
+            if (g0 + j < p.G) {
+                st_cd(p.carry_in, o0 + (size_t)(g0 + j) * p.M, h);
+                h = cfma(P[j], h, S[j]);
+            }
     }
 }
-__global__ void cplx_combine_rev_kernel(CplxParams p) {
+__global__ __launch_bounds__(256) void cplx_combine_rev_kernel(CplxParams p) {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= p.B * p.H * p.M) return;
     const int s = i / p.M, m = i - s * p.M;
     cd v = {0.0, 0.0};
     if (p.gh_last) v = {p.gh_last[2 * (size_t)i], p.gh_last[2 * (size_t)i + 1]};
-    size_t o = ((size_t)s * p.G + p.G - 1) * p.M + m;
-    cd Q = ld_cd(p.segQ, o), R = ld_cd(p.segR, o);
-    for (int g = p.G - 1; g >= 0; --g, o -= p.M) {
-        cd Qn = Q, Rn = R;
-        if (g > 0) { Qn = ld_cd(p.segQ, o - p.M); Rn = ld_cd(p.segR, o - p.M); }
-        st_cd(p.nu_in, o, v);
-        v = cfma(Q, v, R);
-        Q = Qn; R = Rn;
+    const size_t o0 = (size_t)s * p.G * p.M + m;
+    for (int g1 = p.G - 1; g1 >= 0; g1 -= kCombBatch) {
+        cd Q[kCombBatch], R[kCombBatch];
+#pragma unroll
+        for (int j = 0; j < kCombBatch; ++j)
+            if (g1 - j >= 0) {
+                Q[j] = ld_cd(p.segQ, o0 + (size_t)(g1 - j) * p.M);
+                R[j] = ld_cd(p.segR, o0 + (size_t)(g1 - j) * p.M);
+            }
+#pragma unroll
+        for (int j = 0; j < kCombBatch; ++j)
+            if (g1 - j >= 0) {
+                st_cd(p.nu_in, o0 + (size_t)(g1 - j) * p.M, v);
+                v = cfma(Q[j], v, R[j]);
+            }
     }
 }
 // (B,G,H,M) partials -> (H,M): one wave per (head, mode); lane l adds the
@@ -605,7 +620,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
 }
 
 // Entering (h, sl, st) of every segment, one lane per (batch, head, mode).
-__global__ void cplx_rtrl_combine_kernel(RtrlParams p) {
+__global__ __launch_bounds__(256) void cplx_rtrl_combine_kernel(RtrlParams p) {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= p.B * p.H * p.M) return;
     const int s = i / p.M, m = i - s * p.M;
@@ -613,34 +628,35 @@ __global__ void cplx_rtrl_combine_kernel(RtrlParams p) {
     const size_t n3 = (size_t)p.B * p.H * p.G * p.M;
     cd h = {0.0, 0.0}, sl = {0.0, 0.0}, stt = {0.0, 0.0};
     if (p.h0) h = {p.h0[2 * (size_t)i], p.h0[2 * (size_t)i + 1]};
-    // segment g's summary is loaded while segment g-1 is applied (the loads do
-    // not depend on the chain)
-    auto load = [&](int g, cd& P, cd& S0, cd& S1, cd& S2, double& R, double& Ph) {
-        const size_t o = ((size_t)s * p.G + g) * p.M + m;
-        P = ld_cd(p.segP, o);
-        S0 = ld_cd(p.segS, o);
-        S1 = ld_cd(p.segS, n3 + o);
-        S2 = ld_cd(p.segS, 2 * n3 + o);
-        R = p.segRP[2 * ((size_t)s * p.G + g)] * ilam;
-        Ph = p.segRP[2 * ((size_t)s * p.G + g) + 1];
-    };
-    cd P, S0, S1, S2;
-    double R, Ph;
-    load(0, P, S0, S1, S2, R, Ph);
-    for (int g = 0; g < p.G; ++g) {
-        cd Pn = P, S0n = S0, S1n = S1, S2n = S2;
-        double Rn = R, Phn = Ph;
-        if (g + 1 < p.G) load(g + 1, Pn, S0n, S1n, S2n, Rn, Phn);
-        const size_t o = ((size_t)s * p.G + g) * p.M + m;
-        st_cd(p.carry, o, h);
-        st_cd(p.carry, n3 + o, sl);
-        st_cd(p.carry, 2 * n3 + o, stt);
-        const cd sl_in = {fma(R, h.re, sl.re), fma(R, h.im, sl.im)};
-        const cd st_in = {fma(-Ph, h.im, stt.re), fma(Ph, h.re, stt.im)};
-        sl = cfma(P, sl_in, S1);
-        stt = cfma(P, st_in, S2);
-        h = cfma(P, h, S0);
-        P = Pn; S0 = S0n; S1 = S1n; S2 = S2n; R = Rn; Ph = Phn;
+    const size_t o0 = (size_t)s * p.G * p.M + m;
+    const size_t r0 = (size_t)s * p.G;
+    for (int g0 = 0; g0 < p.G; g0 += kCombBatch) {
+        cd P[kCombBatch], S0[kCombBatch], S1[kCombBatch], S2[kCombBatch];
+        double R[kCombBatch], Ph[kCombBatch];
+#pragma unroll
+        for (int j = 0; j < kCombBatch; ++j)
+            if (g0 + j < p.G) {
+                const size_t o = o0 + (size_t)(g0 + j) * p.M;
+                P[j] = ld_cd(p.segP, o);
+                S0[j] = ld_cd(p.segS, o);
+                S1[j] = ld_cd(p.segS, n3 + o);
+                S2[j] = ld_cd(p.segS, 2 * n3 + o);
+                R[j] = p.segRP[2 * (r0 + g0 + j)] * ilam;
+                Ph[j] = p.segRP[2 * (r0 + g0 + j) + 1];
+            }
+#pragma unroll
+        for (int j = 0; j < kCombBatch; ++j)
+            if (g0 + j < p.G) {
+                const size_t o = o0 + (size_t)(g0 + j) * p.M;
+                st_cd(p.carry, o, h);
+                st_cd(p.carry, n3 + o, sl);
+                st_cd(p.carry, 2 * n3 + o, stt);
+                const cd sl_in = {fma(R[j], h.re, sl.re), fma(R[j], h.im, sl.im)};
+                const cd st_in = {fma(-Ph[j], h.im, stt.re), fma(Ph[j], h.re, stt.im)};
+                sl = cfma(P[j], sl_in, S1[j]);
+                stt = cfma(P[j], st_in, S2[j]);
+                h = cfma(P[j], h, S0[j]);
+            }
     }
 }
 
