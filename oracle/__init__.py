@@ -64,6 +64,8 @@ def _load():
         lib.orc_pd_fwd.argtypes = [_L, _L, _L, _L, _L, _I, _I] + [_D] * 6
         lib.orc_pd_dense_fwd.argtypes = [_L, _L, _L, _L, _L, _I, _I] + [_D] * 6
         lib.orc_pd_bwd.argtypes = [_L, _L, _L, _L, _L, _I, _I] + [_D] * 10
+        lib.orc_pd_ste.argtypes = [_L, _L, _L, _L, _L, _D, _I, _I] + [_D] * 6 + [ctypes.c_double, _D, _D]
+        lib.orc_pd_mix_fwd.argtypes = [_L, _L, _L, _L, _L, _D, _I] + [_D] * 6
         lib.orc_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -213,3 +215,25 @@ def pd_bwd(*, sel, dict, d, b, C, h0=None, gy, ghlast=None, B, H, L, N, K):
     _load().orc_pd_bwd(B, H, L, N, K, _pi(sel), _pi(dct), *[_p(v) for v in args],
                        _p(gd), _p(gb), _p(gC), _p(gh0))
     return {"gd": gd, "gb": gb, "gC": gC, "gh0": gh0}
+
+
+def pd_ste(*, logits, sel, dict, d, b, C, h0=None, gy, ghlast=None, tau, B, H, L, N, K):
+    """Straight-through surrogate gradients of the PD selection: gw = dLoss/dw
+    of the mixture weights at the hard selection, glogits through the tempered
+    softmax.  Returns dict(gw, glogits), each (B, H, L, K)."""
+    sel, dct = _pd_common(sel, dict)
+    lw = _w(logits)
+    args = [_w(v) for v in (d, b, C, h0, gy, ghlast)]
+    gw, gl = _z((B, H, L, K)), _z((B, H, L, K))
+    _load().orc_pd_ste(B, H, L, N, K, _p(lw), _pi(sel), _pi(dct), *[_p(v) for v in args], float(tau),
+                       _p(gw), _p(gl))
+    return {"gw": gw, "glogits": gl}
+
+
+def pd_mix_fwd(*, w, dict, d, b, C, h0=None, B, H, L, N, K):
+    """Forward of the mixture transition sum_k w[t,k] P_k diag(d_t) (dense matrices)."""
+    dct = np.ascontiguousarray(dict, dtype=np.int32)
+    args = [_w(v) for v in (w, d, b, C, h0)]
+    y, hl = _z((B, H, L)), _z((B, H, N))
+    _load().orc_pd_mix_fwd(B, H, L, N, K, _p(args[0]), _pi(dct), *[_p(v) for v in args[1:]], _p(y), _p(hl))
+    return y, hl

@@ -591,3 +591,121 @@ void orc_pd_bwd(i64 B, i64 H, i64 L, i64 N, i64 K, const int32_t* sel, const int
         free(ln);
     }
 }
+
+/* Straight-through surrogate gradient of the PD selection (Flash PD-SSM page,
+ * "Gradientenpropagation": hard argmax in the forward pass, a tempered softmax
+ * in its place for the backward pass).  Reading: the transition is a mixture
+ * A_t(w) = sum_k w_{t,k} P_k diag(d_t) whose weights are one-hot at the
+ * selected entry in the forward pass and softmax(logits_t / tau) for the
+ * backward pass, every other gradient flowing through the hard forward.  With
+ * lambda_t = dLoss/dh_t (the hard-forward adjoint, lambda_t = C_t gy_t +
+ * A_{t+1}^T lambda_{t+1}):
+ *   gw[t,k]      = dLoss/dw_{t,k} = sum_j lambda_t[pi_k(j)] d_t[j] h_{t-1}[j],
+ *   glogits[t,k] = (1/tau) s_k (gw[t,k] - sum_i s_i gw[t,i]),  s = softmax(logits_t / tau).
+ * gw, glogits (B,H,L,K); either may be NULL. */
+void orc_pd_ste(i64 B, i64 H, i64 L, i64 N, i64 K, const double* logits, const int32_t* sel,
+                const int32_t* dict, const double* d, const double* b, const double* C,
+                const double* h0, const double* gy, const double* ghlast, double tau,
+                double* gw, double* glogits) {
+    #pragma omp parallel
+    {
+        double* hist = (double*)malloc(sizeof(double) * (L + 1) * N);
+        double* lam = (double*)malloc(sizeof(double) * N);
+        double* ln = (double*)malloc(sizeof(double) * N);
+        double* g = (double*)malloc(sizeof(double) * K);
+        double* sm = (double*)malloc(sizeof(double) * K);
+        #pragma omp for schedule(static)
+        for (i64 s = 0; s < B * H; ++s) {
+            i64 hi = s % H;
+            for (i64 i = 0; i < N; ++i) hist[i] = h0 ? h0[s * N + i] : 0.0;
+            for (i64 t = 0; t < L; ++t) {
+                const int32_t* pi = dict + ((i64)hi * K + sel[s * L + t]) * N;
+                double* hn = hist + (t + 1) * N;
+                const double* hp = hist + t * N;
+                for (i64 i = 0; i < N; ++i) hn[i] = b[(s * L + t) * N + i];
+                for (i64 j = 0; j < N; ++j) hn[pi[j]] += d[(s * L + t) * N + j] * hp[j];
+            }
+            for (i64 i = 0; i < N; ++i) lam[i] = ghlast ? ghlast[s * N + i] : 0.0;
+            for (i64 t = L - 1; t >= 0; --t) {
+                const int32_t* pi = dict + ((i64)hi * K + sel[s * L + t]) * N;
+                const double* dt = d + (s * L + t) * N;
+                const double* hp = hist + t * N;
+                for (i64 i = 0; i < N; ++i) lam[i] += C[(s * L + t) * N + i] * gy[s * L + t];
+                /* lam now holds lambda_t */
+                for (i64 k = 0; k < K; ++k) {
+                    const int32_t* pk = dict + ((i64)hi * K + k) * N;
+                    double acc = 0.0;
+                    for (i64 j = 0; j < N; ++j) acc += lam[pk[j]] * dt[j] * hp[j];
+                    g[k] = acc;
+                }
+                const double* x = logits + (s * L + t) * K;
+                double mx = x[0];
+                for (i64 k = 1; k < K; ++k) mx = x[k] > mx ? x[k] : mx;
+                double z = 0.0;
+                for (i64 k = 0; k < K; ++k) {
+                    sm[k] = exp((x[k] - mx) / tau);
+                    z += sm[k];
+                }
+                double dot = 0.0;
+                for (i64 k = 0; k < K; ++k) {
+                    sm[k] /= z;
+                    dot += sm[k] * g[k];
+                }
+                for (i64 k = 0; k < K; ++k) {
+                    if (gw) gw[(s * L + t) * K + k] = g[k];
+                    if (glogits) glogits[(s * L + t) * K + k] = sm[k] * (g[k] - dot) / tau;
+                }
+                for (i64 j = 0; j < N; ++j) ln[j] = dt[j] * lam[pi[j]];
+                for (i64 j = 0; j < N; ++j) lam[j] = ln[j];
+            }
+        }
+        free(hist);
+        free(lam);
+        free(ln);
+        free(g);
+        free(sm);
+    }
+}
+
+/* The mixture forward of the reading above, as dense N x N matrices:
+ * A_t = sum_k w[t,k] P_k diag(d_t), P_k[i][j] = 1 if dict[h,k,j] == i.
+ * w (B,H,L,K).  With w one-hot at sel it is the PD forward; its derivative in
+ * w at that point is gw above. */
+void orc_pd_mix_fwd(i64 B, i64 H, i64 L, i64 N, i64 K, const double* w, const int32_t* dict,
+                    const double* d, const double* b, const double* C, const double* h0,
+                    double* y, double* hlast) {
+    #pragma omp parallel
+    {
+        double* h = (double*)malloc(sizeof(double) * N);
+        double* hn = (double*)malloc(sizeof(double) * N);
+        double* At = (double*)malloc(sizeof(double) * N * N);
+        #pragma omp for schedule(static)
+        for (i64 s = 0; s < B * H; ++s) {
+            i64 hi = s % H;
+            for (i64 i = 0; i < N; ++i) h[i] = h0 ? h0[s * N + i] : 0.0;
+            for (i64 t = 0; t < L; ++t) {
+                for (i64 e = 0; e < N * N; ++e) At[e] = 0.0;
+                for (i64 k = 0; k < K; ++k) {
+                    const int32_t* pk = dict + ((i64)hi * K + k) * N;
+                    const double wk = w[(s * L + t) * K + k];
+                    for (i64 j = 0; j < N; ++j) At[pk[j] * N + j] += wk * d[(s * L + t) * N + j];
+                }
+                double acc = 0.0;
+                for (i64 i = 0; i < N; ++i) {
+                    double v = b[(s * L + t) * N + i];
+                    for (i64 j = 0; j < N; ++j) v += At[i * N + j] * h[j];
+                    hn[i] = v;
+                }
+                for (i64 i = 0; i < N; ++i) {
+                    h[i] = hn[i];
+                    acc += C[(s * L + t) * N + i] * h[i];
+                }
+                y[s * L + t] = acc;
+            }
+            if (hlast) for (i64 i = 0; i < N; ++i) hlast[s * N + i] = h[i];
+        }
+        free(h);
+        free(hn);
+        free(At);
+    }
+}

@@ -548,6 +548,72 @@ def test_pd_bwd_fd(name, gname):
     fd_check(_loss_pd, p, name, g[gname])
 
 
+def _pd_ste_small(seed=15):
+    cfg = synth.make_pd(B=1, H=2, N=5, L=7, K=3, seed=seed)
+    g = np.random.default_rng(seed)
+    return dict(logits=synth.widen(cfg["logits"]), sel=oracle.pd_select(cfg["logits"]), dict=cfg["dict"],
+                d=synth.widen(cfg["d"]), b=synth.widen(cfg["b"]), C=synth.widen(cfg["C"]),
+                h0=g.standard_normal((1, 2, 5)), gy=g.standard_normal((1, 2, 7)),
+                ghlast=g.standard_normal((1, 2, 5)), B=1, H=2, L=7, N=5, K=3)
+
+
+def _onehot(sel, K):
+    return (sel[..., None] == np.arange(K)).astype(np.float64)
+
+
+def _ste(p, tau):
+    return oracle.pd_ste(**{k: p[k] for k in ("logits", "sel", "dict", "d", "b", "C", "h0", "gy", "ghlast",
+                                              "B", "H", "L", "N", "K")}, tau=tau)
+
+
+def _loss_mix(p, w):
+    y, hl = oracle.pd_mix_fwd(w=w, **{k: p[k] for k in ("dict", "d", "b", "C", "h0", "B", "H", "L", "N", "K")})
+    return float((y * p["gy"]).sum() + (hl * p["ghlast"]).sum())
+
+
+def test_pd_mixture_at_onehot_is_hard_forward():
+    """The mixture transition with one-hot weights is the PD forward (gather route vs dense matrices)."""
+    p = _pd_ste_small()
+    y, hl = oracle.pd_mix_fwd(w=_onehot(p["sel"], 3), **{k: p[k] for k in ("dict", "d", "b", "C", "h0",
+                                                                            "B", "H", "L", "N", "K")})
+    y2, hl2 = oracle.pd_fwd(**{k: p[k] for k in ("sel", "dict", "d", "b", "C", "h0", "B", "H", "L", "N", "K")})
+    close(y, y2, rtol=1e-13, atol=1e-14)
+    close(hl, hl2, rtol=1e-13, atol=1e-14)
+
+
+def test_pd_ste_selection_weight_gradient_fd():
+    """gw = dLoss/dw of the dense mixture forward at the one-hot selection, by central differences
+    (the loss is affine in each single weight, so the difference quotient is exact up to rounding)."""
+    p = _pd_ste_small()
+    gw = _ste(p, 0.7)["gw"]
+    w0 = _onehot(p["sel"], 3)
+    q = dict(p, w=w0)
+    fd_check(lambda q_, w: _loss_mix(q_, w), q, "w", gw, rtol=1e-8, atol=1e-10)
+
+
+@pytest.mark.parametrize("tau", [0.25, 1.0, 3.0])
+def test_pd_ste_logit_gradient_fd(tau):
+    """glogits = d/dlogits of sum_k gw_k softmax(logits/tau)_k with gw held fixed (finite differences)."""
+    p = _pd_ste_small(seed=16)
+    r = _ste(p, tau)
+    gw = r["gw"]
+
+    def f(q, logits):
+        z = logits / tau
+        e = np.exp(z - z.max(axis=-1, keepdims=True))
+        return float((gw * e / e.sum(axis=-1, keepdims=True)).sum())
+    fd_check(f, dict(p), "logits", r["glogits"], rtol=1e-6, atol=1e-10)
+
+
+def test_pd_ste_uniform_limit():
+    """Large tau: softmax -> uniform, so tau * glogits -> (gw - mean_k gw) / K."""
+    p = _pd_ste_small(seed=17)
+    tau = 1e7
+    r = _ste(p, tau)
+    want = (r["gw"] - r["gw"].mean(axis=-1, keepdims=True)) / 3
+    close(r["glogits"] * tau, want, rtol=1e-5, atol=1e-9)
+
+
 # ---------------------------------------------------------------------------
 # generators
 # ---------------------------------------------------------------------------
