@@ -249,6 +249,33 @@ def w_pd(steps, warmup):
                 config=dict(B=B, H=H, N=N, L=L, K=K, chunk_len=64))
 
 
+def w_pd_ste(steps, warmup):
+    """PD scan as w_pd, the backward also producing the straight-through gradient of the scores (tau 1)."""
+    import synth
+    import selective_state_space_chunked_amd as ssm
+    B, H, N, L, K = 8, 32, 16, 17000, 8
+    cfg = synth.make_pd(B=B, H=H, N=N, L=L, K=K, seed=0)
+    t = {k: to_dev(cfg[k]) for k in ("logits", "dict", "d", "b", "C")}
+    gy = to_dev(cfg["gy"])
+    fo = ssm.pd_scan_fwd(want_ckpt=True, **t)
+    tb = dict(t)
+    lg = tb.pop("logits")
+    want = ("gd", "gb", "gC", "gh0", "glogits")
+    go = ssm.pd_scan_bwd(gy=gy, ckpt=fo["ckpt"], sel=fo["sel"], ste_logits=lg, tau=1.0, want=want, **tb)
+
+    def step():
+        ssm.pd_scan_fwd(want_ckpt=True, out=fo, **t)
+        ssm.pd_scan_bwd(gy=gy, ckpt=fo["ckpt"], sel=fo["sel"], ste_logits=lg, tau=1.0, want=want, out=go, **tb)
+
+    ms = time_steps(step, steps, warmup)
+    BHL, E = B * H * L, B * H * L * N
+    ck = B * H * (-(-L // 64)) * N * 4
+    fwd = BHL * K * 4 + 3 * E * 4 + BHL * 4 * 2 + ck
+    bwd = BHL * 4 + 3 * E * 4 + BHL * 4 + ck + 3 * E * 4 + 2 * BHL * K * 4   # + read logits, write glogits
+    return dict(name="pd-ste", elements=E, ms=ms, kernels=profile_kernels(step), bytes_total=fwd + bwd,
+                config=dict(B=B, H=H, N=N, L=L, K=K, chunk_len=64, tau=1.0))
+
+
 def w_dense(steps, warmup):
     """Dense a_t, b_t scan at the Mamba-layer shape B=8 D=2048 N=16 L=4096, fp32."""
     import torch
@@ -342,7 +369,7 @@ def main():
     others = {}
     if not args.no_others:
         todo = [w.strip() for w in args.workloads.split(",") if w.strip()] or \
-            ["impulse", "complex", "complex-rtrl", "pd", "dense", "real-small"]
+            ["impulse", "complex", "complex-rtrl", "pd", "pd-ste", "dense", "real-small"]
         for w in todo:
             if w == "impulse":
                 others[w] = summarize(w_impulse(args.steps, args.warmup))
@@ -352,6 +379,8 @@ def main():
                 others[w] = summarize(w_complex_rtrl(args.steps, args.warmup))
             elif w == "pd":
                 others[w] = summarize(w_pd(args.steps, args.warmup))
+            elif w == "pd-ste":
+                others[w] = summarize(w_pd_ste(args.steps, args.warmup))
             elif w == "dense":
                 others[w] = summarize(w_dense(args.steps, args.warmup))
             elif w == "real-small":

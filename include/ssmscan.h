@@ -71,7 +71,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 1
+#define SSM_ABI_VERSION 2
 
 /* status codes */
 #define SSM_OK               0
@@ -193,14 +193,26 @@ typedef struct {
     const float* gy;       /* (B,H,L)                                                   */
     const float* gh_last;  /* nullable (B,H,N)                                          */
     const float* ckpt;     /* nullable checkpoints from pd_scan_fwd; NULL = recomputed  */
+    const float* ste_logits; /* (B,H,L,K) selection scores for glogits; required when
+                                glogits is wanted, ignored otherwise                     */
+    float tau;             /* softmax temperature of glogits (> 0, finite)              */
 } pd_scan_bwd_in;
 
-/* Gradients with the selection held fixed (argmax is piecewise constant). */
+/* Gradients with the selection held fixed (argmax is piecewise constant), and
+ * optionally the straight-through surrogate gradient of the selection scores
+ * (Flash PD-SSM page, gradient propagation: hard argmax in the forward pass, a
+ * tempered softmax in its place in the backward pass).  Reading: the
+ * transition is sum_k w_k P_k diag(d_t) with w one-hot at the selected entry;
+ *   gw[t,k] = dLoss/dw_{t,k} = sum_j lambda_t[dict[h,k,j]] d_t[j] h_{t-1}[j]
+ * (lambda_t = dLoss/dh_t of the hard forward) and
+ *   glogits[t,k] = (1/tau) s_k (gw[t,k] - sum_i s_i gw[t,i]),
+ *   s = softmax(ste_logits[t,:] / tau). */
 typedef struct {
-    float* gd;   /* (B,H,L,N) */
-    float* gb;   /* (B,H,L,N) */
-    float* gC;   /* (B,H,L,N) */
-    float* gh0;  /* (B,H,N)   */
+    float* gd;       /* (B,H,L,N) */
+    float* gb;       /* (B,H,L,N) */
+    float* gC;       /* (B,H,L,N) */
+    float* gh0;      /* (B,H,N)   */
+    float* glogits;  /* (B,H,L,K) surrogate gradient of the scores; NULL = not wanted */
 } pd_scan_grads;
 
 /* Workspace size in bytes for operation `op` (SSM_OP_*) with `args`

@@ -56,11 +56,11 @@ class PDFwdOut(ctypes.Structure):
 
 
 class PDBwdIn(ctypes.Structure):
-    _fields_ = [("gy", _vp), ("gh_last", _vp), ("ckpt", _vp)]
+    _fields_ = [("gy", _vp), ("gh_last", _vp), ("ckpt", _vp), ("ste_logits", _vp), ("tau", ctypes.c_float)]
 
 
 class PDGrads(ctypes.Structure):
-    _fields_ = [("gd", _vp), ("gb", _vp), ("gC", _vp), ("gh0", _vp)]
+    _fields_ = [("gd", _vp), ("gb", _vp), ("gC", _vp), ("gh0", _vp), ("glogits", _vp)]
 
 
 _lib = None
@@ -329,19 +329,27 @@ def pd_scan_fwd(*, want_y=True, want_sel=True, want_h_last=False, want_ckpt=Fals
     return out
 
 
-def pd_scan_bwd(*, gy, gh_last=None, ckpt=None, want=("gd", "gb", "gC", "gh0"), chunk_len=0, out=None, **tensors):
+def pd_scan_bwd(*, gy, gh_last=None, ckpt=None, want=("gd", "gb", "gC", "gh0"), ste_logits=None, tau=1.0,
+                chunk_len=0, out=None, **tensors):
+    """PD backward with the selection held fixed.  ``want`` may also name
+    "glogits", the straight-through surrogate gradient of ``ste_logits``
+    (B, H, L, K) through softmax(ste_logits / tau)."""
     args, (Bsz, H, L, N, K), dev = _pd_args(chunk_len=chunk_len, **tensors)
     _need(gy, "gy", torch.float32, (Bsz, H, L), dev)
     _need(gh_last, "gh_last", torch.float32, (Bsz, H, N), dev)
     nc = n_chunks(L, chunk_len or 64)
     _need(ckpt, "ckpt", torch.float32, (Bsz, H, nc, N), dev)
+    _need(ste_logits, "ste_logits", torch.float32, (Bsz, H, L, K), dev)
     out = dict(out or {})
-    shapes = {"gd": (Bsz, H, L, N), "gb": (Bsz, H, L, N), "gC": (Bsz, H, L, N), "gh0": (Bsz, H, N)}
+    shapes = {"gd": (Bsz, H, L, N), "gb": (Bsz, H, L, N), "gC": (Bsz, H, L, N), "gh0": (Bsz, H, N),
+              "glogits": (Bsz, H, L, K)}
     for k in want:
+        if k not in shapes:
+            raise ValueError(f"unknown PD gradient {k}")
         if k not in out:
             out[k] = torch.empty(shapes[k], dtype=torch.float32, device=dev)
-    g = PDGrads(gd=_ptr(out.get("gd")), gb=_ptr(out.get("gb")), gC=_ptr(out.get("gC")), gh0=_ptr(out.get("gh0")))
-    i = PDBwdIn(gy=_ptr(gy), gh_last=_ptr(gh_last), ckpt=_ptr(ckpt))
+    g = PDGrads(**{f[0]: _ptr(out.get(f[0])) for f in PDGrads._fields_})
+    i = PDBwdIn(gy=_ptr(gy), gh_last=_ptr(gh_last), ckpt=_ptr(ckpt), ste_logits=_ptr(ste_logits), tau=float(tau))
     ws, nws = _workspace(SSM_OP_PD_BWD, ctypes.byref(args), dev)
     _check(lib().pd_scan_bwd(ctypes.byref(args), ctypes.byref(i), ctypes.byref(g), _ptr(ws), nws, _stream(dev)))
     return out

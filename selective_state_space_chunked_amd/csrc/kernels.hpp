@@ -119,6 +119,9 @@ struct PDParams {
     float* nu_in;                  // (B,H,G,N)
     float* y; float* h_last; float* ckpt_out;
     float* gd; float* gb; float* gC; float* gh0;
+    const float* ste_logits;       // selection scores for the surrogate gradient (B,H,L,K)
+    float* glogits;                // (B,H,L,K) surrogate gradient; NULL = not wanted
+    float inv_tau;                 // 1 / softmax temperature
     int B, H, L, N, K, chunk, G;   // G = number of chunks
 };
 hipError_t launch_pd_prep(const PDParams& p, hipStream_t st);

@@ -249,9 +249,87 @@ __global__ __launch_bounds__(256) void pd_fwd_kernel(PDParams p) {
 // steps per batch of loads; the reverse sweep loads its blocks in the same way.
 // SUMMARY: chunk transition (pi_c, D_c) composed right to left, and the
 // adjoint entering the chunk start from zero (R), so nu_start = D_c*nu[pi_c] + R.
+// STE >= 0 (main pass only; 16 = register path for K <= 16): straight-through
+// surrogate gradient of the selection (Flash PD-SSM page, gradient
+// propagation: hard argmax forward, tempered softmax backward).  With the
+// transition read as sum_k w_k P_k diag(d_t),
+//   gw[t,k] = sum_j lambda_t[pi_k(j)] d_t[j] h_{t-1}[j],
+//   glogits[t,k] = (1/tau) s_k (gw[t,k] - <s, gw[t,:]>),  s = softmax(logits_t / tau).
+// Per 16-step block and entry k every lane pulls lambda_t[pi_k(j)] for the 16
+// steps and one transpose-reduction over the row leaves gw of step tb + lane
+// on that lane; each lane then applies the softmax pull-back to its step.
 // ---------------------------------------------------------------------------
-template <bool SUMMARY, int NT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void pd_bwd_kernel(PDParams p) {
+// Surrogate selection gradient of one 16-step block; lam[q], z[q] = lambda_t[j]
+// and d_t[j] h_{t-1}[j] of step tb + q on lane j.  KR = 16: K <= 16, the
+// lane's scores x (preloaded, -inf past K) and its gw stay in registers;
+// KR = 0: any K, gw goes through the output array.
+template <int KR>
+__device__ __forceinline__ void pd_ste_block(const PDParams& p, const PDShared& tb_, const float (&lam)[16],
+                                             const float (&z)[16], const float (&x)[16], size_t srow, int tb,
+                                             int N, int j) {
+    const int K = p.K, L = p.L;
+    const int t = tb + (lane_id() & 15);   // the step whose gw this lane receives
+    float* o = p.glogits + (srow + t) * K;
+    const float sc = p.inv_tau * 1.4426950408889634f;  // exp(v / tau) = 2^(v log2(e) / tau)
+    if (KR == 16) {
+        float g[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            g[k] = 0.0f;
+            if (k < K) {                   // uniform
+                const int pk = tb_.dict[k * N + j];
+                float v[16];
+#pragma unroll
+                for (int q = 0; q < 16; ++q) v[q] = row_pull(lam[q], pk) * z[q];
+                g[k] = row_transpose_sum16(v);
+            }
+        }
+        if (t >= L) return;
+        float mx = x[0];
+#pragma unroll
+        for (int k = 1; k < 16; ++k) mx = fmaxf(mx, x[k]);
+        float e[16], zs = 0.0f, dot = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            e[k] = k < K ? exp2f((x[k] - mx) * sc) : 0.0f;
+            zs += e[k];
+            dot = fmaf(e[k], g[k], dot);
+        }
+        const float rz = 1.0f / zs;
+        dot *= rz;
+#pragma unroll
+        for (int k = 0; k < 16; ++k)
+            if (k < K) o[k] = e[k] * rz * (g[k] - dot) * p.inv_tau;
+        return;
+    }
+    for (int k = 0; k < K; ++k) {          // uniform
+        const int pk = tb_.dict[k * N + j];
+        float v[16];
+#pragma unroll
+        for (int q = 0; q < 16; ++q) v[q] = row_pull(lam[q], pk) * z[q];
+        const float g = row_transpose_sum16(v);
+        if (t < L) o[k] = g;               // gw, replaced by glogits below
+    }
+    if (t >= L) return;
+    const float* xs = p.ste_logits + (srow + t) * K;
+    float mx = xs[0];
+    for (int k = 1; k < K; ++k) mx = fmaxf(mx, xs[k]);
+    float zs = 0.0f, dot = 0.0f;
+    for (int k = 0; k < K; ++k) {
+        const float e = exp2f((xs[k] - mx) * sc);
+        zs += e;
+        dot = fmaf(e, o[k], dot);
+    }
+    const float rz = 1.0f / zs;
+    dot *= rz;
+    for (int k = 0; k < K; ++k) {
+        const float e = exp2f((xs[k] - mx) * sc) * rz;
+        o[k] = e * (o[k] - dot) * p.inv_tau;
+    }
+}
+
+template <bool SUMMARY, int NT, int STE = -1>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(STE >= 0 ? 2 : 3))) void pd_bwd_kernel(PDParams p) {
     __shared__ PDShared tb_;
     const PDRow r = pd_row(p);
     pd_load_tables(p, r.hh, tb_);
@@ -298,6 +376,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
             const int tl = tb + r.lane;
             const int kl = sel_of(tl);
             const float gyl = tl < L ? p.gy[srow + tl] : 0.0f;
+            float xl[16];  // STE == 16: this lane's scores of step tl
+            if (STE == 16) {
+                const float* xs = p.ste_logits + (srow + tl) * p.K;
+#pragma unroll
+                for (int k = 0; k < 16; ++k) xl[k] = (k < p.K && tl < L) ? xs[k] : -INFINITY;
+            }
             float dv[16], cv[16];
             pd_load16<NT>(dbase, tb, L, N, j, dv);
             pd_load16<NT>(cbase, tb, L, N, j, cv);
@@ -327,7 +411,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
                     }
                     nu = dv[q] * lp;
                 }
+                if (STE >= 0) {  // keep lambda_t and d_t[j] h_{t-1}[j] of the block (the slots are free now)
+                    cv[q] = tv ? lam : 0.0f;
+                    dv[q] = (tv && nl) ? dv[q] * hs[16 * blk + q] : 0.0f;
+                }
             }
+            if (STE >= 0) pd_ste_block<STE == 16 ? 16 : 0>(p, tb_, cv, dv, xl, srow, tb, N, j);
         }
         if (!nl) return;
         const size_t so = ((size_t)r.s * p.G + r.ch) * N + j;
@@ -484,6 +573,9 @@ hipError_t launch_pd_bwd(const PDParams& p, bool summary, hipStream_t st) {
     if (summary) {
         if (p.N == 16) pd_bwd_kernel<true, 16><<<grid, 256, 0, st>>>(p);
         else pd_bwd_kernel<true, 0><<<grid, 256, 0, st>>>(p);
+    } else if (p.glogits) {
+        if (p.K <= 16) pd_bwd_kernel<false, 0, 16><<<grid, 256, 0, st>>>(p);
+        else pd_bwd_kernel<false, 0, 0><<<grid, 256, 0, st>>>(p);
     } else {
         pd_bwd_kernel<false, 0><<<grid, 256, 0, st>>>(p);
     }

@@ -45,6 +45,8 @@ def test_struct_layouts():
     assert ctypes.sizeof(B.ScanArgs) == 8 + 5 * 8 + 14 * 8
     assert ctypes.sizeof(B.ScanGrads) == 14 * 8
     assert ctypes.sizeof(B.PDArgs) == 6 * 8 + 7 * 8
+    assert ctypes.sizeof(B.PDBwdIn) == 4 * 8 + 8   # 4 pointers + float tau (padded)
+    assert ctypes.sizeof(B.PDGrads) == 5 * 8
 
 
 FAKE = 1 << 20  # never dereferenced: validation fails or only sizes are computed
@@ -187,4 +189,23 @@ def test_complex_rtrl_host_checks():
     rc = L.ssm_complex_rtrl(ctypes.byref(a), gy, FAKE * 40 + 4, None, gl, gt, None, 0, None)  # gh_last misaligned
     assert rc == status("SSM_ERR_LAYOUT")
     rc = L.ssm_complex_rtrl(ctypes.byref(a), gy, None, None, gl, gt, None, 0, None)
+    assert rc == status("SSM_ERR_WORKSPACE")
+
+
+def test_pd_ste_host_checks():
+    """The surrogate selection gradient needs the scores and a positive finite temperature."""
+    L = B.lib()
+    a = pd_args()
+    g = B.PDGrads(gd=FAKE * 64, glogits=FAKE * 128)
+    for ste, tau, code in [(None, 1.0, "SSM_ERR_NULL"), (FAKE * 256, 0.0, "SSM_ERR_SHAPE"),
+                           (FAKE * 256, -1.0, "SSM_ERR_SHAPE"), (FAKE * 256, float("inf"), "SSM_ERR_SHAPE"),
+                           (FAKE * 256, float("nan"), "SSM_ERR_SHAPE"), (FAKE * 256, 1e-45, "SSM_ERR_SHAPE"),
+                           (FAKE * 256 + 2, 1.0, "SSM_ERR_LAYOUT"), (FAKE * 128 + 64, 1.0, "SSM_ERR_LAYOUT"),
+                           (FAKE * 256, 1.0, "SSM_ERR_WORKSPACE")]:
+        i = B.PDBwdIn(gy=FAKE * 32, ste_logits=ste, tau=tau)
+        rc = L.pd_scan_bwd(ctypes.byref(a), ctypes.byref(i), ctypes.byref(g), None, 0, None)
+        assert rc == status(code), (ste, tau, L.ssm_last_error_detail())
+    # the scores are not read (and tau not checked) when glogits is not wanted
+    i = B.PDBwdIn(gy=FAKE * 32, ste_logits=None, tau=0.0)
+    rc = L.pd_scan_bwd(ctypes.byref(a), ctypes.byref(i), ctypes.byref(B.PDGrads(gd=FAKE * 64)), None, 0, None)
     assert rc == status("SSM_ERR_WORKSPACE")

@@ -205,6 +205,48 @@ def run_pd(cfg, h0=None, ghl=None, use_sel=False):
         assert torch.equal(g[k], g2[k]), k
 
 
+def run_pd_ste(cfg, tau, h0=None, ghl=None, with_ckpt=True):
+    """Straight-through surrogate gradient of the selection scores against the
+    oracle; the other PD gradients must be unchanged by asking for it."""
+    ssm = _ssm()
+    B, H, L, N, K = cfg["B"], cfg["H"], cfg["L"], cfg["N"], cfg["K"]
+    osel = oracle.pd_select(cfg["logits"])
+    t = dict(dict=T(cfg["dict"]), d=T(cfg["d"]), b=T(cfg["b"]), C=T(cfg["C"]), sel=T(osel))
+    if h0 is not None:
+        t["h0"] = T(h0.astype(np.float32))
+    gyt = T(cfg["gy"])
+    glt = None if ghl is None else T(ghl.astype(np.float32))
+    lg = T(cfg["logits"])
+    ck = ssm.pd_scan_fwd(want_ckpt=True, want_y=False, want_sel=False, **t)["ckpt"] if with_ckpt else None
+    g = ssm.pd_scan_bwd(gy=gyt, ckpt=ck, gh_last=glt, ste_logits=lg, tau=tau,
+                        want=("gd", "gb", "gC", "gh0", "glogits"), **t)
+    g0 = ssm.pd_scan_bwd(gy=gyt, ckpt=ck, gh_last=glt, **t)
+    torch.cuda.synchronize()
+    o = oracle.pd_ste(logits=cfg["logits"], sel=osel, dict=cfg["dict"], d=cfg["d"], b=cfg["b"], C=cfg["C"],
+                      h0=None if h0 is None else h0.astype(np.float32), gy=cfg["gy"],
+                      ghlast=None if ghl is None else ghl.astype(np.float32), tau=tau, B=B, H=H, L=L, N=N, K=K)
+    assert_close("glogits", g["glogits"], o["glogits"], **F32)
+    for k in ("gd", "gb", "gC", "gh0"):
+        assert torch.equal(g[k], g0[k]), k
+
+
+@pytest.mark.parametrize("tau", [0.5, 1.0, 4.0])
+def test_pd_ste_small(tau):
+    cfg = synth.make_pd(B=2, H=3, N=16, L=300, K=8, seed=31)
+    g = np.random.default_rng(32)
+    run_pd_ste(cfg, tau, h0=g.standard_normal((2, 3, 16)), ghl=g.standard_normal((2, 3, 16)))
+
+
+@pytest.mark.parametrize("N,K,L", [(5, 3, 100), (16, 1, 70), (7, 64, 129), (16, 8, 1), (3, 17, 64)])
+def test_pd_ste_shapes(N, K, L):
+    run_pd_ste(synth.make_pd(B=1, H=2, N=N, L=L, K=K, seed=N * K + L), tau=1.0, with_ckpt=(L % 2 == 0))
+
+
+def test_pd_ste_full_config():
+    """B=8 H=32 N=16 L=17000 K=8, seed 0, tau 1: every surrogate gradient compared."""
+    run_pd_ste(synth.make_pd(B=8, H=32, N=16, L=17000, K=8, seed=0), tau=1.0)
+
+
 def test_pd_small():
     cfg = synth.make_pd(B=2, H=3, N=16, L=500, K=8, seed=1)
     g = np.random.default_rng(2)
