@@ -57,6 +57,7 @@ def _load():
         lib.orc_real_fwd.argtypes = [ctypes.c_int, _L, _L, _L, _L] + [_D] * 10
         lib.orc_real_bwd.argtypes = [ctypes.c_int, _L, _L, _L, _L] + [_D] * 18
         lib.orc_impulse_sens.argtypes = [_L, _L, _L, _L, _L] + [_D] * 5
+        lib.orc_output_sens.argtypes = [_L, _L, _L, _L, _L] + [_D] * 8
         lib.orc_complex_fwd.argtypes = [_L, _L, _L, _L] + [_D] * 9
         lib.orc_complex_bwd.argtypes = [_L, _L, _L, _L] + [_D] * 16
         lib.orc_complex_rtrl.argtypes = [_L, _L, _L, _L] + [_D] * 12
@@ -237,3 +238,13 @@ def pd_mix_fwd(*, w, dict, d, b, C, h0=None, B, H, L, N, K):
     y, hl = _z((B, H, L)), _z((B, H, N))
     _load().orc_pd_mix_fwd(B, H, L, N, K, _p(args[0]), _pi(dct), *[_p(v) for v in args[1:]], _p(y), _p(hl))
     return y, hl
+
+
+def output_sens(*, delta, x, A, Bm, C, h0=None, B, D, L, N, t_out=None):
+    """d y[b,d,t_out] / d x[b,d,t] and / d delta[b,d,t] of the selective scan.
+    Returns (s_x, s_delta), each (B, D, L)."""
+    t_out = L - 1 if t_out is None else t_out
+    args = [_w(v) for v in (delta, x, A, Bm, C, h0)]
+    sx, sd = _z((B, D, L)), _z((B, D, L))
+    _load().orc_output_sens(B, D, L, N, t_out, *[_p(v) for v in args], _p(sx), _p(sd))
+    return sx, sd

@@ -236,6 +236,51 @@ void orc_impulse_sens(i64 B, i64 D, i64 L, i64 N, i64 t_out,
     }
 }
 
+/* Sensitivity of one output to the step sizes as well (PGF page, abstract:
+ * sensitivities of the SSM dynamics), for the selective real scan:
+ *   s_x[b,d,t]     = d y[b,d,t_out] / d x[b,d,t]     = mu_t . (delta_t Bm_t),
+ *   s_delta[b,d,t] = d y[b,d,t_out] / d delta[b,d,t] = mu_t . (A a_t h_{t-1} + x_t Bm_t),
+ * t <= t_out (0 after), with mu_{t_out} = C[b,t_out,:], mu_{t-1} = a_t mu_t and
+ * h_t the forward states (h_{-1} = h0).  Either output may be NULL. */
+void orc_output_sens(i64 B, i64 D, i64 L, i64 N, i64 t_out,
+                     const double* delta, const double* x, const double* A, const double* Bm,
+                     const double* C, const double* h0, double* s_x, double* s_delta) {
+    #pragma omp parallel
+    {
+        double* mu = (double*)malloc(sizeof(double) * N);
+        double* hist = (double*)malloc(sizeof(double) * (t_out + 2) * N);
+        #pragma omp for schedule(static)
+        for (i64 s = 0; s < B * D; ++s) {
+            i64 bi = s / D, di = s % D;
+            for (i64 n = 0; n < N; ++n) hist[n] = h0 ? h0[s * N + n] : 0.0;
+            for (i64 t = 0; t <= t_out; ++t) {
+                double dl = delta[s * L + t], xv = x[s * L + t];
+                for (i64 n = 0; n < N; ++n)
+                    hist[(t + 1) * N + n] = exp(dl * A[di * N + n]) * hist[t * N + n] +
+                                            dl * xv * Bm[(bi * L + t) * N + n];
+            }
+            for (i64 t = t_out + 1; t < L; ++t) {
+                if (s_x) s_x[s * L + t] = 0.0;
+                if (s_delta) s_delta[s * L + t] = 0.0;
+            }
+            for (i64 n = 0; n < N; ++n) mu[n] = C[(bi * L + t_out) * N + n];
+            for (i64 t = t_out; t >= 0; --t) {
+                double dl = delta[s * L + t], xv = x[s * L + t], gx = 0.0, gd = 0.0;
+                for (i64 n = 0; n < N; ++n) {
+                    double An = A[di * N + n], a = exp(dl * An), bt = Bm[(bi * L + t) * N + n];
+                    gx += mu[n] * dl * bt;
+                    gd += mu[n] * (An * a * hist[t * N + n] + xv * bt);
+                }
+                if (s_x) s_x[s * L + t] = gx;
+                if (s_delta) s_delta[s * L + t] = gd;
+                for (i64 n = 0; n < N; ++n) mu[n] *= exp(dl * A[di * N + n]);
+            }
+        }
+        free(mu);
+        free(hist);
+    }
+}
+
 /* ------------------------------------------------------------------------- */
 /* Complex diagonal scan with shared controls.  Complex arrays are            */
 /* interleaved (re, im).  r, phi, y, gy (B,H,L); lam, theta (H,M);            */

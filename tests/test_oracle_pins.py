@@ -256,6 +256,35 @@ def test_impulse_linearity_and_backward():
         assert np.all(s[:, :, t_out + 1:] == 0.0)
 
 
+@pytest.mark.parametrize("t_out", [16, 9, 0])
+def test_output_sensitivity_delta_fd(t_out):
+    """d y[t_out] / d delta_t by central differences of the forward (h0 and x nonzero)."""
+    p = small_real(B=1, D=2, N=4, L=17, seed=21)
+    kw = {k: p[k] for k in ("delta", "x", "A", "Bm", "C", "h0", "B", "D", "L", "N")}
+    sx, sd = oracle.output_sens(**kw, t_out=t_out)
+
+    def f(q, delta):
+        y, _ = oracle.real_fwd(**dict(kw, delta=delta))
+        return float(y[:, :, t_out].sum())
+    fd_check(f, dict(p), "delta", sd, rtol=2e-6, atol=1e-9)
+    assert np.all(sd[:, :, t_out + 1:] == 0.0) and np.all(sx[:, :, t_out + 1:] == 0.0)
+
+
+def test_output_sensitivity_matches_backward():
+    """Equal to the general backward's gdelta and gx at gy = e_{t_out}, and s_x to the impulse routine."""
+    p = small_real(B=2, D=3, N=5, L=60, seed=22)
+    kw = {k: p[k] for k in ("delta", "x", "A", "Bm", "C", "h0", "B", "D", "L", "N")}
+    for t_out in (59, 31):
+        sx, sd = oracle.output_sens(**kw, t_out=t_out)
+        gy = np.zeros((2, 3, 60))
+        gy[:, :, t_out] = 1.0
+        g = oracle.real_bwd(**kw, gy=gy)
+        close(sd, g["gdelta"], rtol=1e-12, atol=1e-14)
+        close(sx, g["gx"], rtol=1e-12, atol=1e-14)
+        si = oracle.impulse_sens(**{k: p[k] for k in ("delta", "A", "Bm", "C", "B", "D", "L", "N")}, t_out=t_out)
+        close(sx, si, rtol=1e-13, atol=1e-300)
+
+
 # ---------------------------------------------------------------------------
 # complex scan
 # ---------------------------------------------------------------------------
