@@ -5,9 +5,11 @@ A step is one forward + backward pass (every hot-path kernel) over one batch
 of seeded synthetic inputs.  The headline workload is the Mamba-layer-shaped
 selective scan B=8 D=2048 N=16 L=4096 with bf16 streams, fp32 state and
 accumulation, chunk length 256; value = B*D*N*L / (time of forward+backward).
-The other workloads (impulse sensitivity at L=128000, complex shared-control
-scan, PD scan, dense-a/b scan at the Mamba-layer shape, the small fp32 case)
-are reported under "others" with the same fields.
+The other workloads (impulse sensitivity at L=128000, with and without the
+step-size sensitivity, complex shared-control scan and its forward-mode
+gradients, PD scan with and without the straight-through selection gradient,
+dense-a/b scan at the Mamba-layer shape, the small fp32 case) are reported
+under "others" with the same fields.
 
 Inputs are resident in HBM before timing.  The timed region is K steps
 bracketed by torch.cuda.synchronize(); per-kernel durations come from HIP
@@ -176,6 +178,27 @@ def w_impulse(steps, warmup):
     BDL, BLN = B * D * L, B * L * N
     byts = (2 * BDL + 2 * BLN + BDL) * 4 + (BDL + BLN + BDL) * 4  # forward: x, delta, B, C -> y; sens: delta, B -> s
     return dict(name="impulse", elements=BDL * N, ms=ms, kernels=profile_kernels(step, reps=2),
+                bytes_total=byts, config=dict(B=B, D=D, N=N, L=L, streams="f32", t_out=L - 1))
+
+
+def w_output_sens(steps, warmup):
+    """y and dy[L-1]/dx[t], dy[L-1]/ddelta[t] on the impulse workload, B=1 D=1024 N=16 L=128000 fp32."""
+    import synth
+    import selective_state_space_chunked_amd as ssm
+    B, D, N, L = 1, 1024, 16, 128000
+    cfg = synth.make_impulse(B=B, D=D, N=N, L=L, seed=0)
+    t = {k: to_dev(cfg[k]) for k in ("delta", "x", "Bm", "C", "A")}
+    out = ssm.output_sensitivity(want_y=True, **t)
+
+    def step():
+        ssm.output_sensitivity(want_y=True, out=out, **t)
+
+    ms = time_steps(step, max(3, steps // 4), max(1, warmup // 2))
+    BDL, BLN = B * D * L, B * L * N
+    ck = B * D * (-(-L // 256)) * N * 4
+    # forward: x, delta, B, C -> y, checkpoints; sensitivities: delta, x, B, checkpoints -> s_x, s_delta
+    byts = (2 * BDL + 2 * BLN + BDL) * 4 + ck + (2 * BDL + BLN + 2 * BDL) * 4 + ck
+    return dict(name="output-sens", elements=BDL * N, ms=ms, kernels=profile_kernels(step, reps=2),
                 bytes_total=byts, config=dict(B=B, D=D, N=N, L=L, streams="f32", t_out=L - 1))
 
 
@@ -369,10 +392,12 @@ def main():
     others = {}
     if not args.no_others:
         todo = [w.strip() for w in args.workloads.split(",") if w.strip()] or \
-            ["impulse", "complex", "complex-rtrl", "pd", "pd-ste", "dense", "real-small"]
+            ["impulse", "output-sens", "complex", "complex-rtrl", "pd", "pd-ste", "dense", "real-small"]
         for w in todo:
             if w == "impulse":
                 others[w] = summarize(w_impulse(args.steps, args.warmup))
+            elif w == "output-sens":
+                others[w] = summarize(w_output_sens(args.steps, args.warmup))
             elif w == "complex":
                 others[w] = summarize(w_complex(args.steps, args.warmup))
             elif w == "complex-rtrl":

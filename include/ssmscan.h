@@ -99,6 +99,7 @@ extern "C" {
 #define SSM_OP_PD_FWD   3
 #define SSM_OP_PD_BWD   4
 #define SSM_OP_COMPLEX_RTRL 5
+#define SSM_OP_OUTPUT_SENS  6
 
 /*
  * Arguments of the diagonal scans.  Sizes: batch = B; channels = D (real) or
@@ -260,6 +261,20 @@ int ssm_impulse_sensitivity(const ssm_scan_args* args, int64_t t_out, void* y, v
  * SSM_ERR_UNSUPPORTED for another mode. */
 int ssm_complex_rtrl(const ssm_scan_args* args, const float* gy, const float* gh_last, float* y,
                      float* glam, float* gtheta, void* ws, size_t ws_bytes, void* stream);
+
+/* Sensitivity of one output of a selective real scan to the inputs and to the
+ * step sizes (PGF page, abstract: sensitivities of the SSM dynamics), with the
+ * reverse costate mu_t = C[b,t_out,:] prod_{s=t+1..t_out} a_s in closed form:
+ *   s_x[b,d,t]     = d y[b,d,t_out] / d x[b,d,t]     = delta_t sum_n Bm[b,t,n] mu_t[n],
+ *   s_delta[b,d,t] = d y[b,d,t_out] / d delta[b,d,t]
+ *                  = sum_n mu_t[n] (A[d,n] a_t[n] h_{t-1}[n] + x_t Bm[b,t,n]),
+ * t <= t_out, 0 after; h_{t-1} are the forward states (from h0), recomputed per
+ * tile from checkpoints the call writes into its workspace (O(n_chunks * N)
+ * per sequence, unlike ssm_impulse_sensitivity).  t_out in [0,L); -1 means
+ * L-1.  y, s_x nullable, s_delta required; all (B,D,L) dtype.
+ * SSM_REAL_SELECTIVE only; workspace from ssm_workspace_bytes(SSM_OP_OUTPUT_SENS, ...). */
+int ssm_output_sensitivity(const ssm_scan_args* args, int64_t t_out, void* y, void* s_x, void* s_delta,
+                           void* ws, size_t ws_bytes, void* stream);
 
 /* PD forward: selection (argmax of logits unless sel is given), scan, readout. */
 int pd_scan_fwd(const pd_scan_args* args, const pd_scan_fwd_out* out,

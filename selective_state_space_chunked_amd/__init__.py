@@ -16,6 +16,7 @@ from .binding import (  # noqa: F401
     impulse_sensitivity,
     lib,
     n_chunks,
+    output_sensitivity,
     pd_scan_bwd,
     pd_scan_fwd,
     scan_bwd,

@@ -18,7 +18,8 @@ LIB_PATH = os.path.join(_HERE, "libssmscan.so")
 
 SSM_F32, SSM_BF16 = 0, 1
 SSM_REAL_SELECTIVE, SSM_REAL_DENSE, SSM_COMPLEX_SHARED = 0, 1, 2
-SSM_OP_SCAN_FWD, SSM_OP_SCAN_BWD, SSM_OP_IMPULSE, SSM_OP_PD_FWD, SSM_OP_PD_BWD, SSM_OP_COMPLEX_RTRL = range(6)
+(SSM_OP_SCAN_FWD, SSM_OP_SCAN_BWD, SSM_OP_IMPULSE, SSM_OP_PD_FWD, SSM_OP_PD_BWD, SSM_OP_COMPLEX_RTRL,
+ SSM_OP_OUTPUT_SENS) = range(7)
 
 _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -79,6 +80,7 @@ def lib():
         L.ssm_scan_bwd.argtypes = [ctypes.POINTER(ScanArgs), ctypes.POINTER(ScanBwdIn), ctypes.POINTER(ScanGrads),
                                    _vp, ctypes.c_size_t, _vp]
         L.ssm_impulse_sensitivity.argtypes = [ctypes.POINTER(ScanArgs), _i64, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+        L.ssm_output_sensitivity.argtypes = [ctypes.POINTER(ScanArgs), _i64, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
         L.ssm_complex_rtrl.argtypes = [ctypes.POINTER(ScanArgs), _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
         L.pd_scan_fwd.argtypes = [ctypes.POINTER(PDArgs), ctypes.POINTER(PDFwdOut), _vp, ctypes.c_size_t, _vp]
         L.pd_scan_bwd.argtypes = [ctypes.POINTER(PDArgs), ctypes.POINTER(PDBwdIn), ctypes.POINTER(PDGrads),
@@ -263,6 +265,20 @@ def impulse_sensitivity(*, t_out=-1, want_y=True, chunk_len=0, out=None, **tenso
     ws, nws = _workspace(SSM_OP_IMPULSE, ctypes.byref(args), dev)
     _check(lib().ssm_impulse_sensitivity(ctypes.byref(args), int(t_out), _ptr(out.get("y")), _ptr(out["s"]),
                                          _ptr(ws), nws, _stream(dev)))
+    return out
+
+
+def output_sensitivity(*, t_out=-1, want_y=False, want_s_x=True, chunk_len=0, out=None, **tensors):
+    """d y[b,d,t_out] / d x[b,d,t] (s_x) and / d delta[b,d,t] (s_delta) of a selective real scan (and y)."""
+    args, (Bsz, D, L, N), dev = _scan_args(SSM_REAL_SELECTIVE, chunk_len=chunk_len, **tensors)
+    dt = tensors["delta"].dtype
+    out = dict(out or {})
+    for k, want in (("s_delta", True), ("s_x", want_s_x), ("y", want_y)):
+        if want and k not in out:
+            out[k] = torch.empty((Bsz, D, L), dtype=dt, device=dev)
+    ws, nws = _workspace(SSM_OP_OUTPUT_SENS, ctypes.byref(args), dev)
+    _check(lib().ssm_output_sensitivity(ctypes.byref(args), int(t_out), _ptr(out.get("y")), _ptr(out.get("s_x")),
+                                        _ptr(out["s_delta"]), _ptr(ws), nws, _stream(dev)))
     return out
 
 

@@ -297,8 +297,8 @@ int scan_fwd_impl(const ssm_scan_args* a, const ssm_scan_fwd_out* out, void* ws,
                   hipStream_t st, size_t* need_only);
 int scan_bwd_impl(const ssm_scan_args* a, const ssm_scan_bwd_in* in, const ssm_scan_grads* g, void* ws,
                   size_t ws_bytes, hipStream_t st, size_t* need_only);
-int impulse_impl(const ssm_scan_args* a, int64_t t_out, void* y, void* s, void* ws, size_t ws_bytes,
-                 hipStream_t st, size_t* need_only);
+int impulse_impl(const ssm_scan_args* a, int64_t t_out, void* y, void* s, void* s_delta, bool with_delta,
+                 void* ws, size_t ws_bytes, hipStream_t st, size_t* need_only);
 int pd_fwd_impl(const pd_scan_args* a, const pd_scan_fwd_out* out, void* ws, size_t ws_bytes, hipStream_t st,
                 size_t* need_only);
 int pd_bwd_impl(const pd_scan_args* a, const pd_scan_bwd_in* in, const pd_scan_grads* g, void* ws,
@@ -466,37 +466,46 @@ int scan_bwd_impl(const ssm_scan_args* a, const ssm_scan_bwd_in* in, const ssm_s
 // ---------------------------------------------------------------------------
 // ssm_impulse_sensitivity
 // ---------------------------------------------------------------------------
-int impulse_impl(const ssm_scan_args* a, int64_t t_out, void* y, void* s, void* ws, size_t ws_bytes,
-                 hipStream_t st, size_t* need_only) {
+// with_delta: also s_delta = d y[t_out] / d delta (ssm_output_sensitivity), which
+// needs the forward checkpoints; s may then be NULL.
+int impulse_impl(const ssm_scan_args* a, int64_t t_out, void* y, void* s, void* s_delta, bool with_delta,
+                 void* ws, size_t ws_bytes, hipStream_t st, size_t* need_only) {
     ScanPlan p;
     int rc = validate_scan_args(a, &p);
     if (rc) return rc;
-    if (p.mode != SSM_REAL_SELECTIVE)
-        return fail(SSM_ERR_UNSUPPORTED, "ssm_impulse_sensitivity supports SSM_REAL_SELECTIVE only");
+    const char* name = with_delta ? "ssm_output_sensitivity" : "ssm_impulse_sensitivity";
+    if (p.mode != SSM_REAL_SELECTIVE) return fail(SSM_ERR_UNSUPPORTED, "%s supports SSM_REAL_SELECTIVE only", name);
     if (t_out == -1) t_out = p.L - 1;
     if (t_out < 0 || t_out >= p.L) return fail(SSM_ERR_SHAPE, "t_out %lld outside [0, L)", (long long)t_out);
     if (!need_only) {
-        if (!s) return fail(SSM_ERR_NULL, "s is NULL");
+        if (!with_delta && !s) return fail(SSM_ERR_NULL, "s is NULL");
+        if (with_delta && !s_delta) return fail(SSM_ERR_NULL, "s_delta is NULL");
         const size_t BDL = p.B * p.D * p.L;
-        if ((rc = check_align(s, p.esz, "s")) || (rc = check_align(y, p.esz, "y"))) return rc;
-        if ((rc = check_overlaps(scan_inputs(a, p), {{y, BDL * p.esz, "y"}, {s, BDL * p.esz, "s"}}))) return rc;
+        if ((rc = check_align(s, p.esz, "s")) || (rc = check_align(y, p.esz, "y")) ||
+            (rc = check_align(s_delta, p.esz, "s_delta")))
+            return rc;
+        if ((rc = check_overlaps(scan_inputs(a, p), {{y, BDL * p.esz, "y"}, {s, BDL * p.esz, "s"},
+                                                     {s_delta, BDL * p.esz, "s_delta"}})))
+            return rc;
     }
-    auto layout = [&](Carve& cv, SelFwdLayout* lay, float** tsum, double** send) {
+    auto layout = [&](Carve& cv, SelFwdLayout* lay, float** tsum, double** send, float** ckpt) {
         sel_fwd_layout(p, cv, lay);
         *tsum = cv.take<float>((size_t)p.B * p.D * p.nchunks);
         *send = cv.take<double>((size_t)p.B * p.D * p.nchunks);
+        *ckpt = with_delta ? cv.take<float>((size_t)p.B * p.D * p.nchunks * p.N) : nullptr;
     };
     Carve cv(nullptr);
     SelFwdLayout lay;
     float* tsum;
     double* send;
-    layout(cv, &lay, &tsum, &send);
+    float* ckpt;
+    layout(cv, &lay, &tsum, &send, &ckpt);
     if (need_only) { *need_only = cv.off; return ok(); }
     if ((rc = check_ws(ws, ws_bytes, cv.off))) return rc;
     Carve real(ws);
-    layout(real, &lay, &tsum, &send);
-    if (y) {
-        if ((rc = run_sel_fwd(a, p, lay, y, nullptr, nullptr, tsum, st))) return rc;
+    layout(real, &lay, &tsum, &send, &ckpt);
+    if (y || with_delta) {
+        if ((rc = run_sel_fwd(a, p, lay, y, nullptr, ckpt, tsum, st))) return rc;
     } else {
         SSM_LAUNCH(launch_tile_dsum(a->delta, tsum, (int)p.B, (int)p.D, (int)p.L, p.nchunks, p.kpl, p.dtype, st),
                    "tile sums");
@@ -505,8 +514,9 @@ int impulse_impl(const ssm_scan_args* a, int64_t t_out, void* y, void* s, void* 
                                   p.dtype, st), "suffix sums");
     SensParams q{};
     q.delta = a->delta; q.A = a->A; q.Bm = a->Bm; q.C = a->C; q.send = send; q.s = s;
+    q.x = a->x; q.ckpt = ckpt; q.s_delta = with_delta ? s_delta : nullptr;
     q.B = (int)p.B; q.D = (int)p.D; q.L = (int)p.L; q.N = (int)p.N; q.ntiles = p.nchunks; q.t_out = (int)t_out;
-    q.vec = sel_vec(p, {a->delta, s});
+    q.vec = sel_vec(p, {a->delta, s, a->x, s_delta});
     SSM_LAUNCH(launch_sens(q, p.dtype, p.kpl, st), "sensitivity");
     return ok();
 }
@@ -526,7 +536,12 @@ int ssm_workspace_bytes(int op, const void* args, size_t* out_bytes) {
     switch (op) {
         case SSM_OP_SCAN_FWD: return scan_fwd_impl((const ssm_scan_args*)args, nullptr, nullptr, 0, nullptr, out_bytes);
         case SSM_OP_SCAN_BWD: return scan_bwd_impl((const ssm_scan_args*)args, nullptr, nullptr, nullptr, 0, nullptr, out_bytes);
-        case SSM_OP_IMPULSE: return impulse_impl((const ssm_scan_args*)args, -1, nullptr, nullptr, nullptr, 0, nullptr, out_bytes);
+        case SSM_OP_IMPULSE:
+            return impulse_impl((const ssm_scan_args*)args, -1, nullptr, nullptr, nullptr, false, nullptr, 0, nullptr,
+                                out_bytes);
+        case SSM_OP_OUTPUT_SENS:
+            return impulse_impl((const ssm_scan_args*)args, -1, nullptr, nullptr, nullptr, true, nullptr, 0, nullptr,
+                                out_bytes);
         case SSM_OP_PD_FWD: return pd_fwd_impl((const pd_scan_args*)args, nullptr, nullptr, 0, nullptr, out_bytes);
         case SSM_OP_PD_BWD: return pd_bwd_impl((const pd_scan_args*)args, nullptr, nullptr, nullptr, 0, nullptr, out_bytes);
         case SSM_OP_COMPLEX_RTRL:
@@ -544,7 +559,11 @@ int ssm_scan_bwd(const ssm_scan_args* args, const ssm_scan_bwd_in* in, const ssm
 }
 int ssm_impulse_sensitivity(const ssm_scan_args* args, int64_t t_out, void* y, void* s, void* ws, size_t ws_bytes,
                             void* stream) {
-    return impulse_impl(args, t_out, y, s, ws, ws_bytes, (hipStream_t)stream, nullptr);
+    return impulse_impl(args, t_out, y, s, nullptr, false, ws, ws_bytes, (hipStream_t)stream, nullptr);
+}
+int ssm_output_sensitivity(const ssm_scan_args* args, int64_t t_out, void* y, void* s_x, void* s_delta, void* ws,
+                           size_t ws_bytes, void* stream) {
+    return impulse_impl(args, t_out, y, s_x, s_delta, true, ws, ws_bytes, (hipStream_t)stream, nullptr);
 }
 int ssm_complex_rtrl(const ssm_scan_args* args, const float* gy, const float* gh_last, float* y, float* glam,
                      float* gtheta, void* ws, size_t ws_bytes, void* stream) {

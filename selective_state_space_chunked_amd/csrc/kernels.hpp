@@ -33,7 +33,9 @@ struct SelBwdParams {
 struct SensParams {
     const void* delta; const float* A; const void* Bm; const void* C;
     const double* send;     // (B,D,ntiles) sum of delta over later steps up to t_out
-    void* s;
+    void* s;                // nullable d y[t_out] / d x
+    const void* x; const float* ckpt;   // with s_delta: inputs and the states entering each tile
+    void* s_delta;          // nullable d y[t_out] / d delta
     int B, D, L, N, ntiles, t_out, vec;
 };
 

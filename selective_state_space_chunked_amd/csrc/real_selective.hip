@@ -691,7 +691,11 @@ __global__ __launch_bounds__(256) void sens_suffix_kernel(const T* __restrict__ 
 // are loaded while the current tile is computed.
 constexpr int kSensTiles = 4;
 
-template <typename T, int KPL, int NT>
+// WD: also s_delta_t = d y[t_out] / d delta_t = sum_n mu_t[n] (A[n] a_t[n] h_{t-1}[n] + x_t B_t[n])
+//     = x_t * (the s_x sum) + sum_n C_out[n] A[n] 2^(A2[n] (S_t + delta_t)) h_{t-1}[n],
+// with the states h re-run inside the tile from its checkpoint (lane fold, DPP
+// scan, re-run, as in the forward).  B is then staged without the C_out factor.
+template <typename T, int KPL, int NT, bool WD = false>
 __global__ __launch_bounds__(256) void sens_kernel(SensParams p) {
     using Gm = TileGeom<KPL>;
     constexpr int TILE = Gm::TILE;
@@ -728,14 +732,14 @@ __global__ __launch_bounds__(256) void sens_kernel(SensParams p) {
 #pragma unroll
             for (int q = 0; q < SPT; ++q) {
                 const int e = tid + 256 * q, tt = e / NT, n = e - tt * NT;
-                sBC[Gm::idx(n, tt)] = v[q] * sCout[n];
+                sBC[Gm::idx(n, tt)] = WD ? v[q] : v[q] * sCout[n];
             }
         } else {
             const int t0 = tile * TILE;
             for (int e = tid; e < TILE * N; e += 256) {
                 const int tt = e / N, n = e - tt * N;
                 const int t = t0 + tt;
-                sBC[Gm::idx(n, tt)] = t < L ? to_f32(Bm[((size_t)b * L + t) * N + n]) * sCout[n] : 0.0f;
+                sBC[Gm::idx(n, tt)] = t < L ? to_f32(Bm[((size_t)b * L + t) * N + n]) * (WD ? 1.0f : sCout[n]) : 0.0f;
             }
         }
     };
@@ -752,7 +756,8 @@ __global__ __launch_bounds__(256) void sens_kernel(SensParams p) {
                 float z[KPL];
 #pragma unroll
                 for (int j = 0; j < KPL; ++j) z[j] = 0.0f;
-                store_run<KPL>((T*)p.s + seq * L + tl, z, vec, L - tl);
+                if (p.s) store_run<KPL>((T*)p.s + seq * L + tl, z, vec, L - tl);
+                if (WD) store_run<KPL>((T*)p.s_delta + seq * L + tl, z, vec, L - tl);
             }
             continue;
         }
@@ -774,23 +779,56 @@ __global__ __launch_bounds__(256) void sens_kernel(SensParams p) {
                 run += dl[j];
             }
         }
-        float acc[KPL];
+        float acc[KPL], gd[KPL], xv[KPL], hin = 0.0f;
 #pragma unroll
-        for (int j = 0; j < KPL; ++j) acc[j] = 0.0f;
+        for (int j = 0; j < KPL; ++j) { acc[j] = 0.0f; gd[j] = 0.0f; }
+        if (WD) {
+            load_run_masked<T, KPL>((const T*)p.x + seq * L + tl, xv, min(L, p.t_out + 1) - tl);
+            if (lane < N) hin = p.ckpt[(seq * p.ntiles + tile) * N + lane];   // state entering the tile
+        }
         for_states<NT>(N, [&](auto st) {
             const float A2n = st.bc(A2);
             float bc[KPL], e[KPL];
             read_run<KPL>(sBC + st.n * Gm::LDSW + lane * Gm::SEG, bc);
 #pragma unroll
             for (int j = 0; j < KPL; ++j) e[j] = __builtin_amdgcn_exp2f(A2n * S[j]);
+            if constexpr (!WD) {
 #pragma unroll
-            for (int j = 0; j < KPL; ++j) acc[j] = fmaf(bc[j], e[j], acc[j]);
+                for (int j = 0; j < KPL; ++j) acc[j] = fmaf(bc[j], e[j], acc[j]);
+            } else {
+                const float Cn = sCout[st.n];
+                float a[KPL], bx[KPL], Sf = 0.0f;
+#pragma unroll
+                for (int j = 0; j < KPL; ++j) {
+                    acc[j] = fmaf(bc[j] * Cn, e[j], acc[j]);
+                    a[j] = __builtin_amdgcn_exp2f(dl[j] * A2n);
+                    bx[j] = dl[j] * xv[j] * bc[j];
+                    Sf = fmaf(a[j], Sf, bx[j]);
+                }
+                float Pf = __builtin_amdgcn_exp2f(lsum * A2n);
+                row_scan_affine_up(Pf, Sf);
+                const float cin = st.bc(hin);
+                float h = dpp<SSM_DPP_ROW_SHR(1)>(cin, fmaf(Pf, cin, Sf));   // state entering this lane's run
+                const float CA = Cn * (A2n * kLn2);
+#pragma unroll
+                for (int j = 0; j < KPL; ++j) {
+                    gd[j] = fmaf(CA, e[j] * a[j] * h, gd[j]);
+                    h = fmaf(a[j], h, bx[j]);
+                }
+            }
         });
         if (act && tl < L) {
             float v[KPL];
+            if (p.s) {
 #pragma unroll
-            for (int j = 0; j < KPL; ++j) v[j] = (tl + j <= p.t_out) ? dl[j] * acc[j] : 0.0f;
-            store_run<KPL>((T*)p.s + seq * L + tl, v, vec, L - tl);
+                for (int j = 0; j < KPL; ++j) v[j] = (tl + j <= p.t_out) ? dl[j] * acc[j] : 0.0f;
+                store_run<KPL>((T*)p.s + seq * L + tl, v, vec, L - tl);
+            }
+            if (WD) {
+#pragma unroll
+                for (int j = 0; j < KPL; ++j) v[j] = (tl + j <= p.t_out) ? fmaf(xv[j], acc[j], gd[j]) : 0.0f;
+                store_run<KPL>((T*)p.s_delta + seq * L + tl, v, vec, L - tl);
+            }
         }
         if (more) {
             __syncthreads();   // every lane is done with this tile's values
@@ -889,6 +927,16 @@ hipError_t launch_sens_suffix(const void* delta, const float* tile_dsum, double*
 hipError_t launch_sens(const SensParams& p, int dtype, int kpl, hipStream_t st) {
     dim3 grid((p.D + 15) / 16, p.B, (p.ntiles + kSensTiles - 1) / kSensTiles);
     const bool n16 = p.N == 16;
+    if (p.s_delta) {
+        if (dtype == 0) {
+            if (n16) { SSM_DISPATCH_KPL(kpl, sens_kernel<float, K_, 16, true><<<grid, 256, 0, st>>>(p)) }
+            else { SSM_DISPATCH_KPL(kpl, sens_kernel<float, K_, 0, true><<<grid, 256, 0, st>>>(p)) }
+        } else {
+            if (n16) { SSM_DISPATCH_KPL(kpl, sens_kernel<bf16_t, K_, 16, true><<<grid, 256, 0, st>>>(p)) }
+            else { SSM_DISPATCH_KPL(kpl, sens_kernel<bf16_t, K_, 0, true><<<grid, 256, 0, st>>>(p)) }
+        }
+        return hipGetLastError();
+    }
     if (dtype == 0) {
         if (n16) { SSM_DISPATCH_KPL(kpl, sens_kernel<float, K_, 16><<<grid, 256, 0, st>>>(p)) }
         else { SSM_DISPATCH_KPL(kpl, sens_kernel<float, K_, 0><<<grid, 256, 0, st>>>(p)) }

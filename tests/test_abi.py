@@ -22,7 +22,7 @@ def header_functions():
 def test_exports_every_declared_function():
     names = header_functions()
     assert {"ssm_scan_fwd", "ssm_scan_bwd", "ssm_impulse_sensitivity", "pd_scan_fwd", "pd_scan_bwd",
-            "ssm_complex_rtrl", "ssm_workspace_bytes"} <= set(names)
+            "ssm_complex_rtrl", "ssm_output_sensitivity", "ssm_workspace_bytes"} <= set(names)
     lib = B.lib()
     missing = [n for n in names if not hasattr(lib, n)]
     assert not missing, missing
@@ -37,6 +37,7 @@ def test_header_constants_match_binding():
     assert consts["SSM_COMPLEX_SHARED"] == B.SSM_COMPLEX_SHARED
     assert consts["SSM_OP_PD_BWD"] == B.SSM_OP_PD_BWD
     assert consts["SSM_OP_COMPLEX_RTRL"] == B.SSM_OP_COMPLEX_RTRL
+    assert consts["SSM_OP_OUTPUT_SENS"] == B.SSM_OP_OUTPUT_SENS
     assert B.lib().ssm_abi_version() == consts["SSM_ABI_VERSION"]
 
 
@@ -209,3 +210,24 @@ def test_pd_ste_host_checks():
     i = B.PDBwdIn(gy=FAKE * 32, ste_logits=None, tau=0.0)
     rc = L.pd_scan_bwd(ctypes.byref(a), ctypes.byref(i), ctypes.byref(B.PDGrads(gd=FAKE * 64)), None, 0, None)
     assert rc == status("SSM_ERR_WORKSPACE")
+
+
+def test_output_sensitivity_host_checks():
+    """s_delta is required; its workspace holds the per-tile checkpoints (grows with L, unlike the impulse path)."""
+    L = B.lib()
+    rc, n1 = ws_bytes(B.SSM_OP_OUTPUT_SENS, sel_args(length=4096))
+    assert rc == 0
+    _, n2 = ws_bytes(B.SSM_OP_OUTPUT_SENS, sel_args(length=8192))
+    _, m1 = ws_bytes(B.SSM_OP_IMPULSE, sel_args(length=4096))
+    assert n2 - n1 >= 2 * 32 * 16 * 16 * 4 and n1 > m1   # 16 more tiles x 16 states per channel
+    a = sel_args()
+    rc = L.ssm_output_sensitivity(ctypes.byref(a), -1, None, FAKE * 64, None, None, 0, None)
+    assert rc == status("SSM_ERR_NULL")
+    rc = L.ssm_output_sensitivity(ctypes.byref(a), -1, None, None, FAKE * 2 + 8, None, 0, None)   # inside x
+    assert rc == status("SSM_ERR_LAYOUT")
+    rc = L.ssm_output_sensitivity(ctypes.byref(a), 5000, None, None, FAKE * 64, None, 0, None)
+    assert rc == status("SSM_ERR_SHAPE")
+    rc = L.ssm_output_sensitivity(ctypes.byref(a), -1, None, None, FAKE * 64, None, 0, None)
+    assert rc == status("SSM_ERR_WORKSPACE")
+    rc, _ = ws_bytes(B.SSM_OP_OUTPUT_SENS, cplx_args())
+    assert rc == status("SSM_ERR_UNSUPPORTED")

@@ -140,3 +140,47 @@ def test_impulse_sensitivity_variants(dt, N, chunk_len, L, t_out):
     tol = BF16 if dt == "bf16" else F32
     assert_close("s", out["s"], s, **tol)
     assert_close("y", out["y"], y, **tol)
+
+
+@pytest.mark.parametrize("dt,N,chunk_len,L,t_out,h0", [
+    ("f32", 16, 256, 1300, -1, True),    # ragged last tile, t_out at the end, nonzero h0
+    ("f32", 16, 256, 3000, 1777, False),  # t_out inside a tile, zero tail after it
+    ("bf16", 16, 256, 2600, 2100, True),
+    ("f32", 5, 128, 900, 450, True),      # generic state count, 128-step tiles
+    ("f32", 16, 64, 700, 0, True),        # t_out = 0: only the first step is sensitive
+])
+def test_output_sensitivity(dt, N, chunk_len, L, t_out, h0):
+    """d y[t_out]/d x and d y[t_out]/d delta (and y) against the oracle; s_x equal to the impulse path's."""
+    ssm = _ssm()
+    cfg = synth.make_real(B=2, D=20, N=N, L=L, dtype=dt, seed=60 + N + L)
+    t = {k: _dev(cfg[k], dt) for k in ("delta", "x", "Bm", "C")}
+    t["A"] = _dev(cfg["A"], "f32")
+    hh = None
+    if h0:
+        hh = np.random.default_rng(61).standard_normal((2, 20, N)).astype(np.float32)
+        t["h0"] = torch.from_numpy(hh).cuda()
+    out = ssm.output_sensitivity(t_out=t_out, want_y=True, chunk_len=chunk_len, **t)
+    ref = ssm.impulse_sensitivity(t_out=t_out, want_y=False, chunk_len=chunk_len,
+                                  **{k: v for k, v in t.items() if k != "h0"})
+    torch.cuda.synchronize()
+    kw = dict(delta=cfg["delta"], x=cfg["x"], A=cfg["A"], Bm=cfg["Bm"], C=cfg["C"], h0=hh, B=2, D=20, L=L, N=N)
+    sx, sd = oracle.output_sens(**kw, t_out=None if t_out == -1 else t_out)
+    y, _ = oracle.real_fwd(**kw)
+    tol = BF16 if dt == "bf16" else F32
+    assert_close("s_delta", out["s_delta"], sd, **tol)
+    assert_close("s_x", out["s_x"], sx, **tol)
+    assert_close("y", out["y"], y, **tol)
+    assert torch.equal(out["s_x"], ref["s"])   # the same closed-form costate, bit for bit
+
+
+def test_output_sensitivity_impulse_config():
+    """The impulse workload's inputs (x = e_0, slow decay), B=1 D=64 N=16 L=20000, y[L-1]."""
+    ssm = _ssm()
+    cfg = synth.make_impulse(B=1, D=64, N=16, L=20000, seed=8)
+    t = {k: _dev(cfg[k], "f32") for k in ("delta", "x", "Bm", "C", "A")}
+    out = ssm.output_sensitivity(**t)
+    torch.cuda.synchronize()
+    kw = dict(delta=cfg["delta"], x=cfg["x"], A=cfg["A"], Bm=cfg["Bm"], C=cfg["C"], B=1, D=64, L=20000, N=16)
+    sx, sd = oracle.output_sens(**kw)
+    assert_close("s_delta", out["s_delta"], sd, **F32)
+    assert_close("s_x", out["s_x"], sx, **F32)
