@@ -136,6 +136,30 @@ def real_bwd(*, delta=None, x=None, A=None, Bm=None, a=None, b=None, C, h0=None,
     return out
 
 
+def step_sizes(z, delta_bias=None, softplus=False):
+    """Step sizes from the input-projection output (the discretisation input of
+    the S3M page, section 1.1: delta = softplus(projection(x))), in fp64:
+    delta = softplus(z + bias[d]) with softplus(v) = log(1 + e^v), or z + bias
+    without softplus.  z (B,D,L) (bf16 bit arrays accepted), bias (D,)."""
+    v = _w(z).copy()
+    if delta_bias is not None:
+        v += _w(delta_bias)[None, :, None]
+    return np.logaddexp(0.0, v) if softplus else v
+
+
+def step_size_grads(gdelta, z, delta_bias=None, softplus=False):
+    """Pull-back of dLoss/ddelta to the pre-activation: gz = gdelta * sigmoid(z + bias)
+    (d softplus(v)/dv = 1 / (1 + e^-v)), or gdelta without softplus; gbias = sum over b, t."""
+    if softplus:
+        v = _w(z).copy()
+        if delta_bias is not None:
+            v += _w(delta_bias)[None, :, None]
+        gz = gdelta * (0.5 * (1.0 + np.tanh(0.5 * v)))   # logistic function, no overflow
+    else:
+        gz = np.array(gdelta, dtype=np.float64)
+    return gz, gz.sum(axis=(0, 2))
+
+
 def impulse_sens(*, delta, A, Bm, C, B, D, L, N, t_out=None):
     """s[b,d,t] = d y[b,d,t_out] / d x[b,d,t]  (B,D,L)."""
     t_out = L - 1 if t_out is None else int(t_out)

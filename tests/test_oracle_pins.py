@@ -256,6 +256,32 @@ def test_impulse_linearity_and_backward():
         assert np.all(s[:, :, t_out + 1:] == 0.0)
 
 
+@pytest.mark.parametrize("softplus", [True, False])
+def test_step_size_pullback_fd(softplus):
+    """Gradients w.r.t. the projection output z and the bias through delta = softplus(z + bias),
+    by central differences of the forward loss; softplus of a known value; identity without softplus."""
+    p = small_real(B=2, D=3, N=4, L=11, seed=23)
+    g = np.random.default_rng(24)
+    z = g.standard_normal((2, 3, 11)) * 2.0
+    bias = g.standard_normal(3)
+    kw = {k: p[k] for k in ("x", "A", "Bm", "C", "h0", "B", "D", "L", "N")}
+
+    def loss(q, **over):
+        zz = over.get("z", z)
+        bb = over.get("bias", bias)
+        y, hl = oracle.real_fwd(delta=oracle.step_sizes(zz, bb, softplus), **kw)
+        return float((y * p["gy"]).sum() + (hl * p["ghlast"]).sum())
+    dl = oracle.step_sizes(z, bias, softplus)
+    gd = oracle.real_bwd(delta=dl, gy=p["gy"], ghlast=p["ghlast"], **kw)["gdelta"]
+    gz, gb = oracle.step_size_grads(gd, z, bias, softplus)
+    fd_check(loss, {"z": z, "bias": bias}, "z", gz)
+    fd_check(loss, {"z": z, "bias": bias}, "bias", gb)
+    if softplus:
+        close(oracle.step_sizes(np.zeros((1, 1, 1)), None, True), np.full((1, 1, 1), math.log(2.0)), rtol=1e-15)
+    else:
+        close(oracle.step_sizes(z, None, False), z, rtol=0, atol=0)
+
+
 @pytest.mark.parametrize("t_out", [16, 9, 0])
 def test_output_sensitivity_delta_fd(t_out):
     """d y[t_out] / d delta_t by central differences of the forward (h0 and x nonzero)."""
