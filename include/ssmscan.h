@@ -132,6 +132,14 @@ typedef struct {
     const float* c;      /* (H,M) complex64 readout                        */
     /* all modes */
     const float* h0;     /* nullable initial state (B,D,N) f32 / (B,H,M) complex64; NULL = 0 */
+    /* SSM_REAL_SELECTIVE: step sizes from the input projection, with the
+     * discretisation merged into the scan (S3M page, sections 1.1 and 4.1):
+     * when delta_bias is non-NULL or delta_softplus is 1, delta holds the
+     * projection output z and the scan uses delta = softplus(z + delta_bias[d])
+     * (softplus(v) = log(1 + e^v)), or z + delta_bias[d] without softplus;
+     * gdelta is then the gradient w.r.t. z.  Both off: delta is used as given. */
+    const float* delta_bias;  /* nullable (D) f32 */
+    int32_t delta_softplus;   /* 0 or 1 */
 } ssm_scan_args;
 
 typedef struct {
@@ -166,6 +174,7 @@ typedef struct {
     float* gtheta;  /* complex (H,M) f32 (sum over b and t)     */
     float* gc;      /* complex (H,M) complex64                  */
     float* gh0;     /* (B,D,N) f32 / (B,H,M) complex64          */
+    float* gdelta_bias;  /* selective (D) f32, sum over b and t (bias taken as 0 if delta_bias is NULL) */
 } ssm_scan_grads;
 
 /* Arguments of the PD scan.  N = state (1..16), K = dictionary size (1..64).
@@ -271,7 +280,8 @@ int ssm_complex_rtrl(const ssm_scan_args* args, const float* gy, const float* gh
  * t <= t_out, 0 after; h_{t-1} are the forward states (from h0), recomputed per
  * tile from checkpoints the call writes into its workspace (O(n_chunks * N)
  * per sequence, unlike ssm_impulse_sensitivity).  t_out in [0,L); -1 means
- * L-1.  y, s_x nullable, s_delta required; all (B,D,L) dtype.
+ * L-1.  y, s_x nullable, s_delta required; all (B,D,L) dtype.  With delta_bias or
+ * delta_softplus set, s_delta is the sensitivity to the projection output z.
  * SSM_REAL_SELECTIVE only; workspace from ssm_workspace_bytes(SSM_OP_OUTPUT_SENS, ...). */
 int ssm_output_sensitivity(const ssm_scan_args* args, int64_t t_out, void* y, void* s_x, void* s_delta,
                            void* ws, size_t ws_bytes, void* stream);

@@ -29,7 +29,8 @@ class ScanArgs(ctypes.Structure):
     _fields_ = [("mode", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("batch", _i64), ("channels", _i64), ("length", _i64), ("state", _i64), ("chunk_len", _i64),
                 ("delta", _vp), ("x", _vp), ("A", _vp), ("Bm", _vp), ("a", _vp), ("b", _vp), ("C", _vp),
-                ("r", _vp), ("phi", _vp), ("lam", _vp), ("theta", _vp), ("u", _vp), ("c", _vp), ("h0", _vp)]
+                ("r", _vp), ("phi", _vp), ("lam", _vp), ("theta", _vp), ("u", _vp), ("c", _vp), ("h0", _vp),
+                ("delta_bias", _vp), ("delta_softplus", ctypes.c_int32)]
 
 
 class ScanFwdOut(ctypes.Structure):
@@ -43,7 +44,7 @@ class ScanBwdIn(ctypes.Structure):
 class ScanGrads(ctypes.Structure):
     _fields_ = [("gdelta", _vp), ("gx", _vp), ("gA", _vp), ("gBm", _vp), ("ga", _vp), ("gb", _vp),
                 ("gC", _vp), ("gu", _vp), ("gr", _vp), ("gphi", _vp), ("glam", _vp), ("gtheta", _vp),
-                ("gc", _vp), ("gh0", _vp)]
+                ("gc", _vp), ("gh0", _vp), ("gdelta_bias", _vp)]
 
 
 class PDArgs(ctypes.Structure):
@@ -146,7 +147,10 @@ def n_chunks(L, chunk_len):
 # diagonal scans
 # ---------------------------------------------------------------------------
 def _scan_args(mode, *, delta=None, x=None, A=None, Bm=None, a=None, b=None, C=None, r=None, phi=None, lam=None,
-               theta=None, u=None, c=None, h0=None, chunk_len=0):
+               theta=None, u=None, c=None, h0=None, delta_bias=None, delta_softplus=False, chunk_len=0):
+    """Marshal the scan arguments.  Selective mode: with ``delta_bias`` (D,) or
+    ``delta_softplus`` set, ``delta`` is the projection output z and the scan uses
+    softplus(z + delta_bias) (or z + delta_bias)."""
     if mode == SSM_REAL_SELECTIVE:
         _need(delta, "delta")
         Bsz, D, L = delta.shape
@@ -159,6 +163,7 @@ def _scan_args(mode, *, delta=None, x=None, A=None, Bm=None, a=None, b=None, C=N
             _need(t, nm, st, shp, dev)
         _need(A, "A", torch.float32, (D, N), dev)
         _need(h0, "h0", torch.float32, (Bsz, D, N), dev)
+        _need(delta_bias, "delta_bias", torch.float32, (D,), dev)
         dt = SSM_BF16 if st == torch.bfloat16 else SSM_F32
     elif mode == SSM_REAL_DENSE:
         _need(a, "a", torch.float32)
@@ -182,7 +187,7 @@ def _scan_args(mode, *, delta=None, x=None, A=None, Bm=None, a=None, b=None, C=N
     args = ScanArgs(mode=mode, dtype=dt, batch=Bsz, channels=D, length=L, state=N, chunk_len=chunk_len,
                     delta=_ptr(delta), x=_ptr(x), A=_ptr(A), Bm=_ptr(Bm), a=_ptr(a), b=_ptr(b), C=_ptr(C),
                     r=_ptr(r), phi=_ptr(phi), lam=_ptr(lam), theta=_ptr(theta), u=_ptr(u), c=_ptr(c),
-                    h0=_ptr(h0))
+                    h0=_ptr(h0), delta_bias=_ptr(delta_bias), delta_softplus=int(bool(delta_softplus)))
     return args, (Bsz, D, L, N), dev
 
 
@@ -215,7 +220,7 @@ def scan_fwd(mode, *, want_y=True, want_h_last=False, want_ckpt=False, chunk_len
 
 
 _GRADS = {
-    SSM_REAL_SELECTIVE: ("gdelta", "gx", "gA", "gBm", "gC", "gh0"),
+    SSM_REAL_SELECTIVE: ("gdelta", "gx", "gA", "gBm", "gC", "gh0"),   # gdelta_bias on request
     SSM_REAL_DENSE: ("ga", "gb", "gC", "gh0"),
     SSM_COMPLEX_SHARED: ("gu", "gr", "gphi", "glam", "gtheta", "gc", "gh0"),
 }
@@ -238,10 +243,11 @@ def scan_bwd(mode, *, gy, gh_last=None, ckpt=None, want=None, chunk_len=0, out=N
         "gu": ((Bsz, D, L, N), torch.complex64), "gr": ((Bsz, D, L), torch.float32),
         "gphi": ((Bsz, D, L), torch.float32), "glam": ((D, N), torch.float32),
         "gtheta": ((D, N), torch.float32), "gc": ((D, N), torch.complex64),
+        "gdelta_bias": ((D,), torch.float32),
     }
     out = dict(out or {})
     for k in want:
-        if k not in _GRADS[mode]:
+        if k not in _GRADS[mode] and not (k == "gdelta_bias" and mode == SSM_REAL_SELECTIVE):
             raise ValueError(f"gradient {k} does not exist for mode {mode}")
         if k not in out:
             shp, dt = shapes[k]

@@ -172,9 +172,14 @@ int validate_scan_args(const ssm_scan_args* a, ScanPlan* pl) {
     pl->nchunks = (int)cdiv(pl->L, T);
     const size_t BDL = pl->B * pl->D * pl->L;
     const size_t BLN = pl->B * pl->L * pl->N;
+    if (a->delta_softplus != 0 && a->delta_softplus != 1)
+        return fail(SSM_ERR_SHAPE, "delta_softplus must be 0 or 1 (got %d)", a->delta_softplus);
+    if (a->mode != SSM_REAL_SELECTIVE && (a->delta_bias || a->delta_softplus))
+        return fail(SSM_ERR_UNSUPPORTED, "delta_bias / delta_softplus apply to SSM_REAL_SELECTIVE only");
     if (a->mode == SSM_REAL_SELECTIVE) {
         if (!a->delta || !a->x || !a->A || !a->Bm || !a->C)
             return fail(SSM_ERR_NULL, "SSM_REAL_SELECTIVE needs delta, x, A, Bm and C");
+        if (int rc = check_align(a->delta_bias, 4, "delta_bias")) return rc;
         const size_t al = pl->esz;
         int rc;
         if ((rc = check_align(a->delta, al, "delta")) || (rc = check_align(a->x, al, "x")) ||
@@ -212,6 +217,7 @@ std::vector<Range> scan_inputs(const ssm_scan_args* a, const ScanPlan& p) {
         {a->lam, (size_t)p.D * p.N * 4, "lam"}, {a->theta, (size_t)p.D * p.N * 4, "theta"},
         {a->u, BDLN * 8, "u"}, {a->c, (size_t)p.D * p.N * 8, "c"},
         {a->h0, (size_t)p.B * p.D * st, "h0"},
+        {a->delta_bias, (size_t)p.D * 4, "delta_bias"},
     };
 }
 
@@ -250,6 +256,7 @@ int run_sel_fwd(const ssm_scan_args* a, const ScanPlan& p, const SelFwdLayout& l
     q.B = (int)p.B; q.D = (int)p.D; q.L = (int)p.L; q.N = (int)p.N;
     q.ntiles = p.nchunks; q.tiles_per_seg = lay.tps; q.G = lay.G;
     q.vec = sel_vec(p, {a->delta, a->x, y});
+    q.stepf = StepXform{a->delta_bias, a->delta_softplus};
     if (lay.G > 1) {
         SSM_LAUNCH(launch_sel_fwd(q, p.dtype, p.kpl, true, st), "selective forward summary");
         SSM_LAUNCH(launch_seg_combine_fwd(lay.segP, lay.segS, a->h0, lay.carry, (int)(p.B * p.D), lay.G,
@@ -267,9 +274,9 @@ struct SelBwdLayout {
     float* ckpt = nullptr;
     int G, tps;
     float *segQ = nullptr, *segR = nullptr, *nu = nullptr;
-    float *partB = nullptr, *partC = nullptr, *partA = nullptr;
+    float *partB = nullptr, *partC = nullptr, *partA = nullptr, *partBias = nullptr;
 };
-void sel_bwd_layout(const ScanPlan& p, bool have_ckpt, bool wantB, bool wantC, bool wantA, Carve& cv,
+void sel_bwd_layout(const ScanPlan& p, bool have_ckpt, bool wantB, bool wantC, bool wantA, bool wantBias, Carve& cv,
                     SelBwdLayout* lay) {
     if (!have_ckpt) {
         lay->ckpt = cv.take<float>((size_t)p.B * p.D * p.nchunks * p.N);
@@ -288,6 +295,7 @@ void sel_bwd_layout(const ScanPlan& p, bool have_ckpt, bool wantB, bool wantC, b
     if (wantB) lay->partB = cv.take<float>(np);
     if (wantC) lay->partC = cv.take<float>(np);
     if (wantA) lay->partA = cv.take<float>((size_t)p.B * lay->G * p.D * p.N);
+    if (wantBias) lay->partBias = cv.take<float>((size_t)p.B * lay->G * p.D);
 }
 
 // ---------------------------------------------------------------------------
@@ -402,7 +410,7 @@ int scan_bwd_impl(const ssm_scan_args* a, const ssm_scan_bwd_in* in, const ssm_s
             {g->gC, BLN * es, "gC"}, {g->gu, BDL * p.N * 8, "gu"}, {g->gr, BDL * 4, "gr"},
             {g->gphi, BDL * 4, "gphi"}, {g->glam, (size_t)p.D * p.N * 4, "glam"},
             {g->gtheta, (size_t)p.D * p.N * 4, "gtheta"}, {g->gc, (size_t)p.D * p.N * 8, "gc"},
-            {g->gh0, hb, "gh0"}};
+            {g->gh0, hb, "gh0"}, {g->gdelta_bias, (size_t)p.D * 4, "gdelta_bias"}};
         for (const auto& o : outs)
             if ((rc = check_align(o.p, 2, o.name))) return rc;
         if ((rc = check_overlaps(ins, outs))) return rc;
@@ -411,12 +419,13 @@ int scan_bwd_impl(const ssm_scan_args* a, const ssm_scan_bwd_in* in, const ssm_s
     if (p.mode == SSM_REAL_SELECTIVE) {
         // workspace is sized for the worst case (checkpoints recomputed, every gradient wanted)
         SelBwdLayout sizing;
-        sel_bwd_layout(p, false, true, true, true, cv, &sizing);
+        sel_bwd_layout(p, false, true, true, true, true, cv, &sizing);
         if (need_only) { *need_only = cv.off; return ok(); }
         if ((rc = check_ws(ws, ws_bytes, cv.off))) return rc;
         Carve real(ws);
         SelBwdLayout lay;  // only the buffers this call needs are non-null
-        sel_bwd_layout(p, have_ckpt, g->gBm != nullptr, g->gC != nullptr, g->gA != nullptr, real, &lay);
+        sel_bwd_layout(p, have_ckpt, g->gBm != nullptr, g->gC != nullptr, g->gA != nullptr,
+                       g->gdelta_bias != nullptr, real, &lay);
         const float* ckpt = in->ckpt;
         if (!have_ckpt) {
             if ((rc = run_sel_fwd(a, p, lay.fwd, nullptr, nullptr, lay.ckpt, nullptr, st))) return rc;
@@ -431,6 +440,8 @@ int scan_bwd_impl(const ssm_scan_args* a, const ssm_scan_bwd_in* in, const ssm_s
         q.B = (int)p.B; q.D = (int)p.D; q.L = (int)p.L; q.N = (int)p.N;
         q.ntiles = p.nchunks; q.tiles_per_seg = lay.tps; q.G = lay.G;
         q.vec = sel_vec(p, {a->delta, a->x, in->gy, g->gdelta, g->gx});
+        q.stepf = StepXform{a->delta_bias, a->delta_softplus};
+        q.partBias = lay.partBias;
         if (lay.G > 1) {
             SSM_LAUNCH(launch_sel_bwd(q, p.dtype, p.kpl, true, st), "selective backward summary");
             SSM_LAUNCH(launch_seg_combine_rev(lay.segQ, lay.segR, in->gh_last, lay.nu, (int)(p.B * p.D), lay.G,
@@ -445,6 +456,9 @@ int scan_bwd_impl(const ssm_scan_args* a, const ssm_scan_bwd_in* in, const ssm_s
         if (g->gA)
             SSM_LAUNCH(launch_reduce_parts_dn(lay.partA, (int)p.B, lay.G, (int)p.D, (int)p.N, g->gA, st),
                        "reduce gA");
+        if (g->gdelta_bias)
+            SSM_LAUNCH(launch_reduce_parts_dn(lay.partBias, (int)p.B, lay.G, (int)p.D, 1, g->gdelta_bias, st),
+                       "reduce gdelta_bias");
         return ok();
     }
     if (p.mode == SSM_REAL_DENSE) {
@@ -507,14 +521,17 @@ int impulse_impl(const ssm_scan_args* a, int64_t t_out, void* y, void* s, void* 
     if (y || with_delta) {
         if ((rc = run_sel_fwd(a, p, lay, y, nullptr, ckpt, tsum, st))) return rc;
     } else {
-        SSM_LAUNCH(launch_tile_dsum(a->delta, tsum, (int)p.B, (int)p.D, (int)p.L, p.nchunks, p.kpl, p.dtype, st),
+        SSM_LAUNCH(launch_tile_dsum(a->delta, StepXform{a->delta_bias, a->delta_softplus}, tsum, (int)p.B,
+                                    (int)p.D, (int)p.L, p.nchunks, p.kpl, p.dtype, st),
                    "tile sums");
     }
-    SSM_LAUNCH(launch_sens_suffix(a->delta, tsum, send, (int)p.B, (int)p.D, (int)p.L, p.nchunks, p.T, (int)t_out,
+    SSM_LAUNCH(launch_sens_suffix(a->delta, StepXform{a->delta_bias, a->delta_softplus}, tsum, send, (int)p.B,
+                                  (int)p.D, (int)p.L, p.nchunks, p.T, (int)t_out,
                                   p.dtype, st), "suffix sums");
     SensParams q{};
     q.delta = a->delta; q.A = a->A; q.Bm = a->Bm; q.C = a->C; q.send = send; q.s = s;
     q.x = a->x; q.ckpt = ckpt; q.s_delta = with_delta ? s_delta : nullptr;
+    q.stepf = StepXform{a->delta_bias, a->delta_softplus};
     q.B = (int)p.B; q.D = (int)p.D; q.L = (int)p.L; q.N = (int)p.N; q.ntiles = p.nchunks; q.t_out = (int)t_out;
     q.vec = sel_vec(p, {a->delta, s, a->x, s_delta});
     SSM_LAUNCH(launch_sens(q, p.dtype, p.kpl, st), "sensitivity");

@@ -8,6 +8,12 @@
 namespace ssm {
 
 // ------------------------------- real, selective ---------------------------
+// Step sizes taken from the input-projection output z: delta = softplus(z + bias[d])
+// (softplus = 1) or z + bias[d]; both off: delta as given.
+struct StepXform {
+    const float* bias;  // (D) or null
+    int softplus;
+};
 struct SelFwdParams {
     const void* delta; const void* x; const float* A; const void* Bm; const void* C;
     const float* h0;        // (B,D,N) or null
@@ -18,6 +24,7 @@ struct SelFwdParams {
     float* segP;            // summary pass: product of a over each segment (B,D,G,N)
     float* segS;            // summary pass: local state at segment end (B,D,G,N)
     float* tile_dsum;       // (B,D,ntiles) sum of delta over each tile, or null
+    StepXform stepf;
     int B, D, L, N, ntiles, tiles_per_seg, G, vec;
 };
 struct SelBwdParams {
@@ -27,7 +34,9 @@ struct SelBwdParams {
     void* gdelta; void* gx; float* gh0;
     float* partB; float* partC;  // (nblk,B,N,L) partial sums over each block of channels
     float* partA;                // (B,G,D,N)
+    float* partBias;             // (B,G,D) partial sums of the step-size bias gradient, or null
     float* segQ; float* segR;    // summary pass outputs (B,D,G,N)
+    StepXform stepf;
     int B, D, L, N, ntiles, tiles_per_seg, G, vec;
 };
 struct SensParams {
@@ -36,6 +45,7 @@ struct SensParams {
     void* s;                // nullable d y[t_out] / d x
     const void* x; const float* ckpt;   // with s_delta: inputs and the states entering each tile
     void* s_delta;          // nullable d y[t_out] / d delta
+    StepXform stepf;
     int B, D, L, N, ntiles, t_out, vec;
 };
 
@@ -50,10 +60,10 @@ hipError_t launch_seg_combine_rev(const float* Q, const float* R, const float* n
 hipError_t launch_reduce_parts_btn(const float* partB, const float* partC, int nblk, int B, int N, int L,
                                    void* outB, void* outC, int dtype, hipStream_t st);
 hipError_t launch_reduce_parts_dn(const float* part, int B, int G, int D, int N, float* out, hipStream_t st);
-hipError_t launch_sens_suffix(const void* delta, const float* tile_dsum, double* send, int B, int D, int L,
-                              int ntiles, int tile_len, int t_out, int dtype, hipStream_t st);
-hipError_t launch_tile_dsum(const void* delta, float* tile_dsum, int B, int D, int L, int ntiles, int kpl,
-                            int dtype, hipStream_t st);
+hipError_t launch_sens_suffix(const void* delta, StepXform stepf, const float* tile_dsum, double* send, int B, int D,
+                              int L, int ntiles, int tile_len, int t_out, int dtype, hipStream_t st);
+hipError_t launch_tile_dsum(const void* delta, StepXform stepf, float* tile_dsum, int B, int D, int L, int ntiles,
+                            int kpl, int dtype, hipStream_t st);
 hipError_t launch_sens(const SensParams& p, int dtype, int kpl, hipStream_t st);
 
 // ------------------------------- real, dense -------------------------------

@@ -130,6 +130,33 @@ __device__ __forceinline__ void stage_states(float* __restrict__ dst, const T* _
     }
 }
 
+// Step sizes from the projection output (S3M page, sections 1.1 and 4.1: the
+// discretisation takes delta = softplus(projection(x)), merged into the scan
+// kernel): log(1 + e^v), exactly v above 20 (e^-20 is below half an ulp).
+__device__ __forceinline__ float softplus_f(float v) { return v > 20.0f ? v : log1pf(expf(v)); }
+__device__ __forceinline__ float step_xform(float z, float bias, int softplus) {
+    const float v = z + bias;
+    return softplus ? softplus_f(v) : v;
+}
+// d delta / d z = sigmoid(z + bias) = 1 - e^-delta (from the step size itself)
+__device__ __forceinline__ float step_xform_grad(float delta, int softplus) {
+    return softplus ? -expm1f(-delta) : 1.0f;
+}
+
+// A lane's run of step sizes, with the projection-output transform applied;
+// steps past the end stay 0 (identity steps).
+template <typename T, int KPL>
+__device__ __forceinline__ void load_steps(const T* __restrict__ p, float (&dl)[KPL], int nval, bool vec,
+                                           const StepXform& f, int d) {
+    if (nval >= KPL) load_run<KPL>(p, dl, vec);
+    else load_run_masked<T, KPL>(p, dl, nval);
+    if (f.bias != nullptr || f.softplus) {   // uniform
+        const float bias = f.bias ? f.bias[d] : 0.0f;
+#pragma unroll
+        for (int j = 0; j < KPL; ++j) dl[j] = j < nval ? step_xform(dl[j], bias, f.softplus) : 0.0f;
+    }
+}
+
 template <int KPL>
 __device__ __forceinline__ void read_run(const float* __restrict__ s, float (&v)[KPL]) {
 #pragma unroll
@@ -184,13 +211,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
         float dl[KPL], dx[KPL];
         {
             float xv[KPL];
-            if (nval >= KPL) {
-                load_run<KPL>(delta + rowoff + tl, dl, vec);
-                load_run<KPL>(xin + rowoff + tl, xv, vec);
-            } else {
-                load_run_masked<T, KPL>(delta + rowoff + tl, dl, nval);
-                load_run_masked<T, KPL>(xin + rowoff + tl, xv, nval);
-            }
+            load_steps<T, KPL>(delta + rowoff + tl, dl, nval, vec, p.stepf, dc);
+            if (nval >= KPL) load_run<KPL>(xin + rowoff + tl, xv, vec);
+            else load_run_masked<T, KPL>(xin + rowoff + tl, xv, nval);
 #pragma unroll
             for (int j = 0; j < KPL; ++j) dx[j] = dl[j] * xv[j];
         }
@@ -310,7 +333,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
     const bool vec = p.vec != 0;
     const bool wantB = p.partB != nullptr, wantC = p.partC != nullptr;
 
-    float A2 = 0.0f, nu = 0.0f, gAacc = 0.0f, Qseg = 1.0f;
+    float A2 = 0.0f, nu = 0.0f, gAacc = 0.0f, Qseg = 1.0f, gbias = 0.0f;
     if (lane < N) {
         A2 = p.A[(size_t)dc * N + lane] * kLog2e;
         if (!SUMMARY) {
@@ -333,12 +356,11 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
         float dl[KPL], dx[KPL], gyv[KPL];
         {
             float xv[KPL];
+            load_steps<T, KPL>(delta + rowoff + tl, dl, nval, vec, p.stepf, dc);
             if (nval >= KPL) {
-                load_run<KPL>(delta + rowoff + tl, dl, vec);
                 load_run<KPL>(gyin + rowoff + tl, gyv, vec);
                 if (!SUMMARY) load_run<KPL>(xin + rowoff + tl, xv, vec);
             } else {
-                load_run_masked<T, KPL>(delta + rowoff + tl, dl, nval);
                 load_run_masked<T, KPL>(gyin + rowoff + tl, gyv, nval);
                 if (!SUMMARY) load_run_masked<T, KPL>(xin + rowoff + tl, xv, nval);
             }
@@ -504,13 +526,18 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
                 for (int j = 0; j < KPL; ++j) v[j] = dl[j] * Sb[j];
                 store_run<KPL>((T*)p.gx + rowoff + tl, v, vec, nval);
             }
-            if (p.gdelta) {
+            if (p.gdelta || p.partBias) {
+                // gradient w.r.t. delta as given (the projection output when the
+                // step sizes are transformed): d delta/d z times d Loss/d delta
                 float xv[KPL], v[KPL];
                 if (nval >= KPL) load_run<KPL>(xin + rowoff + tl, xv, vec);
                 else load_run_masked<T, KPL>(xin + rowoff + tl, xv, nval);
 #pragma unroll
-                for (int j = 0; j < KPL; ++j) v[j] = fmaf(xv[j], Sb[j], Gd[j]);
-                store_run<KPL>((T*)p.gdelta + rowoff + tl, v, vec, nval);
+                for (int j = 0; j < KPL; ++j)
+                    v[j] = fmaf(xv[j], Sb[j], Gd[j]) * step_xform_grad(dl[j], p.stepf.softplus);
+                if (p.gdelta) store_run<KPL>((T*)p.gdelta + rowoff + tl, v, vec, nval);
+#pragma unroll
+                for (int j = 0; j < KPL; ++j) gbias += j < nval ? v[j] : 0.0f;
             }
         }
     }
@@ -520,6 +547,10 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
             p.segR[(seq * p.G + g) * N + lane] = nu;
         }
         return;
+    }
+    if (p.partBias) {   // uniform; every lane of the row takes part in the sum
+        gbias = row_sum(gbias);
+        if (act && lane == 0) p.partBias[((size_t)b * p.G + g) * p.D + dc] = gbias;
     }
     if (act && lane < N) {
         if (p.gh0 && g == 0) p.gh0[seq * N + lane] = nu;
@@ -625,15 +656,15 @@ __global__ void reduce_parts_dn_kernel(const float* __restrict__ part, int B, in
 // suffix sums.  Every tile is independent, so the grid spans all tiles.
 // ---------------------------------------------------------------------------
 template <typename T, int KPL>
-__global__ void tile_dsum_kernel(const T* __restrict__ delta, float* __restrict__ out, int B, int D, int L,
-                                 int ntiles) {
+__global__ void tile_dsum_kernel(const T* __restrict__ delta, StepXform stepf, float* __restrict__ out, int B,
+                                 int D, int L, int ntiles) {
     const int lane = threadIdx.x & 15, row = threadIdx.x >> 4;
     const int d = blockIdx.x * 16 + row, b = blockIdx.y, tile = blockIdx.z;
     const bool act = d < D;
     const int dc = act ? d : D - 1;
     const int tl = tile * 16 * KPL + lane * KPL;
     float v[KPL];
-    load_run_masked<T, KPL>(delta + ((size_t)b * D + dc) * L + tl, v, L - tl);
+    load_steps<T, KPL>(delta + ((size_t)b * D + dc) * L + tl, v, L - tl, false, stepf, dc);
     float s = 0.0f;
 #pragma unroll
     for (int j = 0; j < KPL; ++j) s += v[j];
@@ -647,16 +678,21 @@ __global__ void tile_dsum_kernel(const T* __restrict__ delta, float* __restrict_
 // taken in blocks of 256 from the end, suffix-scanned in LDS, and each
 // block's total is carried to the next.
 template <typename T>
-__global__ __launch_bounds__(256) void sens_suffix_kernel(const T* __restrict__ delta,
+__global__ __launch_bounds__(256) void sens_suffix_kernel(const T* __restrict__ delta, StepXform stepf,
                                                           const float* __restrict__ tile_dsum,
-                                                          double* __restrict__ send, int BD, int L, int ntiles,
+                                                          double* __restrict__ send, int D, int L, int ntiles,
                                                           int tile_len, int t_out) {
     __shared__ double sc[257];
     const int s = blockIdx.x, tid = threadIdx.x;
     const int tout_tile = t_out / tile_len;
     // partial sum of t_out's own tile (fixed-order tree reduction)
     double part = 0.0;
-    for (int t = tout_tile * tile_len + tid; t <= t_out; t += 256) part += (double)to_f32(delta[(size_t)s * L + t]);
+    const float bias = stepf.bias ? stepf.bias[s % D] : 0.0f;
+    const bool xf = stepf.bias != nullptr || stepf.softplus;
+    for (int t = tout_tile * tile_len + tid; t <= t_out; t += 256) {
+        const float z = to_f32(delta[(size_t)s * L + t]);
+        part += (double)(xf ? step_xform(z, bias, stepf.softplus) : z);
+    }
     sc[tid] = part;
     __syncthreads();
     for (int w = 128; w >= 1; w >>= 1) {
@@ -764,7 +800,7 @@ __global__ __launch_bounds__(256) void sens_kernel(SensParams p) {
         const bool more = tile + 1 < tile1 && (tile + 1) * TILE <= p.t_out;
         if (more) fetchB(tile + 1, nb);   // in flight while this tile runs
         float dl[KPL];
-        load_run_masked<T, KPL>((const T*)p.delta + seq * L + tl, dl, min(L, p.t_out + 1) - tl);
+        load_steps<T, KPL>((const T*)p.delta + seq * L + tl, dl, min(L, p.t_out + 1) - tl, false, p.stepf, dc);
         // S_j = sum of delta over steps after j up to t_out
         float lsum = 0.0f;
 #pragma unroll
@@ -826,7 +862,10 @@ __global__ __launch_bounds__(256) void sens_kernel(SensParams p) {
             }
             if (WD) {
 #pragma unroll
-                for (int j = 0; j < KPL; ++j) v[j] = (tl + j <= p.t_out) ? fmaf(xv[j], acc[j], gd[j]) : 0.0f;
+                for (int j = 0; j < KPL; ++j)
+                    v[j] = (tl + j <= p.t_out)
+                               ? fmaf(xv[j], acc[j], gd[j]) * step_xform_grad(dl[j], p.stepf.softplus)
+                               : 0.0f;
                 store_run<KPL>((T*)p.s_delta + seq * L + tl, v, vec, L - tl);
             }
         }
@@ -903,25 +942,27 @@ hipError_t launch_reduce_parts_dn(const float* part, int B, int G, int D, int N,
     reduce_parts_dn_kernel<<<(D * N + 255) / 256, 256, 0, st>>>(part, B, G, D, N, out);
     return hipGetLastError();
 }
-hipError_t launch_tile_dsum(const void* delta, float* tile_dsum, int B, int D, int L, int ntiles, int kpl,
-                            int dtype, hipStream_t st) {
+hipError_t launch_tile_dsum(const void* delta, StepXform stepf, float* tile_dsum, int B, int D, int L, int ntiles,
+                            int kpl, int dtype, hipStream_t st) {
     dim3 grid((D + 15) / 16, B, ntiles);
     if (dtype == 0) {
-        SSM_DISPATCH_KPL(kpl, tile_dsum_kernel<float, K_><<<grid, 256, 0, st>>>((const float*)delta, tile_dsum, B, D, L, ntiles))
+        SSM_DISPATCH_KPL(kpl, tile_dsum_kernel<float, K_><<<grid, 256, 0, st>>>((const float*)delta, stepf, tile_dsum,
+                                                                                  B, D, L, ntiles))
     } else {
-        SSM_DISPATCH_KPL(kpl, tile_dsum_kernel<bf16_t, K_><<<grid, 256, 0, st>>>((const bf16_t*)delta, tile_dsum, B, D, L, ntiles))
+        SSM_DISPATCH_KPL(kpl, tile_dsum_kernel<bf16_t, K_><<<grid, 256, 0, st>>>((const bf16_t*)delta, stepf,
+                                                                                   tile_dsum, B, D, L, ntiles))
     }
     return hipGetLastError();
 }
-hipError_t launch_sens_suffix(const void* delta, const float* tile_dsum, double* send, int B, int D, int L,
-                              int ntiles, int tile_len, int t_out, int dtype, hipStream_t st) {
+hipError_t launch_sens_suffix(const void* delta, StepXform stepf, const float* tile_dsum, double* send, int B, int D,
+                              int L, int ntiles, int tile_len, int t_out, int dtype, hipStream_t st) {
     const int BD = B * D;
     if (dtype == 0)
-        sens_suffix_kernel<float><<<BD, 256, 0, st>>>((const float*)delta, tile_dsum, send, BD, L,
-                                                                    ntiles, tile_len, t_out);
+        sens_suffix_kernel<float><<<BD, 256, 0, st>>>((const float*)delta, stepf, tile_dsum, send, D, L, ntiles,
+                                                      tile_len, t_out);
     else
-        sens_suffix_kernel<bf16_t><<<BD, 256, 0, st>>>((const bf16_t*)delta, tile_dsum, send, BD,
-                                                                     L, ntiles, tile_len, t_out);
+        sens_suffix_kernel<bf16_t><<<BD, 256, 0, st>>>((const bf16_t*)delta, stepf, tile_dsum, send, D, L, ntiles,
+                                                       tile_len, t_out);
     return hipGetLastError();
 }
 hipError_t launch_sens(const SensParams& p, int dtype, int kpl, hipStream_t st) {

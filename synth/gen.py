@@ -84,13 +84,16 @@ def _stream(a, dtype):
 # ----------------------------------------------------------------------------
 # workloads
 # ----------------------------------------------------------------------------
-def make_real(B=1, D=16, N=16, L=1024, dtype="f32", seed=0, with_grad=True):
+def make_real(B=1, D=16, N=16, L=1024, dtype="f32", seed=0, with_grad=True, projection_output=False):
     """Diagonal real selective-scan inputs.
 
     Draw order: x, z (delta = softplus(z)), U (A = -exp(U)), Bm, C, gy.
     Shapes: x, delta, gy (B,D,L); A (D,N); Bm, C (B,L,N).  h0 = 0.
     ``dtype`` 'bf16' rounds the streamed tensors (x, delta, Bm, C, gy) to
     bfloat16; A always stays float32.
+    ``projection_output``: ``delta`` holds the pre-activation z - bias instead
+    (so softplus(delta + bias) is the same step-size distribution) and
+    ``delta_bias`` a per-channel bias ~ N(0, 1/4), drawn last.
     """
     g = np.random.Generator(np.random.PCG64(seed))
     x = g.standard_normal((B, D, L))
@@ -108,6 +111,10 @@ def make_real(B=1, D=16, N=16, L=1024, dtype="f32", seed=0, with_grad=True):
     )
     if with_grad:
         out["gy"] = _stream(g.standard_normal((B, D, L)), dtype)
+    if projection_output:
+        bias = g.standard_normal(D) * 0.5
+        out["delta_bias"] = _f32(bias)
+        out["delta"] = _stream(z - _f32(bias).astype(np.float64)[None, :, None], dtype)
     return out
 
 

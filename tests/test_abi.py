@@ -43,8 +43,9 @@ def test_header_constants_match_binding():
 
 def test_struct_layouts():
     # 2 x int32 + 5 x int64 + 14 pointers
-    assert ctypes.sizeof(B.ScanArgs) == 8 + 5 * 8 + 14 * 8
-    assert ctypes.sizeof(B.ScanGrads) == 14 * 8
+    # + delta_bias pointer + delta_softplus int32 (padded to 8)
+    assert ctypes.sizeof(B.ScanArgs) == 8 + 5 * 8 + 15 * 8 + 8
+    assert ctypes.sizeof(B.ScanGrads) == 15 * 8
     assert ctypes.sizeof(B.PDArgs) == 6 * 8 + 7 * 8
     assert ctypes.sizeof(B.PDBwdIn) == 4 * 8 + 8   # 4 pointers + float tau (padded)
     assert ctypes.sizeof(B.PDGrads) == 5 * 8
@@ -89,6 +90,8 @@ def test_workspace_query_valid():
     (dict(mode=9), "SSM_ERR_UNSUPPORTED"),
     (dict(chunk_len=100), "SSM_ERR_UNSUPPORTED"),
     (dict(x=FAKE * 2 + 2), "SSM_ERR_LAYOUT"),
+    (dict(delta_softplus=2), "SSM_ERR_SHAPE"),
+    (dict(delta_bias=FAKE * 6 + 2), "SSM_ERR_LAYOUT"),
 ])
 def test_validation_errors(over, code):
     rc, _ = ws_bytes(B.SSM_OP_SCAN_FWD, sel_args(**over))
@@ -231,3 +234,12 @@ def test_output_sensitivity_host_checks():
     assert rc == status("SSM_ERR_WORKSPACE")
     rc, _ = ws_bytes(B.SSM_OP_OUTPUT_SENS, cplx_args())
     assert rc == status("SSM_ERR_UNSUPPORTED")
+
+
+def test_step_size_transform_selective_only():
+    rc, _ = ws_bytes(B.SSM_OP_SCAN_FWD, cplx_args(delta_softplus=1))
+    assert rc == status("SSM_ERR_UNSUPPORTED")
+    rc, _ = ws_bytes(B.SSM_OP_SCAN_FWD, sel_args(mode=B.SSM_REAL_DENSE, a=FAKE * 6, b=FAKE * 7, delta_bias=FAKE * 8))
+    assert rc == status("SSM_ERR_UNSUPPORTED")
+    rc, n = ws_bytes(B.SSM_OP_SCAN_BWD, sel_args(delta_bias=FAKE * 8, delta_softplus=1))
+    assert rc == 0 and n > 0

@@ -184,3 +184,66 @@ def test_output_sensitivity_impulse_config():
     sx, sd = oracle.output_sens(**kw)
     assert_close("s_delta", out["s_delta"], sd, **F32)
     assert_close("s_x", out["s_x"], sx, **F32)
+
+
+@pytest.mark.parametrize("dt,softplus,with_bias,L,chunk_len", [
+    ("f32", True, True, 1000, 256),
+    ("f32", True, False, 777, 128),
+    ("f32", False, True, 300, 64),
+    ("bf16", True, True, 1100, 256),
+])
+def test_step_sizes_from_projection(dt, softplus, with_bias, L, chunk_len):
+    """delta = softplus(z + bias) merged into the scan: y, every gradient (w.r.t. z) and gdelta_bias."""
+    ssm = _ssm()
+    cfg = synth.make_real(B=2, D=24, N=16, L=L, dtype=dt, seed=70 + L, projection_output=True)
+    if not softplus:   # step sizes must stay positive: feed softplus(z) - bias as the projection output
+        pos = synth.make_real(B=2, D=24, N=16, L=L, dtype="f32", seed=70 + L)["delta"].astype(np.float64)
+        assert dt == "f32"
+        cfg["delta"] = (pos - (cfg["delta_bias"][None, :, None] if with_bias else 0.0)).astype(np.float32)
+    t = {k: _dev(cfg[k], dt) for k in ("delta", "x", "Bm", "C")}
+    t["A"] = _dev(cfg["A"], "f32")
+    bias = cfg["delta_bias"] if with_bias else None
+    if with_bias:
+        t["delta_bias"] = _dev(bias, "f32")
+    t["delta_softplus"] = softplus
+    gy = _dev(cfg["gy"], dt)
+    want = ("gdelta", "gx", "gA", "gBm", "gC", "gh0", "gdelta_bias")
+    f = ssm.scan_fwd(ssm.SSM_REAL_SELECTIVE, want_h_last=True, want_ckpt=True, chunk_len=chunk_len, **t)
+    g = ssm.scan_bwd(ssm.SSM_REAL_SELECTIVE, gy=gy, ckpt=f["ckpt"], want=want, chunk_len=chunk_len, **t)
+    g2 = ssm.scan_bwd(ssm.SSM_REAL_SELECTIVE, gy=gy, want=want, chunk_len=chunk_len, **t)
+    torch.cuda.synchronize()
+    delta = oracle.step_sizes(cfg["delta"], bias, softplus)
+    kw = dict(delta=delta, x=cfg["x"], A=cfg["A"], Bm=cfg["Bm"], C=cfg["C"], B=2, D=24, L=L, N=16)
+    y, hl = oracle.real_fwd(**kw)
+    og = oracle.real_bwd(**kw, gy=cfg["gy"])
+    gz, gb = oracle.step_size_grads(og["gdelta"], cfg["delta"], bias, softplus)
+    tol = BF16 if dt == "bf16" else F32
+    assert_close("y", f["y"], y, **tol)
+    assert_close("h_last", f["h_last"], hl, **tol)
+    assert_close("gdelta (w.r.t. z)", g["gdelta"], gz, **tol)
+    assert_close("gdelta_bias", g["gdelta_bias"], gb, **tol)
+    for k in ("gx", "gBm", "gC", "gh0"):
+        assert_close(k, g[k], og[k], **tol)
+    for k in want:
+        assert torch.equal(g[k], g2[k]), k
+
+
+def test_step_sizes_from_projection_sensitivities():
+    """The impulse and output-sensitivity paths with the transformed step sizes."""
+    ssm = _ssm()
+    L = 2300
+    cfg = synth.make_real(B=1, D=20, N=16, L=L, seed=77, projection_output=True)
+    t = {k: _dev(cfg[k], "f32") for k in ("delta", "x", "Bm", "C", "A", "delta_bias")}
+    t["delta_softplus"] = True
+    out = ssm.output_sensitivity(t_out=1500, want_y=True, **t)
+    imp = ssm.impulse_sensitivity(t_out=1500, want_y=False, **t)
+    torch.cuda.synchronize()
+    delta = oracle.step_sizes(cfg["delta"], cfg["delta_bias"], True)
+    kw = dict(delta=delta, x=cfg["x"], A=cfg["A"], Bm=cfg["Bm"], C=cfg["C"], B=1, D=20, L=L, N=16)
+    sx, sd = oracle.output_sens(**kw, t_out=1500)
+    sz, _ = oracle.step_size_grads(sd, cfg["delta"], cfg["delta_bias"], True)
+    y, _ = oracle.real_fwd(**kw)
+    assert_close("s_x", out["s_x"], sx, **F32)
+    assert_close("s_z", out["s_delta"], sz, **F32)
+    assert_close("y", out["y"], y, **F32)
+    assert_close("impulse s", imp["s"], sx, **F32)
