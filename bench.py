@@ -57,8 +57,8 @@ FLOPS_PER_ELEMENT = {"selective forward": 7, "selective backward": 17}
 # kernel sources they were measured on and reported only while those are
 # unchanged (profiles/selective_mamba_layer_fwd_bwd.md holds the run).
 MEASURED_TRAFFIC = {
-    "selective backward": {"read_bytes": 514.8e6, "written_bytes": 542.8e6,
-                           "sources_sha256": "898a3c03def789af69b6324e6b37ec5aea50e03b593a45da6700075dcbc12aa2"},
+    "selective backward": {"read_bytes": 509.1e6, "written_bytes": 542.2e6,
+                           "sources_sha256": "a621b3e94a13ea1e79567cfa0978a8cff3896c2250a093cb6daf05174e0e62e0"},
 }
 TRAFFIC_SOURCES = ("real_selective.hip", "common.hpp", "kernels.hpp")
 
@@ -159,7 +159,7 @@ def w_real(name, B, D, N, L, dtype, steps, warmup, keep_inputs=False):
     return dict(name=name, elements=B * D * N * L, ms=ms, kernels=profile_kernels(step),
                 bytes_total=fwd + bwd, bytes_kernel={"selective forward": fwd, "selective backward": bwd_k},
                 config=dict(B=B, D=D, N=N, L=L, streams=dtype, chunk_len=256),
-                inputs=cfg if keep_inputs else None)
+                inputs=cfg if keep_inputs else None, step=step)
 
 
 def w_impulse(steps, warmup):
@@ -350,6 +350,85 @@ def cpu_baseline(inputs, batches):
                       f"forward + backward in fp64, {dt:.1f} s wall"}
 
 
+def cpu_per_core(seconds=3.0):
+    """The oracle on one thread, forward + backward of the small fp32 selective case (B=1 D=16 N=16 L=1024),
+    repeated for about `seconds`: the per-core rate."""
+    import oracle
+    import synth
+    cfg = synth.make_real(B=1, D=16, N=16, L=1024, seed=0)
+    kw = dict(delta=cfg["delta"], x=cfg["x"], A=cfg["A"], Bm=cfg["Bm"], C=cfg["C"], B=1, D=16, L=1024, N=16)
+    prev = oracle.threads()
+    oracle.set_threads(1)
+    try:
+        n, t0 = 0, time.perf_counter()
+        while True:
+            oracle.real_fwd(**kw)
+            oracle.real_bwd(**kw, gy=cfg["gy"])
+            n += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+        dt = time.perf_counter() - t0
+    finally:
+        oracle.set_threads(prev)
+    return n * 16 * 1024 * 16 / dt
+
+
+def step_stats(step, n, flush):
+    """Per-step times (ms) from HIP events on the current stream: p10, median, p90.  With `flush`, a 1 GiB
+    buffer is written before every step (outside the events) so the 256 MB Infinity Cache holds none of the
+    step's inputs."""
+    import torch
+    buf = torch.empty(1 << 28, dtype=torch.float32, device="cuda") if flush else None
+    ts = []
+    for i in range(n):
+        if flush:
+            buf.fill_(float(i))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        step()
+        e1.record()
+        e1.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    del buf
+    q = np.percentile(np.array(ts), [10, 50, 90])
+    return {"p10": round(float(q[0]), 4), "median": round(float(q[1]), 4), "p90": round(float(q[2]), 4), "n": n}
+
+
+def copy_ceiling():
+    """Device-to-device copy of 1 GiB, best of 5: GB/s counting read + write bytes."""
+    import torch
+    src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    best = float("inf")
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        e1.synchronize()
+        best = min(best, e0.elapsed_time(e1))
+    del src, dst
+    return 2 * (1 << 30) / (best * 1e-3) / 1e9
+
+
+def device_info():
+    import glob
+    import torch
+    pr = torch.cuda.get_device_properties(0)
+    info = {"name": pr.name, "arch": getattr(pr, "gcnArchName", None), "compute_units": pr.multi_processor_count,
+            "hip": torch.version.hip, "torch": torch.__version__}
+    for f in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            lines = open(f).read().split("\n")
+        except OSError:
+            continue
+        cur = [l for l in lines if l.strip().endswith("*")]
+        info["sclk"] = (cur[0] if cur else lines[0]).strip()
+        info["sclk_max"] = [l for l in lines if l.strip()][-1].strip()
+        break
+    return info
+
+
 def calib_copy():
     """One device copy of exactly 1 GiB (reads 1 GiB, writes 1 GiB)."""
     import torch
@@ -411,9 +490,16 @@ def main():
             elif w == "real-small":
                 others[w] = summarize(w_real(w, 1, 16, 16, 1024, "f32", args.steps, args.warmup))
             torch.cuda.empty_cache()
+    timing = {"back_to_back_ms": step_stats(head["step"], 20, False),
+              "cache_flushed_ms": step_stats(head["step"], 20, True),
+              "note": "per-step HIP-event times of the headline step; cache_flushed writes 1 GiB before each step"}
+    hbm_copy = copy_ceiling()
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(head["inputs"], args.cpu_batches)
+        cpu["per_core_value"] = cpu_per_core()
+        cpu["per_core_sample"] = ("one thread, forward + backward of B=1 D=16 N=16 L=1024 fp32 "
+                                  "(the small selective case), repeated for 3 s")
     line = {
         "metric": METRIC, "value": s["el_per_s"], "unit": "elements/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": s["ms_per_step"], "higher_is_better": True, "scaling": "weak",
@@ -422,6 +508,7 @@ def main():
                                "fp32 state, chunk 256", **head["config"]},
         "hbm_frac": s["hbm_frac"], "algorithmic_bytes_per_step": head["bytes_total"],
         "kernels_ms": s["kernels_ms"], "roofline": roof, "cpu_baseline": cpu, "others": others,
+        "timing": timing, "hbm_copy_GBps": round(hbm_copy, 1), "device": device_info(),
     }
     print(json.dumps(line))
 

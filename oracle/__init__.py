@@ -68,12 +68,18 @@ def _load():
         lib.orc_pd_ste.argtypes = [_L, _L, _L, _L, _L, _D, _I, _I] + [_D] * 6 + [ctypes.c_double, _D, _D]
         lib.orc_pd_mix_fwd.argtypes = [_L, _L, _L, _L, _L, _D, _I] + [_D] * 6
         lib.orc_threads.restype = ctypes.c_int
+        lib.orc_set_threads.argtypes = [ctypes.c_int]
         _lib = lib
     return _lib
 
 
 def threads() -> int:
     return int(_load().orc_threads())
+
+
+def set_threads(n: int) -> None:
+    """Thread count of later calls (n >= 1)."""
+    _load().orc_set_threads(int(n))
 
 
 def _w(a):

@@ -62,6 +62,14 @@ static int thread_id(void) {
 }
 
 int orc_threads(void) { return nthreads(); }
+/* Thread count of the following calls (timing of a single core); n < 1 leaves it unchanged. */
+void orc_set_threads(int n) {
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
 
 /* ------------------------------------------------------------------------- */
 /* Diagonal real scan.                                                        */
