@@ -178,33 +178,37 @@ typedef struct {
 } ssm_scan_grads;
 
 /* Arguments of the PD scan.  N = state (1..16), K = dictionary size (1..64).
- * chunk_len: 0 = default 64; only 64 is accepted. */
+ * chunk_len: 0 = default 64; only 64 is accepted.  dtype: element type of the
+ * streams (logits, d, b, C, and gy, ste_logits, y, gd, gb, gC, glogits of the
+ * calls below), SSM_F32 or SSM_BF16; h0, h_last, gh_last, gh0 and checkpoints
+ * are always f32, and the recurrence runs in fp32 either way. */
 typedef struct {
     int64_t batch, heads, length, state, dict_size, chunk_len;
-    const float*   logits; /* (B,H,L,K) f32 selection scores; may be NULL if sel is given */
+    const void*    logits; /* (B,H,L,K) dtype selection scores; may be NULL if sel is given */
     const int32_t* sel;    /* (B,H,L) selected entries; input alternative to logits (used
                               when logits is NULL); values must lie in [0,K)               */
     const int32_t* dict;   /* (H,K,N): dict[h,k,j] = row of the one in column j of entry k,
                               values in [0,N)                                              */
-    const float* d;        /* (B,H,L,N) diagonal d_t                                        */
-    const float* b;        /* (B,H,L,N) input term b_t                                      */
-    const float* C;        /* (B,H,L,N) readout C_t                                         */
-    const float* h0;       /* nullable (B,H,N)                                              */
+    const void*  d;        /* (B,H,L,N) dtype diagonal d_t                                  */
+    const void*  b;        /* (B,H,L,N) dtype input term b_t                                */
+    const void*  C;        /* (B,H,L,N) dtype readout C_t                                   */
+    const float* h0;       /* nullable (B,H,N) f32                                          */
+    int32_t dtype;         /* SSM_F32 or SSM_BF16                                           */
 } pd_scan_args;
 
 typedef struct {
-    float*   y;       /* nullable (B,H,L)                                               */
+    void*    y;       /* nullable (B,H,L) dtype                                         */
     int32_t* sel;     /* nullable (B,H,L): argmax_k logits (lowest index among ties)    */
     float*   h_last;  /* nullable (B,H,N)                                               */
     float*   ckpt;    /* nullable (B,H,n_chunks,N): state entering each chunk           */
 } pd_scan_fwd_out;
 
 typedef struct {
-    const float* gy;       /* (B,H,L)                                                   */
+    const void*  gy;       /* (B,H,L) dtype                                             */
     const float* gh_last;  /* nullable (B,H,N)                                          */
     const float* ckpt;     /* nullable checkpoints from pd_scan_fwd; NULL = recomputed  */
-    const float* ste_logits; /* (B,H,L,K) selection scores for glogits; required when
-                                glogits is wanted, ignored otherwise                     */
+    const void*  ste_logits; /* (B,H,L,K) dtype selection scores for glogits; required
+                                when glogits is wanted, ignored otherwise                */
     float tau;             /* softmax temperature of glogits (> 0, finite)              */
 } pd_scan_bwd_in;
 
@@ -218,11 +222,12 @@ typedef struct {
  *   glogits[t,k] = (1/tau) s_k (gw[t,k] - sum_i s_i gw[t,i]),
  *   s = softmax(ste_logits[t,:] / tau). */
 typedef struct {
-    float* gd;       /* (B,H,L,N) */
-    float* gb;       /* (B,H,L,N) */
-    float* gC;       /* (B,H,L,N) */
-    float* gh0;      /* (B,H,N)   */
-    float* glogits;  /* (B,H,L,K) surrogate gradient of the scores; NULL = not wanted */
+    void*  gd;       /* (B,H,L,N) dtype */
+    void*  gb;       /* (B,H,L,N) dtype */
+    void*  gC;       /* (B,H,L,N) dtype */
+    float* gh0;      /* (B,H,N) f32     */
+    void*  glogits;  /* (B,H,L,K) dtype surrogate gradient of the scores; NULL = not wanted
+                        (with bf16 streams: K <= 16)                                    */
 } pd_scan_grads;
 
 /* Workspace size in bytes for operation `op` (SSM_OP_*) with `args`

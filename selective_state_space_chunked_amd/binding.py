@@ -50,7 +50,7 @@ class ScanGrads(ctypes.Structure):
 class PDArgs(ctypes.Structure):
     _fields_ = [("batch", _i64), ("heads", _i64), ("length", _i64), ("state", _i64), ("dict_size", _i64),
                 ("chunk_len", _i64), ("logits", _vp), ("sel", _vp), ("dict", _vp), ("d", _vp), ("b", _vp),
-                ("C", _vp), ("h0", _vp)]
+                ("C", _vp), ("h0", _vp), ("dtype", ctypes.c_int32)]
 
 
 class PDFwdOut(ctypes.Structure):
@@ -313,21 +313,25 @@ def complex_rtrl(*, gy, gh_last=None, want_y=True, chunk_len=0, out=None, **tens
 # PD scan
 # ---------------------------------------------------------------------------
 def _pd_args(*, logits=None, sel=None, dict, d, b, C, h0=None, chunk_len=0):
-    _need(d, "d", torch.float32)
+    """Streams (logits, d, b, C) are all float32 or all bfloat16 (the dtype of d)."""
+    _need(d, "d")
+    st = d.dtype
+    if st not in (torch.float32, torch.bfloat16):
+        raise TypeError("d must be float32 or bfloat16")
     Bsz, H, L, N = d.shape
     dev = d.device
     K = dict.shape[1]
     _need(dict, "dict", torch.int32, (H, K, N), dev)
-    _need(logits, "logits", torch.float32, (Bsz, H, L, K), dev)
+    _need(logits, "logits", st, (Bsz, H, L, K), dev)
     _need(sel, "sel", torch.int32, (Bsz, H, L), dev)
     if logits is None and sel is None:
         raise ValueError("logits or sel is required")
     for nm, t in (("b", b), ("C", C)):
-        _need(t, nm, torch.float32, (Bsz, H, L, N), dev)
+        _need(t, nm, st, (Bsz, H, L, N), dev)
     _need(h0, "h0", torch.float32, (Bsz, H, N), dev)
     args = PDArgs(batch=Bsz, heads=H, length=L, state=N, dict_size=K, chunk_len=chunk_len,
                   logits=_ptr(logits), sel=_ptr(sel), dict=_ptr(dict), d=_ptr(d), b=_ptr(b), C=_ptr(C),
-                  h0=_ptr(h0))
+                  h0=_ptr(h0), dtype=SSM_BF16 if st == torch.bfloat16 else SSM_F32)
     return args, (Bsz, H, L, N, K), dev
 
 
@@ -337,7 +341,7 @@ def pd_scan_fwd(*, want_y=True, want_sel=True, want_h_last=False, want_ckpt=Fals
     nc = n_chunks(L, chunk_len or 64)
     out = dict(out or {})
     if want_y and "y" not in out:
-        out["y"] = torch.empty((Bsz, H, L), dtype=torch.float32, device=dev)
+        out["y"] = torch.empty((Bsz, H, L), dtype=tensors["d"].dtype, device=dev)
     if want_sel and "sel" not in out:
         out["sel"] = torch.empty((Bsz, H, L), dtype=torch.int32, device=dev)
     if want_h_last and "h_last" not in out:
@@ -357,11 +361,12 @@ def pd_scan_bwd(*, gy, gh_last=None, ckpt=None, want=("gd", "gb", "gC", "gh0"), 
     "glogits", the straight-through surrogate gradient of ``ste_logits``
     (B, H, L, K) through softmax(ste_logits / tau)."""
     args, (Bsz, H, L, N, K), dev = _pd_args(chunk_len=chunk_len, **tensors)
-    _need(gy, "gy", torch.float32, (Bsz, H, L), dev)
+    st = tensors["d"].dtype
+    _need(gy, "gy", st, (Bsz, H, L), dev)
     _need(gh_last, "gh_last", torch.float32, (Bsz, H, N), dev)
     nc = n_chunks(L, chunk_len or 64)
     _need(ckpt, "ckpt", torch.float32, (Bsz, H, nc, N), dev)
-    _need(ste_logits, "ste_logits", torch.float32, (Bsz, H, L, K), dev)
+    _need(ste_logits, "ste_logits", st, (Bsz, H, L, K), dev)
     out = dict(out or {})
     shapes = {"gd": (Bsz, H, L, N), "gb": (Bsz, H, L, N), "gC": (Bsz, H, L, N), "gh0": (Bsz, H, N),
               "glogits": (Bsz, H, L, K)}
@@ -369,7 +374,7 @@ def pd_scan_bwd(*, gy, gh_last=None, ckpt=None, want=("gd", "gb", "gC", "gh0"), 
         if k not in shapes:
             raise ValueError(f"unknown PD gradient {k}")
         if k not in out:
-            out[k] = torch.empty(shapes[k], dtype=torch.float32, device=dev)
+            out[k] = torch.empty(shapes[k], dtype=torch.float32 if k == "gh0" else st, device=dev)
     g = PDGrads(**{f[0]: _ptr(out.get(f[0])) for f in PDGrads._fields_})
     i = PDBwdIn(gy=_ptr(gy), gh_last=_ptr(gh_last), ckpt=_ptr(ckpt), ste_logits=_ptr(ste_logits), tau=float(tau))
     ws, nws = _workspace(SSM_OP_PD_BWD, ctypes.byref(args), dev)

@@ -118,9 +118,11 @@ hipError_t launch_cplx_rtrl_reduce(const RtrlParams& p, hipStream_t st);
 
 // ------------------------------- PD ----------------------------------------
 struct PDParams {
-    const float* logits; const int32_t* sel_in; const int32_t* dict;
-    const float* d; const float* b; const float* C; const float* h0;
-    const float* gy; const float* gh_last; const float* ckpt;
+    // streams (logits, d, b, C, gy, y, gd, gb, gC, ste_logits, glogits) are fp32
+    // or bf16 (dtype 0 / 1); states, checkpoints and summaries are fp32
+    const void* logits; const int32_t* sel_in; const int32_t* dict;
+    const void* d; const void* b; const void* C; const float* h0;
+    const void* gy; const float* gh_last; const float* ckpt;
     int32_t* sel_out;              // selection written by the summary pass
     const int32_t* sel;            // selection read by the later passes
     int8_t* pre;                   // (H,K,N,N) preimage lists, -1 padded
@@ -129,12 +131,13 @@ struct PDParams {
                                                 // state, or in the backward the adjoint R
     float* carry_in;               // (B,H,G,N)
     float* nu_in;                  // (B,H,G,N)
-    float* y; float* h_last; float* ckpt_out;
-    float* gd; float* gb; float* gC; float* gh0;
-    const float* ste_logits;       // selection scores for the surrogate gradient (B,H,L,K)
-    float* glogits;                // (B,H,L,K) surrogate gradient; NULL = not wanted
+    void* y; float* h_last; float* ckpt_out;
+    void* gd; void* gb; void* gC; float* gh0;
+    const void* ste_logits;        // selection scores for the surrogate gradient (B,H,L,K)
+    void* glogits;                 // (B,H,L,K) surrogate gradient; NULL = not wanted
     float inv_tau;                 // 1 / softmax temperature
     int B, H, L, N, K, chunk, G;   // G = number of chunks
+    int dtype;                     // 0 fp32, 1 bf16 streams
 };
 hipError_t launch_pd_prep(const PDParams& p, hipStream_t st);
 hipError_t launch_pd_fwd(const PDParams& p, bool summary, hipStream_t st);

@@ -126,11 +126,12 @@ __device__ __forceinline__ void pd_with_rounds(int maxc, F&& body) {
     else body(std::integral_constant<int, 16>{});
 }
 
-__device__ __forceinline__ int pd_argmax(const float* __restrict__ lg, int K) {
+template <typename T>
+__device__ __forceinline__ int pd_argmax(const T* __restrict__ lg, int K) {
     int best = 0;
-    float bv = lg[0];
+    float bv = to_f32(lg[0]);
     for (int k = 1; k < K; ++k) {
-        const float v = lg[k];
+        const float v = to_f32(lg[k]);
         if (v > bv) { bv = v; best = k; }
     }
     return best;
@@ -147,17 +148,17 @@ __device__ __forceinline__ PDRow pd_row(const PDParams& p) {
     return r;
 }
 
-// 16 steps tb.. of state i of a (L, N) stream; steps past L read 0.
-template <int NT>
-__device__ __forceinline__ void pd_load16(const float* __restrict__ base, int tb, int L, int N, int i,
+// 16 steps tb.. of state i of a (L, N) stream (fp32 or bf16); steps past L read 0.
+template <typename T, int NT>
+__device__ __forceinline__ void pd_load16(const T* __restrict__ base, int tb, int L, int N, int i,
                                           float (&v)[16]) {
-    const float* __restrict__ q = base + (size_t)tb * (NT ? NT : N) + i;
+    const T* __restrict__ q = base + (size_t)tb * (NT ? NT : N) + i;
     if (tb + 16 <= L) {
 #pragma unroll
-        for (int j = 0; j < 16; ++j) v[j] = q[j * (NT ? NT : N)];
+        for (int j = 0; j < 16; ++j) v[j] = to_f32(q[j * (NT ? NT : N)]);
     } else {
 #pragma unroll
-        for (int j = 0; j < 16; ++j) v[j] = tb + j < L ? q[j * (NT ? NT : N)] : 0.0f;
+        for (int j = 0; j < 16; ++j) v[j] = tb + j < L ? to_f32(q[j * (NT ? NT : N)]) : 0.0f;
     }
 }
 
@@ -166,7 +167,7 @@ __device__ __forceinline__ void pd_load16(const float* __restrict__ base, int tb
 // Each 16-step block first loads everything it needs (lane l takes the
 // selection of step l; d, b and C for all 16 steps), then runs the steps.
 // ---------------------------------------------------------------------------
-template <bool SUMMARY, int NT>
+template <typename T, bool SUMMARY, int NT>
 __global__ __launch_bounds__(256) void pd_fwd_kernel(PDParams p) {
     __shared__ PDShared tb_;
     const PDRow r = pd_row(p);
@@ -187,24 +188,24 @@ __global__ __launch_bounds__(256) void pd_fwd_kernel(PDParams p) {
             if (p.ckpt_out && nl) p.ckpt_out[((size_t)r.s * p.G + r.ch) * N + i] = h;
             if (!nl) h = 0.0f;
         }
-        const float* dbase = p.d + srow * N;
-        const float* bbase = p.b + srow * N;
-        const float* cbase = p.C + srow * N;
+        const T* dbase = (const T*)p.d + srow * N;
+        const T* bbase = (const T*)p.b + srow * N;
+        const T* cbase = (const T*)p.C + srow * N;
         const int t0 = r.ch * kPChunk;
         for (int blk = 0; blk < kPChunk / 16; ++blk) {
             const int tb = t0 + 16 * blk;
             const int tl = tb + r.lane;          // the step whose selection this lane loads
             int kl = 0;
             if (tl < L) {
-                if (SUMMARY) kl = p.logits ? pd_argmax(p.logits + (srow + tl) * K, K) : p.sel_in[srow + tl];
+                if (SUMMARY) kl = p.logits ? pd_argmax((const T*)p.logits + (srow + tl) * K, K) : p.sel_in[srow + tl];
                 else kl = p.sel[srow + tl];
                 kl = min(max(kl, 0), K - 1);   // given selections outside [0, K) are clamped
             }
             if (SUMMARY && p.sel_out && tl < L) p.sel_out[srow + tl] = kl;
             float dv[16], bv[16], cv[16];
-            pd_load16<NT>(dbase, tb, L, N, i, dv);
-            pd_load16<NT>(bbase, tb, L, N, i, bv);
-            if (!SUMMARY) pd_load16<NT>(cbase, tb, L, N, i, cv);
+            pd_load16<T, NT>(dbase, tb, L, N, i, dv);
+            pd_load16<T, NT>(bbase, tb, L, N, i, bv);
+            if (!SUMMARY) pd_load16<T, NT>(cbase, tb, L, N, i, cv);
             float yp[16];
     #pragma unroll
             for (int j = 0; j < 16; ++j) {
@@ -225,7 +226,7 @@ __global__ __launch_bounds__(256) void pd_fwd_kernel(PDParams p) {
             }
             if (!SUMMARY && p.y) {
                 const float ys = row_transpose_sum16(yp);
-                if (tl < L) p.y[srow + tl] = ys;
+                if (tl < L) ((T*)p.y)[srow + tl] = from_f32<T>(ys);
             }
         }
         if (!nl) return;
@@ -263,13 +264,13 @@ __global__ __launch_bounds__(256) void pd_fwd_kernel(PDParams p) {
 // and d_t[j] h_{t-1}[j] of step tb + q on lane j.  KR = 16: K <= 16, the
 // lane's scores x (preloaded, -inf past K) and its gw stay in registers;
 // KR = 0: any K, gw goes through the output array.
-template <int KR>
+template <typename T, int KR>
 __device__ __forceinline__ void pd_ste_block(const PDParams& p, const PDShared& tb_, const float (&lam)[16],
                                              const float (&z)[16], const float (&x)[16], size_t srow, int tb,
                                              int N, int j) {
     const int K = p.K, L = p.L;
     const int t = tb + (lane_id() & 15);   // the step whose gw this lane receives
-    float* o = p.glogits + (srow + t) * K;
+    T* o = (T*)p.glogits + (srow + t) * K;
     const float sc = p.inv_tau * 1.4426950408889634f;  // exp(v / tau) = 2^(v log2(e) / tau)
     if (KR == 16) {
         float g[16];
@@ -299,7 +300,7 @@ __device__ __forceinline__ void pd_ste_block(const PDParams& p, const PDShared& 
         dot *= rz;
 #pragma unroll
         for (int k = 0; k < 16; ++k)
-            if (k < K) o[k] = e[k] * rz * (g[k] - dot) * p.inv_tau;
+            if (k < K) o[k] = from_f32<T>(e[k] * rz * (g[k] - dot) * p.inv_tau);
         return;
     }
     for (int k = 0; k < K; ++k) {          // uniform
@@ -308,27 +309,27 @@ __device__ __forceinline__ void pd_ste_block(const PDParams& p, const PDShared& 
 #pragma unroll
         for (int q = 0; q < 16; ++q) v[q] = row_pull(lam[q], pk) * z[q];
         const float g = row_transpose_sum16(v);
-        if (t < L) o[k] = g;               // gw, replaced by glogits below
+        if (t < L) o[k] = from_f32<T>(g);  // gw, replaced by glogits below (fp32 only, see the launcher)
     }
     if (t >= L) return;
-    const float* xs = p.ste_logits + (srow + t) * K;
-    float mx = xs[0];
-    for (int k = 1; k < K; ++k) mx = fmaxf(mx, xs[k]);
+    const T* xs = (const T*)p.ste_logits + (srow + t) * K;
+    float mx = to_f32(xs[0]);
+    for (int k = 1; k < K; ++k) mx = fmaxf(mx, to_f32(xs[k]));
     float zs = 0.0f, dot = 0.0f;
     for (int k = 0; k < K; ++k) {
-        const float e = exp2f((xs[k] - mx) * sc);
+        const float e = exp2f((to_f32(xs[k]) - mx) * sc);
         zs += e;
-        dot = fmaf(e, o[k], dot);
+        dot = fmaf(e, to_f32(o[k]), dot);
     }
     const float rz = 1.0f / zs;
     dot *= rz;
     for (int k = 0; k < K; ++k) {
-        const float e = exp2f((xs[k] - mx) * sc) * rz;
-        o[k] = e * (o[k] - dot) * p.inv_tau;
+        const float e = exp2f((to_f32(xs[k]) - mx) * sc) * rz;
+        o[k] = from_f32<T>(e * (to_f32(o[k]) - dot) * p.inv_tau);
     }
 }
 
-template <bool SUMMARY, int NT, int STE = -1>
+template <typename T, bool SUMMARY, int NT, int STE = -1>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(STE >= 0 ? 2 : 3))) void pd_bwd_kernel(PDParams p) {
     __shared__ PDShared tb_;
     const PDRow r = pd_row(p);
@@ -348,9 +349,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(STE >= 0 ? 
             if (p.G > 1) nu = p.nu_in[((size_t)r.s * p.G + r.ch) * N + j];
             else if (p.gh_last) nu = p.gh_last[(size_t)r.s * N + j];
         }
-        const float* dbase = p.d + srow * N;
-        const float* bbase = p.b + srow * N;
-        const float* cbase = p.C + srow * N;
+        const T* dbase = (const T*)p.d + srow * N;
+        const T* bbase = (const T*)p.b + srow * N;
+        const T* cbase = (const T*)p.C + srow * N;
         auto sel_of = [&](int tl) { return tl < L ? min(max(p.sel[srow + tl], 0), K - 1) : 0; };
         float hs[kPChunk + 1];
         if (!SUMMARY) {
@@ -360,8 +361,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(STE >= 0 ? 
                 const int tb = t0 + 16 * blk;
                 const int kl = sel_of(tb + r.lane);
                 float dv[16], bv[16];
-                pd_load16<NT>(dbase, tb, L, N, j, dv);
-                pd_load16<NT>(bbase, tb, L, N, j, bv);
+                pd_load16<T, NT>(dbase, tb, L, N, j, dv);
+                pd_load16<T, NT>(bbase, tb, L, N, j, bv);
     #pragma unroll
                 for (int q = 0; q < 16; ++q) {
                     const int k = __float_as_int(bcast16(__int_as_float(kl), q));
@@ -375,16 +376,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(STE >= 0 ? 
             const int tb = t0 + 16 * blk;
             const int tl = tb + r.lane;
             const int kl = sel_of(tl);
-            const float gyl = tl < L ? p.gy[srow + tl] : 0.0f;
+            const float gyl = tl < L ? to_f32(((const T*)p.gy)[srow + tl]) : 0.0f;
             float xl[16];  // STE == 16: this lane's scores of step tl
             if (STE == 16) {
-                const float* xs = p.ste_logits + (srow + tl) * p.K;
+                const T* xs = (const T*)p.ste_logits + (srow + tl) * p.K;
 #pragma unroll
-                for (int k = 0; k < 16; ++k) xl[k] = (k < p.K && tl < L) ? xs[k] : -INFINITY;
+                for (int k = 0; k < 16; ++k) xl[k] = (k < p.K && tl < L) ? to_f32(xs[k]) : -INFINITY;
             }
             float dv[16], cv[16];
-            pd_load16<NT>(dbase, tb, L, N, j, dv);
-            pd_load16<NT>(cbase, tb, L, N, j, cv);
+            pd_load16<T, NT>(dbase, tb, L, N, j, dv);
+            pd_load16<T, NT>(cbase, tb, L, N, j, cv);
             const size_t obase = (srow + tb) * N + j;   // step q at obase + q * N
     #pragma unroll
             for (int q = 15; q >= 0; --q) {
@@ -405,9 +406,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(STE >= 0 ? 
                 } else if (tv) {
                     if (nl) {
                         const size_t o = obase + (size_t)q * N;
-                        if (p.gb) p.gb[o] = lam;
-                        if (p.gC) p.gC[o] = gyt * hs[16 * blk + q + 1];
-                        if (p.gd) p.gd[o] = lp * hs[16 * blk + q];
+                        if (p.gb) ((T*)p.gb)[o] = from_f32<T>(lam);
+                        if (p.gC) ((T*)p.gC)[o] = from_f32<T>(gyt * hs[16 * blk + q + 1]);
+                        if (p.gd) ((T*)p.gd)[o] = from_f32<T>(lp * hs[16 * blk + q]);
                     }
                     nu = dv[q] * lp;
                 }
@@ -416,7 +417,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(STE >= 0 ? 
                     dv[q] = (tv && nl) ? dv[q] * hs[16 * blk + q] : 0.0f;
                 }
             }
-            if (STE >= 0) pd_ste_block<STE == 16 ? 16 : 0>(p, tb_, cv, dv, xl, srow, tb, N, j);
+            if (STE >= 0) pd_ste_block<T, STE == 16 ? 16 : 0>(p, tb_, cv, dv, xl, srow, tb, N, j);
         }
         if (!nl) return;
         const size_t so = ((size_t)r.s * p.G + r.ch) * N + j;
@@ -551,35 +552,44 @@ hipError_t launch_pd_prep(const PDParams& p, hipStream_t st) {
     pd_prep_kernel<<<(n + 255) / 256, 256, 0, st>>>(p.dict, p.pre, p.pre_cnt, p.H, p.K, p.N);
     return hipGetLastError();
 }
-hipError_t launch_pd_fwd(const PDParams& p, bool summary, hipStream_t st) {
+template <typename T>
+hipError_t pd_fwd_t(const PDParams& p, bool summary, hipStream_t st) {
     dim3 grid((p.G + 15) / 16, p.B * p.H);
     if (p.N == 16) {
-        if (summary) pd_fwd_kernel<true, 16><<<grid, 256, 0, st>>>(p);
-        else pd_fwd_kernel<false, 16><<<grid, 256, 0, st>>>(p);
+        if (summary) pd_fwd_kernel<T, true, 16><<<grid, 256, 0, st>>>(p);
+        else pd_fwd_kernel<T, false, 16><<<grid, 256, 0, st>>>(p);
     } else {
-        if (summary) pd_fwd_kernel<true, 0><<<grid, 256, 0, st>>>(p);
-        else pd_fwd_kernel<false, 0><<<grid, 256, 0, st>>>(p);
+        if (summary) pd_fwd_kernel<T, true, 0><<<grid, 256, 0, st>>>(p);
+        else pd_fwd_kernel<T, false, 0><<<grid, 256, 0, st>>>(p);
     }
     return hipGetLastError();
+}
+hipError_t launch_pd_fwd(const PDParams& p, bool summary, hipStream_t st) {
+    return p.dtype == 0 ? pd_fwd_t<float>(p, summary, st) : pd_fwd_t<bf16_t>(p, summary, st);
 }
 hipError_t launch_pd_combine_fwd(const PDParams& p, hipStream_t st) {
     pd_combine_fwd_kernel<<<p.B * p.H, 256, 0, st>>>(p);
     return hipGetLastError();
 }
-hipError_t launch_pd_bwd(const PDParams& p, bool summary, hipStream_t st) {
+template <typename T>
+hipError_t pd_bwd_t(const PDParams& p, bool summary, hipStream_t st) {
     dim3 grid((p.G + 15) / 16, p.B * p.H);
     // the main backward keeps the generic state count: specialised to 16 its
     // register allocation exceeds the three-waves-per-SIMD budget and spills
     if (summary) {
-        if (p.N == 16) pd_bwd_kernel<true, 16><<<grid, 256, 0, st>>>(p);
-        else pd_bwd_kernel<true, 0><<<grid, 256, 0, st>>>(p);
+        if (p.N == 16) pd_bwd_kernel<T, true, 16><<<grid, 256, 0, st>>>(p);
+        else pd_bwd_kernel<T, true, 0><<<grid, 256, 0, st>>>(p);
     } else if (p.glogits) {
-        if (p.K <= 16) pd_bwd_kernel<false, 0, 16><<<grid, 256, 0, st>>>(p);
-        else pd_bwd_kernel<false, 0, 0><<<grid, 256, 0, st>>>(p);
+        if (p.K <= 16) pd_bwd_kernel<T, false, 0, 16><<<grid, 256, 0, st>>>(p);
+        else if (std::is_same<T, float>::value) pd_bwd_kernel<T, false, 0, 0><<<grid, 256, 0, st>>>(p);
+        else return hipErrorInvalidValue;   // rejected on the host before: the raw gw needs fp32 storage
     } else {
-        pd_bwd_kernel<false, 0><<<grid, 256, 0, st>>>(p);
+        pd_bwd_kernel<T, false, 0><<<grid, 256, 0, st>>>(p);
     }
     return hipGetLastError();
+}
+hipError_t launch_pd_bwd(const PDParams& p, bool summary, hipStream_t st) {
+    return p.dtype == 0 ? pd_bwd_t<float>(p, summary, st) : pd_bwd_t<bf16_t>(p, summary, st);
 }
 hipError_t launch_pd_combine_rev(const PDParams& p, hipStream_t st) {
     pd_combine_rev_kernel<<<p.B * p.H, 256, 0, st>>>(p);

@@ -174,8 +174,9 @@ def make_complex(B=16, H=8, M=64, L=2048, seed=0, with_grad=True):
     return out
 
 
-def make_pd(B=8, H=32, N=16, L=17000, K=8, seed=0, with_grad=True):
-    """PD-transition scan inputs (fp32 values, int32 indices).
+def make_pd(B=8, H=32, N=16, L=17000, K=8, seed=0, with_grad=True, dtype="f32"):
+    """PD-transition scan inputs (fp32 values, int32 indices; ``dtype`` 'bf16'
+    rounds the streams logits, d, b, C, gy to bfloat16 bits).
 
     Draw order: dict ~ U{0..N-1} i.i.d. per (head, entry, column) (H,K,N);
     logits ~ N(0,1) (B,H,L,K); z ~ N(0,1), d = logistic(z) (B,H,L,N);
@@ -190,8 +191,8 @@ def make_pd(B=8, H=32, N=16, L=17000, K=8, seed=0, with_grad=True):
     s = 1.0 / math.sqrt(N)
     b = g.standard_normal((B, H, L, N)) * s
     C = g.standard_normal((B, H, L, N)) * s
-    out = dict(B=B, H=H, N=N, L=L, K=K, dict=np.ascontiguousarray(dct),
-               logits=_f32(logits), d=_f32(d), b=_f32(b), C=_f32(C))
+    out = dict(B=B, H=H, N=N, L=L, K=K, dict=np.ascontiguousarray(dct), dtype=dtype,
+               logits=_stream(logits, dtype), d=_stream(d, dtype), b=_stream(b, dtype), C=_stream(C, dtype))
     if with_grad:
-        out["gy"] = _f32(g.standard_normal((B, H, L)))
+        out["gy"] = _stream(g.standard_normal((B, H, L)), dtype)
     return out

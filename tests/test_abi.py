@@ -46,7 +46,7 @@ def test_struct_layouts():
     # + delta_bias pointer + delta_softplus int32 (padded to 8)
     assert ctypes.sizeof(B.ScanArgs) == 8 + 5 * 8 + 15 * 8 + 8
     assert ctypes.sizeof(B.ScanGrads) == 15 * 8
-    assert ctypes.sizeof(B.PDArgs) == 6 * 8 + 7 * 8
+    assert ctypes.sizeof(B.PDArgs) == 6 * 8 + 7 * 8 + 8   # + dtype (int32, padded)
     assert ctypes.sizeof(B.PDBwdIn) == 4 * 8 + 8   # 4 pointers + float tau (padded)
     assert ctypes.sizeof(B.PDGrads) == 5 * 8
 
@@ -243,3 +243,24 @@ def test_step_size_transform_selective_only():
     assert rc == status("SSM_ERR_UNSUPPORTED")
     rc, n = ws_bytes(B.SSM_OP_SCAN_BWD, sel_args(delta_bias=FAKE * 8, delta_softplus=1))
     assert rc == 0 and n > 0
+
+
+def test_pd_dtype_checks():
+    L = B.lib()
+    rc, _ = ws_bytes_pd(pd_args(dtype=5))
+    assert rc == status("SSM_ERR_DTYPE")
+    rc, _ = ws_bytes_pd(pd_args(dtype=B.SSM_BF16, d=FAKE * 3 + 2))   # 2-byte aligned is fine for bf16
+    assert rc == 0, L.ssm_last_error_detail()
+    rc, _ = ws_bytes_pd(pd_args(d=FAKE * 3 + 2))                      # but not for fp32
+    assert rc == status("SSM_ERR_LAYOUT")
+    a = pd_args(dtype=B.SSM_BF16, dict_size=32)
+    i = B.PDBwdIn(gy=FAKE * 32, ste_logits=FAKE * 256, tau=1.0)
+    g = B.PDGrads(gd=FAKE * 64, glogits=FAKE * 128)
+    rc = L.pd_scan_bwd(ctypes.byref(a), ctypes.byref(i), ctypes.byref(g), None, 0, None)
+    assert rc == status("SSM_ERR_UNSUPPORTED")   # bf16 glogits needs K <= 16
+
+
+def ws_bytes_pd(args):
+    n = ctypes.c_size_t(0)
+    rc = B.lib().ssm_workspace_bytes(B.SSM_OP_PD_FWD, ctypes.byref(args), ctypes.byref(n))
+    return rc, n.value

@@ -6,7 +6,7 @@ import torch
 
 import oracle
 import synth
-from tests._compare import F32, assert_close
+from tests._compare import BF16, F32, assert_close
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -176,18 +176,25 @@ def test_complex_rtrl_full_config():
 # ---------------------------------------------------------------------------
 # PD
 # ---------------------------------------------------------------------------
+def S(a):
+    """A stream to the device: bf16 bit arrays (uint16) as bfloat16, else as is."""
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).astype(np.int16)).view(torch.bfloat16).to(DEV)
+    return T(a)
+
+
 def run_pd(cfg, h0=None, ghl=None, use_sel=False):
     ssm = _ssm()
     B, H, L, N, K = cfg["B"], cfg["H"], cfg["L"], cfg["N"], cfg["K"]
     osel = oracle.pd_select(cfg["logits"])
-    t = dict(dict=T(cfg["dict"]), d=T(cfg["d"]), b=T(cfg["b"]), C=T(cfg["C"]))
+    t = dict(dict=T(cfg["dict"]), d=S(cfg["d"]), b=S(cfg["b"]), C=S(cfg["C"]))
     if use_sel:
         t["sel"] = T(osel)
     else:
-        t["logits"] = T(cfg["logits"])
+        t["logits"] = S(cfg["logits"])
     if h0 is not None:
         t["h0"] = T(h0.astype(np.float32))
-    gyt = T(cfg["gy"])
+    gyt = S(cfg["gy"])
     glt = None if ghl is None else T(ghl.astype(np.float32))
     f = ssm.pd_scan_fwd(want_h_last=True, want_ckpt=True, **t)
     g = ssm.pd_scan_bwd(gy=gyt, ckpt=f["ckpt"], gh_last=glt, **t)
@@ -198,10 +205,11 @@ def run_pd(cfg, h0=None, ghl=None, use_sel=False):
               h0=None if h0 is None else h0.astype(np.float32), B=B, H=H, L=L, N=N, K=K)
     y, hl = oracle.pd_fwd(**kw)
     og = oracle.pd_bwd(**kw, gy=cfg["gy"], ghlast=None if ghl is None else ghl.astype(np.float32))
-    assert_close("y", f["y"], y, **F32)
-    assert_close("h_last", f["h_last"], hl, **F32)
+    tol = BF16 if cfg.get("dtype") == "bf16" else F32
+    assert_close("y", f["y"], y, **tol)
+    assert_close("h_last", f["h_last"], hl, **tol)
     for k in ("gd", "gb", "gC", "gh0"):
-        assert_close(k, g[k], og[k], **F32)
+        assert_close(k, g[k], og[k], **tol)
         assert torch.equal(g[k], g2[k]), k
 
 
@@ -211,12 +219,12 @@ def run_pd_ste(cfg, tau, h0=None, ghl=None, with_ckpt=True):
     ssm = _ssm()
     B, H, L, N, K = cfg["B"], cfg["H"], cfg["L"], cfg["N"], cfg["K"]
     osel = oracle.pd_select(cfg["logits"])
-    t = dict(dict=T(cfg["dict"]), d=T(cfg["d"]), b=T(cfg["b"]), C=T(cfg["C"]), sel=T(osel))
+    t = dict(dict=T(cfg["dict"]), d=S(cfg["d"]), b=S(cfg["b"]), C=S(cfg["C"]), sel=T(osel))
     if h0 is not None:
         t["h0"] = T(h0.astype(np.float32))
-    gyt = T(cfg["gy"])
+    gyt = S(cfg["gy"])
     glt = None if ghl is None else T(ghl.astype(np.float32))
-    lg = T(cfg["logits"])
+    lg = S(cfg["logits"])
     ck = ssm.pd_scan_fwd(want_ckpt=True, want_y=False, want_sel=False, **t)["ckpt"] if with_ckpt else None
     g = ssm.pd_scan_bwd(gy=gyt, ckpt=ck, gh_last=glt, ste_logits=lg, tau=tau,
                         want=("gd", "gb", "gC", "gh0", "glogits"), **t)
@@ -225,7 +233,7 @@ def run_pd_ste(cfg, tau, h0=None, ghl=None, with_ckpt=True):
     o = oracle.pd_ste(logits=cfg["logits"], sel=osel, dict=cfg["dict"], d=cfg["d"], b=cfg["b"], C=cfg["C"],
                       h0=None if h0 is None else h0.astype(np.float32), gy=cfg["gy"],
                       ghlast=None if ghl is None else ghl.astype(np.float32), tau=tau, B=B, H=H, L=L, N=N, K=K)
-    assert_close("glogits", g["glogits"], o["glogits"], **F32)
+    assert_close("glogits", g["glogits"], o["glogits"], **(BF16 if cfg.get("dtype") == "bf16" else F32))
     for k in ("gd", "gb", "gC", "gh0"):
         assert torch.equal(g[k], g0[k]), k
 
@@ -242,9 +250,20 @@ def test_pd_ste_shapes(N, K, L):
     run_pd_ste(synth.make_pd(B=1, H=2, N=N, L=L, K=K, seed=N * K + L), tau=1.0, with_ckpt=(L % 2 == 0))
 
 
+def test_pd_ste_bf16():
+    run_pd_ste(synth.make_pd(B=2, H=3, N=16, L=300, K=8, seed=33, dtype="bf16"), tau=1.0)
+
+
 def test_pd_ste_full_config():
     """B=8 H=32 N=16 L=17000 K=8, seed 0, tau 1: every surrogate gradient compared."""
     run_pd_ste(synth.make_pd(B=8, H=32, N=16, L=17000, K=8, seed=0), tau=1.0)
+
+
+def test_pd_bf16_streams():
+    """bf16 logits, d, b, C, gy (selection bit-exact on the bf16 scores, many ties), fp32 state."""
+    g = np.random.default_rng(41)
+    run_pd(synth.make_pd(B=2, H=4, N=16, L=700, K=8, seed=40, dtype="bf16"),
+           h0=g.standard_normal((2, 4, 16)), ghl=g.standard_normal((2, 4, 16)))
 
 
 def test_pd_small():
