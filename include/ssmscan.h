@@ -111,7 +111,7 @@ extern "C" {
  */
 typedef struct {
     int32_t mode;      /* SSM_REAL_SELECTIVE, SSM_REAL_DENSE or SSM_COMPLEX_SHARED */
-    int32_t dtype;     /* SSM_F32 or SSM_BF16 (bf16: SSM_REAL_SELECTIVE only) */
+    int32_t dtype;     /* SSM_F32 or SSM_BF16 (bf16: SSM_REAL_SELECTIVE and SSM_COMPLEX_SHARED) */
     int64_t batch, channels, length, state, chunk_len;
     /* SSM_REAL_SELECTIVE */
     const void*  delta;  /* (B,D,L) dtype, step sizes                      */
@@ -124,11 +124,11 @@ typedef struct {
     /* both real modes */
     const void*  C;      /* (B,L,N) dtype (f32 for dense), readout C_t (shared over D) */
     /* SSM_COMPLEX_SHARED */
-    const float* r;      /* (B,H,L) retention control r_t                  */
-    const float* phi;    /* (B,H,L) phase control phi_t                    */
+    const void*  r;      /* (B,H,L) dtype retention control r_t            */
+    const void*  phi;    /* (B,H,L) dtype phase control phi_t              */
     const float* lam;    /* (H,M) baseline rate, 0 < lambda <= 1           */
     const float* theta;  /* (H,M) baseline frequency                       */
-    const float* u;      /* (B,H,L,M) complex64 input b_t = u_t            */
+    const void*  u;      /* (B,H,L,M) input b_t = u_t: (re, im) pairs of dtype (complex64 for f32) */
     const float* c;      /* (H,M) complex64 readout                        */
     /* all modes */
     const float* h0;     /* nullable initial state (B,D,N) f32 / (B,H,M) complex64; NULL = 0 */
@@ -143,14 +143,14 @@ typedef struct {
 } ssm_scan_args;
 
 typedef struct {
-    void*  y;        /* nullable (B,D,L) dtype; complex: (B,H,L) f32                       */
+    void*  y;        /* nullable (B,D,L) dtype (dense: f32)                                */
     float* h_last;   /* nullable h_{L-1}: (B,D,N) f32 / (B,H,M) complex64                  */
     float* ckpt;     /* nullable (B,D,n_chunks,N) f32 / (B,H,n_chunks,M) complex64:
                         ckpt[.., c, :] = state entering chunk c (h_{cT-1}; c = 0 holds h0) */
 } ssm_scan_fwd_out;
 
 typedef struct {
-    const void*  gy;       /* (B,D,L) dtype / (B,H,L) f32: dLoss/dy                       */
+    const void*  gy;       /* (B,D,L) dtype (dense: f32): dLoss/dy                        */
     const float* gh_last;  /* nullable dLoss/dh_{L-1}, same layout as h_last; NULL = 0    */
     const float* ckpt;     /* nullable checkpoints from ssm_scan_fwd with the same args;
                               NULL = recomputed into the workspace                         */
@@ -167,9 +167,9 @@ typedef struct {
     float* ga;      /* dense (B,D,L,N) f32                      */
     float* gb;      /* dense (B,D,L,N) f32                      */
     void*  gC;      /* real (B,L,N) dtype (sum over d)          */
-    float* gu;      /* complex (B,H,L,M) complex64              */
-    float* gr;      /* complex (B,H,L) f32                      */
-    float* gphi;    /* complex (B,H,L) f32                      */
+    void*  gu;      /* complex (B,H,L,M) (re, im) pairs of dtype */
+    void*  gr;      /* complex (B,H,L) dtype                    */
+    void*  gphi;    /* complex (B,H,L) dtype                    */
     float* glam;    /* complex (H,M) f32 (sum over b and t)     */
     float* gtheta;  /* complex (H,M) f32 (sum over b and t)     */
     float* gc;      /* complex (H,M) complex64                  */
@@ -266,14 +266,14 @@ int ssm_impulse_sensitivity(const ssm_scan_args* args, int64_t t_out, void* y, v
  *   glam[h,m]   = sum_{b,t} gy_t Re(c_m S^lambda_t) + <gh_last, S^lambda_{L-1}>,
  *   gtheta[h,m] = the same with S^theta.
  * The results equal ssm_scan_bwd's glam and gtheta up to rounding; no
- * checkpoints or reverse pass.  args: mode SSM_COMPLEX_SHARED, f32 (the
- * ssm_scan_fwd argument rules).  gy: (B,H,L) f32, required.  gh_last:
- * nullable (B,H,M) complex64, real-pair convention.  y: nullable (B,H,L) f32,
+ * checkpoints or reverse pass.  args: mode SSM_COMPLEX_SHARED (the
+ * ssm_scan_fwd argument rules).  gy: (B,H,L) dtype, required.  gh_last:
+ * nullable (B,H,M) complex64, real-pair convention.  y: nullable (B,H,L) dtype,
  * receives the forward output.  glam, gtheta: nullable (H,M) f32, overwritten.
  * Segments of the sequence run in parallel (workspace from
  * ssm_workspace_bytes(SSM_OP_COMPLEX_RTRL, ...)).  Errors as for ssm_scan_fwd;
  * SSM_ERR_UNSUPPORTED for another mode. */
-int ssm_complex_rtrl(const ssm_scan_args* args, const float* gy, const float* gh_last, float* y,
+int ssm_complex_rtrl(const ssm_scan_args* args, const void* gy, const float* gh_last, void* y,
                      float* glam, float* gtheta, void* ws, size_t ws_bytes, void* stream);
 
 /* Sensitivity of one output of a selective real scan to the inputs and to the

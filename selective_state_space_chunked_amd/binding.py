@@ -174,21 +174,38 @@ def _scan_args(mode, *, delta=None, x=None, A=None, Bm=None, a=None, b=None, C=N
         _need(h0, "h0", torch.float32, (Bsz, D, N), dev)
         dt = SSM_F32
     else:
-        _need(u, "u", torch.complex64)
-        Bsz, D, L, N = u.shape
+        # u: complex64 (B,H,L,M), or bfloat16 (B,H,L,M,2) holding (re, im) pairs; r, phi follow
+        _need(u, "u")
+        if u.dtype == torch.complex64:
+            Bsz, D, L, N = u.shape
+            st = torch.float32
+        elif u.dtype == torch.bfloat16 and u.dim() == 5 and u.shape[-1] == 2:
+            Bsz, D, L, N = u.shape[:4]
+            st = torch.bfloat16
+        else:
+            raise TypeError("u must be complex64 (B,H,L,M) or bfloat16 (B,H,L,M,2)")
         dev = u.device
         for nm, t in (("r", r), ("phi", phi)):
-            _need(t, nm, torch.float32, (Bsz, D, L), dev)
+            _need(t, nm, st, (Bsz, D, L), dev)
         for nm, t in (("lam", lam), ("theta", theta)):
             _need(t, nm, torch.float32, (D, N), dev)
         _need(c, "c", torch.complex64, (D, N), dev)
         _need(h0, "h0", torch.complex64, (Bsz, D, N), dev)
-        dt = SSM_F32
+        dt = SSM_BF16 if st == torch.bfloat16 else SSM_F32
     args = ScanArgs(mode=mode, dtype=dt, batch=Bsz, channels=D, length=L, state=N, chunk_len=chunk_len,
                     delta=_ptr(delta), x=_ptr(x), A=_ptr(A), Bm=_ptr(Bm), a=_ptr(a), b=_ptr(b), C=_ptr(C),
                     r=_ptr(r), phi=_ptr(phi), lam=_ptr(lam), theta=_ptr(theta), u=_ptr(u), c=_ptr(c),
                     h0=_ptr(h0), delta_bias=_ptr(delta_bias), delta_softplus=int(bool(delta_softplus)))
     return args, (Bsz, D, L, N), dev
+
+
+def _stream_dtype(mode, tensors):
+    """Element type of the per-step streams (y, gy and their gradients) of a call."""
+    if mode == SSM_REAL_SELECTIVE:
+        return tensors["delta"].dtype
+    if mode == SSM_COMPLEX_SHARED and tensors["u"].dtype == torch.bfloat16:
+        return torch.bfloat16
+    return torch.float32
 
 
 def _chunk(mode, chunk_len):
@@ -204,7 +221,7 @@ def scan_fwd(mode, *, want_y=True, want_h_last=False, want_ckpt=False, chunk_len
     """
     args, (Bsz, D, L, N), dev = _scan_args(mode, chunk_len=chunk_len, **tensors)
     out = dict(out or {})
-    ydt = tensors["delta"].dtype if mode == SSM_REAL_SELECTIVE else torch.float32
+    ydt = _stream_dtype(mode, tensors)
     sdt = torch.complex64 if mode == SSM_COMPLEX_SHARED else torch.float32
     nc = n_chunks(L, _chunk(mode, chunk_len))
     if want_y and "y" not in out:
@@ -229,7 +246,7 @@ _GRADS = {
 def scan_bwd(mode, *, gy, gh_last=None, ckpt=None, want=None, chunk_len=0, out=None, **tensors):
     """Backward scan.  ``want`` lists gradient names (default: all of the mode)."""
     args, (Bsz, D, L, N), dev = _scan_args(mode, chunk_len=chunk_len, **tensors)
-    ydt = tensors["delta"].dtype if mode == SSM_REAL_SELECTIVE else torch.float32
+    ydt = _stream_dtype(mode, tensors)
     sdt = torch.complex64 if mode == SSM_COMPLEX_SHARED else torch.float32
     _need(gy, "gy", ydt, (Bsz, D, L), dev)
     _need(gh_last, "gh_last", sdt, (Bsz, D, N), dev)
@@ -240,8 +257,8 @@ def scan_bwd(mode, *, gy, gh_last=None, ckpt=None, want=None, chunk_len=0, out=N
         "gdelta": ((Bsz, D, L), ydt), "gx": ((Bsz, D, L), ydt), "gA": ((D, N), torch.float32),
         "gBm": ((Bsz, L, N), ydt), "gC": ((Bsz, L, N), ydt), "gh0": ((Bsz, D, N), sdt),
         "ga": ((Bsz, D, L, N), torch.float32), "gb": ((Bsz, D, L, N), torch.float32),
-        "gu": ((Bsz, D, L, N), torch.complex64), "gr": ((Bsz, D, L), torch.float32),
-        "gphi": ((Bsz, D, L), torch.float32), "glam": ((D, N), torch.float32),
+        "gu": (((Bsz, D, L, N), torch.complex64) if ydt == torch.float32 else ((Bsz, D, L, N, 2), ydt)),
+        "gr": ((Bsz, D, L), ydt), "gphi": ((Bsz, D, L), ydt), "glam": ((D, N), torch.float32),
         "gtheta": ((D, N), torch.float32), "gc": ((D, N), torch.complex64),
         "gdelta_bias": ((D,), torch.float32),
     }
@@ -295,14 +312,15 @@ def complex_rtrl(*, gy, gh_last=None, want_y=True, chunk_len=0, out=None, **tens
     ((H, M) float32) and y ((B, H, L) float32) when ``want_y``.
     """
     args, (Bsz, H, L, M), dev = _scan_args(SSM_COMPLEX_SHARED, chunk_len=chunk_len, **tensors)
-    _need(gy, "gy", torch.float32, (Bsz, H, L), dev)
+    ydt = _stream_dtype(SSM_COMPLEX_SHARED, tensors)
+    _need(gy, "gy", ydt, (Bsz, H, L), dev)
     _need(gh_last, "gh_last", torch.complex64, (Bsz, H, M), dev)
     out = dict(out or {})
     for k in ("glam", "gtheta"):
         if k not in out:
             out[k] = torch.empty((H, M), dtype=torch.float32, device=dev)
     if want_y and "y" not in out:
-        out["y"] = torch.empty((Bsz, H, L), dtype=torch.float32, device=dev)
+        out["y"] = torch.empty((Bsz, H, L), dtype=ydt, device=dev)
     ws, nws = _workspace(SSM_OP_COMPLEX_RTRL, ctypes.byref(args), dev)
     _check(lib().ssm_complex_rtrl(ctypes.byref(args), _ptr(gy), _ptr(gh_last), _ptr(out.get("y")),
                                   _ptr(out["glam"]), _ptr(out["gtheta"]), _ptr(ws), nws, _stream(dev)))

@@ -145,8 +145,8 @@ int validate_scan_args(const ssm_scan_args* a, ScanPlan* pl) {
     if (a->mode != SSM_REAL_SELECTIVE && a->mode != SSM_REAL_DENSE && a->mode != SSM_COMPLEX_SHARED)
         return fail(SSM_ERR_UNSUPPORTED, "unknown mode %d", a->mode);
     if (a->dtype != SSM_F32 && a->dtype != SSM_BF16) return fail(SSM_ERR_DTYPE, "unknown dtype %d", a->dtype);
-    if (a->dtype == SSM_BF16 && a->mode != SSM_REAL_SELECTIVE)
-        return fail(SSM_ERR_DTYPE, "bf16 streams are supported by SSM_REAL_SELECTIVE only");
+    if (a->dtype == SSM_BF16 && a->mode == SSM_REAL_DENSE)
+        return fail(SSM_ERR_DTYPE, "bf16 streams are supported by SSM_REAL_SELECTIVE and SSM_COMPLEX_SHARED only");
     if (pl->B < 1 || pl->D < 1 || pl->L < 1 || pl->N < 1)
         return fail(SSM_ERR_SHAPE, "sizes must be >= 1 (B=%lld D=%lld L=%lld N=%lld)", (long long)pl->B,
                     (long long)pl->D, (long long)pl->L, (long long)pl->N);
@@ -197,8 +197,8 @@ int validate_scan_args(const ssm_scan_args* a, ScanPlan* pl) {
         if (!a->r || !a->phi || !a->lam || !a->theta || !a->u || !a->c)
             return fail(SSM_ERR_NULL, "SSM_COMPLEX_SHARED needs r, phi, lam, theta, u and c");
         int rc;
-        if ((rc = check_align(a->u, 8, "u")) || (rc = check_align(a->c, 8, "c")) ||
-            (rc = check_align(a->r, 4, "r")) || (rc = check_align(a->phi, 4, "phi")) ||
+        if ((rc = check_align(a->u, 2 * pl->esz, "u")) || (rc = check_align(a->c, 8, "c")) ||
+            (rc = check_align(a->r, pl->esz, "r")) || (rc = check_align(a->phi, pl->esz, "phi")) ||
             (rc = check_align(a->h0, 8, "h0")))
             return rc;
     }
@@ -213,9 +213,9 @@ std::vector<Range> scan_inputs(const ssm_scan_args* a, const ScanPlan& p) {
         {a->A, (size_t)p.D * p.N * 4, "A"}, {a->Bm, BLN * p.esz, "Bm"},
         {a->a, BDLN * 4, "a"}, {a->b, BDLN * 4, "b"},
         {a->C, BLN * (p.mode == SSM_REAL_SELECTIVE ? p.esz : 4), "C"},
-        {a->r, BDL * 4, "r"}, {a->phi, BDL * 4, "phi"},
+        {a->r, BDL * p.esz, "r"}, {a->phi, BDL * p.esz, "phi"},
         {a->lam, (size_t)p.D * p.N * 4, "lam"}, {a->theta, (size_t)p.D * p.N * 4, "theta"},
-        {a->u, BDLN * 8, "u"}, {a->c, (size_t)p.D * p.N * 8, "c"},
+        {a->u, BDLN * 2 * p.esz, "u"}, {a->c, (size_t)p.D * p.N * 8, "c"},
         {a->h0, (size_t)p.B * p.D * st, "h0"},
         {a->delta_bias, (size_t)p.D * 4, "delta_bias"},
     };
@@ -341,11 +341,11 @@ int scan_fwd_impl(const ssm_scan_args* a, const ssm_scan_fwd_out* out, void* ws,
     if (!need_only) {
         if (!out) return fail(SSM_ERR_NULL, "out is NULL");
         const size_t st_b = p.mode == SSM_COMPLEX_SHARED ? 8 : 4;
-        const size_t yb = p.B * p.D * p.L * (p.mode == SSM_REAL_SELECTIVE ? p.esz : 4);
+        const size_t yb = p.B * p.D * p.L * (p.mode == SSM_REAL_DENSE ? 4 : p.esz);
         const size_t hb = p.B * p.D * p.N * st_b;
         std::vector<Range> outs = {{out->y, yb, "y"}, {out->h_last, hb, "h_last"},
                                    {out->ckpt, hb * p.nchunks, "ckpt"}};
-        if ((rc = check_align(out->y, p.mode == SSM_REAL_SELECTIVE ? p.esz : 4, "y")) ||
+        if ((rc = check_align(out->y, p.mode == SSM_REAL_DENSE ? 4 : p.esz, "y")) ||
             (rc = check_align(out->h_last, st_b, "h_last")) || (rc = check_align(out->ckpt, st_b, "ckpt")))
             return rc;
         if ((rc = check_overlaps(scan_inputs(a, p), outs))) return rc;
@@ -397,7 +397,7 @@ int scan_bwd_impl(const ssm_scan_args* a, const ssm_scan_bwd_in* in, const ssm_s
     const bool have_ckpt = need_only ? false : in->ckpt != nullptr;
     if (!need_only) {
         const size_t st_b = p.mode == SSM_COMPLEX_SHARED ? 8 : 4;
-        const size_t es = p.mode == SSM_REAL_SELECTIVE ? p.esz : 4;
+        const size_t es = p.mode == SSM_REAL_DENSE ? 4 : p.esz;
         const size_t BDL = p.B * p.D * p.L, BLN = p.B * p.L * p.N;
         const size_t hb = p.B * p.D * p.N * st_b;
         std::vector<Range> ins = scan_inputs(a, p);
@@ -407,8 +407,8 @@ int scan_bwd_impl(const ssm_scan_args* a, const ssm_scan_bwd_in* in, const ssm_s
         std::vector<Range> outs = {
             {g->gdelta, BDL * es, "gdelta"}, {g->gx, BDL * es, "gx"}, {g->gA, (size_t)p.D * p.N * 4, "gA"},
             {g->gBm, BLN * es, "gBm"}, {g->ga, BDL * p.N * 4, "ga"}, {g->gb, BDL * p.N * 4, "gb"},
-            {g->gC, BLN * es, "gC"}, {g->gu, BDL * p.N * 8, "gu"}, {g->gr, BDL * 4, "gr"},
-            {g->gphi, BDL * 4, "gphi"}, {g->glam, (size_t)p.D * p.N * 4, "glam"},
+            {g->gC, BLN * es, "gC"}, {g->gu, BDL * p.N * 2 * es, "gu"}, {g->gr, BDL * es, "gr"},
+            {g->gphi, BDL * es, "gphi"}, {g->glam, (size_t)p.D * p.N * 4, "glam"},
             {g->gtheta, (size_t)p.D * p.N * 4, "gtheta"}, {g->gc, (size_t)p.D * p.N * 8, "gc"},
             {g->gh0, hb, "gh0"}, {g->gdelta_bias, (size_t)p.D * 4, "gdelta_bias"}};
         for (const auto& o : outs)
@@ -582,7 +582,7 @@ int ssm_output_sensitivity(const ssm_scan_args* args, int64_t t_out, void* y, vo
                            size_t ws_bytes, void* stream) {
     return impulse_impl(args, t_out, y, s_x, s_delta, true, ws, ws_bytes, (hipStream_t)stream, nullptr);
 }
-int ssm_complex_rtrl(const ssm_scan_args* args, const float* gy, const float* gh_last, float* y, float* glam,
+int ssm_complex_rtrl(const ssm_scan_args* args, const void* gy, const float* gh_last, void* y, float* glam,
                      float* gtheta, void* ws, size_t ws_bytes, void* stream) {
     return rtrl_impl(args, gy, gh_last, y, glam, gtheta, ws, ws_bytes, (hipStream_t)stream, nullptr);
 }

@@ -145,16 +145,35 @@ __device__ __forceinline__ float lanev(float v, int j) { return __int_as_float(_
 // u of steps t0 .. t0+K-1 for mode mc (complex64); zero past L and on idle
 // lanes.  A block inside the sequence loads unconditionally, so all K loads
 // are in flight before the first step runs.
-template <int K>
-__device__ __forceinline__ void load_u(const float* __restrict__ urow, int t0, int L, int M, int mc, bool act,
+// One complex value of a stream: an (re, im) pair of fp32 or of bf16.
+template <typename T> struct CPair;
+template <> struct CPair<float> {
+    using V = float2;
+    __device__ static float2 widen(float2 v) { return v; }
+    __device__ static float2 narrow(float re, float im) { return make_float2(re, im); }
+};
+template <> struct CPair<bf16_t> {
+    using V = uint32_t;   // re in the low half, im in the high half
+    __device__ static float2 widen(uint32_t v) {
+        return make_float2(__uint_as_float(v << 16), __uint_as_float(v & 0xffff0000u));
+    }
+    __device__ static uint32_t narrow(float re, float im) {
+        return (uint32_t)from_f32<bf16_t>(re) | ((uint32_t)from_f32<bf16_t>(im) << 16);
+    }
+};
+
+template <typename T, int K>
+__device__ __forceinline__ void load_u(const T* __restrict__ urow, int t0, int L, int M, int mc, bool act,
                                        float2 (&v)[K]) {
-    const float2* __restrict__ q = reinterpret_cast<const float2*>(urow) + (size_t)t0 * M + mc;
+    using V = typename CPair<T>::V;
+    const V* __restrict__ q = reinterpret_cast<const V*>(urow) + (size_t)t0 * M + mc;
     if (t0 + K <= L) {
 #pragma unroll
-        for (int j = 0; j < K; ++j) v[j] = q[(size_t)j * M];
+        for (int j = 0; j < K; ++j) v[j] = CPair<T>::widen(q[(size_t)j * M]);
     } else {
 #pragma unroll
-        for (int j = 0; j < K; ++j) v[j] = t0 + j < L ? q[(size_t)j * M] : make_float2(0.0f, 0.0f);
+        for (int j = 0; j < K; ++j)
+            v[j] = t0 + j < L ? CPair<T>::widen(q[(size_t)j * M]) : make_float2(0.0f, 0.0f);
     }
     if (!act) {
 #pragma unroll
@@ -183,7 +202,7 @@ __device__ __forceinline__ bool cunit(const CplxParams& p, CUnit& u) {
 // ---------------------------------------------------------------------------
 // forward.  SUMMARY: per segment the map h_end = P h_start + S (h_start = 0).
 // ---------------------------------------------------------------------------
-template <bool SUMMARY>
+template <typename T, bool SUMMARY>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void cplx_fwd_kernel(CplxParams p) {
     CUnit u;
     if (!cunit(p, u)) return;
@@ -202,7 +221,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void c
     }
     const int c0 = u.g * p.chunks_per_seg;
     const int c1 = min(c0 + p.chunks_per_seg, p.nchunks);
-    const float* urow = p.u + (size_t)u.s * L * M * 2;
+    const T* urow = (const T*)p.u + (size_t)u.s * L * M * 2;
     for (int ch = c0; ch < c1; ++ch) {
         const int t0 = ch * kCChunk;
         if (!SUMMARY && p.ckpt_out && u.act) {
@@ -212,15 +231,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void c
         }
         const int tl = t0 + (u.m & 31);
         const bool tv = tl < L;
-        const float rv = tv ? p.r[(size_t)u.s * L + tl] : 0.0f;
-        const float pv = tv ? p.phi[(size_t)u.s * L + tl] : 0.0f;
+        const float rv = tv ? to_f32(((const T*)p.r)[(size_t)u.s * L + tl]) : 0.0f;
+        const float pv = tv ? to_f32(((const T*)p.phi)[(size_t)u.s * L + tl]) : 0.0f;
         float yp[kCChunk];
         cplx_chunk(pv, thmax, t0 + kCChunk <= L, [&](auto fastc, auto fullc) {
             constexpr bool FAST = decltype(fastc)::value, FULL = decltype(fullc)::value;
 #pragma unroll
             for (int hb = 0; hb < kCChunk / 16; ++hb) {
                 float2 uv[16];
-                load_u<16>(urow, t0 + 16 * hb, L, M, u.mc, u.act, uv);
+                load_u<T, 16>(urow, t0 + 16 * hb, L, M, u.mc, u.act, uv);
 #pragma unroll
                 for (int jj = 0; jj < 16; ++jj) {
                     const int j = 16 * hb + jj;
@@ -237,7 +256,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void c
         if (!SUMMARY && p.y) {
             const float ys = wave_transpose_sum32(yp);
             const int t = t0 + (u.m >> 1);
-            if ((u.m & 1) == 0 && t < L) p.y[(size_t)u.s * L + t] = ys;
+            if ((u.m & 1) == 0 && t < L) ((T*)p.y)[(size_t)u.s * L + t] = from_f32<T>(ys);
         }
     }
     if (!u.act) return;
@@ -262,7 +281,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void c
 // (in fp64, from its checkpoint) and kept in registers as complex64.
 // SUMMARY: per segment the adjoint map nu_start = Q nu_end + R.
 // ---------------------------------------------------------------------------
-template <bool SUMMARY>
+template <typename T, bool SUMMARY>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void cplx_bwd_kernel(CplxParams p) {
     CUnit u;
     if (!cunit(p, u)) return;
@@ -282,14 +301,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
     double gl = 0.0, gt = 0.0, gcr = 0.0, gci = 0.0;
     const int c0 = u.g * p.chunks_per_seg;
     const int c1 = min(c0 + p.chunks_per_seg, p.nchunks);
-    const float* urow = p.u + (size_t)u.s * L * M * 2;
+    const T* urow = (const T*)p.u + (size_t)u.s * L * M * 2;
     for (int ch = c1 - 1; ch >= c0; --ch) {
         const int t0 = ch * kCChunk;
         const int tl = t0 + (u.m & 31);
         const bool tv = tl < L;
-        const float rv = tv ? p.r[(size_t)u.s * L + tl] : 0.0f;
-        const float pv = tv ? p.phi[(size_t)u.s * L + tl] : 0.0f;
-        const float gv = tv ? p.gy[(size_t)u.s * L + tl] : 0.0f;
+        const float rv = tv ? to_f32(((const T*)p.r)[(size_t)u.s * L + tl]) : 0.0f;
+        const float pv = tv ? to_f32(((const T*)p.phi)[(size_t)u.s * L + tl]) : 0.0f;
+        const float gv = tv ? to_f32(((const T*)p.gy)[(size_t)u.s * L + tl]) : 0.0f;
         cplx_chunk(pv, thmax, t0 + kCChunk <= L, [&](auto fastc, auto fullc) {
         constexpr bool FAST = decltype(fastc)::value, FULL = decltype(fullc)::value;
         if (SUMMARY) {
@@ -317,7 +336,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
 #pragma unroll
         for (int hb = 0; hb < kCChunk / 16; ++hb) {
             float2 uv[16];
-            load_u<16>(urow, t0 + 16 * hb, L, M, u.mc, u.act, uv);
+            load_u<T, 16>(urow, t0 + 16 * hb, L, M, u.mc, u.act, uv);
 #pragma unroll
             for (int jj = 0; jj < 16; ++jj) {
                 const int j = 16 * hb + jj;
@@ -345,11 +364,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
                     const double g = lanev(gv, j);
                     const cd a = trans_a<FAST>(rj, lnl, pj, th);
                     const cd mu = {fma(g, cjr, nu.re), fma(g, cji, nu.im)};
-                    if (p.gu && u.act) {
-                        float* dst = p.gu + (((size_t)u.s * L + t) * M + u.m) * 2;
-                        dst[0] = (float)mu.re;
-                        dst[1] = (float)mu.im;
-                    }
+                    if (p.gu && u.act)
+                        reinterpret_cast<typename CPair<T>::V*>(p.gu)[((size_t)u.s * L + t) * M + u.m] =
+                            CPair<T>::narrow((float)mu.re, (float)mu.im);
                     const cd ga = cmul(mu, cd{hre[j], -(double)him[j]});
                     const cd gz = cmul_conj_a(a, ga);
                     if (u.act) {
@@ -367,8 +384,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
             const double sp = wave_transpose_sum16_f64(gpp);
             const int t = t0 + 16 * half + (u.m >> 2);
             if ((u.m & 3) == 0 && t < L) {
-                if (p.gr) p.gr[(size_t)u.s * L + t] = (float)sr;
-                if (p.gphi) p.gphi[(size_t)u.s * L + t] = (float)sp;
+                if (p.gr) ((T*)p.gr)[(size_t)u.s * L + t] = from_f32<T>((float)sr);
+                if (p.gphi) ((T*)p.gphi)[(size_t)u.s * L + t] = from_f32<T>((float)sp);
             }
         }
         });
@@ -511,7 +528,7 @@ __global__ __launch_bounds__(256) void cplx_reduce_kernel(CplxParams p, float* g
 // ---------------------------------------------------------------------------
 // Triples (h, sl, st) are stored as three planes of complex values, so a wave's
 // 64 modes move as contiguous 1 KB rows.
-template <bool SUMMARY>
+template <typename T, bool SUMMARY>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void cplx_rtrl_kernel(RtrlParams p) {
     const int wave = threadIdx.x >> 6;
     const int unit = blockIdx.x * 4 + wave;
@@ -544,21 +561,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
     }
     const int c0 = g * p.chunks_per_seg;
     const int c1 = min(c0 + p.chunks_per_seg, p.nchunks);
-    const float* urow = p.u + (size_t)s * L * M * 2;
+    const T* urow = (const T*)p.u + (size_t)s * L * M * 2;
     for (int ch = c0; ch < c1; ++ch) {
         const int t0 = ch * kCChunk;
         const int tl = t0 + (m & 31);
         const bool tv = tl < L;
-        const float rv = tv ? p.r[(size_t)s * L + tl] : 0.0f;
-        const float pv = tv ? p.phi[(size_t)s * L + tl] : 0.0f;
-        const float gv = (!SUMMARY && tv) ? p.gy[(size_t)s * L + tl] : 0.0f;
+        const float rv = tv ? to_f32(((const T*)p.r)[(size_t)s * L + tl]) : 0.0f;
+        const float pv = tv ? to_f32(((const T*)p.phi)[(size_t)s * L + tl]) : 0.0f;
+        const float gv = (!SUMMARY && tv) ? to_f32(((const T*)p.gy)[(size_t)s * L + tl]) : 0.0f;
         float yp[kCChunk];
         cplx_chunk(pv, thmax, t0 + kCChunk <= L, [&](auto fastc, auto fullc) {
             constexpr bool FAST = decltype(fastc)::value, FULL = decltype(fullc)::value;
 #pragma unroll
             for (int hb = 0; hb < kCChunk / 16; ++hb) {
                 float2 uv[16];
-                load_u<16>(urow, t0 + 16 * hb, L, M, mc, act, uv);
+                load_u<T, 16>(urow, t0 + 16 * hb, L, M, mc, act, uv);
 #pragma unroll
                 for (int jj = 0; jj < 16; ++jj) {
                     const int j = 16 * hb + jj;
@@ -588,7 +605,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
         if (!SUMMARY && p.y) {
             const float ys = wave_transpose_sum32(yp);
             const int t = t0 + (m >> 1);
-            if ((m & 1) == 0 && t < L) p.y[(size_t)s * L + t] = ys;
+            if ((m & 1) == 0 && t < L) ((T*)p.y)[(size_t)s * L + t] = from_f32<T>(ys);
         }
     }
     if (SUMMARY) {
@@ -677,8 +694,13 @@ __global__ __launch_bounds__(256) void cplx_rtrl_reduce_kernel(RtrlParams p) {
 
 hipError_t launch_cplx_rtrl(const RtrlParams& p, bool summary, hipStream_t st) {
     const int units = p.B * p.H * p.G;
-    if (summary) cplx_rtrl_kernel<true><<<(units + 3) / 4, 256, 0, st>>>(p);
-    else cplx_rtrl_kernel<false><<<(units + 3) / 4, 256, 0, st>>>(p);
+    if (p.dtype == 0) {
+        if (summary) cplx_rtrl_kernel<float, true><<<(units + 3) / 4, 256, 0, st>>>(p);
+        else cplx_rtrl_kernel<float, false><<<(units + 3) / 4, 256, 0, st>>>(p);
+    } else {
+        if (summary) cplx_rtrl_kernel<bf16_t, true><<<(units + 3) / 4, 256, 0, st>>>(p);
+        else cplx_rtrl_kernel<bf16_t, false><<<(units + 3) / 4, 256, 0, st>>>(p);
+    }
     return hipGetLastError();
 }
 hipError_t launch_cplx_rtrl_combine(const RtrlParams& p, hipStream_t st) {
@@ -695,15 +717,25 @@ hipError_t launch_cplx_rtrl_reduce(const RtrlParams& p, hipStream_t st) {
 hipError_t launch_cplx_fwd(const CplxParams& p, bool summary, hipStream_t st) {
     const int units = p.B * p.H * p.G;
     dim3 grid((units + 3) / 4), block(256);
-    if (summary) cplx_fwd_kernel<true><<<grid, block, 0, st>>>(p);
-    else cplx_fwd_kernel<false><<<grid, block, 0, st>>>(p);
+    if (p.dtype == 0) {
+        if (summary) cplx_fwd_kernel<float, true><<<grid, block, 0, st>>>(p);
+        else cplx_fwd_kernel<float, false><<<grid, block, 0, st>>>(p);
+    } else {
+        if (summary) cplx_fwd_kernel<bf16_t, true><<<grid, block, 0, st>>>(p);
+        else cplx_fwd_kernel<bf16_t, false><<<grid, block, 0, st>>>(p);
+    }
     return hipGetLastError();
 }
 hipError_t launch_cplx_bwd(const CplxParams& p, bool summary, hipStream_t st) {
     const int units = p.B * p.H * p.G;
     dim3 grid((units + 3) / 4), block(256);
-    if (summary) cplx_bwd_kernel<true><<<grid, block, 0, st>>>(p);
-    else cplx_bwd_kernel<false><<<grid, block, 0, st>>>(p);
+    if (p.dtype == 0) {
+        if (summary) cplx_bwd_kernel<float, true><<<grid, block, 0, st>>>(p);
+        else cplx_bwd_kernel<float, false><<<grid, block, 0, st>>>(p);
+    } else {
+        if (summary) cplx_bwd_kernel<bf16_t, true><<<grid, block, 0, st>>>(p);
+        else cplx_bwd_kernel<bf16_t, false><<<grid, block, 0, st>>>(p);
+    }
     return hipGetLastError();
 }
 hipError_t launch_cplx_combine_fwd(const CplxParams& p, hipStream_t st) {

@@ -82,17 +82,21 @@ hipError_t launch_dense_fwd(const DenseParams& p, bool summary, hipStream_t st);
 hipError_t launch_dense_bwd(const DenseParams& p, bool summary, hipStream_t st);
 
 // ------------------------------- complex -----------------------------------
+// Streams (r, phi, u, gy, y, gu, gr, gphi) are fp32 or bf16 (dtype 0 / 1; a
+// complex value is an (re, im) pair of the type); parameters, states,
+// checkpoints and summaries are fp32 / fp64.
 struct CplxParams {
-    const float* r; const float* phi; const float* lam; const float* theta;
-    const float* u; const float* c; const float* h0;
+    const void* r; const void* phi; const float* lam; const float* theta;
+    const void* u; const float* c; const float* h0;
     double* carry_in;        // (B,H,G,M) complex double, written by the combine pass
-    const float* gy; const float* gh_last; const float* ckpt;
+    const void* gy; const float* gh_last; const float* ckpt;
     double* nu_in;           // (B,H,G,M) complex double, written by the reverse combine pass
-    float* y; float* h_last; float* ckpt_out;
+    void* y; float* h_last; float* ckpt_out;
     double* segP; double* segS; double* segQ; double* segR;   // complex double (B,H,G,M)
-    float* gu; float* gr; float* gphi; float* gh0;
+    void* gu; void* gr; void* gphi; float* gh0;
     double* partL; double* partT; double* partC;              // (B,G,H,M) [partC complex]
     int B, H, L, M, nchunks, chunk, chunks_per_seg, G;
+    int dtype;
 };
 hipError_t launch_cplx_fwd(const CplxParams& p, bool summary, hipStream_t st);
 hipError_t launch_cplx_bwd(const CplxParams& p, bool summary, hipStream_t st);
@@ -101,16 +105,17 @@ hipError_t launch_cplx_combine_rev(const CplxParams& p, hipStream_t st);
 hipError_t launch_cplx_reduce(const CplxParams& p, float* glam, float* gtheta, float* gc, hipStream_t st);
 
 struct RtrlParams {
-    const float* r; const float* phi; const float* lam; const float* theta;
-    const float* u; const float* c; const float* h0;
-    const float* gy; const float* gh_last;
-    float* y; float* glam; float* gtheta;
+    const void* r; const void* phi; const float* lam; const float* theta;
+    const void* u; const float* c; const float* h0;
+    const void* gy; const float* gh_last;
+    void* y; float* glam; float* gtheta;
     double* segP;    // (B,H,G,M) complex: product of a over the segment
     double* segS;    // 3 planes (h, sl, st) of (B,H,G,M) complex: local triple from zero
     double* segRP;   // (B,H,G) x (sum r, sum phi)
     double* carry;   // 3 planes (h, sl, st) of (B,H,G,M) complex entering each segment
     double* partL; double* partT;   // (B,G,H,M)
     int B, H, L, M, nchunks, chunks_per_seg, G;
+    int dtype;
 };
 hipError_t launch_cplx_rtrl(const RtrlParams& p, bool summary, hipStream_t st);
 hipError_t launch_cplx_rtrl_combine(const RtrlParams& p, hipStream_t st);

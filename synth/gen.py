@@ -142,13 +142,16 @@ def make_impulse(B=1, D=1024, N=16, L=128000, seed=0, with_xrand=False):
     return out
 
 
-def make_complex(B=16, H=8, M=64, L=2048, seed=0, with_grad=True):
+def make_complex(B=16, H=8, M=64, L=2048, seed=0, with_grad=True, dtype="f32"):
     """Complex diagonal recurrence with shared retention/phase controls.
 
     Draw order: lam ~ U[0.9, 0.999] (H,M); theta ~ U[0, pi] (H,M);
     z ~ N(0,1), r = softplus(z) (B,H,L); phi ~ N(0,1) (B,H,L);
     u = N(0,1/2) + i N(0,1/2) (B,H,L,M); c = N(0,1/(2M)) + i N(0,1/(2M)) (H,M);
     gy ~ N(0,1) (B,H,L).  Complex arrays are complex64 (interleaved re, im).
+    ``dtype`` 'bf16' rounds the streams r, phi, gy to bfloat16 bits and gives u
+    as bfloat16 bits of shape (B,H,L,M,2) (re, im), plus ``u_c``, the complex
+    values those bits hold; lam, theta and c stay fp32 / complex64.
     """
     g = np.random.Generator(np.random.PCG64(seed))
     lam = g.uniform(0.9, 0.999, (H, M))
@@ -167,10 +170,17 @@ def make_complex(B=16, H=8, M=64, L=2048, seed=0, with_grad=True):
     c = np.empty((H, M), dtype=np.complex64)
     c.real = c_re
     c.imag = c_im
-    out = dict(B=B, H=H, M=M, L=L, lam=_f32(lam), theta=_f32(theta), r=_f32(r),
-               phi=_f32(phi), u=u, c=c)
+    out = dict(B=B, H=H, M=M, L=L, dtype=dtype, lam=_f32(lam), theta=_f32(theta), r=_stream(r, dtype),
+               phi=_stream(phi, dtype), u=u, c=c)
+    if dtype == "bf16":
+        bits = np.stack([f32_to_bf16_bits(u.real), f32_to_bf16_bits(u.imag)], axis=-1)
+        out["u"] = np.ascontiguousarray(bits)
+        u_c = np.empty((B, H, L, M), dtype=np.complex64)
+        u_c.real = bf16_bits_to_f32(bits[..., 0])
+        u_c.imag = bf16_bits_to_f32(bits[..., 1])
+        out["u_c"] = u_c
     if with_grad:
-        out["gy"] = _f32(g.standard_normal((B, H, L)))
+        out["gy"] = _stream(g.standard_normal((B, H, L)), dtype)
     return out
 
 

@@ -63,26 +63,45 @@ def test_dense_many_segments():
 # ---------------------------------------------------------------------------
 # complex
 # ---------------------------------------------------------------------------
+def S(a):
+    """A stream to the device: bf16 bit arrays (uint16) as bfloat16, else as is."""
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).astype(np.int16)).view(torch.bfloat16).to(DEV)
+    return T(a)
+
+
+def _cplx_oracle_kw(cfg):
+    kw = {k: cfg[k] for k in ("r", "phi", "lam", "theta", "u", "c")}
+    if cfg.get("dtype") == "bf16":
+        kw["u"] = cfg["u_c"]
+    return kw
+
+
 def run_complex(cfg, h0=None, ghl=None):
     ssm = _ssm()
     B, H, L, M = cfg["B"], cfg["H"], cfg["L"], cfg["M"]
-    t = {k: T(cfg[k]) for k in ("r", "phi", "lam", "theta", "u", "c")}
+    t = {k: S(cfg[k]) for k in ("r", "phi", "lam", "theta", "u", "c")}
     if h0 is not None:
         t["h0"] = T(h0.astype(np.complex64))
-    gyt = T(cfg["gy"])
+    gyt = S(cfg["gy"])
     glt = None if ghl is None else T(ghl.astype(np.complex64))
     f = ssm.scan_fwd(ssm.SSM_COMPLEX_SHARED, want_h_last=True, want_ckpt=True, **t)
     g = ssm.scan_bwd(ssm.SSM_COMPLEX_SHARED, gy=gyt, ckpt=f["ckpt"], gh_last=glt, **t)
     g2 = ssm.scan_bwd(ssm.SSM_COMPLEX_SHARED, gy=gyt, gh_last=glt, **t)
     torch.cuda.synchronize()
-    kw = {k: cfg[k] for k in ("r", "phi", "lam", "theta", "u", "c")}
+    kw = _cplx_oracle_kw(cfg)
     h0c = None if h0 is None else h0.astype(np.complex64)
     y, hl = oracle.complex_fwd(**kw, h0=h0c, B=B, H=H, L=L, M=M)
     og = oracle.complex_bwd(**kw, h0=h0c, gy=cfg["gy"], ghlast=None if ghl is None else ghl.astype(np.complex64),
                             B=B, H=H, L=L, M=M)
-    errs = {"y": assert_close("y", f["y"], y, **F32), "h_last": assert_close("h_last", f["h_last"], hl, **F32)}
+    bf = cfg.get("dtype") == "bf16"
+    tol = BF16 if bf else F32
+    errs = {"y": assert_close("y", f["y"], y, **tol), "h_last": assert_close("h_last", f["h_last"], hl, **F32)}
     for k in ("gu", "gr", "gphi", "glam", "gtheta", "gc", "gh0"):
-        errs[k] = assert_close(k, g[k], og[k], **F32)
+        gk = g[k]
+        if k == "gu" and bf:   # (re, im) bf16 pairs -> complex
+            gk = torch.complex(gk[..., 0].float(), gk[..., 1].float())
+        errs[k] = assert_close(k, gk, og[k], **(tol if k in ("gu", "gr", "gphi") else F32))
         assert torch.equal(g[k], g2[k]), k
     return errs
 
@@ -108,6 +127,17 @@ def test_complex_large_phase_arguments():
     run_complex(cfg)
 
 
+def test_complex_bf16_streams():
+    """bf16 r, phi, u (pairs), gy and stream gradients; fp64 recurrence, fp32 parameter gradients."""
+    g = np.random.default_rng(43)
+    run_complex(synth.make_complex(B=2, H=3, M=64, L=300, seed=42, dtype="bf16"),
+                h0=g.standard_normal((2, 3, 64)) + 1j * g.standard_normal((2, 3, 64)))
+
+
+def test_complex_rtrl_bf16():
+    run_complex_rtrl(synth.make_complex(B=2, H=2, M=64, L=500, seed=44, dtype="bf16"))
+
+
 def test_complex_full_config():
     """B=16 H=8 M=64 L=2048 complex64, seed 0: every output compared element-wise."""
     run_complex(synth.make_complex(B=16, H=8, M=64, L=2048, seed=0))
@@ -121,20 +151,20 @@ def run_complex_rtrl(cfg, h0=None, ghl=None):
     and against the GPU reverse-mode (BPTT) gradients of the same loss."""
     ssm = _ssm()
     B, H, L, M = cfg["B"], cfg["H"], cfg["L"], cfg["M"]
-    t = {k: T(cfg[k]) for k in ("r", "phi", "lam", "theta", "u", "c")}
+    t = {k: S(cfg[k]) for k in ("r", "phi", "lam", "theta", "u", "c")}
     if h0 is not None:
         t["h0"] = T(h0.astype(np.complex64))
-    gyt = T(cfg["gy"])
+    gyt = S(cfg["gy"])
     glt = None if ghl is None else T(ghl.astype(np.complex64))
     g = ssm.complex_rtrl(gy=gyt, gh_last=glt, **t)
     g2 = ssm.complex_rtrl(gy=gyt, gh_last=glt, want_y=False, **t)
     bp = ssm.scan_bwd(ssm.SSM_COMPLEX_SHARED, gy=gyt, gh_last=glt, want=("glam", "gtheta"), **t)
     torch.cuda.synchronize()
-    kw = {k: cfg[k] for k in ("r", "phi", "lam", "theta", "u", "c")}
+    kw = _cplx_oracle_kw(cfg)
     h0c = None if h0 is None else h0.astype(np.complex64)
     o = oracle.complex_rtrl(**kw, h0=h0c, gy=cfg["gy"], ghlast=None if ghl is None else ghl.astype(np.complex64),
                             B=B, H=H, L=L, M=M)
-    assert_close("y", g["y"], o["y"], **F32)
+    assert_close("y", g["y"], o["y"], **(BF16 if cfg.get("dtype") == "bf16" else F32))
     for k in ("glam", "gtheta"):
         assert_close(k, g[k], o[k], **F32)
         assert_close(k + " vs bptt", g[k], bp[k].cpu().numpy().astype(np.float64), rtol=2e-4, atol=2e-5)
@@ -176,13 +206,6 @@ def test_complex_rtrl_full_config():
 # ---------------------------------------------------------------------------
 # PD
 # ---------------------------------------------------------------------------
-def S(a):
-    """A stream to the device: bf16 bit arrays (uint16) as bfloat16, else as is."""
-    if a.dtype == np.uint16:
-        return torch.from_numpy(np.ascontiguousarray(a).astype(np.int16)).view(torch.bfloat16).to(DEV)
-    return T(a)
-
-
 def run_pd(cfg, h0=None, ghl=None, use_sel=False):
     ssm = _ssm()
     B, H, L, N, K = cfg["B"], cfg["H"], cfg["L"], cfg["N"], cfg["K"]
