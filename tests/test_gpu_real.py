@@ -64,6 +64,28 @@ def test_real_chunk_lengths_with_state(chunk_len):
     run_real(cfg, h0=g.standard_normal((2, 24, 16)), ghl=g.standard_normal((2, 24, 16)), chunk_len=chunk_len)
 
 
+@pytest.mark.parametrize("chunk_len,L", [(64, 777), (128, 777), (128, 896), (128, 1024), (256, 777)])
+def test_real_checkpoints_are_chunk_states(chunk_len, L):
+    """ckpt[:, :, c] is the state entering chunk c: the oracle's final state of the first c*T steps
+    (at 128 steps the forward writes two checkpoints per 256-step tile)."""
+    ssm = _ssm()
+    cfg = synth.make_real(B=2, D=20, N=16, L=L, seed=11)
+    g = np.random.default_rng(12)
+    h0 = g.standard_normal((2, 20, 16)).astype(np.float32)
+    t = {k: _dev(cfg[k], "f32") for k in ("delta", "x", "Bm", "C", "A")}
+    f = ssm.scan_fwd(ssm.SSM_REAL_SELECTIVE, want_ckpt=True, chunk_len=chunk_len, h0=_dev(h0, "f32"), **t)
+    torch.cuda.synchronize()
+    ck = f["ckpt"].cpu().numpy()
+    nc = -(-L // chunk_len)
+    assert ck.shape == (2, 20, nc, 16)
+    np.testing.assert_array_equal(ck[:, :, 0], h0)
+    for c in range(1, nc):
+        Lc = c * chunk_len
+        _, hl = oracle.real_fwd(delta=cfg["delta"][:, :, :Lc], x=cfg["x"][:, :, :Lc], A=cfg["A"],
+                                Bm=cfg["Bm"][:, :Lc], C=cfg["C"][:, :Lc], h0=h0, B=2, D=20, L=Lc, N=16)
+        assert_close(f"ckpt[{c}]", torch.from_numpy(ck[:, :, c]), hl, **F32)
+
+
 @pytest.mark.parametrize("L", [1, 2, 3, 63, 64, 65, 255, 257, 1000])
 def test_real_ragged_lengths(L):
     run_real(synth.make_real(B=1, D=16, N=16, L=L, seed=L))
