@@ -6,10 +6,10 @@ of seeded synthetic inputs.  The headline workload is the Mamba-layer-shaped
 selective scan B=8 D=2048 N=16 L=4096 with bf16 streams, fp32 state and
 accumulation, chunk length 256; value = B*D*N*L / (time of forward+backward).
 The other workloads (impulse sensitivity at L=128000, with and without the
-step-size sensitivity, complex shared-control scan and its forward-mode
-gradients, PD scan with and without the straight-through selection gradient,
-dense-a/b scan at the Mamba-layer shape, the small fp32 case) are reported
-under "others" with the same fields.
+step-size sensitivity, 16 rows of the input Jacobian at that length, complex
+shared-control scan and its forward-mode gradients, PD scan with and without
+the straight-through selection gradient, dense-a/b scan at the Mamba-layer
+shape, the small fp32 case) are reported under "others" with the same fields.
 
 Inputs are resident in HBM before timing.  The timed region is K steps
 bracketed by torch.cuda.synchronize(); per-kernel durations come from HIP
@@ -186,6 +186,26 @@ def w_impulse(steps, warmup):
     byts = (2 * BDL + 2 * BLN + BDL) * 4 + (BDL + BLN + BDL) * 4  # forward: x, delta, B, C -> y; sens: delta, B -> s
     return dict(name="impulse", elements=BDL * N, ms=ms, kernels=profile_kernels(step, reps=2),
                 bytes_total=byts, config=dict(B=B, D=D, N=N, L=L, streams="f32", t_out=L - 1))
+
+
+def w_sens_rows(steps, warmup):
+    """The last 16 rows of the input Jacobian, dy[t]/dx for t = L-16 .. L-1, on the impulse workload,
+    B=1 D=1024 N=16 L=128000 fp32."""
+    import synth
+    import selective_state_space_chunked_amd as ssm
+    B, D, N, L, R = 1, 1024, 16, 128000, 16
+    cfg = synth.make_impulse(B=B, D=D, N=N, L=L, seed=0)
+    t = {k: to_dev(cfg[k]) for k in ("delta", "x", "Bm", "C", "A")}
+    s = ssm.sensitivity_rows(t_out0=L - R, rows=R, **t)
+
+    def step():
+        ssm.sensitivity_rows(t_out0=L - R, rows=R, out=s, **t)
+
+    ms = time_steps(step, max(3, steps // 4), max(1, warmup // 2))
+    BDL, BLN = B * D * L, B * L * N
+    byts = (BDL + BLN) * 4 + R * BDL * 4   # read delta, B; write R rows of s
+    return dict(name="sens-rows", elements=R * BDL * N, ms=ms, kernels=profile_kernels(step, reps=2),
+                bytes_total=byts, config=dict(B=B, D=D, N=N, L=L, rows=R, streams="f32", t_out0=L - R))
 
 
 def w_output_sens(steps, warmup):
@@ -478,12 +498,14 @@ def main():
     others = {}
     if not args.no_others:
         todo = [w.strip() for w in args.workloads.split(",") if w.strip()] or \
-            ["impulse", "output-sens", "complex", "complex-rtrl", "pd", "pd-ste", "dense", "real-small"]
+            ["impulse", "output-sens", "sens-rows", "complex", "complex-rtrl", "pd", "pd-ste", "dense", "real-small"]
         for w in todo:
             if w == "impulse":
                 others[w] = summarize(w_impulse(args.steps, args.warmup))
             elif w == "output-sens":
                 others[w] = summarize(w_output_sens(args.steps, args.warmup))
+            elif w == "sens-rows":
+                others[w] = summarize(w_sens_rows(args.steps, args.warmup))
             elif w == "complex":
                 others[w] = summarize(w_complex(args.steps, args.warmup))
             elif w == "complex-rtrl":

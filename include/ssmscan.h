@@ -100,6 +100,7 @@ extern "C" {
 #define SSM_OP_PD_BWD   4
 #define SSM_OP_COMPLEX_RTRL 5
 #define SSM_OP_OUTPUT_SENS  6
+#define SSM_OP_SENS_ROWS    7
 
 /*
  * Arguments of the diagonal scans.  Sizes: batch = B; channels = D (real) or
@@ -290,6 +291,26 @@ int ssm_complex_rtrl(const ssm_scan_args* args, const void* gy, const float* gh_
  * SSM_REAL_SELECTIVE only; workspace from ssm_workspace_bytes(SSM_OP_OUTPUT_SENS, ...). */
 int ssm_output_sensitivity(const ssm_scan_args* args, int64_t t_out, void* y, void* s_x, void* s_delta,
                            void* ws, size_t ws_bytes, void* stream);
+
+/* Rows of the input Jacobian of the selective scan (PGF page, abstract:
+ * sensitivities of outputs to inputs by reverse costate evolution, O(chunk)
+ * working memory).  For the R consecutive output steps tau_r = t_out0 + r:
+ *   s[r,b,d,t] = d y[b,d,tau_r] / d x[b,d,t]
+ *              = delta_t sum_n B_t[n] C_{tau_r}[n] prod_{t < u <= tau_r} a_u[n]  (t <= tau_r), 0 after,
+ * i.e. per channel the (R x L) block of the Jacobian.  One call costs one
+ * exp per (t, n) for all R rows: the product is split at t_out0 into the
+ * costate of row t_out0 and a per-row weight.  s[r] equals
+ * ssm_impulse_sensitivity's s at t_out = tau_r up to rounding.
+ * args: mode SSM_REAL_SELECTIVE, chunk_len 0 or 64 (64-step tiles); the step
+ * transform (delta_bias, delta_softplus) applies as in ssm_scan_fwd, and s is
+ * then still the sensitivity to x.  rows in [1, 16]; 0 <= t_out0 and
+ * t_out0 + rows <= L.  s: (rows,B,D,L) dtype, required, every element written.
+ * Workspace from ssm_workspace_bytes(SSM_OP_SENS_ROWS, ...) (sized for 16
+ * rows).  Errors: SSM_ERR_SHAPE for rows or t_out0 out of range,
+ * SSM_ERR_UNSUPPORTED for another mode or chunk_len, otherwise as for
+ * ssm_scan_fwd. */
+int ssm_sensitivity_rows(const ssm_scan_args* args, int64_t t_out0, int32_t rows, void* s,
+                         void* ws, size_t ws_bytes, void* stream);
 
 /* PD forward: selection (argmax of logits unless sel is given), scan, readout. */
 int pd_scan_fwd(const pd_scan_args* args, const pd_scan_fwd_out* out,

@@ -1,6 +1,7 @@
 """MI355X (gfx950) selective state-space scan: forward, backward, impulse
-sensitivity, forward-mode complex gradients and PD-transition scans behind
-the C ABI of include/ssmscan.h.
+sensitivity (one output row or a block of rows of the input Jacobian),
+forward-mode complex gradients and PD-transition scans behind the C ABI of
+include/ssmscan.h.
 
 The Python functions marshal torch tensors into the C ABI of libssmscan.so;
 all computation runs in the library's HIP kernels.
@@ -21,4 +22,5 @@ from .binding import (  # noqa: F401
     pd_scan_fwd,
     scan_bwd,
     scan_fwd,
+    sensitivity_rows,
 )

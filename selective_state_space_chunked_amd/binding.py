@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libssmscan.so")
 SSM_F32, SSM_BF16 = 0, 1
 SSM_REAL_SELECTIVE, SSM_REAL_DENSE, SSM_COMPLEX_SHARED = 0, 1, 2
 (SSM_OP_SCAN_FWD, SSM_OP_SCAN_BWD, SSM_OP_IMPULSE, SSM_OP_PD_FWD, SSM_OP_PD_BWD, SSM_OP_COMPLEX_RTRL,
- SSM_OP_OUTPUT_SENS) = range(7)
+ SSM_OP_OUTPUT_SENS, SSM_OP_SENS_ROWS) = range(8)
 
 _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -82,6 +82,8 @@ def lib():
                                    _vp, ctypes.c_size_t, _vp]
         L.ssm_impulse_sensitivity.argtypes = [ctypes.POINTER(ScanArgs), _i64, _vp, _vp, _vp, ctypes.c_size_t, _vp]
         L.ssm_output_sensitivity.argtypes = [ctypes.POINTER(ScanArgs), _i64, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+        L.ssm_sensitivity_rows.argtypes = [ctypes.POINTER(ScanArgs), _i64, ctypes.c_int32, _vp, _vp, ctypes.c_size_t,
+                                           _vp]
         L.ssm_complex_rtrl.argtypes = [ctypes.POINTER(ScanArgs), _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
         L.pd_scan_fwd.argtypes = [ctypes.POINTER(PDArgs), ctypes.POINTER(PDFwdOut), _vp, ctypes.c_size_t, _vp]
         L.pd_scan_bwd.argtypes = [ctypes.POINTER(PDArgs), ctypes.POINTER(PDBwdIn), ctypes.POINTER(PDGrads),
@@ -303,6 +305,17 @@ def output_sensitivity(*, t_out=-1, want_y=False, want_s_x=True, chunk_len=0, ou
     _check(lib().ssm_output_sensitivity(ctypes.byref(args), int(t_out), _ptr(out.get("y")), _ptr(out.get("s_x")),
                                         _ptr(out["s_delta"]), _ptr(ws), nws, _stream(dev)))
     return out
+
+
+def sensitivity_rows(*, t_out0, rows, out=None, **tensors):
+    """s[r,b,d,t] = d y[b,d,t_out0+r] / d x[b,d,t] for r < rows (rows 1..16) of a selective real scan."""
+    args, (Bsz, D, L, N), dev = _scan_args(SSM_REAL_SELECTIVE, **tensors)
+    dt = tensors["delta"].dtype
+    s = out if out is not None else torch.empty((int(rows), Bsz, D, L), dtype=dt, device=dev)
+    ws, nws = _workspace(SSM_OP_SENS_ROWS, ctypes.byref(args), dev)
+    _check(lib().ssm_sensitivity_rows(ctypes.byref(args), int(t_out0), int(rows), _ptr(s), _ptr(ws), nws,
+                                      _stream(dev)))
+    return s
 
 
 def complex_rtrl(*, gy, gh_last=None, want_y=True, chunk_len=0, out=None, **tensors):

@@ -137,7 +137,8 @@ struct ScanPlan {
     size_t esz;    // bytes per streamed element
 };
 
-int validate_scan_args(const ssm_scan_args* a, ScanPlan* pl) {
+// sel_default_T: the selective mode's checkpoint interval when chunk_len is 0
+int validate_scan_args(const ssm_scan_args* a, ScanPlan* pl, int sel_default_T = 256) {
     if (!a) return fail(SSM_ERR_NULL, "args is NULL");
     pl->mode = a->mode;
     pl->dtype = a->dtype;
@@ -158,7 +159,7 @@ int validate_scan_args(const ssm_scan_args* a, ScanPlan* pl) {
     pl->esz = a->dtype == SSM_BF16 ? 2 : 4;
     int T = (int)a->chunk_len;
     if (a->mode == SSM_REAL_SELECTIVE) {
-        if (T == 0) T = 256;
+        if (T == 0) T = sel_default_T;
         if (T != 64 && T != 128 && T != 256)
             return fail(SSM_ERR_UNSUPPORTED, "chunk_len %d not supported (64, 128 or 256)", T);
         pl->kpl = T / 16;
@@ -538,6 +539,58 @@ int impulse_impl(const ssm_scan_args* a, int64_t t_out, void* y, void* s, void* 
     return ok();
 }
 
+// ---------------------------------------------------------------------------
+// ssm_sensitivity_rows
+// ---------------------------------------------------------------------------
+int sens_rows_impl(const ssm_scan_args* a, int64_t t0, int32_t rows, void* s, void* ws, size_t ws_bytes,
+                   hipStream_t st, size_t* need_only) {
+    ScanPlan p;
+    int rc = validate_scan_args(a, &p, 64);
+    if (rc) return rc;
+    if (p.mode != SSM_REAL_SELECTIVE)
+        return fail(SSM_ERR_UNSUPPORTED, "ssm_sensitivity_rows supports SSM_REAL_SELECTIVE only");
+    if (p.T != 64) return fail(SSM_ERR_UNSUPPORTED, "ssm_sensitivity_rows runs 64-step tiles (chunk_len 0 or 64)");
+    const int R = need_only ? kSensRowsMax : rows;
+    if (!need_only) {
+        if (R < 1 || R > kSensRowsMax)
+            return fail(SSM_ERR_SHAPE, "rows %d outside [1, %d]", (int)R, kSensRowsMax);
+        if (t0 < 0 || t0 + R > p.L)
+            return fail(SSM_ERR_SHAPE, "output rows [%lld, %lld) outside [0, L=%lld)", (long long)t0,
+                        (long long)(t0 + R), (long long)p.L);
+        if (!s) return fail(SSM_ERR_NULL, "s is NULL");
+        if ((rc = check_align(s, p.esz, "s"))) return rc;
+        const size_t sb = (size_t)R * p.B * p.D * p.L * p.esz;
+        if ((rc = check_overlaps(scan_inputs(a, p), {{s, sb, "s"}}))) return rc;
+    }
+    const size_t BD = (size_t)p.B * p.D;
+    auto layout = [&](Carve& cv, float** tsum, double** send, float** w) {
+        *tsum = cv.take<float>(BD * p.nchunks);
+        *send = cv.take<double>(BD * p.nchunks);
+        *w = cv.take<float>(BD * kSensRowsMax * p.N);
+    };
+    Carve cv(nullptr);
+    float *tsum, *w;
+    double* send;
+    layout(cv, &tsum, &send, &w);
+    if (need_only) { *need_only = cv.off; return ok(); }
+    if ((rc = check_ws(ws, ws_bytes, cv.off))) return rc;
+    Carve real(ws);
+    layout(real, &tsum, &send, &w);
+    const StepXform sx{a->delta_bias, a->delta_softplus};
+    SSM_LAUNCH(launch_tile_dsum(a->delta, sx, tsum, (int)p.B, (int)p.D, (int)p.L, p.nchunks, p.kpl, p.dtype, st),
+               "tile sums");
+    SSM_LAUNCH(launch_sens_suffix(a->delta, sx, tsum, send, (int)p.B, (int)p.D, (int)p.L, p.nchunks, p.T, (int)t0,
+                                  p.dtype, st), "suffix sums");
+    SensRowsParams q{};
+    q.delta = a->delta; q.A = a->A; q.Bm = a->Bm; q.C = a->C; q.send = send; q.w = w; q.s = s; q.stepf = sx;
+    q.B = (int)p.B; q.D = (int)p.D; q.L = (int)p.L; q.N = (int)p.N; q.ntiles = p.nchunks; q.t0 = (int)t0; q.R = R;
+    q.vec = sel_vec(p, {s});
+    SSM_LAUNCH(launch_sens_rows_edge(q, false, p.dtype, st), "sensitivity rows (weights)");
+    SSM_LAUNCH(launch_sens_rows(q, p.dtype, st), "sensitivity rows");
+    SSM_LAUNCH(launch_sens_rows_edge(q, true, p.dtype, st), "sensitivity rows (tail)");
+    return ok();
+}
+
 }  // namespace
 
 #include "api_modes.inc"
@@ -561,6 +614,8 @@ int ssm_workspace_bytes(int op, const void* args, size_t* out_bytes) {
                                 out_bytes);
         case SSM_OP_PD_FWD: return pd_fwd_impl((const pd_scan_args*)args, nullptr, nullptr, 0, nullptr, out_bytes);
         case SSM_OP_PD_BWD: return pd_bwd_impl((const pd_scan_args*)args, nullptr, nullptr, nullptr, 0, nullptr, out_bytes);
+        case SSM_OP_SENS_ROWS:
+            return sens_rows_impl((const ssm_scan_args*)args, 0, 0, nullptr, nullptr, 0, nullptr, out_bytes);
         case SSM_OP_COMPLEX_RTRL:
             return rtrl_impl((const ssm_scan_args*)args, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0, nullptr, out_bytes);
         default: return fail(SSM_ERR_UNSUPPORTED, "unknown op %d", op);
@@ -581,6 +636,10 @@ int ssm_impulse_sensitivity(const ssm_scan_args* args, int64_t t_out, void* y, v
 int ssm_output_sensitivity(const ssm_scan_args* args, int64_t t_out, void* y, void* s_x, void* s_delta, void* ws,
                            size_t ws_bytes, void* stream) {
     return impulse_impl(args, t_out, y, s_x, s_delta, true, ws, ws_bytes, (hipStream_t)stream, nullptr);
+}
+int ssm_sensitivity_rows(const ssm_scan_args* args, int64_t t_out0, int32_t rows, void* s, void* ws,
+                         size_t ws_bytes, void* stream) {
+    return sens_rows_impl(args, t_out0, rows, s, ws, ws_bytes, (hipStream_t)stream, nullptr);
 }
 int ssm_complex_rtrl(const ssm_scan_args* args, const void* gy, const float* gh_last, void* y, float* glam,
                      float* gtheta, void* ws, size_t ws_bytes, void* stream) {

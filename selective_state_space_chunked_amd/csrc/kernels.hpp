@@ -49,6 +49,17 @@ struct SensParams {
     int B, D, L, N, ntiles, t_out, vec;
 };
 
+// Rows r = 0..R-1 of the input Jacobian, s[r] = d y[t0 + r] / d x (R <= kSensRowsMax).
+constexpr int kSensRowsMax = 16;
+struct SensRowsParams {
+    const void* delta; const float* A; const void* Bm; const void* C;
+    const double* send;     // (B,D,ntiles) sum of delta over later steps up to t0 (64-step tiles)
+    float* w;               // (B,D,R,N) C_{t0+r}[n] * prod_{t0 < s <= t0+r} a_s[n]
+    void* s;                // (R,B,D,L)
+    StepXform stepf;
+    int B, D, L, N, ntiles, t0, R, vec;
+};
+
 hipError_t launch_sel_fwd(const SelFwdParams& p, int dtype, int kpl, bool summary, hipStream_t st);
 hipError_t launch_sel_bwd(const SelBwdParams& p, int dtype, int kpl, bool summary, hipStream_t st);
 int sel_bwd_rows();  // channels per backward workgroup (one gB/gC partial per block)
@@ -65,6 +76,10 @@ hipError_t launch_sens_suffix(const void* delta, StepXform stepf, const float* t
 hipError_t launch_tile_dsum(const void* delta, StepXform stepf, float* tile_dsum, int B, int D, int L, int ntiles,
                             int kpl, int dtype, hipStream_t st);
 hipError_t launch_sens(const SensParams& p, int dtype, int kpl, hipStream_t st);
+// rows of the input Jacobian: the weights (tail = false) before the main pass,
+// the steps in (t0, t0 + R) (tail = true) after it
+hipError_t launch_sens_rows_edge(const SensRowsParams& p, bool tail, int dtype, hipStream_t st);
+hipError_t launch_sens_rows(const SensRowsParams& p, int dtype, hipStream_t st);
 
 // ------------------------------- real, dense -------------------------------
 struct DenseParams {

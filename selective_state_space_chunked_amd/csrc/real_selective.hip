@@ -878,6 +878,165 @@ __global__ __launch_bounds__(256) void sens_kernel(SensParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// Rows of the input Jacobian (PGF page, abstract: sensitivities of the outputs
+// to the inputs by reverse evolution of the costate).  For the output steps
+// tau_r = t0 + r, r < R:
+//   s[r, t] = delta_t sum_n B_t[n] C_{tau_r}[n] prod_{t < u <= tau_r} a_u[n]    (t <= tau_r), 0 after.
+// For t <= t0 the product splits at t0: prod_{t < u <= t0} a_u[n] = 2^(A2[n] S_t)
+// with S_t the sum of delta over (t, t0] (the costate of row t0), and
+//   w_r[n] = C_{tau_r}[n] prod_{t0 < u <= tau_r} a_u[n],
+// so s[r, t] = delta_t sum_n (B_t[n] 2^(A2[n] S_t)) w_r[n]: one exp per (t, n)
+// for all R rows.  Both factors are products of a's, as in the direct form.
+// The few steps t in (t0, t0 + R) use the direct form in a second kernel.
+// Output layout (R, B, D, L): row r is a (B, D, L) slab; every store of a
+// 16-lane row covers 64 consecutive steps of one row.
+// ---------------------------------------------------------------------------
+
+// One thread per (sequence, row r).  D_k = sum of delta over (t0, t0 + k].
+// TAIL = false: w_r into the workspace (before the main pass); TAIL = true:
+// the entries s[r, t] for t in (t0, t0 + R) by the direct form (after it).
+template <typename T, bool TAIL>
+__global__ __launch_bounds__(256) void sens_rows_edge_kernel(SensRowsParams p) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= p.B * p.D * p.R) return;
+    const int R = p.R, r = i % R, sq = i / R, d = sq % p.D, b = sq / p.D;
+    const int N = p.N, L = p.L, t0 = p.t0, tau = t0 + r;
+    const T* delta = (const T*)p.delta + (size_t)sq * L;
+    const T* Bm = (const T*)p.Bm + (size_t)b * L * N;
+    const T* C = (const T*)p.C + (size_t)b * L * N;
+    const float* A = p.A + (size_t)d * N;
+    const float bias = p.stepf.bias ? p.stepf.bias[d] : 0.0f;
+    auto step = [&](int t) { return step_xform(to_f32(delta[t]), bias, p.stepf.softplus); };
+    float Dr = 0.0f;
+    for (int k = 1; k <= r; ++k) Dr += step(t0 + k);
+    if (!TAIL) {
+        float* w = p.w + ((size_t)sq * R + r) * N;
+        for (int n = 0; n < N; ++n) w[n] = to_f32(C[(size_t)tau * N + n]) * __builtin_amdgcn_exp2f(A[n] * kLog2e * Dr);
+        return;
+    }
+    T* out = (T*)p.s + ((size_t)r * p.B * p.D + sq) * L;
+    float Dk = 0.0f;
+    for (int k = 1; k < R; ++k) {
+        const int t = t0 + k;
+        float v = 0.0f;
+        if (k <= r) {
+            const float dt = step(t);
+            Dk += dt;
+            for (int n = 0; n < N; ++n)
+                v = fmaf(to_f32(Bm[(size_t)t * N + n]) * to_f32(C[(size_t)tau * N + n]),
+                         __builtin_amdgcn_exp2f(A[n] * kLog2e * (Dr - Dk)), v);
+            v *= dt;
+        }
+        out[t] = from_f32<T>(v);
+    }
+}
+
+// Main pass: 64-step tiles, 16 sequences per workgroup, lane l owns 4 steps;
+// per state n one exp per step and kSensRowsMax multiply-adds against the row
+// weights (zero past R).  Every step gets a value: step sizes past t0 load as
+// 0, so steps t > t0 come out 0, and the tail kernel then overwrites
+// (t0, t0 + R).
+template <typename T, int NT>
+__global__ __launch_bounds__(256) void sens_rows_kernel(SensRowsParams p) {
+    constexpr int KPL = 4, RM = kSensRowsMax;
+    using Gm = TileGeom<KPL>;
+    constexpr int TILE = Gm::TILE;
+    __shared__ __align__(16) float sB[16 * Gm::LDSW];
+    __shared__ __align__(16) float sW[16 * 16 * RM];    // [row][n][r]
+    const int tid = threadIdx.x, lane = tid & 15, row = tid >> 4;
+    const int b = blockIdx.y;
+    const int d = blockIdx.x * 16 + row;
+    const bool act = d < p.D;
+    const int dc = act ? d : p.D - 1;
+    const int N = NT ? NT : p.N, L = p.L, R = p.R, t0 = p.t0;
+    const size_t seq = (size_t)b * p.D + dc;
+    const size_t plane = (size_t)p.B * p.D * L;   // elements per output row
+    const bool vec = p.vec != 0;
+    for (int e = tid; e < 16 * 16 * RM; e += 256) {
+        const int rw = e / (16 * RM), n = (e / RM) % 16, r = e % RM;
+        const int dd = min(blockIdx.x * 16 + rw, p.D - 1);
+        sW[e] = (n < N && r < R) ? p.w[(((size_t)b * p.D + dd) * R + r) * N + n] : 0.0f;
+    }
+    float A2 = 0.0f;
+    if (lane < N) A2 = p.A[(size_t)dc * N + lane] * kLog2e;
+    const int tile0 = blockIdx.z * kSensTiles;
+    const int tile1 = min(tile0 + kSensTiles, p.ntiles);
+    for (int tile = tile0; tile < tile1; ++tile) {
+        const int ts = tile * TILE;
+        const int tl = ts + lane * KPL;
+        T* o = (T*)p.s + seq * L + tl;   // this lane's first step in row 0
+        if (ts > t0) {   // tiles after t0 (uniform; later tiles too): zeros
+            if (act && tl < L) {
+                const float z[KPL] = {};
+                for (int r = 0; r < R; ++r) store_run<KPL>(o + r * plane, z, vec, L - tl);
+            }
+            continue;
+        }
+        __syncthreads();   // sW ready (first tile) / the previous tile's B no longer read
+        if constexpr (NT == 16) {
+            const int tt = tid >> 2, q = tid & 3;   // 64 steps x 4 quarters of 4 states
+            const int t = ts + tt;
+            float v[4];
+            if (t < L) load_run<4>((const T*)p.Bm + ((size_t)b * L + t) * 16 + 4 * q, v, true);
+            else v[0] = v[1] = v[2] = v[3] = 0.0f;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) sB[Gm::idx(4 * q + k, tt)] = v[k];
+        } else {
+            for (int e = tid; e < TILE * N; e += 256) {
+                const int tt = e / N, n = e - tt * N, t = ts + tt;
+                sB[Gm::idx(n, tt)] = t < L ? to_f32(((const T*)p.Bm)[((size_t)b * L + t) * N + n]) : 0.0f;
+            }
+        }
+        __syncthreads();
+        float dl[KPL];
+        load_steps<T, KPL>((const T*)p.delta + seq * L + tl, dl, min(L, t0 + 1) - tl, false, p.stepf, dc);
+        // S_j = sum of delta over steps after j up to t0
+        float lsum = 0.0f;
+#pragma unroll
+        for (int j = 0; j < KPL; ++j) lsum += dl[j];
+        const float base = (float)p.send[seq * p.ntiles + tile] + row_excl_sum_down(lsum);
+        float S[KPL];
+        {
+            float run = 0.0f;
+#pragma unroll
+            for (int j = KPL - 1; j >= 0; --j) {
+                S[j] = base + run;
+                run += dl[j];
+            }
+        }
+        float acc[RM][KPL];
+#pragma unroll
+        for (int r = 0; r < RM; ++r)
+#pragma unroll
+            for (int j = 0; j < KPL; ++j) acc[r][j] = 0.0f;
+        auto body = [&](auto st) {
+            const float A2n = st.bc(A2);
+            float m[KPL];
+            read_run<KPL>(sB + st.n * Gm::LDSW + lane * Gm::SEG, m);
+#pragma unroll
+            for (int j = 0; j < KPL; ++j) m[j] *= __builtin_amdgcn_exp2f(A2n * S[j]);
+            float wv[RM];
+            read_run<RM>(sW + (row * 16 + st.n) * RM, wv);
+#pragma unroll
+            for (int r = 0; r < RM; ++r)
+#pragma unroll
+                for (int j = 0; j < KPL; ++j) acc[r][j] = fmaf(m[j], wv[r], acc[r][j]);
+        };
+        for_states<NT>(N, body);
+        if (act && tl < L) {
+#pragma unroll
+            for (int r = 0; r < RM; ++r)   // predicated, not exited: acc stays in registers
+                if (r < R) {
+                    float v[KPL];
+#pragma unroll
+                    for (int j = 0; j < KPL; ++j) v[j] = dl[j] * acc[r][j];
+                    store_run<KPL>(o + r * plane, v, vec, L - tl);
+                }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
 #define SSM_DISPATCH_KPL(kpl, ...)                         \
@@ -984,6 +1143,31 @@ hipError_t launch_sens(const SensParams& p, int dtype, int kpl, hipStream_t st) 
     } else {
         if (n16) { SSM_DISPATCH_KPL(kpl, sens_kernel<bf16_t, K_, 16><<<grid, 256, 0, st>>>(p)) }
         else { SSM_DISPATCH_KPL(kpl, sens_kernel<bf16_t, K_, 0><<<grid, 256, 0, st>>>(p)) }
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_sens_rows_edge(const SensRowsParams& p, bool tail, int dtype, hipStream_t st) {
+    const int total = p.B * p.D * p.R, blocks = (total + 255) / 256;
+    if (dtype == 0) {
+        if (tail) sens_rows_edge_kernel<float, true><<<blocks, 256, 0, st>>>(p);
+        else sens_rows_edge_kernel<float, false><<<blocks, 256, 0, st>>>(p);
+    } else {
+        if (tail) sens_rows_edge_kernel<bf16_t, true><<<blocks, 256, 0, st>>>(p);
+        else sens_rows_edge_kernel<bf16_t, false><<<blocks, 256, 0, st>>>(p);
+    }
+    return hipGetLastError();
+}
+hipError_t launch_sens_rows(const SensRowsParams& p, int dtype, hipStream_t st) {
+    if (p.R < 1 || p.R > kSensRowsMax || p.N > 16) return hipErrorInvalidValue;
+    dim3 grid((p.D + 15) / 16, p.B, (p.ntiles + kSensTiles - 1) / kSensTiles);
+    const bool n16 = p.N == 16;
+    if (dtype == 0) {
+        if (n16) sens_rows_kernel<float, 16><<<grid, 256, 0, st>>>(p);
+        else sens_rows_kernel<float, 0><<<grid, 256, 0, st>>>(p);
+    } else {
+        if (n16) sens_rows_kernel<bf16_t, 16><<<grid, 256, 0, st>>>(p);
+        else sens_rows_kernel<bf16_t, 0><<<grid, 256, 0, st>>>(p);
     }
     return hipGetLastError();
 }

@@ -22,7 +22,8 @@ def header_functions():
 def test_exports_every_declared_function():
     names = header_functions()
     assert {"ssm_scan_fwd", "ssm_scan_bwd", "ssm_impulse_sensitivity", "pd_scan_fwd", "pd_scan_bwd",
-            "ssm_complex_rtrl", "ssm_output_sensitivity", "ssm_workspace_bytes"} <= set(names)
+            "ssm_complex_rtrl", "ssm_output_sensitivity", "ssm_sensitivity_rows",
+            "ssm_workspace_bytes"} <= set(names)
     lib = B.lib()
     missing = [n for n in names if not hasattr(lib, n)]
     assert not missing, missing
@@ -38,6 +39,7 @@ def test_header_constants_match_binding():
     assert consts["SSM_OP_PD_BWD"] == B.SSM_OP_PD_BWD
     assert consts["SSM_OP_COMPLEX_RTRL"] == B.SSM_OP_COMPLEX_RTRL
     assert consts["SSM_OP_OUTPUT_SENS"] == B.SSM_OP_OUTPUT_SENS
+    assert consts["SSM_OP_SENS_ROWS"] == B.SSM_OP_SENS_ROWS
     assert B.lib().ssm_abi_version() == consts["SSM_ABI_VERSION"]
 
 
@@ -234,6 +236,31 @@ def test_output_sensitivity_host_checks():
     assert rc == status("SSM_ERR_WORKSPACE")
     rc, _ = ws_bytes(B.SSM_OP_OUTPUT_SENS, cplx_args())
     assert rc == status("SSM_ERR_UNSUPPORTED")
+
+
+def test_sensitivity_rows_host_checks():
+    """Rows 1..16 inside [0, L), s required and disjoint from the inputs, 64-step tiles, selective mode only."""
+    L = B.lib()
+    rc, n1 = ws_bytes(B.SSM_OP_SENS_ROWS, sel_args(length=4096))
+    assert rc == 0, L.ssm_last_error_detail()
+    _, n2 = ws_bytes(B.SSM_OP_SENS_ROWS, sel_args(length=8192))
+    assert n2 - n1 >= 2 * 32 * 64 * 12   # one float and one double per 64-step tile and channel
+    for over in ({"chunk_len": 128}, {"chunk_len": 256}):
+        rc, _ = ws_bytes(B.SSM_OP_SENS_ROWS, sel_args(**over))
+        assert rc == status("SSM_ERR_UNSUPPORTED")
+    rc, _ = ws_bytes(B.SSM_OP_SENS_ROWS, cplx_args())
+    assert rc == status("SSM_ERR_UNSUPPORTED")
+    a = sel_args()
+    for t0, rows in ((0, 0), (0, 17), (-1, 4), (997, 4), (999, 2)):
+        rc = L.ssm_sensitivity_rows(ctypes.byref(a), t0, rows, FAKE * 64, None, 0, None)
+        assert rc == status("SSM_ERR_SHAPE"), (t0, rows)
+    rc = L.ssm_sensitivity_rows(ctypes.byref(a), 10, 4, None, None, 0, None)
+    assert rc == status("SSM_ERR_NULL")
+    rc = L.ssm_sensitivity_rows(ctypes.byref(a), 10, 4, FAKE + 8, None, 0, None)   # inside delta
+    assert rc == status("SSM_ERR_LAYOUT")
+    for t0, rows in ((0, 1), (996, 4), (984, 16)):
+        rc = L.ssm_sensitivity_rows(ctypes.byref(a), t0, rows, FAKE * 64, None, 0, None)
+        assert rc == status("SSM_ERR_WORKSPACE"), (t0, rows)
 
 
 def test_step_size_transform_selective_only():

@@ -164,6 +164,68 @@ def test_impulse_sensitivity_variants(dt, N, chunk_len, L, t_out):
     assert_close("y", out["y"], y, **tol)
 
 
+@pytest.mark.parametrize("dt,N,L,t0,rows", [
+    ("f32", 16, 777, 0, 1),       # the first output only
+    ("f32", 16, 777, 100, 16),    # 16 rows inside a 64-step tile and across its end
+    ("f32", 16, 777, 761, 16),    # the last 16 outputs, ragged last tile
+    ("f32", 5, 600, 250, 7),      # generic state count
+    ("bf16", 16, 1024, 511, 16),  # bf16 streams, rows across a tile boundary
+    ("bf16", 7, 300, 40, 3),
+])
+def test_sensitivity_rows(dt, N, L, t0, rows):
+    """Rows t0 .. t0+rows-1 of the input Jacobian against the oracle's impulse sensitivity of each row."""
+    ssm = _ssm()
+    cfg = synth.make_real(B=2, D=20, N=N, L=L, dtype=dt, seed=80 + N + L + rows)
+    t = {k: _dev(cfg[k], dt) for k in ("delta", "x", "Bm", "C")}
+    t["A"] = _dev(cfg["A"], "f32")
+    s = ssm.sensitivity_rows(t_out0=t0, rows=rows, **t)
+    torch.cuda.synchronize()
+    assert s.shape == (rows, 2, 20, L)
+    kw = dict(delta=cfg["delta"], A=cfg["A"], Bm=cfg["Bm"], C=cfg["C"], B=2, D=20, L=L, N=N)
+    tol = BF16 if dt == "bf16" else F32
+    for r in range(rows):
+        assert_close(f"s[{r}]", s[r], oracle.impulse_sens(**kw, t_out=t0 + r), **tol)
+
+
+@pytest.mark.parametrize("softplus,with_bias", [(True, True), (True, False), (False, True)])
+def test_sensitivity_rows_projection_output(softplus, with_bias):
+    """Rows of the Jacobian with the step sizes taken from the projection output (bias, softplus)."""
+    ssm = _ssm()
+    L = 500
+    cfg = synth.make_real(B=1, D=24, N=16, L=L, seed=90, projection_output=True)
+    if not softplus:   # keep the step sizes positive
+        pos = oracle.step_sizes(cfg["delta"], cfg["delta_bias"], softplus=True)
+        cfg["delta"] = (pos - cfg["delta_bias"][None, :, None]).astype(np.float32)
+    bias = cfg["delta_bias"] if with_bias else None
+    t = {k: _dev(cfg[k], "f32") for k in ("delta", "x", "Bm", "C", "A")}
+    if with_bias:
+        t["delta_bias"] = _dev(bias, "f32")
+    t["delta_softplus"] = softplus
+    s = ssm.sensitivity_rows(t_out0=300, rows=12, **t)
+    torch.cuda.synchronize()
+    dl = oracle.step_sizes(cfg["delta"], bias, softplus=softplus)
+    kw = dict(delta=dl, A=cfg["A"], Bm=cfg["Bm"], C=cfg["C"], B=1, D=24, L=L, N=16)
+    for r in range(12):
+        assert_close(f"s[{r}]", s[r], oracle.impulse_sens(**kw, t_out=300 + r), **F32)
+
+
+def test_sensitivity_rows_impulse_config():
+    """The impulse workload's inputs at full length (B=1 D=1024 N=16 L=128000), the last 16 outputs;
+    sampled channels against the oracle, every channel against the single-row call."""
+    ssm = _ssm()
+    L, D = 128000, 1024
+    cfg = synth.make_impulse(B=1, D=D, N=16, L=L, seed=0)
+    t = {k: _dev(cfg[k], "f32") for k in ("delta", "x", "Bm", "C", "A")}
+    s = ssm.sensitivity_rows(t_out0=L - 16, rows=16, **t)
+    one = ssm.impulse_sensitivity(t_out=L - 16, want_y=False, **t)["s"]
+    torch.cuda.synchronize()
+    assert_close("row 0 vs single-row call", s[0], one.cpu().numpy().astype(np.float64), rtol=1e-4, atol=1e-6)
+    for d in (0, 517, 1023):
+        kw = dict(delta=cfg["delta"][:, d:d + 1], A=cfg["A"][d:d + 1], Bm=cfg["Bm"], C=cfg["C"], B=1, D=1, L=L, N=16)
+        for r in (0, 7, 15):
+            assert_close(f"s[{r}] d={d}", s[r, :, d:d + 1], oracle.impulse_sens(**kw, t_out=L - 16 + r), **F32)
+
+
 @pytest.mark.parametrize("dt,N,chunk_len,L,t_out,h0", [
     ("f32", 16, 256, 1300, -1, True),    # ragged last tile, t_out at the end, nonzero h0
     ("f32", 16, 256, 3000, 1777, False),  # t_out inside a tile, zero tail after it
