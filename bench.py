@@ -58,19 +58,21 @@ FLOPS_PER_ELEMENT = {"selective forward": 7, "selective backward": 17}
 # unchanged (profiles/selective_mamba_layer_fwd_bwd.md holds the run).
 MEASURED_TRAFFIC = {
     "selective backward": {"read_bytes": 509.9e6, "written_bytes": 541.4e6,
-                           "sources_sha256": "7376ed6c438c56e782da00b1ec51cd5438ccd92b55ef5eaea5b2d566c6d91075"},
+                           "sources_sha256": "2888ceea2c8defc157be1499a377840fdf02c892395fb02acd0e4ac3aed841dc"},
 }
-TRAFFIC_SOURCES = ("real_selective.hip", "common.hpp")
+# (file, marker where the hashed text ends; None = whole file)
+TRAFFIC_SOURCES = (("real_selective.hip", "// segment combines"), ("common.hpp", None))
 
 
 def kernel_sources_sha256():
-    """SHA-256 of what the selective backward is built from: its source file, the shared device helpers and
-    its parameter struct (the other modes' structs in kernels.hpp do not change it)."""
+    """SHA-256 of what the selective backward is built from: the part of its source file up to and including
+    the backward kernel (constants, helpers, the kernel itself), the shared device helpers and its parameter
+    struct (later kernels in the file and the other modes' structs in kernels.hpp do not change it)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "selective_state_space_chunked_amd", "csrc")
-    for f in TRAFFIC_SOURCES:
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(fh.read())
+    for f, end in TRAFFIC_SOURCES:
+        text = open(os.path.join(csrc, f)).read()
+        h.update(text[:text.index(end)].encode() if end else text.encode())
     hdr = open(os.path.join(csrc, "kernels.hpp")).read()
     for struct in ("struct StepXform {", "struct SelBwdParams {"):
         i = hdr.index(struct)

@@ -47,6 +47,7 @@ struct SensParams {
     void* s_delta;          // nullable d y[t_out] / d delta
     StepXform stepf;
     int B, D, L, N, ntiles, t_out, vec;
+    int tiles_per_wg;       // set by the launcher: grid.z stays within its limit for any L
 };
 
 // Rows r = 0..R-1 of the input Jacobian, s[r] = d y[t0 + r] / d x (R <= kSensRowsMax).
@@ -58,6 +59,7 @@ struct SensRowsParams {
     void* s;                // (R,B,D,L)
     StepXform stepf;
     int B, D, L, N, ntiles, t0, R, vec;
+    int tiles_per_wg;       // set by the launcher: grid.z stays within its limit for any L
 };
 
 hipError_t launch_sel_fwd(const SelFwdParams& p, int dtype, int kpl, bool summary, hipStream_t st);

@@ -22,6 +22,8 @@
 // B_t and C_t are shared by all 16 rows and staged once per tile in LDS,
 // transposed to [n][t] with 4 floats of padding after every lane's run so the
 // 16-byte LDS reads of a row hit distinct banks.
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -659,17 +661,19 @@ template <typename T, int KPL>
 __global__ void tile_dsum_kernel(const T* __restrict__ delta, StepXform stepf, float* __restrict__ out, int B,
                                  int D, int L, int ntiles) {
     const int lane = threadIdx.x & 15, row = threadIdx.x >> 4;
-    const int d = blockIdx.x * 16 + row, b = blockIdx.y, tile = blockIdx.z;
+    const int d = blockIdx.x * 16 + row, b = blockIdx.y;
     const bool act = d < D;
     const int dc = act ? d : D - 1;
-    const int tl = tile * 16 * KPL + lane * KPL;
-    float v[KPL];
-    load_steps<T, KPL>(delta + ((size_t)b * D + dc) * L + tl, v, L - tl, false, stepf, dc);
-    float s = 0.0f;
+    for (int tile = blockIdx.z; tile < ntiles; tile += gridDim.z) {   // grid.z is capped at 65535
+        const int tl = tile * 16 * KPL + lane * KPL;
+        float v[KPL];
+        load_steps<T, KPL>(delta + ((size_t)b * D + dc) * L + tl, v, L - tl, false, stepf, dc);
+        float s = 0.0f;
 #pragma unroll
-    for (int j = 0; j < KPL; ++j) s += v[j];
-    s = row_sum(s);
-    if (act && lane == 0) out[((size_t)b * D + dc) * ntiles + tile] = s;
+        for (int j = 0; j < KPL; ++j) s += v[j];
+        s = row_sum(s);
+        if (act && lane == 0) out[((size_t)b * D + dc) * ntiles + tile] = s;
+    }
 }
 
 // send[s, k] = sum of delta over the steps of tiles after k, up to t_out, in
@@ -745,8 +749,8 @@ __global__ __launch_bounds__(256) void sens_kernel(SensParams p) {
     const int dc = act ? d : p.D - 1;
     const int N = NT ? NT : p.N, L = p.L;
     const size_t seq = (size_t)b * p.D + dc;
-    const int tile0 = blockIdx.z * kSensTiles;
-    const int tile1 = min(tile0 + kSensTiles, p.ntiles);
+    const int tile0 = blockIdx.z * p.tiles_per_wg;
+    const int tile1 = min(tile0 + p.tiles_per_wg, p.ntiles);
     const T* Bm = (const T*)p.Bm;
     const bool vec = p.vec != 0;
     if (tid < N) sCout[tid] = to_f32(((const T*)p.C)[((size_t)b * L + p.t_out) * N + tid]);
@@ -959,8 +963,8 @@ __global__ __launch_bounds__(256) void sens_rows_kernel(SensRowsParams p) {
     }
     float A2 = 0.0f;
     if (lane < N) A2 = p.A[(size_t)dc * N + lane] * kLog2e;
-    const int tile0 = blockIdx.z * kSensTiles;
-    const int tile1 = min(tile0 + kSensTiles, p.ntiles);
+    const int tile0 = blockIdx.z * p.tiles_per_wg;
+    const int tile1 = min(tile0 + p.tiles_per_wg, p.ntiles);
     for (int tile = tile0; tile < tile1; ++tile) {
         const int ts = tile * TILE;
         const int tl = ts + lane * KPL;
@@ -1103,7 +1107,7 @@ hipError_t launch_reduce_parts_dn(const float* part, int B, int G, int D, int N,
 }
 hipError_t launch_tile_dsum(const void* delta, StepXform stepf, float* tile_dsum, int B, int D, int L, int ntiles,
                             int kpl, int dtype, hipStream_t st) {
-    dim3 grid((D + 15) / 16, B, ntiles);
+    dim3 grid((D + 15) / 16, B, std::min(ntiles, 65535));
     if (dtype == 0) {
         SSM_DISPATCH_KPL(kpl, tile_dsum_kernel<float, K_><<<grid, 256, 0, st>>>((const float*)delta, stepf, tile_dsum,
                                                                                   B, D, L, ntiles))
@@ -1124,8 +1128,14 @@ hipError_t launch_sens_suffix(const void* delta, StepXform stepf, const float* t
                                                        tile_len, t_out);
     return hipGetLastError();
 }
-hipError_t launch_sens(const SensParams& p, int dtype, int kpl, hipStream_t st) {
-    dim3 grid((p.D + 15) / 16, p.B, (p.ntiles + kSensTiles - 1) / kSensTiles);
+// Tiles per workgroup: kSensTiles, more when the sequence has so many tiles
+// that grid.z would pass its 65535 limit.
+static int sens_tiles_per_wg(int ntiles) { return std::max(kSensTiles, (ntiles + 65534) / 65535); }
+
+hipError_t launch_sens(const SensParams& pin, int dtype, int kpl, hipStream_t st) {
+    SensParams p = pin;
+    p.tiles_per_wg = sens_tiles_per_wg(p.ntiles);
+    dim3 grid((p.D + 15) / 16, p.B, (p.ntiles + p.tiles_per_wg - 1) / p.tiles_per_wg);
     const bool n16 = p.N == 16;
     if (p.s_delta) {
         if (dtype == 0) {
@@ -1158,9 +1168,11 @@ hipError_t launch_sens_rows_edge(const SensRowsParams& p, bool tail, int dtype, 
     }
     return hipGetLastError();
 }
-hipError_t launch_sens_rows(const SensRowsParams& p, int dtype, hipStream_t st) {
-    if (p.R < 1 || p.R > kSensRowsMax || p.N > 16) return hipErrorInvalidValue;
-    dim3 grid((p.D + 15) / 16, p.B, (p.ntiles + kSensTiles - 1) / kSensTiles);
+hipError_t launch_sens_rows(const SensRowsParams& pin, int dtype, hipStream_t st) {
+    if (pin.R < 1 || pin.R > kSensRowsMax || pin.N > 16) return hipErrorInvalidValue;
+    SensRowsParams p = pin;
+    p.tiles_per_wg = sens_tiles_per_wg(p.ntiles);
+    dim3 grid((p.D + 15) / 16, p.B, (p.ntiles + p.tiles_per_wg - 1) / p.tiles_per_wg);
     const bool n16 = p.N == 16;
     if (dtype == 0) {
         if (n16) sens_rows_kernel<float, 16><<<grid, 256, 0, st>>>(p);

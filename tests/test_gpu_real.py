@@ -257,6 +257,25 @@ def test_output_sensitivity(dt, N, chunk_len, L, t_out, h0):
     assert torch.equal(out["s_x"], ref["s"])   # the same closed-form costate, bit for bit
 
 
+def test_sensitivity_very_long_sequence():
+    """L = 17,000,000 with 64-step tiles: 265,625 tiles per sequence, more than the grid's z limit (65,535)
+    times the tiles a workgroup takes by default; single-row and multi-row sensitivities against the oracle."""
+    ssm = _ssm()
+    L, D, N = 17_000_000, 2, 2
+    cfg = synth.make_impulse(B=1, D=D, N=N, L=L, seed=3)
+    t = {k: _dev(cfg[k], "f32") for k in ("delta", "x", "Bm", "C", "A")}
+    out = ssm.impulse_sensitivity(t_out=L - 1, chunk_len=64, **t)
+    rows = ssm.sensitivity_rows(t_out0=L - 4, rows=4, **t)
+    torch.cuda.synchronize()
+    kw = dict(delta=cfg["delta"], A=cfg["A"], Bm=cfg["Bm"], C=cfg["C"], B=1, D=D, L=L, N=N)
+    s_last = oracle.impulse_sens(**kw, t_out=L - 1)
+    assert_close("s", out["s"], s_last, **F32)
+    assert_close("rows[3]", rows[3], s_last, **F32)
+    assert_close("rows[0]", rows[0], oracle.impulse_sens(**kw, t_out=L - 4), **F32)
+    y, _ = oracle.real_fwd(x=cfg["x"], **kw)
+    assert_close("y", out["y"], y, **F32)
+
+
 def test_output_sensitivity_impulse_config():
     """The impulse workload's inputs (x = e_0, slow decay), B=1 D=64 N=16 L=20000, y[L-1]."""
     ssm = _ssm()
