@@ -127,6 +127,26 @@ def test_complex_large_phase_arguments():
     run_complex(cfg)
 
 
+@pytest.mark.parametrize("case", ["no_rotation_unit_decay", "rotation_only", "retention_huge", "u_zero"])
+def test_complex_degenerate_inputs(case):
+    """Degenerate controls: lambda = 1 and theta = 0 (a = 1, pure accumulation), r = 0 (|a| = 1, phase rotation
+    only), r = 1e3 (|a| underflows), u = 0 (no input); nonzero h0 and gh_last carry state and adjoint."""
+    cfg = synth.make_complex(B=2, H=3, M=64, L=200, seed=31)
+    g = np.random.default_rng(32)
+    h0 = g.standard_normal((2, 3, 64)) + 1j * g.standard_normal((2, 3, 64))
+    ghl = g.standard_normal((2, 3, 64)) + 1j * g.standard_normal((2, 3, 64))
+    if case == "no_rotation_unit_decay":
+        cfg["lam"] = np.ones_like(cfg["lam"])
+        cfg["theta"] = np.zeros_like(cfg["theta"])
+    elif case == "rotation_only":
+        cfg["r"] = np.zeros_like(cfg["r"])
+    elif case == "retention_huge":
+        cfg["r"] = np.full_like(cfg["r"], 1e3)
+    else:
+        cfg["u"] = np.zeros_like(cfg["u"])
+    run_complex(cfg, h0=h0, ghl=ghl)
+
+
 def test_complex_bf16_streams():
     """bf16 r, phi, u (pairs), gy and stream gradients; fp64 recurrence, fp32 parameter gradients."""
     g = np.random.default_rng(43)
@@ -287,6 +307,24 @@ def test_pd_bf16_streams():
     g = np.random.default_rng(41)
     run_pd(synth.make_pd(B=2, H=4, N=16, L=700, K=8, seed=40, dtype="bf16"),
            h0=g.standard_normal((2, 4, 16)), ghl=g.standard_normal((2, 4, 16)))
+
+
+@pytest.mark.parametrize("case", ["d_one_identity", "d_zero", "b_zero"])
+def test_pd_degenerate_inputs(case):
+    """Degenerate PD steps: an identity dictionary with d = 1 (pure accumulation), d = 0 (the state is cleared
+    every step), b = 0 (only h0 propagates); nonzero h0 and gh_last."""
+    cfg = synth.make_pd(B=2, H=3, N=16, L=300, K=4, seed=33)
+    g = np.random.default_rng(34)
+    h0 = g.standard_normal((2, 3, 16))
+    ghl = g.standard_normal((2, 3, 16))
+    if case == "d_one_identity":
+        cfg["dict"] = np.broadcast_to(np.arange(16, dtype=np.int32), cfg["dict"].shape).copy()
+        cfg["d"] = np.ones_like(cfg["d"])
+    elif case == "d_zero":
+        cfg["d"] = np.zeros_like(cfg["d"])
+    else:
+        cfg["b"] = np.zeros_like(cfg["b"])
+    run_pd(cfg, h0=h0, ghl=ghl)
 
 
 def test_pd_small():

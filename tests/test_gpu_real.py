@@ -64,6 +64,32 @@ def test_real_chunk_lengths_with_state(chunk_len):
     run_real(cfg, h0=g.standard_normal((2, 24, 16)), ghl=g.standard_normal((2, 24, 16)), chunk_len=chunk_len)
 
 
+@pytest.mark.parametrize("case", ["A_zero", "delta_zero", "delta_huge", "x_zero", "gy_zero", "mixed_channels"])
+def test_real_degenerate_inputs(case):
+    """Degenerate transitions and inputs: a = 1 (A = 0, or delta = 0 with no input), a underflowing to 0
+    (delta = 1e3), no input (x = 0), no output gradient (gy = 0), and channels of both kinds in one workgroup;
+    with a nonzero h0 and gh_last so the carried state and its adjoint matter."""
+    cfg = synth.make_real(B=2, D=40, N=16, L=600, seed=21)
+    g = np.random.default_rng(22)
+    h0 = g.standard_normal((2, 40, 16))
+    ghl = g.standard_normal((2, 40, 16))
+    if case == "A_zero":
+        cfg["A"] = np.zeros_like(cfg["A"])
+    elif case == "delta_zero":
+        cfg["delta"] = np.zeros_like(cfg["delta"])
+    elif case == "delta_huge":
+        cfg["delta"] = np.full_like(cfg["delta"], 1e3)
+        cfg["x"] = (cfg["x"] * 1e-3).astype(np.float32)   # keeps b = delta x B of order one
+    elif case == "x_zero":
+        cfg["x"] = np.zeros_like(cfg["x"])
+    elif case == "gy_zero":
+        cfg["gy"] = np.zeros_like(cfg["gy"])
+    else:
+        cfg["A"][::3] = 0.0                                # every third channel accumulates
+        cfg["delta"][:, 1::4] = 0.0                        # every fourth channel holds its state
+    run_real(cfg, h0=h0, ghl=ghl)
+
+
 @pytest.mark.parametrize("chunk_len,L", [(64, 777), (128, 777), (128, 896), (128, 1024), (256, 777)])
 def test_real_checkpoints_are_chunk_states(chunk_len, L):
     """ckpt[:, :, c] is the state entering chunk c: the oracle's final state of the first c*T steps
