@@ -71,7 +71,8 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 2
+/* 3: adds ssm_sensitivity_rows and SSM_OP_SENS_ROWS; struct layouts as in 2 */
+#define SSM_ABI_VERSION 3
 
 /* status codes */
 #define SSM_OK               0
