@@ -53,11 +53,14 @@ FLOPS_PER_ELEMENT = {"selective forward": 7, "selective backward": 17}
 
 # HBM bytes per launch of the dominant kernel, measured with rocprofv3 --pmc
 # FETCH_SIZE and --pmc WRITE_SIZE and scaled by what the same counters read for
-# a 1 GiB device copy (reads x2.0, writes x1.0).  Kept with the SHA-256 of the
+# a 1 GiB device copy (reads x2.0, writes x1.0), and its VALU occupancy.  Kept with the SHA-256 of the
 # kernel sources they were measured on and reported only while those are
 # unchanged (profiles/selective_mamba_layer_fwd_bwd.md holds the run).
 MEASURED_TRAFFIC = {
     "selective backward": {"read_bytes": 509.9e6, "written_bytes": 541.4e6,
+                           # SQ_ACTIVE_INST_VALU x 4 cycles over 1024 SIMD x kernel cycles, and cycles per
+                           # VALU instruction (profiles/selective_headline_counters.md)
+                           "valu_busy": 0.77, "cycles_per_valu_instr": 4.46,
                            "sources_sha256": "2888ceea2c8defc157be1499a377840fdf02c892395fb02acd0e4ac3aed841dc"},
 }
 # (file, marker where the hashed text ends; None = whole file)
@@ -489,14 +492,17 @@ def main():
     dur = kern[dom][0] * 1e-3
     flops = FLOPS_PER_ELEMENT[dom] * head["elements"]
     meas = MEASURED_TRAFFIC.get(dom)
-    traffic = None
+    traffic = valu_busy = None
     if meas and meas["sources_sha256"] == kernel_sources_sha256():
         traffic = meas["read_bytes"] + meas["written_bytes"]
+        valu_busy = meas.get("valu_busy")
     roof = {"kernel": dom, "bound": "alu", "achieved": flops / dur / 1e12, "peak": VALU_F32_PEAK / 1e12,
             "unit": "TFLOP/s", "frac": flops / dur / VALU_F32_PEAK, "traffic": traffic,
             "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
             "duration_ms": kern[dom][0], "hbm_frac": head["bytes_kernel"][dom] / dur / HBM_PEAK,
-            "flops_per_element": FLOPS_PER_ELEMENT[dom]}
+            "flops_per_element": FLOPS_PER_ELEMENT[dom],
+            "valu_busy_frac": valu_busy,
+            "valu_busy_note": "fraction of SIMD cycles with a VALU instruction in flight (rocprofv3 counters)"}
     others = {}
     if not args.no_others:
         todo = [w.strip() for w in args.workloads.split(",") if w.strip()] or \
