@@ -109,7 +109,11 @@ extern "C" {
  * per head (complex, 1..64).  chunk_len = checkpoint interval T in steps:
  * 0 picks the default (256 selective, 32 dense and complex); the selective
  * mode accepts 64, 128 or 256, the dense and complex modes 32.
- * n_chunks = ceil(L / T).
+ * n_chunks = ceil(L / T).  batch, channels and length may be 0 (an empty
+ * problem): nothing is read, outputs with no elements are not touched (their
+ * pointers may be NULL), h_last becomes h0 (or 0), gh0 becomes gh_last (or 0)
+ * and the parameter gradients 0; the sensitivity calls still need
+ * 0 <= t_out < L.  state must be >= 1.
  */
 typedef struct {
     int32_t mode;      /* SSM_REAL_SELECTIVE, SSM_REAL_DENSE or SSM_COMPLEX_SHARED */
@@ -183,7 +187,9 @@ typedef struct {
  * chunk_len: 0 = default 64; only 64 is accepted.  dtype: element type of the
  * streams (logits, d, b, C, and gy, ste_logits, y, gd, gb, gC, glogits of the
  * calls below), SSM_F32 or SSM_BF16; h0, h_last, gh_last, gh0 and checkpoints
- * are always f32, and the recurrence runs in fp32 either way. */
+ * are always f32, and the recurrence runs in fp32 either way.  batch, heads and
+ * length may be 0 (an empty problem: h_last = h0 or 0, gh0 = gh_last or 0,
+ * nothing else is touched). */
 typedef struct {
     int64_t batch, heads, length, state, dict_size, chunk_len;
     const void*    logits; /* (B,H,L,K) dtype selection scores; may be NULL if sel is given */

@@ -135,6 +135,7 @@ struct ScanPlan {
     int kpl;       // selective: steps per lane (T/16)
     int nchunks;   // ceil(L/T)
     size_t esz;    // bytes per streamed element
+    bool empty;    // no batch rows, channels or steps: only h_last / gh0 / parameter gradients are defined
 };
 
 // sel_default_T: the selective mode's checkpoint interval when chunk_len is 0
@@ -148,9 +149,10 @@ int validate_scan_args(const ssm_scan_args* a, ScanPlan* pl, int sel_default_T =
     if (a->dtype != SSM_F32 && a->dtype != SSM_BF16) return fail(SSM_ERR_DTYPE, "unknown dtype %d", a->dtype);
     if (a->dtype == SSM_BF16 && a->mode == SSM_REAL_DENSE)
         return fail(SSM_ERR_DTYPE, "bf16 streams are supported by SSM_REAL_SELECTIVE and SSM_COMPLEX_SHARED only");
-    if (pl->B < 1 || pl->D < 1 || pl->L < 1 || pl->N < 1)
-        return fail(SSM_ERR_SHAPE, "sizes must be >= 1 (B=%lld D=%lld L=%lld N=%lld)", (long long)pl->B,
-                    (long long)pl->D, (long long)pl->L, (long long)pl->N);
+    if (pl->B < 0 || pl->D < 0 || pl->L < 0 || pl->N < 1)
+        return fail(SSM_ERR_SHAPE, "sizes must be >= 0 and state >= 1 (B=%lld D=%lld L=%lld N=%lld)",
+                    (long long)pl->B, (long long)pl->D, (long long)pl->L, (long long)pl->N);
+    pl->empty = pl->B == 0 || pl->D == 0 || pl->L == 0;
     const int64_t nmax = a->mode == SSM_COMPLEX_SHARED ? 64 : 16;
     if (pl->N > nmax) return fail(SSM_ERR_SHAPE, "state size %lld exceeds %lld", (long long)pl->N, (long long)nmax);
     if (pl->B > 65535) return fail(SSM_ERR_SHAPE, "batch %lld exceeds 65535", (long long)pl->B);
@@ -178,7 +180,7 @@ int validate_scan_args(const ssm_scan_args* a, ScanPlan* pl, int sel_default_T =
     if (a->mode != SSM_REAL_SELECTIVE && (a->delta_bias || a->delta_softplus))
         return fail(SSM_ERR_UNSUPPORTED, "delta_bias / delta_softplus apply to SSM_REAL_SELECTIVE only");
     if (a->mode == SSM_REAL_SELECTIVE) {
-        if (!a->delta || !a->x || !a->A || !a->Bm || !a->C)
+        if (!pl->empty && (!a->delta || !a->x || !a->A || !a->Bm || !a->C))
             return fail(SSM_ERR_NULL, "SSM_REAL_SELECTIVE needs delta, x, A, Bm and C");
         if (int rc = check_align(a->delta_bias, 4, "delta_bias")) return rc;
         const size_t al = pl->esz;
@@ -189,13 +191,13 @@ int validate_scan_args(const ssm_scan_args* a, ScanPlan* pl, int sel_default_T =
             return rc;
         (void)BDL; (void)BLN;
     } else if (a->mode == SSM_REAL_DENSE) {
-        if (!a->a || !a->b || !a->C) return fail(SSM_ERR_NULL, "SSM_REAL_DENSE needs a, b and C");
+        if (!pl->empty && (!a->a || !a->b || !a->C)) return fail(SSM_ERR_NULL, "SSM_REAL_DENSE needs a, b and C");
         int rc;
         if ((rc = check_align(a->a, 4, "a")) || (rc = check_align(a->b, 4, "b")) ||
             (rc = check_align(a->C, 4, "C")) || (rc = check_align(a->h0, 4, "h0")))
             return rc;
     } else {
-        if (!a->r || !a->phi || !a->lam || !a->theta || !a->u || !a->c)
+        if (!pl->empty && (!a->r || !a->phi || !a->lam || !a->theta || !a->u || !a->c))
             return fail(SSM_ERR_NULL, "SSM_COMPLEX_SHARED needs r, phi, lam, theta, u and c");
         int rc;
         if ((rc = check_align(a->u, 2 * pl->esz, "u")) || (rc = check_align(a->c, 8, "c")) ||
@@ -351,6 +353,12 @@ int scan_fwd_impl(const ssm_scan_args* a, const ssm_scan_fwd_out* out, void* ws,
             return rc;
         if ((rc = check_overlaps(scan_inputs(a, p), outs))) return rc;
     }
+    if (p.empty) {   // y and the checkpoints have no elements; h_last = h0 (or 0)
+        if (need_only) { *need_only = 0; return ok(); }
+        const size_t nh = p.B * p.D * p.N * (p.mode == SSM_COMPLEX_SHARED ? 2 : 1);
+        SSM_LAUNCH(launch_fill_copy_f32(out->h_last, a->h0, nh, st), "h_last of an empty scan");
+        return ok();
+    }
     Carve cv(nullptr);
     if (p.mode == SSM_REAL_SELECTIVE) {
         SelFwdLayout lay;
@@ -391,7 +399,7 @@ int scan_bwd_impl(const ssm_scan_args* a, const ssm_scan_bwd_in* in, const ssm_s
     if (!need_only) {
         if (!in) return fail(SSM_ERR_NULL, "in is NULL");
         if (!g) return fail(SSM_ERR_NULL, "grads is NULL");
-        if (!in->gy) return fail(SSM_ERR_NULL, "gy is NULL");
+        if (!in->gy && !p.empty) return fail(SSM_ERR_NULL, "gy is NULL");
     }
     if (!in) in = &kNoIn;
     if (!g) g = &kNoGrads;
@@ -415,6 +423,17 @@ int scan_bwd_impl(const ssm_scan_args* a, const ssm_scan_bwd_in* in, const ssm_s
         for (const auto& o : outs)
             if ((rc = check_align(o.p, 2, o.name))) return rc;
         if ((rc = check_overlaps(ins, outs))) return rc;
+    }
+    if (p.empty) {   // stream gradients have no elements; gh0 = gh_last (or 0), parameter gradients 0
+        if (need_only) { *need_only = 0; return ok(); }
+        const size_t cx = p.mode == SSM_COMPLEX_SHARED ? 2 : 1, dn = (size_t)p.D * p.N;
+        SSM_LAUNCH(launch_fill_copy_f32(g->gh0, in->gh_last, p.B * p.D * p.N * cx, st), "gh0 of an empty scan");
+        SSM_LAUNCH(launch_fill_copy_f32(g->gA, nullptr, dn, st), "zero gA");
+        SSM_LAUNCH(launch_fill_copy_f32(g->glam, nullptr, dn, st), "zero glam");
+        SSM_LAUNCH(launch_fill_copy_f32(g->gtheta, nullptr, dn, st), "zero gtheta");
+        SSM_LAUNCH(launch_fill_copy_f32((float*)g->gc, nullptr, 2 * dn, st), "zero gc");
+        SSM_LAUNCH(launch_fill_copy_f32(g->gdelta_bias, nullptr, (size_t)p.D, st), "zero gdelta_bias");
+        return ok();
     }
     Carve cv(nullptr);
     if (p.mode == SSM_REAL_SELECTIVE) {
@@ -492,6 +511,10 @@ int impulse_impl(const ssm_scan_args* a, int64_t t_out, void* y, void* s, void* 
     if (p.mode != SSM_REAL_SELECTIVE) return fail(SSM_ERR_UNSUPPORTED, "%s supports SSM_REAL_SELECTIVE only", name);
     if (t_out == -1) t_out = p.L - 1;
     if (t_out < 0 || t_out >= p.L) return fail(SSM_ERR_SHAPE, "t_out %lld outside [0, L)", (long long)t_out);
+    if (p.empty) {   // no batch rows or channels: every output has zero elements
+        if (need_only) *need_only = 0;
+        return ok();
+    }
     if (!need_only) {
         if (!with_delta && !s) return fail(SSM_ERR_NULL, "s is NULL");
         if (with_delta && !s_delta) return fail(SSM_ERR_NULL, "s_delta is NULL");
@@ -557,6 +580,12 @@ int sens_rows_impl(const ssm_scan_args* a, int64_t t0, int32_t rows, void* s, vo
         if (t0 < 0 || t0 + R > p.L)
             return fail(SSM_ERR_SHAPE, "output rows [%lld, %lld) outside [0, L=%lld)", (long long)t0,
                         (long long)(t0 + R), (long long)p.L);
+    }
+    if (p.empty) {   // no batch rows, channels or steps: s has zero elements
+        if (need_only) *need_only = 0;
+        return ok();
+    }
+    if (!need_only) {
         if (!s) return fail(SSM_ERR_NULL, "s is NULL");
         if ((rc = check_align(s, p.esz, "s"))) return rc;
         const size_t sb = (size_t)R * p.B * p.D * p.L * p.esz;

@@ -62,6 +62,9 @@ struct SensRowsParams {
     int tiles_per_wg;       // set by the launcher: grid.z stays within its limit for any L
 };
 
+// dst[0..n) = src (or 0 when src is NULL); nothing when dst is NULL or n is 0
+hipError_t launch_fill_copy_f32(float* dst, const float* src, size_t n, hipStream_t st);
+
 hipError_t launch_sel_fwd(const SelFwdParams& p, int dtype, int kpl, bool summary, hipStream_t st);
 hipError_t launch_sel_bwd(const SelBwdParams& p, int dtype, int kpl, bool summary, hipStream_t st);
 int sel_bwd_rows();  // channels per backward workgroup (one gB/gC partial per block)

@@ -85,8 +85,9 @@ def test_workspace_query_valid():
 @pytest.mark.parametrize("over,code", [
     (dict(delta=None), "SSM_ERR_NULL"),
     (dict(C=None), "SSM_ERR_NULL"),
-    (dict(batch=0), "SSM_ERR_SHAPE"),
-    (dict(length=0), "SSM_ERR_SHAPE"),
+    (dict(batch=-1), "SSM_ERR_SHAPE"),
+    (dict(length=-1), "SSM_ERR_SHAPE"),
+    (dict(state=0), "SSM_ERR_SHAPE"),
     (dict(state=17), "SSM_ERR_SHAPE"),
     (dict(dtype=7), "SSM_ERR_DTYPE"),
     (dict(mode=9), "SSM_ERR_UNSUPPORTED"),
@@ -100,6 +101,26 @@ def test_validation_errors(over, code):
     assert rc == status(code), (rc, B.lib().ssm_last_error_detail())
     assert B.lib().ssm_last_error_detail()
     assert B.lib().ssm_status_string(rc).decode() == code
+
+
+@pytest.mark.parametrize("over", [dict(batch=0), dict(channels=0), dict(length=0)])
+def test_empty_problems_are_valid(over):
+    """No batch rows, channels or steps: a valid call with an empty workspace; streamed inputs and outputs
+    with no elements may be NULL."""
+    L = B.lib()
+    for op in (B.SSM_OP_SCAN_FWD, B.SSM_OP_SCAN_BWD):
+        for args in (sel_args(**over), cplx_args(**over)):
+            rc, n = ws_bytes(op, args)
+            assert rc == 0 and n == 0, (op, over, L.ssm_last_error_detail())
+    a = sel_args(delta=None, x=None, Bm=None, C=None, A=None, **over)
+    assert ws_bytes(B.SSM_OP_SCAN_FWD, a) == (0, 0)
+    rc, _ = ws_bytes(B.SSM_OP_SCAN_FWD, sel_args(delta=None))   # not empty: inputs are required
+    assert rc == status("SSM_ERR_NULL")
+    if over.get("length") != 0:   # the sensitivity calls need 0 <= t_out < L
+        assert ws_bytes(B.SSM_OP_IMPULSE, sel_args(**over)) == (0, 0)
+        assert ws_bytes(B.SSM_OP_SENS_ROWS, sel_args(**over)) == (0, 0)
+    else:
+        assert ws_bytes(B.SSM_OP_IMPULSE, sel_args(**over))[0] == status("SSM_ERR_SHAPE")
 
 
 def test_bf16_only_for_selective():
@@ -153,7 +174,8 @@ def pd_args(**over):
     (dict(dict=None), "SSM_ERR_NULL"),
     (dict(state=17), "SSM_ERR_SHAPE"),
     (dict(dict_size=65), "SSM_ERR_SHAPE"),
-    (dict(length=0), "SSM_ERR_SHAPE"),
+    (dict(length=-1), "SSM_ERR_SHAPE"),
+    (dict(state=0), "SSM_ERR_SHAPE"),
     (dict(chunk_len=32), "SSM_ERR_UNSUPPORTED"),
 ])
 def test_pd_validation(over, code):
