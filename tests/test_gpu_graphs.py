@@ -151,3 +151,32 @@ def test_graph_pd_fwd_bwd_ste():
 
     g = _capture(step)
     _replay_and_check(g, outs, inp, [mk(1), mk(2)], eager)
+
+
+def test_graph_sensitivities():
+    """Impulse sensitivity, output sensitivity (with its forward into the workspace) and Jacobian rows."""
+    ssm = _ssm()
+
+    def mk(seed):
+        cfg = synth.make_real(B=1, D=40, N=16, L=900, seed=seed)
+        return {k: T(cfg[k]) for k in ("delta", "x", "Bm", "C", "A")}
+
+    inp = mk(10)
+
+    def eager(i):
+        a = ssm.impulse_sensitivity(t_out=700, **i)
+        b = ssm.output_sensitivity(t_out=650, want_y=True, **i)
+        r = ssm.sensitivity_rows(t_out0=600, rows=16, **i)
+        return {"s": a["s"], "y": a["y"], "s_x": b["s_x"], "s_delta": b["s_delta"], "y2": b["y"], "rows": r}
+
+    outs = eager(inp)
+    ao = {"s": outs["s"], "y": outs["y"]}
+    bo = {"s_x": outs["s_x"], "s_delta": outs["s_delta"], "y": outs["y2"]}
+
+    def step():
+        ssm.impulse_sensitivity(t_out=700, out=ao, **inp)
+        ssm.output_sensitivity(t_out=650, want_y=True, out=bo, **inp)
+        ssm.sensitivity_rows(t_out0=600, rows=16, out=outs["rows"], **inp)
+
+    g = _capture(step)
+    _replay_and_check(g, outs, inp, [mk(11), mk(12)], eager)
