@@ -59,6 +59,8 @@ def _load():
         lib.orc_impulse_sens.argtypes = [_L, _L, _L, _L, _L] + [_D] * 5
         lib.orc_output_sens.argtypes = [_L, _L, _L, _L, _L] + [_D] * 8
         lib.orc_complex_fwd.argtypes = [_L, _L, _L, _L] + [_D] * 9
+        lib.orc_complex_dense_fwd.argtypes = [_L, _L, _L, _L] + [_D] * 6
+        lib.orc_complex_dense_bwd.argtypes = [_L, _L, _L, _L] + [_D] * 10
         lib.orc_complex_bwd.argtypes = [_L, _L, _L, _L] + [_D] * 16
         lib.orc_complex_rtrl.argtypes = [_L, _L, _L, _L] + [_D] * 12
         lib.orc_pd_select.argtypes = [_L, _L, _L, _L, _D, _I]
@@ -201,6 +203,25 @@ def complex_bwd(*, r, phi, lam, theta, u, c, h0=None, gy, ghlast=None, B, H, L, 
                             _p(glam), _p(gtheta), _p(gc), _p(gh0))
     return dict(gu=_c(gu).reshape(B, H, L, M), gr=gr, gphi=gphi, glam=glam, gtheta=gtheta,
                 gc=_c(gc).reshape(H, M), gh0=_c(gh0).reshape(B, H, M))
+
+
+def complex_dense_fwd(*, a, u, c, h0=None, B, H, L, M):
+    """Given-transition complex scan: y (B,H,L) and h_last (B,H,M) (oracle.c orc_complex_dense_fwd)."""
+    args = [_w(v) for v in (a, u, c, h0)]
+    y = _z((B, H, L))
+    hl = _z((B, H, M, 2))
+    _load().orc_complex_dense_fwd(B, H, L, M, *[_p(v) for v in args], _p(y), _p(hl))
+    return y, _c(hl).reshape(B, H, M)
+
+
+def complex_dense_bwd(*, a, u, c, h0=None, gy, ghlast=None, B, H, L, M):
+    """Gradients of sum<gy,y> + Re<ghlast,h_last> w.r.t. a, u, c, h0 (oracle.c orc_complex_dense_bwd)."""
+    args = [_w(v) for v in (a, u, c, h0, gy, ghlast)]
+    ga, gu = _z((B, H, L, M, 2)), _z((B, H, L, M, 2))
+    gc, gh0 = _z((H, M, 2)), _z((B, H, M, 2))
+    _load().orc_complex_dense_bwd(B, H, L, M, *[_p(v) for v in args], _p(ga), _p(gu), _p(gc), _p(gh0))
+    return dict(ga=_c(ga).reshape(B, H, L, M), gu=_c(gu).reshape(B, H, L, M), gc=_c(gc).reshape(H, M),
+                gh0=_c(gh0).reshape(B, H, M))
 
 
 def complex_rtrl(*, r, phi, lam, theta, u, c, h0=None, gy, ghlast=None, B, H, L, M):

@@ -332,6 +332,106 @@ void orc_complex_fwd(i64 B, i64 H, i64 L, i64 M,
     }
 }
 
+/* Complex diagonal scan with the transitions given (SPARC page, abstract:
+ * the diagonal affine recurrence h_t = a_t * h_{t-1} + u_t per complex mode,
+ * here with a_t an input instead of the shared-control form):
+ *   h_t[m] = a_t[m] h_{t-1}[m] + u_t[m],  y_t = Re sum_m c_m h_t[m].
+ * a, u (B,H,L,M) complex; c (H,M) complex; h0 (B,H,M) complex or NULL;
+ * y (B,H,L); hlast (B,H,M) complex or NULL.  Complex arrays are (re, im). */
+void orc_complex_dense_fwd(i64 B, i64 H, i64 L, i64 M, const double* a, const double* u, const double* c,
+                           const double* h0, double* y, double* hlast) {
+    #pragma omp parallel
+    {
+        double* h = (double*)malloc(sizeof(double) * 2 * M);
+        #pragma omp for schedule(static)
+        for (i64 s = 0; s < B * H; ++s) {
+            i64 hi = s % H;
+            for (i64 m = 0; m < 2 * M; ++m) h[m] = h0 ? h0[s * 2 * M + m] : 0.0;
+            for (i64 t = 0; t < L; ++t) {
+                double acc = 0.0;
+                for (i64 m = 0; m < M; ++m) {
+                    const double* at = a + ((s * L + t) * M + m) * 2;
+                    const double* ut = u + ((s * L + t) * M + m) * 2;
+                    double hre = at[0] * h[2 * m] - at[1] * h[2 * m + 1] + ut[0];
+                    double him = at[0] * h[2 * m + 1] + at[1] * h[2 * m] + ut[1];
+                    h[2 * m] = hre;
+                    h[2 * m + 1] = him;
+                    acc += c[(hi * M + m) * 2] * hre - c[(hi * M + m) * 2 + 1] * him;
+                }
+                y[s * L + t] = acc;
+            }
+            if (hlast) for (i64 m = 0; m < 2 * M; ++m) hlast[s * 2 * M + m] = h[m];
+        }
+        free(h);
+    }
+}
+
+/* Backward of the given-transition complex scan for Loss = sum_t gy_t y_t +
+ * Re <gh_last, h_{L-1}> (real-pair inner product).  With the adjoint
+ * mu_t = gy_t conj(c) + conj(a_{t+1}) mu_{t+1} (mu_L = gh_last):
+ *   gu_t = mu_t,  ga_t = mu_t conj(h_{t-1}),  gc = sum_t gy_t conj(h_t),  gh0 = conj(a_0) mu_0.
+ * Outputs (any may be NULL): ga, gu (B,H,L,M) complex; gc (H,M) complex;
+ * gh0 (B,H,M) complex. */
+void orc_complex_dense_bwd(i64 B, i64 H, i64 L, i64 M, const double* a, const double* u, const double* c,
+                           const double* h0, const double* gy, const double* ghlast,
+                           double* ga, double* gu, double* gc, double* gh0) {
+    int T = nthreads();
+    double* pc = (double*)calloc((size_t)T * H * M * 2, sizeof(double));
+    #pragma omp parallel
+    {
+        int tid = thread_id();
+        double* hist = (double*)malloc(sizeof(double) * (L + 1) * 2 * M);
+        double* mu = (double*)malloc(sizeof(double) * 2 * M);
+        double* myc = pc + (size_t)tid * H * M * 2;
+        #pragma omp for schedule(static)
+        for (i64 s = 0; s < B * H; ++s) {
+            i64 hi = s % H;
+            for (i64 m = 0; m < 2 * M; ++m) hist[m] = h0 ? h0[s * 2 * M + m] : 0.0;
+            for (i64 t = 0; t < L; ++t)
+                for (i64 m = 0; m < M; ++m) {
+                    const double* at = a + ((s * L + t) * M + m) * 2;
+                    const double* hp = hist + t * 2 * M + 2 * m;
+                    const double* ut = u + ((s * L + t) * M + m) * 2;
+                    hist[(t + 1) * 2 * M + 2 * m] = at[0] * hp[0] - at[1] * hp[1] + ut[0];
+                    hist[(t + 1) * 2 * M + 2 * m + 1] = at[0] * hp[1] + at[1] * hp[0] + ut[1];
+                }
+            for (i64 m = 0; m < 2 * M; ++m) mu[m] = ghlast ? ghlast[s * 2 * M + m] : 0.0;
+            for (i64 t = L - 1; t >= 0; --t) {
+                double g = gy[s * L + t];
+                for (i64 m = 0; m < M; ++m) {
+                    mu[2 * m] += g * c[(hi * M + m) * 2];
+                    mu[2 * m + 1] += -g * c[(hi * M + m) * 2 + 1];
+                    const double* ht = hist + (t + 1) * 2 * M + 2 * m;
+                    const double* hp = hist + t * 2 * M + 2 * m;
+                    myc[(hi * M + m) * 2] += g * ht[0];
+                    myc[(hi * M + m) * 2 + 1] += -g * ht[1];
+                    const i64 o = ((s * L + t) * M + m) * 2;
+                    if (gu) { gu[o] = mu[2 * m]; gu[o + 1] = mu[2 * m + 1]; }
+                    if (ga) {
+                        ga[o] = mu[2 * m] * hp[0] + mu[2 * m + 1] * hp[1];
+                        ga[o + 1] = mu[2 * m + 1] * hp[0] - mu[2 * m] * hp[1];
+                    }
+                    const double* at = a + o;
+                    double mre = at[0] * mu[2 * m] + at[1] * mu[2 * m + 1];
+                    double mim = at[0] * mu[2 * m + 1] - at[1] * mu[2 * m];
+                    mu[2 * m] = mre;
+                    mu[2 * m + 1] = mim;
+                }
+            }
+            if (gh0) for (i64 m = 0; m < 2 * M; ++m) gh0[s * 2 * M + m] = mu[m];
+        }
+        free(hist);
+        free(mu);
+    }
+    if (gc)
+        for (i64 o = 0; o < H * M * 2; ++o) {
+            double v = 0.0;
+            for (int k = 0; k < T; ++k) v += pc[(size_t)k * H * M * 2 + o];
+            gc[o] = v;
+        }
+    free(pc);
+}
+
 /* Backward of the complex scan.  Outputs (any may be NULL):
  * gu (B,H,L,M) complex; gr, gphi (B,H,L); glam, gtheta (H,M); gc (H,M) complex;
  * gh0 (B,H,M) complex. */

@@ -441,6 +441,71 @@ def test_complex_adjoint_identity():
     assert abs(lhs - rhs) <= 1e-11 * max(1.0, abs(lhs))
 
 
+def _dense_complex(B=2, H=2, M=3, L=10, seed=14):
+    g = np.random.default_rng(seed)
+    rho = g.uniform(0.8, 0.999, (B, H, L, M))
+    ang = g.uniform(-np.pi, np.pi, (B, H, L, M))
+    return dict(a=rho * np.exp(1j * ang),
+                u=g.standard_normal((B, H, L, M)) + 1j * g.standard_normal((B, H, L, M)),
+                c=g.standard_normal((H, M)) + 1j * g.standard_normal((H, M)),
+                h0=g.standard_normal((B, H, M)) + 1j * g.standard_normal((B, H, M)),
+                gy=g.standard_normal((B, H, L)),
+                ghlast=g.standard_normal((B, H, M)) + 1j * g.standard_normal((B, H, M)), B=B, H=H, L=L, M=M)
+
+
+def test_complex_dense_matches_shared_controls():
+    """Given transitions a = lam^r e^{i phi theta} (formed in numpy) reproduce the shared-control oracle:
+    y, h_last, gu, gc, gh0."""
+    p = small_complex(B=2, H=3, M=4, L=60, seed=15)
+    a = (p["lam"][None, :, None, :] ** p["r"][:, :, :, None]) * \
+        np.exp(1j * p["phi"][:, :, :, None] * p["theta"][None, :, None, :])
+    kw = dict(u=p["u"], c=p["c"], h0=p["h0"], B=2, H=3, L=60, M=4)
+    y, hl = oracle.complex_dense_fwd(a=a, **kw)
+    ys, hs = oracle.complex_fwd(r=p["r"], phi=p["phi"], lam=p["lam"], theta=p["theta"], **kw)
+    close(y, ys, rtol=1e-12, atol=1e-12)
+    close(hl, hs, rtol=1e-12, atol=1e-12)
+    g = oracle.complex_dense_bwd(a=a, gy=p["gy"], ghlast=p["ghlast"], **kw)
+    gs = oracle.complex_bwd(r=p["r"], phi=p["phi"], lam=p["lam"], theta=p["theta"], gy=p["gy"],
+                            ghlast=p["ghlast"], **kw)
+    for k in ("gu", "gc", "gh0"):
+        close(g[k], gs[k], rtol=1e-11, atol=1e-11)
+
+
+def test_complex_dense_geometric():
+    """Constant a per mode: h_L = a^L h0 + u (1 - a^L) / (1 - a) for a constant u."""
+    B, H, M, L = 1, 1, 3, 150
+    ac = np.array([0.97 * np.exp(0.4j), 0.5 - 0.6j, 0.999j])
+    uc = np.array([1 - 1j, 2.0, -0.5j])
+    h0 = np.array([[[0.3, -1j, 1 + 1j]]])
+    _, hl = oracle.complex_dense_fwd(a=np.broadcast_to(ac, (B, H, L, M)).copy(),
+                                     u=np.broadcast_to(uc, (B, H, L, M)).copy(), c=np.ones((H, M), complex),
+                                     h0=h0, B=B, H=H, L=L, M=M)
+    close(hl[0, 0], ac ** L * h0[0, 0] + uc * (1 - ac ** L) / (1 - ac), rtol=1e-12, atol=1e-12)
+
+
+def _loss_dense_complex(q, **over):
+    r = dict(q)
+    r.update(over)
+    z = {k: r[k + "_re"] + 1j * r[k + "_im"] for k in ("a", "u", "c", "h0")}
+    y, hl = oracle.complex_dense_fwd(**z, B=r["B"], H=r["H"], L=r["L"], M=r["M"])
+    return float((y * r["gy"]).sum() + (hl.real * r["ghlast"].real).sum() + (hl.imag * r["ghlast"].imag).sum())
+
+
+@pytest.mark.parametrize("name", ["a_re", "a_im", "u_re", "u_im", "c_re", "c_im", "h0_re", "h0_im"])
+def test_complex_dense_bwd_fd(name):
+    """Central differences of the loss in the real and imaginary parts of every input: the gradient of a real
+    loss w.r.t. z = x + iy is dL/dx + i dL/dy."""
+    p = _dense_complex()
+    g = oracle.complex_dense_bwd(**{k: p[k] for k in ("a", "u", "c", "h0", "gy", "ghlast")},
+                                 B=p["B"], H=p["H"], L=p["L"], M=p["M"])
+    q = dict(p)
+    for k in ("a", "u", "c", "h0"):
+        q[k + "_re"], q[k + "_im"] = p[k].real.copy(), p[k].imag.copy()
+    base, part = name.split("_")
+    grad = getattr(g["g" + base], "real" if part == "re" else "imag")
+    fd_check(_loss_dense_complex, q, name, grad, rtol=5e-6)
+
+
 @pytest.mark.parametrize("name", ["lam", "theta"])
 def test_complex_rtrl_fd(name):
     """Forward-mode (RTRL) parameter gradients against central differences of the forward scan."""
