@@ -7,7 +7,8 @@ selective scan B=8 D=2048 N=16 L=4096 with bf16 streams, fp32 state and
 accumulation, chunk length 256; value = B*D*N*L / (time of forward+backward).
 The other workloads (impulse sensitivity at L=128000, with and without the
 step-size sensitivity, 16 rows of the input Jacobian at that length, complex
-shared-control scan and its forward-mode gradients, PD scan with and without
+shared-control scan and its forward-mode gradients, complex scan with given
+transitions, PD scan with and without
 the straight-through selection gradient, dense-a/b scan at the Mamba-layer
 shape, the small fp32 case) are reported under "others" with the same fields.
 
@@ -255,6 +256,30 @@ def w_complex(steps, warmup):
     fwd = E * 8 + 2 * BHL * 4 + BHL * 4 + ck                       # read u, r, phi; write y, ckpt
     bwd = E * 8 + 3 * BHL * 4 + ck + E * 8 + 2 * BHL * 4            # read u, r, phi, gy, ckpt; write gu, gr, gphi
     return dict(name="complex", elements=E, ms=ms, kernels=profile_kernels(step), bytes_total=fwd + bwd,
+                config=dict(B=B, H=H, M=M, L=L, streams="complex64", chunk_len=32))
+
+
+def w_complex_dense(steps, warmup):
+    """Complex scan with given transitions, B=16 H=8 M=64 L=2048, forward + backward."""
+    import synth
+    import selective_state_space_chunked_amd as ssm
+    B, H, M, L = 16, 8, 64, 2048
+    cfg = synth.make_complex_dense(B=B, H=H, M=M, L=L, seed=0)
+    t = {k: to_dev(cfg[k]) for k in ("a", "u", "c")}
+    gy = to_dev(cfg["gy"])
+    fo = ssm.scan_fwd(ssm.SSM_COMPLEX_DENSE, want_ckpt=True, **t)
+    go = ssm.scan_bwd(ssm.SSM_COMPLEX_DENSE, gy=gy, ckpt=fo["ckpt"], **t)
+
+    def step():
+        ssm.scan_fwd(ssm.SSM_COMPLEX_DENSE, want_ckpt=True, out=fo, **t)
+        ssm.scan_bwd(ssm.SSM_COMPLEX_DENSE, gy=gy, ckpt=fo["ckpt"], out=go, **t)
+
+    ms = time_steps(step, steps, warmup)
+    BHL, E = B * H * L, B * H * L * M
+    ck = B * H * (-(-L // 32)) * M * 8
+    fwd = 2 * E * 8 + BHL * 4 + ck                                  # read a, u; write y, ckpt
+    bwd = 2 * E * 8 + BHL * 4 + ck + 2 * E * 8                      # read a, u, gy, ckpt; write ga, gu
+    return dict(name="complex-dense", elements=E, ms=ms, kernels=profile_kernels(step), bytes_total=fwd + bwd,
                 config=dict(B=B, H=H, M=M, L=L, streams="complex64", chunk_len=32))
 
 
@@ -506,7 +531,8 @@ def main():
     others = {}
     if not args.no_others:
         todo = [w.strip() for w in args.workloads.split(",") if w.strip()] or \
-            ["impulse", "output-sens", "sens-rows", "complex", "complex-rtrl", "pd", "pd-ste", "dense", "real-small"]
+            ["impulse", "output-sens", "sens-rows", "complex", "complex-dense", "complex-rtrl", "pd", "pd-ste", "dense",
+             "real-small"]
         for w in todo:
             if w == "impulse":
                 others[w] = summarize(w_impulse(args.steps, args.warmup))
@@ -516,6 +542,8 @@ def main():
                 others[w] = summarize(w_sens_rows(args.steps, args.warmup))
             elif w == "complex":
                 others[w] = summarize(w_complex(args.steps, args.warmup))
+            elif w == "complex-dense":
+                others[w] = summarize(w_complex_dense(args.steps, args.warmup))
             elif w == "complex-rtrl":
                 others[w] = summarize(w_complex_rtrl(args.steps, args.warmup))
             elif w == "pd":

@@ -17,6 +17,8 @@
  *     per-step scalars, retention r_t and phase phi_t, drive every complex mode
  *     m through a_{t,m} = exp(r_t ln(lambda_m) + i phi_t theta_m), with
  *     b_t = u_t and the real readout y_t = Re sum_m c_m h_{t,m}.
+ *     SSM_COMPLEX_DENSE takes the complex a_{t,m} as a given tensor (same
+ *     recurrence and readout).
  *   - PD (Flash PD-SSM page, section "Neuer Selektionsmechanismus"): per step,
  *     argmax over K scores picks one column-one-hot matrix P from a per-head
  *     dictionary; A_t = P diag(d_t), i.e. h_t[i] = b_t[i] + sum over the
@@ -71,8 +73,9 @@
 extern "C" {
 #endif
 
-/* 3: adds ssm_sensitivity_rows and SSM_OP_SENS_ROWS; struct layouts as in 2 */
-#define SSM_ABI_VERSION 3
+/* 4: adds SSM_COMPLEX_DENSE; 3 added ssm_sensitivity_rows and SSM_OP_SENS_ROWS;
+ * struct layouts as in 2 */
+#define SSM_ABI_VERSION 4
 
 /* status codes */
 #define SSM_OK               0
@@ -92,6 +95,7 @@ extern "C" {
 #define SSM_REAL_SELECTIVE 0
 #define SSM_REAL_DENSE     1
 #define SSM_COMPLEX_SHARED 2
+#define SSM_COMPLEX_DENSE  3  /* complex a_t given; f32 only */
 
 /* operation ids for ssm_workspace_bytes */
 #define SSM_OP_SCAN_FWD 0
@@ -116,7 +120,7 @@ extern "C" {
  * 0 <= t_out < L.  state must be >= 1.
  */
 typedef struct {
-    int32_t mode;      /* SSM_REAL_SELECTIVE, SSM_REAL_DENSE or SSM_COMPLEX_SHARED */
+    int32_t mode;      /* SSM_REAL_SELECTIVE, SSM_REAL_DENSE, SSM_COMPLEX_SHARED or SSM_COMPLEX_DENSE */
     int32_t dtype;     /* SSM_F32 or SSM_BF16 (bf16: SSM_REAL_SELECTIVE and SSM_COMPLEX_SHARED) */
     int64_t batch, channels, length, state, chunk_len;
     /* SSM_REAL_SELECTIVE */
@@ -125,11 +129,12 @@ typedef struct {
     const float* A;      /* (D,N)  f32, continuous-time diagonal (A < 0)   */
     const void*  Bm;     /* (B,L,N) dtype, input projection B_t (shared over D) */
     /* SSM_REAL_DENSE */
-    const float* a;      /* (B,D,L,N) f32, transition diagonal a_t         */
+    const float* a;      /* (B,D,L,N) f32, transition diagonal a_t;
+                            SSM_COMPLEX_DENSE: (B,H,L,M) complex64 a_{t,m}  */
     const float* b;      /* (B,D,L,N) f32, input term b_t                   */
     /* both real modes */
     const void*  C;      /* (B,L,N) dtype (f32 for dense), readout C_t (shared over D) */
-    /* SSM_COMPLEX_SHARED */
+    /* SSM_COMPLEX_SHARED (SSM_COMPLEX_DENSE reads u, c and a instead of r, phi, lam, theta) */
     const void*  r;      /* (B,H,L) dtype retention control r_t            */
     const void*  phi;    /* (B,H,L) dtype phase control phi_t              */
     const float* lam;    /* (H,M) baseline rate, 0 < lambda <= 1           */
@@ -164,13 +169,14 @@ typedef struct {
 
 /* Gradients of Loss = sum_t <gy_t, y_t> + <gh_last, h_{L-1}>; every pointer
  * nullable.  Complex gradients use the real-pair convention
- * g = dLoss/dRe + i dLoss/dIm (interleaved). */
+ * g = dLoss/dRe + i dLoss/dIm (interleaved).  SSM_COMPLEX_DENSE writes ga,
+ * gu, gc and gh0 only (the other pointers are ignored). */
 typedef struct {
     void*  gdelta;  /* selective (B,D,L) dtype                  */
     void*  gx;      /* selective (B,D,L) dtype                  */
     float* gA;      /* selective (D,N) f32 (sum over b and t)   */
     void*  gBm;     /* selective (B,L,N) dtype (sum over d)     */
-    float* ga;      /* dense (B,D,L,N) f32                      */
+    float* ga;      /* dense (B,D,L,N) f32; complex dense (B,H,L,M) complex64 */
     float* gb;      /* dense (B,D,L,N) f32                      */
     void*  gC;      /* real (B,L,N) dtype (sum over d)          */
     void*  gu;      /* complex (B,H,L,M) (re, im) pairs of dtype */

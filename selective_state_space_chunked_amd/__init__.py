@@ -1,6 +1,7 @@
 """MI355X (gfx950) selective state-space scan: forward, backward, impulse
 sensitivity (one output row or a block of rows of the input Jacobian),
-forward-mode complex gradients and PD-transition scans behind the C ABI of
+forward-mode complex gradients, complex scans with given transitions and
+PD-transition scans behind the C ABI of
 include/ssmscan.h.
 
 The Python functions marshal torch tensors into the C ABI of libssmscan.so;
@@ -8,6 +9,7 @@ all computation runs in the library's HIP kernels.
 """
 from .binding import (  # noqa: F401
     SSM_BF16,
+    SSM_COMPLEX_DENSE,
     SSM_COMPLEX_SHARED,
     SSM_F32,
     SSM_REAL_DENSE,

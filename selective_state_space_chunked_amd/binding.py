@@ -17,7 +17,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libssmscan.so")
 
 SSM_F32, SSM_BF16 = 0, 1
-SSM_REAL_SELECTIVE, SSM_REAL_DENSE, SSM_COMPLEX_SHARED = 0, 1, 2
+SSM_REAL_SELECTIVE, SSM_REAL_DENSE, SSM_COMPLEX_SHARED, SSM_COMPLEX_DENSE = 0, 1, 2, 3
+_COMPLEX_MODES = (SSM_COMPLEX_SHARED, SSM_COMPLEX_DENSE)
 (SSM_OP_SCAN_FWD, SSM_OP_SCAN_BWD, SSM_OP_IMPULSE, SSM_OP_PD_FWD, SSM_OP_PD_BWD, SSM_OP_COMPLEX_RTRL,
  SSM_OP_OUTPUT_SENS, SSM_OP_SENS_ROWS) = range(8)
 
@@ -175,6 +176,16 @@ def _scan_args(mode, *, delta=None, x=None, A=None, Bm=None, a=None, b=None, C=N
         _need(C, "C", torch.float32, (Bsz, L, N), dev)
         _need(h0, "h0", torch.float32, (Bsz, D, N), dev)
         dt = SSM_F32
+    elif mode == SSM_COMPLEX_DENSE:
+        if a is None:
+            raise ValueError("SSM_COMPLEX_DENSE needs the transitions a")
+        _need(a, "a", torch.complex64)
+        Bsz, D, L, N = a.shape
+        dev = a.device
+        _need(u, "u", torch.complex64, (Bsz, D, L, N), dev)
+        _need(c, "c", torch.complex64, (D, N), dev)
+        _need(h0, "h0", torch.complex64, (Bsz, D, N), dev)
+        dt = SSM_F32
     else:
         # u: complex64 (B,H,L,M), or bfloat16 (B,H,L,M,2) holding (re, im) pairs; r, phi follow
         _need(u, "u")
@@ -224,7 +235,7 @@ def scan_fwd(mode, *, want_y=True, want_h_last=False, want_ckpt=False, chunk_len
     args, (Bsz, D, L, N), dev = _scan_args(mode, chunk_len=chunk_len, **tensors)
     out = dict(out or {})
     ydt = _stream_dtype(mode, tensors)
-    sdt = torch.complex64 if mode == SSM_COMPLEX_SHARED else torch.float32
+    sdt = torch.complex64 if mode in _COMPLEX_MODES else torch.float32
     nc = n_chunks(L, _chunk(mode, chunk_len))
     if want_y and "y" not in out:
         out["y"] = torch.empty((Bsz, D, L), dtype=ydt, device=dev)
@@ -242,6 +253,7 @@ _GRADS = {
     SSM_REAL_SELECTIVE: ("gdelta", "gx", "gA", "gBm", "gC", "gh0"),   # gdelta_bias on request
     SSM_REAL_DENSE: ("ga", "gb", "gC", "gh0"),
     SSM_COMPLEX_SHARED: ("gu", "gr", "gphi", "glam", "gtheta", "gc", "gh0"),
+    SSM_COMPLEX_DENSE: ("ga", "gu", "gc", "gh0"),
 }
 
 
@@ -249,7 +261,7 @@ def scan_bwd(mode, *, gy, gh_last=None, ckpt=None, want=None, chunk_len=0, out=N
     """Backward scan.  ``want`` lists gradient names (default: all of the mode)."""
     args, (Bsz, D, L, N), dev = _scan_args(mode, chunk_len=chunk_len, **tensors)
     ydt = _stream_dtype(mode, tensors)
-    sdt = torch.complex64 if mode == SSM_COMPLEX_SHARED else torch.float32
+    sdt = torch.complex64 if mode in _COMPLEX_MODES else torch.float32
     _need(gy, "gy", ydt, (Bsz, D, L), dev)
     _need(gh_last, "gh_last", sdt, (Bsz, D, N), dev)
     nc = n_chunks(L, _chunk(mode, chunk_len))
@@ -258,7 +270,7 @@ def scan_bwd(mode, *, gy, gh_last=None, ckpt=None, want=None, chunk_len=0, out=N
     shapes = {
         "gdelta": ((Bsz, D, L), ydt), "gx": ((Bsz, D, L), ydt), "gA": ((D, N), torch.float32),
         "gBm": ((Bsz, L, N), ydt), "gC": ((Bsz, L, N), ydt), "gh0": ((Bsz, D, N), sdt),
-        "ga": ((Bsz, D, L, N), torch.float32), "gb": ((Bsz, D, L, N), torch.float32),
+        "ga": ((Bsz, D, L, N), sdt), "gb": ((Bsz, D, L, N), torch.float32),
         "gu": (((Bsz, D, L, N), torch.complex64) if ydt == torch.float32 else ((Bsz, D, L, N, 2), ydt)),
         "gr": ((Bsz, D, L), ydt), "gphi": ((Bsz, D, L), ydt), "glam": ((D, N), torch.float32),
         "gtheta": ((D, N), torch.float32), "gc": ((D, N), torch.complex64),

@@ -83,6 +83,7 @@ struct Carve {
 };
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+bool is_complex(int mode) { return mode == SSM_COMPLEX_SHARED || mode == SSM_COMPLEX_DENSE; }
 
 int device_status(hipError_t e, const char* what) {
     if (e != hipSuccess) return fail(SSM_ERR_DEVICE, "%s: %s", what, hipGetErrorName(e));
@@ -144,16 +145,17 @@ int validate_scan_args(const ssm_scan_args* a, ScanPlan* pl, int sel_default_T =
     pl->mode = a->mode;
     pl->dtype = a->dtype;
     pl->B = a->batch; pl->D = a->channels; pl->L = a->length; pl->N = a->state;
-    if (a->mode != SSM_REAL_SELECTIVE && a->mode != SSM_REAL_DENSE && a->mode != SSM_COMPLEX_SHARED)
+    if (a->mode != SSM_REAL_SELECTIVE && a->mode != SSM_REAL_DENSE && a->mode != SSM_COMPLEX_SHARED &&
+        a->mode != SSM_COMPLEX_DENSE)
         return fail(SSM_ERR_UNSUPPORTED, "unknown mode %d", a->mode);
     if (a->dtype != SSM_F32 && a->dtype != SSM_BF16) return fail(SSM_ERR_DTYPE, "unknown dtype %d", a->dtype);
-    if (a->dtype == SSM_BF16 && a->mode == SSM_REAL_DENSE)
+    if (a->dtype == SSM_BF16 && (a->mode == SSM_REAL_DENSE || a->mode == SSM_COMPLEX_DENSE))
         return fail(SSM_ERR_DTYPE, "bf16 streams are supported by SSM_REAL_SELECTIVE and SSM_COMPLEX_SHARED only");
     if (pl->B < 0 || pl->D < 0 || pl->L < 0 || pl->N < 1)
         return fail(SSM_ERR_SHAPE, "sizes must be >= 0 and state >= 1 (B=%lld D=%lld L=%lld N=%lld)",
                     (long long)pl->B, (long long)pl->D, (long long)pl->L, (long long)pl->N);
     pl->empty = pl->B == 0 || pl->D == 0 || pl->L == 0;
-    const int64_t nmax = a->mode == SSM_COMPLEX_SHARED ? 64 : 16;
+    const int64_t nmax = is_complex(a->mode) ? 64 : 16;
     if (pl->N > nmax) return fail(SSM_ERR_SHAPE, "state size %lld exceeds %lld", (long long)pl->N, (long long)nmax);
     if (pl->B > 65535) return fail(SSM_ERR_SHAPE, "batch %lld exceeds 65535", (long long)pl->B);
     if (pl->L >= (1LL << 31) || pl->D >= (1LL << 24) || pl->B * pl->D * pl->L * pl->N >= (1LL << 46))
@@ -196,6 +198,12 @@ int validate_scan_args(const ssm_scan_args* a, ScanPlan* pl, int sel_default_T =
         if ((rc = check_align(a->a, 4, "a")) || (rc = check_align(a->b, 4, "b")) ||
             (rc = check_align(a->C, 4, "C")) || (rc = check_align(a->h0, 4, "h0")))
             return rc;
+    } else if (a->mode == SSM_COMPLEX_DENSE) {
+        if (!pl->empty && (!a->a || !a->u || !a->c)) return fail(SSM_ERR_NULL, "SSM_COMPLEX_DENSE needs a, u and c");
+        int rc;
+        if ((rc = check_align(a->a, 8, "a")) || (rc = check_align(a->u, 8, "u")) || (rc = check_align(a->c, 8, "c")) ||
+            (rc = check_align(a->h0, 8, "h0")))
+            return rc;
     } else {
         if (!pl->empty && (!a->r || !a->phi || !a->lam || !a->theta || !a->u || !a->c))
             return fail(SSM_ERR_NULL, "SSM_COMPLEX_SHARED needs r, phi, lam, theta, u and c");
@@ -210,11 +218,11 @@ int validate_scan_args(const ssm_scan_args* a, ScanPlan* pl, int sel_default_T =
 
 std::vector<Range> scan_inputs(const ssm_scan_args* a, const ScanPlan& p) {
     const size_t BDL = p.B * p.D * p.L, BLN = p.B * p.L * p.N, BDLN = BDL * p.N;
-    const size_t st = p.N * (p.mode == SSM_COMPLEX_SHARED ? 8 : 4);
+    const size_t st = p.N * (is_complex(p.mode) ? 8 : 4);
     return {
         {a->delta, BDL * p.esz, "delta"}, {a->x, BDL * p.esz, "x"},
         {a->A, (size_t)p.D * p.N * 4, "A"}, {a->Bm, BLN * p.esz, "Bm"},
-        {a->a, BDLN * 4, "a"}, {a->b, BDLN * 4, "b"},
+        {a->a, BDLN * (p.mode == SSM_COMPLEX_DENSE ? 8 : 4), "a"}, {a->b, BDLN * 4, "b"},
         {a->C, BLN * (p.mode == SSM_REAL_SELECTIVE ? p.esz : 4), "C"},
         {a->r, BDL * p.esz, "r"}, {a->phi, BDL * p.esz, "phi"},
         {a->lam, (size_t)p.D * p.N * 4, "lam"}, {a->theta, (size_t)p.D * p.N * 4, "theta"},
@@ -343,8 +351,8 @@ int scan_fwd_impl(const ssm_scan_args* a, const ssm_scan_fwd_out* out, void* ws,
     if (rc) return rc;
     if (!need_only) {
         if (!out) return fail(SSM_ERR_NULL, "out is NULL");
-        const size_t st_b = p.mode == SSM_COMPLEX_SHARED ? 8 : 4;
-        const size_t yb = p.B * p.D * p.L * (p.mode == SSM_REAL_DENSE ? 4 : p.esz);
+        const size_t st_b = is_complex(p.mode) ? 8 : 4;
+        const size_t yb = p.B * p.D * p.L * (p.mode == SSM_REAL_DENSE ? 4 : p.esz);  // esz is 4 for complex dense
         const size_t hb = p.B * p.D * p.N * st_b;
         std::vector<Range> outs = {{out->y, yb, "y"}, {out->h_last, hb, "h_last"},
                                    {out->ckpt, hb * p.nchunks, "ckpt"}};
@@ -355,7 +363,7 @@ int scan_fwd_impl(const ssm_scan_args* a, const ssm_scan_fwd_out* out, void* ws,
     }
     if (p.empty) {   // y and the checkpoints have no elements; h_last = h0 (or 0)
         if (need_only) { *need_only = 0; return ok(); }
-        const size_t nh = p.B * p.D * p.N * (p.mode == SSM_COMPLEX_SHARED ? 2 : 1);
+        const size_t nh = p.B * p.D * p.N * (is_complex(p.mode) ? 2 : 1);
         SSM_LAUNCH(launch_fill_copy_f32(out->h_last, a->h0, nh, st), "h_last of an empty scan");
         return ok();
     }
@@ -405,7 +413,7 @@ int scan_bwd_impl(const ssm_scan_args* a, const ssm_scan_bwd_in* in, const ssm_s
     if (!g) g = &kNoGrads;
     const bool have_ckpt = need_only ? false : in->ckpt != nullptr;
     if (!need_only) {
-        const size_t st_b = p.mode == SSM_COMPLEX_SHARED ? 8 : 4;
+        const size_t st_b = is_complex(p.mode) ? 8 : 4;
         const size_t es = p.mode == SSM_REAL_DENSE ? 4 : p.esz;
         const size_t BDL = p.B * p.D * p.L, BLN = p.B * p.L * p.N;
         const size_t hb = p.B * p.D * p.N * st_b;
@@ -415,7 +423,8 @@ int scan_bwd_impl(const ssm_scan_args* a, const ssm_scan_bwd_in* in, const ssm_s
         ins.push_back({in->ckpt, hb * p.nchunks, "ckpt"});
         std::vector<Range> outs = {
             {g->gdelta, BDL * es, "gdelta"}, {g->gx, BDL * es, "gx"}, {g->gA, (size_t)p.D * p.N * 4, "gA"},
-            {g->gBm, BLN * es, "gBm"}, {g->ga, BDL * p.N * 4, "ga"}, {g->gb, BDL * p.N * 4, "gb"},
+            {g->gBm, BLN * es, "gBm"}, {g->ga, BDL * p.N * (p.mode == SSM_COMPLEX_DENSE ? 8 : 4), "ga"},
+            {g->gb, BDL * p.N * 4, "gb"},
             {g->gC, BLN * es, "gC"}, {g->gu, BDL * p.N * 2 * es, "gu"}, {g->gr, BDL * es, "gr"},
             {g->gphi, BDL * es, "gphi"}, {g->glam, (size_t)p.D * p.N * 4, "glam"},
             {g->gtheta, (size_t)p.D * p.N * 4, "gtheta"}, {g->gc, (size_t)p.D * p.N * 8, "gc"},
@@ -426,13 +435,24 @@ int scan_bwd_impl(const ssm_scan_args* a, const ssm_scan_bwd_in* in, const ssm_s
     }
     if (p.empty) {   // stream gradients have no elements; gh0 = gh_last (or 0), parameter gradients 0
         if (need_only) { *need_only = 0; return ok(); }
-        const size_t cx = p.mode == SSM_COMPLEX_SHARED ? 2 : 1, dn = (size_t)p.D * p.N;
+        const size_t cx = is_complex(p.mode) ? 2 : 1, dn = (size_t)p.D * p.N;
         SSM_LAUNCH(launch_fill_copy_f32(g->gh0, in->gh_last, p.B * p.D * p.N * cx, st), "gh0 of an empty scan");
-        SSM_LAUNCH(launch_fill_copy_f32(g->gA, nullptr, dn, st), "zero gA");
-        SSM_LAUNCH(launch_fill_copy_f32(g->glam, nullptr, dn, st), "zero glam");
-        SSM_LAUNCH(launch_fill_copy_f32(g->gtheta, nullptr, dn, st), "zero gtheta");
-        SSM_LAUNCH(launch_fill_copy_f32((float*)g->gc, nullptr, 2 * dn, st), "zero gc");
-        SSM_LAUNCH(launch_fill_copy_f32(g->gdelta_bias, nullptr, (size_t)p.D, st), "zero gdelta_bias");
+        // gBm and gC sum over channels: with D = 0 but B, L > 0 they have elements, all zero
+        const size_t btn = p.D == 0 ? p.B * p.L * p.N : 0;
+        if (p.mode == SSM_REAL_SELECTIVE) {
+            SSM_LAUNCH(launch_fill_copy_f32(g->gA, nullptr, dn, st), "zero gA");
+            SSM_LAUNCH(launch_fill_copy_f32(g->gdelta_bias, nullptr, (size_t)p.D, st), "zero gdelta_bias");
+            SSM_LAUNCH(launch_zero_bytes(g->gBm, btn * p.esz, st), "zero gBm");
+            SSM_LAUNCH(launch_zero_bytes(g->gC, btn * p.esz, st), "zero gC");
+        } else if (p.mode == SSM_REAL_DENSE) {
+            SSM_LAUNCH(launch_zero_bytes(g->gC, btn * 4, st), "zero gC");
+        } else {
+            if (p.mode == SSM_COMPLEX_SHARED) {
+                SSM_LAUNCH(launch_fill_copy_f32(g->glam, nullptr, dn, st), "zero glam");
+                SSM_LAUNCH(launch_fill_copy_f32(g->gtheta, nullptr, dn, st), "zero gtheta");
+            }
+            SSM_LAUNCH(launch_fill_copy_f32(g->gc, nullptr, 2 * dn, st), "zero gc");
+        }
         return ok();
     }
     Carve cv(nullptr);

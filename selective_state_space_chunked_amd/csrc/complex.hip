@@ -202,16 +202,18 @@ __device__ __forceinline__ bool cunit(const CplxParams& p, CUnit& u) {
 // ---------------------------------------------------------------------------
 // forward.  SUMMARY: per segment the map h_end = P h_start + S (h_start = 0).
 // ---------------------------------------------------------------------------
-template <typename T, bool SUMMARY>
+// DENSE: the transitions a_t are given (SSM_COMPLEX_DENSE, complex64 streams)
+// and loaded like u instead of being formed from the controls.
+template <typename T, bool SUMMARY, bool DENSE = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void cplx_fwd_kernel(CplxParams p) {
     CUnit u;
     if (!cunit(p, u)) return;
     const int L = p.L, M = p.M;
     const size_t pm = (size_t)u.hh * M + u.mc;
-    const double lnl = log((double)p.lam[pm]);
-    const float th = p.theta[pm];
+    const double lnl = DENSE ? 0.0 : log((double)p.lam[pm]);
+    const float th = DENSE ? 0.0f : p.theta[pm];
     const double c_re = p.c[2 * pm], c_im = p.c[2 * pm + 1];
-    const float thmax = wave_absmax(th);
+    const float thmax = DENSE ? 0.0f : wave_absmax(th);
     const size_t us = ((size_t)u.s * p.G + u.g) * M + u.mc;  // (B*H, G, M)
     cd h = {0.0, 0.0}, P = {1.0, 0.0};
     if (!SUMMARY) {
@@ -222,6 +224,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void c
     const int c0 = u.g * p.chunks_per_seg;
     const int c1 = min(c0 + p.chunks_per_seg, p.nchunks);
     const T* urow = (const T*)p.u + (size_t)u.s * L * M * 2;
+    const T* arow = DENSE ? (const T*)p.a + (size_t)u.s * L * M * 2 : nullptr;
     for (int ch = c0; ch < c1; ++ch) {
         const int t0 = ch * kCChunk;
         if (!SUMMARY && p.ckpt_out && u.act) {
@@ -231,28 +234,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void c
         }
         const int tl = t0 + (u.m & 31);
         const bool tv = tl < L;
-        const float rv = tv ? to_f32(((const T*)p.r)[(size_t)u.s * L + tl]) : 0.0f;
-        const float pv = tv ? to_f32(((const T*)p.phi)[(size_t)u.s * L + tl]) : 0.0f;
+        const float rv = (tv && !DENSE) ? to_f32(((const T*)p.r)[(size_t)u.s * L + tl]) : 0.0f;
+        const float pv = (tv && !DENSE) ? to_f32(((const T*)p.phi)[(size_t)u.s * L + tl]) : 0.0f;
         float yp[kCChunk];
-        cplx_chunk(pv, thmax, t0 + kCChunk <= L, [&](auto fastc, auto fullc) {
+        auto body = [&](auto fastc, auto fullc) {
             constexpr bool FAST = decltype(fastc)::value, FULL = decltype(fullc)::value;
 #pragma unroll
             for (int hb = 0; hb < kCChunk / 16; ++hb) {
-                float2 uv[16];
+                float2 uv[16], av[16];
                 load_u<T, 16>(urow, t0 + 16 * hb, L, M, u.mc, u.act, uv);
+                if (DENSE) load_u<T, 16>(arow, t0 + 16 * hb, L, M, u.mc, u.act, av);
 #pragma unroll
                 for (int jj = 0; jj < 16; ++jj) {
                     const int j = 16 * hb + jj;
                     yp[j] = 0.0f;
                     if (FULL || t0 + j < L) {  // uniform
-                        const cd a = trans_a<FAST>(lanev(rv, j), lnl, lanev(pv, j), th);
+                        const cd a = DENSE ? cd{av[jj].x, av[jj].y} : trans_a<FAST>(lanev(rv, j), lnl, lanev(pv, j), th);
                         h = cfma(a, h, cd{uv[jj].x, uv[jj].y});
                         if (SUMMARY) P = cmul(a, P);
                         else yp[j] = (float)fma(c_re, h.re, -c_im * h.im);
                     }
                 }
             }
-        });
+        };
+        if constexpr (DENSE) {
+            if (t0 + kCChunk <= L) body(std::true_type{}, std::true_type{});
+            else body(std::true_type{}, std::false_type{});
+        } else {
+            cplx_chunk(pv, thmax, t0 + kCChunk <= L, body);
+        }
         if (!SUMMARY && p.y) {
             const float ys = wave_transpose_sum32(yp);
             const int t = t0 + (u.m >> 1);
@@ -280,17 +290,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void c
 // Reverse over the chunks of a segment; each chunk's states are recomputed
 // (in fp64, from its checkpoint) and kept in registers as complex64.
 // SUMMARY: per segment the adjoint map nu_start = Q nu_end + R.
+// DENSE: given transitions; g_a is written per step and mode instead of the
+// control and mode-parameter gradients.
 // ---------------------------------------------------------------------------
-template <typename T, bool SUMMARY>
+template <typename T, bool SUMMARY, bool DENSE = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void cplx_bwd_kernel(CplxParams p) {
     CUnit u;
     if (!cunit(p, u)) return;
     const int L = p.L, M = p.M;
     const size_t pm = (size_t)u.hh * M + u.mc;
-    const double lnl = log((double)p.lam[pm]);
-    const float th = p.theta[pm];
+    const double lnl = DENSE ? 0.0 : log((double)p.lam[pm]);
+    const float th = DENSE ? 0.0f : p.theta[pm];
     const double cjr = p.c[2 * pm], cji = -(double)p.c[2 * pm + 1];  // conj(c)
-    const float thmax = wave_absmax(th);
+    const float thmax = DENSE ? 0.0f : wave_absmax(th);
     const size_t us = ((size_t)u.s * p.G + u.g) * M + u.mc;
     cd nu = {0.0, 0.0}, Q = {1.0, 0.0};
     if (!SUMMARY) {
@@ -302,24 +314,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
     const int c0 = u.g * p.chunks_per_seg;
     const int c1 = min(c0 + p.chunks_per_seg, p.nchunks);
     const T* urow = (const T*)p.u + (size_t)u.s * L * M * 2;
+    const T* arow = DENSE ? (const T*)p.a + (size_t)u.s * L * M * 2 : nullptr;
     for (int ch = c1 - 1; ch >= c0; --ch) {
         const int t0 = ch * kCChunk;
         const int tl = t0 + (u.m & 31);
         const bool tv = tl < L;
-        const float rv = tv ? to_f32(((const T*)p.r)[(size_t)u.s * L + tl]) : 0.0f;
-        const float pv = tv ? to_f32(((const T*)p.phi)[(size_t)u.s * L + tl]) : 0.0f;
+        const float rv = (tv && !DENSE) ? to_f32(((const T*)p.r)[(size_t)u.s * L + tl]) : 0.0f;
+        const float pv = (tv && !DENSE) ? to_f32(((const T*)p.phi)[(size_t)u.s * L + tl]) : 0.0f;
         const float gv = tv ? to_f32(((const T*)p.gy)[(size_t)u.s * L + tl]) : 0.0f;
-        cplx_chunk(pv, thmax, t0 + kCChunk <= L, [&](auto fastc, auto fullc) {
+        auto body = [&](auto fastc, auto fullc) {
         constexpr bool FAST = decltype(fastc)::value, FULL = decltype(fullc)::value;
         if (SUMMARY) {
 #pragma unroll
-            for (int j = kCChunk - 1; j >= 0; --j) {
-                if (FULL || t0 + j < L) {
-                    const cd a = trans_a<FAST>(lanev(rv, j), lnl, lanev(pv, j), th);
-                    const double g = lanev(gv, j);
-                    const cd mu = {fma(g, cjr, nu.re), fma(g, cji, nu.im)};
-                    nu = cmul_conj_a(a, mu);
-                    Q = cmul_conj_a(a, Q);
+            for (int half = kCChunk / 16 - 1; half >= 0; --half) {
+                float2 av[16];
+                if (DENSE) load_u<T, 16>(arow, t0 + 16 * half, L, M, u.mc, u.act, av);
+#pragma unroll
+                for (int jj = 15; jj >= 0; --jj) {
+                    const int j = 16 * half + jj;
+                    if (FULL || t0 + j < L) {
+                        const cd a = DENSE ? cd{av[jj].x, av[jj].y} : trans_a<FAST>(lanev(rv, j), lnl, lanev(pv, j), th);
+                        const double g = lanev(gv, j);
+                        const cd mu = {fma(g, cjr, nu.re), fma(g, cji, nu.im)};
+                        nu = cmul_conj_a(a, mu);
+                        Q = cmul_conj_a(a, Q);
+                    }
                 }
             }
             return;
@@ -335,13 +354,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
         }
 #pragma unroll
         for (int hb = 0; hb < kCChunk / 16; ++hb) {
-            float2 uv[16];
+            float2 uv[16], av[16];
             load_u<T, 16>(urow, t0 + 16 * hb, L, M, u.mc, u.act, uv);
+            if (DENSE) load_u<T, 16>(arow, t0 + 16 * hb, L, M, u.mc, u.act, av);
 #pragma unroll
             for (int jj = 0; jj < 16; ++jj) {
                 const int j = 16 * hb + jj;
                 if (FULL || t0 + j < L) {
-                    const cd a = trans_a<FAST>(lanev(rv, j), lnl, lanev(pv, j), th);
+                    const cd a = DENSE ? cd{av[jj].x, av[jj].y} : trans_a<FAST>(lanev(rv, j), lnl, lanev(pv, j), th);
                     hcur = cfma(a, hcur, cd{uv[jj].x, uv[jj].y});
                 }
                 hre[j + 1] = (float)hcur.re;
@@ -353,6 +373,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
 #pragma unroll
         for (int half = kCChunk / 16 - 1; half >= 0; --half) {
             double grp[16], gpp[16];
+            float2 av[16];  // the half's transitions again (just read: cache hits)
+            if (DENSE) load_u<T, 16>(arow, t0 + 16 * half, L, M, u.mc, u.act, av);
 #pragma unroll
             for (int jj = 15; jj >= 0; --jj) {
                 const int j = 16 * half + jj;
@@ -362,12 +384,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
                 if (FULL || t < L) {
                     const float rj = lanev(rv, j), pj = lanev(pv, j);
                     const double g = lanev(gv, j);
-                    const cd a = trans_a<FAST>(rj, lnl, pj, th);
+                    const cd a = DENSE ? cd{av[jj].x, av[jj].y} : trans_a<FAST>(rj, lnl, pj, th);
                     const cd mu = {fma(g, cjr, nu.re), fma(g, cji, nu.im)};
                     if (p.gu && u.act)
                         reinterpret_cast<typename CPair<T>::V*>(p.gu)[((size_t)u.s * L + t) * M + u.m] =
                             CPair<T>::narrow((float)mu.re, (float)mu.im);
                     const cd ga = cmul(mu, cd{hre[j], -(double)him[j]});
+                    if (DENSE) {
+                        if (p.ga && u.act)
+                            reinterpret_cast<float2*>(p.ga)[((size_t)u.s * L + t) * M + u.m] =
+                                make_float2((float)ga.re, (float)ga.im);
+                        if (u.act) {
+                            gcr = fma(g, (double)hre[j + 1], gcr);
+                            gci = fma(-g, (double)him[j + 1], gci);
+                        }
+                        nu = cmul_conj_a(a, mu);
+                        continue;
+                    }
                     const cd gz = cmul_conj_a(a, ga);
                     if (u.act) {
                         grp[jj] = gz.re * lnl;
@@ -380,6 +413,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
                     nu = cmul_conj_a(a, mu);
                 }
             }
+            if (DENSE) continue;
             const double sr = wave_transpose_sum16_f64(grp);
             const double sp = wave_transpose_sum16_f64(gpp);
             const int t = t0 + 16 * half + (u.m >> 2);
@@ -388,7 +422,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
                 if (p.gphi) ((T*)p.gphi)[(size_t)u.s * L + t] = from_f32<T>((float)sp);
             }
         }
-        });
+        };
+        if constexpr (DENSE) {
+            if (t0 + kCChunk <= L) body(std::true_type{}, std::true_type{});
+            else body(std::true_type{}, std::false_type{});
+        } else {
+            cplx_chunk(pv, thmax, t0 + kCChunk <= L, body);
+        }
     }
     if (!u.act) return;
     if (SUMMARY) {
@@ -494,10 +534,12 @@ __global__ __launch_bounds__(256) void cplx_reduce_kernel(CplxParams p, float* g
     double sl = 0.0, st = 0.0, cr = 0.0, ci = 0.0;
     for (int k = lane; k < p.B * p.G; k += 64) {
         const size_t o = (size_t)k * HM + i;
-        sl += p.partL[o];
-        st += p.partT[o];
-        cr += p.partC[2 * o];
-        ci += p.partC[2 * o + 1];
+        if (p.partL) sl += p.partL[o];  // uniform: absent for given transitions
+        if (p.partT) st += p.partT[o];
+        if (p.partC) {
+            cr += p.partC[2 * o];
+            ci += p.partC[2 * o + 1];
+        }
     }
     sl = wave_sum_f64(sl);
     st = wave_sum_f64(st);
@@ -717,7 +759,11 @@ hipError_t launch_cplx_rtrl_reduce(const RtrlParams& p, hipStream_t st) {
 hipError_t launch_cplx_fwd(const CplxParams& p, bool summary, hipStream_t st) {
     const int units = p.B * p.H * p.G;
     dim3 grid((units + 3) / 4), block(256);
-    if (p.dtype == 0) {
+    if (p.a) {  // given transitions: complex64 streams only
+        if (p.dtype != 0) return hipErrorInvalidValue;
+        if (summary) cplx_fwd_kernel<float, true, true><<<grid, block, 0, st>>>(p);
+        else cplx_fwd_kernel<float, false, true><<<grid, block, 0, st>>>(p);
+    } else if (p.dtype == 0) {
         if (summary) cplx_fwd_kernel<float, true><<<grid, block, 0, st>>>(p);
         else cplx_fwd_kernel<float, false><<<grid, block, 0, st>>>(p);
     } else {
@@ -729,7 +775,11 @@ hipError_t launch_cplx_fwd(const CplxParams& p, bool summary, hipStream_t st) {
 hipError_t launch_cplx_bwd(const CplxParams& p, bool summary, hipStream_t st) {
     const int units = p.B * p.H * p.G;
     dim3 grid((units + 3) / 4), block(256);
-    if (p.dtype == 0) {
+    if (p.a) {
+        if (p.dtype != 0) return hipErrorInvalidValue;
+        if (summary) cplx_bwd_kernel<float, true, true><<<grid, block, 0, st>>>(p);
+        else cplx_bwd_kernel<float, false, true><<<grid, block, 0, st>>>(p);
+    } else if (p.dtype == 0) {
         if (summary) cplx_bwd_kernel<float, true><<<grid, block, 0, st>>>(p);
         else cplx_bwd_kernel<float, false><<<grid, block, 0, st>>>(p);
     } else {

@@ -64,6 +64,7 @@ struct SensRowsParams {
 
 // dst[0..n) = src (or 0 when src is NULL); nothing when dst is NULL or n is 0
 hipError_t launch_fill_copy_f32(float* dst, const float* src, size_t n, hipStream_t st);
+hipError_t launch_zero_bytes(void* dst, size_t bytes, hipStream_t st);  // bytes even
 
 hipError_t launch_sel_fwd(const SelFwdParams& p, int dtype, int kpl, bool summary, hipStream_t st);
 hipError_t launch_sel_bwd(const SelBwdParams& p, int dtype, int kpl, bool summary, hipStream_t st);
@@ -115,6 +116,9 @@ struct CplxParams {
     double* segP; double* segS; double* segQ; double* segR;   // complex double (B,H,G,M)
     void* gu; void* gr; void* gphi; float* gh0;
     double* partL; double* partT; double* partC;              // (B,G,H,M) [partC complex]
+    // given transitions (SSM_COMPLEX_DENSE): a (B,H,L,M) complex64 replaces r, phi, lam,
+    // theta; ga (B,H,L,M) complex64 replaces gr, gphi, glam, gtheta
+    const float* a; float* ga;
     int B, H, L, M, nchunks, chunk, chunks_per_seg, G;
     int dtype;
 };

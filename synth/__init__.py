@@ -9,6 +9,7 @@ from .gen import (  # noqa: F401
     bf16_bits_to_f32,
     f32_to_bf16_bits,
     make_complex,
+    make_complex_dense,
     make_pd,
     make_real,
     make_impulse,

@@ -184,6 +184,31 @@ def make_complex(B=16, H=8, M=64, L=2048, seed=0, with_grad=True, dtype="f32"):
     return out
 
 
+def make_complex_dense(B=16, H=8, M=64, L=2048, seed=0, with_grad=True):
+    """Complex diagonal recurrence with given per-step transitions (complex64).
+
+    Draw order: rho ~ U[0.9, 0.999] (B,H,L,M); angle ~ U[-pi, pi] (B,H,L,M),
+    a = rho e^{i angle}; u = N(0,1/2) + i N(0,1/2) (B,H,L,M);
+    c = N(0,1/(2M)) + i N(0,1/(2M)) (H,M); gy ~ N(0,1) (B,H,L).
+    """
+    g = np.random.Generator(np.random.PCG64(seed))
+    rho = g.uniform(0.9, 0.999, (B, H, L, M))
+    ang = g.uniform(-math.pi, math.pi, (B, H, L, M))
+    a = (rho * np.exp(1j * ang)).astype(np.complex64)
+    su = math.sqrt(0.5)
+    u = np.empty((B, H, L, M), dtype=np.complex64)
+    u.real = g.standard_normal((B, H, L, M)) * su
+    u.imag = g.standard_normal((B, H, L, M)) * su
+    sc = math.sqrt(1.0 / (2 * M))
+    c = np.empty((H, M), dtype=np.complex64)
+    c.real = g.standard_normal((H, M)) * sc
+    c.imag = g.standard_normal((H, M)) * sc
+    out = dict(B=B, H=H, M=M, L=L, dtype="f32", a=a, u=u, c=c)
+    if with_grad:
+        out["gy"] = _f32(g.standard_normal((B, H, L)))
+    return out
+
+
 def make_pd(B=8, H=32, N=16, L=17000, K=8, seed=0, with_grad=True, dtype="f32"):
     """PD-transition scan inputs (fp32 values, int32 indices; ``dtype`` 'bf16'
     rounds the streams logits, d, b, C, gy to bfloat16 bits).

@@ -36,6 +36,7 @@ def test_header_constants_match_binding():
     assert consts["SSM_REAL_SELECTIVE"] == B.SSM_REAL_SELECTIVE
     assert consts["SSM_REAL_DENSE"] == B.SSM_REAL_DENSE
     assert consts["SSM_COMPLEX_SHARED"] == B.SSM_COMPLEX_SHARED
+    assert consts["SSM_COMPLEX_DENSE"] == B.SSM_COMPLEX_DENSE
     assert consts["SSM_OP_PD_BWD"] == B.SSM_OP_PD_BWD
     assert consts["SSM_OP_COMPLEX_RTRL"] == B.SSM_OP_COMPLEX_RTRL
     assert consts["SSM_OP_OUTPUT_SENS"] == B.SSM_OP_OUTPUT_SENS
@@ -218,6 +219,38 @@ def test_complex_rtrl_host_checks():
     assert rc == status("SSM_ERR_LAYOUT")
     rc = L.ssm_complex_rtrl(ctypes.byref(a), gy, None, None, gl, gt, None, 0, None)
     assert rc == status("SSM_ERR_WORKSPACE")
+
+
+def cdense_args(**over):
+    a = B.ScanArgs(mode=B.SSM_COMPLEX_DENSE, dtype=B.SSM_F32, batch=2, channels=4, length=1000, state=64,
+                   chunk_len=0, a=FAKE * 8, u=FAKE * 16, c=FAKE * 32)
+    for k, v in over.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_complex_dense_host_checks():
+    """Given complex transitions: f32 only, a / u / c required, 8-byte alignment, up to 64 modes,
+    no sensitivity or forward-mode entry points; an empty problem needs no tensors."""
+    L = B.lib()
+    for op in (B.SSM_OP_SCAN_FWD, B.SSM_OP_SCAN_BWD):
+        rc, n = ws_bytes(op, cdense_args())
+        assert rc == 0, L.ssm_last_error_detail()
+    assert ws_bytes(B.SSM_OP_SCAN_FWD, cdense_args(dtype=B.SSM_BF16))[0] == status("SSM_ERR_DTYPE")
+    assert ws_bytes(B.SSM_OP_SCAN_FWD, cdense_args(a=None))[0] == status("SSM_ERR_NULL")
+    assert ws_bytes(B.SSM_OP_SCAN_FWD, cdense_args(u=None))[0] == status("SSM_ERR_NULL")
+    assert ws_bytes(B.SSM_OP_SCAN_FWD, cdense_args(a=FAKE * 8 + 4))[0] == status("SSM_ERR_LAYOUT")
+    assert ws_bytes(B.SSM_OP_SCAN_FWD, cdense_args(state=65))[0] == status("SSM_ERR_SHAPE")
+    assert ws_bytes(B.SSM_OP_SCAN_FWD, cdense_args(chunk_len=64))[0] == status("SSM_ERR_UNSUPPORTED")
+    for op in (B.SSM_OP_COMPLEX_RTRL, B.SSM_OP_IMPULSE, B.SSM_OP_SENS_ROWS):
+        assert ws_bytes(op, cdense_args())[0] == status("SSM_ERR_UNSUPPORTED")
+    assert ws_bytes(B.SSM_OP_SCAN_BWD, cdense_args(length=0, a=None, u=None, c=None)) == (0, 0)
+    # the complex transitions are B*H*L*M complex64: a gradient placed inside them overlaps
+    a = cdense_args()
+    gi = B.ScanBwdIn(gy=FAKE * 64)
+    gr = B.ScanGrads(ga=FAKE * 8 + 2 * 4 * 1000 * 64 * 8 - 64)
+    rc = L.ssm_scan_bwd(ctypes.byref(a), ctypes.byref(gi), ctypes.byref(gr), None, 0, None)
+    assert rc == status("SSM_ERR_LAYOUT"), L.ssm_last_error_detail()
 
 
 def test_pd_ste_host_checks():

@@ -39,6 +39,21 @@ def test_empty_selective(B, D, L):
         assert torch.equal(g["gh0"], ghl)
     assert not g["gA"].any()   # no terms: B = 0 or L = 0, or D = 0 (no entries)
     assert g["gdelta"].shape == (B, D, L) and g["gBm"].shape == (B, L, N)
+    assert not g["gBm"].any() and not g["gC"].any()   # sums over no channels (elements when D = 0 only)
+
+
+@pytest.mark.parametrize("B,D,L", [(2, 3, 0), (2, 0, 50)])
+def test_empty_real_dense(B, D, L):
+    ssm = _ssm()
+    N = 8
+    t = dict(a=_r(B, D, L, N), b=_r(B, D, L, N), C=_r(B, L, N), h0=_r(B, D, N, seed=1))
+    f = ssm.scan_fwd(ssm.SSM_REAL_DENSE, want_h_last=True, **t)
+    ghl = _r(B, D, N, seed=2)
+    g = ssm.scan_bwd(ssm.SSM_REAL_DENSE, gy=_r(B, D, L), gh_last=ghl, **t)
+    torch.cuda.synchronize()
+    assert torch.equal(f["h_last"], t["h0"])
+    assert torch.equal(g["gh0"], ghl)
+    assert g["gC"].shape == (B, L, N) and not g["gC"].any()
 
 
 @pytest.mark.parametrize("B,H,L", [(2, 3, 0), (0, 3, 40)])
@@ -60,6 +75,22 @@ def test_empty_complex(B, H, L):
         assert not g[k].any(), k
     for k in ("glam", "gtheta"):
         assert not rt[k].any(), k
+
+
+@pytest.mark.parametrize("B,H,L", [(2, 3, 0), (0, 3, 40)])
+def test_empty_complex_dense(B, H, L):
+    ssm = _ssm()
+    M = 8
+    t = dict(a=_r(B, H, L, M, dtype=torch.complex64), u=_r(B, H, L, M, dtype=torch.complex64),
+             c=_r(H, M, dtype=torch.complex64), h0=_r(B, H, M, dtype=torch.complex64, seed=3))
+    f = ssm.scan_fwd(ssm.SSM_COMPLEX_DENSE, want_h_last=True, **t)
+    ghl = _r(B, H, M, dtype=torch.complex64, seed=4)
+    g = ssm.scan_bwd(ssm.SSM_COMPLEX_DENSE, gy=_r(B, H, L), gh_last=ghl, **t)
+    torch.cuda.synchronize()
+    assert f["y"].shape == (B, H, L) and g["ga"].shape == (B, H, L, M)
+    assert torch.equal(f["h_last"], t["h0"])
+    assert torch.equal(g["gh0"], ghl)
+    assert not g["gc"].any()
 
 
 @pytest.mark.parametrize("B,H,L", [(2, 3, 0), (0, 3, 70)])

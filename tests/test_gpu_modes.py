@@ -164,6 +164,86 @@ def test_complex_full_config():
 
 
 # ---------------------------------------------------------------------------
+# complex with given transitions
+# ---------------------------------------------------------------------------
+def run_complex_dense(cfg, h0=None, ghl=None):
+    ssm = _ssm()
+    B, H, L, M = cfg["B"], cfg["H"], cfg["L"], cfg["M"]
+    t = dict(a=T(cfg["a"]), u=T(cfg["u"]), c=T(cfg["c"]))
+    h0c = None if h0 is None else h0.astype(np.complex64)
+    ghc = None if ghl is None else ghl.astype(np.complex64)
+    if h0c is not None:
+        t["h0"] = T(h0c)
+    gyt = T(cfg["gy"])
+    glt = None if ghc is None else T(ghc)
+    f = ssm.scan_fwd(ssm.SSM_COMPLEX_DENSE, want_h_last=True, want_ckpt=True, **t)
+    g = ssm.scan_bwd(ssm.SSM_COMPLEX_DENSE, gy=gyt, ckpt=f["ckpt"], gh_last=glt, **t)
+    g2 = ssm.scan_bwd(ssm.SSM_COMPLEX_DENSE, gy=gyt, gh_last=glt, **t)
+    torch.cuda.synchronize()
+    kw = dict(a=cfg["a"], u=cfg["u"], c=cfg["c"], h0=h0c, B=B, H=H, L=L, M=M)
+    y, hl = oracle.complex_dense_fwd(**kw)
+    og = oracle.complex_dense_bwd(**kw, gy=cfg["gy"], ghlast=ghc)
+    errs = {"y": assert_close("y", f["y"], y, **F32), "h_last": assert_close("h_last", f["h_last"], hl, **F32)}
+    for k in ("ga", "gu", "gc", "gh0"):
+        errs[k] = assert_close(k, g[k], og[k], **F32)
+        assert torch.equal(g[k], g2[k]), k
+    return errs
+
+
+def _cplx_state(seed, B, H, M):
+    g = np.random.default_rng(seed)
+    return g.standard_normal((B, H, M)) + 1j * g.standard_normal((B, H, M))
+
+
+def test_complex_dense_small():
+    cfg = synth.make_complex_dense(B=2, H=3, M=64, L=300, seed=1)
+    run_complex_dense(cfg, h0=_cplx_state(2, 2, 3, 64), ghl=_cplx_state(3, 2, 3, 64))
+
+
+@pytest.mark.parametrize("M,L", [(5, 100), (64, 1), (64, 33), (32, 64), (17, 700)])
+def test_complex_dense_shapes(M, L):
+    run_complex_dense(synth.make_complex_dense(B=1, H=2, M=M, L=L, seed=M + L))
+
+
+def test_complex_dense_long_sequence():
+    """One sequence split into many segments (summary, combine and main passes)."""
+    run_complex_dense(synth.make_complex_dense(B=1, H=1, M=64, L=20000, seed=7), h0=_cplx_state(8, 1, 1, 64),
+                      ghl=_cplx_state(9, 1, 1, 64))
+
+
+@pytest.mark.parametrize("case", ["a_one", "a_zero", "rotation_only", "u_zero"])
+def test_complex_dense_degenerate_inputs(case):
+    """a = 1 (pure accumulation), a = 0 (the state restarts every step), |a| = 1 (rotation only), u = 0; nonzero
+    h0 and gh_last carry state and adjoint."""
+    cfg = synth.make_complex_dense(B=2, H=3, M=64, L=200, seed=33)
+    a = cfg["a"]
+    if case == "a_one":
+        cfg["a"] = np.ones_like(a)
+    elif case == "a_zero":
+        cfg["a"] = np.zeros_like(a)
+    elif case == "rotation_only":
+        cfg["a"] = (a / np.abs(a)).astype(np.complex64)
+    else:
+        cfg["u"] = np.zeros_like(cfg["u"])
+    run_complex_dense(cfg, h0=_cplx_state(34, 2, 3, 64), ghl=_cplx_state(35, 2, 3, 64))
+
+
+def test_complex_dense_shared_control_transitions():
+    """Transitions of the shared-control form a = lam^r e^{i phi theta}, formed in numpy and rounded to complex64:
+    slow modes (|a| up to 0.9993) with long horizons through the given-transition kernels."""
+    cfg = synth.make_complex(B=2, H=3, M=64, L=1500, seed=36)
+    a = (cfg["lam"].astype(np.float64)[None, :, None, :] ** cfg["r"].astype(np.float64)[:, :, :, None]) * \
+        np.exp(1j * cfg["phi"].astype(np.float64)[:, :, :, None] * cfg["theta"].astype(np.float64)[None, :, None, :])
+    dense = dict(B=2, H=3, M=64, L=1500, a=a.astype(np.complex64), u=cfg["u"], c=cfg["c"], gy=cfg["gy"])
+    run_complex_dense(dense, h0=_cplx_state(37, 2, 3, 64), ghl=_cplx_state(38, 2, 3, 64))
+
+
+def test_complex_dense_full_config():
+    """B=16 H=8 M=64 L=2048 complex64, seed 0: every output compared element-wise."""
+    run_complex_dense(synth.make_complex_dense(B=16, H=8, M=64, L=2048, seed=0))
+
+
+# ---------------------------------------------------------------------------
 # complex: forward-mode (RTRL) gradients of lambda and theta
 # ---------------------------------------------------------------------------
 def run_complex_rtrl(cfg, h0=None, ghl=None):
