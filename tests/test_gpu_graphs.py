@@ -120,6 +120,40 @@ def test_graph_complex_fwd_bwd_rtrl():
     _replay_and_check(g, outs, inp, [mk(1), mk(2)], eager)
 
 
+def test_graph_complex_dense_fwd_bwd():
+    """Given complex transitions: forward with checkpoints, backward from them and backward recomputing them."""
+    ssm = _ssm()
+    Cx = ssm.SSM_COMPLEX_DENSE
+
+    def mk(seed):
+        cfg = synth.make_complex_dense(B=2, H=3, M=64, L=300, seed=seed)
+        return {k: T(cfg[k]) for k in ("a", "u", "c", "gy")}
+
+    inp = mk(0)
+    want = ("ga", "gu", "gc", "gh0")
+
+    def eager(i):
+        t = {k: v for k, v in i.items() if k != "gy"}
+        f = ssm.scan_fwd(Cx, want_h_last=True, want_ckpt=True, **t)
+        g = ssm.scan_bwd(Cx, gy=i["gy"], ckpt=f["ckpt"], want=want, **t)
+        g2 = ssm.scan_bwd(Cx, gy=i["gy"], want=("ga", "gc"), **t)
+        return {"y": f["y"], "h_last": f["h_last"], "ckpt": f["ckpt"], **g, "ga2": g2["ga"], "gc2": g2["gc"]}
+
+    outs = eager(inp)
+    t = {k: v for k, v in inp.items() if k != "gy"}
+    fo = {k: outs[k] for k in ("y", "h_last", "ckpt")}
+    go = {k: outs[k] for k in want}
+    go2 = {"ga": outs["ga2"], "gc": outs["gc2"]}
+
+    def step():
+        ssm.scan_fwd(Cx, want_h_last=True, want_ckpt=True, out=fo, **t)
+        ssm.scan_bwd(Cx, gy=inp["gy"], ckpt=fo["ckpt"], want=want, out=go, **t)
+        ssm.scan_bwd(Cx, gy=inp["gy"], want=("ga", "gc"), out=go2, **t)
+
+    g = _capture(step)
+    _replay_and_check(g, outs, inp, [mk(1), mk(2)], eager)
+
+
 def test_graph_pd_fwd_bwd_ste():
     ssm = _ssm()
 
