@@ -613,14 +613,14 @@ __global__ __launch_bounds__(256) void reduce_parts_btn_kernel(const float* __re
     if (n < N) {
         const float* src = part + ((size_t)b * N + n) * L + t;
         if ((L & 3) == 0 && t < L) {
-            // eight loads in flight per thread; the additions stay in block order
+            // sixteen loads in flight per thread; the additions stay in block order
             int k = 0;
-            for (; k + 8 <= nblk; k += 8) {
-                float4 v[8];
+            for (; k + 16 <= nblk; k += 16) {
+                float4 v[16];
 #pragma unroll
-                for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const float4*>(src + (size_t)(k + u) * stride);
+                for (int u = 0; u < 16; ++u) v[u] = *reinterpret_cast<const float4*>(src + (size_t)(k + u) * stride);
 #pragma unroll
-                for (int u = 0; u < 8; ++u) { s[0] += v[u].x; s[1] += v[u].y; s[2] += v[u].z; s[3] += v[u].w; }
+                for (int u = 0; u < 16; ++u) { s[0] += v[u].x; s[1] += v[u].y; s[2] += v[u].z; s[3] += v[u].w; }
             }
             for (; k < nblk; ++k) {
                 const float4 v = *reinterpret_cast<const float4*>(src + (size_t)k * stride);
@@ -639,6 +639,52 @@ __global__ __launch_bounds__(256) void reduce_parts_btn_kernel(const float* __re
     const int steps = min(64, L - t0);
     T* dst = out + ((size_t)b * L + t0) * N;
     for (int i = threadIdx.x; i < steps * N; i += 256) dst[i] = from_f32<T>(tile[i / N][i % N]);
+}
+// The same sums when N and L are multiples of 4: wave w of the workgroup takes
+// state n = 4 * blockIdx.z' + w and lane l the steps t0 + 4l .. t0 + 4l + 3, so
+// every load instruction reads 1 KB of one partial row contiguously; each
+// thread then stores the four states of one step.  Additions in block order,
+// as above (the two kernels give identical sums).
+template <typename T>
+__global__ __launch_bounds__(256) void reduce_parts_btn4_kernel(const float* __restrict__ partB,
+                                                                const float* __restrict__ partC, int nblk, int B,
+                                                                int N, int L, T* __restrict__ outB,
+                                                                T* __restrict__ outC) {
+    __shared__ float tile[256][5];
+    const int nq = N >> 2;
+    const int which = blockIdx.z / nq, n0 = 4 * (blockIdx.z - which * nq);
+    const float* __restrict__ part = which ? partC : partB;
+    T* __restrict__ out = which ? outC : outB;
+    if (!part || !out) return;
+    const int b = blockIdx.y, t0 = blockIdx.x * 256;
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+    const int t = t0 + 4 * l;
+    const size_t stride = (size_t)B * N * L;
+    float s[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (t < L) {
+        const float* src = part + ((size_t)b * N + n0 + w) * L + t;
+        int k = 0;
+        for (; k + 16 <= nblk; k += 16) {
+            float4 v[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) v[u] = *reinterpret_cast<const float4*>(src + (size_t)(k + u) * stride);
+#pragma unroll
+            for (int u = 0; u < 16; ++u) { s[0] += v[u].x; s[1] += v[u].y; s[2] += v[u].z; s[3] += v[u].w; }
+        }
+        for (; k < nblk; ++k) {
+            const float4 v = *reinterpret_cast<const float4*>(src + (size_t)k * stride);
+            s[0] += v.x; s[1] += v.y; s[2] += v.z; s[3] += v.w;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) tile[4 * l + i][w] = s[i];
+    __syncthreads();
+    const int tt = t0 + threadIdx.x;
+    if (tt < L) {
+        T* dst = out + ((size_t)b * L + tt) * N + n0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[i] = from_f32<T>(tile[threadIdx.x][i]);
+    }
 }
 // partial (B,G,D,N) -> out (D,N)
 __global__ void reduce_parts_dn_kernel(const float* __restrict__ part, int B, int G, int D, int N,
@@ -1093,6 +1139,16 @@ hipError_t launch_seg_combine_rev(const float* Q, const float* R, const float* n
 }
 hipError_t launch_reduce_parts_btn(const float* partB, const float* partC, int nblk, int B, int N, int L,
                                    void* outB, void* outC, int dtype, hipStream_t st) {
+    if (N % 4 == 0 && L % 4 == 0) {
+        dim3 g4((unsigned)((L + 255) / 256), (unsigned)B, (unsigned)(2 * (N / 4)));
+        if (dtype == 0)
+            reduce_parts_btn4_kernel<float><<<g4, 256, 0, st>>>(partB, partC, nblk, B, N, L, (float*)outB,
+                                                                (float*)outC);
+        else
+            reduce_parts_btn4_kernel<bf16_t><<<g4, 256, 0, st>>>(partB, partC, nblk, B, N, L, (bf16_t*)outB,
+                                                                 (bf16_t*)outC);
+        return hipGetLastError();
+    }
     dim3 grid((unsigned)((L + 63) / 64), (unsigned)B, 2);
     if (dtype == 0)
         reduce_parts_btn_kernel<float><<<grid, 256, 0, st>>>(partB, partC, nblk, B, N, L, (float*)outB, (float*)outC);
