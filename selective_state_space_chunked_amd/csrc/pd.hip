@@ -128,6 +128,24 @@ __device__ __forceinline__ void pd_with_rounds(int maxc, F&& body) {
 
 template <typename T>
 __device__ __forceinline__ int pd_argmax(const T* __restrict__ lg, int K) {
+    // 16-byte loads when the row allows; the comparisons run in the same order
+    constexpr int V = 16 / sizeof(T);
+    if (K % V == 0 && (reinterpret_cast<uintptr_t>(lg) & 15) == 0) {
+        int best = 0;
+        float bv = 0.0f;
+        for (int k0 = 0; k0 < K; k0 += V) {
+            const uint4 w = *reinterpret_cast<const uint4*>(lg + k0);
+            T e[V];
+            __builtin_memcpy(e, &w, 16);
+#pragma unroll
+            for (int u = 0; u < V; ++u) {
+                const float v = to_f32(e[u]);
+                if (k0 + u == 0) bv = v;
+                else if (v > bv) { bv = v; best = k0 + u; }
+            }
+        }
+        return best;
+    }
     int best = 0;
     float bv = to_f32(lg[0]);
     for (int k = 1; k < K; ++k) {
