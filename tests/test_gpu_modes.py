@@ -238,6 +238,33 @@ def test_complex_dense_shared_control_transitions():
     run_complex_dense(dense, h0=_cplx_state(37, 2, 3, 64), ghl=_cplx_state(38, 2, 3, 64))
 
 
+def test_complex_checkpoints_are_chunk_states():
+    """ckpt[:, :, c] of both complex modes is the state entering 32-step chunk c: the oracle's final state of the
+    first 32c steps (c = 0 holds h0); the sequence is long enough to be split into segments."""
+    ssm = _ssm()
+    B, H, M, L = 1, 2, 64, 700
+    h0 = _cplx_state(40, B, H, M).astype(np.complex64)
+    sh = synth.make_complex(B=B, H=H, M=M, L=L, seed=41)
+    dn = synth.make_complex_dense(B=B, H=H, M=M, L=L, seed=42)
+    fs = ssm.scan_fwd(ssm.SSM_COMPLEX_SHARED, want_y=False, want_ckpt=True, h0=T(h0),
+                      **{k: T(sh[k]) for k in ("r", "phi", "lam", "theta", "u", "c")})
+    fd = ssm.scan_fwd(ssm.SSM_COMPLEX_DENSE, want_y=False, want_ckpt=True, h0=T(h0),
+                      **{k: T(dn[k]) for k in ("a", "u", "c")})
+    torch.cuda.synchronize()
+    nc = -(-L // 32)
+    for ck in (fs["ckpt"], fd["ckpt"]):
+        assert ck.shape == (B, H, nc, M)
+        assert torch.equal(ck[:, :, 0].cpu(), torch.from_numpy(h0))
+    for c in (1, 2, 7, 8, 9, nc - 1):
+        Lc = 32 * c
+        _, hs = oracle.complex_fwd(r=sh["r"][:, :, :Lc], phi=sh["phi"][:, :, :Lc], lam=sh["lam"], theta=sh["theta"],
+                                   u=sh["u"][:, :, :Lc], c=sh["c"], h0=h0, B=B, H=H, L=Lc, M=M)
+        _, hd = oracle.complex_dense_fwd(a=dn["a"][:, :, :Lc], u=dn["u"][:, :, :Lc], c=dn["c"], h0=h0,
+                                         B=B, H=H, L=Lc, M=M)
+        assert_close(f"shared ckpt[{c}]", fs["ckpt"][:, :, c], hs, **F32)
+        assert_close(f"dense ckpt[{c}]", fd["ckpt"][:, :, c], hd, **F32)
+
+
 def test_complex_dense_full_config():
     """B=16 H=8 M=64 L=2048 complex64, seed 0: every output compared element-wise."""
     run_complex_dense(synth.make_complex_dense(B=16, H=8, M=64, L=2048, seed=0))
