@@ -363,6 +363,29 @@ def run_pd(cfg, h0=None, ghl=None, use_sel=False):
         assert torch.equal(g[k], g2[k]), k
 
 
+def test_pd_checkpoints_are_chunk_states():
+    """ckpt[:, :, c] of the PD scan is the state entering 64-step chunk c: the oracle's final state of the first
+    64c steps with the same selections (c = 0 holds h0)."""
+    ssm = _ssm()
+    B, H, N, K, L = 2, 3, 16, 8, 1000
+    cfg = synth.make_pd(B=B, H=H, N=N, L=L, K=K, seed=43)
+    h0 = np.random.default_rng(44).standard_normal((B, H, N)).astype(np.float32)
+    t = dict(logits=T(cfg["logits"]), dict=T(cfg["dict"]), d=T(cfg["d"]), b=T(cfg["b"]), C=T(cfg["C"]), h0=T(h0))
+    f = ssm.pd_scan_fwd(want_ckpt=True, **t)
+    torch.cuda.synchronize()
+    osel = oracle.pd_select(cfg["logits"])
+    assert np.array_equal(f["sel"].cpu().numpy(), osel)
+    ck = f["ckpt"]
+    nc = -(-L // 64)
+    assert ck.shape == (B, H, nc, N)
+    assert torch.equal(ck[:, :, 0].cpu(), torch.from_numpy(h0))
+    for c in (1, 2, 5, nc - 1):
+        Lc = 64 * c
+        _, hl = oracle.pd_fwd(sel=osel[:, :, :Lc], dict=cfg["dict"], d=cfg["d"][:, :, :Lc], b=cfg["b"][:, :, :Lc],
+                              C=cfg["C"][:, :, :Lc], h0=h0, B=B, H=H, L=Lc, N=N, K=K)
+        assert_close(f"ckpt[{c}]", ck[:, :, c], hl, **F32)
+
+
 def run_pd_ste(cfg, tau, h0=None, ghl=None, with_ckpt=True):
     """Straight-through surrogate gradient of the selection scores against the
     oracle; the other PD gradients must be unchanged by asking for it."""
