@@ -56,6 +56,27 @@ def test_dense_small_state():
     run_dense(1, 5, 200, 3, seed=3)
 
 
+def test_dense_checkpoints_are_chunk_states():
+    """ckpt[:, :, c] of the dense real scan is the state entering 32-step chunk c (c = 0 holds h0)."""
+    ssm = _ssm()
+    B, D, L, N = 2, 20, 1000, 16
+    g = np.random.default_rng(45)
+    a = g.uniform(0.5, 1.0, (B, D, L, N)).astype(np.float32)
+    b = (g.standard_normal((B, D, L, N)) / 4).astype(np.float32)
+    C = (g.standard_normal((B, L, N)) / 4).astype(np.float32)
+    h0 = g.standard_normal((B, D, N)).astype(np.float32)
+    f = ssm.scan_fwd(ssm.SSM_REAL_DENSE, want_y=False, want_ckpt=True, a=T(a), b=T(b), C=T(C), h0=T(h0))
+    torch.cuda.synchronize()
+    ck = f["ckpt"]
+    nc = -(-L // 32)
+    assert ck.shape == (B, D, nc, N)
+    assert torch.equal(ck[:, :, 0].cpu(), torch.from_numpy(h0))
+    for c in (1, 2, 8, 17, nc - 1):
+        Lc = 32 * c
+        _, hl = oracle.real_fwd(a=a[:, :, :Lc], b=b[:, :, :Lc], C=C[:, :Lc], h0=h0, B=B, D=D, L=Lc, N=N)
+        assert_close(f"ckpt[{c}]", ck[:, :, c], hl, **F32)
+
+
 def test_dense_many_segments():
     run_dense(1, 16, 3000, 16, seed=4, h0=True)
 
