@@ -116,7 +116,8 @@ extern "C" {
  * n_chunks = ceil(L / T).  batch, channels and length may be 0 (an empty
  * problem): nothing is read, outputs with no elements are not touched (their
  * pointers may be NULL), h_last becomes h0 (or 0), gh0 becomes gh_last (or 0)
- * and the parameter gradients 0; the sensitivity calls still need
+ * and the parameter gradients 0 (gBm and gC, sums over channels, are zero when
+ * channels is 0 and batch, length are not); the sensitivity calls still need
  * 0 <= t_out < L.  state must be >= 1.
  */
 typedef struct {
