@@ -316,6 +316,21 @@ __device__ __forceinline__ void pd_ste_block(const PDParams& p, const PDShared& 
         }
         const float rz = 1.0f / zs;
         dot *= rz;
+        constexpr int V = 16 / sizeof(T);   // scores per 16-byte store
+        if (K % V == 0 && (reinterpret_cast<uintptr_t>(o) & 15) == 0) {
+#pragma unroll
+            for (int k0 = 0; k0 < 16; k0 += V) {
+                if (k0 < K) {
+                    T v[V];
+#pragma unroll
+                    for (int u = 0; u < V; ++u) v[u] = from_f32<T>(e[k0 + u] * rz * (g[k0 + u] - dot) * p.inv_tau);
+                    uint4 w;
+                    __builtin_memcpy(&w, v, 16);
+                    *reinterpret_cast<uint4*>(o + k0) = w;
+                }
+            }
+            return;
+        }
 #pragma unroll
         for (int k = 0; k < 16; ++k)
             if (k < K) o[k] = from_f32<T>(e[k] * rz * (g[k] - dot) * p.inv_tau);
@@ -398,8 +413,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(STE >= 0 ? 
             float xl[16];  // STE == 16: this lane's scores of step tl
             if (STE == 16) {
                 const T* xs = (const T*)p.ste_logits + (srow + tl) * p.K;
+                constexpr int V = 16 / sizeof(T);   // scores per 16-byte load
+                if (tl < L && p.K % V == 0 && (reinterpret_cast<uintptr_t>(xs) & 15) == 0) {
 #pragma unroll
-                for (int k = 0; k < 16; ++k) xl[k] = (k < p.K && tl < L) ? to_f32(xs[k]) : -INFINITY;
+                    for (int k0 = 0; k0 < 16; k0 += V) {
+                        T e[V];
+                        if (k0 < p.K) {
+                            const uint4 w = *reinterpret_cast<const uint4*>(xs + k0);
+                            __builtin_memcpy(e, &w, 16);
+                        }
+#pragma unroll
+                        for (int u = 0; u < V; ++u) xl[k0 + u] = k0 < p.K ? to_f32(e[u]) : -INFINITY;
+                    }
+                } else {
+#pragma unroll
+                    for (int k = 0; k < 16; ++k) xl[k] = (k < p.K && tl < L) ? to_f32(xs[k]) : -INFINITY;
+                }
             }
             float dv[16], cv[16];
             pd_load16<T, NT>(dbase, tb, L, N, j, dv);
