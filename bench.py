@@ -211,7 +211,9 @@ def w_sens_rows(steps, warmup):
     BDL, BLN = B * D * L, B * L * N
     byts = (BDL + BLN) * 4 + R * BDL * 4   # read delta, B; write R rows of s
     return dict(name="sens-rows", elements=R * BDL * N, ms=ms, kernels=profile_kernels(step, reps=2),
-                bytes_total=byts, config=dict(B=B, D=D, N=N, L=L, rows=R, streams="f32", t_out0=L - R))
+                bytes_total=byts, config=dict(B=B, D=D, N=N, L=L, rows=R, streams="f32", t_out0=L - R),
+                note=f"elements counts every output row: {R} rows x B*D*N*L, so el_per_s is not comparable "
+                     "with the single-output workloads")
 
 
 def w_output_sens(steps, warmup):
@@ -385,9 +387,12 @@ def w_dense(steps, warmup):
 
 def summarize(w):
     ms = w["ms"]
-    return dict(el_per_s=w["elements"] / (ms * 1e-3), ms_per_step=ms,
-                hbm_frac=w["bytes_total"] / (ms * 1e-3) / HBM_PEAK, algorithmic_bytes=w["bytes_total"],
-                config=w["config"], kernels_ms={k: round(v[0], 4) for k, v in w["kernels"].items()})
+    r = dict(el_per_s=w["elements"] / (ms * 1e-3), ms_per_step=ms,
+             hbm_frac=w["bytes_total"] / (ms * 1e-3) / HBM_PEAK, algorithmic_bytes=w["bytes_total"],
+             config=w["config"], kernels_ms={k: round(v[0], 4) for k, v in w["kernels"].items()})
+    if w.get("note"):
+        r["note"] = w["note"]
+    return r
 
 
 def cpu_baseline(inputs, batches):
@@ -569,6 +574,8 @@ def main():
         "metric": METRIC, "value": s["el_per_s"], "unit": "elements/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": s["ms_per_step"], "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "dtype_note": "arithmetic (state, recurrences, accumulation) in fp32; the streams x, delta, B, C, gy, "
+                      "y and the gradients are bf16 in HBM",
         "config": {"workload": "real-mamba: selective scan fwd+bwd, B=8 D=2048 N=16 L=4096, bf16 streams, "
                                "fp32 state, chunk 256", **head["config"]},
         "hbm_frac": s["hbm_frac"], "algorithmic_bytes_per_step": head["bytes_total"],

@@ -201,9 +201,11 @@ typedef struct {
     int64_t batch, heads, length, state, dict_size, chunk_len;
     const void*    logits; /* (B,H,L,K) dtype selection scores; may be NULL if sel is given */
     const int32_t* sel;    /* (B,H,L) selected entries; input alternative to logits (used
-                              when logits is NULL); values must lie in [0,K)               */
+                              when logits is NULL); values must lie in [0,K) (values outside
+                              are a precondition violation: every pass clamps them to
+                              [0,K), and pd_scan_fwd reports the clamped selection)        */
     const int32_t* dict;   /* (H,K,N): dict[h,k,j] = row of the one in column j of entry k,
-                              values in [0,N)                                              */
+                              values in [0,N) (outside: clamped to [0,N) by every pass)    */
     const void*  d;        /* (B,H,L,N) dtype diagonal d_t                                  */
     const void*  b;        /* (B,H,L,N) dtype input term b_t                                */
     const void*  C;        /* (B,H,L,N) dtype readout C_t                                   */

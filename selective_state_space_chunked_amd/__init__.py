@@ -25,4 +25,5 @@ from .binding import (  # noqa: F401
     scan_bwd,
     scan_fwd,
     sensitivity_rows,
+    set_allocator,
 )

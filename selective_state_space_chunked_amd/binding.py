@@ -1,10 +1,12 @@
 """ctypes binding of libssmscan.so (include/ssmscan.h).
 
-Argument marshalling only: tensors are checked for device, dtype and
-contiguity, outputs and the workspace are allocated with torch on the
-tensors' device, and every step of the scan runs in the library's HIP
-kernels on torch's current stream.  There is no CPU fallback: if the library
-is missing or a call fails, this module raises.
+Argument marshalling only: input tensors and caller-supplied outputs
+(``out=``) are checked for device, dtype, shape and contiguity, missing
+outputs and the workspace are allocated on the tensors' device (with
+torch.empty, or with the allocator installed by ``set_allocator``), and every
+step of the scan runs in the library's HIP kernels on torch's current stream.
+There is no CPU fallback: tensors that are not on a GPU are rejected, and if
+the library is missing or a call fails, this module raises.
 """
 from __future__ import annotations
 
@@ -132,12 +134,49 @@ def _need(t, name, dtype=None, shape=None, device=None):
     return t
 
 
+_allocator = None
+
+
+def set_allocator(fn):
+    """Install ``fn(shape, dtype, device, role) -> tensor`` for the outputs this module allocates
+    (role "output") and the workspaces (role "workspace", uint8); None restores torch.empty.  A caller
+    can route allocations to its own memory pool, or fill them with a sentinel (tests fill outputs
+    with NaN, integers with -1, so an element a kernel never writes cannot pass as a result)."""
+    global _allocator
+    _allocator = fn
+
+
+def _alloc(shape, dtype, device, role="output"):
+    if _allocator is not None:
+        t = _allocator(tuple(shape), dtype, device, role)
+        if tuple(t.shape) != tuple(shape) or t.dtype != dtype or t.device != torch.device(device) \
+                or not t.is_contiguous():
+            raise ValueError(f"allocator returned {tuple(t.shape)} {t.dtype} on {t.device}, "
+                             f"expected {tuple(shape)} {dtype} on {device}")
+        return t
+    return torch.empty(shape, dtype=dtype, device=device)
+
+
+def _out(out, key, shape, dtype, device):
+    """out[key]: the caller's tensor, checked like an input, or a new one of the given shape and dtype."""
+    if key in out and out[key] is not None:
+        return _need(out[key], f"out[{key!r}]", dtype, shape, device)
+    out[key] = _alloc(shape, dtype, device)
+    return out[key]
+
+
+def _on_gpu(device):
+    """The library takes device pointers only: host tensors would reach the kernels as bad addresses."""
+    if torch.device(device).type != "cuda":
+        raise ValueError(f"tensors must be on a GPU device (got {device}); there is no CPU path")
+
+
 def _workspace(op, args_ptr, device):
     n = ctypes.c_size_t(0)
     _check(lib().ssm_workspace_bytes(op, args_ptr, ctypes.byref(n)))
     if n.value == 0:
         return None, 0
-    ws = torch.empty(n.value + 256, dtype=torch.uint8, device=device)
+    ws = _alloc((n.value + 256,), torch.uint8, device, "workspace")
     off = (-ws.data_ptr()) % 256
     return ws[off:off + n.value], n.value
 
@@ -237,12 +276,11 @@ def scan_fwd(mode, *, want_y=True, want_h_last=False, want_ckpt=False, chunk_len
     ydt = _stream_dtype(mode, tensors)
     sdt = torch.complex64 if mode in _COMPLEX_MODES else torch.float32
     nc = n_chunks(L, _chunk(mode, chunk_len))
-    if want_y and "y" not in out:
-        out["y"] = torch.empty((Bsz, D, L), dtype=ydt, device=dev)
-    if want_h_last and "h_last" not in out:
-        out["h_last"] = torch.empty((Bsz, D, N), dtype=sdt, device=dev)
-    if want_ckpt and "ckpt" not in out:
-        out["ckpt"] = torch.empty((Bsz, D, nc, N), dtype=sdt, device=dev)
+    for k, want, shp, dt in (("y", want_y, (Bsz, D, L), ydt), ("h_last", want_h_last, (Bsz, D, N), sdt),
+                             ("ckpt", want_ckpt, (Bsz, D, nc, N), sdt)):
+        if want or out.get(k) is not None:
+            _out(out, k, shp, dt, dev)
+    _on_gpu(dev)
     o = ScanFwdOut(y=_ptr(out.get("y")), h_last=_ptr(out.get("h_last")), ckpt=_ptr(out.get("ckpt")))
     ws, nws = _workspace(SSM_OP_SCAN_FWD, ctypes.byref(args), dev)
     _check(lib().ssm_scan_fwd(ctypes.byref(args), ctypes.byref(o), _ptr(ws), nws, _stream(dev)))
@@ -277,12 +315,13 @@ def scan_bwd(mode, *, gy, gh_last=None, ckpt=None, want=None, chunk_len=0, out=N
         "gdelta_bias": ((D,), torch.float32),
     }
     out = dict(out or {})
-    for k in want:
-        if k not in _GRADS[mode] and not (k == "gdelta_bias" and mode == SSM_REAL_SELECTIVE):
+    def exists(k):
+        return k in _GRADS[mode] or (k == "gdelta_bias" and mode == SSM_REAL_SELECTIVE)
+    for k in set(want) | {k for k, v in out.items() if v is not None}:
+        if not exists(k):
             raise ValueError(f"gradient {k} does not exist for mode {mode}")
-        if k not in out:
-            shp, dt = shapes[k]
-            out[k] = torch.empty(shp, dtype=dt, device=dev)
+        _out(out, k, *shapes[k], dev)
+    _on_gpu(dev)
     g = ScanGrads(**{f[0]: _ptr(out.get(f[0])) for f in ScanGrads._fields_})
     i = ScanBwdIn(gy=_ptr(gy), gh_last=_ptr(gh_last), ckpt=_ptr(ckpt))
     ws, nws = _workspace(SSM_OP_SCAN_BWD, ctypes.byref(args), dev)
@@ -295,10 +334,10 @@ def impulse_sensitivity(*, t_out=-1, want_y=True, chunk_len=0, out=None, **tenso
     args, (Bsz, D, L, N), dev = _scan_args(SSM_REAL_SELECTIVE, chunk_len=chunk_len, **tensors)
     dt = tensors["delta"].dtype
     out = dict(out or {})
-    if "s" not in out:
-        out["s"] = torch.empty((Bsz, D, L), dtype=dt, device=dev)
-    if want_y and "y" not in out:
-        out["y"] = torch.empty((Bsz, D, L), dtype=dt, device=dev)
+    _out(out, "s", (Bsz, D, L), dt, dev)
+    if want_y or out.get("y") is not None:
+        _out(out, "y", (Bsz, D, L), dt, dev)
+    _on_gpu(dev)
     ws, nws = _workspace(SSM_OP_IMPULSE, ctypes.byref(args), dev)
     _check(lib().ssm_impulse_sensitivity(ctypes.byref(args), int(t_out), _ptr(out.get("y")), _ptr(out["s"]),
                                          _ptr(ws), nws, _stream(dev)))
@@ -311,8 +350,9 @@ def output_sensitivity(*, t_out=-1, want_y=False, want_s_x=True, chunk_len=0, ou
     dt = tensors["delta"].dtype
     out = dict(out or {})
     for k, want in (("s_delta", True), ("s_x", want_s_x), ("y", want_y)):
-        if want and k not in out:
-            out[k] = torch.empty((Bsz, D, L), dtype=dt, device=dev)
+        if want or out.get(k) is not None:
+            _out(out, k, (Bsz, D, L), dt, dev)
+    _on_gpu(dev)
     ws, nws = _workspace(SSM_OP_OUTPUT_SENS, ctypes.byref(args), dev)
     _check(lib().ssm_output_sensitivity(ctypes.byref(args), int(t_out), _ptr(out.get("y")), _ptr(out.get("s_x")),
                                         _ptr(out["s_delta"]), _ptr(ws), nws, _stream(dev)))
@@ -323,7 +363,9 @@ def sensitivity_rows(*, t_out0, rows, out=None, **tensors):
     """s[r,b,d,t] = d y[b,d,t_out0+r] / d x[b,d,t] for r < rows (rows 1..16) of a selective real scan."""
     args, (Bsz, D, L, N), dev = _scan_args(SSM_REAL_SELECTIVE, **tensors)
     dt = tensors["delta"].dtype
-    s = out if out is not None else torch.empty((int(rows), Bsz, D, L), dtype=dt, device=dev)
+    shp = (int(rows), Bsz, D, L)
+    s = _need(out, "out", dt, shp, dev) if out is not None else _alloc(shp, dt, dev)
+    _on_gpu(dev)
     ws, nws = _workspace(SSM_OP_SENS_ROWS, ctypes.byref(args), dev)
     _check(lib().ssm_sensitivity_rows(ctypes.byref(args), int(t_out0), int(rows), _ptr(s), _ptr(ws), nws,
                                       _stream(dev)))
@@ -342,10 +384,10 @@ def complex_rtrl(*, gy, gh_last=None, want_y=True, chunk_len=0, out=None, **tens
     _need(gh_last, "gh_last", torch.complex64, (Bsz, H, M), dev)
     out = dict(out or {})
     for k in ("glam", "gtheta"):
-        if k not in out:
-            out[k] = torch.empty((H, M), dtype=torch.float32, device=dev)
-    if want_y and "y" not in out:
-        out["y"] = torch.empty((Bsz, H, L), dtype=ydt, device=dev)
+        _out(out, k, (H, M), torch.float32, dev)
+    if want_y or out.get("y") is not None:
+        _out(out, "y", (Bsz, H, L), ydt, dev)
+    _on_gpu(dev)
     ws, nws = _workspace(SSM_OP_COMPLEX_RTRL, ctypes.byref(args), dev)
     _check(lib().ssm_complex_rtrl(ctypes.byref(args), _ptr(gy), _ptr(gh_last), _ptr(out.get("y")),
                                   _ptr(out["glam"]), _ptr(out["gtheta"]), _ptr(ws), nws, _stream(dev)))
@@ -383,14 +425,13 @@ def pd_scan_fwd(*, want_y=True, want_sel=True, want_h_last=False, want_ckpt=Fals
     args, (Bsz, H, L, N, K), dev = _pd_args(chunk_len=chunk_len, **tensors)
     nc = n_chunks(L, chunk_len or 64)
     out = dict(out or {})
-    if want_y and "y" not in out:
-        out["y"] = torch.empty((Bsz, H, L), dtype=tensors["d"].dtype, device=dev)
-    if want_sel and "sel" not in out:
-        out["sel"] = torch.empty((Bsz, H, L), dtype=torch.int32, device=dev)
-    if want_h_last and "h_last" not in out:
-        out["h_last"] = torch.empty((Bsz, H, N), dtype=torch.float32, device=dev)
-    if want_ckpt and "ckpt" not in out:
-        out["ckpt"] = torch.empty((Bsz, H, nc, N), dtype=torch.float32, device=dev)
+    for k, want, shp, dt in (("y", want_y, (Bsz, H, L), tensors["d"].dtype),
+                             ("sel", want_sel, (Bsz, H, L), torch.int32),
+                             ("h_last", want_h_last, (Bsz, H, N), torch.float32),
+                             ("ckpt", want_ckpt, (Bsz, H, nc, N), torch.float32)):
+        if want or out.get(k) is not None:
+            _out(out, k, shp, dt, dev)
+    _on_gpu(dev)
     o = PDFwdOut(y=_ptr(out.get("y")), sel=_ptr(out.get("sel")), h_last=_ptr(out.get("h_last")),
                  ckpt=_ptr(out.get("ckpt")))
     ws, nws = _workspace(SSM_OP_PD_FWD, ctypes.byref(args), dev)
@@ -413,11 +454,11 @@ def pd_scan_bwd(*, gy, gh_last=None, ckpt=None, want=("gd", "gb", "gC", "gh0"), 
     out = dict(out or {})
     shapes = {"gd": (Bsz, H, L, N), "gb": (Bsz, H, L, N), "gC": (Bsz, H, L, N), "gh0": (Bsz, H, N),
               "glogits": (Bsz, H, L, K)}
-    for k in want:
+    for k in set(want) | {k for k, v in out.items() if v is not None}:
         if k not in shapes:
             raise ValueError(f"unknown PD gradient {k}")
-        if k not in out:
-            out[k] = torch.empty(shapes[k], dtype=torch.float32 if k == "gh0" else st, device=dev)
+        _out(out, k, shapes[k], torch.float32 if k == "gh0" else st, dev)
+    _on_gpu(dev)
     g = PDGrads(**{f[0]: _ptr(out.get(f[0])) for f in PDGrads._fields_})
     i = PDBwdIn(gy=_ptr(gy), gh_last=_ptr(gh_last), ckpt=_ptr(ckpt), ste_logits=_ptr(ste_logits), tau=float(tau))
     ws, nws = _workspace(SSM_OP_PD_BWD, ctypes.byref(args), dev)

@@ -169,6 +169,8 @@ struct PDParams {
     int dtype;                     // 0 fp32, 1 bf16 streams
 };
 hipError_t launch_pd_prep(const PDParams& p, hipStream_t st);
+// out[i] = sel[i] clamped to [0, K), as the kernels read a given selection
+hipError_t launch_pd_sel_copy(const int32_t* sel, int32_t* out, size_t n, int K, hipStream_t st);
 hipError_t launch_pd_fwd(const PDParams& p, bool summary, hipStream_t st);
 hipError_t launch_pd_combine_fwd(const PDParams& p, hipStream_t st);
 hipError_t launch_pd_bwd(const PDParams& p, bool summary, hipStream_t st);

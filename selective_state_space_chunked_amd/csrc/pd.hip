@@ -46,8 +46,10 @@ __global__ void pd_prep_kernel(const int32_t* __restrict__ dict, int8_t* __restr
     const int hk = idx / N, i = idx - hk * N;
     const int32_t* col = dict + (size_t)hk * N;
     int c = 0;
+    // entries outside [0, N) are clamped exactly as pd_load_tables clamps them, so the
+    // gather lists and the compositions see the same dictionary
     for (int j = 0; j < N; ++j)
-        if (col[j] == i) pre[(size_t)hk * N * N + i * N + c++] = (int8_t)j;
+        if (min(max(col[j], 0), N - 1) == i) pre[(size_t)hk * N * N + i * N + c++] = (int8_t)j;
     for (int r = c; r < N; ++r) pre[(size_t)hk * N * N + i * N + r] = 0;
     cnt[idx] = c;
 }
@@ -592,6 +594,20 @@ __global__ __launch_bounds__(256) void pd_combine_rev_kernel(PDParams p) {
         const float vn = fmaf(Dg, row_pull(v, pig), Rg);
         v = nl ? vn : 0.0f;
     }
+}
+
+// out = min(max(sel, 0), K - 1): a given selection is reported as the kernels use it
+__global__ __launch_bounds__(256) void pd_sel_copy_kernel(const int32_t* __restrict__ sel, int32_t* __restrict__ out,
+                                                          size_t n, int K) {
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+        out[i] = min(max(sel[i], 0), K - 1);
+}
+hipError_t launch_pd_sel_copy(const int32_t* sel, int32_t* out, size_t n, int K, hipStream_t st) {
+    if (n == 0) return hipSuccess;
+    const size_t blocks = (n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096;
+    pd_sel_copy_kernel<<<(unsigned)blocks, 256, 0, st>>>(sel, out, n, K);
+    return hipGetLastError();
 }
 
 hipError_t launch_pd_prep(const PDParams& p, hipStream_t st) {

@@ -152,7 +152,7 @@ def test_errors_before_enqueue():
     assert rc == status("SSM_ERR_SHAPE")  # t_out outside [0, L)
 
 
-def test_workspace_independent_of_length_for_sensitivity():
+def test_sensitivity_workspace_grows_by_a_few_numbers_per_chunk():
     """The sensitivity path needs O(n_chunks) scratch: per chunk a few numbers, no per-step state."""
     _, n1 = ws_bytes(B.SSM_OP_IMPULSE, sel_args(length=16384, batch=1, channels=64))
     _, n2 = ws_bytes(B.SSM_OP_IMPULSE, sel_args(length=131072, batch=1, channels=64))
@@ -346,3 +346,82 @@ def ws_bytes_pd(args):
     n = ctypes.c_size_t(0)
     rc = B.lib().ssm_workspace_bytes(B.SSM_OP_PD_FWD, ctypes.byref(args), ctypes.byref(n))
     return rc, n.value
+
+
+# ---------------------------------------------------------------------------
+# binding: caller-supplied outputs are checked like inputs; host tensors are refused
+# ---------------------------------------------------------------------------
+def _cpu_sel(L=40, D=3, N=4, dtype=None):
+    import torch
+    dt = dtype or torch.float32
+    g = torch.Generator().manual_seed(0)
+    return dict(delta=torch.rand(2, D, L, generator=g).to(dt), x=torch.randn(2, D, L, generator=g).to(dt),
+                A=-torch.rand(D, N, generator=g), Bm=torch.randn(2, L, N, generator=g).to(dt),
+                C=torch.randn(2, L, N, generator=g).to(dt))
+
+
+@pytest.mark.parametrize("key,make,exc", [
+    ("y", lambda t: t.zeros(2, 3, 41), ValueError),                      # wrong shape
+    ("y", lambda t: t.zeros(2, 3, 40, dtype=t.bfloat16), TypeError),     # wrong dtype
+    ("y", lambda t: t.zeros(2, 40, 3).transpose(1, 2), ValueError),      # not contiguous
+    ("h_last", lambda t: t.zeros(2, 3, 5), ValueError),
+    ("ckpt", lambda t: t.zeros(2, 3, 1, 4, dtype=t.float64), TypeError),
+])
+def test_scan_fwd_rejects_bad_out(key, make, exc):
+    import torch
+    with pytest.raises(exc):
+        B.scan_fwd(B.SSM_REAL_SELECTIVE, want_h_last=True, want_ckpt=True, out={key: make(torch)}, **_cpu_sel())
+
+
+@pytest.mark.parametrize("key,make,exc", [
+    ("gdelta", lambda t: t.zeros(2, 3, 39), ValueError),
+    ("gBm", lambda t: t.zeros(2, 40, 4, dtype=t.bfloat16), TypeError),
+    ("gA", lambda t: t.zeros(4, 3).t(), ValueError),
+    ("gphi", lambda t: t.zeros(2, 3, 40), ValueError),                   # no such gradient in this mode
+])
+def test_scan_bwd_rejects_bad_out(key, make, exc):
+    import torch
+    t = _cpu_sel()
+    with pytest.raises(exc):
+        B.scan_bwd(B.SSM_REAL_SELECTIVE, gy=torch.zeros(2, 3, 40), out={key: make(torch)}, **t)
+
+
+def test_other_entry_points_reject_bad_out():
+    import torch
+    t = _cpu_sel()
+    with pytest.raises(ValueError):
+        B.impulse_sensitivity(out={"s": torch.zeros(2, 3, 7)}, **t)
+    with pytest.raises(TypeError):
+        B.output_sensitivity(out={"s_delta": torch.zeros(2, 3, 40, dtype=torch.float64)}, **t)
+    with pytest.raises(ValueError):
+        B.sensitivity_rows(t_out0=0, rows=2, out=torch.zeros(3, 2, 3, 40), **t)
+    g = torch.Generator().manual_seed(1)
+    pd = dict(logits=torch.randn(2, 2, 30, 4, generator=g), dict=torch.randint(0, 5, (2, 4, 5), dtype=torch.int32),
+              d=torch.rand(2, 2, 30, 5, generator=g), b=torch.randn(2, 2, 30, 5, generator=g),
+              C=torch.randn(2, 2, 30, 5, generator=g))
+    with pytest.raises(TypeError):
+        B.pd_scan_fwd(out={"sel": torch.zeros(2, 2, 30, dtype=torch.int64)}, **pd)
+    with pytest.raises(ValueError):
+        B.pd_scan_bwd(gy=torch.zeros(2, 2, 30), out={"gd": torch.zeros(2, 2, 30, 4)}, **pd)
+
+
+def test_host_tensors_are_refused():
+    """Valid arguments on the host never reach the library: it takes device pointers only."""
+    import torch
+    t = _cpu_sel()
+    with pytest.raises(ValueError, match="GPU"):
+        B.scan_fwd(B.SSM_REAL_SELECTIVE, **t)
+    with pytest.raises(ValueError, match="GPU"):
+        B.scan_bwd(B.SSM_REAL_SELECTIVE, gy=torch.zeros(2, 3, 40), **t)
+    with pytest.raises(ValueError, match="GPU"):
+        B.impulse_sensitivity(**t)
+
+
+def test_allocator_hook_shapes_are_checked():
+    import torch
+    B.set_allocator(lambda shape, dtype, device, role: torch.zeros(1))
+    try:
+        with pytest.raises(ValueError, match="allocator"):
+            B.scan_fwd(B.SSM_REAL_SELECTIVE, **_cpu_sel())
+    finally:
+        B.set_allocator(None)

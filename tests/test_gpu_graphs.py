@@ -1,5 +1,4 @@
-"""HIP graph capture: every entry point enqueues only kernels (and device copies)
-on the caller's stream and allocates nothing, so a captured forward + backward
+"""HIP graph capture: every entry point enqueues only kernels on the caller's stream and allocates nothing, so a captured forward + backward
 replays correctly.  Each replay follows eager work and a synchronisation, the
 inputs change between replays (copied into the captured tensors), and every
 replay is compared bit for bit with an eager call on the same inputs."""

@@ -384,6 +384,34 @@ def run_pd(cfg, h0=None, ghl=None, use_sel=False):
         assert torch.equal(g[k], g2[k]), k
 
 
+def test_pd_out_of_range_indices_are_clamped():
+    """Dictionary entries outside [0, N) and given selections outside [0, K) violate the documented
+    precondition; the library clamps both, consistently in every pass: results equal the oracle's on the
+    clamped arrays, and the reported selection is the clamped one."""
+    ssm = _ssm()
+    B, H, N, K, L = 2, 3, 16, 8, 700
+    cfg = synth.make_pd(B=B, H=H, N=N, L=L, K=K, seed=47)
+    dct = cfg["dict"].copy()
+    dct[0, 1, 3], dct[1, 5, 0], dct[2, 7, 15] = -4, N + 3, 99
+    sel = oracle.pd_select(cfg["logits"]).copy()
+    sel[0, 0, 5], sel[1, 2, 600], sel[0, 1, 63] = -1, K, K + 20
+    g = np.random.default_rng(48)
+    h0 = g.standard_normal((B, H, N)).astype(np.float32)
+    t = dict(sel=T(sel), dict=T(dct), d=T(cfg["d"]), b=T(cfg["b"]), C=T(cfg["C"]), h0=T(h0))
+    f = ssm.pd_scan_fwd(want_h_last=True, want_ckpt=True, **t)
+    gr = ssm.pd_scan_bwd(gy=T(cfg["gy"]), ckpt=f["ckpt"], **t)
+    torch.cuda.synchronize()
+    csel, cdict = np.clip(sel, 0, K - 1).astype(np.int32), np.clip(dct, 0, N - 1).astype(np.int32)
+    assert np.array_equal(f["sel"].cpu().numpy(), csel)
+    kw = dict(sel=csel, dict=cdict, d=cfg["d"], b=cfg["b"], C=cfg["C"], h0=h0, B=B, H=H, L=L, N=N, K=K)
+    y, hl = oracle.pd_fwd(**kw)
+    og = oracle.pd_bwd(**kw, gy=cfg["gy"])
+    assert_close("y", f["y"], y, **F32)
+    assert_close("h_last", f["h_last"], hl, **F32)
+    for k in ("gd", "gb", "gC", "gh0"):
+        assert_close(k, gr[k], og[k], **F32)
+
+
 def test_pd_checkpoints_are_chunk_states():
     """ckpt[:, :, c] of the PD scan is the state entering 64-step chunk c: the oracle's final state of the first
     64c steps with the same selections (c = 0 holds h0)."""
