@@ -73,9 +73,9 @@
 extern "C" {
 #endif
 
-/* 4: adds SSM_COMPLEX_DENSE; 3 added ssm_sensitivity_rows and SSM_OP_SENS_ROWS;
- * struct layouts as in 2 */
-#define SSM_ABI_VERSION 4
+/* 5: adds ssm_scan_fwd_noalloc; 4 added SSM_COMPLEX_DENSE; 3 added
+ * ssm_sensitivity_rows and SSM_OP_SENS_ROWS; struct layouts as in 2 */
+#define SSM_ABI_VERSION 5
 
 /* status codes */
 #define SSM_OK               0
@@ -255,6 +255,21 @@ int ssm_workspace_bytes(int op, const void* args, size_t* out_bytes);
 /* Forward scan: y, h_last and checkpoints (each nullable). */
 int ssm_scan_fwd(const ssm_scan_args* args, const ssm_scan_fwd_out* out,
                  void* ws, size_t ws_bytes, void* stream);
+
+/* Allocation-free variant of ssm_scan_fwd, for callers that cannot allocate
+ * device memory or pass a workspace (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).  Same arguments, outputs,
+ * results (bit for bit) and errors as ssm_scan_fwd, with the workspace taken
+ * from a static device array of SSM_NOALLOC_SCRATCH_BYTES bytes that every
+ * device the library runs on holds until the process ends.  Every forward
+ * need fits it (at most about 25 MB: complex mode, M = 64, a few thousand
+ * sequences); a larger need would be refused with SSM_ERR_WORKSPACE before
+ * anything is enqueued.  The call allocates nothing.  Calls that overlap on
+ * one device (different streams, or different threads) share the array and
+ * race: serialise them.  On first use on a device the call looks up the
+ * array's device address (hipGetSymbolAddress). */
+#define SSM_NOALLOC_SCRATCH_BYTES (32 * 1024 * 1024)
+int ssm_scan_fwd_noalloc(const ssm_scan_args* args, const ssm_scan_fwd_out* out, void* stream);
 
 /* Exact backward of ssm_scan_fwd by tiled recompute from the checkpoints and a
  * reverse adjoint scan lambda_t = C_t gy_t + A_{t+1}^T lambda_{t+1}. */

@@ -24,6 +24,7 @@ from .binding import (  # noqa: F401
     pd_scan_fwd,
     scan_bwd,
     scan_fwd,
+    scan_fwd_noalloc,
     sensitivity_rows,
     set_allocator,
 )

@@ -81,6 +81,7 @@ def lib():
         L = ctypes.CDLL(LIB_PATH)
         L.ssm_workspace_bytes.argtypes = [ctypes.c_int, _vp, ctypes.POINTER(ctypes.c_size_t)]
         L.ssm_scan_fwd.argtypes = [ctypes.POINTER(ScanArgs), ctypes.POINTER(ScanFwdOut), _vp, ctypes.c_size_t, _vp]
+        L.ssm_scan_fwd_noalloc.argtypes = [ctypes.POINTER(ScanArgs), ctypes.POINTER(ScanFwdOut), _vp]
         L.ssm_scan_bwd.argtypes = [ctypes.POINTER(ScanArgs), ctypes.POINTER(ScanBwdIn), ctypes.POINTER(ScanGrads),
                                    _vp, ctypes.c_size_t, _vp]
         L.ssm_impulse_sensitivity.argtypes = [ctypes.POINTER(ScanArgs), _i64, _vp, _vp, _vp, ctypes.c_size_t, _vp]
@@ -271,6 +272,17 @@ def scan_fwd(mode, *, want_y=True, want_h_last=False, want_ckpt=False, chunk_len
 
     ``out`` may hold preallocated output tensors (keys y, h_last, ckpt).
     """
+    return _scan_fwd(mode, want_y, want_h_last, want_ckpt, chunk_len, out, tensors, noalloc=False)
+
+
+def scan_fwd_noalloc(mode, *, want_y=True, want_h_last=False, want_ckpt=False, chunk_len=0, out=None, **tensors):
+    """ssm_scan_fwd_noalloc: the forward scan with the library's static device scratch in place of a
+    workspace (nothing is allocated when ``out`` holds every requested output).  Same results as
+    scan_fwd; calls that overlap on one device race on the shared scratch."""
+    return _scan_fwd(mode, want_y, want_h_last, want_ckpt, chunk_len, out, tensors, noalloc=True)
+
+
+def _scan_fwd(mode, want_y, want_h_last, want_ckpt, chunk_len, out, tensors, noalloc):
     args, (Bsz, D, L, N), dev = _scan_args(mode, chunk_len=chunk_len, **tensors)
     out = dict(out or {})
     ydt = _stream_dtype(mode, tensors)
@@ -282,6 +294,9 @@ def scan_fwd(mode, *, want_y=True, want_h_last=False, want_ckpt=False, chunk_len
             _out(out, k, shp, dt, dev)
     _on_gpu(dev)
     o = ScanFwdOut(y=_ptr(out.get("y")), h_last=_ptr(out.get("h_last")), ckpt=_ptr(out.get("ckpt")))
+    if noalloc:
+        _check(lib().ssm_scan_fwd_noalloc(ctypes.byref(args), ctypes.byref(o), _stream(dev)))
+        return out
     ws, nws = _workspace(SSM_OP_SCAN_FWD, ctypes.byref(args), dev)
     _check(lib().ssm_scan_fwd(ctypes.byref(args), ctypes.byref(o), _ptr(ws), nws, _stream(dev)))
     return out

@@ -9,6 +9,7 @@
 #include <cstdio>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -645,6 +646,51 @@ int sens_rows_impl(const ssm_scan_args* a, int64_t t0, int32_t rows, void* s, vo
 #include "api_modes.inc"
 
 // ===========================================================================
+// allocation-free forward (ssm_scan_fwd_noalloc): the scratch memory the
+// forward passes need (segment summaries and carries) lives in a static device
+// array instead of a caller workspace.  Each device holds its own copy at its
+// own address, found once per device with hipGetSymbolAddress; the array's
+// name is only a host-side stand-in and is never passed to a kernel.
+// ===========================================================================
+static_assert(SSM_NOALLOC_SCRATCH_BYTES % 256 == 0, "scratch size");
+static __device__ __align__(256) unsigned char scratch[SSM_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the device that runs `st` (the current device
+// for the NULL stream), looked up on the first call for that device.
+int scratch_for_stream(hipStream_t st, void** out) {
+    int cur = 0, dev = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return fail(SSM_ERR_DEVICE, "hipGetDevice: %s", hipGetErrorName(e));
+    dev = cur;
+    if (st) {
+        e = hipStreamGetDevice(st, &dev);
+        if (e != hipSuccess) return fail(SSM_ERR_DEVICE, "hipStreamGetDevice: %s", hipGetErrorName(e));
+    }
+    if (dev < 0 || dev >= kMaxDevices) return fail(SSM_ERR_UNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess)
+            return fail(SSM_ERR_DEVICE, "hipSetDevice(%d): %s", dev, hipGetErrorName(e));
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (dev != cur) hipSetDevice(cur);
+        if (e != hipSuccess || !ptr)
+            return fail(SSM_ERR_DEVICE, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorName(e));
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return SSM_OK;
+}
+
+}  // namespace
+
+// ===========================================================================
 // exported C ABI
 // ===========================================================================
 extern "C" {
@@ -673,6 +719,18 @@ int ssm_workspace_bytes(int op, const void* args, size_t* out_bytes) {
 
 int ssm_scan_fwd(const ssm_scan_args* args, const ssm_scan_fwd_out* out, void* ws, size_t ws_bytes, void* stream) {
     return scan_fwd_impl(args, out, ws, ws_bytes, (hipStream_t)stream, nullptr);
+}
+int ssm_scan_fwd_noalloc(const ssm_scan_args* args, const ssm_scan_fwd_out* out, void* stream) {
+    size_t need = 0;
+    int rc = scan_fwd_impl(args, nullptr, nullptr, 0, nullptr, &need);   // host-only: validation and sizing
+    if (rc) return rc;
+    if (need > (size_t)SSM_NOALLOC_SCRATCH_BYTES)
+        return fail(SSM_ERR_WORKSPACE, "the forward needs %zu bytes of scratch; the static scratch holds %zu",
+                    need, (size_t)SSM_NOALLOC_SCRATCH_BYTES);
+    void* ws = nullptr;
+    if ((rc = scratch_for_stream((hipStream_t)stream, &ws))) return rc;
+    // no part of the scratch has to start at zero: every pass writes what it later reads
+    return scan_fwd_impl(args, out, ws, SSM_NOALLOC_SCRATCH_BYTES, (hipStream_t)stream, nullptr);
 }
 int ssm_scan_bwd(const ssm_scan_args* args, const ssm_scan_bwd_in* in, const ssm_scan_grads* grads, void* ws,
                  size_t ws_bytes, void* stream) {

@@ -425,3 +425,20 @@ def test_allocator_hook_shapes_are_checked():
             B.scan_fwd(B.SSM_REAL_SELECTIVE, **_cpu_sel())
     finally:
         B.set_allocator(None)
+
+
+def test_every_forward_fits_the_static_scratch():
+    """ssm_scan_fwd_noalloc's static scratch holds the workspace of every forward: the largest needs come
+    from the segment summaries when few sequences leave room for many segments."""
+    cap = 32 * 1024 * 1024
+    worst = 0
+    for mode, N in ((B.SSM_REAL_SELECTIVE, 16), (B.SSM_REAL_DENSE, 16), (B.SSM_COMPLEX_SHARED, 64),
+                    (B.SSM_COMPLEX_DENSE, 64)):
+        for bd in (1, 2, 3, 7, 16, 100, 255, 1000, 2049, 4095, 4097, 16383, 16385, 65536):
+            a = sel_args(mode=mode, batch=1, channels=bd, length=1 << 20, state=N, dtype=B.SSM_F32,
+                         a=FAKE * 7, b=FAKE * 8, u=FAKE * 9, c=FAKE * 10, r=FAKE * 11, phi=FAKE * 12,
+                         lam=FAKE * 13, theta=FAKE * 14)
+            rc, n = ws_bytes(B.SSM_OP_SCAN_FWD, a)
+            assert rc == 0, (mode, bd)
+            worst = max(worst, n)
+    assert 0 < worst <= cap
