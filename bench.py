@@ -95,6 +95,9 @@ def parse():
     ap.add_argument("--cpu-batches", type=int, default=8, help="batch rows of the headline in the CPU sample")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one 1 GiB device copy (calibrates HBM byte counters)")
+    ap.add_argument("--roof", action="store_true",
+                    help="also measure the issue rate of each VALU instruction class (ssm_roof_probe) at 1, 2, 4 "
+                         "and 8 waves per SIMD and report the measured fp32 FMA ceiling")
     return ap.parse_args()
 
 
@@ -491,6 +494,41 @@ def device_info():
     return info
 
 
+ROOF_KINDS = {0: "v_fma_f32", 1: "v_mul_f32", 2: "v_exp_f32", 3: "v_fmac_f32 (DPP source)",
+              4: "v_permlane32_swap", 5: "v_permlane16_swap", 6: "v_add_f32"}
+
+
+def roof_probes(iters=2000):
+    """Issue rate (lane operations per second, whole chip) of every instruction class at 1, 2, 4 and 8 waves
+    per SIMD, each lane running independent chains (8, or 4 for the DPP form); and the fp32 FMA ceiling in
+    TFLOP/s (2 flops per lane operation) at the best occupancy."""
+    import torch
+    from selective_state_space_chunked_amd import lib
+    L = lib()
+    L.ssm_roof_probe.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                 ctypes.POINTER(ctypes.c_double), ctypes.c_void_p]
+    simds = 4 * torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.empty(8 * simds * 64, dtype=torch.float32, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+    table = {}
+    for kind, name in ROOF_KINDS.items():
+        chains = 4 if kind == 3 else 8
+        row = {}
+        for w in (1, 2, 4, 8):
+            r = ctypes.c_double(0.0)
+            for _ in range(2):   # the second launch is the one kept (the first pays for loading the code)
+                rc = L.ssm_roof_probe(kind, chains, w * simds, iters, ctypes.c_void_p(sink.data_ptr()),
+                                      ctypes.byref(r), ctypes.c_void_p(st))
+                assert rc == 0, rc
+            row[f"{w}_waves_per_simd"] = r.value
+        table[name] = {k: round(v / 1e12, 3) for k, v in row.items()}
+        table[name]["cycles_per_wave64_instr_best"] = round(simds * 64 * 2.4e9 / max(row.values()), 3)
+    fma_best = max(v for k, v in table["v_fma_f32"].items() if k.endswith("simd")) * 1e12
+    return {"unit": "T lane-ops/s (whole chip)", "iters": iters, "classes": table,
+            "fp32_fma_TFLOPs_measured": round(2 * fma_best / 1e12, 2),
+            "note": "cycles_per_wave64_instr_best = 64 lanes x SIMDs x 2.4 GHz / best rate"}
+
+
 def calib_copy():
     """One device copy of exactly 1 GiB (reads 1 GiB, writes 1 GiB)."""
     import torch
@@ -564,6 +602,7 @@ def main():
               "cache_flushed_ms": step_stats(head["step"], 20, True),
               "note": "per-step HIP-event times of the headline step; cache_flushed writes 1 GiB before each step"}
     hbm_copy = copy_ceiling()
+    roof_meas = roof_probes() if args.roof else None
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(head["inputs"], args.cpu_batches)
@@ -582,6 +621,10 @@ def main():
         "kernels_ms": s["kernels_ms"], "roofline": roof, "cpu_baseline": cpu, "others": others,
         "timing": timing, "hbm_copy_GBps": round(hbm_copy, 1), "device": device_info(),
     }
+    if roof_meas:
+        line["roof_measured"] = roof_meas
+        roof["peak_measured"] = roof_meas["fp32_fma_TFLOPs_measured"]
+        roof["frac_of_measured"] = roof["achieved"] / roof_meas["fp32_fma_TFLOPs_measured"]
     print(json.dumps(line))
 
 

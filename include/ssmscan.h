@@ -73,7 +73,7 @@
 extern "C" {
 #endif
 
-/* 5: adds ssm_scan_fwd_noalloc; 4 added SSM_COMPLEX_DENSE; 3 added
+/* 5: adds ssm_scan_fwd_noalloc and ssm_roof_probe; 4 added SSM_COMPLEX_DENSE; 3 added
  * ssm_sensitivity_rows and SSM_OP_SENS_ROWS; struct layouts as in 2 */
 #define SSM_ABI_VERSION 5
 
@@ -360,6 +360,20 @@ int pd_scan_bwd(const pd_scan_args* args, const pd_scan_bwd_in* in,
  * are created by the library and kept for reuse until the process ends. */
 int ssm_profile_begin(int max_launches);
 int ssm_profile_end(int* n_launches, float* ms, const char** names, int capacity);
+
+/* Diagnostics: issue rate of one VALU instruction class, measured on the
+ * device (the arithmetic ceiling the scan kernels' roofline is taken against).
+ * Launches `waves` one-wave workgroups (waves / (4 x compute units) waves per
+ * SIMD), every lane running `chains` (4 or 8) independent dependency chains of
+ * iters x 8 instructions of class `kind`: 0 v_fma_f32, 1 v_mul_f32,
+ * 2 v_exp_f32, 3 v_fmac_f32 with a DPP row_shr source (4 chains only),
+ * 4 v_permlane32_swap, 5 v_permlane16_swap, 6 v_add_f32.  Times the launch
+ * with two HIP events on `stream`, waits for it, and writes lane operations
+ * per second (64 x waves x instructions per lane / seconds).  `sink` is a
+ * device buffer of waves x 64 floats that is never written in practice (it
+ * keeps the chains live).  Synchronises with the stream. */
+int ssm_roof_probe(int kind, int chains, int waves, int iters, float* sink, double* lane_ops_per_s,
+                   void* stream);
 
 const char* ssm_status_string(int status);   /* static string for a status code */
 const char* ssm_last_error_detail(void);     /* thread-local detail of the last error */

@@ -793,6 +793,32 @@ int ssm_profile_end(int* n_launches, float* ms, const char** names, int capacity
     return ok();
 }
 
+int ssm_roof_probe(int kind, int chains, int waves, int iters, float* sink, double* lane_ops_per_s, void* stream) {
+    if (!sink || !lane_ops_per_s) return fail(SSM_ERR_NULL, "sink and lane_ops_per_s are required");
+    if (kind < 0 || kind > 6) return fail(SSM_ERR_UNSUPPORTED, "unknown probe kind %d", kind);
+    if (chains != 4 && chains != 8) return fail(SSM_ERR_UNSUPPORTED, "chains must be 4 or 8");
+    if (kind == 3 && chains != 4) return fail(SSM_ERR_UNSUPPORTED, "the DPP probe runs 4 chains");
+    if (waves < 1 || waves > 65536 || iters < 1 || iters > (1 << 24))
+        return fail(SSM_ERR_SHAPE, "waves in [1, 65536] and iters in [1, 2^24] required");
+    hipStream_t st = (hipStream_t)stream;
+    hipEvent_t e0, e1;
+    hipError_t e = hipEventCreate(&e0);
+    if (e != hipSuccess) return fail(SSM_ERR_DEVICE, "hipEventCreate: %s", hipGetErrorName(e));
+    if ((e = hipEventCreate(&e1)) != hipSuccess) {
+        hipEventDestroy(e0);
+        return fail(SSM_ERR_DEVICE, "hipEventCreate: %s", hipGetErrorName(e));
+    }
+    float ms = 0.0f;
+    if ((e = hipEventRecord(e0, st)) == hipSuccess && (e = launch_roof(kind, chains, waves, iters, sink, st)) == hipSuccess &&
+        (e = hipEventRecord(e1, st)) == hipSuccess && (e = hipEventSynchronize(e1)) == hipSuccess)
+        e = hipEventElapsedTime(&ms, e0, e1);
+    hipEventDestroy(e0);
+    hipEventDestroy(e1);
+    if (e != hipSuccess) return fail(SSM_ERR_DEVICE, "roof probe: %s", hipGetErrorName(e));
+    *lane_ops_per_s = (double)waves * 64.0 * roof_instrs_per_lane(kind, chains, iters) / (ms * 1e-3);
+    return ok();
+}
+
 const char* ssm_status_string(int status) {
     switch (status) {
         case SSM_OK: return "SSM_OK";

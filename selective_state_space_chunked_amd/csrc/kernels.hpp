@@ -176,4 +176,10 @@ hipError_t launch_pd_combine_fwd(const PDParams& p, hipStream_t st);
 hipError_t launch_pd_bwd(const PDParams& p, bool summary, hipStream_t st);
 hipError_t launch_pd_combine_rev(const PDParams& p, hipStream_t st);
 
+// ------------------------------- issue-rate probes -------------------------
+// `waves` one-wave workgroups, each lane running `chains` dependency chains of
+// instruction class `kind` for iters * 8 steps; sink holds waves * 64 floats.
+hipError_t launch_roof(int kind, int chains, int waves, int iters, float* sink, hipStream_t st);
+double roof_instrs_per_lane(int kind, int chains, int iters);
+
 }  // namespace ssm
