@@ -10,7 +10,12 @@ All routines take numpy arrays holding the exact values the GPU consumes
 (float32, bfloat16 bits as uint16, complex64, int32) and widen them to float64
 here; results come back as float64 (int32 for selections).
 
-Pinned by tests/test_oracle_pins.py: real forward (brute-force O(L^2) sums,
+Pinned by tests/test_oracle_pins.py: general selective scan ``sel_fwd`` / ``sel_bwd``
+(zero-order hold: the exact solution of dh/dt = A h + B x for inputs held
+constant, the A = 0 limit equal to the Euler scan, central finite differences;
+per-channel B and C: brute-force O(L^2) sums, equality with the shared form
+for channel-independent B, C, finite differences; Euler form equal to
+real_fwd / real_bwd), real forward (brute-force O(L^2) sums,
 geometric closed form, prefix-sum special case), real backward (central finite
 differences, adjoint identity), impulse sensitivity (closed form with exactly
 rounded step-size sums, linearity, equality with the general backward),
@@ -56,6 +61,8 @@ def _load():
         lib = ctypes.CDLL(_LIB)
         lib.orc_real_fwd.argtypes = [ctypes.c_int, _L, _L, _L, _L] + [_D] * 10
         lib.orc_real_bwd.argtypes = [ctypes.c_int, _L, _L, _L, _L] + [_D] * 18
+        lib.orc_sel_fwd.argtypes = [ctypes.c_int, ctypes.c_int, _L, _L, _L, _L] + [_D] * 8
+        lib.orc_sel_bwd.argtypes = [ctypes.c_int, ctypes.c_int, _L, _L, _L, _L] + [_D] * 14
         lib.orc_impulse_sens.argtypes = [_L, _L, _L, _L, _L] + [_D] * 5
         lib.orc_output_sens.argtypes = [_L, _L, _L, _L, _L] + [_D] * 8
         lib.orc_complex_fwd.argtypes = [_L, _L, _L, _L] + [_D] * 9
@@ -119,6 +126,27 @@ def real_fwd(*, delta=None, x=None, A=None, Bm=None, a=None, b=None, C, h0=None,
     y, hl = _z((B, D, L)), _z((B, D, N))
     _load().orc_real_fwd(mode, B, D, L, N, *[_p(v) for v in args], _p(y), _p(hl))
     return y, hl
+
+
+def sel_fwd(*, delta, x, A, Bm, C, h0=None, disc=0, perd=False, B, D, L, N):
+    """Selective scan, general form: y (B,D,L) and h_last (B,D,N).  ``disc`` 0 is the Euler input term
+    delta x B, 1 the zero-order hold (exp(delta A) - 1) / A x B (delta x B where A = 0).  ``perd``: Bm and
+    C are (B,D,L,N), one per channel, else (B,L,N) shared by the channels."""
+    args = [_w(v) for v in (delta, x, A, Bm, C, h0)]
+    y, hl = _z((B, D, L)), _z((B, D, N))
+    _load().orc_sel_fwd(int(disc), int(bool(perd)), B, D, L, N, *[_p(v) for v in args], _p(y), _p(hl))
+    return y, hl
+
+
+def sel_bwd(*, delta, x, A, Bm, C, h0=None, gy, ghlast=None, disc=0, perd=False, B, D, L, N):
+    """Gradients of sum<gy,y> + <ghlast,h_last> of ``sel_fwd``: dict(gdelta, gx, gA, gBm, gC, gh0), with
+    gBm, gC (B,L,N) sums over the channels, or (B,D,L,N) when ``perd``."""
+    args = [_w(v) for v in (delta, x, A, Bm, C, h0, gy, ghlast)]
+    gbc = (B, D, L, N) if perd else (B, L, N)
+    out = dict(gdelta=_z((B, D, L)), gx=_z((B, D, L)), gA=_z((D, N)), gBm=_z(gbc), gC=_z(gbc), gh0=_z((B, D, N)))
+    _load().orc_sel_bwd(int(disc), int(bool(perd)), B, D, L, N, *[_p(v) for v in args],
+                        *[_p(out[k]) for k in ("gdelta", "gx", "gA", "gBm", "gC", "gh0")])
+    return out
 
 
 def real_bwd(*, delta=None, x=None, A=None, Bm=None, a=None, b=None, C, h0=None,

@@ -755,3 +755,137 @@ def test_generators_reproducible_and_rounded():
     A = synth.widen(c["A"])
     assert np.all((A <= -np.exp(-3.0) * (1 - 1e-6)) & (A >= -np.exp(-1.0) * (1 + 1e-6)))
     assert abs(synth.widen(c["x"]).mean()) < 0.05 and abs(synth.widen(c["x"]).std() - 1) < 0.05
+
+
+# ---------------------------------------------------------------------------
+# general selective form: zero-order hold and per-channel B_t, C_t
+# ---------------------------------------------------------------------------
+def _sel_kw(p, disc=0, perd=False):
+    return dict(delta=p["delta"], x=p["x"], A=p["A"], Bm=p["Bm"], C=p["C"], h0=p["h0"], disc=disc, perd=perd,
+                B=p["B"], D=p["D"], L=p["L"], N=p["N"])
+
+
+def _perd(p, seed):
+    """The same problem with B_t, C_t drawn per channel (B,D,L,N)."""
+    g = np.random.default_rng(seed)
+    q = dict(p)
+    q["Bm"] = g.standard_normal((p["B"], p["D"], p["L"], p["N"])) / 2
+    q["C"] = g.standard_normal((p["B"], p["D"], p["L"], p["N"])) / 2
+    return q
+
+
+def test_general_euler_equals_real_scan():
+    """The general routine in its Euler, shared-B/C form is the selective scan (forward and backward)."""
+    p = small_real(B=2, D=3, N=4, L=30, seed=41)
+    y, hl = oracle.sel_fwd(**_sel_kw(p))
+    y0, hl0 = oracle.real_fwd(delta=p["delta"], x=p["x"], A=p["A"], Bm=p["Bm"], C=p["C"], h0=p["h0"],
+                              B=2, D=3, L=30, N=4)
+    close(y, y0, rtol=1e-13)
+    close(hl, hl0, rtol=1e-13)
+    g = oracle.sel_bwd(**_sel_kw(p), gy=p["gy"], ghlast=p["ghlast"])
+    g0 = oracle.real_bwd(delta=p["delta"], x=p["x"], A=p["A"], Bm=p["Bm"], C=p["C"], h0=p["h0"], gy=p["gy"],
+                         ghlast=p["ghlast"], B=2, D=3, L=30, N=4)
+    for k in ("gdelta", "gx", "gA", "gBm", "gC", "gh0"):
+        close(g[k], g0[k], rtol=1e-11, atol=1e-13)
+
+
+def test_zoh_is_the_exact_ode_solution_for_held_inputs():
+    """With delta, x and B held constant, the zero-order-hold scan samples the exact solution of
+    dh/dt = A h + B x at t = (k+1) delta: h_k = e^{A (k+1) delta} h0 + (e^{A (k+1) delta} - 1) / A B x
+    (a closed form computed here, not a recurrence)."""
+    B, D, N, L = 1, 2, 3, 40
+    g = np.random.default_rng(42)
+    dl = np.array([0.3, 1.7])
+    xv = np.array([0.8, -1.3])
+    A = -np.exp(g.uniform(-3, 1, (D, N)))
+    Bv = g.standard_normal(N)
+    Cv = g.standard_normal(N)
+    h0 = g.standard_normal((B, D, N))
+    p = dict(delta=np.broadcast_to(dl[None, :, None], (B, D, L)).copy(),
+             x=np.broadcast_to(xv[None, :, None], (B, D, L)).copy(), A=A,
+             Bm=np.broadcast_to(Bv, (B, L, N)).copy(), C=np.broadcast_to(Cv, (B, L, N)).copy(), h0=h0,
+             B=B, D=D, N=N, L=L)
+    y, hl = oracle.sel_fwd(**_sel_kw(p, disc=1))
+    T = (np.arange(L) + 1.0)[:, None]
+    for d in range(D):
+        e = np.exp(A[d][None, :] * T * dl[d])
+        H = e * h0[0, d][None, :] + (e - 1.0) / A[d][None, :] * Bv[None, :] * xv[d]
+        close(y[0, d], H @ Cv, rtol=1e-11, atol=1e-13)
+        close(hl[0, d], H[-1], rtol=1e-11, atol=1e-13)
+
+
+def test_zoh_at_zero_A_is_the_euler_scan():
+    """A = 0: the zero-order-hold input term is delta x B (its limit), so both discretisations agree."""
+    p = small_real(B=2, D=2, N=3, L=25, seed=43)
+    p["A"] = np.zeros_like(p["A"])
+    y1, h1 = oracle.sel_fwd(**_sel_kw(p, disc=1))
+    y0, h0 = oracle.real_fwd(delta=p["delta"], x=p["x"], A=p["A"], Bm=p["Bm"], C=p["C"], h0=p["h0"],
+                             B=2, D=2, L=25, N=3)
+    close(y1, y0, rtol=1e-14)
+    close(h1, h0, rtol=1e-14)
+
+
+def test_zoh_input_term_bruteforce():
+    """Every state by the unrolled O(L^2) sum with b_s = expm1(delta A) / A x B, a written out per step."""
+    p = small_real(B=1, D=2, N=3, L=18, seed=44)
+    y, _ = oracle.sel_fwd(**_sel_kw(p, disc=1))
+    for di in range(2):
+        z = p["delta"][0, di][:, None] * p["A"][di][None, :]
+        a = np.exp(z)
+        bb = np.expm1(z) / p["A"][di][None, :] * (p["x"][0, di][:, None] * p["Bm"][0])
+        yb, _ = brute_real(a, bb, p["C"][0], p["h0"][0, di])
+        close(y[0, di], yb, rtol=1e-12, atol=1e-14)
+
+
+def _loss_sel(p, disc, perd, **over):
+    q = dict(p)
+    q.update(over)
+    y, hl = oracle.sel_fwd(**_sel_kw(q, disc=disc, perd=perd))
+    return float((y * q["gy"]).sum() + (hl * q["ghlast"]).sum())
+
+
+@pytest.mark.parametrize("name,gname", [("delta", "gdelta"), ("x", "gx"), ("A", "gA"), ("Bm", "gBm"),
+                                        ("C", "gC"), ("h0", "gh0")])
+@pytest.mark.parametrize("disc,perd", [(1, False), (0, True), (1, True)])
+def test_general_selective_bwd_fd(name, gname, disc, perd):
+    """Central differences of the general forward in every input entry (ZOH and / or per-channel B_t, C_t;
+    one A entry set to 0 and one tiny, so the A = 0 limit and the series branch of d coef / d A are
+    covered)."""
+    p = small_real(B=2, D=2, N=3, L=9, seed=45)
+    p["A"][0, 1] = 0.0
+    p["A"][1, 2] = -3e-5
+    if perd:
+        p = _perd(p, 46)
+    g = oracle.sel_bwd(**_sel_kw(p, disc=disc, perd=perd), gy=p["gy"], ghlast=p["ghlast"])
+    fd_check(lambda q, **o: _loss_sel(q, disc, perd, **o), p, name, g[gname])
+
+
+def test_perd_bruteforce():
+    """Per-channel B_t, C_t: every output by the unrolled O(L^2) sum on that channel's own B, C."""
+    p = _perd(small_real(B=2, D=3, N=3, L=16, seed=47), 48)
+    y, _ = oracle.sel_fwd(**_sel_kw(p, perd=True))
+    for bi in range(2):
+        for di in range(3):
+            a = np.exp(p["delta"][bi, di][:, None] * p["A"][di][None, :])
+            bb = (p["delta"][bi, di] * p["x"][bi, di])[:, None] * p["Bm"][bi, di]
+            yb, _ = brute_real(a, bb, p["C"][bi, di], p["h0"][bi, di])
+            close(y[bi, di], yb, rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("disc", [0, 1])
+def test_perd_with_channel_independent_BC_equals_shared(disc):
+    """B_t, C_t repeated over the channels: the per-channel form gives the shared form's y, and its per-channel
+    gB, gC summed over the channels give the shared form's sums."""
+    p = small_real(B=2, D=3, N=4, L=21, seed=49)
+    q = dict(p)
+    q["Bm"] = np.repeat(p["Bm"][:, None], 3, axis=1)
+    q["C"] = np.repeat(p["C"][:, None], 3, axis=1)
+    y, hl = oracle.sel_fwd(**_sel_kw(p, disc=disc))
+    yq, hq = oracle.sel_fwd(**_sel_kw(q, disc=disc, perd=True))
+    close(yq, y, rtol=1e-13)
+    g = oracle.sel_bwd(**_sel_kw(p, disc=disc), gy=p["gy"], ghlast=p["ghlast"])
+    gq = oracle.sel_bwd(**_sel_kw(q, disc=disc, perd=True), gy=p["gy"], ghlast=p["ghlast"])
+    close(gq["gBm"].sum(axis=1), g["gBm"], rtol=1e-11, atol=1e-13)
+    close(gq["gC"].sum(axis=1), g["gC"], rtol=1e-11, atol=1e-13)
+    for k in ("gdelta", "gx", "gA", "gh0"):
+        close(gq[k], g[k], rtol=1e-11, atol=1e-13)
