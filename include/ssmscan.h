@@ -9,10 +9,11 @@
  * transition A_t:
  *
  *   - diagonal real.  SSM_REAL_SELECTIVE forms a_t = exp(delta_t * A) and the
- *     Euler input term b_t = delta_t * x_t * B_t from a step size delta, as in
- *     the selection-and-discretisation step of the lpnh.cn page "Selective
- *     State Space Models (S3M)", section 1.1.  SSM_REAL_DENSE takes a_t and
- *     b_t as given tensors.
+ *     Euler input term b_t = delta_t * x_t * B_t (or the zero-order-hold term
+ *     (exp(delta_t A) - 1) / A * x_t * B_t) from a step size delta, as in the
+ *     selection-and-discretisation step of the lpnh.cn page "Selective State
+ *     Space Models (S3M)", section 1.1.  SSM_REAL_DENSE takes a_t and b_t as
+ *     given tensors.
  *   - diagonal complex with shared controls (SPARC page, abstract): two
  *     per-step scalars, retention r_t and phase phi_t, drive every complex mode
  *     m through a_{t,m} = exp(r_t ln(lambda_m) + i phi_t theta_m), with
@@ -37,7 +38,8 @@
  * ---------------------------------------
  *  Memory.   Every pointer is a device pointer the caller owns, except where
  *            noted.  Tensors are dense, row-major, in the shapes stated, with
- *            no padding (the last dimension is contiguous).  The library never
+ *            no padding (the last dimension is contiguous), unless the call's
+ *            ssm_layout describes them as strided views.  The library never
  *            allocates device memory; scratch memory is the caller's workspace
  *            `ws` of at least ssm_workspace_bytes() bytes (256-byte aligned),
  *            used only during the call's stream work.  No pointer is kept
@@ -73,9 +75,11 @@
 extern "C" {
 #endif
 
-/* 5: adds ssm_scan_fwd_noalloc and ssm_roof_probe; 4 added SSM_COMPLEX_DENSE; 3 added
+/* 6: adds strided views (ssm_layout, the layout fields of ssm_scan_args and
+ * pd_scan_args) and the ZOH discretisation (discretization field); 5 added
+ * ssm_scan_fwd_noalloc and ssm_roof_probe; 4 added SSM_COMPLEX_DENSE; 3 added
  * ssm_sensitivity_rows and SSM_OP_SENS_ROWS; struct layouts as in 2 */
-#define SSM_ABI_VERSION 5
+#define SSM_ABI_VERSION 6
 
 /* status codes */
 #define SSM_OK               0
@@ -106,6 +110,74 @@ extern "C" {
 #define SSM_OP_COMPLEX_RTRL 5
 #define SSM_OP_OUTPUT_SENS  6
 #define SSM_OP_SENS_ROWS    7
+
+/* discretisations of SSM_REAL_SELECTIVE (S3M page, section 1.1) */
+#define SSM_EULER 0   /* b_t = delta_t x_t B_t (the default)                               */
+#define SSM_ZOH   1   /* zero-order hold: b_t[n] = (exp(delta_t A[d,n]) - 1) / A[d,n] x_t B_t[n],
+                         delta_t x_t B_t[n] where A[d,n] = 0 (the limit)                     */
+
+/*
+ * Strided views.  By default every tensor is dense and row-major in the shape
+ * stated for it.  A caller whose tensors are views -- slices of a larger
+ * buffer, or inputs expanded (broadcast) along a dimension -- passes an
+ * ssm_layout: for every tensor role r whose bit (1 << r) is set in `given`,
+ * stride[r] holds the element strides of the role's dimensions, outermost
+ * first (entries past the role's rank are ignored); other roles stay dense.
+ * Rules (checked before anything is enqueued):
+ *   - the innermost stride must be 1, strides are >= 0  -> SSM_ERR_LAYOUT;
+ *   - stride 0 (broadcast) is allowed on inputs only; an output's strides
+ *     must give distinct elements                        -> SSM_ERR_LAYOUT;
+ *   - a role the mode or entry point does not take as a view -> SSM_ERR_UNSUPPORTED.
+ * Gradients of a broadcast input are returned per broadcast position (in the
+ * expanded shape); the caller sums them over the broadcast dimension.
+ *
+ * Roles of ssm_scan_args.layout (logical shape; dense strides):
+ *   SSM_REAL_SELECTIVE, every entry point:
+ *     SSM_V_DELTA, SSM_V_X  (B,D,L)    inputs; any batch / channel stride
+ *     SSM_V_A               (D,N)      channel stride 0: one A row for every channel
+ *     SSM_V_BM, SSM_V_C     (B,D,L,N)  dense = (L*N, 0, N, 1): B_t, C_t shared by the
+ *                                      channels.  A nonzero channel stride (on either)
+ *                                      gives every channel its own B_t / C_t
+ *                                      (ssm_scan_fwd / _bwd only); gBm and gC are then
+ *                                      both (B,D,L,N) dense, per channel, not sums over
+ *                                      channels.  Batch stride 0: shared by the batch
+ *                                      rows (gBm / gC stay per batch row).
+ *   SSM_REAL_SELECTIVE, ssm_scan_fwd / ssm_scan_bwd:
+ *     SSM_V_Y, SSM_V_GY, SSM_V_GDELTA, SSM_V_GX (B,D,L) outputs / upstream gradient
+ *   SSM_COMPLEX_SHARED, ssm_scan_fwd / ssm_scan_bwd / ssm_complex_rtrl:
+ *     SSM_V_R, SSM_V_PHI    (B,H,L)    head stride 0: one control signal for all heads
+ *     SSM_V_U               (B,H,L,M)  complex elements (one (re, im) pair = 1)
+ *     SSM_V_LAM, SSM_V_THETA, SSM_V_CC (H,M) head stride 0: shared per-mode parameters
+ * Roles of pd_scan_args.layout:
+ *     SSM_V_LOGITS          (B,H,L,K)
+ *     SSM_V_PD_D, SSM_V_PD_B, SSM_V_PD_C (B,H,L,N)
+ *     SSM_V_DICT            (H,K,N)    head stride 0: one dictionary for every head
+ */
+#define SSM_V_DELTA   0
+#define SSM_V_X       1
+#define SSM_V_A       2
+#define SSM_V_BM      3
+#define SSM_V_C       4
+#define SSM_V_Y       5
+#define SSM_V_GY      6
+#define SSM_V_GDELTA  7
+#define SSM_V_GX      8
+#define SSM_V_R       9
+#define SSM_V_PHI    10
+#define SSM_V_U      11
+#define SSM_V_LAM    12
+#define SSM_V_THETA  13
+#define SSM_V_CC     14
+#define SSM_V_LOGITS 15
+#define SSM_V_PD_D   16
+#define SSM_V_PD_B   17
+#define SSM_V_PD_C   18
+#define SSM_V_DICT   19
+#define SSM_V_COUNT  20
+typedef struct {
+    uint64_t given;                    /* bit r: stride[r] describes role r */
+    int64_t  stride[SSM_V_COUNT][4];   /* element strides, outermost dimension first */
+} ssm_layout;
 
 /*
  * Arguments of the diagonal scans.  Sizes: batch = B; channels = D (real) or
@@ -152,6 +224,9 @@ typedef struct {
      * gdelta is then the gradient w.r.t. z.  Both off: delta is used as given. */
     const float* delta_bias;  /* nullable (D) f32 */
     int32_t delta_softplus;   /* 0 or 1 */
+    int32_t discretization;   /* SSM_REAL_SELECTIVE: SSM_EULER (0) or SSM_ZOH (ssm_scan_fwd,
+                                 ssm_scan_bwd, ssm_scan_fwd_noalloc); other modes: 0 */
+    const ssm_layout* layout; /* nullable: strided views (above); NULL = every tensor dense */
 } ssm_scan_args;
 
 typedef struct {
@@ -176,10 +251,10 @@ typedef struct {
     void*  gdelta;  /* selective (B,D,L) dtype                  */
     void*  gx;      /* selective (B,D,L) dtype                  */
     float* gA;      /* selective (D,N) f32 (sum over b and t)   */
-    void*  gBm;     /* selective (B,L,N) dtype (sum over d)     */
+    void*  gBm;     /* selective (B,L,N) dtype (sum over d); (B,D,L,N) for a per-channel Bm */
     float* ga;      /* dense (B,D,L,N) f32; complex dense (B,H,L,M) complex64 */
     float* gb;      /* dense (B,D,L,N) f32                      */
-    void*  gC;      /* real (B,L,N) dtype (sum over d)          */
+    void*  gC;      /* real (B,L,N) dtype (sum over d); (B,D,L,N) for a per-channel C */
     void*  gu;      /* complex (B,H,L,M) (re, im) pairs of dtype */
     void*  gr;      /* complex (B,H,L) dtype                    */
     void*  gphi;    /* complex (B,H,L) dtype                    */
@@ -211,6 +286,7 @@ typedef struct {
     const void*  C;        /* (B,H,L,N) dtype readout C_t                                   */
     const float* h0;       /* nullable (B,H,N) f32                                          */
     int32_t dtype;         /* SSM_F32 or SSM_BF16                                           */
+    const ssm_layout* layout;  /* nullable: strided views (roles above); NULL = dense       */
 } pd_scan_args;
 
 typedef struct {

@@ -9,6 +9,8 @@ all computation runs in the library's HIP kernels.
 """
 from .binding import (  # noqa: F401
     SSM_BF16,
+    SSM_EULER,
+    SSM_ZOH,
     SSM_COMPLEX_DENSE,
     SSM_COMPLEX_SHARED,
     SSM_F32,

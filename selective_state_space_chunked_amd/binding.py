@@ -19,6 +19,11 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libssmscan.so")
 
 SSM_F32, SSM_BF16 = 0, 1
+SSM_EULER, SSM_ZOH = 0, 1
+# roles of the strided views (ssm_layout)
+(V_DELTA, V_X, V_A, V_BM, V_C, V_Y, V_GY, V_GDELTA, V_GX, V_R, V_PHI, V_U, V_LAM, V_THETA, V_CC, V_LOGITS,
+ V_PD_D, V_PD_B, V_PD_C, V_DICT) = range(20)
+V_COUNT = 20
 SSM_REAL_SELECTIVE, SSM_REAL_DENSE, SSM_COMPLEX_SHARED, SSM_COMPLEX_DENSE = 0, 1, 2, 3
 _COMPLEX_MODES = (SSM_COMPLEX_SHARED, SSM_COMPLEX_DENSE)
 (SSM_OP_SCAN_FWD, SSM_OP_SCAN_BWD, SSM_OP_IMPULSE, SSM_OP_PD_FWD, SSM_OP_PD_BWD, SSM_OP_COMPLEX_RTRL,
@@ -28,12 +33,44 @@ _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64
 
 
+class Layout(ctypes.Structure):
+    _fields_ = [("given", ctypes.c_uint64), ("stride", (ctypes.c_int64 * 4) * V_COUNT)]
+
+
+class _Views:
+    """The strides of the tensors of one call that are views (non-dense or broadcast)."""
+
+    def __init__(self):
+        self.lay = Layout()
+        self.any = False
+
+    def set(self, role, strides, dense):
+        strides = tuple(int(v) for v in strides)
+        if strides != tuple(int(v) for v in dense):
+            self.lay.given |= 1 << role
+            for i, v in enumerate(strides):
+                self.lay.stride[role][i] = v
+            self.any = True
+
+    def ptr(self):
+        return ctypes.pointer(self.lay) if self.any else None
+
+
+def _dense_strides(shape):
+    st, acc = [], 1
+    for n in reversed(shape):
+        st.append(acc)
+        acc *= int(n)
+    return tuple(reversed(st))
+
+
 class ScanArgs(ctypes.Structure):
     _fields_ = [("mode", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("batch", _i64), ("channels", _i64), ("length", _i64), ("state", _i64), ("chunk_len", _i64),
                 ("delta", _vp), ("x", _vp), ("A", _vp), ("Bm", _vp), ("a", _vp), ("b", _vp), ("C", _vp),
                 ("r", _vp), ("phi", _vp), ("lam", _vp), ("theta", _vp), ("u", _vp), ("c", _vp), ("h0", _vp),
-                ("delta_bias", _vp), ("delta_softplus", ctypes.c_int32)]
+                ("delta_bias", _vp), ("delta_softplus", ctypes.c_int32), ("discretization", ctypes.c_int32),
+                ("layout", ctypes.POINTER(Layout))]
 
 
 class ScanFwdOut(ctypes.Structure):
@@ -53,7 +90,7 @@ class ScanGrads(ctypes.Structure):
 class PDArgs(ctypes.Structure):
     _fields_ = [("batch", _i64), ("heads", _i64), ("length", _i64), ("state", _i64), ("dict_size", _i64),
                 ("chunk_len", _i64), ("logits", _vp), ("sel", _vp), ("dict", _vp), ("d", _vp), ("b", _vp),
-                ("C", _vp), ("h0", _vp), ("dtype", ctypes.c_int32)]
+                ("C", _vp), ("h0", _vp), ("dtype", ctypes.c_int32), ("layout", ctypes.POINTER(Layout))]
 
 
 class PDFwdOut(ctypes.Structure):
@@ -119,7 +156,9 @@ def _stream(dev):
     return torch.cuda.current_stream(dev).cuda_stream
 
 
-def _need(t, name, dtype=None, shape=None, device=None):
+def _need(t, name, dtype=None, shape=None, device=None, view=False):
+    """Check a tensor argument.  ``view``: a strided view is accepted (any strides with the last dimension
+    contiguous; the library takes its strides), otherwise the tensor must be contiguous."""
     if t is None:
         return None
     if not isinstance(t, torch.Tensor):
@@ -130,7 +169,10 @@ def _need(t, name, dtype=None, shape=None, device=None):
         raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
     if shape is not None and tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
-    if not t.is_contiguous():
+    if view:
+        if t.dim() and t.shape[-1] > 1 and t.stride(-1) != 1:
+            raise ValueError(f"{name}: the last dimension must be contiguous (stride 1)")
+    elif not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     return t
 
@@ -158,12 +200,27 @@ def _alloc(shape, dtype, device, role="output"):
     return torch.empty(shape, dtype=dtype, device=device)
 
 
-def _out(out, key, shape, dtype, device):
-    """out[key]: the caller's tensor, checked like an input, or a new one of the given shape and dtype."""
+def _out(out, key, shape, dtype, device, view=False):
+    """out[key]: the caller's tensor, checked like an input, or a new one of the given shape and dtype.
+    ``view``: the caller's tensor may be a strided view (distinct elements, last dimension contiguous)."""
     if key in out and out[key] is not None:
-        return _need(out[key], f"out[{key!r}]", dtype, shape, device)
+        t = _need(out[key], f"out[{key!r}]", dtype, shape, device, view=view)
+        if view and not _distinct(t):
+            raise ValueError(f"out[{key!r}]: an output view needs distinct elements (no stride 0)")
+        return t
     out[key] = _alloc(shape, dtype, device)
     return out[key]
+
+
+def _distinct(t):
+    """True when no two indices of t address the same element."""
+    dims = sorted((st, n) for st, n in zip(t.stride(), t.shape) if n > 1)
+    span = 1
+    for st, n in dims:
+        if st < span:
+            return False
+        span += st * (n - 1)
+    return True
 
 
 def _on_gpu(device):
@@ -190,23 +247,41 @@ def n_chunks(L, chunk_len):
 # diagonal scans
 # ---------------------------------------------------------------------------
 def _scan_args(mode, *, delta=None, x=None, A=None, Bm=None, a=None, b=None, C=None, r=None, phi=None, lam=None,
-               theta=None, u=None, c=None, h0=None, delta_bias=None, delta_softplus=False, chunk_len=0):
+               theta=None, u=None, c=None, h0=None, delta_bias=None, delta_softplus=False, discretization=SSM_EULER,
+               chunk_len=0):
     """Marshal the scan arguments.  Selective mode: with ``delta_bias`` (D,) or
     ``delta_softplus`` set, ``delta`` is the projection output z and the scan uses
-    softplus(z + delta_bias) (or z + delta_bias)."""
+    softplus(z + delta_bias) (or z + delta_bias); ``discretization`` SSM_ZOH selects the
+    zero-order-hold input term.  Inputs may be strided views (slices, ``expand``): the
+    selective delta, x, A, Bm, C (Bm, C either (B, L, N), shared by the channels, or
+    (B, D, L, N), per channel unless expanded along D) and the complex r, phi, u, lam,
+    theta, c; their strides go to the library."""
+    vw = _Views()
+    perd = False
     if mode == SSM_REAL_SELECTIVE:
-        _need(delta, "delta")
+        _need(delta, "delta", view=True)
         Bsz, D, L = delta.shape
         N = A.shape[1]
         st = delta.dtype
         if st not in (torch.float32, torch.bfloat16):
             raise TypeError("delta must be float32 or bfloat16")
         dev = delta.device
-        for nm, t, shp in (("x", x, (Bsz, D, L)), ("Bm", Bm, (Bsz, L, N)), ("C", C, (Bsz, L, N))):
-            _need(t, nm, st, shp, dev)
-        _need(A, "A", torch.float32, (D, N), dev)
+        _need(x, "x", st, (Bsz, D, L), dev, view=True)
+        for nm, t, role in (("Bm", Bm, V_BM), ("C", C, V_C)):
+            if t is not None and t.dim() == 4:
+                _need(t, nm, st, (Bsz, D, L, N), dev, view=True)
+                vw.set(role, t.stride(), (L * N, 0, N, 1))
+                perd = perd or (t.stride(1) != 0 and D > 1)
+            else:
+                _need(t, nm, st, (Bsz, L, N), dev, view=True)
+                if t is not None:
+                    vw.set(role, (t.stride(0), 0, t.stride(1), t.stride(2)), (L * N, 0, N, 1))
+        _need(A, "A", torch.float32, (D, N), dev, view=True)
         _need(h0, "h0", torch.float32, (Bsz, D, N), dev)
         _need(delta_bias, "delta_bias", torch.float32, (D,), dev)
+        vw.set(V_DELTA, delta.stride(), (D * L, L, 1))
+        vw.set(V_X, x.stride(), (D * L, L, 1))
+        vw.set(V_A, A.stride(), (N, 1))
         dt = SSM_BF16 if st == torch.bfloat16 else SSM_F32
     elif mode == SSM_REAL_DENSE:
         _need(a, "a", torch.float32)
@@ -228,28 +303,45 @@ def _scan_args(mode, *, delta=None, x=None, A=None, Bm=None, a=None, b=None, C=N
         dt = SSM_F32
     else:
         # u: complex64 (B,H,L,M), or bfloat16 (B,H,L,M,2) holding (re, im) pairs; r, phi follow
-        _need(u, "u")
+        _need(u, "u", view=True)
         if u.dtype == torch.complex64:
             Bsz, D, L, N = u.shape
             st = torch.float32
+            vw.set(V_U, u.stride(), _dense_strides(u.shape))
         elif u.dtype == torch.bfloat16 and u.dim() == 5 and u.shape[-1] == 2:
             Bsz, D, L, N = u.shape[:4]
             st = torch.bfloat16
+            if u.stride(3) != 2 and N > 1:
+                raise ValueError("u: the (re, im) pairs of the modes must be contiguous")
+            if any(v % 2 for v in u.stride()[:3]):
+                raise ValueError("u: strides must be whole (re, im) pairs")
+            vw.set(V_U, tuple(v // 2 for v in u.stride()[:3]) + (1,), _dense_strides(u.shape[:4]))
         else:
             raise TypeError("u must be complex64 (B,H,L,M) or bfloat16 (B,H,L,M,2)")
         dev = u.device
-        for nm, t in (("r", r), ("phi", phi)):
-            _need(t, nm, st, (Bsz, D, L), dev)
-        for nm, t in (("lam", lam), ("theta", theta)):
-            _need(t, nm, torch.float32, (D, N), dev)
-        _need(c, "c", torch.complex64, (D, N), dev)
+        for nm, t, role in (("r", r, V_R), ("phi", phi, V_PHI)):
+            _need(t, nm, st, (Bsz, D, L), dev, view=True)
+            vw.set(role, t.stride(), (D * L, L, 1))
+        for nm, t, role in (("lam", lam, V_LAM), ("theta", theta, V_THETA)):
+            _need(t, nm, torch.float32, (D, N), dev, view=True)
+            vw.set(role, t.stride(), (N, 1))
+        _need(c, "c", torch.complex64, (D, N), dev, view=True)
+        vw.set(V_CC, c.stride(), (N, 1))
         _need(h0, "h0", torch.complex64, (Bsz, D, N), dev)
         dt = SSM_BF16 if st == torch.bfloat16 else SSM_F32
     args = ScanArgs(mode=mode, dtype=dt, batch=Bsz, channels=D, length=L, state=N, chunk_len=chunk_len,
                     delta=_ptr(delta), x=_ptr(x), A=_ptr(A), Bm=_ptr(Bm), a=_ptr(a), b=_ptr(b), C=_ptr(C),
                     r=_ptr(r), phi=_ptr(phi), lam=_ptr(lam), theta=_ptr(theta), u=_ptr(u), c=_ptr(c),
-                    h0=_ptr(h0), delta_bias=_ptr(delta_bias), delta_softplus=int(bool(delta_softplus)))
+                    h0=_ptr(h0), delta_bias=_ptr(delta_bias), delta_softplus=int(bool(delta_softplus)),
+                    discretization=int(discretization))
+    args._views = vw          # kept with the struct: the library reads it during the call
+    args._perd = perd
+    args.layout = vw.ptr()
     return args, (Bsz, D, L, N), dev
+
+
+def _set_layout(args):
+    args.layout = args._views.ptr()
 
 
 def _stream_dtype(mode, tensors):
@@ -288,10 +380,14 @@ def _scan_fwd(mode, want_y, want_h_last, want_ckpt, chunk_len, out, tensors, noa
     ydt = _stream_dtype(mode, tensors)
     sdt = torch.complex64 if mode in _COMPLEX_MODES else torch.float32
     nc = n_chunks(L, _chunk(mode, chunk_len))
+    sel = mode == SSM_REAL_SELECTIVE
     for k, want, shp, dt in (("y", want_y, (Bsz, D, L), ydt), ("h_last", want_h_last, (Bsz, D, N), sdt),
                              ("ckpt", want_ckpt, (Bsz, D, nc, N), sdt)):
         if want or out.get(k) is not None:
-            _out(out, k, shp, dt, dev)
+            _out(out, k, shp, dt, dev, view=sel and k == "y")
+    if sel and out.get("y") is not None:
+        args._views.set(V_Y, out["y"].stride(), (D * L, L, 1))
+        _set_layout(args)
     _on_gpu(dev)
     o = ScanFwdOut(y=_ptr(out.get("y")), h_last=_ptr(out.get("h_last")), ckpt=_ptr(out.get("ckpt")))
     if noalloc:
@@ -315,14 +411,16 @@ def scan_bwd(mode, *, gy, gh_last=None, ckpt=None, want=None, chunk_len=0, out=N
     args, (Bsz, D, L, N), dev = _scan_args(mode, chunk_len=chunk_len, **tensors)
     ydt = _stream_dtype(mode, tensors)
     sdt = torch.complex64 if mode in _COMPLEX_MODES else torch.float32
-    _need(gy, "gy", ydt, (Bsz, D, L), dev)
+    sel = mode == SSM_REAL_SELECTIVE
+    _need(gy, "gy", ydt, (Bsz, D, L), dev, view=sel)
     _need(gh_last, "gh_last", sdt, (Bsz, D, N), dev)
     nc = n_chunks(L, _chunk(mode, chunk_len))
     _need(ckpt, "ckpt", sdt, (Bsz, D, nc, N), dev)
     want = tuple(want) if want is not None else _GRADS[mode]
+    gbc = (Bsz, D, L, N) if args._perd else (Bsz, L, N)   # per-channel B_t, C_t: per-channel gradients
     shapes = {
         "gdelta": ((Bsz, D, L), ydt), "gx": ((Bsz, D, L), ydt), "gA": ((D, N), torch.float32),
-        "gBm": ((Bsz, L, N), ydt), "gC": ((Bsz, L, N), ydt), "gh0": ((Bsz, D, N), sdt),
+        "gBm": (gbc, ydt), "gC": (gbc, ydt), "gh0": ((Bsz, D, N), sdt),
         "ga": ((Bsz, D, L, N), sdt), "gb": ((Bsz, D, L, N), torch.float32),
         "gu": (((Bsz, D, L, N), torch.complex64) if ydt == torch.float32 else ((Bsz, D, L, N, 2), ydt)),
         "gr": ((Bsz, D, L), ydt), "gphi": ((Bsz, D, L), ydt), "glam": ((D, N), torch.float32),
@@ -335,7 +433,13 @@ def scan_bwd(mode, *, gy, gh_last=None, ckpt=None, want=None, chunk_len=0, out=N
     for k in set(want) | {k for k, v in out.items() if v is not None}:
         if not exists(k):
             raise ValueError(f"gradient {k} does not exist for mode {mode}")
-        _out(out, k, *shapes[k], dev)
+        _out(out, k, *shapes[k], dev, view=sel and k in ("gdelta", "gx"))
+    if sel:
+        args._views.set(V_GY, gy.stride(), (D * L, L, 1))
+        for k, role in (("gdelta", V_GDELTA), ("gx", V_GX)):
+            if out.get(k) is not None:
+                args._views.set(role, out[k].stride(), (D * L, L, 1))
+        _set_layout(args)
     _on_gpu(dev)
     g = ScanGrads(**{f[0]: _ptr(out.get(f[0])) for f in ScanGrads._fields_})
     i = ScanBwdIn(gy=_ptr(gy), gh_last=_ptr(gh_last), ckpt=_ptr(ckpt))
@@ -413,25 +517,34 @@ def complex_rtrl(*, gy, gh_last=None, want_y=True, chunk_len=0, out=None, **tens
 # PD scan
 # ---------------------------------------------------------------------------
 def _pd_args(*, logits=None, sel=None, dict, d, b, C, h0=None, chunk_len=0):
-    """Streams (logits, d, b, C) are all float32 or all bfloat16 (the dtype of d)."""
-    _need(d, "d")
+    """Streams (logits, d, b, C) are all float32 or all bfloat16 (the dtype of d).  logits, d, b, C and
+    the dictionary may be strided views (a dictionary expanded along the heads is shared by them)."""
+    _need(d, "d", view=True)
     st = d.dtype
     if st not in (torch.float32, torch.bfloat16):
         raise TypeError("d must be float32 or bfloat16")
     Bsz, H, L, N = d.shape
     dev = d.device
     K = dict.shape[1]
-    _need(dict, "dict", torch.int32, (H, K, N), dev)
-    _need(logits, "logits", st, (Bsz, H, L, K), dev)
+    vw = _Views()
+    _need(dict, "dict", torch.int32, (H, K, N), dev, view=True)
+    _need(logits, "logits", st, (Bsz, H, L, K), dev, view=True)
     _need(sel, "sel", torch.int32, (Bsz, H, L), dev)
     if logits is None and sel is None:
         raise ValueError("logits or sel is required")
     for nm, t in (("b", b), ("C", C)):
-        _need(t, nm, st, (Bsz, H, L, N), dev)
+        _need(t, nm, st, (Bsz, H, L, N), dev, view=True)
     _need(h0, "h0", torch.float32, (Bsz, H, N), dev)
+    for t, role in ((d, V_PD_D), (b, V_PD_B), (C, V_PD_C)):
+        vw.set(role, t.stride(), (H * L * N, L * N, N, 1))
+    if logits is not None:
+        vw.set(V_LOGITS, logits.stride(), (H * L * K, L * K, K, 1))
+    vw.set(V_DICT, dict.stride(), (K * N, N, 1))
     args = PDArgs(batch=Bsz, heads=H, length=L, state=N, dict_size=K, chunk_len=chunk_len,
                   logits=_ptr(logits), sel=_ptr(sel), dict=_ptr(dict), d=_ptr(d), b=_ptr(b), C=_ptr(C),
                   h0=_ptr(h0), dtype=SSM_BF16 if st == torch.bfloat16 else SSM_F32)
+    args._views = vw
+    args.layout = vw.ptr()
     return args, (Bsz, H, L, N, K), dev
 
 

@@ -130,6 +130,88 @@ void plan_segments(int64_t wg_per_seg, int64_t nunits, int* G, int* per_seg, int
 // ---------------------------------------------------------------------------
 // diagonal real / complex scans: shared validation
 // ---------------------------------------------------------------------------
+// ---------------------------------------------------------------------------
+// strided views (ssm_layout): per role, the logical shape, the dense strides
+// and the strides this call uses
+// ---------------------------------------------------------------------------
+const char* const kRoleName[SSM_V_COUNT] = {"delta", "x", "A", "Bm", "C", "y", "gy", "gdelta", "gx", "r",
+                                            "phi", "u", "lam", "theta", "c", "logits", "d", "b", "C", "dict"};
+struct Views {
+    int rank[SSM_V_COUNT] = {};
+    int64_t dim[SSM_V_COUNT][4] = {};
+    int64_t s[SSM_V_COUNT][4] = {};    // strides in use (dense unless given)
+    bool given[SSM_V_COUNT] = {};
+    void spec(int r, std::initializer_list<int64_t> dims, std::initializer_list<int64_t> dense) {
+        rank[r] = (int)dims.size();
+        int i = 0;
+        for (int64_t d : dims) dim[r][i++] = d;
+        i = 0;
+        for (int64_t d : dense) s[r][i++] = d;
+    }
+    // elements spanned: 1 + sum (dim - 1) * stride (0 when a dimension is empty)
+    size_t extent(int r) const {
+        size_t e = 1;
+        for (int i = 0; i < rank[r]; ++i) {
+            if (dim[r][i] == 0) return 0;
+            e += (size_t)(dim[r][i] - 1) * (size_t)s[r][i];
+        }
+        return e;
+    }
+    // element offsets of a stream row (b, c): b * s0 + c * s1
+    int64_t sb(int r) const { return s[r][0]; }
+    int64_t sd(int r) const { return s[r][1]; }
+};
+
+// An output's strides must give distinct elements: ordered by stride, every
+// dimension of more than one element strides past everything inside it.
+bool distinct_elements(const Views& v, int r) {
+    int idx[4];
+    int n = 0;
+    for (int i = 0; i < v.rank[r]; ++i)
+        if (v.dim[r][i] > 1) idx[n++] = i;
+    std::sort(idx, idx + n, [&](int x, int y) { return v.s[r][x] < v.s[r][y]; });
+    int64_t span = 1;
+    for (int k = 0; k < n; ++k) {
+        const int i = idx[k];
+        if (v.s[r][i] < span) return false;
+        span = v.s[r][i] * (v.dim[r][i] - 1) + span;
+    }
+    return true;
+}
+
+// Take the caller's strides for the roles in `use_in` (inputs) and `use_out`
+// (outputs); any other given role is refused.
+int resolve_views(const ssm_layout* lay, uint64_t use_in, uint64_t use_out, Views* v, const char* who) {
+    if (!lay) return SSM_OK;
+    if (lay->given >> SSM_V_COUNT) return fail(SSM_ERR_UNSUPPORTED, "layout names an unknown role");
+    for (int r = 0; r < SSM_V_COUNT; ++r) {
+        if (!((lay->given >> r) & 1)) continue;
+        const bool in = (use_in >> r) & 1, out = (use_out >> r) & 1;
+        if (!in && !out) return fail(SSM_ERR_UNSUPPORTED, "%s does not take %s as a strided view", who, kRoleName[r]);
+        const int k = v->rank[r];
+        for (int i = 0; i < k; ++i) {
+            const int64_t st = lay->stride[r][i];
+            if (st < 0) return fail(SSM_ERR_LAYOUT, "%s: negative stride %lld", kRoleName[r], (long long)st);
+            v->s[r][i] = st;
+        }
+        // the innermost dimension must be contiguous (its stride is irrelevant for a single element)
+        if (v->dim[r][k - 1] > 1 && v->s[r][k - 1] != 1)
+            return fail(SSM_ERR_LAYOUT, "%s: innermost stride must be 1 (got %lld)", kRoleName[r],
+                        (long long)v->s[r][k - 1]);
+        v->s[r][k - 1] = 1;
+        if (out && !distinct_elements(*v, r))
+            return fail(SSM_ERR_LAYOUT, "output %s: strides must give distinct elements (no stride 0)", kRoleName[r]);
+        if (v->s[r][0] >= (1LL << 40) || (k > 1 && v->s[r][1] >= (1LL << 40)))
+            return fail(SSM_ERR_LAYOUT, "%s: stride too large", kRoleName[r]);
+        v->given[r] = true;
+    }
+    return SSM_OK;
+}
+constexpr uint64_t bit(int r) { return 1ull << r; }
+
+// Entry points, for the roles each takes as views.
+enum Entry { E_FWD, E_BWD, E_SENS, E_RTRL };
+
 struct ScanPlan {
     int mode, dtype;
     int64_t B, D, L, N;
@@ -138,10 +220,25 @@ struct ScanPlan {
     int nchunks;   // ceil(L/T)
     size_t esz;    // bytes per streamed element
     bool empty;    // no batch rows, channels or steps: only h_last / gh0 / parameter gradients are defined
+    int disc;      // SSM_EULER or SSM_ZOH
+    bool perd;     // selective: Bm and C given per channel
+    Views v;
 };
 
+void scan_view_specs(ScanPlan* pl) {
+    const int64_t B = pl->B, D = pl->D, L = pl->L, N = pl->N;
+    Views& v = pl->v;
+    for (int r : {SSM_V_DELTA, SSM_V_X, SSM_V_Y, SSM_V_GY, SSM_V_GDELTA, SSM_V_GX, SSM_V_R, SSM_V_PHI})
+        v.spec(r, {B, D, L}, {D * L, L, 1});
+    v.spec(SSM_V_A, {D, N}, {N, 1});
+    v.spec(SSM_V_BM, {B, D, L, N}, {L * N, 0, N, 1});   // shared by the channels
+    v.spec(SSM_V_C, {B, D, L, N}, {L * N, 0, N, 1});
+    v.spec(SSM_V_U, {B, D, L, N}, {D * L * N, L * N, N, 1});
+    for (int r : {SSM_V_LAM, SSM_V_THETA, SSM_V_CC}) v.spec(r, {D, N}, {N, 1});
+}
+
 // sel_default_T: the selective mode's checkpoint interval when chunk_len is 0
-int validate_scan_args(const ssm_scan_args* a, ScanPlan* pl, int sel_default_T = 256) {
+int validate_scan_args(const ssm_scan_args* a, ScanPlan* pl, int sel_default_T = 256, Entry entry = E_FWD) {
     if (!a) return fail(SSM_ERR_NULL, "args is NULL");
     pl->mode = a->mode;
     pl->dtype = a->dtype;
@@ -182,6 +279,35 @@ int validate_scan_args(const ssm_scan_args* a, ScanPlan* pl, int sel_default_T =
         return fail(SSM_ERR_SHAPE, "delta_softplus must be 0 or 1 (got %d)", a->delta_softplus);
     if (a->mode != SSM_REAL_SELECTIVE && (a->delta_bias || a->delta_softplus))
         return fail(SSM_ERR_UNSUPPORTED, "delta_bias / delta_softplus apply to SSM_REAL_SELECTIVE only");
+    if (a->discretization != SSM_EULER && a->discretization != SSM_ZOH)
+        return fail(SSM_ERR_SHAPE, "unknown discretization %d", a->discretization);
+    pl->disc = a->discretization;
+    if (pl->disc == SSM_ZOH && a->mode != SSM_REAL_SELECTIVE)
+        return fail(SSM_ERR_UNSUPPORTED, "the ZOH discretisation applies to SSM_REAL_SELECTIVE only");
+    if (pl->disc == SSM_ZOH && entry != E_FWD && entry != E_BWD)
+        return fail(SSM_ERR_UNSUPPORTED, "the sensitivity entry points take the Euler discretisation only");
+    scan_view_specs(pl);
+    {
+        uint64_t in = 0, out = 0;
+        if (a->mode == SSM_REAL_SELECTIVE) {
+            in = bit(SSM_V_DELTA) | bit(SSM_V_X) | bit(SSM_V_A) | bit(SSM_V_BM) | bit(SSM_V_C);
+            if (entry == E_FWD) out = bit(SSM_V_Y);
+            if (entry == E_BWD) { in |= bit(SSM_V_GY); out = bit(SSM_V_GDELTA) | bit(SSM_V_GX); }
+        } else if (a->mode == SSM_COMPLEX_SHARED) {
+            in = bit(SSM_V_R) | bit(SSM_V_PHI) | bit(SSM_V_U) | bit(SSM_V_LAM) | bit(SSM_V_THETA) | bit(SSM_V_CC);
+        }
+        if (int rc = resolve_views(a->layout, in, out, &pl->v, "this mode and entry point")) return rc;
+    }
+    pl->perd = false;
+    if (a->mode == SSM_REAL_SELECTIVE) {
+        // either one per channel: both are read per channel (a shared one through its zero channel
+        // stride) and both gradients are per channel
+        pl->perd = pl->D > 1 && (pl->v.sd(SSM_V_BM) != 0 || pl->v.sd(SSM_V_C) != 0);
+        if (pl->perd && entry != E_FWD && entry != E_BWD)
+            return fail(SSM_ERR_UNSUPPORTED, "the sensitivity entry points take Bm and C shared by the channels");
+        if (pl->perd && pl->disc == SSM_ZOH)
+            return fail(SSM_ERR_UNSUPPORTED, "the ZOH discretisation takes Bm and C shared by the channels");
+    }
     if (a->mode == SSM_REAL_SELECTIVE) {
         if (!pl->empty && (!a->delta || !a->x || !a->A || !a->Bm || !a->C))
             return fail(SSM_ERR_NULL, "SSM_REAL_SELECTIVE needs delta, x, A, Bm and C");
@@ -218,16 +344,17 @@ int validate_scan_args(const ssm_scan_args* a, ScanPlan* pl, int sel_default_T =
 }
 
 std::vector<Range> scan_inputs(const ssm_scan_args* a, const ScanPlan& p) {
-    const size_t BDL = p.B * p.D * p.L, BLN = p.B * p.L * p.N, BDLN = BDL * p.N;
+    const size_t BDL = p.B * p.D * p.L, BDLN = BDL * p.N;
     const size_t st = p.N * (is_complex(p.mode) ? 8 : 4);
+    const Views& v = p.v;
     return {
-        {a->delta, BDL * p.esz, "delta"}, {a->x, BDL * p.esz, "x"},
-        {a->A, (size_t)p.D * p.N * 4, "A"}, {a->Bm, BLN * p.esz, "Bm"},
+        {a->delta, v.extent(SSM_V_DELTA) * p.esz, "delta"}, {a->x, v.extent(SSM_V_X) * p.esz, "x"},
+        {a->A, v.extent(SSM_V_A) * 4, "A"}, {a->Bm, v.extent(SSM_V_BM) * p.esz, "Bm"},
         {a->a, BDLN * (p.mode == SSM_COMPLEX_DENSE ? 8 : 4), "a"}, {a->b, BDLN * 4, "b"},
-        {a->C, BLN * (p.mode == SSM_REAL_SELECTIVE ? p.esz : 4), "C"},
-        {a->r, BDL * p.esz, "r"}, {a->phi, BDL * p.esz, "phi"},
-        {a->lam, (size_t)p.D * p.N * 4, "lam"}, {a->theta, (size_t)p.D * p.N * 4, "theta"},
-        {a->u, BDLN * 2 * p.esz, "u"}, {a->c, (size_t)p.D * p.N * 8, "c"},
+        {a->C, v.extent(SSM_V_C) * (p.mode == SSM_REAL_SELECTIVE ? p.esz : 4), "C"},
+        {a->r, v.extent(SSM_V_R) * p.esz, "r"}, {a->phi, v.extent(SSM_V_PHI) * p.esz, "phi"},
+        {a->lam, v.extent(SSM_V_LAM) * 4, "lam"}, {a->theta, v.extent(SSM_V_THETA) * 4, "theta"},
+        {a->u, v.extent(SSM_V_U) * 2 * p.esz, "u"}, {a->c, v.extent(SSM_V_CC) * 8, "c"},
         {a->h0, (size_t)p.B * p.D * st, "h0"},
         {a->delta_bias, (size_t)p.D * 4, "delta_bias"},
     };
@@ -251,12 +378,30 @@ void sel_fwd_layout(const ScanPlan& p, Carve& cv, SelFwdLayout* lay) {
     }
 }
 
-int sel_vec(const ScanPlan& p, std::initializer_list<const void*> ptrs) {
+// 16-byte loads and stores of the (B,D,L) streams: every row start aligned
+// (steps contiguous, batch and channel strides whole 16-byte units)
+int sel_vec(const ScanPlan& p, std::initializer_list<const void*> ptrs, std::initializer_list<int> roles = {}) {
     if (p.L % 8 != 0) return 0;
     for (const void* q : ptrs)
         if (!aligned16(q)) return 0;
+    const int64_t unit = 16 / (int64_t)p.esz;
+    for (int r : roles)
+        if (p.v.s[r][0] % unit || p.v.s[r][1] % unit) return 0;
     return 1;
 }
+// 16-byte loads of B_t / C_t rows (state dimension contiguous)
+int sel_bc_vec(const ScanPlan& p, const void* Bm, const void* C) {
+    const int64_t unit = 16 / (int64_t)p.esz;
+    if (!aligned16(Bm) || !aligned16(C) || p.N % unit) return 0;
+    for (int r : {SSM_V_BM, SSM_V_C})
+        if (p.v.s[r][0] % unit || p.v.s[r][2] % unit) return 0;
+    return 1;
+}
+template <int K>
+void copy_strides(int64_t (&dst)[K], const ScanPlan& p, int r) {
+    for (int i = 0; i < K; ++i) dst[i] = p.v.s[r][i];
+}
+int sel_var(const ScanPlan& p) { return p.perd ? kVarPerD : p.disc == SSM_ZOH ? kVarZoh : kVarEuler; }
 
 int run_sel_fwd(const ssm_scan_args* a, const ScanPlan& p, const SelFwdLayout& lay, void* y, float* h_last,
                 float* ckpt, float* tile_dsum, hipStream_t st) {
@@ -267,8 +412,13 @@ int run_sel_fwd(const ssm_scan_args* a, const ScanPlan& p, const SelFwdLayout& l
     q.segP = lay.segP; q.segS = lay.segS;
     q.B = (int)p.B; q.D = (int)p.D; q.L = (int)p.L; q.N = (int)p.N;
     q.ntiles = p.nchunks; q.tiles_per_seg = lay.tps; q.G = lay.G;
-    q.vec = sel_vec(p, {a->delta, a->x, y});
+    q.vec = sel_vec(p, {a->delta, a->x, y}, {SSM_V_DELTA, SSM_V_X, SSM_V_Y});
     q.stepf = StepXform{a->delta_bias, a->delta_softplus};
+    copy_strides(q.sdelta, p, SSM_V_DELTA); copy_strides(q.sx, p, SSM_V_X); copy_strides(q.sy, p, SSM_V_Y);
+    copy_strides(q.sBm, p, SSM_V_BM); copy_strides(q.sC, p, SSM_V_C);
+    q.sA = p.v.s[SSM_V_A][0];
+    q.bc_vec = sel_bc_vec(p, a->Bm, a->C);
+    q.var = sel_var(p);
     if (lay.G > 1) {
         SSM_LAUNCH(launch_sel_fwd(q, p.dtype, p.kpl, true, st), "selective forward summary");
         SSM_LAUNCH(launch_seg_combine_fwd(lay.segP, lay.segS, a->h0, lay.carry, (int)(p.B * p.D), lay.G,
@@ -353,7 +503,7 @@ int scan_fwd_impl(const ssm_scan_args* a, const ssm_scan_fwd_out* out, void* ws,
     if (!need_only) {
         if (!out) return fail(SSM_ERR_NULL, "out is NULL");
         const size_t st_b = is_complex(p.mode) ? 8 : 4;
-        const size_t yb = p.B * p.D * p.L * (p.mode == SSM_REAL_DENSE ? 4 : p.esz);  // esz is 4 for complex dense
+        const size_t yb = p.v.extent(SSM_V_Y) * (p.mode == SSM_REAL_DENSE ? 4 : p.esz);  // esz is 4 for complex dense
         const size_t hb = p.B * p.D * p.N * st_b;
         std::vector<Range> outs = {{out->y, yb, "y"}, {out->h_last, hb, "h_last"},
                                    {out->ckpt, hb * p.nchunks, "ckpt"}};
@@ -401,7 +551,7 @@ int scan_fwd_impl(const ssm_scan_args* a, const ssm_scan_fwd_out* out, void* ws,
 int scan_bwd_impl(const ssm_scan_args* a, const ssm_scan_bwd_in* in, const ssm_scan_grads* g, void* ws,
                   size_t ws_bytes, hipStream_t st, size_t* need_only) {
     ScanPlan p;
-    int rc = validate_scan_args(a, &p);
+    int rc = validate_scan_args(a, &p, 256, E_BWD);
     if (rc) return rc;
     static const ssm_scan_grads kNoGrads{};
     static const ssm_scan_bwd_in kNoIn{};
@@ -419,14 +569,16 @@ int scan_bwd_impl(const ssm_scan_args* a, const ssm_scan_bwd_in* in, const ssm_s
         const size_t BDL = p.B * p.D * p.L, BLN = p.B * p.L * p.N;
         const size_t hb = p.B * p.D * p.N * st_b;
         std::vector<Range> ins = scan_inputs(a, p);
-        ins.push_back({in->gy, BDL * es, "gy"});
+        ins.push_back({in->gy, p.v.extent(SSM_V_GY) * es, "gy"});
         ins.push_back({in->gh_last, hb, "gh_last"});
         ins.push_back({in->ckpt, hb * p.nchunks, "ckpt"});
+        const size_t gbc = p.perd ? BDL * p.N : BLN;   // per-channel Bm / C: gradients per channel
         std::vector<Range> outs = {
-            {g->gdelta, BDL * es, "gdelta"}, {g->gx, BDL * es, "gx"}, {g->gA, (size_t)p.D * p.N * 4, "gA"},
-            {g->gBm, BLN * es, "gBm"}, {g->ga, BDL * p.N * (p.mode == SSM_COMPLEX_DENSE ? 8 : 4), "ga"},
+            {g->gdelta, p.v.extent(SSM_V_GDELTA) * es, "gdelta"}, {g->gx, p.v.extent(SSM_V_GX) * es, "gx"},
+            {g->gA, (size_t)p.D * p.N * 4, "gA"},
+            {g->gBm, gbc * es, "gBm"}, {g->ga, BDL * p.N * (p.mode == SSM_COMPLEX_DENSE ? 8 : 4), "ga"},
             {g->gb, BDL * p.N * 4, "gb"},
-            {g->gC, BLN * es, "gC"}, {g->gu, BDL * p.N * 2 * es, "gu"}, {g->gr, BDL * es, "gr"},
+            {g->gC, gbc * es, "gC"}, {g->gu, BDL * p.N * 2 * es, "gu"}, {g->gr, BDL * es, "gr"},
             {g->gphi, BDL * es, "gphi"}, {g->glam, (size_t)p.D * p.N * 4, "glam"},
             {g->gtheta, (size_t)p.D * p.N * 4, "gtheta"}, {g->gc, (size_t)p.D * p.N * 8, "gc"},
             {g->gh0, hb, "gh0"}, {g->gdelta_bias, (size_t)p.D * 4, "gdelta_bias"}};
@@ -458,14 +610,15 @@ int scan_bwd_impl(const ssm_scan_args* a, const ssm_scan_bwd_in* in, const ssm_s
     }
     Carve cv(nullptr);
     if (p.mode == SSM_REAL_SELECTIVE) {
-        // workspace is sized for the worst case (checkpoints recomputed, every gradient wanted)
+        // workspace is sized for the worst case (checkpoints recomputed, every gradient wanted);
+        // per-channel Bm, C have per-channel gradients: no channel-block partials
         SelBwdLayout sizing;
-        sel_bwd_layout(p, false, true, true, true, true, cv, &sizing);
+        sel_bwd_layout(p, false, !p.perd, !p.perd, true, true, cv, &sizing);
         if (need_only) { *need_only = cv.off; return ok(); }
         if ((rc = check_ws(ws, ws_bytes, cv.off))) return rc;
         Carve real(ws);
         SelBwdLayout lay;  // only the buffers this call needs are non-null
-        sel_bwd_layout(p, have_ckpt, g->gBm != nullptr, g->gC != nullptr, g->gA != nullptr,
+        sel_bwd_layout(p, have_ckpt, g->gBm != nullptr && !p.perd, g->gC != nullptr && !p.perd, g->gA != nullptr,
                        g->gdelta_bias != nullptr, real, &lay);
         const float* ckpt = in->ckpt;
         if (!have_ckpt) {
@@ -480,9 +633,17 @@ int scan_bwd_impl(const ssm_scan_args* a, const ssm_scan_bwd_in* in, const ssm_s
         q.segQ = lay.segQ; q.segR = lay.segR;
         q.B = (int)p.B; q.D = (int)p.D; q.L = (int)p.L; q.N = (int)p.N;
         q.ntiles = p.nchunks; q.tiles_per_seg = lay.tps; q.G = lay.G;
-        q.vec = sel_vec(p, {a->delta, a->x, in->gy, g->gdelta, g->gx});
+        q.vec = sel_vec(p, {a->delta, a->x, in->gy, g->gdelta, g->gx},
+                        {SSM_V_DELTA, SSM_V_X, SSM_V_GY, SSM_V_GDELTA, SSM_V_GX});
         q.stepf = StepXform{a->delta_bias, a->delta_softplus};
         q.partBias = lay.partBias;
+        copy_strides(q.sdelta, p, SSM_V_DELTA); copy_strides(q.sx, p, SSM_V_X); copy_strides(q.sgy, p, SSM_V_GY);
+        copy_strides(q.sgx, p, SSM_V_GX); copy_strides(q.sgdelta, p, SSM_V_GDELTA);
+        copy_strides(q.sBm, p, SSM_V_BM); copy_strides(q.sC, p, SSM_V_C);
+        q.sA = p.v.s[SSM_V_A][0];
+        q.bc_vec = sel_bc_vec(p, a->Bm, a->C);
+        q.var = sel_var(p);
+        if (p.perd) { q.gBm_pd = g->gBm; q.gC_pd = g->gC; }
         if (lay.G > 1) {
             SSM_LAUNCH(launch_sel_bwd(q, p.dtype, p.kpl, true, st), "selective backward summary");
             SSM_LAUNCH(launch_seg_combine_rev(lay.segQ, lay.segR, in->gh_last, lay.nu, (int)(p.B * p.D), lay.G,
@@ -490,7 +651,7 @@ int scan_bwd_impl(const ssm_scan_args* a, const ssm_scan_bwd_in* in, const ssm_s
         }
         SSM_LAUNCH(launch_sel_bwd(q, p.dtype, p.kpl, false, st), "selective backward");
         const int nblk = (int)cdiv(p.D, sel_bwd_rows());
-        if (g->gBm || g->gC)
+        if ((g->gBm || g->gC) && !p.perd)
             SSM_LAUNCH(launch_reduce_parts_btn(g->gBm ? lay.partB : nullptr, g->gC ? lay.partC : nullptr, nblk,
                                                (int)p.B, (int)p.N, (int)p.L, g->gBm, g->gC, p.dtype, st),
                        "reduce gB gC");
@@ -526,7 +687,7 @@ int scan_bwd_impl(const ssm_scan_args* a, const ssm_scan_bwd_in* in, const ssm_s
 int impulse_impl(const ssm_scan_args* a, int64_t t_out, void* y, void* s, void* s_delta, bool with_delta,
                  void* ws, size_t ws_bytes, hipStream_t st, size_t* need_only) {
     ScanPlan p;
-    int rc = validate_scan_args(a, &p);
+    int rc = validate_scan_args(a, &p, 256, E_SENS);
     if (rc) return rc;
     const char* name = with_delta ? "ssm_output_sensitivity" : "ssm_impulse_sensitivity";
     if (p.mode != SSM_REAL_SELECTIVE) return fail(SSM_ERR_UNSUPPORTED, "%s supports SSM_REAL_SELECTIVE only", name);
@@ -566,19 +727,24 @@ int impulse_impl(const ssm_scan_args* a, int64_t t_out, void* y, void* s, void* 
     if (y || with_delta) {
         if ((rc = run_sel_fwd(a, p, lay, y, nullptr, ckpt, tsum, st))) return rc;
     } else {
-        SSM_LAUNCH(launch_tile_dsum(a->delta, StepXform{a->delta_bias, a->delta_softplus}, tsum, (int)p.B,
-                                    (int)p.D, (int)p.L, p.nchunks, p.kpl, p.dtype, st),
+        SSM_LAUNCH(launch_tile_dsum(a->delta, p.v.s[SSM_V_DELTA][0], p.v.s[SSM_V_DELTA][1],
+                                    StepXform{a->delta_bias, a->delta_softplus}, tsum, (int)p.B, (int)p.D, (int)p.L,
+                                    p.nchunks, p.kpl, p.dtype, st),
                    "tile sums");
     }
-    SSM_LAUNCH(launch_sens_suffix(a->delta, StepXform{a->delta_bias, a->delta_softplus}, tsum, send, (int)p.B,
-                                  (int)p.D, (int)p.L, p.nchunks, p.T, (int)t_out,
-                                  p.dtype, st), "suffix sums");
+    SSM_LAUNCH(launch_sens_suffix(a->delta, p.v.s[SSM_V_DELTA][0], p.v.s[SSM_V_DELTA][1],
+                                  StepXform{a->delta_bias, a->delta_softplus}, tsum, send, (int)p.B, (int)p.D, (int)p.L,
+                                  p.nchunks, p.T, (int)t_out, p.dtype, st),
+               "suffix sums");
     SensParams q{};
     q.delta = a->delta; q.A = a->A; q.Bm = a->Bm; q.C = a->C; q.send = send; q.s = s;
     q.x = a->x; q.ckpt = ckpt; q.s_delta = with_delta ? s_delta : nullptr;
     q.stepf = StepXform{a->delta_bias, a->delta_softplus};
     q.B = (int)p.B; q.D = (int)p.D; q.L = (int)p.L; q.N = (int)p.N; q.ntiles = p.nchunks; q.t_out = (int)t_out;
     q.vec = sel_vec(p, {a->delta, s, a->x, s_delta});
+    copy_strides(q.sdelta, p, SSM_V_DELTA); copy_strides(q.sx, p, SSM_V_X);
+    copy_strides(q.sBm, p, SSM_V_BM); copy_strides(q.sC, p, SSM_V_C);
+    q.sA = p.v.s[SSM_V_A][0];
     SSM_LAUNCH(launch_sens(q, p.dtype, p.kpl, st), "sensitivity");
     return ok();
 }
@@ -589,7 +755,7 @@ int impulse_impl(const ssm_scan_args* a, int64_t t_out, void* y, void* s, void* 
 int sens_rows_impl(const ssm_scan_args* a, int64_t t0, int32_t rows, void* s, void* ws, size_t ws_bytes,
                    hipStream_t st, size_t* need_only) {
     ScanPlan p;
-    int rc = validate_scan_args(a, &p, 64);
+    int rc = validate_scan_args(a, &p, 64, E_SENS);
     if (rc) return rc;
     if (p.mode != SSM_REAL_SELECTIVE)
         return fail(SSM_ERR_UNSUPPORTED, "ssm_sensitivity_rows supports SSM_REAL_SELECTIVE only");
@@ -627,14 +793,20 @@ int sens_rows_impl(const ssm_scan_args* a, int64_t t0, int32_t rows, void* s, vo
     Carve real(ws);
     layout(real, &tsum, &send, &w);
     const StepXform sx{a->delta_bias, a->delta_softplus};
-    SSM_LAUNCH(launch_tile_dsum(a->delta, sx, tsum, (int)p.B, (int)p.D, (int)p.L, p.nchunks, p.kpl, p.dtype, st),
+    const int64_t sdb = p.v.s[SSM_V_DELTA][0], sdd = p.v.s[SSM_V_DELTA][1];
+    SSM_LAUNCH(launch_tile_dsum(a->delta, sdb, sdd, sx, tsum, (int)p.B, (int)p.D, (int)p.L, p.nchunks, p.kpl, p.dtype,
+                                st),
                "tile sums");
-    SSM_LAUNCH(launch_sens_suffix(a->delta, sx, tsum, send, (int)p.B, (int)p.D, (int)p.L, p.nchunks, p.T, (int)t0,
-                                  p.dtype, st), "suffix sums");
+    SSM_LAUNCH(launch_sens_suffix(a->delta, sdb, sdd, sx, tsum, send, (int)p.B, (int)p.D, (int)p.L, p.nchunks, p.T,
+                                  (int)t0, p.dtype, st),
+               "suffix sums");
     SensRowsParams q{};
     q.delta = a->delta; q.A = a->A; q.Bm = a->Bm; q.C = a->C; q.send = send; q.w = w; q.s = s; q.stepf = sx;
     q.B = (int)p.B; q.D = (int)p.D; q.L = (int)p.L; q.N = (int)p.N; q.ntiles = p.nchunks; q.t0 = (int)t0; q.R = R;
     q.vec = sel_vec(p, {s});
+    copy_strides(q.sdelta, p, SSM_V_DELTA); copy_strides(q.sBm, p, SSM_V_BM); copy_strides(q.sC, p, SSM_V_C);
+    q.sA = p.v.s[SSM_V_A][0];
+    q.bc_vec = sel_bc_vec(p, a->Bm, a->C);
     SSM_LAUNCH(launch_sens_rows_edge(q, false, p.dtype, st), "sensitivity rows (weights)");
     SSM_LAUNCH(launch_sens_rows(q, p.dtype, st), "sensitivity rows");
     SSM_LAUNCH(launch_sens_rows_edge(q, true, p.dtype, st), "sensitivity rows (tail)");

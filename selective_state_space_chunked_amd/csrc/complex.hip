@@ -162,18 +162,20 @@ template <> struct CPair<bf16_t> {
     }
 };
 
+// K steps of mode mc from t0 of a (step, mode) slice whose steps are sl
+// complex elements apart (modes contiguous)
 template <typename T, int K>
-__device__ __forceinline__ void load_u(const T* __restrict__ urow, int t0, int L, int M, int mc, bool act,
+__device__ __forceinline__ void load_u(const T* __restrict__ urow, int t0, int L, int64_t sl, int mc, bool act,
                                        float2 (&v)[K]) {
     using V = typename CPair<T>::V;
-    const V* __restrict__ q = reinterpret_cast<const V*>(urow) + (size_t)t0 * M + mc;
+    const V* __restrict__ q = reinterpret_cast<const V*>(urow) + (int64_t)t0 * sl + mc;
     if (t0 + K <= L) {
 #pragma unroll
-        for (int j = 0; j < K; ++j) v[j] = CPair<T>::widen(q[(size_t)j * M]);
+        for (int j = 0; j < K; ++j) v[j] = CPair<T>::widen(q[(int64_t)j * sl]);
     } else {
 #pragma unroll
         for (int j = 0; j < K; ++j)
-            v[j] = t0 + j < L ? CPair<T>::widen(q[(size_t)j * M]) : make_float2(0.0f, 0.0f);
+            v[j] = t0 + j < L ? CPair<T>::widen(q[(int64_t)j * sl]) : make_float2(0.0f, 0.0f);
     }
     if (!act) {
 #pragma unroll
@@ -209,10 +211,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void c
     CUnit u;
     if (!cunit(p, u)) return;
     const int L = p.L, M = p.M;
-    const size_t pm = (size_t)u.hh * M + u.mc;
-    const double lnl = DENSE ? 0.0 : log((double)p.lam[pm]);
-    const float th = DENSE ? 0.0f : p.theta[pm];
-    const double c_re = p.c[2 * pm], c_im = p.c[2 * pm + 1];
+    const double lnl = DENSE ? 0.0 : log((double)p.lam[(int64_t)u.hh * p.slam + u.mc]);
+    const float th = DENSE ? 0.0f : p.theta[(int64_t)u.hh * p.stheta + u.mc];
+    const int64_t pc = (int64_t)u.hh * p.sc + u.mc;
+    const double c_re = p.c[2 * pc], c_im = p.c[2 * pc + 1];
     const float thmax = DENSE ? 0.0f : wave_absmax(th);
     const size_t us = ((size_t)u.s * p.G + u.g) * M + u.mc;  // (B*H, G, M)
     cd h = {0.0, 0.0}, P = {1.0, 0.0};
@@ -223,8 +225,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void c
     }
     const int c0 = u.g * p.chunks_per_seg;
     const int c1 = min(c0 + p.chunks_per_seg, p.nchunks);
-    const T* urow = (const T*)p.u + (size_t)u.s * L * M * 2;
+    const T* urow = (const T*)p.u + 2 * ((int64_t)u.b * p.su[0] + (int64_t)u.hh * p.su[1]);
     const T* arow = DENSE ? (const T*)p.a + (size_t)u.s * L * M * 2 : nullptr;
+    const T* rrow = (const T*)p.r + ((int64_t)u.b * p.sr[0] + (int64_t)u.hh * p.sr[1]);
+    const T* prow = (const T*)p.phi + ((int64_t)u.b * p.sphi[0] + (int64_t)u.hh * p.sphi[1]);
     for (int ch = c0; ch < c1; ++ch) {
         const int t0 = ch * kCChunk;
         if (!SUMMARY && p.ckpt_out && u.act) {
@@ -234,15 +238,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void c
         }
         const int tl = t0 + (u.m & 31);
         const bool tv = tl < L;
-        const float rv = (tv && !DENSE) ? to_f32(((const T*)p.r)[(size_t)u.s * L + tl]) : 0.0f;
-        const float pv = (tv && !DENSE) ? to_f32(((const T*)p.phi)[(size_t)u.s * L + tl]) : 0.0f;
+        const float rv = (tv && !DENSE) ? to_f32(rrow[tl]) : 0.0f;
+        const float pv = (tv && !DENSE) ? to_f32(prow[tl]) : 0.0f;
         float yp[kCChunk];
         auto body = [&](auto fastc, auto fullc) {
             constexpr bool FAST = decltype(fastc)::value, FULL = decltype(fullc)::value;
 #pragma unroll
             for (int hb = 0; hb < kCChunk / 16; ++hb) {
                 float2 uv[16], av[16];
-                load_u<T, 16>(urow, t0 + 16 * hb, L, M, u.mc, u.act, uv);
+                load_u<T, 16>(urow, t0 + 16 * hb, L, p.su[2], u.mc, u.act, uv);
                 if (DENSE) load_u<T, 16>(arow, t0 + 16 * hb, L, M, u.mc, u.act, av);
 #pragma unroll
                 for (int jj = 0; jj < 16; ++jj) {
@@ -298,10 +302,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
     CUnit u;
     if (!cunit(p, u)) return;
     const int L = p.L, M = p.M;
-    const size_t pm = (size_t)u.hh * M + u.mc;
-    const double lnl = DENSE ? 0.0 : log((double)p.lam[pm]);
-    const float th = DENSE ? 0.0f : p.theta[pm];
-    const double cjr = p.c[2 * pm], cji = -(double)p.c[2 * pm + 1];  // conj(c)
+    const double lnl = DENSE ? 0.0 : log((double)p.lam[(int64_t)u.hh * p.slam + u.mc]);
+    const float th = DENSE ? 0.0f : p.theta[(int64_t)u.hh * p.stheta + u.mc];
+    const int64_t pc = (int64_t)u.hh * p.sc + u.mc;
+    const double cjr = p.c[2 * pc], cji = -(double)p.c[2 * pc + 1];  // conj(c)
     const float thmax = DENSE ? 0.0f : wave_absmax(th);
     const size_t us = ((size_t)u.s * p.G + u.g) * M + u.mc;
     cd nu = {0.0, 0.0}, Q = {1.0, 0.0};
@@ -313,14 +317,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
     double gl = 0.0, gt = 0.0, gcr = 0.0, gci = 0.0;
     const int c0 = u.g * p.chunks_per_seg;
     const int c1 = min(c0 + p.chunks_per_seg, p.nchunks);
-    const T* urow = (const T*)p.u + (size_t)u.s * L * M * 2;
+    const T* urow = (const T*)p.u + 2 * ((int64_t)u.b * p.su[0] + (int64_t)u.hh * p.su[1]);
     const T* arow = DENSE ? (const T*)p.a + (size_t)u.s * L * M * 2 : nullptr;
+    const T* rrow = (const T*)p.r + ((int64_t)u.b * p.sr[0] + (int64_t)u.hh * p.sr[1]);
+    const T* prow = (const T*)p.phi + ((int64_t)u.b * p.sphi[0] + (int64_t)u.hh * p.sphi[1]);
     for (int ch = c1 - 1; ch >= c0; --ch) {
         const int t0 = ch * kCChunk;
         const int tl = t0 + (u.m & 31);
         const bool tv = tl < L;
-        const float rv = (tv && !DENSE) ? to_f32(((const T*)p.r)[(size_t)u.s * L + tl]) : 0.0f;
-        const float pv = (tv && !DENSE) ? to_f32(((const T*)p.phi)[(size_t)u.s * L + tl]) : 0.0f;
+        const float rv = (tv && !DENSE) ? to_f32(rrow[tl]) : 0.0f;
+        const float pv = (tv && !DENSE) ? to_f32(prow[tl]) : 0.0f;
         const float gv = tv ? to_f32(((const T*)p.gy)[(size_t)u.s * L + tl]) : 0.0f;
         auto body = [&](auto fastc, auto fullc) {
         constexpr bool FAST = decltype(fastc)::value, FULL = decltype(fullc)::value;
@@ -355,7 +361,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
 #pragma unroll
         for (int hb = 0; hb < kCChunk / 16; ++hb) {
             float2 uv[16], av[16];
-            load_u<T, 16>(urow, t0 + 16 * hb, L, M, u.mc, u.act, uv);
+            load_u<T, 16>(urow, t0 + 16 * hb, L, p.su[2], u.mc, u.act, uv);
             if (DENSE) load_u<T, 16>(arow, t0 + 16 * hb, L, M, u.mc, u.act, av);
 #pragma unroll
             for (int jj = 0; jj < 16; ++jj) {
@@ -546,7 +552,7 @@ __global__ __launch_bounds__(256) void cplx_reduce_kernel(CplxParams p, float* g
     cr = wave_sum_f64(cr);
     ci = wave_sum_f64(ci);
     if (lane != 0) return;
-    if (glam) glam[i] = (float)(sl / (double)p.lam[i]);  // d/d lambda = (d/d ln lambda) / lambda
+    if (glam) glam[i] = (float)(sl / (double)p.lam[(int64_t)(i / p.M) * p.slam + i % p.M]);  // d/d ln lambda / lambda
     if (gtheta) gtheta[i] = (float)st;
     if (gc) {
         gc[2 * i] = (float)cr;
@@ -581,11 +587,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
     const bool act = m < p.M;
     const int mc = act ? m : p.M - 1;
     const int L = p.L, M = p.M;
-    const size_t pm = (size_t)hh * M + mc;
-    const double lamd = p.lam[pm];
+    const double lamd = p.lam[(int64_t)hh * p.slam + mc];
     const double lnl = log(lamd), ilam = 1.0 / lamd;
-    const float th = p.theta[pm];
-    const double c_re = p.c[2 * pm], c_im = p.c[2 * pm + 1];
+    const float th = p.theta[(int64_t)hh * p.stheta + mc];
+    const int64_t pc = (int64_t)hh * p.sc + mc;
+    const double c_re = p.c[2 * pc], c_im = p.c[2 * pc + 1];
     const float thmax = wave_absmax(th);
     const size_t us = ((size_t)s * p.G + g) * M + mc;   // (B*H, G, M)
     cd h = {0.0, 0.0}, sl = {0.0, 0.0}, stt = {0.0, 0.0}, P = {1.0, 0.0};
@@ -603,13 +609,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
     }
     const int c0 = g * p.chunks_per_seg;
     const int c1 = min(c0 + p.chunks_per_seg, p.nchunks);
-    const T* urow = (const T*)p.u + (size_t)s * L * M * 2;
+    const T* urow = (const T*)p.u + 2 * ((int64_t)b * p.su[0] + (int64_t)hh * p.su[1]);
+    const T* rrow = (const T*)p.r + ((int64_t)b * p.sr[0] + (int64_t)hh * p.sr[1]);
+    const T* prow = (const T*)p.phi + ((int64_t)b * p.sphi[0] + (int64_t)hh * p.sphi[1]);
     for (int ch = c0; ch < c1; ++ch) {
         const int t0 = ch * kCChunk;
         const int tl = t0 + (m & 31);
         const bool tv = tl < L;
-        const float rv = tv ? to_f32(((const T*)p.r)[(size_t)s * L + tl]) : 0.0f;
-        const float pv = tv ? to_f32(((const T*)p.phi)[(size_t)s * L + tl]) : 0.0f;
+        const float rv = tv ? to_f32(rrow[tl]) : 0.0f;
+        const float pv = tv ? to_f32(prow[tl]) : 0.0f;
         const float gv = (!SUMMARY && tv) ? to_f32(((const T*)p.gy)[(size_t)s * L + tl]) : 0.0f;
         float yp[kCChunk];
         cplx_chunk(pv, thmax, t0 + kCChunk <= L, [&](auto fastc, auto fullc) {
@@ -617,7 +625,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
 #pragma unroll
             for (int hb = 0; hb < kCChunk / 16; ++hb) {
                 float2 uv[16];
-                load_u<T, 16>(urow, t0 + 16 * hb, L, M, mc, act, uv);
+                load_u<T, 16>(urow, t0 + 16 * hb, L, p.su[2], mc, act, uv);
 #pragma unroll
                 for (int jj = 0; jj < 16; ++jj) {
                     const int j = 16 * hb + jj;
@@ -680,7 +688,7 @@ __global__ __launch_bounds__(256) void cplx_rtrl_combine_kernel(RtrlParams p) {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= p.B * p.H * p.M) return;
     const int s = i / p.M, m = i - s * p.M;
-    const double ilam = 1.0 / (double)p.lam[(size_t)(s % p.H) * p.M + m];
+    const double ilam = 1.0 / (double)p.lam[(int64_t)(s % p.H) * p.slam + m];
     const size_t n3 = (size_t)p.B * p.H * p.G * p.M;
     cd h = {0.0, 0.0}, sl = {0.0, 0.0}, stt = {0.0, 0.0};
     if (p.h0) h = {p.h0[2 * (size_t)i], p.h0[2 * (size_t)i + 1]};

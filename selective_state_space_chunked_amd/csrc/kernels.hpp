@@ -14,8 +14,20 @@ struct StepXform {
     const float* bias;  // (D) or null
     int softplus;
 };
+// Selective kernel variants: input term and where B_t, C_t come from.
+constexpr int kVarEuler = 0;   // Euler input term, B_t / C_t shared by the channels (LDS tiles)
+constexpr int kVarPerD = 1;    // Euler input term, B_t / C_t per channel (read by each row)
+constexpr int kVarZoh = 2;     // zero-order-hold input term, B_t / C_t shared by the channels
+
+// Strides of the selective mode's streamed views, in elements: (B,D,L)
+// streams s[0] batch, s[1] channel (steps contiguous); B_t, C_t (B,D,L,N)
+// s[0] batch, s[1] channel (0 = shared by the channels), s[2] step; A (D,N)
+// channel stride sA.
 struct SelFwdParams {
     const void* delta; const void* x; const float* A; const void* Bm; const void* C;
+    int64_t sdelta[2], sx[2], sy[2], sBm[3], sC[3], sA;
+    int bc_vec;             // 16-byte loads of the B_t / C_t rows (aligned)
+    int var;                // kernel variant: 0 Euler, 1 per-channel B_t / C_t, 2 ZOH
     const float* h0;        // (B,D,N) or null
     const float* carry_in;  // (B,D,G,N) state entering each segment (G > 1)
     void* y;                // (B,D,L) or null
@@ -30,6 +42,10 @@ struct SelFwdParams {
 struct SelBwdParams {
     const void* delta; const void* x; const float* A; const void* Bm; const void* C;
     const void* gy; const float* gh_last; const float* ckpt;
+    int64_t sdelta[2], sx[2], sgy[2], sgx[2], sgdelta[2], sBm[3], sC[3], sA;
+    int bc_vec;
+    int var;
+    void* gBm_pd; void* gC_pd;   // per-channel B_t, C_t: their gradients (B,D,L,N), written directly
     const float* nu_in;     // (B,D,G,N) adjoint entering each segment from the right (G > 1)
     void* gdelta; void* gx; float* gh0;
     float* partB; float* partC;  // (nblk,B,N,L) partial sums over each block of channels
@@ -41,6 +57,7 @@ struct SelBwdParams {
 };
 struct SensParams {
     const void* delta; const float* A; const void* Bm; const void* C;
+    int64_t sdelta[2], sx[2], sBm[3], sC[3], sA;   // views, as in SelFwdParams (B_t, C_t shared)
     const double* send;     // (B,D,ntiles) sum of delta over later steps up to t_out
     void* s;                // nullable d y[t_out] / d x
     const void* x; const float* ckpt;   // with s_delta: inputs and the states entering each tile
@@ -54,6 +71,8 @@ struct SensParams {
 constexpr int kSensRowsMax = 16;
 struct SensRowsParams {
     const void* delta; const float* A; const void* Bm; const void* C;
+    int64_t sdelta[2], sBm[3], sC[3], sA;
+    int bc_vec;
     const double* send;     // (B,D,ntiles) sum of delta over later steps up to t0 (64-step tiles)
     float* w;               // (B,D,R,N) C_{t0+r}[n] * prod_{t0 < s <= t0+r} a_s[n]
     void* s;                // (R,B,D,L)
@@ -68,6 +87,11 @@ hipError_t launch_zero_bytes(void* dst, size_t bytes, hipStream_t st);  // bytes
 
 hipError_t launch_sel_fwd(const SelFwdParams& p, int dtype, int kpl, bool summary, hipStream_t st);
 hipError_t launch_sel_bwd(const SelBwdParams& p, int dtype, int kpl, bool summary, hipStream_t st);
+// the variants (selective_perd.hip, selective_zoh.hip)
+hipError_t launch_sel_fwd_perd(const SelFwdParams& p, int dtype, int kpl, bool summary, hipStream_t st);
+hipError_t launch_sel_bwd_perd(const SelBwdParams& p, int dtype, int kpl, bool summary, hipStream_t st);
+hipError_t launch_sel_fwd_zoh(const SelFwdParams& p, int dtype, int kpl, bool summary, hipStream_t st);
+hipError_t launch_sel_bwd_zoh(const SelBwdParams& p, int dtype, int kpl, bool summary, hipStream_t st);
 int sel_bwd_rows();  // channels per backward workgroup (one gB/gC partial per block)
 hipError_t launch_seg_combine_fwd(const float* P, const float* S, const float* h0, float* carry_in,
                                   int BD, int G, int N, hipStream_t st);
@@ -77,10 +101,11 @@ hipError_t launch_seg_combine_rev(const float* Q, const float* R, const float* n
 hipError_t launch_reduce_parts_btn(const float* partB, const float* partC, int nblk, int B, int N, int L,
                                    void* outB, void* outC, int dtype, hipStream_t st);
 hipError_t launch_reduce_parts_dn(const float* part, int B, int G, int D, int N, float* out, hipStream_t st);
-hipError_t launch_sens_suffix(const void* delta, StepXform stepf, const float* tile_dsum, double* send, int B, int D,
-                              int L, int ntiles, int tile_len, int t_out, int dtype, hipStream_t st);
-hipError_t launch_tile_dsum(const void* delta, StepXform stepf, float* tile_dsum, int B, int D, int L, int ntiles,
-                            int kpl, int dtype, hipStream_t st);
+hipError_t launch_sens_suffix(const void* delta, int64_t sdb, int64_t sdd, StepXform stepf, const float* tile_dsum,
+                              double* send, int B, int D, int L, int ntiles, int tile_len, int t_out, int dtype,
+                              hipStream_t st);
+hipError_t launch_tile_dsum(const void* delta, int64_t sdb, int64_t sdd, StepXform stepf, float* tile_dsum, int B,
+                            int D, int L, int ntiles, int kpl, int dtype, hipStream_t st);
 hipError_t launch_sens(const SensParams& p, int dtype, int kpl, hipStream_t st);
 // rows of the input Jacobian: the weights (tail = false) before the main pass,
 // the steps in (t0, t0 + R) (tail = true) after it
@@ -119,6 +144,9 @@ struct CplxParams {
     // given transitions (SSM_COMPLEX_DENSE): a (B,H,L,M) complex64 replaces r, phi, lam,
     // theta; ga (B,H,L,M) complex64 replaces gr, gphi, glam, gtheta
     const float* a; float* ga;
+    // views: r, phi (b, h) rows at b * s[0] + h * s[1]; u (b, h, t) at su[0..2] (complex
+    // elements); lam, theta, c per head at h * s (0 = shared by the heads)
+    int64_t sr[2], sphi[2], su[3], slam, stheta, sc;
     int B, H, L, M, nchunks, chunk, chunks_per_seg, G;
     int dtype;
 };
@@ -138,6 +166,7 @@ struct RtrlParams {
     double* segRP;   // (B,H,G) x (sum r, sum phi)
     double* carry;   // 3 planes (h, sl, st) of (B,H,G,M) complex entering each segment
     double* partL; double* partT;   // (B,G,H,M)
+    int64_t sr[2], sphi[2], su[3], slam, stheta, sc;   // views, as in CplxParams
     int B, H, L, M, nchunks, chunks_per_seg, G;
     int dtype;
 };
@@ -165,6 +194,9 @@ struct PDParams {
     const void* ste_logits;        // selection scores for the surrogate gradient (B,H,L,K)
     void* glogits;                 // (B,H,L,K) surrogate gradient; NULL = not wanted
     float inv_tau;                 // 1 / softmax temperature
+    // views: d, b, C, logits rows (b, h) at b * s[0] + h * s[1], steps s[2] apart;
+    // dictionary entry (h, k) at h * sdict[0] + k * sdict[1] (0 = shared by the heads)
+    int64_t s_d[3], s_b[3], s_C[3], s_lg[3], sdict[2];
     int B, H, L, N, K, chunk, G;   // G = number of chunks
     int dtype;                     // 0 fp32, 1 bf16 streams
 };

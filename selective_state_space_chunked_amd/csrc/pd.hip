@@ -39,12 +39,12 @@ __device__ __forceinline__ int row_pull_i(int v, int src) {
 
 // preimage lists: pre[(h*K+k)*N*N + i*N + r] = r-th column j (ascending) with
 // dict[h,k,j] == i, padded with 0; cnt[(h*K+k)*N + i] = number of such columns.
-__global__ void pd_prep_kernel(const int32_t* __restrict__ dict, int8_t* __restrict__ pre,
+__global__ void pd_prep_kernel(const int32_t* __restrict__ dict, int64_t sdh, int64_t sdk, int8_t* __restrict__ pre,
                                int32_t* __restrict__ cnt, int H, int K, int N) {
     const int idx = blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= H * K * N) return;
     const int hk = idx / N, i = idx - hk * N;
-    const int32_t* col = dict + (size_t)hk * N;
+    const int32_t* col = dict + (int64_t)(hk / K) * sdh + (int64_t)(hk % K) * sdk;   // entry k of head h
     int c = 0;
     // entries outside [0, N) are clamped exactly as pd_load_tables clamps them, so the
     // gather lists and the compositions see the same dictionary
@@ -77,7 +77,7 @@ __device__ __forceinline__ void pd_load_tables(const PDParams& p, int hh, PDShar
     int m = 0;
     for (int e = threadIdx.x; e < K * N; e += 256) {
         // entries outside [0, N) are a precondition violation; clamping keeps every access in bounds
-        t.dict[e] = min(max(p.dict[(size_t)hh * K * N + e], 0), N - 1);
+        t.dict[e] = min(max(p.dict[(int64_t)hh * p.sdict[0] + (int64_t)(e / N) * p.sdict[1] + e % N], 0), N - 1);
         const int c = p.pre_cnt[(size_t)hh * K * N + e];
         t.cnt[e] = c;
         m = max(m, c);
@@ -168,17 +168,18 @@ __device__ __forceinline__ PDRow pd_row(const PDParams& p) {
     return r;
 }
 
-// 16 steps tb.. of state i of a (L, N) stream (fp32 or bf16); steps past L read 0.
+// 16 steps tb.. of state i of an (L, N) slice (fp32 or bf16) whose steps are
+// sl elements apart (states contiguous); steps past L read 0.
 template <typename T, int NT>
-__device__ __forceinline__ void pd_load16(const T* __restrict__ base, int tb, int L, int N, int i,
+__device__ __forceinline__ void pd_load16(const T* __restrict__ base, int64_t sl, int tb, int L, int i,
                                           float (&v)[16]) {
-    const T* __restrict__ q = base + (size_t)tb * (NT ? NT : N) + i;
+    const T* __restrict__ q = base + (int64_t)tb * sl + i;
     if (tb + 16 <= L) {
 #pragma unroll
-        for (int j = 0; j < 16; ++j) v[j] = to_f32(q[j * (NT ? NT : N)]);
+        for (int j = 0; j < 16; ++j) v[j] = to_f32(q[(int64_t)j * sl]);
     } else {
 #pragma unroll
-        for (int j = 0; j < 16; ++j) v[j] = tb + j < L ? to_f32(q[j * (NT ? NT : N)]) : 0.0f;
+        for (int j = 0; j < 16; ++j) v[j] = tb + j < L ? to_f32(q[(int64_t)j * sl]) : 0.0f;
     }
 }
 
@@ -208,24 +209,25 @@ __global__ __launch_bounds__(256) void pd_fwd_kernel(PDParams p) {
             if (p.ckpt_out && nl) p.ckpt_out[((size_t)r.s * p.G + r.ch) * N + i] = h;
             if (!nl) h = 0.0f;
         }
-        const T* dbase = (const T*)p.d + srow * N;
-        const T* bbase = (const T*)p.b + srow * N;
-        const T* cbase = (const T*)p.C + srow * N;
+        const T* dbase = (const T*)p.d + ((int64_t)r.b * p.s_d[0] + (int64_t)r.hh * p.s_d[1]);
+        const T* bbase = (const T*)p.b + ((int64_t)r.b * p.s_b[0] + (int64_t)r.hh * p.s_b[1]);
+        const T* cbase = (const T*)p.C + ((int64_t)r.b * p.s_C[0] + (int64_t)r.hh * p.s_C[1]);
+        const T* lbase = p.logits ? (const T*)p.logits + ((int64_t)r.b * p.s_lg[0] + (int64_t)r.hh * p.s_lg[1]) : nullptr;
         const int t0 = r.ch * kPChunk;
         for (int blk = 0; blk < kPChunk / 16; ++blk) {
             const int tb = t0 + 16 * blk;
             const int tl = tb + r.lane;          // the step whose selection this lane loads
             int kl = 0;
             if (tl < L) {
-                if (SUMMARY) kl = p.logits ? pd_argmax((const T*)p.logits + (srow + tl) * K, K) : p.sel_in[srow + tl];
+                if (SUMMARY) kl = lbase ? pd_argmax(lbase + (int64_t)tl * p.s_lg[2], K) : p.sel_in[srow + tl];
                 else kl = p.sel[srow + tl];
                 kl = min(max(kl, 0), K - 1);   // given selections outside [0, K) are clamped
             }
             if (SUMMARY && p.sel_out && tl < L) p.sel_out[srow + tl] = kl;
             float dv[16], bv[16], cv[16];
-            pd_load16<T, NT>(dbase, tb, L, N, i, dv);
-            pd_load16<T, NT>(bbase, tb, L, N, i, bv);
-            if (!SUMMARY) pd_load16<T, NT>(cbase, tb, L, N, i, cv);
+            pd_load16<T, NT>(dbase, p.s_d[2], tb, L, i, dv);
+            pd_load16<T, NT>(bbase, p.s_b[2], tb, L, i, bv);
+            if (!SUMMARY) pd_load16<T, NT>(cbase, p.s_C[2], tb, L, i, cv);
             float yp[16];
     #pragma unroll
             for (int j = 0; j < 16; ++j) {
@@ -384,9 +386,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(STE >= 0 ? 
             if (p.G > 1) nu = p.nu_in[((size_t)r.s * p.G + r.ch) * N + j];
             else if (p.gh_last) nu = p.gh_last[(size_t)r.s * N + j];
         }
-        const T* dbase = (const T*)p.d + srow * N;
-        const T* bbase = (const T*)p.b + srow * N;
-        const T* cbase = (const T*)p.C + srow * N;
+        const T* dbase = (const T*)p.d + ((int64_t)r.b * p.s_d[0] + (int64_t)r.hh * p.s_d[1]);
+        const T* bbase = (const T*)p.b + ((int64_t)r.b * p.s_b[0] + (int64_t)r.hh * p.s_b[1]);
+        const T* cbase = (const T*)p.C + ((int64_t)r.b * p.s_C[0] + (int64_t)r.hh * p.s_C[1]);
         auto sel_of = [&](int tl) { return tl < L ? min(max(p.sel[srow + tl], 0), K - 1) : 0; };
         float hs[kPChunk + 1];
         if (!SUMMARY) {
@@ -396,8 +398,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(STE >= 0 ? 
                 const int tb = t0 + 16 * blk;
                 const int kl = sel_of(tb + r.lane);
                 float dv[16], bv[16];
-                pd_load16<T, NT>(dbase, tb, L, N, j, dv);
-                pd_load16<T, NT>(bbase, tb, L, N, j, bv);
+                pd_load16<T, NT>(dbase, p.s_d[2], tb, L, j, dv);
+                pd_load16<T, NT>(bbase, p.s_b[2], tb, L, j, bv);
     #pragma unroll
                 for (int q = 0; q < 16; ++q) {
                     const int k = __float_as_int(bcast16(__int_as_float(kl), q));
@@ -433,8 +435,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(STE >= 0 ? 
                 }
             }
             float dv[16], cv[16];
-            pd_load16<T, NT>(dbase, tb, L, N, j, dv);
-            pd_load16<T, NT>(cbase, tb, L, N, j, cv);
+            pd_load16<T, NT>(dbase, p.s_d[2], tb, L, j, dv);
+            pd_load16<T, NT>(cbase, p.s_C[2], tb, L, j, cv);
             const size_t obase = (srow + tb) * N + j;   // step q at obase + q * N
     #pragma unroll
             for (int q = 15; q >= 0; --q) {
@@ -612,7 +614,7 @@ hipError_t launch_pd_sel_copy(const int32_t* sel, int32_t* out, size_t n, int K,
 
 hipError_t launch_pd_prep(const PDParams& p, hipStream_t st) {
     const int n = p.H * p.K * p.N;
-    pd_prep_kernel<<<(n + 255) / 256, 256, 0, st>>>(p.dict, p.pre, p.pre_cnt, p.H, p.K, p.N);
+    pd_prep_kernel<<<(n + 255) / 256, 256, 0, st>>>(p.dict, p.sdict[0], p.sdict[1], p.pre, p.pre_cnt, p.H, p.K, p.N);
     return hipGetLastError();
 }
 template <typename T>

@@ -46,10 +46,11 @@ def test_header_constants_match_binding():
 
 def test_struct_layouts():
     # 2 x int32 + 5 x int64 + 14 pointers
-    # + delta_bias pointer + delta_softplus int32 (padded to 8)
-    assert ctypes.sizeof(B.ScanArgs) == 8 + 5 * 8 + 15 * 8 + 8
+    # + delta_bias pointer + delta_softplus, discretization int32 + layout pointer
+    assert ctypes.sizeof(B.ScanArgs) == 8 + 5 * 8 + 15 * 8 + 8 + 8
     assert ctypes.sizeof(B.ScanGrads) == 15 * 8
-    assert ctypes.sizeof(B.PDArgs) == 6 * 8 + 7 * 8 + 8   # + dtype (int32, padded)
+    assert ctypes.sizeof(B.PDArgs) == 6 * 8 + 7 * 8 + 8 + 8   # + dtype (int32, padded) + layout pointer
+    assert ctypes.sizeof(B.Layout) == 8 + 20 * 4 * 8
     assert ctypes.sizeof(B.PDBwdIn) == 4 * 8 + 8   # 4 pointers + float tau (padded)
     assert ctypes.sizeof(B.PDGrads) == 5 * 8
 
@@ -442,3 +443,111 @@ def test_every_forward_fits_the_static_scratch():
             assert rc == 0, (mode, bd)
             worst = max(worst, n)
     assert 0 < worst <= cap
+
+
+# ---------------------------------------------------------------------------
+# strided views (ssm_layout) and the discretisation selector: host-side checks
+# ---------------------------------------------------------------------------
+def _lay(**roles):
+    lay = B.Layout()
+    for role, st in roles.items():
+        r = getattr(B, "V_" + role.upper())
+        lay.given |= 1 << r
+        for i, v in enumerate(st):
+            lay.stride[r][i] = v
+    return lay
+
+
+def _fwd_rc(a, out_y=FAKE * 9):
+    o = B.ScanFwdOut(y=out_y, h_last=None, ckpt=None)
+    return B.lib().ssm_scan_fwd(ctypes.byref(a), ctypes.byref(o), None, 0, None)
+
+
+@pytest.mark.parametrize("roles,code", [
+    (dict(x=(32000, 1000, 2)), "SSM_ERR_LAYOUT"),            # innermost stride must be 1
+    (dict(delta=(-1000, 1000, 1)), "SSM_ERR_LAYOUT"),        # negative stride
+    (dict(y=(32000, 0, 1)), "SSM_ERR_LAYOUT"),               # output with stride 0 (channels alias)
+    (dict(y=(1000, 1000, 1)), "SSM_ERR_LAYOUT"),             # output rows that overlap
+    (dict(gy=(32000, 1000, 1)), "SSM_ERR_UNSUPPORTED"),      # gy is no forward argument
+    (dict(r=(32000, 1000, 1)), "SSM_ERR_UNSUPPORTED"),       # a complex role in the selective mode
+    (dict(dict=(0, 16, 1)), "SSM_ERR_UNSUPPORTED"),          # a PD role in a diagonal scan
+])
+def test_layout_errors(roles, code):
+    a = sel_args()
+    lay = _lay(**roles)
+    a.layout = ctypes.pointer(lay)
+    assert _fwd_rc(a) == status(code), B.lib().ssm_last_error_detail()
+
+
+def test_layout_accepts_views():
+    """Broadcast inputs (stride 0), slices and per-channel B_t, C_t pass validation (sizes only)."""
+    for roles in (dict(delta=(0, 1000, 1), x=(64000, 2000, 1), a=(0, 1)),
+                  dict(bm=(0, 0, 16, 1), c=(0, 0, 16, 1)),
+                  dict(bm=(32 * 16000, 16000, 16, 1), c=(32 * 16000, 16000, 16, 1)),
+                  dict(bm=(16000, 16, 16, 1)),   # per-channel Bm next to a shared C
+                  dict(y=(64000, 2000, 1))):
+        a = sel_args()
+        lay = _lay(**roles)
+        a.layout = ctypes.pointer(lay)
+        rc, n = ws_bytes(B.SSM_OP_SCAN_FWD, a)
+        assert rc == 0, (roles, B.lib().ssm_last_error_detail())
+
+
+def test_perd_and_zoh_limits():
+    """Per-channel B_t, C_t and the ZOH term are scan-only; ZOH is the selective mode's; unknown selector."""
+    perd = _lay(bm=(32 * 16000, 16000, 16, 1), c=(32 * 16000, 16000, 16, 1))
+    a = sel_args()
+    a.layout = ctypes.pointer(perd)
+    rc, _ = ws_bytes(B.SSM_OP_IMPULSE, a)
+    assert rc == status("SSM_ERR_UNSUPPORTED")
+    rc, _ = ws_bytes(B.SSM_OP_SCAN_BWD, a)
+    assert rc == 0
+    a = sel_args(discretization=B.SSM_ZOH)
+    assert ws_bytes(B.SSM_OP_SCAN_FWD, a)[0] == 0
+    assert ws_bytes(B.SSM_OP_SCAN_BWD, a)[0] == 0
+    assert ws_bytes(B.SSM_OP_IMPULSE, a)[0] == status("SSM_ERR_UNSUPPORTED")
+    assert ws_bytes(B.SSM_OP_SENS_ROWS, a)[0] == status("SSM_ERR_UNSUPPORTED")
+    a.layout = ctypes.pointer(perd)
+    assert ws_bytes(B.SSM_OP_SCAN_FWD, a)[0] == status("SSM_ERR_UNSUPPORTED")
+    a = sel_args(discretization=7)
+    assert ws_bytes(B.SSM_OP_SCAN_FWD, a)[0] == status("SSM_ERR_SHAPE")
+    c = sel_args(mode=B.SSM_COMPLEX_SHARED, state=8, u=FAKE * 9, c=FAKE * 10, r=FAKE * 11, phi=FAKE * 12,
+                 lam=FAKE * 13, theta=FAKE * 14, discretization=B.SSM_ZOH)
+    assert ws_bytes(B.SSM_OP_SCAN_FWD, c)[0] == status("SSM_ERR_UNSUPPORTED")
+
+
+def test_pd_layout_checks():
+    shared = _lay(dict=(0, 16, 1), pd_d=(2 * 4 * 500 * 16, 500 * 16, 16, 1))
+    a = pd_args()
+    a.layout = ctypes.pointer(shared)
+    assert ws_bytes_pd(a)[0] == 0
+    bad = _lay(dict=(128, 16, 2))
+    a.layout = ctypes.pointer(bad)
+    assert ws_bytes_pd(a)[0] == status("SSM_ERR_LAYOUT")
+    bad = _lay(x=(1, 1, 1))
+    a.layout = ctypes.pointer(bad)
+    assert ws_bytes_pd(a)[0] == status("SSM_ERR_UNSUPPORTED")
+
+
+def test_binding_passes_views():
+    """The binding takes strided views of its inputs (no copies) and describes them to the library."""
+    import torch
+    t = _cpu_sel(L=40, D=3, N=4)
+    big = torch.randn(2, 6, 40)
+    t["x"] = big[:, ::2]                                  # channel stride 80
+    t["A"] = (-torch.rand(1, 4)).expand(3, 4)             # one A row for every channel
+    args, _, _ = B._scan_args(B.SSM_REAL_SELECTIVE, **t)
+    lay = args.layout.contents
+    assert lay.given == (1 << B.V_X) | (1 << B.V_A)
+    assert list(lay.stride[B.V_X])[:3] == [240, 80, 1]
+    assert list(lay.stride[B.V_A])[:2] == [0, 1]
+    t = _cpu_sel(L=40, D=3, N=4)
+    args, _, _ = B._scan_args(B.SSM_REAL_SELECTIVE, **t)
+    assert not args.layout                                 # dense: no layout at all
+    t["Bm"] = torch.randn(2, 3, 40, 4)
+    t["C"] = torch.randn(2, 40, 4).unsqueeze(1).expand(2, 3, 40, 4)
+    args, _, _ = B._scan_args(B.SSM_REAL_SELECTIVE, **t)
+    lay = args.layout.contents
+    # per-channel Bm is a view; C expanded over the channels is the default shared layout
+    assert args._perd and (lay.given >> B.V_BM) & 1 and not (lay.given >> B.V_C) & 1
+    assert list(lay.stride[B.V_BM]) == [480, 160, 4, 1]
