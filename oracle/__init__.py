@@ -10,7 +10,10 @@ All routines take numpy arrays holding the exact values the GPU consumes
 (float32, bfloat16 bits as uint16, complex64, int32) and widen them to float64
 here; results come back as float64 (int32 for selections).
 
-Pinned by tests/test_oracle_pins.py: general selective scan ``sel_fwd`` / ``sel_bwd``
+Pinned by tests/test_oracle_pins.py: scalar transition per head ``head_fwd`` /
+``head_bwd`` (the quadratic form y_t = sum_s (C_t . B_s) exp(A sum delta) delta_s
+x_s written out as a matrix product, equality with the diagonal scan on expanded
+arrays, finite differences); general selective scan ``sel_fwd`` / ``sel_bwd``
 (zero-order hold: the exact solution of dh/dt = A h + B x for inputs held
 constant, the A = 0 limit equal to the Euler scan, central finite differences;
 per-channel B and C: brute-force O(L^2) sums, equality with the shared form
@@ -63,6 +66,8 @@ def _load():
         lib.orc_real_bwd.argtypes = [ctypes.c_int, _L, _L, _L, _L] + [_D] * 18
         lib.orc_sel_fwd.argtypes = [ctypes.c_int, ctypes.c_int, _L, _L, _L, _L] + [_D] * 8
         lib.orc_sel_bwd.argtypes = [ctypes.c_int, ctypes.c_int, _L, _L, _L, _L] + [_D] * 14
+        lib.orc_head_fwd.argtypes = [_L, _L, _L, _L, _L] + [_D] * 8
+        lib.orc_head_bwd.argtypes = [_L, _L, _L, _L, _L] + [_D] * 14
         lib.orc_impulse_sens.argtypes = [_L, _L, _L, _L, _L] + [_D] * 5
         lib.orc_output_sens.argtypes = [_L, _L, _L, _L, _L] + [_D] * 8
         lib.orc_complex_fwd.argtypes = [_L, _L, _L, _L] + [_D] * 9
@@ -146,6 +151,26 @@ def sel_bwd(*, delta, x, A, Bm, C, h0=None, gy, ghlast=None, disc=0, perd=False,
     out = dict(gdelta=_z((B, D, L)), gx=_z((B, D, L)), gA=_z((D, N)), gBm=_z(gbc), gC=_z(gbc), gh0=_z((B, D, N)))
     _load().orc_sel_bwd(int(disc), int(bool(perd)), B, D, L, N, *[_p(v) for v in args],
                         *[_p(out[k]) for k in ("gdelta", "gx", "gA", "gBm", "gC", "gh0")])
+    return out
+
+
+def head_fwd(*, delta, x, A, Bm, C, h0=None, B, H, P, L, N):
+    """Scalar transition per head: y (B,H*P,L), h_last (B,H*P,N).  delta (B,H,L), x (B,H*P,L), A (H),
+    Bm, C (B,L,N); channel d = h*P + p belongs to head h."""
+    args = [_w(v) for v in (delta, x, A, Bm, C, h0)]
+    y, hl = _z((B, H * P, L)), _z((B, H * P, N))
+    _load().orc_head_fwd(B, H, P, L, N, *[_p(v) for v in args], _p(y), _p(hl))
+    return y, hl
+
+
+def head_bwd(*, delta, x, A, Bm, C, h0=None, gy, ghlast=None, B, H, P, L, N):
+    """Gradients of sum<gy,y> + <ghlast,h_last> of ``head_fwd``: gdelta (B,H,L), gx (B,H*P,L), gA (H),
+    gBm, gC (B,L,N), gh0 (B,H*P,N)."""
+    args = [_w(v) for v in (delta, x, A, Bm, C, h0, gy, ghlast)]
+    out = dict(gdelta=_z((B, H, L)), gx=_z((B, H * P, L)), gA=_z((H,)), gBm=_z((B, L, N)), gC=_z((B, L, N)),
+               gh0=_z((B, H * P, N)))
+    _load().orc_head_bwd(B, H, P, L, N, *[_p(v) for v in args],
+                         *[_p(out[k]) for k in ("gdelta", "gx", "gA", "gBm", "gC", "gh0")])
     return out
 
 

@@ -222,6 +222,126 @@ void orc_sel_bwd(int disc, int perd, i64 B, i64 D, i64 L, i64 N,
 /* Layouts: delta, x, y, gy (B,D,L); A (D,N); Bm, C (B,L,N); a, b (B,D,L,N);  */
 /* h0, hlast (B,D,N).                                                         */
 /* ------------------------------------------------------------------------- */
+/* Selective scan with a scalar transition per head (the S3M page's chunked   */
+/* matrix form applies to it, section 4.1): head h owns channels              */
+/* d = h*P .. h*P+P-1 and one state matrix of P x N; per step                 */
+/*   a_t = exp(delta[b,h,t] * A[h])          (one number per head and step)   */
+/*   h_t[p,n] = a_t h_{t-1}[p,n] + delta[b,h,t] x[b,d,t] B[b,t,n]             */
+/*   y[b,d,t] = sum_n C[b,t,n] h_t[p,n]                                       */
+/* Layouts: delta (B,H,L); x, y, gy (B,D,L); A (H); Bm, C (B,L,N);            */
+/* h0, hlast (B,D,N) with d = h*P + p.                                        */
+/* ------------------------------------------------------------------------- */
+void orc_head_fwd(i64 B, i64 H, i64 P, i64 L, i64 N, const double* delta, const double* x, const double* A,
+                  const double* Bm, const double* C, const double* h0, double* y, double* hlast) {
+    const i64 D = H * P;
+    #pragma omp parallel
+    {
+        double* h = (double*)malloc(sizeof(double) * N);
+        #pragma omp for schedule(static)
+        for (i64 s = 0; s < B * D; ++s) {
+            i64 bi = s / D, di = s % D, hi = di / P;
+            for (i64 n = 0; n < N; ++n) h[n] = h0 ? h0[s * N + n] : 0.0;
+            for (i64 t = 0; t < L; ++t) {
+                double dl = delta[(bi * H + hi) * L + t];
+                double at = exp(dl * A[hi]), u = dl * x[s * L + t], acc = 0.0;
+                for (i64 n = 0; n < N; ++n) {
+                    h[n] = at * h[n] + u * Bm[(bi * L + t) * N + n];
+                    acc += C[(bi * L + t) * N + n] * h[n];
+                }
+                y[s * L + t] = acc;
+            }
+            if (hlast) for (i64 n = 0; n < N; ++n) hlast[s * N + n] = h[n];
+        }
+        free(h);
+    }
+}
+
+/* Gradients of sum <gy,y> + <ghlast,h_last>:
+ *   gdelta[b,h,t] = sum_{p,n} lambda_t (h_{t-1} a_t A[h] + x B_t),  gx = delta sum_n lambda B,
+ *   gA[h] = sum_{b,p,t,n} lambda h_{t-1} a_t delta,  gB, gC (B,L,N) sums over every channel;
+ * sums over channels and batch rows in per-thread partials added in thread order. */
+void orc_head_bwd(i64 B, i64 H, i64 P, i64 L, i64 N, const double* delta, const double* x, const double* A,
+                  const double* Bm, const double* C, const double* h0, const double* gy, const double* ghlast,
+                  double* gdelta, double* gx, double* gA, double* gBm, double* gC, double* gh0) {
+    const i64 D = H * P;
+    int T = nthreads();
+    double* pB = (double*)calloc((size_t)T * L * N, sizeof(double));
+    double* pC = (double*)calloc((size_t)T * L * N, sizeof(double));
+    double* pA = (double*)calloc((size_t)T * H, sizeof(double));
+    double* pD = (double*)calloc((size_t)T * H * L, sizeof(double));
+    for (i64 bi = 0; bi < B; ++bi) {
+        #pragma omp parallel
+        {
+            int tid = thread_id();
+            double* hist = (double*)malloc(sizeof(double) * (L + 1) * N);
+            double* lam = (double*)malloc(sizeof(double) * N);
+            #pragma omp for schedule(static)
+            for (i64 di = 0; di < D; ++di) {
+                i64 s = bi * D + di, hi = di / P;
+                const double* dl = delta + (bi * H + hi) * L;
+                for (i64 n = 0; n < N; ++n) hist[n] = h0 ? h0[s * N + n] : 0.0;
+                for (i64 t = 0; t < L; ++t) {
+                    double at = exp(dl[t] * A[hi]), u = dl[t] * x[s * L + t];
+                    for (i64 n = 0; n < N; ++n)
+                        hist[(t + 1) * N + n] = at * hist[t * N + n] + u * Bm[(bi * L + t) * N + n];
+                }
+                for (i64 n = 0; n < N; ++n) lam[n] = ghlast ? ghlast[s * N + n] : 0.0;
+                for (i64 t = L - 1; t >= 0; --t) {
+                    double g = gy[s * L + t], at = exp(dl[t] * A[hi]), xv = x[s * L + t];
+                    double dsum = 0.0, xsum = 0.0, asum = 0.0;
+                    for (i64 n = 0; n < N; ++n) {
+                        i64 o = (bi * L + t) * N + n;
+                        lam[n] += C[o] * g;
+                        pC[(size_t)tid * L * N + t * N + n] += g * hist[(t + 1) * N + n];
+                        pB[(size_t)tid * L * N + t * N + n] += lam[n] * dl[t] * xv;
+                        double q = lam[n] * hist[t * N + n] * at;   /* lambda h_{t-1} a_t */
+                        dsum += q * A[hi] + lam[n] * xv * Bm[o];
+                        xsum += lam[n] * Bm[o];
+                        asum += q * dl[t];
+                        lam[n] *= at;
+                    }
+                    pD[((size_t)tid * H + hi) * L + t] += dsum;
+                    pA[(size_t)tid * H + hi] += asum;
+                    if (gx) gx[s * L + t] = dl[t] * xsum;
+                }
+                if (gh0) for (i64 n = 0; n < N; ++n) gh0[s * N + n] = lam[n];
+            }
+            free(hist);
+            free(lam);
+        }
+        for (i64 o = 0; o < L * N; ++o) {
+            double sb = 0.0, sc = 0.0;
+            for (int k = 0; k < T; ++k) {
+                sb += pB[(size_t)k * L * N + o];
+                sc += pC[(size_t)k * L * N + o];
+                pB[(size_t)k * L * N + o] = 0.0;
+                pC[(size_t)k * L * N + o] = 0.0;
+            }
+            if (gBm) gBm[bi * L * N + o] = sb;
+            if (gC) gC[bi * L * N + o] = sc;
+        }
+        for (i64 o = 0; o < H * L; ++o) {
+            double sd = 0.0;
+            for (int k = 0; k < T; ++k) {
+                sd += pD[(size_t)k * H * L + o];
+                pD[(size_t)k * H * L + o] = 0.0;
+            }
+            if (gdelta) gdelta[bi * H * L + o] = sd;
+        }
+    }
+    if (gA)
+        for (i64 hh = 0; hh < H; ++hh) {
+            double sa = 0.0;
+            for (int k = 0; k < T; ++k) sa += pA[(size_t)k * H + hh];
+            gA[hh] = sa;
+        }
+    free(pB);
+    free(pC);
+    free(pA);
+    free(pD);
+}
+
+/* ------------------------------------------------------------------------- */
 static void real_terms(int mode, i64 D, i64 L, i64 N, i64 bi, i64 di, i64 t,
                        const double* delta, const double* x, const double* A,
                        const double* Bm, const double* a, const double* b,

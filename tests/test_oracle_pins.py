@@ -889,3 +889,70 @@ def test_perd_with_channel_independent_BC_equals_shared(disc):
     close(gq["gC"].sum(axis=1), g["gC"], rtol=1e-11, atol=1e-13)
     for k in ("gdelta", "gx", "gA", "gh0"):
         close(gq[k], g[k], rtol=1e-11, atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# scalar transition per head (the chunked-matrix form's problem)
+# ---------------------------------------------------------------------------
+def small_head(B=2, H=2, P=3, N=4, L=20, seed=0):
+    g = np.random.default_rng(seed)
+    return dict(delta=np.log1p(np.exp(g.standard_normal((B, H, L)))), x=g.standard_normal((B, H * P, L)),
+                A=-np.exp(g.uniform(-3, 0, H)), Bm=g.standard_normal((B, L, N)) / 2, C=g.standard_normal((B, L, N)) / 2,
+                h0=g.standard_normal((B, H * P, N)), gy=g.standard_normal((B, H * P, L)),
+                ghlast=g.standard_normal((B, H * P, N)), B=B, H=H, P=P, N=N, L=L)
+
+
+def _head_kw(p):
+    return {k: p[k] for k in ("delta", "x", "A", "Bm", "C", "h0", "B", "H", "P", "L", "N")}
+
+
+def test_head_quadratic_form():
+    """y = (L o C B^T) (delta x) + decayed h0: the masked-matrix (quadratic) form of the scan written out with
+    numpy matrix products, Lmat[t, s] = exp(A (S_t - S_s)) for s <= t with S the prefix sums of delta."""
+    p = small_head(B=2, H=2, P=3, N=4, L=24, seed=61)
+    y, _ = oracle.head_fwd(**_head_kw(p))
+    for b in range(2):
+        G = p["C"][b] @ p["Bm"][b].T                       # (L, L): C_t . B_s
+        for h in range(2):
+            S = np.cumsum(p["delta"][b, h])
+            Lm = np.tril(np.exp(p["A"][h] * (S[:, None] - S[None, :])))
+            for q in range(3):
+                d = h * 3 + q
+                u = p["delta"][b, h] * p["x"][b, d]
+                ref = (Lm * G) @ u + (p["C"][b] @ p["h0"][b, d]) * np.exp(p["A"][h] * S)
+                close(y[b, d], ref, rtol=1e-11, atol=1e-13)
+
+
+def test_head_equals_diagonal_scan():
+    """The scalar-per-head scan is the diagonal selective scan with delta repeated over the head's channels
+    and A[d, n] = A[h] for every state: forward, and the backward with gdelta / gA summed over the head."""
+    p = small_head(B=2, H=3, P=2, N=4, L=30, seed=62)
+    H, P = 3, 2
+    dexp = np.repeat(p["delta"], P, axis=1)
+    Aexp = np.repeat(p["A"], P)[:, None] * np.ones((1, 4))
+    kw = dict(delta=dexp, x=p["x"], A=Aexp, Bm=p["Bm"], C=p["C"], h0=p["h0"], B=2, D=H * P, L=30, N=4)
+    y0, hl0 = oracle.real_fwd(**kw)
+    y, hl = oracle.head_fwd(**_head_kw(p))
+    close(y, y0, rtol=1e-12)
+    close(hl, hl0, rtol=1e-12)
+    g0 = oracle.real_bwd(**kw, gy=p["gy"], ghlast=p["ghlast"])
+    g = oracle.head_bwd(**_head_kw(p), gy=p["gy"], ghlast=p["ghlast"])
+    close(g["gdelta"], g0["gdelta"].reshape(2, H, P, 30).sum(axis=2), rtol=1e-11, atol=1e-13)
+    close(g["gA"], g0["gA"].reshape(H, P * 4).sum(axis=1), rtol=1e-11, atol=1e-13)
+    for k in ("gx", "gBm", "gC", "gh0"):
+        close(g[k], g0[k], rtol=1e-11, atol=1e-13)
+
+
+def _loss_head(p, **over):
+    q = dict(p)
+    q.update(over)
+    y, hl = oracle.head_fwd(**_head_kw(q))
+    return float((y * q["gy"]).sum() + (hl * q["ghlast"]).sum())
+
+
+@pytest.mark.parametrize("name,gname", [("delta", "gdelta"), ("x", "gx"), ("A", "gA"), ("Bm", "gBm"),
+                                        ("C", "gC"), ("h0", "gh0")])
+def test_head_bwd_fd(name, gname):
+    p = small_head(B=2, H=2, P=2, N=3, L=9, seed=63)
+    g = oracle.head_bwd(**_head_kw(p), gy=p["gy"], ghlast=p["ghlast"])
+    fd_check(_loss_head, p, name, g[gname])
