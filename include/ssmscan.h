@@ -75,11 +75,11 @@
 extern "C" {
 #endif
 
-/* 6: adds strided views (ssm_layout, the layout fields of ssm_scan_args and
+/* 7: adds SSM_HEAD_SCALAR (head_dim field); 6 added strided views (ssm_layout, the layout fields of ssm_scan_args and
  * pd_scan_args) and the ZOH discretisation (discretization field); 5 added
  * ssm_scan_fwd_noalloc and ssm_roof_probe; 4 added SSM_COMPLEX_DENSE; 3 added
  * ssm_sensitivity_rows and SSM_OP_SENS_ROWS; struct layouts as in 2 */
-#define SSM_ABI_VERSION 6
+#define SSM_ABI_VERSION 7
 
 /* status codes */
 #define SSM_OK               0
@@ -100,6 +100,7 @@ extern "C" {
 #define SSM_REAL_DENSE     1
 #define SSM_COMPLEX_SHARED 2
 #define SSM_COMPLEX_DENSE  3  /* complex a_t given; f32 only */
+#define SSM_HEAD_SCALAR    4  /* one scalar transition per head of head_dim channels (below) */
 
 /* operation ids for ssm_workspace_bytes */
 #define SSM_OP_SCAN_FWD 0
@@ -124,7 +125,8 @@ extern "C" {
  * stride[r] holds the element strides of the role's dimensions, outermost
  * first (entries past the role's rank are ignored); other roles stay dense.
  * Rules (checked before anything is enqueued):
- *   - the innermost stride must be 1, strides are >= 0  -> SSM_ERR_LAYOUT;
+ *   - the innermost stride must be 1 (rank-1 inputs excepted: the per-head
+ *     A may have any stride, 0 included), strides are >= 0 -> SSM_ERR_LAYOUT;
  *   - stride 0 (broadcast) is allowed on inputs only; an output's strides
  *     must give distinct elements                        -> SSM_ERR_LAYOUT;
  *   - a role the mode or entry point does not take as a view -> SSM_ERR_UNSUPPORTED.
@@ -227,6 +229,20 @@ typedef struct {
     int32_t discretization;   /* SSM_REAL_SELECTIVE: SSM_EULER (0) or SSM_ZOH (ssm_scan_fwd,
                                  ssm_scan_bwd, ssm_scan_fwd_noalloc); other modes: 0 */
     const ssm_layout* layout; /* nullable: strided views (above); NULL = every tensor dense */
+    /* SSM_HEAD_SCALAR: channels per head P (16, 32, 48 or 64; channels = H * P).
+     * The selective scan with one scalar transition per head, as in the S3M
+     * page's matrix form (section 4.1): head h owns channels d = h*P .. h*P+P-1,
+     *   a_t = exp(delta[b,h,t] * A[h]),  h_t[d,n] = a_t h_{t-1}[d,n] + delta[b,h,t] x[b,d,t] Bm[b,t,n],
+     *   y[b,d,t] = sum_n C[b,t,n] h_t[d,n].
+     * Tensors: delta (B,H,L) dtype, x (B,D,L) dtype, A (H) f32, Bm, C (B,L,N)
+     * dtype (shared by the channels), h0 (B,D,N); state N in {16, 32, 48, 64}
+     * for the forward, 16 for the backward; chunk_len 0 or 64.  The forward
+     * runs the chunked matrix form on the matrix cores; the backward the exact
+     * tiled adjoint of the diagonal kernels.  Gradients: gdelta
+     * (B,H,L) dtype, gx (B,D,L), gA (H) f32, gBm, gC (B,L,N), gh0.  Views:
+     * SSM_V_DELTA is (B,H,L), SSM_V_A (H); Bm and C are shared by the channels.
+     * No step-size transform, no ZOH.  Other modes: 0. */
+    int64_t head_dim;
 } ssm_scan_args;
 
 typedef struct {
@@ -248,9 +264,9 @@ typedef struct {
  * g = dLoss/dRe + i dLoss/dIm (interleaved).  SSM_COMPLEX_DENSE writes ga,
  * gu, gc and gh0 only (the other pointers are ignored). */
 typedef struct {
-    void*  gdelta;  /* selective (B,D,L) dtype                  */
+    void*  gdelta;  /* selective (B,D,L) dtype; SSM_HEAD_SCALAR (B,H,L) */
     void*  gx;      /* selective (B,D,L) dtype                  */
-    float* gA;      /* selective (D,N) f32 (sum over b and t)   */
+    float* gA;      /* selective (D,N) f32 (sum over b and t); SSM_HEAD_SCALAR (H) */
     void*  gBm;     /* selective (B,L,N) dtype (sum over d); (B,D,L,N) for a per-channel Bm */
     float* ga;      /* dense (B,D,L,N) f32; complex dense (B,H,L,M) complex64 */
     float* gb;      /* dense (B,D,L,N) f32                      */

@@ -14,6 +14,7 @@ from .binding import (  # noqa: F401
     SSM_COMPLEX_DENSE,
     SSM_COMPLEX_SHARED,
     SSM_F32,
+    SSM_HEAD_SCALAR,
     SSM_REAL_DENSE,
     SSM_REAL_SELECTIVE,
     SSMError,

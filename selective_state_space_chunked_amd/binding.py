@@ -24,7 +24,7 @@ SSM_EULER, SSM_ZOH = 0, 1
 (V_DELTA, V_X, V_A, V_BM, V_C, V_Y, V_GY, V_GDELTA, V_GX, V_R, V_PHI, V_U, V_LAM, V_THETA, V_CC, V_LOGITS,
  V_PD_D, V_PD_B, V_PD_C, V_DICT) = range(20)
 V_COUNT = 20
-SSM_REAL_SELECTIVE, SSM_REAL_DENSE, SSM_COMPLEX_SHARED, SSM_COMPLEX_DENSE = 0, 1, 2, 3
+SSM_REAL_SELECTIVE, SSM_REAL_DENSE, SSM_COMPLEX_SHARED, SSM_COMPLEX_DENSE, SSM_HEAD_SCALAR = 0, 1, 2, 3, 4
 _COMPLEX_MODES = (SSM_COMPLEX_SHARED, SSM_COMPLEX_DENSE)
 (SSM_OP_SCAN_FWD, SSM_OP_SCAN_BWD, SSM_OP_IMPULSE, SSM_OP_PD_FWD, SSM_OP_PD_BWD, SSM_OP_COMPLEX_RTRL,
  SSM_OP_OUTPUT_SENS, SSM_OP_SENS_ROWS) = range(8)
@@ -70,7 +70,7 @@ class ScanArgs(ctypes.Structure):
                 ("delta", _vp), ("x", _vp), ("A", _vp), ("Bm", _vp), ("a", _vp), ("b", _vp), ("C", _vp),
                 ("r", _vp), ("phi", _vp), ("lam", _vp), ("theta", _vp), ("u", _vp), ("c", _vp), ("h0", _vp),
                 ("delta_bias", _vp), ("delta_softplus", ctypes.c_int32), ("discretization", ctypes.c_int32),
-                ("layout", ctypes.POINTER(Layout))]
+                ("layout", ctypes.POINTER(Layout)), ("head_dim", _i64)]
 
 
 class ScanFwdOut(ctypes.Structure):
@@ -170,7 +170,7 @@ def _need(t, name, dtype=None, shape=None, device=None, view=False):
     if shape is not None and tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
     if view:
-        if t.dim() and t.shape[-1] > 1 and t.stride(-1) != 1:
+        if t.dim() > 1 and t.shape[-1] > 1 and t.stride(-1) != 1:
             raise ValueError(f"{name}: the last dimension must be contiguous (stride 1)")
     elif not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
@@ -258,7 +258,32 @@ def _scan_args(mode, *, delta=None, x=None, A=None, Bm=None, a=None, b=None, C=N
     theta, c; their strides go to the library."""
     vw = _Views()
     perd = False
-    if mode == SSM_REAL_SELECTIVE:
+    head_dim = 0
+    if mode == SSM_HEAD_SCALAR:
+        # delta (B,H,L) and A (H) one per head; x (B,H*P,L); Bm, C (B,L,N)
+        _need(delta, "delta", view=True)
+        Bsz, H, L = delta.shape
+        st = delta.dtype
+        if st not in (torch.float32, torch.bfloat16):
+            raise TypeError("delta must be float32 or bfloat16")
+        dev = delta.device
+        _need(x, "x", view=True)
+        if x.dim() != 3 or x.shape[0] != Bsz or x.shape[2] != L or x.shape[1] % H:
+            raise ValueError(f"x has shape {tuple(x.shape)}; expected (B, H*P, L) with B={Bsz} H={H} L={L}")
+        D = x.shape[1]
+        head_dim = D // H
+        N = Bm.shape[-1]
+        _need(x, "x", st, (Bsz, D, L), dev, view=True)
+        for nm, t, role in (("Bm", Bm, V_BM), ("C", C, V_C)):
+            _need(t, nm, st, (Bsz, L, N), dev, view=True)
+            vw.set(role, (t.stride(0), 0, t.stride(1), t.stride(2)), (L * N, 0, N, 1))
+        _need(A, "A", torch.float32, (H,), dev, view=True)
+        _need(h0, "h0", torch.float32, (Bsz, D, N), dev)
+        vw.set(V_DELTA, delta.stride(), (H * L, L, 1))
+        vw.set(V_X, x.stride(), (D * L, L, 1))
+        vw.set(V_A, A.stride(), (1,))
+        dt = SSM_BF16 if st == torch.bfloat16 else SSM_F32
+    elif mode == SSM_REAL_SELECTIVE:
         _need(delta, "delta", view=True)
         Bsz, D, L = delta.shape
         N = A.shape[1]
@@ -333,7 +358,7 @@ def _scan_args(mode, *, delta=None, x=None, A=None, Bm=None, a=None, b=None, C=N
                     delta=_ptr(delta), x=_ptr(x), A=_ptr(A), Bm=_ptr(Bm), a=_ptr(a), b=_ptr(b), C=_ptr(C),
                     r=_ptr(r), phi=_ptr(phi), lam=_ptr(lam), theta=_ptr(theta), u=_ptr(u), c=_ptr(c),
                     h0=_ptr(h0), delta_bias=_ptr(delta_bias), delta_softplus=int(bool(delta_softplus)),
-                    discretization=int(discretization))
+                    discretization=int(discretization), head_dim=head_dim)
     args._views = vw          # kept with the struct: the library reads it during the call
     args._perd = perd
     args.layout = vw.ptr()
@@ -346,7 +371,7 @@ def _set_layout(args):
 
 def _stream_dtype(mode, tensors):
     """Element type of the per-step streams (y, gy and their gradients) of a call."""
-    if mode == SSM_REAL_SELECTIVE:
+    if mode in (SSM_REAL_SELECTIVE, SSM_HEAD_SCALAR):
         return tensors["delta"].dtype
     if mode == SSM_COMPLEX_SHARED and tensors["u"].dtype == torch.bfloat16:
         return torch.bfloat16
@@ -356,7 +381,7 @@ def _stream_dtype(mode, tensors):
 def _chunk(mode, chunk_len):
     if chunk_len:
         return chunk_len
-    return 256 if mode == SSM_REAL_SELECTIVE else 32
+    return {SSM_REAL_SELECTIVE: 256, SSM_HEAD_SCALAR: 64}.get(mode, 32)
 
 
 def scan_fwd(mode, *, want_y=True, want_h_last=False, want_ckpt=False, chunk_len=0, out=None, **tensors):
@@ -380,7 +405,7 @@ def _scan_fwd(mode, want_y, want_h_last, want_ckpt, chunk_len, out, tensors, noa
     ydt = _stream_dtype(mode, tensors)
     sdt = torch.complex64 if mode in _COMPLEX_MODES else torch.float32
     nc = n_chunks(L, _chunk(mode, chunk_len))
-    sel = mode == SSM_REAL_SELECTIVE
+    sel = mode in (SSM_REAL_SELECTIVE, SSM_HEAD_SCALAR)
     for k, want, shp, dt in (("y", want_y, (Bsz, D, L), ydt), ("h_last", want_h_last, (Bsz, D, N), sdt),
                              ("ckpt", want_ckpt, (Bsz, D, nc, N), sdt)):
         if want or out.get(k) is not None:
@@ -400,6 +425,7 @@ def _scan_fwd(mode, want_y, want_h_last, want_ckpt, chunk_len, out, tensors, noa
 
 _GRADS = {
     SSM_REAL_SELECTIVE: ("gdelta", "gx", "gA", "gBm", "gC", "gh0"),   # gdelta_bias on request
+    SSM_HEAD_SCALAR: ("gdelta", "gx", "gA", "gBm", "gC", "gh0"),
     SSM_REAL_DENSE: ("ga", "gb", "gC", "gh0"),
     SSM_COMPLEX_SHARED: ("gu", "gr", "gphi", "glam", "gtheta", "gc", "gh0"),
     SSM_COMPLEX_DENSE: ("ga", "gu", "gc", "gh0"),
@@ -411,7 +437,7 @@ def scan_bwd(mode, *, gy, gh_last=None, ckpt=None, want=None, chunk_len=0, out=N
     args, (Bsz, D, L, N), dev = _scan_args(mode, chunk_len=chunk_len, **tensors)
     ydt = _stream_dtype(mode, tensors)
     sdt = torch.complex64 if mode in _COMPLEX_MODES else torch.float32
-    sel = mode == SSM_REAL_SELECTIVE
+    sel = mode in (SSM_REAL_SELECTIVE, SSM_HEAD_SCALAR)
     _need(gy, "gy", ydt, (Bsz, D, L), dev, view=sel)
     _need(gh_last, "gh_last", sdt, (Bsz, D, N), dev)
     nc = n_chunks(L, _chunk(mode, chunk_len))
@@ -427,6 +453,10 @@ def scan_bwd(mode, *, gy, gh_last=None, ckpt=None, want=None, chunk_len=0, out=N
         "gtheta": ((D, N), torch.float32), "gc": ((D, N), torch.complex64),
         "gdelta_bias": ((D,), torch.float32),
     }
+    if mode == SSM_HEAD_SCALAR:   # per-head step sizes and transitions
+        H = tensors["delta"].shape[1]
+        shapes["gdelta"] = ((Bsz, H, L), ydt)
+        shapes["gA"] = ((H,), torch.float32)
     out = dict(out or {})
     def exists(k):
         return k in _GRADS[mode] or (k == "gdelta_bias" and mode == SSM_REAL_SELECTIVE)
@@ -438,7 +468,7 @@ def scan_bwd(mode, *, gy, gh_last=None, ckpt=None, want=None, chunk_len=0, out=N
         args._views.set(V_GY, gy.stride(), (D * L, L, 1))
         for k, role in (("gdelta", V_GDELTA), ("gx", V_GX)):
             if out.get(k) is not None:
-                args._views.set(role, out[k].stride(), (D * L, L, 1))
+                args._views.set(role, out[k].stride(), _dense_strides(out[k].shape))
         _set_layout(args)
     _on_gpu(dev)
     g = ScanGrads(**{f[0]: _ptr(out.get(f[0])) for f in ScanGrads._fields_})

@@ -194,11 +194,14 @@ int resolve_views(const ssm_layout* lay, uint64_t use_in, uint64_t use_out, View
             if (st < 0) return fail(SSM_ERR_LAYOUT, "%s: negative stride %lld", kRoleName[r], (long long)st);
             v->s[r][i] = st;
         }
-        // the innermost dimension must be contiguous (its stride is irrelevant for a single element)
-        if (v->dim[r][k - 1] > 1 && v->s[r][k - 1] != 1)
-            return fail(SSM_ERR_LAYOUT, "%s: innermost stride must be 1 (got %lld)", kRoleName[r],
-                        (long long)v->s[r][k - 1]);
-        v->s[r][k - 1] = 1;
+        // the innermost dimension must be contiguous (its stride is irrelevant for a single element);
+        // a rank-1 role (the per-head A) is indexed with its stride, which may be 0 on an input
+        if (k > 1 || out) {
+            if (v->dim[r][k - 1] > 1 && v->s[r][k - 1] != 1)
+                return fail(SSM_ERR_LAYOUT, "%s: innermost stride must be 1 (got %lld)", kRoleName[r],
+                            (long long)v->s[r][k - 1]);
+            v->s[r][k - 1] = 1;
+        }
         if (out && !distinct_elements(*v, r))
             return fail(SSM_ERR_LAYOUT, "output %s: strides must give distinct elements (no stride 0)", kRoleName[r]);
         if (v->s[r][0] >= (1LL << 40) || (k > 1 && v->s[r][1] >= (1LL << 40)))
@@ -222,6 +225,7 @@ struct ScanPlan {
     bool empty;    // no batch rows, channels or steps: only h_last / gh0 / parameter gradients are defined
     int disc;      // SSM_EULER or SSM_ZOH
     bool perd;     // selective: Bm and C given per channel
+    int64_t P, H;  // SSM_HEAD_SCALAR: channels per head, heads
     Views v;
 };
 
@@ -235,6 +239,11 @@ void scan_view_specs(ScanPlan* pl) {
     v.spec(SSM_V_C, {B, D, L, N}, {L * N, 0, N, 1});
     v.spec(SSM_V_U, {B, D, L, N}, {D * L * N, L * N, N, 1});
     for (int r : {SSM_V_LAM, SSM_V_THETA, SSM_V_CC}) v.spec(r, {D, N}, {N, 1});
+    if (pl->mode == SSM_HEAD_SCALAR) {   // per-head step sizes and transitions
+        const int64_t H = pl->H;
+        for (int r : {SSM_V_DELTA, SSM_V_GDELTA}) v.spec(r, {B, H, L}, {H * L, L, 1});
+        v.spec(SSM_V_A, {H}, {1});
+    }
 }
 
 // sel_default_T: the selective mode's checkpoint interval when chunk_len is 0
@@ -244,16 +253,38 @@ int validate_scan_args(const ssm_scan_args* a, ScanPlan* pl, int sel_default_T =
     pl->dtype = a->dtype;
     pl->B = a->batch; pl->D = a->channels; pl->L = a->length; pl->N = a->state;
     if (a->mode != SSM_REAL_SELECTIVE && a->mode != SSM_REAL_DENSE && a->mode != SSM_COMPLEX_SHARED &&
-        a->mode != SSM_COMPLEX_DENSE)
+        a->mode != SSM_COMPLEX_DENSE && a->mode != SSM_HEAD_SCALAR)
         return fail(SSM_ERR_UNSUPPORTED, "unknown mode %d", a->mode);
     if (a->dtype != SSM_F32 && a->dtype != SSM_BF16) return fail(SSM_ERR_DTYPE, "unknown dtype %d", a->dtype);
+    pl->P = 0;
+    pl->H = 0;
+    if (a->mode == SSM_HEAD_SCALAR) {
+        if (a->head_dim != 16 && a->head_dim != 32 && a->head_dim != 48 && a->head_dim != 64)
+            return fail(SSM_ERR_UNSUPPORTED, "head_dim %lld not supported (16, 32, 48 or 64)", (long long)a->head_dim);
+        if (a->channels % a->head_dim)
+            return fail(SSM_ERR_SHAPE, "channels %lld are not a multiple of head_dim %lld", (long long)a->channels,
+                        (long long)a->head_dim);
+        if (a->state != 16 && a->state != 32 && a->state != 48 && a->state != 64)
+            return fail(SSM_ERR_UNSUPPORTED, "SSM_HEAD_SCALAR takes state 16, 32, 48 or 64 (got %lld)",
+                        (long long)a->state);
+        if (entry != E_FWD && entry != E_BWD)
+            return fail(SSM_ERR_UNSUPPORTED, "SSM_HEAD_SCALAR supports ssm_scan_fwd and ssm_scan_bwd");
+        if (entry == E_BWD && a->state != 16)
+            return fail(SSM_ERR_UNSUPPORTED, "the SSM_HEAD_SCALAR backward takes state 16 (got %lld)",
+                        (long long)a->state);
+        pl->P = a->head_dim;
+        pl->H = a->channels / a->head_dim;
+    } else if (a->head_dim != 0) {
+        return fail(SSM_ERR_SHAPE, "head_dim applies to SSM_HEAD_SCALAR only");
+    }
     if (a->dtype == SSM_BF16 && (a->mode == SSM_REAL_DENSE || a->mode == SSM_COMPLEX_DENSE))
-        return fail(SSM_ERR_DTYPE, "bf16 streams are supported by SSM_REAL_SELECTIVE and SSM_COMPLEX_SHARED only");
+        return fail(SSM_ERR_DTYPE, "bf16 streams are supported by SSM_REAL_SELECTIVE, SSM_COMPLEX_SHARED and "
+                                   "SSM_HEAD_SCALAR only");
     if (pl->B < 0 || pl->D < 0 || pl->L < 0 || pl->N < 1)
         return fail(SSM_ERR_SHAPE, "sizes must be >= 0 and state >= 1 (B=%lld D=%lld L=%lld N=%lld)",
                     (long long)pl->B, (long long)pl->D, (long long)pl->L, (long long)pl->N);
     pl->empty = pl->B == 0 || pl->D == 0 || pl->L == 0;
-    const int64_t nmax = is_complex(a->mode) ? 64 : 16;
+    const int64_t nmax = is_complex(a->mode) || a->mode == SSM_HEAD_SCALAR ? 64 : 16;
     if (pl->N > nmax) return fail(SSM_ERR_SHAPE, "state size %lld exceeds %lld", (long long)pl->N, (long long)nmax);
     if (pl->B > 65535) return fail(SSM_ERR_SHAPE, "batch %lld exceeds 65535", (long long)pl->B);
     if (pl->L >= (1LL << 31) || pl->D >= (1LL << 24) || pl->B * pl->D * pl->L * pl->N >= (1LL << 46))
@@ -265,6 +296,10 @@ int validate_scan_args(const ssm_scan_args* a, ScanPlan* pl, int sel_default_T =
         if (T != 64 && T != 128 && T != 256)
             return fail(SSM_ERR_UNSUPPORTED, "chunk_len %d not supported (64, 128 or 256)", T);
         pl->kpl = T / 16;
+    } else if (a->mode == SSM_HEAD_SCALAR) {
+        if (T == 0) T = 64;
+        if (T != 64) return fail(SSM_ERR_UNSUPPORTED, "chunk_len %d not supported (64)", T);
+        pl->kpl = 4;   // the backward's tiles (16 lanes x 4 steps)
     } else {
         if (T == 0) T = 32;
         if (T != 32) return fail(SSM_ERR_UNSUPPORTED, "chunk_len %d not supported (32)", T);
@@ -289,7 +324,7 @@ int validate_scan_args(const ssm_scan_args* a, ScanPlan* pl, int sel_default_T =
     scan_view_specs(pl);
     {
         uint64_t in = 0, out = 0;
-        if (a->mode == SSM_REAL_SELECTIVE) {
+        if (a->mode == SSM_REAL_SELECTIVE || a->mode == SSM_HEAD_SCALAR) {
             in = bit(SSM_V_DELTA) | bit(SSM_V_X) | bit(SSM_V_A) | bit(SSM_V_BM) | bit(SSM_V_C);
             if (entry == E_FWD) out = bit(SSM_V_Y);
             if (entry == E_BWD) { in |= bit(SSM_V_GY); out = bit(SSM_V_GDELTA) | bit(SSM_V_GX); }
@@ -307,6 +342,19 @@ int validate_scan_args(const ssm_scan_args* a, ScanPlan* pl, int sel_default_T =
             return fail(SSM_ERR_UNSUPPORTED, "the sensitivity entry points take Bm and C shared by the channels");
         if (pl->perd && pl->disc == SSM_ZOH)
             return fail(SSM_ERR_UNSUPPORTED, "the ZOH discretisation takes Bm and C shared by the channels");
+    }
+    if (a->mode == SSM_HEAD_SCALAR) {
+        if (pl->D > 1 && (pl->v.sd(SSM_V_BM) != 0 || pl->v.sd(SSM_V_C) != 0))
+            return fail(SSM_ERR_UNSUPPORTED, "SSM_HEAD_SCALAR takes Bm and C shared by the channels");
+        if (!pl->empty && (!a->delta || !a->x || !a->A || !a->Bm || !a->C))
+            return fail(SSM_ERR_NULL, "SSM_HEAD_SCALAR needs delta, x, A, Bm and C");
+        int rc;
+        const size_t al = pl->esz;
+        if ((rc = check_align(a->delta, al, "delta")) || (rc = check_align(a->x, al, "x")) ||
+            (rc = check_align(a->Bm, al, "Bm")) || (rc = check_align(a->C, al, "C")) ||
+            (rc = check_align(a->A, 4, "A")) || (rc = check_align(a->h0, 4, "h0")))
+            return rc;
+        return SSM_OK;
     }
     if (a->mode == SSM_REAL_SELECTIVE) {
         if (!pl->empty && (!a->delta || !a->x || !a->A || !a->Bm || !a->C))
@@ -351,7 +399,7 @@ std::vector<Range> scan_inputs(const ssm_scan_args* a, const ScanPlan& p) {
         {a->delta, v.extent(SSM_V_DELTA) * p.esz, "delta"}, {a->x, v.extent(SSM_V_X) * p.esz, "x"},
         {a->A, v.extent(SSM_V_A) * 4, "A"}, {a->Bm, v.extent(SSM_V_BM) * p.esz, "Bm"},
         {a->a, BDLN * (p.mode == SSM_COMPLEX_DENSE ? 8 : 4), "a"}, {a->b, BDLN * 4, "b"},
-        {a->C, v.extent(SSM_V_C) * (p.mode == SSM_REAL_SELECTIVE ? p.esz : 4), "C"},
+        {a->C, v.extent(SSM_V_C) * (p.mode == SSM_REAL_DENSE ? 4 : p.esz), "C"},
         {a->r, v.extent(SSM_V_R) * p.esz, "r"}, {a->phi, v.extent(SSM_V_PHI) * p.esz, "phi"},
         {a->lam, v.extent(SSM_V_LAM) * 4, "lam"}, {a->theta, v.extent(SSM_V_THETA) * 4, "theta"},
         {a->u, v.extent(SSM_V_U) * 2 * p.esz, "u"}, {a->c, v.extent(SSM_V_CC) * 8, "c"},
@@ -461,6 +509,31 @@ void sel_bwd_layout(const ScanPlan& p, bool have_ckpt, bool wantB, bool wantC, b
 }
 
 // ---------------------------------------------------------------------------
+// scalar transition per head: the matrix-form forward
+// ---------------------------------------------------------------------------
+struct HeadFwdLayout {
+    float *state = nullptr, *decay = nullptr;
+};
+void head_fwd_layout(const ScanPlan& p, Carve& cv, HeadFwdLayout* l) {
+    l->state = cv.take<float>((size_t)p.B * p.H * p.nchunks * p.N * p.P);
+    l->decay = cv.take<float>((size_t)p.B * p.H * p.nchunks);
+}
+// y nullable: only the entering states (checkpoints, h_last) are produced
+int run_head_fwd(const ssm_scan_args* a, const ScanPlan& p, const HeadFwdLayout& l, void* y, float* h_last,
+                 float* ckpt, hipStream_t st) {
+    HeadParams q{};
+    q.delta = a->delta; q.x = a->x; q.A = a->A; q.Bm = a->Bm; q.C = a->C; q.h0 = a->h0;
+    copy_strides(q.sdelta, p, SSM_V_DELTA); copy_strides(q.sx, p, SSM_V_X); copy_strides(q.sy, p, SSM_V_Y);
+    copy_strides(q.sBm, p, SSM_V_BM); copy_strides(q.sC, p, SSM_V_C);
+    q.sA = p.v.s[SSM_V_A][0];
+    q.y = y; q.h_last = h_last; q.ckpt = ckpt;
+    q.state = l.state; q.decay = l.decay;
+    q.B = (int)p.B; q.H = (int)p.H; q.P = (int)p.P; q.L = (int)p.L; q.N = (int)p.N; q.nchunks = p.nchunks;
+    SSM_LAUNCH(launch_head_fwd(q, p.dtype, st), "head forward (matrix form)");
+    return SSM_OK;
+}
+
+// ---------------------------------------------------------------------------
 // entry-point helpers per mode (dense, complex and PD live further below)
 // ---------------------------------------------------------------------------
 int scan_fwd_impl(const ssm_scan_args* a, const ssm_scan_fwd_out* out, void* ws, size_t ws_bytes,
@@ -519,6 +592,16 @@ int scan_fwd_impl(const ssm_scan_args* a, const ssm_scan_fwd_out* out, void* ws,
         return ok();
     }
     Carve cv(nullptr);
+    if (p.mode == SSM_HEAD_SCALAR) {
+        HeadFwdLayout lay;
+        head_fwd_layout(p, cv, &lay);
+        if (need_only) { *need_only = cv.off; return ok(); }
+        if ((rc = check_ws(ws, ws_bytes, cv.off))) return rc;
+        Carve real(ws);
+        head_fwd_layout(p, real, &lay);
+        if ((rc = run_head_fwd(a, p, lay, out->y, out->h_last, out->ckpt, st))) return rc;
+        return ok();
+    }
     if (p.mode == SSM_REAL_SELECTIVE) {
         SelFwdLayout lay;
         sel_fwd_layout(p, cv, &lay);
@@ -575,7 +658,7 @@ int scan_bwd_impl(const ssm_scan_args* a, const ssm_scan_bwd_in* in, const ssm_s
         const size_t gbc = p.perd ? BDL * p.N : BLN;   // per-channel Bm / C: gradients per channel
         std::vector<Range> outs = {
             {g->gdelta, p.v.extent(SSM_V_GDELTA) * es, "gdelta"}, {g->gx, p.v.extent(SSM_V_GX) * es, "gx"},
-            {g->gA, (size_t)p.D * p.N * 4, "gA"},
+            {g->gA, (p.mode == SSM_HEAD_SCALAR ? (size_t)p.H : (size_t)p.D * p.N) * 4, "gA"},
             {g->gBm, gbc * es, "gBm"}, {g->ga, BDL * p.N * (p.mode == SSM_COMPLEX_DENSE ? 8 : 4), "ga"},
             {g->gb, BDL * p.N * 4, "gb"},
             {g->gC, gbc * es, "gC"}, {g->gu, BDL * p.N * 2 * es, "gu"}, {g->gr, BDL * es, "gr"},
@@ -592,7 +675,11 @@ int scan_bwd_impl(const ssm_scan_args* a, const ssm_scan_bwd_in* in, const ssm_s
         SSM_LAUNCH(launch_fill_copy_f32(g->gh0, in->gh_last, p.B * p.D * p.N * cx, st), "gh0 of an empty scan");
         // gBm and gC sum over channels: with D = 0 but B, L > 0 they have elements, all zero
         const size_t btn = p.D == 0 ? p.B * p.L * p.N : 0;
-        if (p.mode == SSM_REAL_SELECTIVE) {
+        if (p.mode == SSM_HEAD_SCALAR) {
+            SSM_LAUNCH(launch_fill_copy_f32(g->gA, nullptr, (size_t)p.H, st), "zero gA");
+            SSM_LAUNCH(launch_zero_bytes(g->gBm, btn * p.esz, st), "zero gBm");
+            SSM_LAUNCH(launch_zero_bytes(g->gC, btn * p.esz, st), "zero gC");
+        } else if (p.mode == SSM_REAL_SELECTIVE) {
             SSM_LAUNCH(launch_fill_copy_f32(g->gA, nullptr, dn, st), "zero gA");
             SSM_LAUNCH(launch_fill_copy_f32(g->gdelta_bias, nullptr, (size_t)p.D, st), "zero gdelta_bias");
             SSM_LAUNCH(launch_zero_bytes(g->gBm, btn * p.esz, st), "zero gBm");
@@ -609,6 +696,74 @@ int scan_bwd_impl(const ssm_scan_args* a, const ssm_scan_bwd_in* in, const ssm_s
         return ok();
     }
     Carve cv(nullptr);
+    if (p.mode == SSM_HEAD_SCALAR) {
+        // the exact tiled adjoint of the diagonal kernels, with delta and A one per head
+        struct L2 {
+            float* ckpt = nullptr;
+            HeadFwdLayout fwd;
+            SelBwdLayout sb;
+            float *gdc = nullptr, *gadn = nullptr;
+        };
+        auto layout = [&](Carve& c, bool have, bool wB, bool wC, bool wA, bool wD, L2* l) {
+            if (!have) {
+                l->ckpt = c.take<float>((size_t)p.B * p.D * p.nchunks * p.N);
+                head_fwd_layout(p, c, &l->fwd);
+            }
+            sel_bwd_layout(p, true, wB, wC, wA, false, c, &l->sb);
+            if (wD) l->gdc = c.take<float>((size_t)p.B * p.D * p.L);
+            if (wA) l->gadn = c.take<float>((size_t)p.D * p.N);
+        };
+        L2 sizing;
+        layout(cv, false, true, true, true, true, &sizing);
+        if (need_only) { *need_only = cv.off; return ok(); }
+        if ((rc = check_ws(ws, ws_bytes, cv.off))) return rc;
+        Carve real(ws);
+        L2 l;
+        layout(real, in->ckpt != nullptr, g->gBm != nullptr, g->gC != nullptr, g->gA != nullptr, g->gdelta != nullptr,
+               &l);
+        const float* ckpt = in->ckpt;
+        if (!ckpt) {
+            if ((rc = run_head_fwd(a, p, l.fwd, nullptr, nullptr, l.ckpt, st))) return rc;
+            ckpt = l.ckpt;
+        }
+        SelBwdParams q{};
+        q.delta = a->delta; q.x = a->x; q.A = a->A; q.Bm = a->Bm; q.C = a->C;
+        q.gy = in->gy; q.gh_last = in->gh_last; q.ckpt = ckpt; q.nu_in = l.sb.nu;
+        q.gdelta = l.gdc; q.gx = g->gx; q.gh0 = g->gh0;
+        q.partB = l.sb.partB; q.partC = l.sb.partC; q.partA = l.sb.partA;
+        q.segQ = l.sb.segQ; q.segR = l.sb.segR;
+        q.B = (int)p.B; q.D = (int)p.D; q.L = (int)p.L; q.N = (int)p.N;
+        q.ntiles = p.nchunks; q.tiles_per_seg = l.sb.tps; q.G = l.sb.G;
+        q.vec = sel_vec(p, {a->delta, a->x, in->gy, g->gx, l.gdc}, {SSM_V_DELTA, SSM_V_X, SSM_V_GY, SSM_V_GX});
+        q.stepf = StepXform{nullptr, 0};
+        copy_strides(q.sdelta, p, SSM_V_DELTA); copy_strides(q.sx, p, SSM_V_X); copy_strides(q.sgy, p, SSM_V_GY);
+        copy_strides(q.sgx, p, SSM_V_GX);
+        q.sgdelta[0] = p.D * p.L; q.sgdelta[1] = p.L;   // per-channel gdelta, fp32, dense
+        q.gdelta_f32 = 1;
+        copy_strides(q.sBm, p, SSM_V_BM); copy_strides(q.sC, p, SSM_V_C);
+        q.sA = p.v.s[SSM_V_A][0]; q.sAn = 0;             // one A per head, the same for every state
+        q.dgrp = (int)p.P; q.agrp = (int)p.P;
+        q.bc_vec = sel_bc_vec(p, a->Bm, a->C);
+        q.var = kVarEuler;
+        if (l.sb.G > 1) {
+            SSM_LAUNCH(launch_sel_bwd(q, p.dtype, p.kpl, true, st), "head backward summary");
+            SSM_LAUNCH(launch_seg_combine_rev(l.sb.segQ, l.sb.segR, in->gh_last, l.sb.nu, (int)(p.B * p.D), l.sb.G,
+                                              (int)p.N, st), "segment combine (reverse)");
+        }
+        SSM_LAUNCH(launch_sel_bwd(q, p.dtype, p.kpl, false, st), "head backward");
+        if (g->gBm || g->gC)
+            SSM_LAUNCH(launch_reduce_parts_btn(g->gBm ? l.sb.partB : nullptr, g->gC ? l.sb.partC : nullptr,
+                                               (int)cdiv(p.D, sel_bwd_rows()), (int)p.B, (int)p.N, (int)p.L, g->gBm,
+                                               g->gC, p.dtype, st),
+                       "reduce gB gC");
+        if (g->gA)
+            SSM_LAUNCH(launch_reduce_parts_dn(l.sb.partA, (int)p.B, l.sb.G, (int)p.D, (int)p.N, l.gadn, st), "reduce gA");
+        if (g->gdelta || g->gA)
+            SSM_LAUNCH(launch_head_reduce(l.gdc, g->gdelta, l.gadn, g->gA, (int)p.B, (int)p.H, (int)p.P, (int)p.N,
+                                          (int)p.L, p.dtype, st),
+                       "head sums of gdelta, gA");
+        return ok();
+    }
     if (p.mode == SSM_REAL_SELECTIVE) {
         // workspace is sized for the worst case (checkpoints recomputed, every gradient wanted);
         // per-channel Bm, C have per-channel gradients: no channel-block partials

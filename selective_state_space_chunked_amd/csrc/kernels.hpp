@@ -28,6 +28,10 @@ struct SelFwdParams {
     int64_t sdelta[2], sx[2], sy[2], sBm[3], sC[3], sA;
     int bc_vec;             // 16-byte loads of the B_t / C_t rows (aligned)
     int var;                // kernel variant: 0 Euler, 1 per-channel B_t / C_t, 2 ZOH
+    // channels per delta row and per A row (one scalar transition per head of
+    // dgrp = agrp channels), and A's state stride (0: one value for every state)
+    int dgrp = 1, agrp = 1;
+    int64_t sAn = 1;
     const float* h0;        // (B,D,N) or null
     const float* carry_in;  // (B,D,G,N) state entering each segment (G > 1)
     void* y;                // (B,D,L) or null
@@ -45,6 +49,9 @@ struct SelBwdParams {
     int64_t sdelta[2], sx[2], sgy[2], sgx[2], sgdelta[2], sBm[3], sC[3], sA;
     int bc_vec;
     int var;
+    int dgrp = 1, agrp = 1;
+    int64_t sAn = 1;
+    int gdelta_f32 = 0;     // gdelta stored as fp32 whatever the stream type
     void* gBm_pd; void* gC_pd;   // per-channel B_t, C_t: their gradients (B,D,L,N), written directly
     const float* nu_in;     // (B,D,G,N) adjoint entering each segment from the right (G > 1)
     void* gdelta; void* gx; float* gh0;
@@ -173,6 +180,24 @@ struct RtrlParams {
 hipError_t launch_cplx_rtrl(const RtrlParams& p, bool summary, hipStream_t st);
 hipError_t launch_cplx_rtrl_combine(const RtrlParams& p, hipStream_t st);
 hipError_t launch_cplx_rtrl_reduce(const RtrlParams& p, hipStream_t st);
+
+// --------------------- scalar transition per head (matrix form) ------------
+// Head h owns channels d = h*P + p; delta (B,H,L) rows at b*sdelta[0] +
+// h*sdelta[1]; x, y (B,D,L) rows at b*s[0] + d*s[1]; A (H) at h*sA; Bm, C
+// (B,L,N) at b*s[0] + t*s[2] + n.  Workspace: state (B,H,nchunks,N,P) chunk
+// states (local, then entering), decay (B,H,nchunks).
+struct HeadParams {
+    const void* delta; const void* x; const float* A; const void* Bm; const void* C; const float* h0;
+    int64_t sdelta[2], sx[2], sy[2], sBm[3], sC[3], sA;
+    void* y; float* h_last; float* ckpt;
+    float* state; float* decay;
+    int B, H, P, L, N, nchunks;
+};
+hipError_t launch_head_fwd(const HeadParams& p, int dtype, hipStream_t st);
+// gdelta (B,H,L) = sums over each head's channels of gdc (B,D,L) fp32; gA (H) =
+// sums of ga_dn (D,N) over each head's channels and states (null skips either)
+hipError_t launch_head_reduce(const float* gdc, void* gdelta, const float* ga_dn, float* gA, int B, int H, int P,
+                              int N, int L, int dtype, hipStream_t st);
 
 // ------------------------------- PD ----------------------------------------
 struct PDParams {

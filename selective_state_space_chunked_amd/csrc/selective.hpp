@@ -229,7 +229,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
     const bool act = d < p.D;
     const int dc = act ? d : p.D - 1;
     const int N = NT ? NT : p.N, L = p.L;
-    const T* __restrict__ delta = (const T*)p.delta + ((int64_t)b * p.sdelta[0] + (int64_t)dc * p.sdelta[1]);
+    const T* __restrict__ delta = (const T*)p.delta + ((int64_t)b * p.sdelta[0] + (int64_t)(dc / p.dgrp) * p.sdelta[1]);
     const T* __restrict__ xin = (const T*)p.x + ((int64_t)b * p.sx[0] + (int64_t)dc * p.sx[1]);
     // per-channel B_t, C_t: this row's (b, d) slice, element (t, n) at t * sl + n
     const T* __restrict__ bmrow = (const T*)p.Bm + ((int64_t)b * p.sBm[0] + (int64_t)dc * p.sBm[1]);
@@ -238,7 +238,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
 
     float A2 = 0.0f, carry = 0.0f, Pseg = 1.0f, invA = 0.0f;
     if (lane < N) {
-        const float Av = p.A[(int64_t)dc * p.sA + lane];
+        const float Av = p.A[(int64_t)(dc / p.agrp) * p.sA + lane * p.sAn];
         A2 = Av * kLog2e;
         if (ZOH) invA = zoh_inv(Av);
         if (!SUMMARY) {
@@ -384,7 +384,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
     const bool act = d < p.D;
     const int dc = act ? d : p.D - 1;
     const int N = NT ? NT : p.N, L = p.L;
-    const T* __restrict__ delta = (const T*)p.delta + ((int64_t)b * p.sdelta[0] + (int64_t)dc * p.sdelta[1]);
+    const T* __restrict__ delta = (const T*)p.delta + ((int64_t)b * p.sdelta[0] + (int64_t)(dc / p.dgrp) * p.sdelta[1]);
     const T* __restrict__ xin = (const T*)p.x + ((int64_t)b * p.sx[0] + (int64_t)dc * p.sx[1]);
     const T* __restrict__ gyin = (const T*)p.gy + ((int64_t)b * p.sgy[0] + (int64_t)dc * p.sgy[1]);
     const T* __restrict__ bmrow = (const T*)p.Bm + ((int64_t)b * p.sBm[0] + (int64_t)dc * p.sBm[1]);
@@ -398,7 +398,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
 
     float A2 = 0.0f, nu = 0.0f, gAacc = 0.0f, Qseg = 1.0f, gbias = 0.0f, invA = 0.0f;
     if (lane < N) {
-        const float Av = p.A[(int64_t)dc * p.sA + lane];
+        const float Av = p.A[(int64_t)(dc / p.agrp) * p.sA + lane * p.sAn];
         A2 = Av * kLog2e;
         if (ZOH) invA = zoh_inv(Av);
         if (!SUMMARY) {
@@ -648,9 +648,11 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
                     for (int j = 0; j < KPL; ++j)
                         v[j] = fmaf(xv[j], Sb[j], Gd[j]) * step_xform_grad(dl[j], p.stepf.softplus);
                 }
-                if (p.gdelta)
-                    store_run<KPL>((T*)p.gdelta + ((int64_t)b * p.sgdelta[0] + (int64_t)dc * p.sgdelta[1]) + tl, v,
-                                   vec, nval);
+                if (p.gdelta) {
+                    const int64_t o = (int64_t)b * p.sgdelta[0] + (int64_t)dc * p.sgdelta[1] + tl;
+                    if (p.gdelta_f32) store_run<KPL>((float*)p.gdelta + o, v, vec, nval);   // uniform
+                    else store_run<KPL>((T*)p.gdelta + o, v, vec, nval);
+                }
 #pragma unroll
                 for (int j = 0; j < KPL; ++j) gbias += j < nval ? v[j] : 0.0f;
             }

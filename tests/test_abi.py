@@ -37,6 +37,7 @@ def test_header_constants_match_binding():
     assert consts["SSM_REAL_DENSE"] == B.SSM_REAL_DENSE
     assert consts["SSM_COMPLEX_SHARED"] == B.SSM_COMPLEX_SHARED
     assert consts["SSM_COMPLEX_DENSE"] == B.SSM_COMPLEX_DENSE
+    assert consts["SSM_HEAD_SCALAR"] == B.SSM_HEAD_SCALAR
     assert consts["SSM_OP_PD_BWD"] == B.SSM_OP_PD_BWD
     assert consts["SSM_OP_COMPLEX_RTRL"] == B.SSM_OP_COMPLEX_RTRL
     assert consts["SSM_OP_OUTPUT_SENS"] == B.SSM_OP_OUTPUT_SENS
@@ -47,7 +48,7 @@ def test_header_constants_match_binding():
 def test_struct_layouts():
     # 2 x int32 + 5 x int64 + 14 pointers
     # + delta_bias pointer + delta_softplus, discretization int32 + layout pointer
-    assert ctypes.sizeof(B.ScanArgs) == 8 + 5 * 8 + 15 * 8 + 8 + 8
+    assert ctypes.sizeof(B.ScanArgs) == 8 + 5 * 8 + 15 * 8 + 8 + 8 + 8   # + head_dim
     assert ctypes.sizeof(B.ScanGrads) == 15 * 8
     assert ctypes.sizeof(B.PDArgs) == 6 * 8 + 7 * 8 + 8 + 8   # + dtype (int32, padded) + layout pointer
     assert ctypes.sizeof(B.Layout) == 8 + 20 * 4 * 8
