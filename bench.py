@@ -388,6 +388,62 @@ def w_dense(steps, warmup):
                 config=dict(B=B, D=D, N=N, L=L, streams="f32", chunk_len=32, data="torch-generated on device"))
 
 
+# fp32 MFMA peak of MI355X (dense): 256 CUs x 4 SIMDs x 64 flops per cycle x 2.4 GHz
+MFMA_F32_PEAK = 256 * 4 * 64 * 2.4e9
+
+
+def w_head(steps, warmup):
+    """Scalar transition per head (matrix form on the matrix cores in the forward, the exact tiled adjoint
+    in the backward): B=8 H=32 P=64 (D=2048) N=16 L=4096, bf16 streams, the element count of the Mamba-layer
+    workload.  Reports the matrix-core rate of the two MFMA passes."""
+    import torch
+    import selective_state_space_chunked_amd as ssm
+    B, H, P, N, L = 8, 32, 64, 16, 4096
+    D = H * P
+    gen = torch.Generator(device="cuda").manual_seed(0)
+    bf = torch.bfloat16
+    t = dict(delta=torch.nn.functional.softplus(torch.randn((B, H, L), device="cuda", generator=gen)).to(bf),
+             x=torch.randn((B, D, L), device="cuda", generator=gen).to(bf),
+             A=-torch.exp(torch.rand((H,), device="cuda", generator=gen) * 2 - 3),
+             Bm=(torch.randn((B, L, N), device="cuda", generator=gen) / 4).to(bf),
+             C=(torch.randn((B, L, N), device="cuda", generator=gen) / 4).to(bf))
+    gy = torch.randn((B, D, L), device="cuda", generator=gen).to(bf)
+    fo = ssm.scan_fwd(ssm.SSM_HEAD_SCALAR, want_ckpt=True, **t)
+    go = ssm.scan_bwd(ssm.SSM_HEAD_SCALAR, gy=gy, ckpt=fo["ckpt"], want=("gdelta", "gx", "gBm", "gC"), **t)
+
+    def step():
+        ssm.scan_fwd(ssm.SSM_HEAD_SCALAR, want_ckpt=True, out=fo, **t)
+        ssm.scan_bwd(ssm.SSM_HEAD_SCALAR, gy=gy, ckpt=fo["ckpt"], want=("gdelta", "gx", "gBm", "gC"), out=go, **t)
+
+    ms = time_steps(step, max(3, steps // 4), max(1, warmup // 2))
+    kern = profile_kernels(step, reps=2)
+    nch = L // 64
+    # MFMAs (v_mfma_f32_16x16x4_f32, 2048 flops each) executed per 64-step chunk.  States: (P/16)(N/16)
+    # tiles of K = 64.  Outputs: the wave with row block rb (0..3) forms G tiles up to the diagonal
+    # ((rb+1) N/4), multiplies M by X over K = 16 (rb+1) for P/16 column tiles, and adds the carried term
+    # (N/4 per column tile).  SQ_VALU_MFMA_BUSY_CYCLES / 32 per chunk reads the same counts.
+    per_chunk = {"head chunk states (matrix cores)": (P // 16) * (N // 16) * 16,
+                 "head outputs (matrix cores)": sum((rb + 1) * (N // 4) + (P // 16) * 4 * (rb + 1)
+                                                    + (P // 16) * (N // 4) for rb in range(4))}
+    mfma = {}
+    for k, n_mfma in per_chunk.items():
+        if k in kern:
+            fl = n_mfma * 2048.0 * B * H * nch
+            rate = fl / (kern[k][0] * 1e-3)
+            mfma[k] = {"mfma_per_chunk": n_mfma, "TFLOP/s": round(rate / 1e12, 2),
+                       "busy_frac": round(rate / MFMA_F32_PEAK, 3)}
+    BDL, BHL, BLN = B * D * L, B * H * L, B * L * N
+    ck = B * D * nch * N * 4
+    fwd = 2 * (BHL + BDL + 2 * BLN) + 2 * BDL + ck                 # read delta, x, B, C; write y, ckpt
+    bwd = 2 * (BHL + 2 * BDL + 2 * BLN) + ck + 2 * (BHL + BDL + 2 * BLN)  # + gy; write gdelta, gx, gB, gC
+    return dict(name="head", elements=B * D * N * L, ms=ms, kernels=kern, bytes_total=fwd + bwd,
+                config=dict(B=B, H=H, P=P, D=D, N=N, L=L, streams="bf16", chunk_len=64,
+                            data="torch-generated on device"),
+                mfma=dict(kernels=mfma, peak_TFLOP_s=round(MFMA_F32_PEAK / 1e12, 1),
+                          note="busy_frac: executed fp32 MFMA flops over the dense fp32 matrix-core peak, "
+                               "i.e. the fraction of SIMD cycles the matrix cores are busy"))
+
+
 def summarize(w):
     ms = w["ms"]
     r = dict(el_per_s=w["elements"] / (ms * 1e-3), ms_per_step=ms,
@@ -395,6 +451,8 @@ def summarize(w):
              config=w["config"], kernels_ms={k: round(v[0], 4) for k, v in w["kernels"].items()})
     if w.get("note"):
         r["note"] = w["note"]
+    if w.get("mfma"):
+        r["mfma"] = w["mfma"]
     return r
 
 
@@ -575,7 +633,7 @@ def main():
     if not args.no_others:
         todo = [w.strip() for w in args.workloads.split(",") if w.strip()] or \
             ["impulse", "output-sens", "sens-rows", "complex", "complex-dense", "complex-rtrl", "pd", "pd-ste", "dense",
-             "real-small"]
+             "head", "real-small"]
         for w in todo:
             if w == "impulse":
                 others[w] = summarize(w_impulse(args.steps, args.warmup))
@@ -595,6 +653,8 @@ def main():
                 others[w] = summarize(w_pd_ste(args.steps, args.warmup))
             elif w == "dense":
                 others[w] = summarize(w_dense(args.steps, args.warmup))
+            elif w == "head":
+                others[w] = summarize(w_head(args.steps, args.warmup))
             elif w == "real-small":
                 others[w] = summarize(w_real(w, 1, 16, 16, 1024, "f32", args.steps, args.warmup))
             torch.cuda.empty_cache()

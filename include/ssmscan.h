@@ -353,10 +353,12 @@ int ssm_scan_fwd(const ssm_scan_args* args, const ssm_scan_fwd_out* out,
  * serving loops, harnesses that forbid hipMalloc).  Same arguments, outputs,
  * results (bit for bit) and errors as ssm_scan_fwd, with the workspace taken
  * from a static device array of SSM_NOALLOC_SCRATCH_BYTES bytes that every
- * device the library runs on holds until the process ends.  Every forward
- * need fits it (at most about 25 MB: complex mode, M = 64, a few thousand
- * sequences); a larger need would be refused with SSM_ERR_WORKSPACE before
- * anything is enqueued.  The call allocates nothing.  Calls that overlap on
+ * device the library runs on holds until the process ends.  Every diagonal,
+ * dense and complex forward fits it (at most about 25 MB: complex mode,
+ * M = 64, a few thousand sequences).  The SSM_HEAD_SCALAR forward keeps its
+ * chunk states there, 4 * B * D * N * ceil(L / 64) bytes plus
+ * 4 * B * H * ceil(L / 64): a need beyond the array is refused with
+ * SSM_ERR_WORKSPACE before anything is enqueued.  The call allocates nothing.  Calls that overlap on
  * one device (different streams, or different threads) share the array and
  * race: serialise them.  On first use on a device the call looks up the
  * array's device address (hipGetSymbolAddress). */

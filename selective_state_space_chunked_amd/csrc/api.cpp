@@ -529,7 +529,17 @@ int run_head_fwd(const ssm_scan_args* a, const ScanPlan& p, const HeadFwdLayout&
     q.y = y; q.h_last = h_last; q.ckpt = ckpt;
     q.state = l.state; q.decay = l.decay;
     q.B = (int)p.B; q.H = (int)p.H; q.P = (int)p.P; q.L = (int)p.L; q.N = (int)p.N; q.nchunks = p.nchunks;
-    SSM_LAUNCH(launch_head_fwd(q, p.dtype, st), "head forward (matrix form)");
+    {   // 16-byte row loads need 16-byte aligned rows; 4-step stores of y, 4-element aligned rows
+        const int64_t e16 = 16 / (int64_t)p.esz;
+        auto al = [](const void* ptr, int64_t bytes) { return ((uintptr_t)ptr % (uintptr_t)bytes) == 0; };
+        q.vx = al(a->x, 16) && q.sx[0] % e16 == 0 && q.sx[1] % e16 == 0;
+        q.vb = al(a->Bm, 16) && q.sBm[0] % e16 == 0 && q.sBm[2] % e16 == 0;
+        q.vc = al(a->C, 16) && q.sC[0] % e16 == 0 && q.sC[2] % e16 == 0;
+        q.vy = y && al(y, 4 * (int64_t)p.esz) && q.sy[0] % 4 == 0 && q.sy[1] % 4 == 0;
+    }
+    SSM_LAUNCH(launch_head_state(q, p.dtype, st), "head chunk states (matrix cores)");
+    SSM_LAUNCH(launch_head_chain(q, st), "head chunk chain");
+    if (y) SSM_LAUNCH(launch_head_out(q, p.dtype, st), "head outputs (matrix cores)");
     return SSM_OK;
 }
 

@@ -24,8 +24,8 @@
 
 namespace ssm {
 
-constexpr int kHT = 64;          // chunk length (steps)
-constexpr int kHPad = kHT + 1;   // LDS row of one chunk (+1 spreads the rows over banks)
+constexpr int kHT = 64;     // chunk length (steps)
+constexpr int kXLd = 68;    // LDS row of a chunk of x, B^T or M: 16-byte aligned rows 4 banks apart
 
 typedef float f4 __attribute__((ext_vector_type(4)));
 
@@ -33,22 +33,26 @@ __device__ __forceinline__ f4 mfma4(float a, float b, f4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// LDS layout (float offsets) of a chunk for P channels and N states: delta and
-// s (T each), x as [p][u] rows of T + 1, B and C as [u][n] rows of N + 1, the
-// entering state as [n][p] rows of P + 1, and each wave's 16 rows of M.
+// LDS row of N states: N + 4 (16-byte aligned rows that start 4 banks apart).
+__host__ __device__ inline int ld_rows_i(int N) { return N + 4; }
+
+// LDS layout (float offsets, multiples of 4): delta, s and the state weights w
+// (T each), x as [p][u], B and C as [u][n] (B as [n][u] in the state pass), the
+// entering state as [p][n], and each wave's 16 rows of M.
 struct HeadLds {
-    int dl, s, sx, sB, sC, sH, sM, total;
+    int dl, s, w, sx, sB, sC, sH, sM, total;
 };
 __host__ __device__ inline HeadLds head_lds(int P, int N, bool out) {
     HeadLds o;
     o.dl = 0;
     o.s = kHT;
-    o.sx = 2 * kHT;
-    o.sB = o.sx + P * kHPad;
-    o.sC = o.sB + kHT * (N + 1);
-    o.sH = o.sC + (out ? kHT * (N + 1) : 0);
-    o.sM = o.sH + (out ? N * (P + 1) : 0);
-    o.total = o.sM + (out ? 4 * 16 * kHPad : 0);
+    o.w = 2 * kHT;
+    o.sx = 3 * kHT;
+    o.sB = o.sx + P * kXLd;
+    o.sC = o.sB + (out ? kHT * ld_rows_i(N) : N * kXLd);
+    o.sH = o.sC + (out ? kHT * ld_rows_i(N) : 0);
+    o.sM = o.sH + (out ? P * ld_rows_i(N) : 0);
+    o.total = o.sM + (out ? 4 * 16 * kXLd : 0);
     return o;
 }
 
@@ -65,32 +69,148 @@ __device__ __forceinline__ HeadTile head_tile(const HeadParams& p) {
     return q;
 }
 
-// Stage the chunk: delta (T), x as [p][u] (P rows of T), B and C as [u][n]
-// (T rows of N); steps past the end are zero.  s[u] = A * (inclusive prefix sum
-// of delta) in fp32, by one wave (a 64-lane scan: DPP within rows of 16, then
-// the row totals).
+__device__ __forceinline__ void unpack16(const uint4& r, float (&f)[8]) {   // 8 bf16
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        f[2 * q] = __uint_as_float(w[q] << 16);
+        f[2 * q + 1] = __uint_as_float(w[q] & 0xffff0000u);
+    }
+}
+__device__ __forceinline__ void unpack16(const uint4& r, float (&f)[4]) {   // 4 fp32
+    f[0] = __uint_as_float(r.x); f[1] = __uint_as_float(r.y);
+    f[2] = __uint_as_float(r.z); f[3] = __uint_as_float(r.w);
+}
+
+// An R x K tile (row r at base + r * rs, K contiguous elements; R * K <= 4096,
+// K a multiple of 16) moves to LDS as fp32, dst[r * ld + k] (dst[k * ld + r]
+// when tr), zero outside rows < vr and columns < vk.  Whole tiles with 16-byte
+// aligned rows (VEC) go in two steps: tile_fetch issues a thread's 16-byte
+// loads into 16 registers, so that the loads of several tiles are in flight
+// together, and tile_put unpacks and writes them.  Otherwise tile_put loads
+// and writes the tile by itself, 16 elements a thread, all loads first.  No
+// branch guards a load: an index past the tile is clamped to its last element
+// (the same value goes to the same place twice) and a masked one reads the
+// first element and writes zero.  Row and column of a flat index come from a
+// float product with the reciprocal of the row length: exact for indices
+// below 2^12 and rows of at most 64.
 template <typename T>
-__device__ __forceinline__ void head_stage(const HeadParams& p, const HeadTile& q, float* dl, float* sx, float* sB,
-                                           float* sC, float* s, bool needC) {
+struct TileSrc {
+    const T* base;
+    int64_t rs;
+    int R, K, vr, vk;
+};
+__device__ __forceinline__ int tile_row(int i, float inv) { return (int)(((float)i + 0.5f) * inv); }
+
+template <typename T, bool VEC>
+__device__ __forceinline__ void tile_fetch(const TileSrc<T>& ts, float (&v)[16]) {
+    if constexpr (VEC) {
+        constexpr int E = 16 / (int)sizeof(T);
+        const int kp = ts.K / E, np = ts.R * kp;
+        const float inv = 1.0f / (float)kp;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (256 * j >= np) break;   // uniform
+            const int i = min((int)threadIdx.x + 256 * j, np - 1);
+            const int r = tile_row(i, inv), k = (i - r * kp) * E;
+            const uint4 raw = *(const uint4*)(ts.base + (int64_t)r * ts.rs + k);
+            v[4 * j] = __uint_as_float(raw.x); v[4 * j + 1] = __uint_as_float(raw.y);
+            v[4 * j + 2] = __uint_as_float(raw.z); v[4 * j + 3] = __uint_as_float(raw.w);
+        }
+    }
+}
+
+template <typename T, bool VEC>
+__device__ __forceinline__ void tile_put(const TileSrc<T>& ts, const float (&v)[16], float* __restrict__ dst, int ld,
+                                         bool tr) {
+    const int tid = threadIdx.x;
+    if constexpr (VEC) {
+        constexpr int E = 16 / (int)sizeof(T);
+        const int kp = ts.K / E, np = ts.R * kp;
+        const float inv = 1.0f / (float)kp;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (256 * j >= np) break;   // uniform
+            const int i = min(tid + 256 * j, np - 1);
+            const int r = tile_row(i, inv), k = (i - r * kp) * E;
+            float f[E];
+            if constexpr (E == 8) {   // 8 bf16
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t w = __float_as_uint(v[4 * j + q]);
+                    f[2 * q] = __uint_as_float(w << 16);
+                    f[2 * q + 1] = __uint_as_float(w & 0xffff0000u);
+                }
+            } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) f[q] = v[4 * j + q];
+            }
+            if (tr) {
+#pragma unroll
+                for (int q = 0; q < E; ++q) dst[(k + q) * ld + r] = f[q];
+            } else {
+#pragma unroll
+                for (int q = 0; q < E; q += 4)
+                    *(float4*)&dst[r * ld + k + q] = make_float4(f[q], f[q + 1], f[q + 2], f[q + 3]);
+            }
+        }
+    } else {
+        const float inv = 1.0f / (float)ts.K;
+        const int ne = ts.R * ts.K;
+        float u[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            if (256 * j >= ne) break;   // uniform
+            const int i = min(tid + 256 * j, ne - 1);
+            const int r = tile_row(i, inv), k = i - r * ts.K;
+            u[j] = to_f32(ts.base[r < ts.vr && k < ts.vk ? (int64_t)r * ts.rs + k : 0]);
+        }
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            if (256 * j >= ne) break;   // uniform
+            const int i = min(tid + 256 * j, ne - 1);
+            const int r = tile_row(i, inv), k = i - r * ts.K;
+            dst[tr ? k * ld + r : r * ld + k] = r < ts.vr && k < ts.vk ? u[j] : 0.0f;
+        }
+    }
+}
+
+// The chunk's tiles: delta (T), x as [p][u] (P rows of T), B (and C) as [u][n];
+// steps past the end are zero.  head_fetch issues the loads (all of them for
+// whole aligned tiles); head_put writes LDS, then wave 0 forms s[u] = A * the
+// inclusive prefix sum of delta over the chunk in fp32 (a 64-lane scan: DPP
+// within rows of 16, then the row totals) and the state weights
+// w[u] = e^(s_{T-1} - s_u) delta_u.
+template <typename T>
+struct HeadRegs {
+    float x[16], b[16], c[16], dv, A;
+    TileSrc<T> tx, tb, tc;
+};
+template <typename T, bool VEC>
+__device__ __forceinline__ void head_fetch(const HeadParams& p, const HeadTile& q, bool needC, HeadRegs<T>& g) {
     const int tid = threadIdx.x, P = p.P, N = p.N;
     const T* delta = (const T*)p.delta + (int64_t)q.b * p.sdelta[0] + (int64_t)q.hh * p.sdelta[1] + q.t0;
-    for (int u = tid; u < kHT; u += 256) dl[u] = u < q.nval ? to_f32(delta[u]) : 0.0f;
-    const T* xb = (const T*)p.x + (int64_t)q.b * p.sx[0] + (int64_t)q.hh * P * p.sx[1] + q.t0;
-    for (int e = tid; e < P * kHT; e += 256) {
-        const int pp = e / kHT, u = e - pp * kHT;
-        sx[pp * kHPad + u] = u < q.nval ? to_f32(xb[(int64_t)pp * p.sx[1] + u]) : 0.0f;
-    }
-    const T* bb = (const T*)p.Bm + (int64_t)q.b * p.sBm[0] + (int64_t)q.t0 * p.sBm[2];
-    const T* cb = (const T*)p.C + (int64_t)q.b * p.sC[0] + (int64_t)q.t0 * p.sC[2];
-    for (int e = tid; e < kHT * N; e += 256) {
-        const int u = e / N, n = e - u * N;
-        const bool v = u < q.nval;
-        sB[u * (N + 1) + n] = v ? to_f32(bb[(int64_t)u * p.sBm[2] + n]) : 0.0f;
-        if (needC) sC[u * (N + 1) + n] = v ? to_f32(cb[(int64_t)u * p.sC[2] + n]) : 0.0f;
-    }
-    __syncthreads();
-    if (tid < 64) {   // prefix sum of delta over the chunk (wave 0, lane = step)
-        float v = dl[tid];
+    g.dv = to_f32(delta[min(tid, q.nval - 1)]);
+    g.A = p.A[(int64_t)q.hh * p.sA];
+    g.tx = TileSrc<T>{(const T*)p.x + (int64_t)q.b * p.sx[0] + (int64_t)q.hh * P * p.sx[1] + q.t0, p.sx[1], P, kHT,
+                      P, q.nval};
+    g.tb = TileSrc<T>{(const T*)p.Bm + (int64_t)q.b * p.sBm[0] + (int64_t)q.t0 * p.sBm[2], p.sBm[2], kHT, N, q.nval,
+                      N};
+    g.tc = TileSrc<T>{(const T*)p.C + (int64_t)q.b * p.sC[0] + (int64_t)q.t0 * p.sC[2], p.sC[2], kHT, N, q.nval, N};
+    tile_fetch<T, VEC>(g.tx, g.x);
+    tile_fetch<T, VEC>(g.tb, g.b);
+    if (needC) tile_fetch<T, VEC>(g.tc, g.c);
+}
+template <typename T, bool VEC>
+__device__ __forceinline__ void head_put(const HeadParams& p, const HeadTile& q, const HeadRegs<T>& g, float* dl,
+                                         float* s, float* w, float* sx, float* sB, float* sC, int ldb, bool trB) {
+    const int tid = threadIdx.x;
+    tile_put<T, VEC>(g.tx, g.x, sx, kXLd, false);
+    tile_put<T, VEC>(g.tb, g.b, sB, ldb, trB);
+    if (sC) tile_put<T, VEC>(g.tc, g.c, sC, ldb, false);
+    if (tid < kHT) {   // wave 0, lane = step
+        const float dv = tid < q.nval ? g.dv : 0.0f;
+        float v = dv;
         v += dpp<SSM_DPP_ROW_SHR(1)>(0.0f, v);
         v += dpp<SSM_DPP_ROW_SHR(2)>(0.0f, v);
         v += dpp<SSM_DPP_ROW_SHR(4)>(0.0f, v);
@@ -99,142 +219,216 @@ __device__ __forceinline__ void head_stage(const HeadParams& p, const HeadTile& 
         const float r0 = __shfl(v, 15), r1 = __shfl(v, 31), r2 = __shfl(v, 47);
         const int row = tid >> 4;
         v += (row > 0 ? r0 : 0.0f) + (row > 1 ? r1 : 0.0f) + (row > 2 ? r2 : 0.0f);
-        s[tid] = p.A[(int64_t)q.hh * p.sA] * v;
+        const float su = g.A * v;
+        const float sT = __shfl(su, kHT - 1);
+        dl[tid] = dv;
+        s[tid] = su;
+        w[tid] = __expf(sT - su) * dv;
     }
     __syncthreads();
 }
 
 // ---------------------------------------------------------------------------
-// pass 1: chunk-local end state S = B^T diag(w) X (N x P) and decay e^(s_{T-1})
+// pass 1: chunk-local end state, as S^T = X^T diag(w) B (P x N; zero entering
+// state), stored [p][n], and the chunk decay e^(s_{T-1}).
 // ---------------------------------------------------------------------------
-template <typename T>
-__global__ __launch_bounds__(256) void head_state_kernel(HeadParams p) {
-    extern __shared__ float lds[];
+template <typename T, bool VEC>
+__device__ __forceinline__ void head_state_body(const HeadParams& p, const HeadTile& q, float* lds) {
     const int P = p.P, N = p.N, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const HeadLds o = head_lds(P, N, false);
-    float *dl = lds + o.dl, *s = lds + o.s, *sx = lds + o.sx, *sB = lds + o.sB;
-    const HeadTile q = head_tile(p);
-    head_stage<T>(p, q, dl, sx, sB, nullptr, s, false);
-    const float sT = s[kHT - 1];
-    const int ntiles = (N / 16) * (P / 16);
+    float *dl = lds + o.dl, *s = lds + o.s, *w = lds + o.w, *sx = lds + o.sx, *sB = lds + o.sB;
+    HeadRegs<T> g;
+    head_fetch<T, VEC>(p, q, false, g);
+    head_put<T, VEC>(p, q, g, dl, s, w, sx, sB, nullptr, kXLd, true);
+    const int ntiles = (N / 16) * (P / 16), i = lane & 15, j = lane >> 4;
     float* S = p.state + (((size_t)q.b * p.H + q.hh) * p.nchunks + q.c) * (size_t)N * P;
     for (int tile = wave; tile < ntiles; tile += 4) {   // uniform per wave
-        const int n0 = 16 * (tile / (P / 16)), p0 = 16 * (tile % (P / 16));
+        const int p0 = 16 * (tile / (N / 16)), n0 = 16 * (tile % (N / 16));
+        // k-group j of every MFMA covers steps u = 16 j .. 16 j + 15 in turn, so a lane reads
+        // 16 consecutive steps of its row: A[p][u] = X[u][p], B[u][n] = w_u B[u][n]
+        const float* xa = sx + (p0 + i) * kXLd + 16 * j;
+        const float* ba = sB + (n0 + i) * kXLd + 16 * j;
+        const float* wa = w + 16 * j;
         f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll 4
-        for (int kk = 0; kk < kHT / 4; ++kk) {
-            const int u = 4 * kk + (lane >> 4);
-            const float w = __expf(sT - s[u]) * dl[u];
-            const float a = sB[u * (N + 1) + n0 + (lane & 15)] * w;   // A[n][u] = B[u][n] w_u
-            const float bx = sx[(p0 + (lane & 15)) * kHPad + u];     // B[u][p] = X[u][p]
-            acc = mfma4(a, bx, acc);
-        }
-        // D[n][p]: register r of lane l holds n = n0 + 4 (l / 16) + r, p = p0 + l % 16
 #pragma unroll
-        for (int r = 0; r < 4; ++r) S[(size_t)(n0 + 4 * (lane >> 4) + r) * P + p0 + (lane & 15)] = acc[r];
+        for (int k4 = 0; k4 < 4; ++k4) {
+            const float4 a4 = *(const float4*)(xa + 4 * k4), b4 = *(const float4*)(ba + 4 * k4),
+                         w4 = *(const float4*)(wa + 4 * k4);
+            acc = mfma4(a4.x, b4.x * w4.x, acc);
+            acc = mfma4(a4.y, b4.y * w4.y, acc);
+            acc = mfma4(a4.z, b4.z * w4.z, acc);
+            acc = mfma4(a4.w, b4.w * w4.w, acc);
+        }
+        // D[p][n]: register r of lane l holds p = p0 + 4 (l / 16) + r, n = n0 + l % 16
+#pragma unroll
+        for (int r = 0; r < 4; ++r) S[(size_t)(p0 + 4 * (lane >> 4) + r) * N + n0 + (lane & 15)] = acc[r];
     }
-    if (threadIdx.x == 0) p.decay[((size_t)q.b * p.H + q.hh) * p.nchunks + q.c] = __expf(sT);
+    if (threadIdx.x == 0) p.decay[((size_t)q.b * p.H + q.hh) * p.nchunks + q.c] = __expf(s[kHT - 1]);
+}
+template <typename T>
+__global__ __launch_bounds__(256) void head_state_kernel(HeadParams p) {
+    extern __shared__ __align__(16) float lds[];
+    const HeadTile q = head_tile(p);
+    if (p.vx && p.vb && q.nval == kHT) head_state_body<T, true>(p, q, lds);   // uniform per block
+    else head_state_body<T, false>(p, q, lds);
 }
 
 // ---------------------------------------------------------------------------
-// pass 2: entering states.  One thread per (batch, head, n, p) element: walk the
-// chunks in order, H_in(c) = state entering chunk c, H_in(c+1) = decay_c H_in(c)
-// + S_c; the local states are overwritten with the entering states; the state
-// after the last chunk goes to h_last, and the entering states to the
-// checkpoints (B, D, nchunks, N) when requested.
+// pass 2: entering states.  One thread per (batch, head, p, n) element walks
+// the chunks in order: H_in(0) = h0, H_in(c+1) = decay_c H_in(c) + S_c.  The
+// entering states go to the checkpoints (B, D, nchunks, N) when requested,
+// else over the local states; the state after the last chunk to h_last.
 // ---------------------------------------------------------------------------
+constexpr int kChainGroup = 16;   // chunks whose loads are in flight together
 __global__ __launch_bounds__(256) void head_chain_kernel(HeadParams p) {
-    const int P = p.P, N = p.N;
+    const int P = p.P, N = p.N, NP = N * P, nch = p.nchunks;
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= (int64_t)p.B * p.H * N * P) return;
-    const int64_t bh = i / ((int64_t)N * P);
-    const int e = (int)(i - bh * N * P), n = e / P, pp = e - n * P;
+    if (i >= (int64_t)p.B * p.H * NP) return;
+    const int64_t bh = i / NP;
+    const int e = (int)(i - bh * NP), pp = e / N, n = e - pp * N;
     const int b = (int)(bh / p.H), hh = (int)(bh - (int64_t)b * p.H);
     const int64_t seq = (int64_t)b * p.H * P + (int64_t)hh * P + pp;   // channel row (b, d = h*P + p)
     float h = p.h0 ? p.h0[seq * N + n] : 0.0f;
-    float* S = p.state + (size_t)bh * p.nchunks * N * P + e;
-    const float* dec = p.decay + (size_t)bh * p.nchunks;
-    for (int c = 0; c < p.nchunks; ++c) {
-        const float loc = S[(size_t)c * N * P];
-        S[(size_t)c * N * P] = h;
-        if (p.ckpt) p.ckpt[(seq * p.nchunks + c) * N + n] = h;
-        h = fmaf(dec[c], h, loc);
+    const float* S = p.state + (size_t)bh * nch * NP + e;
+    const float* dec = p.decay + (size_t)bh * nch;
+    float* out = p.ckpt ? p.ckpt + seq * nch * N + n : p.state + (size_t)bh * nch * NP + e;
+    const int64_t os = p.ckpt ? N : NP;
+    for (int c0 = 0; c0 < nch; c0 += kChainGroup) {
+        float loc[kChainGroup], dc[kChainGroup];
+#pragma unroll
+        for (int j = 0; j < kChainGroup; ++j)
+            if (c0 + j < nch) {
+                loc[j] = S[(size_t)(c0 + j) * NP];
+                dc[j] = dec[c0 + j];
+            }
+#pragma unroll
+        for (int j = 0; j < kChainGroup; ++j)
+            if (c0 + j < nch) {
+                out[(c0 + j) * os] = h;
+                h = fmaf(dc[j], h, loc[j]);
+            }
     }
     if (p.h_last) p.h_last[seq * N + n] = h;
 }
 
 // ---------------------------------------------------------------------------
-// pass 3: outputs.  Wave w computes the 16 steps t = 16w .. 16w+15 of every p:
-//   row block of G = C B^T (16 x T), masked and scaled in registers to
-//   M[t][u] = G[t][u] e^(s_t - s_u) delta_u (u <= t), written to LDS and read back
-//   as A operands; Y = M X + (e^s C) H_in.
+// pass 3: outputs.  Each wave computes one block of 16 steps t = t0 .. t0+15 for
+// every p: the row block of G = C B^T up to the diagonal block, masked and
+// scaled in registers to M[t][u] = G[t][u] e^(s_t - s_u) delta_u (u <= t),
+// written to LDS and read back as A operands; Y = M X + (e^s C) H_in.
 // ---------------------------------------------------------------------------
-template <typename T>
-__global__ __launch_bounds__(256) void head_out_kernel(HeadParams p) {
-    extern __shared__ float lds[];
+template <typename T, bool VEC>
+__device__ __forceinline__ void head_out_body(const HeadParams& p, const HeadTile& q, float* lds) {
     const int P = p.P, N = p.N, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const HeadLds o = head_lds(P, N, true);
-    float *dl = lds + o.dl, *s = lds + o.s, *sx = lds + o.sx, *sB = lds + o.sB, *sC = lds + o.sC;
-    float* sH = lds + o.sH;   // H_in as [n][p], rows of P + 1
-    const HeadTile q = head_tile(p);
+    float *dl = lds + o.dl, *s = lds + o.s, *w = lds + o.w, *sx = lds + o.sx, *sB = lds + o.sB, *sC = lds + o.sC;
+    float* sH = lds + o.sH;   // H_in as [p][n]
+    const int ldn = ld_rows_i(N);
+    // entering state: from the checkpoints (rows of nchunks * N) or the chained state buffer
+    const int64_t row0 = (int64_t)q.b * p.H * P + (int64_t)q.hh * P;
+    const TileSrc<float> th =
+        p.ckpt ? TileSrc<float>{p.ckpt + (row0 * p.nchunks + q.c) * N, (int64_t)p.nchunks * N, P, N, P, N}
+               : TileSrc<float>{p.state + (((size_t)q.b * p.H + q.hh) * p.nchunks + q.c) * (size_t)N * P, N, P, N, P, N};
+    float vh[16];
+    tile_fetch<float, VEC>(th, vh);
     {
-        const float* Hin = p.state + (((size_t)q.b * p.H + q.hh) * p.nchunks + q.c) * (size_t)N * P;
-        for (int e = threadIdx.x; e < N * P; e += 256) sH[(e / P) * (P + 1) + e % P] = Hin[e];
+        HeadRegs<T> st;
+        head_fetch<T, VEC>(p, q, true, st);
+        tile_put<float, VEC>(th, vh, sH, ldn, false);
+        head_put<T, VEC>(p, q, st, dl, s, w, sx, sB, sC, ldn, false);
     }
-    head_stage<T>(p, q, dl, sx, sB, sC, s, true);
-    const int t0 = 16 * wave;
+    // row block of this wave, rotated with the chunk so that the causal work (row block rb
+    // needs columns u < 16 (rb + 1) only) spreads evenly over the SIMDs
+    const int rb = (wave + q.c) & 3, t0 = 16 * rb;
     if (t0 >= q.nval) return;   // whole waves past the end (no barrier follows)
-    // G rows t0.., all 64 columns: 4 column tiles, K = N
+    // G rows t0.., column tiles jt <= rb, K = N.  k-group j of every MFMA takes
+    // n = 16 nb + 4 j .. 16 nb + 4 j + 3 in turn, so a lane reads 4 consecutive states of a row.
+    const int i = lane & 15, j = lane >> 4;
     f4 g[4];
 #pragma unroll
-    for (int jt = 0; jt < 4; ++jt) {
-        g[jt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
-        for (int kk = 0; kk < N / 4; ++kk) {
-            const int n = 4 * kk + (lane >> 4);
-            const float a = sC[(t0 + (lane & 15)) * (N + 1) + n];      // A[t][n] = C[t][n]
-            const float bb = sB[(16 * jt + (lane & 15)) * (N + 1) + n]; // B[n][u] = B[u][n]
-            g[jt] = mfma4(a, bb, g[jt]);
+    for (int jt = 0; jt < 4; ++jt) g[jt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int nb = 0; nb < N / 16; ++nb) {
+        const float4 c4 = *(const float4*)&sC[(t0 + i) * ldn + 16 * nb + 4 * j];   // A[t][n] = C[t][n]
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) {
+            if (jt > rb) break;   // uniform
+            const float4 b4 = *(const float4*)&sB[(16 * jt + i) * ldn + 16 * nb + 4 * j];   // B[n][u] = B[u][n]
+            g[jt] = mfma4(c4.x, b4.x, g[jt]);
+            g[jt] = mfma4(c4.y, b4.y, g[jt]);
+            g[jt] = mfma4(c4.z, b4.z, g[jt]);
+            g[jt] = mfma4(c4.w, b4.w, g[jt]);
         }
     }
     // mask, decay and delta: register r of lane l holds t = t0 + 4 (l/16) + r, u = 16 jt + l % 16
-    float* Mw = lds + o.sM + wave * 16 * kHPad;   // this wave's rows of M
+    float* Mw = lds + o.sM + wave * 16 * kXLd;   // this wave's rows of M
 #pragma unroll
     for (int jt = 0; jt < 4; ++jt) {
+        if (jt > rb) break;   // uniform; columns past the diagonal block are never read
         const int u = 16 * jt + (lane & 15);
         const float su = s[u], du = dl[u];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int tr = 4 * (lane >> 4) + r, t = t0 + tr;
             const float m = u <= t ? g[jt][r] * __expf(s[t] - su) * du : 0.0f;
-            Mw[tr * kHPad + u] = m;
+            Mw[tr * kXLd + u] = m;
         }
     }
     __builtin_amdgcn_s_waitcnt(0xc07f);   // this wave's LDS writes done (lgkmcnt 0) before the reads below
     __builtin_amdgcn_wave_barrier();
-    const float es = __expf(s[t0 + (lane & 15)]);   // e^(s_t) for the A operand rows
+    const float es = __expf(s[t0 + i]);   // e^(s_t) for the A operand rows
+    const int tb = t0 + 4 * j;
+    const bool vy = p.vy && q.nval == kHT;   // uniform
+    const float* ma = Mw + i * kXLd + 4 * j;   // A[t][u] = M[t][u], u = 16 kb + 4 j + kk in turn
     for (int pt = 0; pt < P / 16; ++pt) {
         const int p0 = 16 * pt;
         f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-        // intra-chunk: K = T
-#pragma unroll 4
-        for (int kk = 0; kk < kHT / 4; ++kk) {
-            const int u = 4 * kk + (lane >> 4);
-            acc = mfma4(Mw[(lane & 15) * kHPad + u], sx[(p0 + (lane & 15)) * kHPad + u], acc);
-        }
-        // carried state: K = N
-        for (int kk = 0; kk < N / 4; ++kk) {
-            const int n = 4 * kk + (lane >> 4);
-            const float a = sC[(t0 + (lane & 15)) * (N + 1) + n] * es;   // e^(s_t) C[t][n]
-            acc = mfma4(a, sH[n * (P + 1) + p0 + (lane & 15)], acc);
-        }
-        // D[t][p]: lane l, register r: t = t0 + 4 (l/16) + r, p = p0 + l % 16
-        const int pp = p0 + (lane & 15), tb = t0 + 4 * (lane >> 4);
-        T* yrow = (T*)p.y + (int64_t)q.b * p.sy[0] + ((int64_t)q.hh * P + pp) * p.sy[1] + q.t0;
+        // intra-chunk: K = 16 (rb + 1) (M is zero past the diagonal block)
+        const float* xb = sx + (p0 + i) * kXLd + 4 * j;   // B[u][p] = X[u][p]
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            if (tb + r < q.nval) yrow[tb + r] = from_f32<T>(acc[r]);
+        for (int kb = 0; kb < 4; ++kb) {
+            if (kb > rb) break;   // uniform
+            const float4 a4 = *(const float4*)(ma + 16 * kb), b4 = *(const float4*)(xb + 16 * kb);
+            acc = mfma4(a4.x, b4.x, acc);
+            acc = mfma4(a4.y, b4.y, acc);
+            acc = mfma4(a4.z, b4.z, acc);
+            acc = mfma4(a4.w, b4.w, acc);
+        }
+        // carried state: K = N, n = 16 nb + 4 j + kk
+        for (int nb = 0; nb < N / 16; ++nb) {
+            const float4 c4 = *(const float4*)&sC[(t0 + i) * ldn + 16 * nb + 4 * j];   // e^(s_t) C[t][n]
+            const float4 h4 = *(const float4*)&sH[(p0 + i) * ldn + 16 * nb + 4 * j];   // B[n][p] = H_in[p][n]
+            acc = mfma4(c4.x * es, h4.x, acc);
+            acc = mfma4(c4.y * es, h4.y, acc);
+            acc = mfma4(c4.z * es, h4.z, acc);
+            acc = mfma4(c4.w * es, h4.w, acc);
+        }
+        // D[t][p]: lane l, register r: t = tb + r, p = p0 + l % 16
+        const int pp = p0 + i;
+        T* yrow = (T*)p.y + (int64_t)q.b * p.sy[0] + ((int64_t)q.hh * P + pp) * p.sy[1] + q.t0 + tb;
+        if (vy) {   // four consecutive steps in one store
+            if constexpr (sizeof(T) == 2) {
+                const uint32_t lo = (uint32_t)from_f32<T>(acc[0]) | ((uint32_t)from_f32<T>(acc[1]) << 16);
+                const uint32_t hi = (uint32_t)from_f32<T>(acc[2]) | ((uint32_t)from_f32<T>(acc[3]) << 16);
+                *(uint2*)yrow = make_uint2(lo, hi);
+            } else {
+                *(float4*)yrow = make_float4(acc[0], acc[1], acc[2], acc[3]);
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (tb + r < q.nval) yrow[r] = from_f32<T>(acc[r]);
+        }
     }
 }
+template <typename T>
+__global__ __launch_bounds__(256) void head_out_kernel(HeadParams p) {
+    extern __shared__ __align__(16) float lds[];
+    const HeadTile q = head_tile(p);
+    const bool hal = p.ckpt ? ((uintptr_t)p.ckpt & 15) == 0 : true;   // entering-state rows aligned
+    if (p.vx && p.vb && p.vc && hal && q.nval == kHT) head_out_body<T, true>(p, q, lds);   // uniform per block
+    else head_out_body<T, false>(p, q, lds);
+}
+
 
 // gdelta of the head form from the per-channel step-size gradients: the sum over
 // the head's P channels, in channel order.  gdc (B, D, L) fp32, out (B, H, L).
@@ -260,19 +454,25 @@ __global__ __launch_bounds__(64) void head_ga_kernel(const float* __restrict__ g
     out[hh] = acc;
 }
 
-hipError_t launch_head_fwd(const HeadParams& p, int dtype, hipStream_t st) {
+hipError_t launch_head_state(const HeadParams& p, int dtype, hipStream_t st) {
     if (p.P % 16 || p.P > 64 || p.N % 16 || p.N > 64) return hipErrorInvalidValue;
     const dim3 grid((unsigned)p.nchunks, (unsigned)p.H, (unsigned)p.B);
-    const size_t l1 = head_lds(p.P, p.N, false).total * sizeof(float), l3 = head_lds(p.P, p.N, true).total * sizeof(float);
-    if (dtype == 0) head_state_kernel<float><<<grid, 256, l1, st>>>(p);
-    else head_state_kernel<bf16_t><<<grid, 256, l1, st>>>(p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    const size_t lds = head_lds(p.P, p.N, false).total * sizeof(float);
+    if (dtype == 0) head_state_kernel<float><<<grid, 256, lds, st>>>(p);
+    else head_state_kernel<bf16_t><<<grid, 256, lds, st>>>(p);
+    return hipGetLastError();
+}
+hipError_t launch_head_chain(const HeadParams& p, hipStream_t st) {
     const int64_t n = (int64_t)p.B * p.H * p.N * p.P;
     head_chain_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(p);
-    if ((e = hipGetLastError()) != hipSuccess || !p.y) return e;
-    if (dtype == 0) head_out_kernel<float><<<grid, 256, l3, st>>>(p);
-    else head_out_kernel<bf16_t><<<grid, 256, l3, st>>>(p);
+    return hipGetLastError();
+}
+hipError_t launch_head_out(const HeadParams& p, int dtype, hipStream_t st) {
+    if (p.P % 16 || p.P > 64 || p.N % 16 || p.N > 64) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)p.nchunks, (unsigned)p.H, (unsigned)p.B);
+    const size_t lds = head_lds(p.P, p.N, true).total * sizeof(float);
+    if (dtype == 0) head_out_kernel<float><<<grid, 256, lds, st>>>(p);
+    else head_out_kernel<bf16_t><<<grid, 256, lds, st>>>(p);
     return hipGetLastError();
 }
 hipError_t launch_head_reduce(const float* gdc, void* gdelta, const float* ga_dn, float* gA, int B, int H, int P,

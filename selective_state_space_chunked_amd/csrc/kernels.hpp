@@ -192,8 +192,13 @@ struct HeadParams {
     void* y; float* h_last; float* ckpt;
     float* state; float* decay;
     int B, H, P, L, N, nchunks;
+    int vx, vb, vc, vy;   // 16-byte row loads of x, B, C and 4-step stores of y are aligned
 };
-hipError_t launch_head_fwd(const HeadParams& p, int dtype, hipStream_t st);
+// the three passes: chunk-local states (matrix cores), the chain over chunks,
+// the outputs (matrix cores; needs p.y)
+hipError_t launch_head_state(const HeadParams& p, int dtype, hipStream_t st);
+hipError_t launch_head_chain(const HeadParams& p, hipStream_t st);
+hipError_t launch_head_out(const HeadParams& p, int dtype, hipStream_t st);
 // gdelta (B,H,L) = sums over each head's channels of gdc (B,D,L) fp32; gA (H) =
 // sums of ga_dn (D,N) over each head's channels and states (null skips either)
 hipError_t launch_head_reduce(const float* gdc, void* gdelta, const float* ga_dn, float* gA, int B, int H, int P,

@@ -446,6 +446,27 @@ def test_every_forward_fits_the_static_scratch():
     assert 0 < worst <= cap
 
 
+def test_head_mode_noalloc_refuses_chunk_states_beyond_the_scratch():
+    """The per-head forward keeps 4 B D N ceil(L/64) + 4 B H ceil(L/64) bytes of chunk states; the
+    allocation-free forward takes them up to the static array's size and refuses more before any device
+    call (SSM_ERR_WORKSPACE)."""
+    cap = 32 * 1024 * 1024
+
+    def head(B_, H, P, L):
+        return sel_args(mode=B.SSM_HEAD_SCALAR, dtype=B.SSM_BF16, batch=B_, channels=H * P, length=L, state=16,
+                        head_dim=P)
+    for B_, H, P, L in ((8, 32, 64, 4096), (1, 2, 16, 65), (2, 4, 64, 1000)):
+        rc, n = ws_bytes(B.SSM_OP_SCAN_FWD, head(B_, H, P, L))
+        assert rc == 0, B.lib().ssm_last_error_detail()
+        nch = -(-L // 64)
+        assert n >= 4 * B_ * H * P * 16 * nch + 4 * B_ * H * nch
+    big = head(8, 32, 64, 4096)   # 67 MB of chunk states
+    o = B.ScanFwdOut(y=FAKE * 9, h_last=None, ckpt=None)
+    rc = B.lib().ssm_scan_fwd_noalloc(ctypes.byref(big), ctypes.byref(o), None)
+    assert rc == status("SSM_ERR_WORKSPACE")
+    assert ws_bytes(B.SSM_OP_SCAN_FWD, head(2, 4, 64, 1000))[1] <= cap
+
+
 # ---------------------------------------------------------------------------
 # strided views (ssm_layout) and the discretisation selector: host-side checks
 # ---------------------------------------------------------------------------
