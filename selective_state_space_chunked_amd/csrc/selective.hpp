@@ -198,6 +198,37 @@ __device__ __forceinline__ float zoh_coef_dA(float dl, float z, float a, float c
 // 1 / A for the ZOH coefficient (unused where A = 0: the series applies there)
 __device__ __forceinline__ float zoh_inv(float A) { return A != 0.0f ? 1.0f / A : 0.0f; }
 
+// LDS DMA: every lane of the wave loads 16 bytes from `src` straight into LDS
+// at wave_base + 16 * (lane in wave), with no VGPR in between; completion is
+// counted by vmcnt like any vector load.
+__device__ __forceinline__ void lds_dma16(const void* src, void* wave_base) {
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)wave_base, 16, 0, 0);
+}
+// Workgroup barrier for LDS traffic only: this wave's LDS operations complete,
+// then s_barrier.  Outstanding global loads, stores and LDS DMA keep running
+// (__syncthreads would first wait for every one of them to complete).
+__device__ __forceinline__ void lds_barrier() { __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+// 16-byte LDS store written as assembly.  The compiler cannot tell the LDS DMA
+// target from other shared arrays in this kernel and would make every LDS
+// store wait for all DMA in flight; these stores never touch the DMA target.
+// Completion is covered by the lgkmcnt(0) of lds_barrier.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void lds_store16(float* p, float x, float y, float z, float w) {
+    const uint32_t a = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) float*)p;
+    const f32x4 v = {x, y, z, w};
+    __asm__ volatile("ds_write_b128 %0, %1" ::"v"(a), "v"(v) : "memory");
+}
+constexpr int kWaitVm0 = 0x0f70;    // s_waitcnt vmcnt(0)
+constexpr int kWaitLgkm0 = 0xc07f;  // s_waitcnt lgkmcnt(0)
+__device__ __forceinline__ void unpack8_bf16(const uint4& w, float* v) {
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        v[2 * e] = __uint_as_float(ws[e] << 16);
+        v[2 * e + 1] = __uint_as_float(ws[e] & 0xffff0000u);
+    }
+}
+
 template <int KPL>
 __device__ __forceinline__ void read_run(const float* __restrict__ s, float (&v)[KPL]) {
 #pragma unroll
@@ -280,12 +311,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
         for (int nb = 0; nb < N; nb += NH) {
             const int ne = min(nb + NH, N);
             if constexpr (!PERD) {
-                __syncthreads();
+                lds_barrier();
                 stage_states<T, KPL, NT, NH>(sB, (const T*)p.Bm, b, t0, L, N, nb, ne, p.sBm[0],
                                              p.sBm[2], bcvec);
                 if (!SUMMARY)
                     stage_states<T, KPL, NT, NH>(sC, (const T*)p.C, b, t0, L, N, nb, ne, p.sC[0], p.sC[2], bcvec);
-                __syncthreads();
+                lds_barrier();
             }
             // the broadcasts for state n+1 are issued while state n runs (lane n+1's
             // carry does not change during step n)
@@ -362,6 +393,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
 // swaps, then over the 8 waves in LDS, and written as one partial per
 // 32-channel block; a second kernel adds the blocks in order.
 // SUMMARY: per segment, the composed adjoint map nu_start = Q nu_end + R.
+// bf16 streams with 16-step runs and 16 states: while a tile runs, the next
+// tile's delta, x and gy runs and its B and C rows are fetched into LDS by DMA
+// (no registers held), and its checkpoint into a register, so a tile starts
+// without waiting on HBM.
 // ---------------------------------------------------------------------------
 template <typename T, int KPL, int NT, bool SUMMARY, bool WA, int VAR>
 __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))) void sel_bwd_kernel(SelBwdParams p) {
@@ -377,6 +412,11 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
     // have per-channel gradients: no sum over channels, no LDS.
     constexpr int RB = ROWS / kPresum;
     __shared__ __align__(16) float red[(SUMMARY || PERD) ? 4 : 2 * 2 * RB * G::LDSW];
+    // next-tile prefetch: per wave [delta | x | gy][half run][lane], and the raw B, C rows [t][half]
+    constexpr bool PF = sizeof(T) == 2 && KPL == 16 && NT == 16 && !SUMMARY && !PERD;
+    static_assert(!PF || kBwdThreads == 2 * TILE, "one B row half per thread");
+    __shared__ __align__(16) uint4 pfs[PF ? (ROWS / 4) * 3 * 2 * 64 : 1];
+    __shared__ __align__(16) uint4 pfbc[PF ? 2 * 2 * TILE : 1];
 
     const int tid = threadIdx.x, lane = tid & 15, row = tid >> 4;
     const int b = blockIdx.y, g = blockIdx.z;
@@ -408,29 +448,84 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
     }
     const int tile0 = g * p.tiles_per_seg;
     const int tile1 = min(tile0 + p.tiles_per_seg, p.ntiles);
+    // prefetch (uniform): aligned rows; every tile but the last of the sequence is whole
+    const bool pf = PF && vec && bcvec;
+    uint4* pfw = pfs + (tid >> 6) * (3 * 2 * 64);   // this wave's slots
+    float hs_nx = 0.0f;                            // checkpoint of the next tile, one ahead
+    if (!SUMMARY && lane < N) hs_nx = p.ckpt[(seq * p.ntiles + (tile1 - 1)) * N + lane];
 
     for (int tile = tile1 - 1; tile >= tile0; --tile) {
         const int t0 = tile * TILE;
+        const bool have = pf && tile != tile1 - 1;   // this tile's streams are in LDS
         if constexpr (!PERD) {
-            __syncthreads();
-            if (!SUMMARY) stage_tile<T, KPL, NT, kBwdThreads>(sB, (const T*)p.Bm, b, t0, L, N, p.sBm[0], p.sBm[2], bcvec);
-            stage_tile<T, KPL, NT, kBwdThreads>(sC, (const T*)p.C, b, t0, L, N, p.sC[0], p.sC[2], bcvec);
-            __syncthreads();
+            if (PF && have) __builtin_amdgcn_s_waitcnt(kWaitVm0);   // this wave's DMA has landed
+            lds_barrier();
+            if (PF && have) {
+                // rows of the raw B (threads 0..TILE-1) and C tiles into [n][t'] layout
+                const int tt = tid & (TILE - 1);
+                const uint4* src = pfbc + (tid >= TILE ? 2 * TILE : 0) + 2 * tt;
+                float* dst = tid >= TILE ? sC : sB;
+                float v[16];
+                unpack8_bf16(src[0], v);
+                unpack8_bf16(src[1], v + 8);
+                const int base = (tt / KPL) * G::SEG + (tt % KPL);
+#pragma unroll
+                for (int n = 0; n < 16; ++n) dst[n * G::LDSW + base] = v[n];
+            } else {
+                if (!SUMMARY) stage_tile<T, KPL, NT, kBwdThreads>(sB, (const T*)p.Bm, b, t0, L, N, p.sBm[0], p.sBm[2], bcvec);
+                stage_tile<T, KPL, NT, kBwdThreads>(sC, (const T*)p.C, b, t0, L, N, p.sC[0], p.sC[2], bcvec);
+            }
+            lds_barrier();
+            if (PF && pf && tile > tile0) {   // B and C rows of the next tile: thread i, row i / 2, half i % 2
+                const int64_t tn = (int64_t)(t0 - TILE) + (tid >> 1);
+                const int h8 = 8 * (tid & 1);
+                lds_dma16((const T*)p.Bm + b * p.sBm[0] + tn * p.sBm[2] + h8, pfbc + (tid & ~63));
+                lds_dma16((const T*)p.C + b * p.sC[0] + tn * p.sC[2] + h8, pfbc + 2 * TILE + (tid & ~63));
+            }
         }
 
         const int tl = t0 + lane * KPL;
         const int nval = L - tl;
         // dx = delta x (Euler); the ZOH form keeps x itself
         float dl[KPL], dx[KPL], gyv[KPL];
+        uint4 xr0 = {0u, 0u, 0u, 0u}, xr1 = {0u, 0u, 0u, 0u};   // prefetched x run, kept for the delta gradient
         {
             float xv[KPL];
-            load_steps<T, KPL>(delta + tl, dl, nval, vec, p.stepf, dc);
-            if (nval >= KPL) {
-                load_run<KPL>(gyin + tl, gyv, vec);
-                if (!SUMMARY) load_run<KPL>(xin + tl, xv, vec);
+            if (PF && have) {
+                const int wl = tid & 63;
+                const uint4 d0 = pfw[wl], d1 = pfw[64 + wl], g0 = pfw[256 + wl], g1 = pfw[320 + wl];
+                xr0 = pfw[128 + wl];
+                xr1 = pfw[192 + wl];
+                unpack8_bf16(d0, dl);
+                unpack8_bf16(d1, dl + 8);
+                unpack8_bf16(g0, gyv);
+                unpack8_bf16(g1, gyv + 8);
+                unpack8_bf16(xr0, xv);
+                unpack8_bf16(xr1, xv + 8);
+                if (p.stepf.bias != nullptr || p.stepf.softplus) {   // uniform
+                    const float bias = p.stepf.bias ? p.stepf.bias[dc] : 0.0f;
+#pragma unroll
+                    for (int j = 0; j < KPL; ++j) dl[j] = step_xform(dl[j], bias, p.stepf.softplus);
+                }
             } else {
-                load_run_masked<T, KPL>(gyin + tl, gyv, nval);
-                if (!SUMMARY) load_run_masked<T, KPL>(xin + tl, xv, nval);
+                load_steps<T, KPL>(delta + tl, dl, nval, vec, p.stepf, dc);
+                if (nval >= KPL) {
+                    load_run<KPL>(gyin + tl, gyv, vec);
+                    if (!SUMMARY) load_run<KPL>(xin + tl, xv, vec);
+                } else {
+                    load_run_masked<T, KPL>(gyin + tl, gyv, nval);
+                    if (!SUMMARY) load_run_masked<T, KPL>(xin + tl, xv, nval);
+                }
+            }
+            if (PF && pf && tile > tile0) {   // this lane's runs of the next tile
+                __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // the slots above have been read
+                const int tn = tl - TILE;
+                lds_dma16(delta + tn, pfw);
+                lds_dma16(delta + tn + 8, pfw + 64);
+                lds_dma16(xin + tn, pfw + 128);
+                lds_dma16(xin + tn + 8, pfw + 192);
+                lds_dma16(gyin + tn, pfw + 256);
+                lds_dma16(gyin + tn + 8, pfw + 320);
             }
             // rows past D contribute nothing to the sums over channels
             const float live = act ? 1.0f : 0.0f;
@@ -443,8 +538,8 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
         float dsum = 0.0f;
 #pragma unroll
         for (int j = 0; j < KPL; ++j) dsum += dl[j];
-        float hs = 0.0f;
-        if (!SUMMARY && lane < N) hs = p.ckpt[(seq * p.ntiles + tile) * N + lane];
+        const float hs = hs_nx;
+        if (!SUMMARY && lane < N && tile > tile0) hs_nx = p.ckpt[(seq * p.ntiles + tile - 1) * N + lane];
 
         float Gd[KPL], Sb[KPL];
 #pragma unroll
@@ -586,7 +681,13 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
                     const int rb = w * GRP + (q % GRP);
                     float* rB = buf + rb * G::LDSW + lane * G::SEG + (q / GRP) * CNT;
                     float* rC = rB + RB * G::LDSW;
-                    if constexpr (CNT % 4 == 0) {
+                    if constexpr (PF) {
+#pragma unroll
+                        for (int k = 0; k < CNT / 4; ++k) {
+                            lds_store16(rB + 4 * k, pB[4 * k], pB[4 * k + 1], pB[4 * k + 2], pB[4 * k + 3]);
+                            lds_store16(rC + 4 * k, pC[4 * k], pC[4 * k + 1], pC[4 * k + 2], pC[4 * k + 3]);
+                        }
+                    } else if constexpr (CNT % 4 == 0) {
 #pragma unroll
                         for (int k = 0; k < CNT / 4; ++k) {
                             *reinterpret_cast<float4*>(rB + 4 * k) =
@@ -607,7 +708,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
                 if (wantB || wantC) {
                     // the other buffer was last read before the previous state's barrier, so
                     // this single barrier orders both the writes above and the reads below
-                    __syncthreads();
+                    lds_barrier();
                     // one output per thread; each half-wave takes 8 lane runs x 4 steps, whose
                     // words (run * (KPL + 4) + step) fall in 32 distinct banks
                     for (int o = tid; o < 2 * TILE; o += kBwdThreads) {
@@ -642,8 +743,14 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
                     for (int j = 0; j < KPL; ++j) v[j] = Gd[j] * step_xform_grad(dl[j], p.stepf.softplus);
                 } else {
                     float xv[KPL];
-                    if (nval >= KPL) load_run<KPL>(xin + tl, xv, vec);
-                    else load_run_masked<T, KPL>(xin + tl, xv, nval);
+                    if (PF && have) {
+                        unpack8_bf16(xr0, xv);
+                        unpack8_bf16(xr1, xv + 8);
+                    } else if (nval >= KPL) {
+                        load_run<KPL>(xin + tl, xv, vec);
+                    } else {
+                        load_run_masked<T, KPL>(xin + tl, xv, nval);
+                    }
 #pragma unroll
                     for (int j = 0; j < KPL; ++j)
                         v[j] = fmaf(xv[j], Sb[j], Gd[j]) * step_xform_grad(dl[j], p.stepf.softplus);
