@@ -127,15 +127,23 @@ def profile_kernels(fn, reps=5, cap=8192):
 
 
 def time_steps(step, steps, warmup):
+    import gc
     import torch
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        step()
-    torch.cuda.synchronize()
-    return (time.perf_counter() - t0) / steps * 1e3
+    # no garbage-collection pause of the interpreter inside the timed region
+    gc.collect()
+    gc.disable()
+    try:
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            step()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    finally:
+        gc.enable()
+    return (t1 - t0) / steps * 1e3
 
 
 def to_dev(arr, bf16=False):
@@ -635,6 +643,10 @@ def main():
             ["impulse", "output-sens", "sens-rows", "complex", "complex-dense", "complex-rtrl", "pd", "pd-ste", "dense",
              "head", "real-small"]
         for w in todo:
+            # each workload starts from an empty allocator cache: blocks cached by the previous
+            # workload's differently sized tensors otherwise fragment the next one's allocations
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
             if w == "impulse":
                 others[w] = summarize(w_impulse(args.steps, args.warmup))
             elif w == "output-sens":
