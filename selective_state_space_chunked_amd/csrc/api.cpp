@@ -707,7 +707,12 @@ int scan_bwd_impl(const ssm_scan_args* a, const ssm_scan_bwd_in* in, const ssm_s
     }
     Carve cv(nullptr);
     if (p.mode == SSM_HEAD_SCALAR) {
-        // the exact tiled adjoint of the diagonal kernels, with delta and A one per head
+        // the exact tiled adjoint of the diagonal kernels, with delta and A one per head, on
+        // 256-step tiles (16-step lane runs) that start at every fourth 64-step checkpoint
+        ScanPlan pb = p;
+        pb.T = 256;
+        pb.kpl = 16;
+        pb.nchunks = (int)cdiv(p.L, 256);
         struct L2 {
             float* ckpt = nullptr;
             HeadFwdLayout fwd;
@@ -719,7 +724,7 @@ int scan_bwd_impl(const ssm_scan_args* a, const ssm_scan_bwd_in* in, const ssm_s
                 l->ckpt = c.take<float>((size_t)p.B * p.D * p.nchunks * p.N);
                 head_fwd_layout(p, c, &l->fwd);
             }
-            sel_bwd_layout(p, true, wB, wC, wA, false, c, &l->sb);
+            sel_bwd_layout(pb, true, wB, wC, wA, false, c, &l->sb);
             if (wD) l->gdc = c.take<float>((size_t)p.B * p.D * p.L);
             if (wA) l->gadn = c.take<float>((size_t)p.D * p.N);
         };
@@ -743,7 +748,8 @@ int scan_bwd_impl(const ssm_scan_args* a, const ssm_scan_bwd_in* in, const ssm_s
         q.partB = l.sb.partB; q.partC = l.sb.partC; q.partA = l.sb.partA;
         q.segQ = l.sb.segQ; q.segR = l.sb.segR;
         q.B = (int)p.B; q.D = (int)p.D; q.L = (int)p.L; q.N = (int)p.N;
-        q.ntiles = p.nchunks; q.tiles_per_seg = l.sb.tps; q.G = l.sb.G;
+        q.ntiles = pb.nchunks; q.tiles_per_seg = l.sb.tps; q.G = l.sb.G;
+        q.ckpt_tiles = p.nchunks; q.ckpt_every = 4;
         q.vec = sel_vec(p, {a->delta, a->x, in->gy, g->gx, l.gdc}, {SSM_V_DELTA, SSM_V_X, SSM_V_GY, SSM_V_GX});
         q.stepf = StepXform{nullptr, 0};
         copy_strides(q.sdelta, p, SSM_V_DELTA); copy_strides(q.sx, p, SSM_V_X); copy_strides(q.sgy, p, SSM_V_GY);
@@ -756,11 +762,11 @@ int scan_bwd_impl(const ssm_scan_args* a, const ssm_scan_bwd_in* in, const ssm_s
         q.bc_vec = sel_bc_vec(p, a->Bm, a->C);
         q.var = kVarEuler;
         if (l.sb.G > 1) {
-            SSM_LAUNCH(launch_sel_bwd(q, p.dtype, p.kpl, true, st), "head backward summary");
+            SSM_LAUNCH(launch_sel_bwd(q, p.dtype, pb.kpl, true, st), "head backward summary");
             SSM_LAUNCH(launch_seg_combine_rev(l.sb.segQ, l.sb.segR, in->gh_last, l.sb.nu, (int)(p.B * p.D), l.sb.G,
                                               (int)p.N, st), "segment combine (reverse)");
         }
-        SSM_LAUNCH(launch_sel_bwd(q, p.dtype, p.kpl, false, st), "head backward");
+        SSM_LAUNCH(launch_sel_bwd(q, p.dtype, pb.kpl, false, st), "head backward");
         if (g->gBm || g->gC)
             SSM_LAUNCH(launch_reduce_parts_btn(g->gBm ? l.sb.partB : nullptr, g->gC ? l.sb.partC : nullptr,
                                                (int)cdiv(p.D, sel_bwd_rows()), (int)p.B, (int)p.N, (int)p.L, g->gBm,

@@ -61,6 +61,8 @@ struct SelBwdParams {
     float* segQ; float* segR;    // summary pass outputs (B,D,G,N)
     StepXform stepf;
     int B, D, L, N, ntiles, tiles_per_seg, G, vec;
+    // checkpoints of tile k at index k * ckpt_every of ckpt_tiles per sequence (0: ntiles, 1)
+    int ckpt_tiles = 0, ckpt_every = 1;
 };
 struct SensParams {
     const void* delta; const float* A; const void* Bm; const void* C;

@@ -452,7 +452,8 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
     const bool pf = PF && vec && bcvec;
     uint4* pfw = pfs + (tid >> 6) * (3 * 2 * 64);   // this wave's slots
     float hs_nx = 0.0f;                            // checkpoint of the next tile, one ahead
-    if (!SUMMARY && lane < N) hs_nx = p.ckpt[(seq * p.ntiles + (tile1 - 1)) * N + lane];
+    const size_t ckt = p.ckpt_tiles ? (size_t)p.ckpt_tiles : (size_t)p.ntiles;
+    if (!SUMMARY && lane < N) hs_nx = p.ckpt[(seq * ckt + (size_t)(tile1 - 1) * p.ckpt_every) * N + lane];
 
     for (int tile = tile1 - 1; tile >= tile0; --tile) {
         const int t0 = tile * TILE;
@@ -539,7 +540,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
 #pragma unroll
         for (int j = 0; j < KPL; ++j) dsum += dl[j];
         const float hs = hs_nx;
-        if (!SUMMARY && lane < N && tile > tile0) hs_nx = p.ckpt[(seq * p.ntiles + tile - 1) * N + lane];
+        if (!SUMMARY && lane < N && tile > tile0) hs_nx = p.ckpt[(seq * ckt + (size_t)(tile - 1) * p.ckpt_every) * N + lane];
 
         float Gd[KPL], Sb[KPL];
 #pragma unroll
