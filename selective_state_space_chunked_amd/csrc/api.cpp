@@ -719,13 +719,17 @@ int scan_bwd_impl(const ssm_scan_args* a, const ssm_scan_bwd_in* in, const ssm_s
             SelBwdLayout sb;
             float *gdc = nullptr, *gadn = nullptr;
         };
+        // gdelta: sums over groups of channels inside the kernel when a head's channels tile the
+        // workgroup's rows (P a multiple or a divisor of them), else per channel
+        const int rows = sel_bwd_rows();
+        const int gs = (p.P % rows == 0) ? rows : (rows % p.P == 0 ? (int)p.P : 0);
         auto layout = [&](Carve& c, bool have, bool wB, bool wC, bool wA, bool wD, L2* l) {
             if (!have) {
                 l->ckpt = c.take<float>((size_t)p.B * p.D * p.nchunks * p.N);
                 head_fwd_layout(p, c, &l->fwd);
             }
             sel_bwd_layout(pb, true, wB, wC, wA, false, c, &l->sb);
-            if (wD) l->gdc = c.take<float>((size_t)p.B * p.D * p.L);
+            if (wD) l->gdc = c.take<float>((size_t)p.B * (gs ? p.D / gs : p.D) * p.L);
             if (wA) l->gadn = c.take<float>((size_t)p.D * p.N);
         };
         L2 sizing;
@@ -744,7 +748,12 @@ int scan_bwd_impl(const ssm_scan_args* a, const ssm_scan_bwd_in* in, const ssm_s
         SelBwdParams q{};
         q.delta = a->delta; q.x = a->x; q.A = a->A; q.Bm = a->Bm; q.C = a->C;
         q.gy = in->gy; q.gh_last = in->gh_last; q.ckpt = ckpt; q.nu_in = l.sb.nu;
-        q.gdelta = l.gdc; q.gx = g->gx; q.gh0 = g->gh0;
+        if (gs) {
+            q.gdgrp = l.gdc; q.gdgs = gs;
+        } else {
+            q.gdelta = l.gdc;
+        }
+        q.gx = g->gx; q.gh0 = g->gh0;
         q.partB = l.sb.partB; q.partC = l.sb.partC; q.partA = l.sb.partA;
         q.segQ = l.sb.segQ; q.segR = l.sb.segR;
         q.B = (int)p.B; q.D = (int)p.D; q.L = (int)p.L; q.N = (int)p.N;
@@ -774,9 +783,9 @@ int scan_bwd_impl(const ssm_scan_args* a, const ssm_scan_bwd_in* in, const ssm_s
                        "reduce gB gC");
         if (g->gA)
             SSM_LAUNCH(launch_reduce_parts_dn(l.sb.partA, (int)p.B, l.sb.G, (int)p.D, (int)p.N, l.gadn, st), "reduce gA");
-        if (g->gdelta || g->gA)
-            SSM_LAUNCH(launch_head_reduce(l.gdc, g->gdelta, l.gadn, g->gA, (int)p.B, (int)p.H, (int)p.P, (int)p.N,
-                                          (int)p.L, p.dtype, st),
+        if (g->gdelta || g->gA)   // gdelta: the head's P / gs group sums (or P channels)
+            SSM_LAUNCH(launch_head_reduce(l.gdc, g->gdelta, l.gadn, g->gA, (int)p.B, (int)p.H,
+                                          gs ? (int)p.P / gs : (int)p.P, (int)p.N, (int)p.L, p.dtype, st, (int)p.P),
                        "head sums of gdelta, gA");
         return ok();
     }

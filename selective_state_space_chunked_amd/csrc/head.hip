@@ -430,8 +430,9 @@ __global__ __launch_bounds__(256) void head_out_kernel(HeadParams p) {
 }
 
 
-// gdelta of the head form from the per-channel step-size gradients: the sum over
-// the head's P channels, in channel order.  gdc (B, D, L) fp32, out (B, H, L).
+// gdelta of the head form: the sum of the head's P rows of gdc (per-channel
+// step-size gradients, or sums over groups of its channels), in order.
+// gdc (B, H * P, L) fp32, out (B, H, L).
 template <typename T>
 __global__ __launch_bounds__(256) void head_gdelta_kernel(const float* __restrict__ gdc, T* __restrict__ out, int B,
                                                           int H, int P, int L) {
@@ -475,14 +476,14 @@ hipError_t launch_head_out(const HeadParams& p, int dtype, hipStream_t st) {
     else head_out_kernel<bf16_t><<<grid, 256, lds, st>>>(p);
     return hipGetLastError();
 }
-hipError_t launch_head_reduce(const float* gdc, void* gdelta, const float* ga_dn, float* gA, int B, int H, int P,
-                              int N, int L, int dtype, hipStream_t st) {
+hipError_t launch_head_reduce(const float* gdc, void* gdelta, const float* ga_dn, float* gA, int B, int H, int R,
+                              int N, int L, int dtype, hipStream_t st, int P) {
     if (gdelta) {
         const int64_t n = (int64_t)B * H * L;
         if (dtype == 0)
-            head_gdelta_kernel<float><<<(unsigned)((n + 255) / 256), 256, 0, st>>>(gdc, (float*)gdelta, B, H, P, L);
+            head_gdelta_kernel<float><<<(unsigned)((n + 255) / 256), 256, 0, st>>>(gdc, (float*)gdelta, B, H, R, L);
         else
-            head_gdelta_kernel<bf16_t><<<(unsigned)((n + 255) / 256), 256, 0, st>>>(gdc, (bf16_t*)gdelta, B, H, P, L);
+            head_gdelta_kernel<bf16_t><<<(unsigned)((n + 255) / 256), 256, 0, st>>>(gdc, (bf16_t*)gdelta, B, H, R, L);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
