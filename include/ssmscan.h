@@ -235,10 +235,10 @@ typedef struct {
      *   a_t = exp(delta[b,h,t] * A[h]),  h_t[d,n] = a_t h_{t-1}[d,n] + delta[b,h,t] x[b,d,t] Bm[b,t,n],
      *   y[b,d,t] = sum_n C[b,t,n] h_t[d,n].
      * Tensors: delta (B,H,L) dtype, x (B,D,L) dtype, A (H) f32, Bm, C (B,L,N)
-     * dtype (shared by the channels), h0 (B,D,N); state N in {16, 32, 48, 64}
-     * for the forward, 16 for the backward; chunk_len 0 or 64.  The forward
-     * runs the chunked matrix form on the matrix cores; the backward the exact
-     * tiled adjoint of the diagonal kernels.  Gradients: gdelta
+     * dtype (shared by the channels), h0 (B,D,N); state N in {16, 32, 48, 64};
+     * chunk_len 0 or 64.  Forward and backward run the chunked matrix form on
+     * the matrix cores (the backward is its exact adjoint, from the 64-step
+     * checkpoints or a recompute of them).  Gradients: gdelta
      * (B,H,L) dtype, gx (B,D,L), gA (H) f32, gBm, gC (B,L,N), gh0.  Views:
      * SSM_V_DELTA is (B,H,L), SSM_V_A (H); Bm and C are shared by the channels.
      * No step-size transform, no ZOH.  Other modes: 0. */

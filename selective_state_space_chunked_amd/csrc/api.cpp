@@ -269,9 +269,6 @@ int validate_scan_args(const ssm_scan_args* a, ScanPlan* pl, int sel_default_T =
                         (long long)a->state);
         if (entry != E_FWD && entry != E_BWD)
             return fail(SSM_ERR_UNSUPPORTED, "SSM_HEAD_SCALAR supports ssm_scan_fwd and ssm_scan_bwd");
-        if (entry == E_BWD && a->state != 16)
-            return fail(SSM_ERR_UNSUPPORTED, "the SSM_HEAD_SCALAR backward takes state 16 (got %lld)",
-                        (long long)a->state);
         pl->P = a->head_dim;
         pl->H = a->channels / a->head_dim;
     } else if (a->head_dim != 0) {
@@ -707,86 +704,76 @@ int scan_bwd_impl(const ssm_scan_args* a, const ssm_scan_bwd_in* in, const ssm_s
     }
     Carve cv(nullptr);
     if (p.mode == SSM_HEAD_SCALAR) {
-        // the exact tiled adjoint of the diagonal kernels, with delta and A one per head, on
-        // 256-step tiles (16-step lane runs) that start at every fourth 64-step checkpoint
-        ScanPlan pb = p;
-        pb.T = 256;
-        pb.kpl = 16;
-        pb.nchunks = (int)cdiv(p.L, 256);
+        // the adjoint of the matrix form: chunk sums of the adjoint (the state pass on gy and C),
+        // their reverse chain, then one workgroup per (chunk, head, batch); gB, gC and gA add
+        // per-head terms in head order
         struct L2 {
             float* ckpt = nullptr;
             HeadFwdLayout fwd;
-            SelBwdLayout sb;
-            float *gdc = nullptr, *gadn = nullptr;
+            float *gstate = nullptr, *decay = nullptr, *partB = nullptr, *partC = nullptr, *partA = nullptr;
         };
-        // gdelta: sums over groups of channels inside the kernel when a head's channels tile the
-        // workgroup's rows (P a multiple or a divisor of them), else per channel
-        const int rows = sel_bwd_rows();
-        const int gs = (p.P % rows == 0) ? rows : (rows % p.P == 0 ? (int)p.P : 0);
-        auto layout = [&](Carve& c, bool have, bool wB, bool wC, bool wA, bool wD, L2* l) {
+        const size_t hbnl = (size_t)p.H * p.B * p.N * p.L;
+        auto layout = [&](Carve& c, bool have, bool wB, bool wC, bool wA, L2* l) {
             if (!have) {
                 l->ckpt = c.take<float>((size_t)p.B * p.D * p.nchunks * p.N);
                 head_fwd_layout(p, c, &l->fwd);
             }
-            sel_bwd_layout(pb, true, wB, wC, wA, false, c, &l->sb);
-            if (wD) l->gdc = c.take<float>((size_t)p.B * (gs ? p.D / gs : p.D) * p.L);
-            if (wA) l->gadn = c.take<float>((size_t)p.D * p.N);
+            l->gstate = c.take<float>((size_t)p.B * p.D * p.nchunks * p.N);
+            l->decay = c.take<float>((size_t)p.B * p.H * p.nchunks);
+            if (wB) l->partB = c.take<float>(hbnl);
+            if (wC) l->partC = c.take<float>(hbnl);
+            if (wA) l->partA = c.take<float>((size_t)p.H * p.B * p.nchunks);
         };
         L2 sizing;
-        layout(cv, false, true, true, true, true, &sizing);
+        layout(cv, false, true, true, true, &sizing);
         if (need_only) { *need_only = cv.off; return ok(); }
         if ((rc = check_ws(ws, ws_bytes, cv.off))) return rc;
         Carve real(ws);
         L2 l;
-        layout(real, in->ckpt != nullptr, g->gBm != nullptr, g->gC != nullptr, g->gA != nullptr, g->gdelta != nullptr,
-               &l);
+        layout(real, in->ckpt != nullptr, g->gBm != nullptr, g->gC != nullptr, g->gA != nullptr, &l);
         const float* ckpt = in->ckpt;
         if (!ckpt) {
             if ((rc = run_head_fwd(a, p, l.fwd, nullptr, nullptr, l.ckpt, st))) return rc;
             ckpt = l.ckpt;
         }
-        SelBwdParams q{};
-        q.delta = a->delta; q.x = a->x; q.A = a->A; q.Bm = a->Bm; q.C = a->C;
-        q.gy = in->gy; q.gh_last = in->gh_last; q.ckpt = ckpt; q.nu_in = l.sb.nu;
-        if (gs) {
-            q.gdgrp = l.gdc; q.gdgs = gs;
-        } else {
-            q.gdelta = l.gdc;
-        }
-        q.gx = g->gx; q.gh0 = g->gh0;
-        q.partB = l.sb.partB; q.partC = l.sb.partC; q.partA = l.sb.partA;
-        q.segQ = l.sb.segQ; q.segR = l.sb.segR;
-        q.B = (int)p.B; q.D = (int)p.D; q.L = (int)p.L; q.N = (int)p.N;
-        q.ntiles = pb.nchunks; q.tiles_per_seg = l.sb.tps; q.G = l.sb.G;
-        q.ckpt_tiles = p.nchunks; q.ckpt_every = 4;
-        q.vec = sel_vec(p, {a->delta, a->x, in->gy, g->gx, l.gdc}, {SSM_V_DELTA, SSM_V_X, SSM_V_GY, SSM_V_GX});
-        q.stepf = StepXform{nullptr, 0};
+        const int64_t e16 = 16 / (int64_t)p.esz;
+        auto al = [](const void* ptr, int64_t bytes) { return ((uintptr_t)ptr % (uintptr_t)bytes) == 0; };
+        // Q_c = C^T diag(e^s) dY for every chunk: the state pass with x = gy, B = C, weights e^(s_u)
+        HeadParams hs{};
+        hs.delta = a->delta; hs.x = in->gy; hs.A = a->A; hs.Bm = a->C; hs.C = a->C;
+        copy_strides(hs.sdelta, p, SSM_V_DELTA); copy_strides(hs.sx, p, SSM_V_GY);
+        copy_strides(hs.sBm, p, SSM_V_C); copy_strides(hs.sC, p, SSM_V_C);
+        hs.sA = p.v.s[SSM_V_A][0];
+        hs.state = l.gstate; hs.decay = l.decay;
+        hs.B = (int)p.B; hs.H = (int)p.H; hs.P = (int)p.P; hs.L = (int)p.L; hs.N = (int)p.N; hs.nchunks = p.nchunks;
+        hs.vx = al(in->gy, 16) && hs.sx[0] % e16 == 0 && hs.sx[1] % e16 == 0;
+        hs.vb = al(a->C, 16) && hs.sBm[0] % e16 == 0 && hs.sBm[2] % e16 == 0;
+        hs.bstate = 1;
+        HeadBwdParams q{};
+        q.delta = a->delta; q.x = a->x; q.A = a->A; q.Bm = a->Bm; q.C = a->C; q.gy = in->gy;
+        q.ckpt = ckpt; q.gh_last = in->gh_last;
         copy_strides(q.sdelta, p, SSM_V_DELTA); copy_strides(q.sx, p, SSM_V_X); copy_strides(q.sgy, p, SSM_V_GY);
-        copy_strides(q.sgx, p, SSM_V_GX);
-        q.sgdelta[0] = p.D * p.L; q.sgdelta[1] = p.L;   // per-channel gdelta, fp32, dense
-        q.gdelta_f32 = 1;
+        copy_strides(q.sgx, p, SSM_V_GX); copy_strides(q.sgdelta, p, SSM_V_GDELTA);
         copy_strides(q.sBm, p, SSM_V_BM); copy_strides(q.sC, p, SSM_V_C);
-        q.sA = p.v.s[SSM_V_A][0]; q.sAn = 0;             // one A per head, the same for every state
-        q.dgrp = (int)p.P; q.agrp = (int)p.P;
-        q.bc_vec = sel_bc_vec(p, a->Bm, a->C);
-        q.var = kVarEuler;
-        if (l.sb.G > 1) {
-            SSM_LAUNCH(launch_sel_bwd(q, p.dtype, pb.kpl, true, st), "head backward summary");
-            SSM_LAUNCH(launch_seg_combine_rev(l.sb.segQ, l.sb.segR, in->gh_last, l.sb.nu, (int)(p.B * p.D), l.sb.G,
-                                              (int)p.N, st), "segment combine (reverse)");
-        }
-        SSM_LAUNCH(launch_sel_bwd(q, p.dtype, pb.kpl, false, st), "head backward");
+        q.sA = p.v.s[SSM_V_A][0];
+        q.gstate = l.gstate; q.decay = l.decay;
+        q.gx = g->gx; q.gdelta = g->gdelta; q.gh0 = g->gh0;
+        q.partB = l.partB; q.partC = l.partC; q.partA = l.partA;
+        q.B = (int)p.B; q.H = (int)p.H; q.P = (int)p.P; q.L = (int)p.L; q.N = (int)p.N; q.nchunks = p.nchunks;
+        q.vx = al(a->x, 16) && q.sx[0] % e16 == 0 && q.sx[1] % e16 == 0;
+        q.vgy = hs.vx;
+        q.vb = al(a->Bm, 16) && q.sBm[0] % e16 == 0 && q.sBm[2] % e16 == 0;
+        q.vc = hs.vb;
+        SSM_LAUNCH(launch_head_state(hs, p.dtype, st), "head backward chunk sums (matrix cores)");
+        SSM_LAUNCH(launch_head_rchain(q, st), "head backward chain over the chunks");
+        SSM_LAUNCH(launch_head_bwd(q, p.dtype, st), "head backward (matrix cores)");
         if (g->gBm || g->gC)
-            SSM_LAUNCH(launch_reduce_parts_btn(g->gBm ? l.sb.partB : nullptr, g->gC ? l.sb.partC : nullptr,
-                                               (int)cdiv(p.D, sel_bwd_rows()), (int)p.B, (int)p.N, (int)p.L, g->gBm,
+            SSM_LAUNCH(launch_reduce_parts_btn(l.partB, l.partC, (int)p.H, (int)p.B, (int)p.N, (int)p.L, g->gBm,
                                                g->gC, p.dtype, st),
-                       "reduce gB gC");
+                       "gB gC: sums over the heads");
         if (g->gA)
-            SSM_LAUNCH(launch_reduce_parts_dn(l.sb.partA, (int)p.B, l.sb.G, (int)p.D, (int)p.N, l.gadn, st), "reduce gA");
-        if (g->gdelta || g->gA)   // gdelta: the head's P / gs group sums (or P channels)
-            SSM_LAUNCH(launch_head_reduce(l.gdc, g->gdelta, l.gadn, g->gA, (int)p.B, (int)p.H,
-                                          gs ? (int)p.P / gs : (int)p.P, (int)p.N, (int)p.L, p.dtype, st, (int)p.P),
-                       "head sums of gdelta, gA");
+            SSM_LAUNCH(launch_head_sum_rows(l.partA, g->gA, (int)p.H, (int)(p.B * p.nchunks), st),
+                       "gA: sums over batch rows and chunks");
         return ok();
     }
     if (p.mode == SSM_REAL_SELECTIVE) {

@@ -59,7 +59,8 @@ __host__ __device__ inline HeadLds head_lds(int P, int N, bool out) {
 struct HeadTile {
     int b, hh, c, t0, nval;   // batch row, head, chunk, first step, steps in the chunk
 };
-__device__ __forceinline__ HeadTile head_tile(const HeadParams& p) {
+template <typename Prm>   // HeadParams or HeadBwdParams: grid (chunk, head, batch)
+__device__ __forceinline__ HeadTile head_tile(const Prm& p) {
     HeadTile q;
     q.c = blockIdx.x;
     q.hh = blockIdx.y;
@@ -84,7 +85,7 @@ __device__ __forceinline__ void unpack16(const uint4& r, float (&f)[4]) {   // 4
 
 // An R x K tile (row r at base + r * rs, K contiguous elements; R * K <= 4096,
 // K a multiple of 16) moves to LDS as fp32, dst[r * ld + k] (dst[k * ld + r]
-// when tr), zero outside rows < vr and columns < vk.  Whole tiles with 16-byte
+// when tr), zero outside rows < vr and columns < vk, by 256 threads (tid < 256).  Whole tiles with 16-byte
 // aligned rows (VEC) go in two steps: tile_fetch issues a thread's 16-byte
 // loads into 16 registers, so that the loads of several tiles are in flight
 // together, and tile_put unpacks and writes them.  Otherwise tile_put loads
@@ -103,7 +104,7 @@ struct TileSrc {
 __device__ __forceinline__ int tile_row(int i, float inv) { return (int)(((float)i + 0.5f) * inv); }
 
 template <typename T, bool VEC>
-__device__ __forceinline__ void tile_fetch(const TileSrc<T>& ts, float (&v)[16]) {
+__device__ __forceinline__ void tile_fetch(const TileSrc<T>& ts, float (&v)[16], int tid) {
     if constexpr (VEC) {
         constexpr int E = 16 / (int)sizeof(T);
         const int kp = ts.K / E, np = ts.R * kp;
@@ -111,7 +112,7 @@ __device__ __forceinline__ void tile_fetch(const TileSrc<T>& ts, float (&v)[16])
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             if (256 * j >= np) break;   // uniform
-            const int i = min((int)threadIdx.x + 256 * j, np - 1);
+            const int i = min(tid + 256 * j, np - 1);
             const int r = tile_row(i, inv), k = (i - r * kp) * E;
             const uint4 raw = *(const uint4*)(ts.base + (int64_t)r * ts.rs + k);
             v[4 * j] = __uint_as_float(raw.x); v[4 * j + 1] = __uint_as_float(raw.y);
@@ -122,8 +123,7 @@ __device__ __forceinline__ void tile_fetch(const TileSrc<T>& ts, float (&v)[16])
 
 template <typename T, bool VEC>
 __device__ __forceinline__ void tile_put(const TileSrc<T>& ts, const float (&v)[16], float* __restrict__ dst, int ld,
-                                         bool tr) {
-    const int tid = threadIdx.x;
+                                         bool tr, int tid) {
     if constexpr (VEC) {
         constexpr int E = 16 / (int)sizeof(T);
         const int kp = ts.K / E, np = ts.R * kp;
@@ -197,17 +197,17 @@ __device__ __forceinline__ void head_fetch(const HeadParams& p, const HeadTile& 
     g.tb = TileSrc<T>{(const T*)p.Bm + (int64_t)q.b * p.sBm[0] + (int64_t)q.t0 * p.sBm[2], p.sBm[2], kHT, N, q.nval,
                       N};
     g.tc = TileSrc<T>{(const T*)p.C + (int64_t)q.b * p.sC[0] + (int64_t)q.t0 * p.sC[2], p.sC[2], kHT, N, q.nval, N};
-    tile_fetch<T, VEC>(g.tx, g.x);
-    tile_fetch<T, VEC>(g.tb, g.b);
-    if (needC) tile_fetch<T, VEC>(g.tc, g.c);
+    tile_fetch<T, VEC>(g.tx, g.x, tid);
+    tile_fetch<T, VEC>(g.tb, g.b, tid);
+    if (needC) tile_fetch<T, VEC>(g.tc, g.c, tid);
 }
 template <typename T, bool VEC>
 __device__ __forceinline__ void head_put(const HeadParams& p, const HeadTile& q, const HeadRegs<T>& g, float* dl,
                                          float* s, float* w, float* sx, float* sB, float* sC, int ldb, bool trB) {
     const int tid = threadIdx.x;
-    tile_put<T, VEC>(g.tx, g.x, sx, kXLd, false);
-    tile_put<T, VEC>(g.tb, g.b, sB, ldb, trB);
-    if (sC) tile_put<T, VEC>(g.tc, g.c, sC, ldb, false);
+    tile_put<T, VEC>(g.tx, g.x, sx, kXLd, false, tid);
+    tile_put<T, VEC>(g.tb, g.b, sB, ldb, trB, tid);
+    if (sC) tile_put<T, VEC>(g.tc, g.c, sC, ldb, false, tid);
     if (tid < kHT) {   // wave 0, lane = step
         const float dv = tid < q.nval ? g.dv : 0.0f;
         float v = dv;
@@ -223,7 +223,8 @@ __device__ __forceinline__ void head_put(const HeadParams& p, const HeadTile& q,
         const float sT = __shfl(su, kHT - 1);
         dl[tid] = dv;
         s[tid] = su;
-        w[tid] = __expf(sT - su) * dv;
+        // the backward's state pass (x = gy, B = C) weighs step u by e^(s_u)
+        w[tid] = p.bstate ? __expf(su) : __expf(sT - su) * dv;
     }
     __syncthreads();
 }
@@ -330,11 +331,11 @@ __device__ __forceinline__ void head_out_body(const HeadParams& p, const HeadTil
         p.ckpt ? TileSrc<float>{p.ckpt + (row0 * p.nchunks + q.c) * N, (int64_t)p.nchunks * N, P, N, P, N}
                : TileSrc<float>{p.state + (((size_t)q.b * p.H + q.hh) * p.nchunks + q.c) * (size_t)N * P, N, P, N, P, N};
     float vh[16];
-    tile_fetch<float, VEC>(th, vh);
+    tile_fetch<float, VEC>(th, vh, threadIdx.x);
     {
         HeadRegs<T> st;
         head_fetch<T, VEC>(p, q, true, st);
-        tile_put<float, VEC>(th, vh, sH, ldn, false);
+        tile_put<float, VEC>(th, vh, sH, ldn, false, threadIdx.x);
         head_put<T, VEC>(p, q, st, dl, s, w, sx, sB, sC, ldn, false);
     }
     // row block of this wave, rotated with the chunk so that the causal work (row block rb
@@ -430,6 +431,372 @@ __global__ __launch_bounds__(256) void head_out_kernel(HeadParams p) {
 }
 
 
+// ---------------------------------------------------------------------------
+// Backward: the exact adjoint of the three products.  With dY the chunk's rows
+// of gy, H_in its entering state and G_out the adjoint of its end state (from
+// the later chunks; gh_last for the last one), the adjoint of the state at step
+// u of the chunk is
+//   Lam_u = sum_{t >= u} e^(s_t - s_u) C_t dY_t^T + e^(s_{T-1} - s_u) G_out,
+// so that, with G = C B^T, K = dY X^T (T x T), Lm the causal decay mask,
+// Mf = G o Lm, Kd = K o Lm diag(delta), e^s and ed = e^(s_{T-1} - s) per step:
+//   gx = diag(delta) Z,  Z = Mf^T dY + diag(ed) B G_out,
+//   gB = Kd^T C + diag(delta ed) X G_out^T,      (this head's term)
+//   gC = diag(e^s) dY H_in^T + Kd B,             (this head's term)
+//   gdelta_u = sum_p X[u][p] Z[u][p] + A xi_u,   gA = sum_u delta_u xi_u,
+// where xi_u = sum_{t >= u} ds_t is the adjoint of log a_u and ds_t that of
+// s_t: ds_t = sum_u W[t][u] - sum_v W[v][t] + e^(s_t) C_t . (dY H_in^T)_t - V_t
+// (+ e^(s_{T-1}) <G_out, H_in> + sum_v V_v at t = T-1), with W = Kd o G and
+// V_u = delta_u ed_u B_u . (X G_out^T)_u.  The chunk adjoints come from the
+// state pass run on (gy, C) with weights e^(s_u), Q_c = C^T diag(e^s) dY, and a
+// reverse chain G_out(c-1) = Q_c + e^(s_{T-1}) G_out(c); gh0 = Q_0 + decay_0 G_out(0).
+// ---------------------------------------------------------------------------
+
+// reverse chain: one thread per (batch, head, p, n), chunks from the last
+// down; Q_c in gstate is replaced by G_out(c)
+__global__ __launch_bounds__(256) void head_rchain_kernel(HeadBwdParams p) {
+    const int P = p.P, N = p.N, NP = N * P, nch = p.nchunks;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (int64_t)p.B * p.H * NP) return;
+    const int64_t bh = i / NP;
+    const int e = (int)(i - bh * NP), pp = e / N, n = e - pp * N;
+    const int b = (int)(bh / p.H), hh = (int)(bh - (int64_t)b * p.H);
+    const int64_t seq = (int64_t)b * p.H * P + (int64_t)hh * P + pp;
+    float g = p.gh_last ? p.gh_last[seq * N + n] : 0.0f;
+    float* S = p.gstate + (size_t)bh * nch * NP + e;
+    const float* dec = p.decay + (size_t)bh * nch;
+    for (int c1 = nch; c1 > 0; c1 -= kChainGroup) {
+        const int c0 = max(0, c1 - kChainGroup);
+        float loc[kChainGroup], dc[kChainGroup];
+#pragma unroll
+        for (int j = 0; j < kChainGroup; ++j)
+            if (c0 + j < c1) {
+                loc[j] = S[(size_t)(c0 + j) * NP];
+                dc[j] = dec[c0 + j];
+            }
+#pragma unroll
+        for (int j = kChainGroup - 1; j >= 0; --j)
+            if (c0 + j < c1) {
+                S[(size_t)(c0 + j) * NP] = g;
+                g = fmaf(dc[j], g, loc[j]);
+            }
+    }
+    if (p.gh0) p.gh0[seq * N + n] = g;
+}
+
+// LDS layout (float offsets, multiples of 4): delta, s, e^s, ed (T each); the
+// W row sums per 16-column block and column sums per 16-row block (4 x T
+// each), sum_p X Z per 16-channel block (4 x T), the carried and V terms (T
+// each), <G_out, H_in>; x and gy as [p][t], B and C as [t][n], H_in and G_out
+// as [p][n], Mf and Kd transposed, as [u][t].
+struct HeadBwdLds {
+    int dl, s, es, ed, wrow, wcol, expl, carr, V, misc, sx, sy, sB, sC, sH, sG, MT, KT, total;
+};
+__host__ __device__ inline HeadBwdLds head_bwd_lds(int P, int N) {
+    const int ldn = ld_rows_i(N);
+    HeadBwdLds o;
+    o.dl = 0;
+    o.s = kHT;
+    o.es = 2 * kHT;
+    o.ed = 3 * kHT;
+    o.wrow = 4 * kHT;
+    o.wcol = o.wrow + 4 * kHT;   // follows wrow: the two are cleared as one run of 8 T
+    o.expl = o.wcol + 4 * kHT;
+    o.carr = o.expl + 4 * kHT;
+    o.V = o.carr + kHT;
+    o.misc = o.V + kHT;
+    o.sx = o.misc + 4;
+    o.sy = o.sx + P * kXLd;
+    o.sB = o.sy + P * kXLd;
+    o.sC = o.sB + kHT * ldn;
+    o.sH = o.sC + kHT * ldn;
+    o.sG = o.sH + P * ldn;
+    o.MT = o.sG + P * ldn;
+    o.KT = o.MT + kHT * kXLd;
+    o.total = o.KT + kHT * kXLd;
+    return o;
+}
+constexpr int kBwdThreads = 512;
+
+// sum over the 64 lanes, the same value in every lane
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int k = 1; k < 64; k <<= 1) v += __shfl_xor(v, k);
+    return v;
+}
+
+template <typename T, bool VEC>
+__device__ __forceinline__ void head_bwd_body(const HeadBwdParams& p, const HeadTile& q, float* lds) {
+    const int P = p.P, N = p.N, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int ldn = ld_rows_i(N), i = lane & 15, j = lane >> 4;
+    const HeadBwdLds o = head_bwd_lds(P, N);
+    float *dl = lds + o.dl, *s = lds + o.s, *es = lds + o.es, *ed = lds + o.ed;
+    float *wrow = lds + o.wrow, *wcol = lds + o.wcol, *expl = lds + o.expl, *carr = lds + o.carr;
+    float *Vs = lds + o.V, *misc = lds + o.misc, *sx = lds + o.sx, *sy = lds + o.sy, *sB = lds + o.sB;
+    float *sC = lds + o.sC, *sH = lds + o.sH, *sG = lds + o.sG, *MT = lds + o.MT, *KT = lds + o.KT;
+    const int64_t bh = (int64_t)q.b * p.H + q.hh;
+    const int64_t row0 = bh * P;   // channel row (b, h*P) of the (B, D, ...) arrays
+    const float A = p.A[(int64_t)q.hh * p.sA];
+
+    // loads: threads 0-255 take x, B and H_in, threads 256-511 gy, C and G_out (uniform per wave)
+    {
+        const int grp = tid >> 8, gt = tid & 255;
+        const TileSrc<T> t0s =
+            grp ? TileSrc<T>{(const T*)p.gy + (int64_t)q.b * p.sgy[0] + (int64_t)q.hh * P * p.sgy[1] + q.t0,
+                             p.sgy[1], P, kHT, P, q.nval}
+                : TileSrc<T>{(const T*)p.x + (int64_t)q.b * p.sx[0] + (int64_t)q.hh * P * p.sx[1] + q.t0, p.sx[1], P,
+                             kHT, P, q.nval};
+        const TileSrc<T> t1s =
+            grp ? TileSrc<T>{(const T*)p.C + (int64_t)q.b * p.sC[0] + (int64_t)q.t0 * p.sC[2], p.sC[2], kHT, N,
+                             q.nval, N}
+                : TileSrc<T>{(const T*)p.Bm + (int64_t)q.b * p.sBm[0] + (int64_t)q.t0 * p.sBm[2], p.sBm[2], kHT, N,
+                             q.nval, N};
+        const TileSrc<float> t2s =
+            grp ? TileSrc<float>{p.gstate + ((size_t)bh * p.nchunks + q.c) * (size_t)N * P, N, P, N, P, N}
+                : TileSrc<float>{p.ckpt + (row0 * p.nchunks + q.c) * N, (int64_t)p.nchunks * N, P, N, P, N};
+        float v0[16], v1[16], v2[16];
+        tile_fetch<T, VEC>(t0s, v0, gt);
+        tile_fetch<T, VEC>(t1s, v1, gt);
+        tile_fetch<float, VEC>(t2s, v2, gt);
+        float dv = 0.0f;
+        if (tid < kHT) {
+            const T* delta = (const T*)p.delta + (int64_t)q.b * p.sdelta[0] + (int64_t)q.hh * p.sdelta[1] + q.t0;
+            dv = tid < q.nval ? to_f32(delta[min(tid, q.nval - 1)]) : 0.0f;
+        }
+        wrow[tid] = 0.0f;   // wrow and wcol: 8 T = 512 floats
+        tile_put<T, VEC>(t0s, v0, grp ? sy : sx, kXLd, false, gt);
+        tile_put<T, VEC>(t1s, v1, grp ? sC : sB, ldn, false, gt);
+        tile_put<float, VEC>(t2s, v2, grp ? sG : sH, ldn, false, gt);
+        if (tid < kHT) {   // wave 0, lane = step: s = A * inclusive prefix sum of delta
+            float v = dv;
+            v += dpp<SSM_DPP_ROW_SHR(1)>(0.0f, v);
+            v += dpp<SSM_DPP_ROW_SHR(2)>(0.0f, v);
+            v += dpp<SSM_DPP_ROW_SHR(4)>(0.0f, v);
+            v += dpp<SSM_DPP_ROW_SHR(8)>(0.0f, v);
+            const float r0 = __shfl(v, 15), r1 = __shfl(v, 31), r2 = __shfl(v, 47);
+            const int row = tid >> 4;
+            v += (row > 0 ? r0 : 0.0f) + (row > 1 ? r1 : 0.0f) + (row > 2 ? r2 : 0.0f);
+            const float su = A * v;
+            const float sT = __shfl(su, kHT - 1);
+            dl[tid] = dv;
+            s[tid] = su;
+            es[tid] = __expf(su);
+            ed[tid] = __expf(sT - su);
+        }
+    }
+    __syncthreads();
+
+    // phase 1: the ten causal 16 x 16 blocks (tb >= ub) of G and K, masked and scaled in registers
+    // into Mf and Kd (stored transposed), and the row and column sums of W = Kd o G
+    for (int idx = wave; idx < 10; idx += kBwdThreads / 64) {   // uniform per wave
+        const int tb = idx < 1 ? 0 : idx < 3 ? 1 : idx < 6 ? 2 : 3, ub = idx - tb * (tb + 1) / 2;
+        const int t0 = 16 * tb, u0 = 16 * ub;
+        f4 ga = {0.0f, 0.0f, 0.0f, 0.0f}, ka = {0.0f, 0.0f, 0.0f, 0.0f};
+        // G[t][u] = sum_n C[t][n] B[u][n]; k-group j takes n = 16 nb + 4 j .. + 3 in turn
+        for (int nb = 0; nb < N / 16; ++nb) {
+            const float4 c4 = *(const float4*)&sC[(t0 + i) * ldn + 16 * nb + 4 * j];
+            const float4 b4 = *(const float4*)&sB[(u0 + i) * ldn + 16 * nb + 4 * j];
+            ga = mfma4(c4.x, b4.x, ga);
+            ga = mfma4(c4.y, b4.y, ga);
+            ga = mfma4(c4.z, b4.z, ga);
+            ga = mfma4(c4.w, b4.w, ga);
+        }
+        // K[t][u] = sum_p dY[t][p] X[u][p]: A[t][p] = sy[p][t], B[p][u] = sx[p][u], k-group j = p % 4
+        for (int p16 = 0; p16 < P / 16; ++p16)
+#pragma unroll
+        for (int p4 = 4 * p16; p4 < 4 * p16 + 4; ++p4) {
+            const int pr = 4 * p4 + j;
+            ka = mfma4(sy[pr * kXLd + t0 + i], sx[pr * kXLd + u0 + i], ka);
+        }
+        // register r of lane l: t = t0 + 4 j + r, u = u0 + i
+        const int u = u0 + i;
+        const float su = s[u], du = dl[u];
+        f4 mf, kd;
+        float rs[4], cs = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = t0 + 4 * j + r;
+            const float e = u <= t ? __expf(s[t] - su) : 0.0f;
+            mf[r] = ga[r] * e;
+            kd[r] = ka[r] * e * du;
+            rs[r] = kd[r] * ga[r];
+            cs += rs[r];
+        }
+        *(f4*)&MT[u * kXLd + t0 + 4 * j] = mf;
+        *(f4*)&KT[u * kXLd + t0 + 4 * j] = kd;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {   // sum over the 16 lanes of each row: the total lands in lane 15
+            float v = rs[r];
+            v += dpp<SSM_DPP_ROW_SHR(1)>(0.0f, v);
+            v += dpp<SSM_DPP_ROW_SHR(2)>(0.0f, v);
+            v += dpp<SSM_DPP_ROW_SHR(4)>(0.0f, v);
+            v += dpp<SSM_DPP_ROW_SHR(8)>(0.0f, v);
+            rs[r] = v;
+        }
+        if (i == 15) *(float4*)&wrow[ub * kHT + t0 + 4 * j] = make_float4(rs[0], rs[1], rs[2], rs[3]);
+        cs += __shfl_xor(cs, 16);
+        cs += __shfl_xor(cs, 32);
+        if (j == 0) wcol[tb * kHT + u] = cs;
+    }
+    if (wave == kBwdThreads / 64 - 1) {   // <G_out, H_in>
+        float v = 0.0f;
+        for (int e = lane; e < P * N; e += 64) {
+            const int pp = e / N, n = e - pp * N;
+            v += sG[pp * ldn + n] * sH[pp * ldn + n];
+        }
+        v = wave_sum(v);
+        if (lane == 0) misc[0] = v;
+    }
+    __syncthreads();
+
+    // phase 2.  Waves 0-3: gB for steps 16w.. and gC for steps 16w.. (per-head terms, [n][t]).
+    // Waves 4-7: Z for channels 16(w-4).. and every step: gx and sum_p X Z.
+    const int64_t pofs = ((int64_t)q.hh * p.B + q.b) * N * (int64_t)p.L + q.t0;
+    if (wave < 4) {
+        const int b0 = 16 * wave;
+        float vsum = 0.0f, csum = 0.0f;
+        for (int nt = 0; nt < N / 16; ++nt) {
+            f4 a1 = {0.0f, 0.0f, 0.0f, 0.0f}, a2 = {0.0f, 0.0f, 0.0f, 0.0f};
+            // Kd^T C over the row blocks tb >= this block: A[n][t] = C[t][n], B[t][u] = KT[u][t]
+            for (int tb = wave; tb < 4; ++tb) {
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    const int t = 16 * tb + 4 * kk + j;
+                    a1 = mfma4(sC[t * ldn + 16 * nt + i], KT[(b0 + i) * kXLd + t], a1);
+                }
+            }
+            // X G_out^T: A[n][p] = G_out[p][n], B[p][u] = sx[p][u]
+            for (int p16 = 0; p16 < P / 16; ++p16)
+#pragma unroll
+            for (int p4 = 4 * p16; p4 < 4 * p16 + 4; ++p4) {
+                const int pr = 4 * p4 + j;
+                a2 = mfma4(sG[pr * ldn + 16 * nt + i], sx[pr * kXLd + b0 + i], a2);
+            }
+            // register r of lane l: n = 16 nt + 4 j + r, u = b0 + i
+            {
+                const int u = b0 + i;
+                const float sc = dl[u] * ed[u];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int n = 16 * nt + 4 * j + r;
+                    const float b2 = sc * a2[r];
+                    vsum += sB[u * ldn + n] * b2;
+                    if (p.partB && u < q.nval) p.partB[pofs + (int64_t)n * p.L + u] = a1[r] + b2;
+                }
+            }
+            f4 c1 = {0.0f, 0.0f, 0.0f, 0.0f}, c2 = {0.0f, 0.0f, 0.0f, 0.0f};
+            // dY H_in^T: A[n][p] = H_in[p][n], B[p][t] = sy[p][t]
+            for (int p16 = 0; p16 < P / 16; ++p16)
+#pragma unroll
+            for (int p4 = 4 * p16; p4 < 4 * p16 + 4; ++p4) {
+                const int pr = 4 * p4 + j;
+                c1 = mfma4(sH[pr * ldn + 16 * nt + i], sy[pr * kXLd + b0 + i], c1);
+            }
+            // Kd B over the column blocks ub <= this block: A[n][u] = B[u][n], B[u][t] = KT[u][t]
+            for (int ub = 0; ub <= wave; ++ub) {
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    const int u = 16 * ub + 4 * kk + j;
+                    c2 = mfma4(sB[u * ldn + 16 * nt + i], KT[u * kXLd + b0 + i], c2);
+                }
+            }
+            // register r of lane l: n = 16 nt + 4 j + r, t = b0 + i
+            {
+                const int t = b0 + i;
+                const float e = es[t];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int n = 16 * nt + 4 * j + r;
+                    const float g1 = e * c1[r];
+                    csum += sC[t * ldn + n] * g1;
+                    if (p.partC && t < q.nval) p.partC[pofs + (int64_t)n * p.L + t] = g1 + c2[r];
+                }
+            }
+        }
+        vsum += __shfl_xor(vsum, 16);
+        vsum += __shfl_xor(vsum, 32);
+        csum += __shfl_xor(csum, 16);
+        csum += __shfl_xor(csum, 32);
+        if (j == 0) {
+            Vs[b0 + i] = vsum;
+            carr[b0 + i] = csum;
+        }
+    } else if (16 * (wave - 4) < P) {
+        const int pt = wave - 4, p0 = 16 * pt;
+        T* gx = (T*)p.gx;
+        for (int ub = 0; ub < 4; ++ub) {
+            const int u0 = 16 * ub;
+            f4 z1 = {0.0f, 0.0f, 0.0f, 0.0f}, z2 = {0.0f, 0.0f, 0.0f, 0.0f};
+            // Mf^T dY (as Z^T[p][u] = sum_t dY[t][p] Mf[t][u]) over the row blocks tb >= ub;
+            // k-group j takes t = 16 tb + 4 j .. + 3 in turn
+            for (int tb = ub; tb < 4; ++tb) {
+                const float4 a4 = *(const float4*)&sy[(p0 + i) * kXLd + 16 * tb + 4 * j];
+                const float4 b4 = *(const float4*)&MT[(u0 + i) * kXLd + 16 * tb + 4 * j];
+                z1 = mfma4(a4.x, b4.x, z1);
+                z1 = mfma4(a4.y, b4.y, z1);
+                z1 = mfma4(a4.z, b4.z, z1);
+                z1 = mfma4(a4.w, b4.w, z1);
+            }
+            // B G_out (as Z^T[p][u] = sum_n G_out[p][n] B[u][n])
+            for (int nb = 0; nb < N / 16; ++nb) {
+                const float4 a4 = *(const float4*)&sG[(p0 + i) * ldn + 16 * nb + 4 * j];
+                const float4 b4 = *(const float4*)&sB[(u0 + i) * ldn + 16 * nb + 4 * j];
+                z2 = mfma4(a4.x, b4.x, z2);
+                z2 = mfma4(a4.y, b4.y, z2);
+                z2 = mfma4(a4.z, b4.z, z2);
+                z2 = mfma4(a4.w, b4.w, z2);
+            }
+            // register r of lane l: p = p0 + 4 j + r, u = u0 + i
+            const int u = u0 + i;
+            const float eu = ed[u], du = dl[u];
+            float ex = 0.0f;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int pp = p0 + 4 * j + r;
+                const float z = z1[r] + eu * z2[r];
+                ex += sx[pp * kXLd + u] * z;
+                if (gx && u < q.nval)
+                    gx[(int64_t)q.b * p.sgx[0] + ((int64_t)q.hh * P + pp) * p.sgx[1] + q.t0 + u] = from_f32<T>(du * z);
+            }
+            ex += __shfl_xor(ex, 16);
+            ex += __shfl_xor(ex, 32);
+            if (j == 0) expl[pt * kHT + u] = ex;
+        }
+    }
+    __syncthreads();
+
+    // phase 3 (wave 0, lane = step): ds, its suffix sums xi, gdelta and this chunk's term of gA
+    if (wave == 0) {
+        const int u = lane;
+        const float rw = ((wrow[u] + wrow[kHT + u]) + wrow[2 * kHT + u]) + wrow[3 * kHT + u];
+        const float cw = ((wcol[u] + wcol[kHT + u]) + wcol[2 * kHT + u]) + wcol[3 * kHT + u];
+        float ds = rw - cw + carr[u] - Vs[u];
+        const float vt = wave_sum(Vs[u]);
+        if (u == kHT - 1) ds += __expf(s[kHT - 1]) * misc[0] + vt;
+        float xi = ds;
+#pragma unroll
+        for (int k = 1; k < 64; k <<= 1) {
+            const float y = __shfl_down(xi, k);
+            if (u + k < 64) xi += y;
+        }
+        float ex = 0.0f;
+        for (int pt = 0; pt < P / 16; ++pt) ex += expl[pt * kHT + u];
+        if (p.gdelta && u < q.nval)
+            ((T*)p.gdelta)[(int64_t)q.b * p.sgdelta[0] + (int64_t)q.hh * p.sgdelta[1] + q.t0 + u] =
+                from_f32<T>(ex + A * xi);
+        const float ga = wave_sum(dl[u] * xi);
+        if (p.partA && u == 0) p.partA[((int64_t)q.hh * p.B + q.b) * p.nchunks + q.c] = ga;
+    }
+}
+template <typename T>
+__global__ __launch_bounds__(kBwdThreads) void head_bwd_kernel(HeadBwdParams p) {
+    extern __shared__ __align__(16) float lds[];
+    const HeadTile q = head_tile(p);
+    const bool hal = ((uintptr_t)p.ckpt & 15) == 0;
+    if (p.vx && p.vgy && p.vb && p.vc && hal && q.nval == kHT) head_bwd_body<T, true>(p, q, lds);   // uniform
+    else head_bwd_body<T, false>(p, q, lds);
+}
+
+
 // gdelta of the head form: the sum of the head's P rows of gdc (per-channel
 // step-size gradients, or sums over groups of its channels), in order.
 // gdc (B, H * P, L) fp32, out (B, H, L).
@@ -474,6 +841,23 @@ hipError_t launch_head_out(const HeadParams& p, int dtype, hipStream_t st) {
     const size_t lds = head_lds(p.P, p.N, true).total * sizeof(float);
     if (dtype == 0) head_out_kernel<float><<<grid, 256, lds, st>>>(p);
     else head_out_kernel<bf16_t><<<grid, 256, lds, st>>>(p);
+    return hipGetLastError();
+}
+hipError_t launch_head_rchain(const HeadBwdParams& p, hipStream_t st) {
+    const int64_t n = (int64_t)p.B * p.H * p.N * p.P;
+    head_rchain_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(p);
+    return hipGetLastError();
+}
+hipError_t launch_head_bwd(const HeadBwdParams& p, int dtype, hipStream_t st) {
+    if (p.P % 16 || p.P > 64 || p.N % 16 || p.N > 64) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)p.nchunks, (unsigned)p.H, (unsigned)p.B);
+    const size_t lds = head_bwd_lds(p.P, p.N).total * sizeof(float);
+    if (dtype == 0) head_bwd_kernel<float><<<grid, kBwdThreads, lds, st>>>(p);
+    else head_bwd_kernel<bf16_t><<<grid, kBwdThreads, lds, st>>>(p);
+    return hipGetLastError();
+}
+hipError_t launch_head_sum_rows(const float* part, float* out, int H, int n, hipStream_t st) {
+    head_ga_kernel<<<(unsigned)((H + 63) / 64), 64, 0, st>>>(part, out, H, n, 1);
     return hipGetLastError();
 }
 hipError_t launch_head_reduce(const float* gdc, void* gdelta, const float* ga_dn, float* gA, int B, int H, int R,

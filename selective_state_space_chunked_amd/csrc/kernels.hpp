@@ -199,12 +199,34 @@ struct HeadParams {
     float* state; float* decay;
     int B, H, P, L, N, nchunks;
     int vx, vb, vc, vy;   // 16-byte row loads of x, B, C and 4-step stores of y are aligned
+    int bstate;           // state pass of the backward: weights e^(s_u) (x = gy, Bm = C)
 };
 // the three passes: chunk-local states (matrix cores), the chain over chunks,
 // the outputs (matrix cores; needs p.y)
 hipError_t launch_head_state(const HeadParams& p, int dtype, hipStream_t st);
 hipError_t launch_head_chain(const HeadParams& p, hipStream_t st);
 hipError_t launch_head_out(const HeadParams& p, int dtype, hipStream_t st);
+// backward of the matrix form: the chunk adjoints G_out of every chunk (reverse
+// chain over the chunk sums Q_c = C^T diag(e^s) dY of the state pass), then one
+// workgroup per (chunk, head, batch) for gx, gdelta and the per-head partial
+// sums of gB, gC and gA
+struct HeadBwdParams {
+    const void* delta; const void* x; const float* A; const void* Bm; const void* C; const void* gy;
+    const float* ckpt;       // entering states (B, D, nchunks, N), fp32
+    const float* gh_last;    // (B, D, N) or null
+    int64_t sdelta[2], sx[2], sgy[2], sgx[2], sgdelta[2], sBm[3], sC[3], sA;
+    float* gstate;           // (B, H, nchunks, P, N): Q_c in, G_out(c) out
+    const float* decay;      // (B, H, nchunks)
+    void* gx; void* gdelta; float* gh0;
+    float* partB; float* partC;   // (H, B, N, L) per-head terms of gB, gC (null: not wanted)
+    float* partA;                 // (H, B, nchunks) per-chunk terms of gA (null: not wanted)
+    int B, H, P, L, N, nchunks;
+    int vx, vgy, vb, vc;          // 16-byte row loads of x, gy, B, C are aligned
+};
+hipError_t launch_head_rchain(const HeadBwdParams& p, hipStream_t st);
+hipError_t launch_head_bwd(const HeadBwdParams& p, int dtype, hipStream_t st);
+// out[h] = sum of part[h * n .. h * n + n - 1], in order
+hipError_t launch_head_sum_rows(const float* part, float* out, int H, int n, hipStream_t st);
 // gdelta (B,H,L) = sums over each head's channels of gdc (B,D,L) fp32; gA (H) =
 // sums of ga_dn (D,N) over each head's channels and states (null skips either)
 // gdc rows per head: R (group sums or channels); ga_dn: P channels x N states per head

@@ -42,21 +42,22 @@ __global__ void seg_combine_rev_kernel(const float* __restrict__ Q, const float*
 
 // partial (nblk,B,N,L) -> out (B,L,N), adding the blocks in index order
 // Channel-block partials (nblk, B, N, L) of gB and gC -> outputs (B, L, N).
-// A workgroup takes 64 steps of one batch row and one tensor (blockIdx.z);
-// thread (n, q) adds the nblk partials of steps 4q..4q+3 in block order, then
-// the 64 x N tile is transposed through LDS so the (t, n) output rows are
-// written contiguously.
+// A workgroup takes 64 steps of one batch row, one tensor and 16 states
+// (blockIdx.z = tensor * slabs + slab); thread (n, q) adds the nblk partials of
+// steps 4q..4q+3 in block order, then the 64 x 16 tile is transposed through
+// LDS so that the output rows are written in (t, n) order.
 template <typename T>
 __global__ __launch_bounds__(256) void reduce_parts_btn_kernel(const float* __restrict__ partB,
                                                                const float* __restrict__ partC, int nblk, int B,
                                                                int N, int L, T* __restrict__ outB,
                                                                T* __restrict__ outC) {
     __shared__ float tile[64][17];
-    const float* __restrict__ part = blockIdx.z ? partC : partB;
-    T* __restrict__ out = blockIdx.z ? outC : outB;
+    const int nslab = (N + 15) / 16, which = blockIdx.z / nslab, n0 = 16 * (blockIdx.z - which * nslab);
+    const float* __restrict__ part = which ? partC : partB;
+    T* __restrict__ out = which ? outC : outB;
     if (!part || !out) return;
     const int b = blockIdx.y, t0 = blockIdx.x * 64;
-    const int n = threadIdx.x >> 4, q = threadIdx.x & 15;
+    const int nl = threadIdx.x >> 4, n = n0 + nl, q = threadIdx.x & 15;
     const int tl = 4 * q, t = t0 + tl;
     const size_t stride = (size_t)B * N * L;
     float s[4] = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -84,11 +85,11 @@ __global__ __launch_bounds__(256) void reduce_parts_btn_kernel(const float* __re
         }
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) tile[tl + i][n] = s[i];
+    for (int i = 0; i < 4; ++i) tile[tl + i][nl] = s[i];
     __syncthreads();
-    const int steps = min(64, L - t0);
-    T* dst = out + ((size_t)b * L + t0) * N;
-    for (int i = threadIdx.x; i < steps * N; i += 256) dst[i] = from_f32<T>(tile[i / N][i % N]);
+    const int steps = min(64, L - t0), nw = min(16, N - n0);
+    T* dst = out + ((size_t)b * L + t0) * N + n0;
+    for (int i = threadIdx.x; i < steps * nw; i += 256) dst[(i / nw) * N + i % nw] = from_f32<T>(tile[i / nw][i % nw]);
 }
 // The same sums when N and L are multiples of 4: wave w of the workgroup takes
 // state n = 4 * blockIdx.z' + w and lane l the steps t0 + 4l .. t0 + 4l + 3, so
@@ -602,7 +603,7 @@ hipError_t launch_reduce_parts_btn(const float* partB, const float* partC, int n
                                                                  (bf16_t*)outC);
         return hipGetLastError();
     }
-    dim3 grid((unsigned)((L + 63) / 64), (unsigned)B, 2);
+    dim3 grid((unsigned)((L + 63) / 64), (unsigned)B, (unsigned)(2 * ((N + 15) / 16)));
     if (dtype == 0)
         reduce_parts_btn_kernel<float><<<grid, 256, 0, st>>>(partB, partC, nblk, B, N, L, (float*)outB, (float*)outC);
     else

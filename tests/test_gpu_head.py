@@ -1,5 +1,5 @@
-"""GPU parity of the scalar-transition-per-head mode (chunked matrix form on the matrix cores in the forward,
-the exact tiled adjoint in the backward) against the fp64 oracle, through the C ABI."""
+"""GPU parity of the scalar-transition-per-head mode (the chunked matrix form on the matrix cores, forward and
+its exact adjoint) against the fp64 oracle, through the C ABI."""
 import numpy as np
 import pytest
 import torch
@@ -97,11 +97,13 @@ def test_head_fwd_bwd(dt, B, H, P, N, L):
     ("f32", 1, 1, 48, 48, 65),
     ("bf16", 1, 2, 64, 64, 500),
 ])
-def test_head_forward_large_state(dt, B, H, P, N, L):
-    """State sizes above 16 (forward only; the backward takes N = 16)."""
+def test_head_large_state(dt, B, H, P, N, L):
+    """State sizes above 16, forward and backward (several 16-state blocks in every product)."""
     cfg = make_head(B, H, P, N, L, dt, seed=B + H + P + N + L + 1)
-    h0 = np.random.default_rng(8).standard_normal((B, H * P, N)).astype(np.float32)
-    run_head(cfg, h0=h0, backward=False)
+    g = np.random.default_rng(8)
+    h0 = g.standard_normal((B, H * P, N)).astype(np.float32)
+    ghl = g.standard_normal((B, H * P, N)).astype(np.float32)
+    run_head(cfg, h0=h0, ghl=ghl)
 
 
 @pytest.mark.parametrize("L", [1, 63, 64, 200])
