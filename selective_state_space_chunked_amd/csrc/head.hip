@@ -483,38 +483,47 @@ __global__ __launch_bounds__(256) void head_rchain_kernel(HeadBwdParams p) {
     if (p.gh0) p.gh0[seq * N + n] = g;
 }
 
-// LDS layout (float offsets, multiples of 4): delta, s, e^s, ed (T each); the
-// W row sums per 16-column block and column sums per 16-row block (4 x T
-// each), sum_p X Z per 16-channel block (4 x T), the carried and V terms (T
-// each), <G_out, H_in>; x and gy as [p][t], B and C as [t][n], H_in and G_out
-// as [p][n], Mf and Kd transposed, as [u][t].
+// Mf and Kd are kept transposed, as [u][t], for t >= u's 16-row block only:
+// row u of block ub = u / 16 holds t = 16 ub .. T-1 (64 - 16 ub values) with
+// 4 floats of padding, so the rows of a block start 4 or 20 banks apart.
+__host__ __device__ constexpr int ct_ld(int ub) { return kHT - 16 * ub + 4; }
+__host__ __device__ constexpr int ct_off(int ub) { return 16 * ((kHT + 4) * ub - 8 * ub * (ub - 1)); }
+constexpr int kCtSize = ct_off(4);   // 2816 floats
+
+// LDS layout (float offsets, multiples of 4): delta and s (T each); the W row
+// sums per 16-column block and column sums per 16-row block (4 x T each),
+// sum_p X Z per 16-channel block (4 x T), the carried term minus V (T), and
+// misc = <G_out, H_in> and the four 16-step block sums of V; x and gy as
+// [p][t], B and C as [t][n], H_in and G_out as [p][n]; Mf and Kd in the causal
+// layout above.  At P = 64, N = 16 this is 81696 bytes: two workgroups per CU.
 struct HeadBwdLds {
-    int dl, s, es, ed, wrow, wcol, expl, carr, V, misc, sx, sy, sB, sC, sH, sG, MT, KT, total;
+    int dl, s, wrow, wcol, expl, cv, misc, sx, sy, sB, sC, sH, sG, MT, KT, total;
 };
 __host__ __device__ inline HeadBwdLds head_bwd_lds(int P, int N) {
     const int ldn = ld_rows_i(N);
     HeadBwdLds o;
     o.dl = 0;
     o.s = kHT;
-    o.es = 2 * kHT;
-    o.ed = 3 * kHT;
-    o.wrow = 4 * kHT;
+    o.wrow = 2 * kHT;
     o.wcol = o.wrow + 4 * kHT;   // follows wrow: the two are cleared as one run of 8 T
     o.expl = o.wcol + 4 * kHT;
-    o.carr = o.expl + 4 * kHT;
-    o.V = o.carr + kHT;
-    o.misc = o.V + kHT;
-    o.sx = o.misc + 4;
+    o.cv = o.expl + 4 * kHT;
+    o.misc = o.cv + kHT;
+    o.sx = o.misc + 8;
     o.sy = o.sx + P * kXLd;
     o.sB = o.sy + P * kXLd;
     o.sC = o.sB + kHT * ldn;
     o.sH = o.sC + kHT * ldn;
     o.sG = o.sH + P * ldn;
     o.MT = o.sG + P * ldn;
-    o.KT = o.MT + kHT * kXLd;
-    o.total = o.KT + kHT * kXLd;
+    o.KT = o.MT + kCtSize;
+    o.total = o.KT + kCtSize;
     return o;
 }
+// Workgroup barrier for LDS traffic only: this wave's LDS operations complete,
+// then s_barrier (a plain __syncthreads would first wait for the gx and partial
+// sum stores in flight as well).
+__device__ __forceinline__ void lds_barrier() { __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 constexpr int kBwdThreads = 512;
 
 // sum over the 64 lanes, the same value in every lane
@@ -529,9 +538,9 @@ __device__ __forceinline__ void head_bwd_body(const HeadBwdParams& p, const Head
     const int P = p.P, N = p.N, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int ldn = ld_rows_i(N), i = lane & 15, j = lane >> 4;
     const HeadBwdLds o = head_bwd_lds(P, N);
-    float *dl = lds + o.dl, *s = lds + o.s, *es = lds + o.es, *ed = lds + o.ed;
-    float *wrow = lds + o.wrow, *wcol = lds + o.wcol, *expl = lds + o.expl, *carr = lds + o.carr;
-    float *Vs = lds + o.V, *misc = lds + o.misc, *sx = lds + o.sx, *sy = lds + o.sy, *sB = lds + o.sB;
+    float *dl = lds + o.dl, *s = lds + o.s;
+    float *wrow = lds + o.wrow, *wcol = lds + o.wcol, *expl = lds + o.expl, *cv = lds + o.cv;
+    float *misc = lds + o.misc, *sx = lds + o.sx, *sy = lds + o.sy, *sB = lds + o.sB;
     float *sC = lds + o.sC, *sH = lds + o.sH, *sG = lds + o.sG, *MT = lds + o.MT, *KT = lds + o.KT;
     const int64_t bh = (int64_t)q.b * p.H + q.hh;
     const int64_t row0 = bh * P;   // channel row (b, h*P) of the (B, D, ...) arrays
@@ -575,12 +584,8 @@ __device__ __forceinline__ void head_bwd_body(const HeadBwdParams& p, const Head
             const float r0 = __shfl(v, 15), r1 = __shfl(v, 31), r2 = __shfl(v, 47);
             const int row = tid >> 4;
             v += (row > 0 ? r0 : 0.0f) + (row > 1 ? r1 : 0.0f) + (row > 2 ? r2 : 0.0f);
-            const float su = A * v;
-            const float sT = __shfl(su, kHT - 1);
             dl[tid] = dv;
-            s[tid] = su;
-            es[tid] = __expf(su);
-            ed[tid] = __expf(sT - su);
+            s[tid] = A * v;
         }
     }
     __syncthreads();
@@ -621,8 +626,9 @@ __device__ __forceinline__ void head_bwd_body(const HeadBwdParams& p, const Head
             rs[r] = kd[r] * ga[r];
             cs += rs[r];
         }
-        *(f4*)&MT[u * kXLd + t0 + 4 * j] = mf;
-        *(f4*)&KT[u * kXLd + t0 + 4 * j] = kd;
+        const int ca = ct_off(ub) + i * ct_ld(ub) + 16 * (tb - ub) + 4 * j;   // (u, t0 + 4 j)
+        *(f4*)&MT[ca] = mf;
+        *(f4*)&KT[ca] = kd;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {   // sum over the 16 lanes of each row: the total lands in lane 15
             float v = rs[r];
@@ -646,13 +652,15 @@ __device__ __forceinline__ void head_bwd_body(const HeadBwdParams& p, const Head
         v = wave_sum(v);
         if (lane == 0) misc[0] = v;
     }
-    __syncthreads();
+    lds_barrier();
 
     // phase 2.  Waves 0-3: gB for steps 16w.. and gC for steps 16w.. (per-head terms, [n][t]).
     // Waves 4-7: Z for channels 16(w-4).. and every step: gx and sum_p X Z.
     const int64_t pofs = ((int64_t)q.hh * p.B + q.b) * N * (int64_t)p.L + q.t0;
+    const float sT = s[kHT - 1];
     if (wave < 4) {
         const int b0 = 16 * wave;
+        const float* kb = KT + ct_off(wave) + i * ct_ld(wave) - b0;   // row u = b0 + i of Kd^T, by t
         float vsum = 0.0f, csum = 0.0f;
         for (int nt = 0; nt < N / 16; ++nt) {
             f4 a1 = {0.0f, 0.0f, 0.0f, 0.0f}, a2 = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -661,7 +669,7 @@ __device__ __forceinline__ void head_bwd_body(const HeadBwdParams& p, const Head
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) {
                     const int t = 16 * tb + 4 * kk + j;
-                    a1 = mfma4(sC[t * ldn + 16 * nt + i], KT[(b0 + i) * kXLd + t], a1);
+                    a1 = mfma4(sC[t * ldn + 16 * nt + i], kb[t], a1);
                 }
             }
             // X G_out^T: A[n][p] = G_out[p][n], B[p][u] = sx[p][u]
@@ -674,7 +682,7 @@ __device__ __forceinline__ void head_bwd_body(const HeadBwdParams& p, const Head
             // register r of lane l: n = 16 nt + 4 j + r, u = b0 + i
             {
                 const int u = b0 + i;
-                const float sc = dl[u] * ed[u];
+                const float sc = dl[u] * __expf(sT - s[u]);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int n = 16 * nt + 4 * j + r;
@@ -693,16 +701,17 @@ __device__ __forceinline__ void head_bwd_body(const HeadBwdParams& p, const Head
             }
             // Kd B over the column blocks ub <= this block: A[n][u] = B[u][n], B[u][t] = KT[u][t]
             for (int ub = 0; ub <= wave; ++ub) {
+                const float* kc = KT + ct_off(ub) + b0 - 16 * ub + i;   // column t = b0 + i of Kd^T
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) {
                     const int u = 16 * ub + 4 * kk + j;
-                    c2 = mfma4(sB[u * ldn + 16 * nt + i], KT[u * kXLd + b0 + i], c2);
+                    c2 = mfma4(sB[u * ldn + 16 * nt + i], kc[(4 * kk + j) * ct_ld(ub)], c2);
                 }
             }
             // register r of lane l: n = 16 nt + 4 j + r, t = b0 + i
             {
                 const int t = b0 + i;
-                const float e = es[t];
+                const float e = __expf(s[t]);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int n = 16 * nt + 4 * j + r;
@@ -716,10 +725,13 @@ __device__ __forceinline__ void head_bwd_body(const HeadBwdParams& p, const Head
         vsum += __shfl_xor(vsum, 32);
         csum += __shfl_xor(csum, 16);
         csum += __shfl_xor(csum, 32);
-        if (j == 0) {
-            Vs[b0 + i] = vsum;
-            carr[b0 + i] = csum;
-        }
+        if (j == 0) cv[b0 + i] = csum - vsum;
+        // this block's total of V: lane 15 of the first row ends with it
+        vsum += dpp<SSM_DPP_ROW_SHR(1)>(0.0f, vsum);
+        vsum += dpp<SSM_DPP_ROW_SHR(2)>(0.0f, vsum);
+        vsum += dpp<SSM_DPP_ROW_SHR(4)>(0.0f, vsum);
+        vsum += dpp<SSM_DPP_ROW_SHR(8)>(0.0f, vsum);
+        if (lane == 15) misc[1 + wave] = vsum;
     } else if (16 * (wave - 4) < P) {
         const int pt = wave - 4, p0 = 16 * pt;
         T* gx = (T*)p.gx;
@@ -730,7 +742,7 @@ __device__ __forceinline__ void head_bwd_body(const HeadBwdParams& p, const Head
             // k-group j takes t = 16 tb + 4 j .. + 3 in turn
             for (int tb = ub; tb < 4; ++tb) {
                 const float4 a4 = *(const float4*)&sy[(p0 + i) * kXLd + 16 * tb + 4 * j];
-                const float4 b4 = *(const float4*)&MT[(u0 + i) * kXLd + 16 * tb + 4 * j];
+                const float4 b4 = *(const float4*)&MT[ct_off(ub) + i * ct_ld(ub) + 16 * (tb - ub) + 4 * j];
                 z1 = mfma4(a4.x, b4.x, z1);
                 z1 = mfma4(a4.y, b4.y, z1);
                 z1 = mfma4(a4.z, b4.z, z1);
@@ -747,7 +759,7 @@ __device__ __forceinline__ void head_bwd_body(const HeadBwdParams& p, const Head
             }
             // register r of lane l: p = p0 + 4 j + r, u = u0 + i
             const int u = u0 + i;
-            const float eu = ed[u], du = dl[u];
+            const float eu = __expf(sT - s[u]), du = dl[u];
             float ex = 0.0f;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -762,16 +774,15 @@ __device__ __forceinline__ void head_bwd_body(const HeadBwdParams& p, const Head
             if (j == 0) expl[pt * kHT + u] = ex;
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     // phase 3 (wave 0, lane = step): ds, its suffix sums xi, gdelta and this chunk's term of gA
     if (wave == 0) {
         const int u = lane;
         const float rw = ((wrow[u] + wrow[kHT + u]) + wrow[2 * kHT + u]) + wrow[3 * kHT + u];
         const float cw = ((wcol[u] + wcol[kHT + u]) + wcol[2 * kHT + u]) + wcol[3 * kHT + u];
-        float ds = rw - cw + carr[u] - Vs[u];
-        const float vt = wave_sum(Vs[u]);
-        if (u == kHT - 1) ds += __expf(s[kHT - 1]) * misc[0] + vt;
+        float ds = rw - cw + cv[u];
+        if (u == kHT - 1) ds += __expf(sT) * misc[0] + (((misc[1] + misc[2]) + misc[3]) + misc[4]);
         float xi = ds;
 #pragma unroll
         for (int k = 1; k < 64; k <<= 1) {
