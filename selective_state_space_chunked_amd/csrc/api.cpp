@@ -764,6 +764,7 @@ int scan_bwd_impl(const ssm_scan_args* a, const ssm_scan_bwd_in* in, const ssm_s
         q.vgy = hs.vx;
         q.vb = al(a->Bm, 16) && q.sBm[0] % e16 == 0 && q.sBm[2] % e16 == 0;
         q.vc = hs.vb;
+        q.vgx = g->gx && al(g->gx, 4 * (int64_t)p.esz) && q.sgx[0] % 4 == 0 && q.sgx[1] % 4 == 0;
         SSM_LAUNCH(launch_head_state(hs, p.dtype, st), "head backward chunk sums (matrix cores)");
         SSM_LAUNCH(launch_head_rchain(q, st), "head backward chain over the chunks");
         SSM_LAUNCH(launch_head_bwd(q, p.dtype, st), "head backward (matrix cores)");

@@ -735,43 +735,65 @@ __device__ __forceinline__ void head_bwd_body(const HeadBwdParams& p, const Head
     } else if (16 * (wave - 4) < P) {
         const int pt = wave - 4, p0 = 16 * pt;
         T* gx = (T*)p.gx;
+        T* gxrow = gx ? gx + (int64_t)q.b * p.sgx[0] + ((int64_t)q.hh * P + p0 + i) * p.sgx[1] + q.t0 : nullptr;
+        const bool vgx = p.vgx && q.nval == kHT;   // uniform: four steps in one store
         for (int ub = 0; ub < 4; ++ub) {
             const int u0 = 16 * ub;
             f4 z1 = {0.0f, 0.0f, 0.0f, 0.0f}, z2 = {0.0f, 0.0f, 0.0f, 0.0f};
-            // Mf^T dY (as Z^T[p][u] = sum_t dY[t][p] Mf[t][u]) over the row blocks tb >= ub;
+            // Mf^T dY (Z[u][p] = sum_t Mf[t][u] dY[t][p]) over the row blocks tb >= ub;
             // k-group j takes t = 16 tb + 4 j .. + 3 in turn
             for (int tb = ub; tb < 4; ++tb) {
-                const float4 a4 = *(const float4*)&sy[(p0 + i) * kXLd + 16 * tb + 4 * j];
-                const float4 b4 = *(const float4*)&MT[ct_off(ub) + i * ct_ld(ub) + 16 * (tb - ub) + 4 * j];
+                const float4 a4 = *(const float4*)&MT[ct_off(ub) + i * ct_ld(ub) + 16 * (tb - ub) + 4 * j];
+                const float4 b4 = *(const float4*)&sy[(p0 + i) * kXLd + 16 * tb + 4 * j];
                 z1 = mfma4(a4.x, b4.x, z1);
                 z1 = mfma4(a4.y, b4.y, z1);
                 z1 = mfma4(a4.z, b4.z, z1);
                 z1 = mfma4(a4.w, b4.w, z1);
             }
-            // B G_out (as Z^T[p][u] = sum_n G_out[p][n] B[u][n])
+            // B G_out (Z[u][p] = sum_n B[u][n] G_out[p][n])
             for (int nb = 0; nb < N / 16; ++nb) {
-                const float4 a4 = *(const float4*)&sG[(p0 + i) * ldn + 16 * nb + 4 * j];
-                const float4 b4 = *(const float4*)&sB[(u0 + i) * ldn + 16 * nb + 4 * j];
+                const float4 a4 = *(const float4*)&sB[(u0 + i) * ldn + 16 * nb + 4 * j];
+                const float4 b4 = *(const float4*)&sG[(p0 + i) * ldn + 16 * nb + 4 * j];
                 z2 = mfma4(a4.x, b4.x, z2);
                 z2 = mfma4(a4.y, b4.y, z2);
                 z2 = mfma4(a4.z, b4.z, z2);
                 z2 = mfma4(a4.w, b4.w, z2);
             }
-            // register r of lane l: p = p0 + 4 j + r, u = u0 + i
-            const int u = u0 + i;
-            const float eu = __expf(sT - s[u]), du = dl[u];
-            float ex = 0.0f;
+            // register r of lane l: u = u0 + 4 j + r, p = p0 + i
+            const int ua = u0 + 4 * j;
+            const float4 x4 = *(const float4*)&sx[(p0 + i) * kXLd + ua];
+            const float xs[4] = {x4.x, x4.y, x4.z, x4.w};
+            float g[4], ex[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int pp = p0 + 4 * j + r;
-                const float z = z1[r] + eu * z2[r];
-                ex += sx[pp * kXLd + u] * z;
-                if (gx && u < q.nval)
-                    gx[(int64_t)q.b * p.sgx[0] + ((int64_t)q.hh * P + pp) * p.sgx[1] + q.t0 + u] = from_f32<T>(du * z);
+                const float z = z1[r] + __expf(sT - s[ua + r]) * z2[r];
+                g[r] = dl[ua + r] * z;
+                ex[r] = xs[r] * z;
             }
-            ex += __shfl_xor(ex, 16);
-            ex += __shfl_xor(ex, 32);
-            if (j == 0) expl[pt * kHT + u] = ex;
+            if (vgx) {
+                if constexpr (sizeof(T) == 2) {
+                    const uint32_t lo = (uint32_t)from_f32<T>(g[0]) | ((uint32_t)from_f32<T>(g[1]) << 16);
+                    const uint32_t hi = (uint32_t)from_f32<T>(g[2]) | ((uint32_t)from_f32<T>(g[3]) << 16);
+                    *(uint2*)(gxrow + ua) = make_uint2(lo, hi);
+                } else {
+                    *(float4*)(gxrow + ua) = make_float4(g[0], g[1], g[2], g[3]);
+                }
+            } else if (gxrow) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (ua + r < q.nval) gxrow[ua + r] = from_f32<T>(g[r]);
+            }
+            // sum over the 16 channels of each row of lanes: lane 15 of row j ends with steps ua .. ua + 3
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float v = ex[r];
+                v += dpp<SSM_DPP_ROW_SHR(1)>(0.0f, v);
+                v += dpp<SSM_DPP_ROW_SHR(2)>(0.0f, v);
+                v += dpp<SSM_DPP_ROW_SHR(4)>(0.0f, v);
+                v += dpp<SSM_DPP_ROW_SHR(8)>(0.0f, v);
+                ex[r] = v;
+            }
+            if (i == 15) *(float4*)&expl[pt * kHT + ua] = make_float4(ex[0], ex[1], ex[2], ex[3]);
         }
     }
     lds_barrier();

@@ -222,6 +222,7 @@ struct HeadBwdParams {
     float* partA;                 // (H, B, nchunks) per-chunk terms of gA (null: not wanted)
     int B, H, P, L, N, nchunks;
     int vx, vgy, vb, vc;          // 16-byte row loads of x, gy, B, C are aligned
+    int vgx;                      // 4-step stores of gx are aligned
 };
 hipError_t launch_head_rchain(const HeadBwdParams& p, hipStream_t st);
 hipError_t launch_head_bwd(const HeadBwdParams& p, int dtype, hipStream_t st);
