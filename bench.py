@@ -62,7 +62,7 @@ MEASURED_TRAFFIC = {
                            # SQ_ACTIVE_INST_VALU x 4 cycles over 1024 SIMD x kernel cycles, and cycles per
                            # VALU instruction (profiles/selective_headline_counters.md)
                            "valu_busy": 0.82, "cycles_per_valu_instr": 4.45,
-                           "sources_sha256": "e53606426a16f970dd910564b36cf88326ed9bdce83d5e5534f1cbaa4737b1e4"},
+                           "sources_sha256": "a421d4c30638faba6fe283e193964b8d1488c3b627036862eeafcbc95aa9dbea"},
 }
 # (file, marker where the hashed text ends; None = whole file)
 TRAFFIC_SOURCES = (("selective.hpp", None), ("real_selective.hip", "// segment combines"), ("common.hpp", None))
@@ -401,9 +401,9 @@ MFMA_F32_PEAK = 256 * 4 * 64 * 2.4e9
 
 
 def w_head(steps, warmup):
-    """Scalar transition per head (matrix form on the matrix cores in the forward, the exact tiled adjoint
-    in the backward): B=8 H=32 P=64 (D=2048) N=16 L=4096, bf16 streams, the element count of the Mamba-layer
-    workload.  Reports the matrix-core rate of the two MFMA passes."""
+    """Scalar transition per head (the chunked matrix form on the matrix cores, forward and its exact
+    adjoint): B=8 H=32 P=64 (D=2048) N=16 L=4096, bf16 streams, the element count of the Mamba-layer
+    workload.  Reports the matrix-core rate of the four MFMA passes."""
     import torch
     import selective_state_space_chunked_amd as ssm
     B, H, P, N, L = 8, 32, 64, 16, 4096
@@ -429,10 +429,17 @@ def w_head(steps, warmup):
     # MFMAs (v_mfma_f32_16x16x4_f32, 2048 flops each) executed per 64-step chunk.  States: (P/16)(N/16)
     # tiles of K = 64.  Outputs: the wave with row block rb (0..3) forms G tiles up to the diagonal
     # ((rb+1) N/4), multiplies M by X over K = 16 (rb+1) for P/16 column tiles, and adds the carried term
-    # (N/4 per column tile).  SQ_VALU_MFMA_BUSY_CYCLES / 32 per chunk reads the same counts.
+    # (N/4 per column tile).  Backward chunk sums: the state pass on (gy, C).  Backward: the ten causal
+    # 16 x 16 blocks of G (K = N) and K = dY X^T (K = P); for each 16-step block w and 16-state block,
+    # gB = Kd^T C over the row blocks >= w and X G_out^T (K = P), gC = dY H_in^T (K = P) and Kd B over the
+    # column blocks <= w; for each 16-channel block, Z = Mf^T dY over the row blocks >= each column block
+    # and B G_out (K = N).  SQ_VALU_MFMA_BUSY_CYCLES / 32 per chunk reads the same counts.
     per_chunk = {"head chunk states (matrix cores)": (P // 16) * (N // 16) * 16,
                  "head outputs (matrix cores)": sum((rb + 1) * (N // 4) + (P // 16) * 4 * (rb + 1)
-                                                    + (P // 16) * (N // 4) for rb in range(4))}
+                                                    + (P // 16) * (N // 4) for rb in range(4)),
+                 "head backward chunk sums (matrix cores)": (P // 16) * (N // 16) * 16,
+                 "head backward (matrix cores)": 10 * (N // 4 + P // 4) + (80 + 2 * P) * (N // 16)
+                                                 + (40 + N) * (P // 16)}
     mfma = {}
     for k, n_mfma in per_chunk.items():
         if k in kern:

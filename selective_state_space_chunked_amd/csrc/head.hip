@@ -830,28 +830,13 @@ __global__ __launch_bounds__(kBwdThreads) void head_bwd_kernel(HeadBwdParams p) 
 }
 
 
-// gdelta of the head form: the sum of the head's P rows of gdc (per-channel
-// step-size gradients, or sums over groups of its channels), in order.
-// gdc (B, H * P, L) fp32, out (B, H, L).
-template <typename T>
-__global__ __launch_bounds__(256) void head_gdelta_kernel(const float* __restrict__ gdc, T* __restrict__ out, int B,
-                                                          int H, int P, int L) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= (int64_t)B * H * L) return;
-    const int64_t bh = i / L;
-    const int t = (int)(i - bh * L);
-    const float* src = gdc + bh * P * L + t;
-    float acc = 0.0f;
-    for (int pp = 0; pp < P; ++pp) acc += src[(int64_t)pp * L];
-    out[i] = from_f32<T>(acc);
-}
-// gA[h] = sum over the head's channels p and states n of gA_dn[h*P + p][n], in order
-__global__ __launch_bounds__(64) void head_ga_kernel(const float* __restrict__ ga_dn, float* __restrict__ out, int H,
-                                                     int P, int N) {
+// out[h] = part[h * n] + ... + part[h * n + n - 1], in order (gA from its per-(batch, chunk) terms)
+__global__ __launch_bounds__(64) void head_sum_rows_kernel(const float* __restrict__ part, float* __restrict__ out,
+                                                           int H, int n) {
     const int hh = blockIdx.x * 64 + threadIdx.x;
     if (hh >= H) return;
     float acc = 0.0f;
-    for (int e = 0; e < P * N; ++e) acc += ga_dn[(int64_t)hh * P * N + e];
+    for (int e = 0; e < n; ++e) acc += part[(int64_t)hh * n + e];
     out[hh] = acc;
 }
 
@@ -890,25 +875,8 @@ hipError_t launch_head_bwd(const HeadBwdParams& p, int dtype, hipStream_t st) {
     return hipGetLastError();
 }
 hipError_t launch_head_sum_rows(const float* part, float* out, int H, int n, hipStream_t st) {
-    head_ga_kernel<<<(unsigned)((H + 63) / 64), 64, 0, st>>>(part, out, H, n, 1);
+    head_sum_rows_kernel<<<(unsigned)((H + 63) / 64), 64, 0, st>>>(part, out, H, n);
     return hipGetLastError();
-}
-hipError_t launch_head_reduce(const float* gdc, void* gdelta, const float* ga_dn, float* gA, int B, int H, int R,
-                              int N, int L, int dtype, hipStream_t st, int P) {
-    if (gdelta) {
-        const int64_t n = (int64_t)B * H * L;
-        if (dtype == 0)
-            head_gdelta_kernel<float><<<(unsigned)((n + 255) / 256), 256, 0, st>>>(gdc, (float*)gdelta, B, H, R, L);
-        else
-            head_gdelta_kernel<bf16_t><<<(unsigned)((n + 255) / 256), 256, 0, st>>>(gdc, (bf16_t*)gdelta, B, H, R, L);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    if (gA) {
-        head_ga_kernel<<<(unsigned)((H + 63) / 64), 64, 0, st>>>(ga_dn, gA, H, P, N);
-        return hipGetLastError();
-    }
-    return hipSuccess;
 }
 
 }  // namespace ssm

@@ -63,10 +63,6 @@ struct SelBwdParams {
     int B, D, L, N, ntiles, tiles_per_seg, G, vec;
     // checkpoints of tile k at index k * ckpt_every of ckpt_tiles per sequence (0: ntiles, 1)
     int ckpt_tiles = 0, ckpt_every = 1;
-    // if set: fp32 sums of gdelta over groups of gdgs consecutive channels (gdgs divides the
-    // workgroup's rows), (B, D / gdgs, L), in place of per-channel gdelta
-    float* gdgrp = nullptr;
-    int gdgs = 0;
 };
 struct SensParams {
     const void* delta; const float* A; const void* Bm; const void* C;
@@ -228,11 +224,6 @@ hipError_t launch_head_rchain(const HeadBwdParams& p, hipStream_t st);
 hipError_t launch_head_bwd(const HeadBwdParams& p, int dtype, hipStream_t st);
 // out[h] = sum of part[h * n .. h * n + n - 1], in order
 hipError_t launch_head_sum_rows(const float* part, float* out, int H, int n, hipStream_t st);
-// gdelta (B,H,L) = sums over each head's channels of gdc (B,D,L) fp32; gA (H) =
-// sums of ga_dn (D,N) over each head's channels and states (null skips either)
-// gdc rows per head: R (group sums or channels); ga_dn: P channels x N states per head
-hipError_t launch_head_reduce(const float* gdc, void* gdelta, const float* ga_dn, float* gA, int B, int H, int R,
-                              int N, int L, int dtype, hipStream_t st, int P);
 
 // ------------------------------- PD ----------------------------------------
 struct PDParams {

@@ -398,9 +398,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
 // (no registers held), and its checkpoint into a register, so a tile starts
 // without waiting on HBM.
 // ---------------------------------------------------------------------------
-// GDG: the delta gradients leave as sums over groups of channels (p.gdgrp), a
-// separate instantiation so the other variants' code is unchanged.
-template <typename T, int KPL, int NT, bool SUMMARY, bool WA, int VAR, bool GDG = false>
+template <typename T, int KPL, int NT, bool SUMMARY, bool WA, int VAR>
 __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))) void sel_bwd_kernel(SelBwdParams p) {
     using G = TileGeom<KPL>;
     constexpr int TILE = G::TILE;
@@ -730,9 +728,6 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
                 }
             }
         }
-        float gdv[GDG ? KPL : 1];   // this lane's delta gradients of the tile, for the group sums
-#pragma unroll
-        for (int j = 0; j < (GDG ? KPL : 1); ++j) gdv[j] = 0.0f;
         if (!SUMMARY && act && nval > 0) {
             if (p.gx) {
                 float v[KPL];
@@ -740,7 +735,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
                 for (int j = 0; j < KPL; ++j) v[j] = ZOH ? Sb[j] : dl[j] * Sb[j];
                 store_run<KPL>((T*)p.gx + ((int64_t)b * p.sgx[0] + (int64_t)dc * p.sgx[1]) + tl, v, vec, nval);
             }
-            if (p.gdelta || p.partBias || GDG) {
+            if (p.gdelta || p.partBias) {
                 // gradient w.r.t. delta as given (the projection output when the
                 // step sizes are transformed): d delta/d z times d Loss/d delta
                 float v[KPL];
@@ -767,33 +762,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
                     else store_run<KPL>((T*)p.gdelta + o, v, vec, nval);
                 }
 #pragma unroll
-                for (int j = 0; j < KPL; ++j) {
-                    gbias += j < nval ? v[j] : 0.0f;
-                    if constexpr (GDG) gdv[j] = j < nval ? v[j] : 0.0f;
-                }
-            }
-        }
-        if constexpr (GDG && !SUMMARY && !PERD) {
-            {   // every thread takes part (barriers)
-                // sums over groups of gdgs rows (channels) in row order, through the
-                // reduction buffer, which is free between tiles: rows of TILE + 4 floats
-                constexpr int GW = TILE + 4;
-                static_assert(ROWS * GW <= (int)(sizeof(red) / sizeof(float)), "group-sum rows fit");
-                lds_barrier();   // every wave is past its last read of the buffer
-                float* w = red + row * GW + lane * KPL;
-#pragma unroll
-                for (int j = 0; j < KPL; ++j) w[j] = gdv[j];
-                lds_barrier();
-                const int gs = p.gdgs, ngr = ROWS / gs;
-                for (int o = tid; o < ngr * TILE; o += kBwdThreads) {
-                    const int grp = o / TILE, tt = o - grp * TILE;
-                    const float* src = red + grp * gs * GW + tt;
-                    float sum = 0.0f;
-                    for (int r = 0; r < gs; ++r) sum += src[r * GW];
-                    const int t = t0 + tt;
-                    if (t < L && blockIdx.x * ROWS + grp * gs < p.D)
-                        p.gdgrp[((size_t)b * (p.D / gs) + (size_t)blockIdx.x * ngr + grp) * L + t] = sum;
-                }
+                for (int j = 0; j < KPL; ++j) gbias += j < nval ? v[j] : 0.0f;
             }
         }
     }
@@ -840,16 +809,6 @@ hipError_t launch_sel_fwd_var(const SelFwdParams& p, int dtype, int kpl, bool su
 template <typename T, int NT, int VAR>
 hipError_t sel_bwd_t(const SelBwdParams& p, int kpl, bool summary, hipStream_t st) {
     dim3 grid((p.D + kBwdRows - 1) / kBwdRows, p.B, p.G), block(kBwdThreads);
-    if (p.gdgrp && !summary) {   // group sums of gdelta: 16-step runs, 16 states, Euler
-        if constexpr (NT == 16 && VAR == kVarEuler) {
-            if (kpl != 16) return hipErrorInvalidValue;
-            if (p.partA) sel_bwd_kernel<T, 16, 16, false, true, VAR, true><<<grid, block, 0, st>>>(p);
-            else sel_bwd_kernel<T, 16, 16, false, false, VAR, true><<<grid, block, 0, st>>>(p);
-            return hipGetLastError();
-        } else {
-            return hipErrorInvalidValue;
-        }
-    }
     if (summary) { SSM_SEL_DISPATCH_KPL(kpl, sel_bwd_kernel<T, K_, NT, true, false, VAR><<<grid, block, 0, st>>>(p)) }
     else if (p.partA) { SSM_SEL_DISPATCH_KPL(kpl, sel_bwd_kernel<T, K_, NT, false, true, VAR><<<grid, block, 0, st>>>(p)) }
     else { SSM_SEL_DISPATCH_KPL(kpl, sel_bwd_kernel<T, K_, NT, false, false, VAR><<<grid, block, 0, st>>>(p)) }
