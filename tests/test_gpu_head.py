@@ -157,6 +157,38 @@ def test_head_views_and_noalloc():
         assert_close(k, g[k], og[k], **F32)
 
 
+def test_head_backward_views_and_unaligned_rows():
+    """The backward through strided views: gy a slice of a wider array, gx and gdelta written into slices
+    (the rest left untouched), and x starting one element into its buffer, so no 16-byte row load or 4-step
+    gx store is aligned: every chunk takes the element-wise load and store paths."""
+    ssm = _ssm()
+    B, H, P, N, L = 2, 3, 32, 32, 300
+    cfg = make_head(B, H, P, N, L, "f32", seed=11)
+    g = np.random.default_rng(12)
+    h0 = g.standard_normal((B, H * P, N)).astype(np.float32)
+    ghl = g.standard_normal((B, H * P, N)).astype(np.float32)
+    xbuf = torch.zeros(B * H * P * L + 1, device=DEV)
+    x = xbuf[1:].view(B, H * P, L)
+    x.copy_(T(cfg["x"]))
+    gybig = torch.full((B, H * P, L + 5), 7.0, device=DEV)
+    gybig[:, :, 5:] = T(cfg["gy"])
+    gxbig = torch.full((B, H * P, L + 3), float("nan"), device=DEV)
+    gdbig = torch.full((B, 2 * H, L), float("nan"), device=DEV)
+    t = dict(delta=T(cfg["delta"]), x=x, A=T(cfg["A"]), Bm=T(cfg["Bm"]), C=T(cfg["C"]), h0=T(h0))
+    out = {"gx": gxbig[:, :, 3:], "gdelta": gdbig[:, 1::2]}
+    gr = ssm.scan_bwd(ssm.SSM_HEAD_SCALAR, gy=gybig[:, :, 5:], gh_last=T(ghl), out=out,
+                      want=("gdelta", "gx", "gA", "gBm", "gC", "gh0"), **t)
+    ref = ssm.scan_bwd(ssm.SSM_HEAD_SCALAR, gy=T(cfg["gy"]), gh_last=T(ghl),
+                       want=("gdelta", "gx", "gA", "gBm", "gC", "gh0"), **{**t, "x": T(cfg["x"])})
+    torch.cuda.synchronize()
+    og = oracle.head_bwd(delta=cfg["delta"], x=cfg["x"], A=cfg["A"], Bm=cfg["Bm"], C=cfg["C"], h0=h0, gy=cfg["gy"],
+                         ghlast=ghl, B=B, H=H, P=P, L=L, N=N)
+    for k in ("gdelta", "gx", "gBm", "gC", "gh0", "gA"):
+        assert_close(k, gr[k], og[k], **F32)
+        assert torch.equal(gr[k], ref[k]), k   # the same sums whichever path loaded and stored
+    assert torch.isnan(gxbig[:, :, :3]).all() and torch.isnan(gdbig[:, 0::2]).all()
+
+
 def test_head_full_size():
     """B=8 H=32 P=64 (D=2048) N=16 L=4096 with bf16 streams, the element count of the Mamba-layer workload:
     every element of y, gdelta, gx, gBm, gC against the oracle."""
