@@ -248,6 +248,7 @@ struct PDParams {
     // views: d, b, C, logits rows (b, h) at b * s[0] + h * s[1], steps s[2] apart;
     // dictionary entry (h, k) at h * sdict[0] + k * sdict[1] (0 = shared by the heads)
     int64_t s_d[3], s_b[3], s_C[3], s_lg[3], sdict[2];
+    int dense;   // d, b, C and the scores in their dense (B, H, L, N|K) layout: kernels without the stride math
     int B, H, L, N, K, chunk, G;   // G = number of chunks
     int dtype;                     // 0 fp32, 1 bf16 streams
 };

@@ -168,19 +168,41 @@ __device__ __forceinline__ PDRow pd_row(const PDParams& p) {
     return r;
 }
 
-// 16 steps tb.. of state i of an (L, N) slice (fp32 or bf16) whose steps are
-// sl elements apart (states contiguous); steps past L read 0.
-template <typename T, int NT>
-__device__ __forceinline__ void pd_load16(const T* __restrict__ base, int64_t sl, int tb, int L, int i,
+// 16 steps tb.. of state i of an (L, N) slice (fp32 or bf16); steps past L
+// read 0.  DENSE: rows of N states back to back, 32-bit offsets from one
+// address (constant ones for a compile-time N); otherwise the steps are sl
+// elements apart and each step's address is formed in 64 bits.
+template <typename T, int NT, bool DENSE>
+__device__ __forceinline__ void pd_load16(const T* __restrict__ base, int64_t sl, int tb, int L, int N, int i,
                                           float (&v)[16]) {
-    const T* __restrict__ q = base + (int64_t)tb * sl + i;
-    if (tb + 16 <= L) {
+    if constexpr (DENSE) {
+        const int n = NT ? NT : N;
+        const T* __restrict__ q = base + (size_t)tb * n + i;
+        if (tb + 16 <= L) {
 #pragma unroll
-        for (int j = 0; j < 16; ++j) v[j] = to_f32(q[(int64_t)j * sl]);
+            for (int j = 0; j < 16; ++j) v[j] = to_f32(q[j * n]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) v[j] = tb + j < L ? to_f32(q[j * n]) : 0.0f;
+        }
     } else {
+        const T* __restrict__ q = base + (int64_t)tb * sl + i;
+        if (tb + 16 <= L) {
 #pragma unroll
-        for (int j = 0; j < 16; ++j) v[j] = tb + j < L ? to_f32(q[(int64_t)j * sl]) : 0.0f;
+            for (int j = 0; j < 16; ++j) v[j] = to_f32(q[(int64_t)j * sl]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) v[j] = tb + j < L ? to_f32(q[(int64_t)j * sl]) : 0.0f;
+        }
     }
+}
+
+// The (b, h) rows of d, b, C (and of the scores): dense, or through the views' strides.
+template <typename T, bool DENSE>
+__device__ __forceinline__ const T* pd_rowbase(const void* base, const int64_t (&s)[3], const PDRow& r, size_t srow,
+                                               int W) {
+    if constexpr (DENSE) return (const T*)base + srow * W;
+    return (const T*)base + ((int64_t)r.b * s[0] + (int64_t)r.hh * s[1]);
 }
 
 // ---------------------------------------------------------------------------
@@ -188,7 +210,7 @@ __device__ __forceinline__ void pd_load16(const T* __restrict__ base, int64_t sl
 // Each 16-step block first loads everything it needs (lane l takes the
 // selection of step l; d, b and C for all 16 steps), then runs the steps.
 // ---------------------------------------------------------------------------
-template <typename T, bool SUMMARY, int NT>
+template <typename T, bool SUMMARY, int NT, bool DENSE>
 __global__ __launch_bounds__(256) void pd_fwd_kernel(PDParams p) {
     __shared__ PDShared tb_;
     const PDRow r = pd_row(p);
@@ -209,25 +231,26 @@ __global__ __launch_bounds__(256) void pd_fwd_kernel(PDParams p) {
             if (p.ckpt_out && nl) p.ckpt_out[((size_t)r.s * p.G + r.ch) * N + i] = h;
             if (!nl) h = 0.0f;
         }
-        const T* dbase = (const T*)p.d + ((int64_t)r.b * p.s_d[0] + (int64_t)r.hh * p.s_d[1]);
-        const T* bbase = (const T*)p.b + ((int64_t)r.b * p.s_b[0] + (int64_t)r.hh * p.s_b[1]);
-        const T* cbase = (const T*)p.C + ((int64_t)r.b * p.s_C[0] + (int64_t)r.hh * p.s_C[1]);
-        const T* lbase = p.logits ? (const T*)p.logits + ((int64_t)r.b * p.s_lg[0] + (int64_t)r.hh * p.s_lg[1]) : nullptr;
+        const T* dbase = pd_rowbase<T, DENSE>(p.d, p.s_d, r, srow, N);
+        const T* bbase = pd_rowbase<T, DENSE>(p.b, p.s_b, r, srow, N);
+        const T* cbase = pd_rowbase<T, DENSE>(p.C, p.s_C, r, srow, N);
+        const T* lbase = p.logits ? pd_rowbase<T, DENSE>(p.logits, p.s_lg, r, srow, K) : nullptr;
+        const int64_t lstep = DENSE ? K : p.s_lg[2];
         const int t0 = r.ch * kPChunk;
         for (int blk = 0; blk < kPChunk / 16; ++blk) {
             const int tb = t0 + 16 * blk;
             const int tl = tb + r.lane;          // the step whose selection this lane loads
             int kl = 0;
             if (tl < L) {
-                if (SUMMARY) kl = lbase ? pd_argmax(lbase + (int64_t)tl * p.s_lg[2], K) : p.sel_in[srow + tl];
+                if (SUMMARY) kl = lbase ? pd_argmax(lbase + (int64_t)tl * lstep, K) : p.sel_in[srow + tl];
                 else kl = p.sel[srow + tl];
                 kl = min(max(kl, 0), K - 1);   // given selections outside [0, K) are clamped
             }
             if (SUMMARY && p.sel_out && tl < L) p.sel_out[srow + tl] = kl;
             float dv[16], bv[16], cv[16];
-            pd_load16<T, NT>(dbase, p.s_d[2], tb, L, i, dv);
-            pd_load16<T, NT>(bbase, p.s_b[2], tb, L, i, bv);
-            if (!SUMMARY) pd_load16<T, NT>(cbase, p.s_C[2], tb, L, i, cv);
+            pd_load16<T, NT, DENSE>(dbase, p.s_d[2], tb, L, N, i, dv);
+            pd_load16<T, NT, DENSE>(bbase, p.s_b[2], tb, L, N, i, bv);
+            if (!SUMMARY) pd_load16<T, NT, DENSE>(cbase, p.s_C[2], tb, L, N, i, cv);
             float yp[16];
     #pragma unroll
             for (int j = 0; j < 16; ++j) {
@@ -366,7 +389,7 @@ __device__ __forceinline__ void pd_ste_block(const PDParams& p, const PDShared& 
     }
 }
 
-template <typename T, bool SUMMARY, int NT, int STE = -1>
+template <typename T, bool SUMMARY, int NT, int STE, bool DENSE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(STE >= 0 ? 2 : 3))) void pd_bwd_kernel(PDParams p) {
     __shared__ PDShared tb_;
     const PDRow r = pd_row(p);
@@ -386,9 +409,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(STE >= 0 ? 
             if (p.G > 1) nu = p.nu_in[((size_t)r.s * p.G + r.ch) * N + j];
             else if (p.gh_last) nu = p.gh_last[(size_t)r.s * N + j];
         }
-        const T* dbase = (const T*)p.d + ((int64_t)r.b * p.s_d[0] + (int64_t)r.hh * p.s_d[1]);
-        const T* bbase = (const T*)p.b + ((int64_t)r.b * p.s_b[0] + (int64_t)r.hh * p.s_b[1]);
-        const T* cbase = (const T*)p.C + ((int64_t)r.b * p.s_C[0] + (int64_t)r.hh * p.s_C[1]);
+        const T* dbase = pd_rowbase<T, DENSE>(p.d, p.s_d, r, srow, N);
+        const T* bbase = pd_rowbase<T, DENSE>(p.b, p.s_b, r, srow, N);
+        const T* cbase = pd_rowbase<T, DENSE>(p.C, p.s_C, r, srow, N);
         auto sel_of = [&](int tl) { return tl < L ? min(max(p.sel[srow + tl], 0), K - 1) : 0; };
         float hs[kPChunk + 1];
         if (!SUMMARY) {
@@ -398,8 +421,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(STE >= 0 ? 
                 const int tb = t0 + 16 * blk;
                 const int kl = sel_of(tb + r.lane);
                 float dv[16], bv[16];
-                pd_load16<T, NT>(dbase, p.s_d[2], tb, L, j, dv);
-                pd_load16<T, NT>(bbase, p.s_b[2], tb, L, j, bv);
+                pd_load16<T, NT, DENSE>(dbase, p.s_d[2], tb, L, N, j, dv);
+                pd_load16<T, NT, DENSE>(bbase, p.s_b[2], tb, L, N, j, bv);
     #pragma unroll
                 for (int q = 0; q < 16; ++q) {
                     const int k = __float_as_int(bcast16(__int_as_float(kl), q));
@@ -435,8 +458,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(STE >= 0 ? 
                 }
             }
             float dv[16], cv[16];
-            pd_load16<T, NT>(dbase, p.s_d[2], tb, L, j, dv);
-            pd_load16<T, NT>(cbase, p.s_C[2], tb, L, j, cv);
+            pd_load16<T, NT, DENSE>(dbase, p.s_d[2], tb, L, N, j, dv);
+            pd_load16<T, NT, DENSE>(cbase, p.s_C[2], tb, L, N, j, cv);
             const size_t obase = (srow + tb) * N + j;   // step q at obase + q * N
     #pragma unroll
             for (int q = 15; q >= 0; --q) {
@@ -617,44 +640,46 @@ hipError_t launch_pd_prep(const PDParams& p, hipStream_t st) {
     pd_prep_kernel<<<(n + 255) / 256, 256, 0, st>>>(p.dict, p.sdict[0], p.sdict[1], p.pre, p.pre_cnt, p.H, p.K, p.N);
     return hipGetLastError();
 }
-template <typename T>
+template <typename T, bool DENSE>
 hipError_t pd_fwd_t(const PDParams& p, bool summary, hipStream_t st) {
     dim3 grid((p.G + 15) / 16, p.B * p.H);
     if (p.N == 16) {
-        if (summary) pd_fwd_kernel<T, true, 16><<<grid, 256, 0, st>>>(p);
-        else pd_fwd_kernel<T, false, 16><<<grid, 256, 0, st>>>(p);
+        if (summary) pd_fwd_kernel<T, true, 16, DENSE><<<grid, 256, 0, st>>>(p);
+        else pd_fwd_kernel<T, false, 16, DENSE><<<grid, 256, 0, st>>>(p);
     } else {
-        if (summary) pd_fwd_kernel<T, true, 0><<<grid, 256, 0, st>>>(p);
-        else pd_fwd_kernel<T, false, 0><<<grid, 256, 0, st>>>(p);
+        if (summary) pd_fwd_kernel<T, true, 0, DENSE><<<grid, 256, 0, st>>>(p);
+        else pd_fwd_kernel<T, false, 0, DENSE><<<grid, 256, 0, st>>>(p);
     }
     return hipGetLastError();
 }
 hipError_t launch_pd_fwd(const PDParams& p, bool summary, hipStream_t st) {
-    return p.dtype == 0 ? pd_fwd_t<float>(p, summary, st) : pd_fwd_t<bf16_t>(p, summary, st);
+    if (p.dense) return p.dtype == 0 ? pd_fwd_t<float, true>(p, summary, st) : pd_fwd_t<bf16_t, true>(p, summary, st);
+    return p.dtype == 0 ? pd_fwd_t<float, false>(p, summary, st) : pd_fwd_t<bf16_t, false>(p, summary, st);
 }
 hipError_t launch_pd_combine_fwd(const PDParams& p, hipStream_t st) {
     pd_combine_fwd_kernel<<<p.B * p.H, 256, 0, st>>>(p);
     return hipGetLastError();
 }
-template <typename T>
+template <typename T, bool DENSE>
 hipError_t pd_bwd_t(const PDParams& p, bool summary, hipStream_t st) {
     dim3 grid((p.G + 15) / 16, p.B * p.H);
     // the main backward keeps the generic state count: specialised to 16 its
     // register allocation exceeds the three-waves-per-SIMD budget and spills
     if (summary) {
-        if (p.N == 16) pd_bwd_kernel<T, true, 16><<<grid, 256, 0, st>>>(p);
-        else pd_bwd_kernel<T, true, 0><<<grid, 256, 0, st>>>(p);
+        if (p.N == 16) pd_bwd_kernel<T, true, 16, -1, DENSE><<<grid, 256, 0, st>>>(p);
+        else pd_bwd_kernel<T, true, 0, -1, DENSE><<<grid, 256, 0, st>>>(p);
     } else if (p.glogits) {
-        if (p.K <= 16) pd_bwd_kernel<T, false, 0, 16><<<grid, 256, 0, st>>>(p);
-        else if (std::is_same<T, float>::value) pd_bwd_kernel<T, false, 0, 0><<<grid, 256, 0, st>>>(p);
+        if (p.K <= 16) pd_bwd_kernel<T, false, 0, 16, DENSE><<<grid, 256, 0, st>>>(p);
+        else if (std::is_same<T, float>::value) pd_bwd_kernel<T, false, 0, 0, DENSE><<<grid, 256, 0, st>>>(p);
         else return hipErrorInvalidValue;   // rejected on the host before: the raw gw needs fp32 storage
     } else {
-        pd_bwd_kernel<T, false, 0><<<grid, 256, 0, st>>>(p);
+        pd_bwd_kernel<T, false, 0, -1, DENSE><<<grid, 256, 0, st>>>(p);
     }
     return hipGetLastError();
 }
 hipError_t launch_pd_bwd(const PDParams& p, bool summary, hipStream_t st) {
-    return p.dtype == 0 ? pd_bwd_t<float>(p, summary, st) : pd_bwd_t<bf16_t>(p, summary, st);
+    if (p.dense) return p.dtype == 0 ? pd_bwd_t<float, true>(p, summary, st) : pd_bwd_t<bf16_t, true>(p, summary, st);
+    return p.dtype == 0 ? pd_bwd_t<float, false>(p, summary, st) : pd_bwd_t<bf16_t, false>(p, summary, st);
 }
 hipError_t launch_pd_combine_rev(const PDParams& p, hipStream_t st) {
     pd_combine_rev_kernel<<<p.B * p.H, 256, 0, st>>>(p);
