@@ -280,7 +280,9 @@ def test_output_sensitivity(dt, N, chunk_len, L, t_out, h0):
     assert_close("s_delta", out["s_delta"], sd, **tol)
     assert_close("s_x", out["s_x"], sx, **tol)
     assert_close("y", out["y"], y, **tol)
-    assert torch.equal(out["s_x"], ref["s"])   # the same closed-form costate, bit for bit
+    # the impulse path forms each step's costate factor with its own exp, the delta path as suffix products of
+    # the transitions it needs anyway: the same closed form, equal to rounding
+    assert_close("s_x against the impulse path", out["s_x"], ref["s"].double().cpu().numpy(), **tol)
 
 
 def test_sensitivity_very_long_sequence():
