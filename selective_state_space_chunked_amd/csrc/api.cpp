@@ -448,8 +448,15 @@ void copy_strides(int64_t (&dst)[K], const ScanPlan& p, int r) {
 }
 int sel_var(const ScanPlan& p) { return p.perd ? kVarPerD : p.disc == SSM_ZOH ? kVarZoh : kVarEuler; }
 
+// The impulse sensitivity formed by the main pass (N = 16, Euler, shared B_t and C_t, G > 1): the summary
+// pass writes the tile sums of delta, the suffix kernel turns them into send, the main pass writes s.
+struct FwdSens {
+    void* s;
+    double* send;
+    int t_out;
+};
 int run_sel_fwd(const ssm_scan_args* a, const ScanPlan& p, const SelFwdLayout& lay, void* y, float* h_last,
-                float* ckpt, float* tile_dsum, hipStream_t st) {
+                float* ckpt, float* tile_dsum, hipStream_t st, const FwdSens* sens = nullptr) {
     SelFwdParams q{};
     q.delta = a->delta; q.x = a->x; q.A = a->A; q.Bm = a->Bm; q.C = a->C; q.h0 = a->h0;
     q.carry_in = lay.carry;
@@ -464,10 +471,25 @@ int run_sel_fwd(const ssm_scan_args* a, const ScanPlan& p, const SelFwdLayout& l
     q.sA = p.v.s[SSM_V_A][0];
     q.bc_vec = sel_bc_vec(p, a->Bm, a->C);
     q.var = sel_var(p);
+    if (sens) {
+        q.vec = sel_vec(p, {a->delta, a->x, y, sens->s}, {SSM_V_DELTA, SSM_V_X, SSM_V_Y});
+    }
     if (lay.G > 1) {
-        SSM_LAUNCH(launch_sel_fwd(q, p.dtype, p.kpl, true, st), "selective forward summary");
+        SelFwdParams qs = q;
+        qs.tile_dsum = sens ? tile_dsum : nullptr;   // with the sensitivity the main pass writes none
+        SSM_LAUNCH(launch_sel_fwd(qs, p.dtype, p.kpl, true, st), "selective forward summary");
         SSM_LAUNCH(launch_seg_combine_fwd(lay.segP, lay.segS, a->h0, lay.carry, (int)(p.B * p.D), lay.G,
                                           (int)p.N, st), "segment combine");
+    }
+    if (sens) {
+        SSM_LAUNCH(launch_sens_suffix(a->delta, p.v.s[SSM_V_DELTA][0], p.v.s[SSM_V_DELTA][1],
+                                      StepXform{a->delta_bias, a->delta_softplus}, tile_dsum, sens->send, (int)p.B,
+                                      (int)p.D, (int)p.L, p.nchunks, p.T, sens->t_out, p.dtype, st),
+                   "suffix sums");
+        q.tile_dsum = nullptr;
+        q.s = sens->s; q.send = sens->send; q.t_out = sens->t_out;
+        SSM_LAUNCH(launch_sel_fwd_sens(q, p.dtype, p.kpl, st), "selective forward + sensitivity");
+        return SSM_OK;
     }
     SSM_LAUNCH(launch_sel_fwd(q, p.dtype, p.kpl, false, st), "selective forward");
     return SSM_OK;
@@ -876,6 +898,7 @@ int impulse_impl(const ssm_scan_args* a, int64_t t_out, void* y, void* s, void* 
                                                      {s_delta, BDL * p.esz, "s_delta"}})))
             return rc;
     }
+    const bool fusable = y && s && !with_delta && p.N == 16 && sel_var(p) == kVarEuler;
     auto layout = [&](Carve& cv, SelFwdLayout* lay, float** tsum, double** send, float** ckpt) {
         sel_fwd_layout(p, cv, lay);
         *tsum = cv.take<float>((size_t)p.B * p.D * p.nchunks);
@@ -892,6 +915,11 @@ int impulse_impl(const ssm_scan_args* a, int64_t t_out, void* y, void* s, void* 
     if ((rc = check_ws(ws, ws_bytes, cv.off))) return rc;
     Carve real(ws);
     layout(real, &lay, &tsum, &send, &ckpt);
+    if (fusable && lay.G > 1) {
+        // one pass forms y and s: no separate sensitivity kernel
+        const FwdSens fs{s, send, (int)t_out};
+        return run_sel_fwd(a, p, lay, y, nullptr, nullptr, tsum, st, &fs);
+    }
     if (y || with_delta) {
         if ((rc = run_sel_fwd(a, p, lay, y, nullptr, ckpt, tsum, st))) return rc;
     } else {

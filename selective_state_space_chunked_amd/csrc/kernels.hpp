@@ -40,6 +40,11 @@ struct SelFwdParams {
     float* segP;            // summary pass: product of a over each segment (B,D,G,N)
     float* segS;            // summary pass: local state at segment end (B,D,G,N)
     float* tile_dsum;       // (B,D,ntiles) sum of delta over each tile, or null
+    // main pass with the impulse sensitivity (B_t, C_t shared, Euler): s = d y[t_out] / d x,
+    // (B,D,L) dense, from send = (B,D,ntiles) sums of delta over later tiles up to t_out
+    void* s = nullptr;
+    const double* send = nullptr;
+    int t_out = 0;
     StepXform stepf;
     int B, D, L, N, ntiles, tiles_per_seg, G, vec;
 };
@@ -100,6 +105,8 @@ hipError_t launch_sel_bwd(const SelBwdParams& p, int dtype, int kpl, bool summar
 hipError_t launch_sel_fwd_perd(const SelFwdParams& p, int dtype, int kpl, bool summary, hipStream_t st);
 hipError_t launch_sel_bwd_perd(const SelBwdParams& p, int dtype, int kpl, bool summary, hipStream_t st);
 hipError_t launch_sel_fwd_zoh(const SelFwdParams& p, int dtype, int kpl, bool summary, hipStream_t st);
+// main forward pass that also forms the impulse sensitivity (selective_sens.hip; N = 16, Euler, shared B_t, C_t)
+hipError_t launch_sel_fwd_sens(const SelFwdParams& p, int dtype, int kpl, hipStream_t st);
 hipError_t launch_sel_bwd_zoh(const SelBwdParams& p, int dtype, int kpl, bool summary, hipStream_t st);
 int sel_bwd_rows();  // channels per backward workgroup (one gB/gC partial per block)
 hipError_t launch_seg_combine_fwd(const float* P, const float* S, const float* h0, float* carry_in,

@@ -245,12 +245,20 @@ __device__ __forceinline__ void read_run(const float* __restrict__ s, float (&v)
 // so four workgroups fit on a CU next to the 128-VGPR budget of four waves per SIMD.
 constexpr int kFwdStates = 8;
 
-template <typename T, int KPL, int NT, bool SUMMARY, int VAR>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void sel_fwd_kernel(SelFwdParams p) {
+// SENS (main pass, Euler, shared B_t, C_t): also the impulse sensitivity
+// s_t = d y[t_out] / d x_t = delta_t sum_n B_t[n] mu_t[n] with the costate
+// mu_t[n] = C_out[n] prod_{t < u <= t_out} a_u[n] (PGF page, abstract: reverse
+// evolution of the costate).  Within a lane's run it is carried back from the
+// run's last step as mu_{j-1} = mu_j a_j with the transitions the scan forms
+// anyway; the run's last step takes one exp, 2^(A2 S) with S the sum of delta
+// after the run up to t_out (later tiles from send, later lanes by a row sum).
+template <typename T, int KPL, int NT, bool SUMMARY, int VAR, bool SENS = false>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SENS ? 3 : 4))) void sel_fwd_kernel(SelFwdParams p) {
     using G = TileGeom<KPL>;
     constexpr int TILE = G::TILE;
     constexpr int NH = kFwdStates;
     constexpr bool PERD = VAR == kVarPerD, ZOH = VAR == kVarZoh;
+    static_assert(!SENS || (!SUMMARY && VAR == kVarEuler), "the sensitivity rides on the Euler main pass");
     __shared__ __align__(16) float sB[PERD ? 4 : NH * G::LDSW];
     __shared__ __align__(16) float sC[(SUMMARY || PERD) ? 4 : NH * G::LDSW];
 
@@ -267,7 +275,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
     const T* __restrict__ crow = (const T*)p.C + ((int64_t)b * p.sC[0] + (int64_t)dc * p.sC[1]);
     const size_t seq = (size_t)b * p.D + dc;
 
-    float A2 = 0.0f, carry = 0.0f, Pseg = 1.0f, invA = 0.0f;
+    float A2 = 0.0f, carry = 0.0f, Pseg = 1.0f, invA = 0.0f, cout = 0.0f;
     if (lane < N) {
         const float Av = p.A[(int64_t)(dc / p.agrp) * p.sA + lane * p.sAn];
         A2 = Av * kLog2e;
@@ -276,6 +284,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
             if (p.G > 1) carry = p.carry_in[(seq * p.G + g) * N + lane];
             else if (p.h0) carry = p.h0[seq * N + lane];
         }
+        if (SENS) cout = to_f32(((const T*)p.C)[(int64_t)b * p.sC[0] + (int64_t)p.t_out * p.sC[2] + lane]);
     }
     const int tile0 = g * p.tiles_per_seg;
     const int tile1 = min(tile0 + p.tiles_per_seg, p.ntiles);
@@ -298,7 +307,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
         float dsum = 0.0f;
 #pragma unroll
         for (int j = 0; j < KPL; ++j) dsum += dl[j];
-        if (!SUMMARY && p.tile_dsum) {
+        if (p.tile_dsum) {
             float ts = row_sum(dsum);
             if (act && lane == 0) p.tile_dsum[seq * p.ntiles + tile] = ts;
         }
@@ -307,68 +316,119 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
         float yacc[KPL];
 #pragma unroll
         for (int j = 0; j < KPL; ++j) yacc[j] = 0.0f;
-
-        for (int nb = 0; nb < N; nb += NH) {
-            const int ne = min(nb + NH, N);
-            if constexpr (!PERD) {
-                lds_barrier();
-                stage_states<T, KPL, NT, NH>(sB, (const T*)p.Bm, b, t0, L, N, nb, ne, p.sBm[0],
-                                             p.sBm[2], bcvec);
-                if (!SUMMARY)
-                    stage_states<T, KPL, NT, NH>(sC, (const T*)p.C, b, t0, L, N, nb, ne, p.sC[0], p.sC[2], bcvec);
-                lds_barrier();
-            }
-            // the broadcasts for state n+1 are issued while state n runs (lane n+1's
-            // carry does not change during step n)
-            float A2n_nx = row_bcast_rt(A2, nb), cin_nx = row_bcast_rt(carry, nb);
-            float iA_nx = ZOH ? row_bcast_rt(invA, nb) : 0.0f;
-#pragma unroll 1
-            for (int n = nb; n < ne; ++n) {
-                const int nr = n - nb;   // row of state n in the staged half
-                const float A2n = A2n_nx, cin = cin_nx, iAn = iA_nx;
-                {
-                    const int nn = min(n + 1, ne - 1);
-                    A2n_nx = row_bcast_rt(A2, nn);
-                    cin_nx = row_bcast_rt(carry, nn);
-                    if (ZOH) iA_nx = row_bcast_rt(invA, nn);
-                }
-                float bv[KPL], a[KPL], bx[KPL];
-                if constexpr (PERD) load_col<T, KPL>(bmrow + (int64_t)tl * p.sBm[2] + n, p.sBm[2], nval, bv);
-                else read_run<KPL>(sB + nr * G::LDSW + lane * G::SEG, bv);
-                float S = 0.0f;
+        // sensitivity: tiles after t_out's are zero; in t_out's tile only steps up to t_out count
+        const bool sens_tile = SENS && t0 <= p.t_out;    // uniform
+        const bool tout_tile = SENS && p.t_out < t0 + TILE;
+        float sacc[SENS ? KPL : 1], sbase = 0.0f;
 #pragma unroll
-                for (int j = 0; j < KPL; ++j) {
-                    const float z2 = dl[j] * A2n;
-                    a[j] = __builtin_amdgcn_exp2f(z2);
-                    if constexpr (ZOH) bx[j] = zoh_coef(dl[j], z2 * kLn2, a[j], iAn) * dx[j] * bv[j];
-                    else bx[j] = dx[j] * bv[j];
-                    S = fmaf(a[j], S, bx[j]);
+        for (int j = 0; j < (SENS ? KPL : 1); ++j) sacc[j] = 0.0f;
+        if (sens_tile) {
+            float lsum = dsum;
+            if (tout_tile) {
+                lsum = 0.0f;
+#pragma unroll
+                for (int j = 0; j < KPL; ++j) lsum += tl + j <= p.t_out ? dl[j] : 0.0f;
+            }
+            // sum of delta after this lane's run, up to t_out
+            sbase = (float)p.send[seq * p.ntiles + tile] + row_excl_sum_down(lsum);
+        }
+
+        // the state loop; TOUT: t_out lies inside this tile (sensitivity only)
+        auto states = [&](auto tout_c) {
+            constexpr bool TOUT = decltype(tout_c)::value;
+            for (int nb = 0; nb < N; nb += NH) {
+                const int ne = min(nb + NH, N);
+                if constexpr (!PERD) {
+                    lds_barrier();
+                    stage_states<T, KPL, NT, NH>(sB, (const T*)p.Bm, b, t0, L, N, nb, ne, p.sBm[0],
+                                                 p.sBm[2], bcvec);
+                    if (!SUMMARY)
+                        stage_states<T, KPL, NT, NH>(sC, (const T*)p.C, b, t0, L, N, nb, ne, p.sC[0], p.sC[2], bcvec);
+                    lds_barrier();
                 }
-                float P = __builtin_amdgcn_exp2f(dsum * A2n);
-                row_scan_affine_up(P, S);
-                float newc;
-                if constexpr (SUMMARY) {
-                    const float Pt = row_bcast<15>(P), St = row_bcast<15>(S);
-                    newc = fmaf(Pt, cin, St);
-                    if (lane == n) Pseg *= Pt;
-                } else {
-                    const float hend = fmaf(P, cin, S);
-                    float h = dpp<SSM_DPP_ROW_SHR(1)>(cin, hend);  // state entering this lane's run
-                    newc = row_bcast<15>(hend);
-                    float cv[KPL];
-                    if constexpr (PERD) load_col<T, KPL>(crow + (int64_t)tl * p.sC[2] + n, p.sC[2], nval, cv);
-                    else read_run<KPL>(sC + nr * G::LDSW + lane * G::SEG, cv);
+                // the broadcasts for state n+1 are issued while state n runs (lane n+1's
+                // carry does not change during step n)
+                float A2n_nx = row_bcast_rt(A2, nb), cin_nx = row_bcast_rt(carry, nb);
+                float iA_nx = ZOH ? row_bcast_rt(invA, nb) : 0.0f;
+#pragma unroll 1
+                for (int n = nb; n < ne; ++n) {
+                    const int nr = n - nb;   // row of state n in the staged half
+                    const float A2n = A2n_nx, cin = cin_nx, iAn = iA_nx;
+                    {
+                        const int nn = min(n + 1, ne - 1);
+                        A2n_nx = row_bcast_rt(A2, nn);
+                        cin_nx = row_bcast_rt(carry, nn);
+                        if (ZOH) iA_nx = row_bcast_rt(invA, nn);
+                    }
+                    float bv[KPL], a[KPL], bx[KPL];
+                    if constexpr (PERD) load_col<T, KPL>(bmrow + (int64_t)tl * p.sBm[2] + n, p.sBm[2], nval, bv);
+                    else read_run<KPL>(sB + nr * G::LDSW + lane * G::SEG, bv);
+                    float S = 0.0f;
 #pragma unroll
                     for (int j = 0; j < KPL; ++j) {
-                        h = fmaf(a[j], h, bx[j]);
-                        yacc[j] = fmaf(cv[j], h, yacc[j]);
+                        const float z2 = dl[j] * A2n;
+                        a[j] = __builtin_amdgcn_exp2f(z2);
+                        if constexpr (ZOH) bx[j] = zoh_coef(dl[j], z2 * kLn2, a[j], iAn) * dx[j] * bv[j];
+                        else bx[j] = dx[j] * bv[j];
+                        S = fmaf(a[j], S, bx[j]);
                     }
+                    float P = __builtin_amdgcn_exp2f(dsum * A2n);
+                    row_scan_affine_up(P, S);
+                    if constexpr (SENS) {   // bv is not needed after this
+                        const float Cn = row_bcast_rt(cout, n);
+                        if (sens_tile) {
+                            // costate at the run's last step, then mu_{j-1} = mu_j a_j
+                            float m = Cn * __builtin_amdgcn_exp2f(A2n * sbase);
+                            if constexpr (!TOUT) {
+#pragma unroll
+                                for (int j = KPL - 1; j >= 0; --j) {
+                                    sacc[j] = fmaf(bv[j], m, sacc[j]);
+                                    m *= a[j];
+                                }
+                            } else {
+                                // zero after t_out, C_out at t_out
+                                if (tl + KPL - 1 > p.t_out) m = 0.0f;
+#pragma unroll
+                                for (int j = KPL - 1; j >= 0; --j) {
+                                    if (tl + j == p.t_out) m = Cn;
+                                    sacc[j] = fmaf(bv[j], m, sacc[j]);
+                                    m *= a[j];
+                                }
+                            }
+                        }
+                    }
+                    float newc;
+                    if constexpr (SUMMARY) {
+                        const float Pt = row_bcast<15>(P), St = row_bcast<15>(S);
+                        newc = fmaf(Pt, cin, St);
+                        if (lane == n) Pseg *= Pt;
+                    } else {
+                        const float hend = fmaf(P, cin, S);
+                        float h = dpp<SSM_DPP_ROW_SHR(1)>(cin, hend);  // state entering this lane's run
+                        newc = row_bcast<15>(hend);
+                        float cv[KPL];
+                        if constexpr (PERD) load_col<T, KPL>(crow + (int64_t)tl * p.sC[2] + n, p.sC[2], nval, cv);
+                        else read_run<KPL>(sC + nr * G::LDSW + lane * G::SEG, cv);
+#pragma unroll
+                        for (int j = 0; j < KPL; ++j) {
+                            h = fmaf(a[j], h, bx[j]);
+                            yacc[j] = fmaf(cv[j], h, yacc[j]);
+                        }
+                    }
+                    carry = (lane == n) ? newc : carry;
                 }
-                carry = (lane == n) ? newc : carry;
             }
-        }
+        };
+        if (SENS && tout_tile) states(std::true_type{});
+        else states(std::false_type{});
         if (!SUMMARY && p.y && act && nval > 0)
             store_run<KPL>((T*)p.y + ((int64_t)b * p.sy[0] + (int64_t)dc * p.sy[1]) + tl, yacc, vec, nval);
+        if (SENS && act && nval > 0) {
+            float v[KPL];
+#pragma unroll
+            for (int j = 0; j < KPL; ++j) v[j] = (sens_tile && tl + j <= p.t_out) ? dl[j] * sacc[j] : 0.0f;
+            store_run<KPL>((T*)p.s + seq * L + tl, v, vec, nval);
+        }
     }
     if (SUMMARY) {
         if (act && lane < N) {

@@ -173,9 +173,15 @@ def test_impulse_sensitivity(t_out):
     ("f32", 5, 128, 3000, -1),       # generic state count, 128-step tiles
     ("f32", 16, 64, 2100, 1500),     # 64-step tiles
     ("bf16", 7, 256, 700, 0),
+    ("f32", 16, 256, 4100, 2047),    # t_out at the last step of a tile
+    ("f32", 16, 128, 4100, 2048),    # t_out at the first step of a tile
+    ("f32", 16, 256, 200, 150),      # one tile: no segments, so the separate sensitivity pass
+    ("bf16", 16, 64, 64, 63),
 ])
 def test_impulse_sensitivity_variants(dt, N, chunk_len, L, t_out):
-    """Sensitivity and y for bf16 streams, generic state counts and every tile length, against the oracle."""
+    """Sensitivity and y for bf16 streams, generic state counts and every tile length, against the oracle.
+    With 16 states and the sequence cut into segments the forward's main pass forms s itself; otherwise a
+    separate sensitivity pass does (N = 7 or 5, a single tile)."""
     ssm = _ssm()
     cfg = synth.make_real(B=2, D=20, N=N, L=L, dtype=dt, seed=40 + N + L)
     t = {k: _dev(cfg[k], dt) for k in ("delta", "x", "Bm", "C")}
