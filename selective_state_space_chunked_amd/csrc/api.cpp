@@ -451,7 +451,8 @@ int sel_var(const ScanPlan& p) { return p.perd ? kVarPerD : p.disc == SSM_ZOH ? 
 // The impulse sensitivity formed by the main pass (N = 16, Euler, shared B_t and C_t, G > 1): the summary
 // pass writes the tile sums of delta, the suffix kernel turns them into send, the main pass writes s.
 struct FwdSens {
-    void* s;
+    void* s;         // nullable when s_delta is given
+    void* s_delta;   // nullable: d y[t_out] / d delta
     double* send;
     int t_out;
 };
@@ -472,7 +473,7 @@ int run_sel_fwd(const ssm_scan_args* a, const ScanPlan& p, const SelFwdLayout& l
     q.bc_vec = sel_bc_vec(p, a->Bm, a->C);
     q.var = sel_var(p);
     if (sens) {
-        q.vec = sel_vec(p, {a->delta, a->x, y, sens->s}, {SSM_V_DELTA, SSM_V_X, SSM_V_Y});
+        q.vec = sel_vec(p, {a->delta, a->x, y, sens->s, sens->s_delta}, {SSM_V_DELTA, SSM_V_X, SSM_V_Y});
     }
     if (lay.G > 1) {
         SelFwdParams qs = q;
@@ -487,7 +488,7 @@ int run_sel_fwd(const ssm_scan_args* a, const ScanPlan& p, const SelFwdLayout& l
                                       (int)p.D, (int)p.L, p.nchunks, p.T, sens->t_out, p.dtype, st),
                    "suffix sums");
         q.tile_dsum = nullptr;
-        q.s = sens->s; q.send = sens->send; q.t_out = sens->t_out;
+        q.s = sens->s; q.s_delta = sens->s_delta; q.send = sens->send; q.t_out = sens->t_out;
         SSM_LAUNCH(launch_sel_fwd_sens(q, p.dtype, p.kpl, st), "selective forward + sensitivity");
         return SSM_OK;
     }
@@ -898,12 +899,16 @@ int impulse_impl(const ssm_scan_args* a, int64_t t_out, void* y, void* s, void* 
                                                      {s_delta, BDL * p.esz, "s_delta"}})))
             return rc;
     }
-    const bool fusable = y && s && !with_delta && p.N == 16 && sel_var(p) == kVarEuler;
+    // The forward's main pass forms the sensitivities itself when it runs anyway (y wanted, or the delta
+    // sensitivity, which needs the states), the sequence is cut into segments (their summary pass gives the
+    // tile sums first), N = 16 and the input term is Euler with shared B_t, C_t.
+    const bool fusable = (with_delta || (y && s)) && p.N == 16 && sel_var(p) == kVarEuler;
     auto layout = [&](Carve& cv, SelFwdLayout* lay, float** tsum, double** send, float** ckpt) {
         sel_fwd_layout(p, cv, lay);
         *tsum = cv.take<float>((size_t)p.B * p.D * p.nchunks);
         *send = cv.take<double>((size_t)p.B * p.D * p.nchunks);
-        *ckpt = with_delta ? cv.take<float>((size_t)p.B * p.D * p.nchunks * p.N) : nullptr;
+        const bool fused = fusable && lay->G > 1;
+        *ckpt = with_delta && !fused ? cv.take<float>((size_t)p.B * p.D * p.nchunks * p.N) : nullptr;
     };
     Carve cv(nullptr);
     SelFwdLayout lay;
@@ -916,8 +921,8 @@ int impulse_impl(const ssm_scan_args* a, int64_t t_out, void* y, void* s, void* 
     Carve real(ws);
     layout(real, &lay, &tsum, &send, &ckpt);
     if (fusable && lay.G > 1) {
-        // one pass forms y and s: no separate sensitivity kernel
-        const FwdSens fs{s, send, (int)t_out};
+        // one pass forms y and the sensitivities: no checkpoints, no separate sensitivity kernel
+        const FwdSens fs{s, with_delta ? s_delta : nullptr, send, (int)t_out};
         return run_sel_fwd(a, p, lay, y, nullptr, nullptr, tsum, st, &fs);
     }
     if (y || with_delta) {

@@ -43,6 +43,7 @@ struct SelFwdParams {
     // main pass with the impulse sensitivity (B_t, C_t shared, Euler): s = d y[t_out] / d x,
     // (B,D,L) dense, from send = (B,D,ntiles) sums of delta over later tiles up to t_out
     void* s = nullptr;
+    void* s_delta = nullptr;   // with it also d y[t_out] / d delta, (B,D,L) dense
     const double* send = nullptr;
     int t_out = 0;
     StepXform stepf;
@@ -105,7 +106,8 @@ hipError_t launch_sel_bwd(const SelBwdParams& p, int dtype, int kpl, bool summar
 hipError_t launch_sel_fwd_perd(const SelFwdParams& p, int dtype, int kpl, bool summary, hipStream_t st);
 hipError_t launch_sel_bwd_perd(const SelBwdParams& p, int dtype, int kpl, bool summary, hipStream_t st);
 hipError_t launch_sel_fwd_zoh(const SelFwdParams& p, int dtype, int kpl, bool summary, hipStream_t st);
-// main forward pass that also forms the impulse sensitivity (selective_sens.hip; N = 16, Euler, shared B_t, C_t)
+// main forward pass that also forms the impulse sensitivity, and with s_delta the step-size sensitivity
+// (selective_sens.hip; N = 16, Euler, shared B_t, C_t)
 hipError_t launch_sel_fwd_sens(const SelFwdParams& p, int dtype, int kpl, hipStream_t st);
 hipError_t launch_sel_bwd_zoh(const SelBwdParams& p, int dtype, int kpl, bool summary, hipStream_t st);
 int sel_bwd_rows();  // channels per backward workgroup (one gB/gC partial per block)

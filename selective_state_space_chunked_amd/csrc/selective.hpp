@@ -252,12 +252,16 @@ constexpr int kFwdStates = 8;
 // run's last step as mu_{j-1} = mu_j a_j with the transitions the scan forms
 // anyway; the run's last step takes one exp, 2^(A2 S) with S the sum of delta
 // after the run up to t_out (later tiles from send, later lanes by a row sum).
-template <typename T, int KPL, int NT, bool SUMMARY, int VAR, bool SENS = false>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SENS ? 3 : 4))) void sel_fwd_kernel(SelFwdParams p) {
+// SENS = 2 adds s_delta_t = d y[t_out] / d delta_t
+//   = sum_n mu_t[n] (A[n] a_t[n] h_{t-1}[n] + x_t B_t[n]) = x_t sum_n mu_t B_t + sum_n A[n] mu_{t-1}[n] h_{t-1}[n],
+// with mu_t a_t = mu_{t-1} from the same chain and h_{t-1} from the re-run of the states.
+template <typename T, int KPL, int NT, bool SUMMARY, int VAR, int SENS = 0>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SENS == 2 ? 2 : SENS ? 3 : 4))) void sel_fwd_kernel(SelFwdParams p) {
     using G = TileGeom<KPL>;
     constexpr int TILE = G::TILE;
     constexpr int NH = kFwdStates;
     constexpr bool PERD = VAR == kVarPerD, ZOH = VAR == kVarZoh;
+    constexpr bool WD = SENS == 2;
     static_assert(!SENS || (!SUMMARY && VAR == kVarEuler), "the sensitivity rides on the Euler main pass");
     __shared__ __align__(16) float sB[PERD ? 4 : NH * G::LDSW];
     __shared__ __align__(16) float sC[(SUMMARY || PERD) ? 4 : NH * G::LDSW];
@@ -319,9 +323,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SENS ? 3 : 
         // sensitivity: tiles after t_out's are zero; in t_out's tile only steps up to t_out count
         const bool sens_tile = SENS && t0 <= p.t_out;    // uniform
         const bool tout_tile = SENS && p.t_out < t0 + TILE;
-        float sacc[SENS ? KPL : 1], sbase = 0.0f;
+        float sacc[SENS ? KPL : 1], gd[WD ? KPL : 1], sbase = 0.0f;
 #pragma unroll
         for (int j = 0; j < (SENS ? KPL : 1); ++j) sacc[j] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < (WD ? KPL : 1); ++j) gd[j] = 0.0f;
         if (sens_tile) {
             float lsum = dsum;
             if (tout_tile) {
@@ -374,8 +380,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SENS ? 3 : 
                     }
                     float P = __builtin_amdgcn_exp2f(dsum * A2n);
                     row_scan_affine_up(P, S);
+                    // WD: A[n] mu_{j-1}, used by the re-run below against h_{j-1}
+                    float ma[WD ? KPL : 1];
                     if constexpr (SENS) {   // bv is not needed after this
                         const float Cn = row_bcast_rt(cout, n);
+                        const float An = A2n * kLn2;
                         if (sens_tile) {
                             // costate at the run's last step, then mu_{j-1} = mu_j a_j
                             float m = Cn * __builtin_amdgcn_exp2f(A2n * sbase);
@@ -384,6 +393,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SENS ? 3 : 
                                 for (int j = KPL - 1; j >= 0; --j) {
                                     sacc[j] = fmaf(bv[j], m, sacc[j]);
                                     m *= a[j];
+                                    if constexpr (WD) ma[j] = An * m;
                                 }
                             } else {
                                 // zero after t_out, C_out at t_out
@@ -393,6 +403,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SENS ? 3 : 
                                     if (tl + j == p.t_out) m = Cn;
                                     sacc[j] = fmaf(bv[j], m, sacc[j]);
                                     m *= a[j];
+                                    if constexpr (WD) ma[j] = An * m;
                                 }
                             }
                         }
@@ -409,10 +420,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SENS ? 3 : 
                         float cv[KPL];
                         if constexpr (PERD) load_col<T, KPL>(crow + (int64_t)tl * p.sC[2] + n, p.sC[2], nval, cv);
                         else read_run<KPL>(sC + nr * G::LDSW + lane * G::SEG, cv);
+                        if (WD && sens_tile) {
 #pragma unroll
-                        for (int j = 0; j < KPL; ++j) {
-                            h = fmaf(a[j], h, bx[j]);
-                            yacc[j] = fmaf(cv[j], h, yacc[j]);
+                            for (int j = 0; j < KPL; ++j) {
+                                gd[j] = fmaf(ma[WD ? j : 0], h, gd[j]);   // h = h_{j-1}
+                                h = fmaf(a[j], h, bx[j]);
+                                yacc[j] = fmaf(cv[j], h, yacc[j]);
+                            }
+                        } else {
+#pragma unroll
+                            for (int j = 0; j < KPL; ++j) {
+                                h = fmaf(a[j], h, bx[j]);
+                                yacc[j] = fmaf(cv[j], h, yacc[j]);
+                            }
                         }
                     }
                     carry = (lane == n) ? newc : carry;
@@ -425,9 +445,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SENS ? 3 : 
             store_run<KPL>((T*)p.y + ((int64_t)b * p.sy[0] + (int64_t)dc * p.sy[1]) + tl, yacc, vec, nval);
         if (SENS && act && nval > 0) {
             float v[KPL];
+            if (p.s) {
 #pragma unroll
-            for (int j = 0; j < KPL; ++j) v[j] = (sens_tile && tl + j <= p.t_out) ? dl[j] * sacc[j] : 0.0f;
-            store_run<KPL>((T*)p.s + seq * L + tl, v, vec, nval);
+                for (int j = 0; j < KPL; ++j) v[j] = (sens_tile && tl + j <= p.t_out) ? dl[j] * sacc[j] : 0.0f;
+                store_run<KPL>((T*)p.s + seq * L + tl, v, vec, nval);
+            }
+            if constexpr (WD) {
+                // x is read again here (the tile keeps delta x): d delta / d z times d y / d delta
+                float xv[KPL];
+                if (nval >= KPL) load_run<KPL>(xin + tl, xv, vec);
+                else load_run_masked<T, KPL>(xin + tl, xv, nval);
+#pragma unroll
+                for (int j = 0; j < KPL; ++j)
+                    v[j] = (sens_tile && tl + j <= p.t_out)
+                               ? fmaf(xv[j], sacc[j], gd[j]) * step_xform_grad(dl[j], p.stepf.softplus)
+                               : 0.0f;
+                store_run<KPL>((T*)p.s_delta + seq * L + tl, v, vec, nval);
+            }
         }
     }
     if (SUMMARY) {

@@ -275,13 +275,18 @@ def test_pd_ste_host_checks():
 
 
 def test_output_sensitivity_host_checks():
-    """s_delta is required; its workspace holds the per-tile checkpoints (grows with L, unlike the impulse path)."""
+    """s_delta is required.  With 16 states and the sequence cut into segments the forward's main pass forms
+    the sensitivities and the workspace is the impulse path's; otherwise (here 5 states) it also holds the
+    per-tile checkpoints a separate pass re-runs (growing with L)."""
     L = B.lib()
     rc, n1 = ws_bytes(B.SSM_OP_OUTPUT_SENS, sel_args(length=4096))
     assert rc == 0
-    _, n2 = ws_bytes(B.SSM_OP_OUTPUT_SENS, sel_args(length=8192))
     _, m1 = ws_bytes(B.SSM_OP_IMPULSE, sel_args(length=4096))
-    assert n2 - n1 >= 2 * 32 * 16 * 16 * 4 and n1 > m1   # 16 more tiles x 16 states per channel
+    assert n1 == m1
+    _, k1 = ws_bytes(B.SSM_OP_OUTPUT_SENS, sel_args(length=4096, state=5))
+    _, k2 = ws_bytes(B.SSM_OP_OUTPUT_SENS, sel_args(length=8192, state=5))
+    _, j1 = ws_bytes(B.SSM_OP_IMPULSE, sel_args(length=4096, state=5))
+    assert k2 - k1 >= 2 * 32 * 16 * 5 * 4 and k1 > j1   # 16 more tiles x 5 states per channel
     a = sel_args()
     rc = L.ssm_output_sensitivity(ctypes.byref(a), -1, None, FAKE * 64, None, None, 0, None)
     assert rc == status("SSM_ERR_NULL")

@@ -264,9 +264,13 @@ def test_sensitivity_rows_impulse_config():
     ("bf16", 16, 256, 2600, 2100, True),
     ("f32", 5, 128, 900, 450, True),      # generic state count, 128-step tiles
     ("f32", 16, 64, 700, 0, True),        # t_out = 0: only the first step is sensitive
+    ("f32", 16, 256, 250, 100, True),     # one tile: no segments, so checkpoints and a separate pass
+    ("bf16", 16, 128, 2000, 1023, False),  # t_out at the last step of a tile
 ])
 def test_output_sensitivity(dt, N, chunk_len, L, t_out, h0):
-    """d y[t_out]/d x and d y[t_out]/d delta (and y) against the oracle; s_x equal to the impulse path's."""
+    """d y[t_out]/d x and d y[t_out]/d delta (and y) against the oracle; s_x equal to the impulse path's.
+    With 16 states and segments the forward's main pass forms both sensitivities from the states it re-runs;
+    otherwise (N = 5, a single tile) the forward writes checkpoints and a separate pass re-runs them."""
     ssm = _ssm()
     cfg = synth.make_real(B=2, D=20, N=N, L=L, dtype=dt, seed=60 + N + L)
     t = {k: _dev(cfg[k], dt) for k in ("delta", "x", "Bm", "C")}
