@@ -408,9 +408,12 @@ int ssm_complex_rtrl(const ssm_scan_args* args, const void* gy, const float* gh_
  *   s_x[b,d,t]     = d y[b,d,t_out] / d x[b,d,t]     = delta_t sum_n Bm[b,t,n] mu_t[n],
  *   s_delta[b,d,t] = d y[b,d,t_out] / d delta[b,d,t]
  *                  = sum_n mu_t[n] (A[d,n] a_t[n] h_{t-1}[n] + x_t Bm[b,t,n]),
- * t <= t_out, 0 after; h_{t-1} are the forward states (from h0), recomputed per
- * tile from checkpoints the call writes into its workspace (O(n_chunks * N)
- * per sequence, unlike ssm_impulse_sensitivity).  t_out in [0,L); -1 means
+ * t <= t_out, 0 after; h_{t-1} are the forward states (from h0).  With N = 16,
+ * the Euler term, shared Bm and C and a sequence the call cuts into segments
+ * the forward's main pass forms both sensitivities from the states it re-runs
+ * (workspace as for ssm_impulse_sensitivity); otherwise a separate pass
+ * recomputes the states per tile from checkpoints the call writes into its
+ * workspace (O(n_chunks * N) per sequence).  t_out in [0,L); -1 means
  * L-1.  y, s_x nullable, s_delta required; all (B,D,L) dtype.  With delta_bias or
  * delta_softplus set, s_delta is the sensitivity to the projection output z.
  * SSM_REAL_SELECTIVE only; workspace from ssm_workspace_bytes(SSM_OP_OUTPUT_SENS, ...). */
