@@ -95,9 +95,10 @@ def parse():
     ap.add_argument("--cpu-batches", type=int, default=8, help="batch rows of the headline in the CPU sample")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one 1 GiB device copy (calibrates HBM byte counters)")
-    ap.add_argument("--roof", action="store_true",
-                    help="also measure the issue rate of each VALU instruction class (ssm_roof_probe) at 1, 2, 4 "
-                         "and 8 waves per SIMD and report the measured fp32 FMA ceiling")
+    ap.add_argument("--no-roof", action="store_true",
+                    help="skip the issue-rate probes of each VALU instruction class (ssm_roof_probe) at 1, 2, 4 "
+                         "and 8 waves per SIMD, whose measured fp32 FMA ceiling the line reports by default")
+    ap.add_argument("--roof", action="store_true", help=argparse.SUPPRESS)   # the default; kept for old commands
     return ap.parse_args()
 
 
@@ -681,7 +682,7 @@ def main():
               "cache_flushed_ms": step_stats(head["step"], 20, True),
               "note": "per-step HIP-event times of the headline step; cache_flushed writes 1 GiB before each step"}
     hbm_copy = copy_ceiling()
-    roof_meas = roof_probes() if args.roof else None
+    roof_meas = None if args.no_roof else roof_probes()
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(head["inputs"], args.cpu_batches)
