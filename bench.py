@@ -569,7 +569,7 @@ def device_info():
 
 
 ROOF_KINDS = {0: "v_fma_f32", 1: "v_mul_f32", 2: "v_exp_f32", 3: "v_fmac_f32 (DPP source)",
-              4: "v_permlane32_swap", 5: "v_permlane16_swap", 6: "v_add_f32"}
+              4: "v_permlane32_swap", 5: "v_permlane16_swap", 6: "v_add_f32", 7: "v_fmac_f32"}
 
 
 def roof_probes(iters=2000):
@@ -597,7 +597,9 @@ def roof_probes(iters=2000):
             row[f"{w}_waves_per_simd"] = r.value
         table[name] = {k: round(v / 1e12, 3) for k, v in row.items()}
         table[name]["cycles_per_wave64_instr_best"] = round(simds * 64 * 2.4e9 / max(row.values()), 3)
-    fma_best = max(v for k, v in table["v_fma_f32"].items() if k.endswith("simd")) * 1e12
+    # the fp32 FMA ceiling: the faster of the two encodings (VOP3 v_fma_f32, VOP2 v_fmac_f32)
+    fma_best = max(v for name in ("v_fma_f32", "v_fmac_f32") for k, v in table[name].items()
+                   if k.endswith("simd")) * 1e12
     return {"unit": "T lane-ops/s (whole chip)", "iters": iters, "classes": table,
             "fp32_fma_TFLOPs_measured": round(2 * fma_best / 1e12, 2),
             "note": "cycles_per_wave64_instr_best = 64 lanes x SIMDs x 2.4 GHz / best rate"}

@@ -462,9 +462,10 @@ int ssm_profile_end(int* n_launches, float* ms, const char** names, int capacity
  * device (the arithmetic ceiling the scan kernels' roofline is taken against).
  * Launches `waves` one-wave workgroups (waves / (4 x compute units) waves per
  * SIMD), every lane running `chains` (4 or 8) independent dependency chains of
- * iters x 8 instructions of class `kind`: 0 v_fma_f32, 1 v_mul_f32,
+ * iters x 8 instructions of class `kind`: 0 v_fma_f32 (VOP3), 1 v_mul_f32,
  * 2 v_exp_f32, 3 v_fmac_f32 with a DPP row_shr source (4 chains only),
- * 4 v_permlane32_swap, 5 v_permlane16_swap, 6 v_add_f32.  Times the launch
+ * 4 v_permlane32_swap, 5 v_permlane16_swap, 6 v_add_f32, 7 v_fmac_f32 (VOP2,
+ * accumulating into its addend; 8 chains only).  Times the launch
  * with two HIP events on `stream`, waits for it, and writes lane operations
  * per second (64 x waves x instructions per lane / seconds).  `sink` is a
  * device buffer of waves x 64 floats that is never written in practice (it

@@ -1168,9 +1168,10 @@ int ssm_profile_end(int* n_launches, float* ms, const char** names, int capacity
 
 int ssm_roof_probe(int kind, int chains, int waves, int iters, float* sink, double* lane_ops_per_s, void* stream) {
     if (!sink || !lane_ops_per_s) return fail(SSM_ERR_NULL, "sink and lane_ops_per_s are required");
-    if (kind < 0 || kind > 6) return fail(SSM_ERR_UNSUPPORTED, "unknown probe kind %d", kind);
+    if (kind < 0 || kind > 7) return fail(SSM_ERR_UNSUPPORTED, "unknown probe kind %d", kind);
     if (chains != 4 && chains != 8) return fail(SSM_ERR_UNSUPPORTED, "chains must be 4 or 8");
     if (kind == 3 && chains != 4) return fail(SSM_ERR_UNSUPPORTED, "the DPP probe runs 4 chains");
+    if (kind == 7 && chains != 8) return fail(SSM_ERR_UNSUPPORTED, "the v_fmac_f32 probe runs 8 chains");
     if (waves < 1 || waves > 65536 || iters < 1 || iters > (1 << 24))
         return fail(SSM_ERR_SHAPE, "waves in [1, 65536] and iters in [1, 2^24] required");
     hipStream_t st = (hipStream_t)stream;

@@ -12,13 +12,18 @@
 
 namespace ssm {
 
-// kind: 0 v_fma_f32, 1 v_mul_f32, 2 v_exp_f32, 3 v_fmac_f32 with a row_shr:1
-// DPP source, 4 v_permlane32_swap, 5 v_permlane16_swap, 6 v_add_f32
+// kind: 0 v_fma_f32 (VOP3: the chain value is a multiplicand), 1 v_mul_f32,
+// 2 v_exp_f32, 3 v_fmac_f32 with a row_shr:1 DPP source, 4 v_permlane32_swap,
+// 5 v_permlane16_swap, 6 v_add_f32, 7 v_fmac_f32 (VOP2: the chain value is the
+// addend, which the instruction overwrites)
 template <int KIND, int CH>
 __global__ __launch_bounds__(64) void roof_kernel(float* __restrict__ out, int iters, float seed) {
-    float v[CH];
+    float v[CH], x[CH];
 #pragma unroll
-    for (int c = 0; c < CH; ++c) v[c] = seed + 1e-3f * (float)(threadIdx.x + 7 * c);
+    for (int c = 0; c < CH; ++c) {
+        v[c] = seed + 1e-3f * (float)(threadIdx.x + 7 * c);
+        x[c] = 0.5f + 1e-4f * (float)c * seed;
+    }
     const float m = 0.999f + 1e-7f * seed, k = 1e-3f * seed;
     for (int it = 0; it < iters; ++it) {
 #pragma unroll
@@ -53,6 +58,9 @@ __global__ __launch_bounds__(64) void roof_kernel(float* __restrict__ out, int i
                     v[c] = __int_as_float(s[0]);
                     v[c + 1] = __int_as_float(s[1]);
                 }
+            } else if constexpr (KIND == 7) {
+#pragma unroll
+                for (int c = 0; c < CH; ++c) v[c] = fmaf(x[c], m, v[c]);
             } else {
 #pragma unroll
                 for (int c = 0; c < CH; ++c) v[c] = v[c] + k;
@@ -93,6 +101,7 @@ hipError_t launch_roof(int kind, int chains, int waves, int iters, float* out, h
             case 4: SSM_ROOF(4, 8); break;
             case 5: SSM_ROOF(5, 8); break;
             case 6: SSM_ROOF(6, 8); break;
+            case 7: SSM_ROOF(7, 8); break;
             default: return hipErrorInvalidValue;
         }
     } else {

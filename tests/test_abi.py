@@ -578,3 +578,19 @@ def test_binding_passes_views():
     # per-channel Bm is a view; C expanded over the channels is the default shared layout
     assert args._perd and (lay.given >> B.V_BM) & 1 and not (lay.given >> B.V_C) & 1
     assert list(lay.stride[B.V_BM]) == [480, 160, 4, 1]
+
+
+def test_roof_probe_argument_checks():
+    """The issue-rate probe refuses unknown kinds, chain counts a kind does not run, and NULL outputs before it
+    touches the device."""
+    L = B.lib()
+    L.ssm_roof_probe.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                 ctypes.POINTER(ctypes.c_double), ctypes.c_void_p]
+    r = ctypes.c_double(0.0)
+    sink = ctypes.c_void_p(FAKE)
+    assert L.ssm_roof_probe(8, 8, 4, 10, sink, ctypes.byref(r), None) == status("SSM_ERR_UNSUPPORTED")
+    assert L.ssm_roof_probe(-1, 8, 4, 10, sink, ctypes.byref(r), None) == status("SSM_ERR_UNSUPPORTED")
+    assert L.ssm_roof_probe(3, 8, 4, 10, sink, ctypes.byref(r), None) == status("SSM_ERR_UNSUPPORTED")
+    assert L.ssm_roof_probe(7, 4, 4, 10, sink, ctypes.byref(r), None) == status("SSM_ERR_UNSUPPORTED")
+    assert L.ssm_roof_probe(7, 8, 0, 10, sink, ctypes.byref(r), None) == status("SSM_ERR_SHAPE")
+    assert L.ssm_roof_probe(7, 8, 4, 10, None, ctypes.byref(r), None) == status("SSM_ERR_NULL")

@@ -136,6 +136,25 @@ def test_real_deterministic():
         assert torch.equal(g1[k], g2[k]), k
 
 
+def test_sensitivities_deterministic():
+    """The forward main passes that form the sensitivities give the same bits on every call (y, s; y, s_x,
+    s_delta), with NaN-filled outputs so that an element left unwritten would show."""
+    ssm = _ssm()
+    cfg = synth.make_real(B=2, D=24, N=16, L=3000, dtype="f32", seed=9)
+    t = {k: _dev(cfg[k], "f32") for k in ("delta", "x", "Bm", "C", "A")}
+    runs = []
+    for _ in range(2):
+        out = {k: torch.full((2, 24, 3000), float("nan"), device="cuda") for k in ("y", "s")}
+        ssm.impulse_sensitivity(t_out=2222, out=out, **t)
+        os_ = {k: torch.full((2, 24, 3000), float("nan"), device="cuda") for k in ("y", "s_x", "s_delta")}
+        ssm.output_sensitivity(t_out=2222, want_y=True, out=os_, **t)
+        runs.append({**{"imp_" + k: v for k, v in out.items()}, **{"os_" + k: v for k, v in os_.items()}})
+    torch.cuda.synchronize()
+    for k in runs[0]:
+        assert not torch.isnan(runs[0][k]).any(), k
+        assert torch.equal(runs[0][k], runs[1][k]), k
+
+
 def test_real_resume_split():
     """scan(L) equals scan(L1) followed by scan(L2) started from its h_last."""
     ssm = _ssm()
