@@ -396,7 +396,8 @@ def test_step_sizes_from_projection_sensitivities():
     t = {k: _dev(cfg[k], "f32") for k in ("delta", "x", "Bm", "C", "A", "delta_bias")}
     t["delta_softplus"] = True
     out = ssm.output_sensitivity(t_out=1500, want_y=True, **t)
-    imp = ssm.impulse_sensitivity(t_out=1500, want_y=False, **t)
+    imp = ssm.impulse_sensitivity(t_out=1500, want_y=False, **t)   # separate sensitivity pass
+    impy = ssm.impulse_sensitivity(t_out=1500, want_y=True, **t)   # formed by the forward's main pass
     torch.cuda.synchronize()
     delta = oracle.step_sizes(cfg["delta"], cfg["delta_bias"], True)
     kw = dict(delta=delta, x=cfg["x"], A=cfg["A"], Bm=cfg["Bm"], C=cfg["C"], B=1, D=20, L=L, N=16)
@@ -407,3 +408,5 @@ def test_step_sizes_from_projection_sensitivities():
     assert_close("s_z", out["s_delta"], sz, **F32)
     assert_close("y", out["y"], y, **F32)
     assert_close("impulse s", imp["s"], sx, **F32)
+    assert_close("impulse s (with y)", impy["s"], sx, **F32)
+    assert_close("impulse y", impy["y"], y, **F32)

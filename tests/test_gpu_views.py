@@ -197,8 +197,8 @@ def test_zoh_noalloc_forward():
 
 
 def test_sensitivities_take_views():
-    """The impulse sensitivity and the Jacobian rows with delta a slice, A shared by the channels and B_t, C_t
-    shared by the batch rows."""
+    """The impulse and output sensitivities and the Jacobian rows with delta a slice, A shared by the channels
+    and B_t, C_t shared by the batch rows."""
     ssm = _ssm()
     B, D, N, L = 2, 16, 16, 1500
     cfg = synth.make_real(B=B, D=D, N=N, L=L, seed=40)
@@ -207,9 +207,14 @@ def test_sensitivities_take_views():
              C=T(cfg["C"][:1]).expand(B, L, N))
     out = ssm.impulse_sensitivity(t_out=1234, **t)
     rows = ssm.sensitivity_rows(t_out0=1000, rows=3, **t)
+    osn = ssm.output_sensitivity(t_out=1234, want_y=True, **t)
     torch.cuda.synchronize()
     kw = dict(delta=npy(delta), A=npy(t["A"]), Bm=npy(t["Bm"]), C=npy(t["C"]), B=B, D=D, L=L, N=N)
     assert_close("s", out["s"], oracle.impulse_sens(**kw, t_out=1234), **F32)
+    sx, sd = oracle.output_sens(x=cfg["x"], **kw, t_out=1234)
+    assert_close("s_x", osn["s_x"], sx, **F32)
+    assert_close("s_delta", osn["s_delta"], sd, **F32)
+    assert_close("y (output sensitivity)", osn["y"], oracle.real_fwd(x=cfg["x"], **kw)[0], **F32)
     y, _ = oracle.real_fwd(x=cfg["x"], **kw)
     assert_close("y", out["y"], y, **F32)
     for r in range(3):
