@@ -395,8 +395,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
                     if (p.gu && u.act)
                         reinterpret_cast<typename CPair<T>::V*>(p.gu)[((size_t)u.s * L + t) * M + u.m] =
                             CPair<T>::narrow((float)mu.re, (float)mu.im);
-                    const cd ga = cmul(mu, cd{hre[j], -(double)him[j]});
                     if (DENSE) {
+                        const cd ga = cmul(mu, cd{hre[j], -(double)him[j]});
                         if (p.ga && u.act)
                             reinterpret_cast<float2*>(p.ga)[((size_t)u.s * L + t) * M + u.m] =
                                 make_float2((float)ga.re, (float)ga.im);
@@ -407,7 +407,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
                         nu = cmul_conj_a(a, mu);
                         continue;
                     }
-                    const cd gz = cmul_conj_a(a, ga);
+                    // g_z = conj(a) mu conj(h_{t-1}) = nu_t conj(h_{t-1}): one product on the new adjoint
+                    const cd nun = cmul_conj_a(a, mu);
+                    const cd gz = cmul(nun, cd{hre[j], -(double)him[j]});
                     if (u.act) {
                         grp[jj] = gz.re * lnl;
                         gpp[jj] = gz.im * th;
@@ -416,7 +418,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
                         gcr = fma(g, (double)hre[j + 1], gcr);
                         gci = fma(-g, (double)him[j + 1], gci);
                     }
-                    nu = cmul_conj_a(a, mu);
+                    nu = nun;
                 }
             }
             if (DENSE) continue;
