@@ -241,8 +241,10 @@ __device__ __forceinline__ void read_run(const float* __restrict__ s, float (&v)
 // ---------------------------------------------------------------------------
 // forward (SUMMARY: segment summaries only, no outputs)
 // ---------------------------------------------------------------------------
-// B and C tiles are staged eight states at a time (LDS 2 x 20.7 KB for KPL 16),
-// so four workgroups fit on a CU next to the 128-VGPR budget of four waves per SIMD.
+// The plain main pass stages its B and C tiles eight states at a time (LDS 2 x
+// 10.4 KB for KPL 16), so four workgroups fit on a CU next to the 128-VGPR
+// budget of four waves per SIMD; the summary and sensitivity passes stage all
+// 16 states per round.
 constexpr int kFwdStates = 8;
 
 // SENS (main pass, Euler, shared B_t, C_t): also the impulse sensitivity
@@ -259,7 +261,9 @@ template <typename T, int KPL, int NT, bool SUMMARY, int VAR, int SENS = 0>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SENS == 2 ? 2 : SENS ? 3 : 4))) void sel_fwd_kernel(SelFwdParams p) {
     using G = TileGeom<KPL>;
     constexpr int TILE = G::TILE;
-    constexpr int NH = kFwdStates;
+    // states staged per round: all 16 where LDS does not limit the occupancy (the summary pass stages
+    // no C; the sensitivity pass holds 3 waves per SIMD by its registers anyway)
+    constexpr int NH = (SUMMARY || SENS) ? 16 : kFwdStates;
     constexpr bool PERD = VAR == kVarPerD, ZOH = VAR == kVarZoh;
     constexpr bool WD = SENS == 2;
     static_assert(!SENS || (!SUMMARY && VAR == kVarEuler), "the sensitivity rides on the Euler main pass");
