@@ -62,21 +62,25 @@ MEASURED_TRAFFIC = {
                            # SQ_ACTIVE_INST_VALU x 4 cycles over 1024 SIMD x kernel cycles, and cycles per
                            # VALU instruction (profiles/selective_headline_counters.md)
                            "valu_busy": 0.82, "cycles_per_valu_instr": 4.45,
-                           "sources_sha256": "d1a8ec2334dabd3f1e6996c3d5b0b6d9becc1f7ef7cbce28676bc21e10149b75"},
+                           "sources_sha256": "7aa15ddc9a2c187eaec9312f3f124733b42098951f21341c6748b94e9487cf73"},
 }
-# (file, marker where the hashed text ends; None = whole file)
-TRAFFIC_SOURCES = (("selective.hpp", None), ("real_selective.hip", "// segment combines"), ("common.hpp", None))
+# (file, hashed spans as (start marker, end marker); None = start / end of the file)
+TRAFFIC_SOURCES = (("selective.hpp", ((None, "// forward (SUMMARY"), ("// backward.  Reverse over the tiles", None))),
+                   ("real_selective.hip", ((None, "// segment combines"),)), ("common.hpp", ((None, None),)))
 
 
 def kernel_sources_sha256():
-    """SHA-256 of what the selective backward is built from: the kernel header (helpers, forward and backward
-    kernels), the part of its translation unit before the segment combines, the shared device helpers and its
-    parameter struct (later kernels in that file and the other modes' structs in kernels.hpp do not change it)."""
+    """SHA-256 of what the selective backward is built from: the kernel header's helpers and backward kernel
+    (not its forward kernel), the part of its translation unit before the segment combines, the shared device
+    helpers and its parameter struct (later kernels in that file and the other modes' structs in kernels.hpp do
+    not change it)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "selective_state_space_chunked_amd", "csrc")
-    for f, end in TRAFFIC_SOURCES:
+    for f, spans in TRAFFIC_SOURCES:
         text = open(os.path.join(csrc, f)).read()
-        h.update(text[:text.index(end)].encode() if end else text.encode())
+        for start, end in spans:
+            a = text.index(start) if start else 0
+            h.update(text[a:text.index(end, a) if end else len(text)].encode())
     hdr = open(os.path.join(csrc, "kernels.hpp")).read()
     for struct in ("struct StepXform {", "struct SelBwdParams {"):
         i = hdr.index(struct)
