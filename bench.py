@@ -62,6 +62,10 @@ MEASURED_TRAFFIC = {
                            # SQ_ACTIVE_INST_VALU x 4 cycles over 1024 SIMD x kernel cycles, and cycles per
                            # VALU instruction (profiles/selective_headline_counters.md)
                            "valu_busy": 0.82, "cycles_per_valu_instr": 4.45,
+                           # per-class instruction counts x the issue-rate probes' cycles per class, over the
+                           # kernel's cycles; and the fraction of wave cycles waiting at barriers
+                           # (SQ_WAIT_ANY - SQ_WAIT_INST_ANY over SQ_WAVE_CYCLES)
+                           "issue_model_frac": 0.59, "barrier_wait_frac": 0.13,
                            "sources_sha256": "7aa15ddc9a2c187eaec9312f3f124733b42098951f21341c6748b94e9487cf73"},
 }
 # (file, hashed spans as (start marker, end marker); None = start / end of the file)
@@ -640,17 +644,21 @@ def main():
     dur = kern[dom][0] * 1e-3
     flops = FLOPS_PER_ELEMENT[dom] * head["elements"]
     meas = MEASURED_TRAFFIC.get(dom)
-    traffic = valu_busy = None
+    traffic = valu_busy = issue = barrier = None
     if meas and meas["sources_sha256"] == kernel_sources_sha256():
         traffic = meas["read_bytes"] + meas["written_bytes"]
         valu_busy = meas.get("valu_busy")
+        issue, barrier = meas.get("issue_model_frac"), meas.get("barrier_wait_frac")
     roof = {"kernel": dom, "bound": "alu", "achieved": flops / dur / 1e12, "peak": VALU_F32_PEAK / 1e12,
             "unit": "TFLOP/s", "frac": flops / dur / VALU_F32_PEAK, "traffic": traffic,
             "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
             "duration_ms": kern[dom][0], "hbm_frac": head["bytes_kernel"][dom] / dur / HBM_PEAK,
             "flops_per_element": FLOPS_PER_ELEMENT[dom],
             "valu_busy_frac": valu_busy,
-            "valu_busy_note": "fraction of SIMD cycles with a VALU instruction in flight (rocprofv3 counters)"}
+            "valu_busy_note": "fraction of SIMD cycles with a VALU instruction in flight (rocprofv3 counters)",
+            "issue_model_frac": issue, "barrier_wait_frac": barrier,
+            "issue_note": "issue_model_frac: per-class VALU counts x measured cycles per class / kernel cycles; "
+                          "barrier_wait_frac: wave cycles at barriers / wave cycles (rocprofv3 counters)"}
     others = {}
     if not args.no_others:
         todo = [w.strip() for w in args.workloads.split(",") if w.strip()] or \
