@@ -304,6 +304,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SENS == 2 ?
         const int nval = L - tl;
         // dx = delta x (Euler); the ZOH form keeps x itself (its coefficient depends on the state)
         float dl[KPL], dx[KPL];
+        float xk[WD ? KPL : 1];   // the step-size sensitivity keeps x for its x_t sum_n mu B term
         {
             float xv[KPL];
             load_steps<T, KPL>(delta + tl, dl, nval, vec, p.stepf, dc);
@@ -311,6 +312,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SENS == 2 ?
             else load_run_masked<T, KPL>(xin + tl, xv, nval);
 #pragma unroll
             for (int j = 0; j < KPL; ++j) dx[j] = ZOH ? xv[j] : dl[j] * xv[j];
+            if constexpr (WD) {
+#pragma unroll
+                for (int j = 0; j < KPL; ++j) xk[j] = xv[j];
+            }
         }
         float dsum = 0.0f;
 #pragma unroll
@@ -455,14 +460,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SENS == 2 ?
                 store_run<KPL>((T*)p.s + seq * L + tl, v, vec, nval);
             }
             if constexpr (WD) {
-                // x is read again here (the tile keeps delta x): d delta / d z times d y / d delta
-                float xv[KPL];
-                if (nval >= KPL) load_run<KPL>(xin + tl, xv, vec);
-                else load_run_masked<T, KPL>(xin + tl, xv, nval);
+                // d delta / d z times d y / d delta
 #pragma unroll
                 for (int j = 0; j < KPL; ++j)
                     v[j] = (sens_tile && tl + j <= p.t_out)
-                               ? fmaf(xv[j], sacc[j], gd[j]) * step_xform_grad(dl[j], p.stepf.softplus)
+                               ? fmaf(xk[j], sacc[j], gd[j]) * step_xform_grad(dl[j], p.stepf.softplus)
                                : 0.0f;
                 store_run<KPL>((T*)p.s_delta + seq * L + tl, v, vec, nval);
             }
